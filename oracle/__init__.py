@@ -1,0 +1,180 @@
+"""fp64 CPU oracle for the dual-stream Gated DeltaNet layer -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It wraps ``flare_oracle.c`` (plain C, fp64, pthreads over
+independent (document, head) or (request, head) units) through ctypes on numpy
+float64 arrays.  It never imports the HIP library and the HIP library never
+imports it.
+
+What each entry computes, with its source:
+
+* ``gdn_dual_fwd`` -- the gated delta rule of "FLARE: Diffusion for Hybrid
+  Language Model" (papernotes.org notes, Key designs item 2) run token by token
+  over every document; each noisy block copies the clean boundary state, applies
+  its own noisy updates and all of its positions read the block-end state.
+* ``gdn_dual_bwd`` -- reverse mode of the same recurrence, the noisy block-start
+  adjoint added to the clean adjoint at the block boundary (same item).
+* ``block_step`` -- serving EVAL (no pool write) and COMMIT (causal replay that
+  writes the pool), Key designs item 4.
+* ``shortconv_dual`` -- the dual-source causal ShortConv, Key designs item 3.
+
+Parity pins (closed forms, brute force, invariants, finite differences and a
+hand-worked example) are in the CPU tests; see ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "flare_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+FLAG_QK_L2NORM = 1
+EVAL, COMMIT = 0, 1
+
+
+def build() -> str:
+    """Compile ``liboracle.so`` with gcc (always recompiles)."""
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC",
+           "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, f64 = ctypes.c_int, ctypes.c_double
+    lib.oracle_gdn_dual_fwd.argtypes = [i32, P, P, i32, i32, i32, i32, f64, i32] + [P] * 14 + [i32]
+    lib.oracle_gdn_dual_fwd.restype = i32
+    lib.oracle_gdn_dual_bwd.argtypes = [i32, P, P, i32, i32, i32, i32, f64, i32] + [P] * 25 + [i32]
+    lib.oracle_gdn_dual_bwd.restype = i32
+    lib.oracle_block_step.argtypes = [i32, P, P, i32, i32, i32, i32, i32, f64] + [P] * 6 + [i32, i32]
+    lib.oracle_block_step.restype = i32
+    lib.oracle_shortconv_dual.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, i32, P, P, i32]
+    lib.oracle_shortconv_dual.restype = i32
+    lib.oracle_default_threads.argtypes = []
+    lib.oracle_default_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    return int(_load().oracle_default_threads())
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _i32(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _p(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError("%s: invalid arguments (status %d)" % (name, rc))
+
+
+def gdn_dual_fwd(cu_seqlens, prompt_lens, q, k, v, alpha, beta, qn, kn, vn,
+                 alpha_n, beta_n, block_size, h0=None, scale=0.0, flags=0,
+                 threads=0):
+    """Dual-stream forward.  q,k,qn,kn: [T,H,dk]; v,vn: [T,H,dv];
+    gates [T,H]; h0 [N,H,dk,dv] or None.  Returns (o, on, h_final)."""
+    cu, pl = _i32(cu_seqlens), _i32(prompt_lens)
+    q, k, v, a, b = map(_f64, (q, k, v, alpha, beta))
+    qn, kn, vn, an, bn = map(_f64, (qn, kn, vn, alpha_n, beta_n))
+    h0 = _f64(h0)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = len(pl)
+    o = np.zeros((T, H, dv))
+    on = np.zeros((T, H, dv))
+    hf = np.zeros((N, H, dk, dv))
+    rc = _load().oracle_gdn_dual_fwd(N, _p(cu), _p(pl), H, dk, dv, int(block_size),
+                                     float(scale), int(flags), _p(q), _p(k), _p(v),
+                                     _p(a), _p(b), _p(qn), _p(kn), _p(vn), _p(an),
+                                     _p(bn), _p(h0), _p(o), _p(on), _p(hf), int(threads))
+    _check(rc, "gdn_dual_fwd")
+    return o, on, hf
+
+
+def gdn_dual_bwd(cu_seqlens, prompt_lens, q, k, v, alpha, beta, qn, kn, vn,
+                 alpha_n, beta_n, block_size, do, don, h0=None, dh_final=None,
+                 scale=0.0, flags=0, threads=0):
+    """Reverse mode.  Returns a dict with dq, dk, dv, dalpha, dbeta, dqn, dkn,
+    dvn, dalpha_n, dbeta_n, dh0."""
+    cu, pl = _i32(cu_seqlens), _i32(prompt_lens)
+    q, k, v, a, b = map(_f64, (q, k, v, alpha, beta))
+    qn, kn, vn, an, bn = map(_f64, (qn, kn, vn, alpha_n, beta_n))
+    h0, do, don, dhf = _f64(h0), _f64(do), _f64(don), _f64(dh_final)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = len(pl)
+    out = {
+        "dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+        "dalpha": np.zeros((T, H)), "dbeta": np.zeros((T, H)),
+        "dqn": np.zeros((T, H, dk)), "dkn": np.zeros((T, H, dk)), "dvn": np.zeros((T, H, dv)),
+        "dalpha_n": np.zeros((T, H)), "dbeta_n": np.zeros((T, H)),
+        "dh0": np.zeros((N, H, dk, dv)),
+    }
+    rc = _load().oracle_gdn_dual_bwd(
+        N, _p(cu), _p(pl), H, dk, dv, int(block_size), float(scale), int(flags),
+        _p(q), _p(k), _p(v), _p(a), _p(b), _p(qn), _p(kn), _p(vn), _p(an), _p(bn),
+        _p(h0), _p(do), _p(don), _p(dhf),
+        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dalpha"]), _p(out["dbeta"]),
+        _p(out["dqn"]), _p(out["dkn"]), _p(out["dvn"]), _p(out["dalpha_n"]),
+        _p(out["dbeta_n"]), _p(out["dh0"]), int(threads))
+    _check(rc, "gdn_dual_bwd")
+    return out
+
+
+def block_step(slot_idx, pool, q, k, v, alpha, beta, mode, scale=0.0, threads=0):
+    """Serving step.  pool [n_slots,H,dk,dv] is modified in place for COMMIT;
+    q,k [R,B,H,dk], v [R,B,H,dv], gates [R,B,H].  Returns o [R,B,H,dv]."""
+    slot = _i32(slot_idx)
+    if not (isinstance(pool, np.ndarray) and pool.dtype == np.float64 and pool.flags.c_contiguous):
+        raise TypeError("pool must be a C-contiguous float64 array (updated in place)")
+    q, k, v, a, b = map(_f64, (q, k, v, alpha, beta))
+    R, B, H, dk = q.shape
+    dv = v.shape[3]
+    o = np.zeros((R, B, H, dv))
+    rc = _load().oracle_block_step(R, _p(slot), _p(pool), pool.shape[0], H, dk, dv, B,
+                                   float(scale), _p(q), _p(k), _p(v), _p(a), _p(b),
+                                   _p(o), int(mode), int(threads))
+    _check(rc, "block_step")
+    return o
+
+
+def shortconv_dual(cu_seqlens, prompt_lens, block_size, x, xn, weight,
+                   bias=None, activation=0, threads=0):
+    """x, xn [T,C]; weight [C,W]; bias [C] or None.  Returns (y, yn)."""
+    cu, pl = _i32(cu_seqlens), _i32(prompt_lens)
+    x, xn, w, bias = _f64(x), _f64(xn), _f64(weight), _f64(bias)
+    T, C = x.shape
+    W = w.shape[1]
+    y = np.zeros((T, C))
+    yn = np.zeros((T, C))
+    rc = _load().oracle_shortconv_dual(len(pl), _p(cu), _p(pl), int(block_size), C, W,
+                                       _p(x), _p(xn), _p(w), _p(bias), int(activation),
+                                       _p(y), _p(yn), int(threads))
+    _check(rc, "shortconv_dual")
+    return y, yn
