@@ -1,0 +1,255 @@
+"""gated_deltanet_dual_amd -- MI355X (gfx950) dual-stream Gated DeltaNet layer.
+
+A thin ctypes binding over ``libflare_gdn.so`` (the C ABI declared in
+``include/flare_gdn.h``).  This module only marshals arguments: every step of
+the computation runs in the library's HIP kernels.  PyTorch provides device
+memory and the current stream.  There is no fallback: if the library is not
+built, every call raises.
+
+Method: "FLARE: Diffusion for Hybrid Language Model" (papernotes.org notes),
+Overall framework and Key designs items 2-4.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_bwd",
+           "block_step", "shortconv_dual", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
+           "QK_L2NORM", "F32", "BF16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflare_gdn.so")
+
+F32, BF16 = 0, 1
+EVAL, COMMIT = 0, 1
+QK_L2NORM = 1
+
+_STATUS = {0: "OK", 1: "NULL", 2: "SHAPE", 3: "ALIGN", 4: "UNSUPPORTED", 5: "WORKSPACE", 6: "HIP"}
+
+
+class FlareError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("flare status %s (%d): %s" % (_STATUS.get(status, "?"), status, msg))
+        self.status = status
+
+
+class _Varlen(ctypes.Structure):
+    _fields_ = [("num_docs", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+                ("prompt_lens", ctypes.c_void_p), ("prompt_lens_host", ctypes.c_void_p)]
+
+
+class GDNShape(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libflare_gdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libflare_gdn.so is not built: run `python -m gated_deltanet_dual_amd.build`")
+    # torch owns the device memory and streams this library works on, so the
+    # library must bind to the HIP runtime torch already loaded (same soname);
+    # loading it first would bring in a second, separate runtime.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(LIB_PATH)
+    _check_single_hip_runtime()
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    VP, SP = ctypes.POINTER(_Varlen), ctypes.POINTER(GDNShape)
+    L.flare_gdn_chunk_size.restype = I32
+    L.flare_version.restype = I32
+    L.flare_last_error.restype = ctypes.c_char_p
+    L.flare_gdn_dual_workspace_size.argtypes = [VP, SP, ctypes.c_int]
+    L.flare_gdn_dual_workspace_size.restype = SZ
+    L.flare_gdn_dual_ckpt_size.argtypes = [VP, SP, I32]
+    L.flare_gdn_dual_ckpt_size.restype = SZ
+    L.flare_gdn_ckpt_slot.argtypes = [I32, I32, I32, I32]
+    L.flare_gdn_ckpt_slot.restype = ctypes.c_int64
+    L.flare_gdn_dual_fwd.argtypes = [VP, SP] + [P] * 10 + [P, P, P, P, P, I32, P]
+    L.flare_gdn_dual_fwd.restype = ctypes.c_int
+    L.flare_gdn_dual_bwd.argtypes = [VP, SP] + [P] * 10 + [P, P, I32, P, P, P] + [P] * 11 + [P, SZ, P]
+    L.flare_gdn_dual_bwd.restype = ctypes.c_int
+    L.flare_gdn_block_step.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, I32, P]
+    L.flare_gdn_block_step.restype = ctypes.c_int
+    L.flare_shortconv_dual.argtypes = [VP, I32, I32, I32, I32, P, P, P, P, I32, P, P, P]
+    L.flare_shortconv_dual.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check_single_hip_runtime():
+    try:
+        maps = open("/proc/self/maps").read()
+    except OSError:
+        return
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    if len(libs) > 1:
+        raise ImportError("two HIP runtimes are mapped in this process: %s" % sorted(libs))
+
+
+def _check(status):
+    if status != 0:
+        raise FlareError(status, lib().flare_last_error().decode())
+
+
+def chunk_size() -> int:
+    return int(lib().flare_gdn_chunk_size())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Varlen:
+    """Packed batch description: cu_seqlens [N+1] and prompt_lens [N], kept both on
+    the host (validated before launch) and on the device (read by the kernels)."""
+
+    def __init__(self, cu_seqlens, prompt_lens, device="cuda"):
+        torch = _torch()
+        self.cu_host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        self.pl_host = np.ascontiguousarray(np.asarray(prompt_lens, dtype=np.int32))
+        self.cu_dev = torch.from_numpy(self.cu_host).to(device)
+        self.pl_dev = torch.from_numpy(self.pl_host).to(device)
+        self._s = _Varlen(len(self.pl_host), self.cu_dev.data_ptr(),
+                          self.cu_host.ctypes.data, self.pl_dev.data_ptr(), self.pl_host.ctypes.data)
+
+    @property
+    def num_docs(self):
+        return len(self.pl_host)
+
+    @property
+    def total_tokens(self):
+        return int(self.cu_host[-1])
+
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def _shape(H, d, B, io, flags=0, scale=0.0):
+    return GDNShape(H, d, d, B, io, flags, scale)
+
+
+def _io_of(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("io tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def ckpt_slots(varlen: Varlen, H: int, d: int, B: int, io: int, stride: int = 1) -> int:
+    nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(_shape(H, d, B, io)), stride)
+    return nbytes // (H * d * d * 4)
+
+
+def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,
+                 h0=None, scale=0.0, flags=0, want_h_final=True, want_ckpt=False, out=None):
+    """Dual-stream forward.  q,k,qn,kn [T,H,d]; v,vn [T,H,d]; gates [T,H] fp32;
+    h0 [N,H,d,d] fp32 or None.  Returns (o, on, h_final, ckpt)."""
+    torch = _torch()
+    T, H, d = q.shape
+    io = _io_of(q)
+    shp = _shape(H, d, block_size, io, flags, scale)
+    if out is None:
+        o = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+        on = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    else:
+        o, on = out
+    hf = torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=q.device) if want_h_final else None
+    ck = None
+    if want_ckpt:
+        nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1)
+        if nbytes == 0:
+            raise FlareError(2, "invalid arguments for the checkpoint size")
+        ck = torch.empty((nbytes // (H * d * d * 4), H, d, d), dtype=torch.float32, device=q.device)
+    _check(lib().flare_gdn_dual_fwd(varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(alpha), _ptr(beta), _ptr(qn), _ptr(kn), _ptr(vn),
+                                    _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(o), _ptr(on),
+                                    _ptr(hf), _ptr(ck), 1, _stream(q.device)))
+    return o, on, hf, ck
+
+
+def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,
+                 ckpt, d_o, d_on, h0=None, dh_final=None, scale=0.0, flags=0, want_dh0=True,
+                 workspace=None):
+    """Reverse mode.  Returns a dict of gradients (same names as the oracle)."""
+    torch = _torch()
+    T, H, d = q.shape
+    io = _io_of(q)
+    shp = _shape(H, d, block_size, io, flags, scale)
+    dev = q.device
+    ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 1)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    g = {
+        "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+        "dalpha": torch.empty_like(alpha), "dbeta": torch.empty_like(beta),
+        "dqn": torch.empty_like(qn), "dkn": torch.empty_like(kn), "dvn": torch.empty_like(vn),
+        "dalpha_n": torch.empty_like(alpha_n), "dbeta_n": torch.empty_like(beta_n),
+        "dh0": torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=dev) if want_dh0 else None,
+    }
+    _check(lib().flare_gdn_dual_bwd(
+        varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(qn), _ptr(kn), _ptr(vn), _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(ckpt), 1,
+        _ptr(d_o), _ptr(d_on), _ptr(dh_final), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+        _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g["dqn"]), _ptr(g["dkn"]), _ptr(g["dvn"]),
+        _ptr(g["dalpha_n"]), _ptr(g["dbeta_n"]), _ptr(g["dh0"]), _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+    return g
+
+
+def block_step(slot_idx, pool, q, k, v, alpha, beta, mode, scale=0.0, slot_idx_host=None, o=None):
+    """Serving EVAL / COMMIT.  slot_idx [R] int32 (device); pool [n_slots,H,d,d] fp32;
+    q,k,v [R,B,H,d]; gates [R,B,H].  Returns o [R,B,H,d] (None for COMMIT when
+    o is not wanted: pass o=False)."""
+    torch = _torch()
+    R, B, H, d = q.shape
+    shp = _shape(H, d, B, _io_of(q), 0, scale)
+    if o is None:
+        o = torch.empty((R, B, H, d), dtype=q.dtype, device=q.device)
+    elif o is False:
+        o = None
+    host = None
+    if slot_idx_host is not None:
+        host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
+    _check(lib().flare_gdn_block_step(R, _ptr(slot_idx), None if host is None else host.ctypes.data,
+                                      _ptr(pool), pool.shape[0], ctypes.byref(shp), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), int(mode),
+                                      _stream(q.device)))
+    return o
+
+
+def shortconv_dual(varlen: Varlen, block_size, x, xn, weight, bias=None, activation=0, out=None):
+    """x, xn [T,C] io; weight [C,W] fp32; bias [C] fp32 or None.  Returns (y, yn)."""
+    torch = _torch()
+    T, C = x.shape
+    W = weight.shape[1]
+    if out is None:
+        y, yn = torch.empty_like(x), torch.empty_like(x)
+    else:
+        y, yn = out
+    _check(lib().flare_shortconv_dual(varlen.ref(), int(block_size), C, W, _io_of(x), _ptr(x), _ptr(xn),
+                                      _ptr(weight), _ptr(bias), int(activation), _ptr(y), _ptr(yn),
+                                      _stream(x.device)))
+    return y, yn

@@ -1,0 +1,182 @@
+// api.hip -- extern "C" entry points of libflare_gdn.so.  Every call validates
+// its arguments on the host (host_plan.cpp) before enqueuing anything on the
+// caller's stream; the library never allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include "host_plan.h"
+#include "kernels.h"
+
+using namespace flare;
+
+static flare_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return FLARE_OK;
+  return fail(FLARE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static flare_status check_fwd_common(const flare_varlen *varlen, const flare_gdn_shape *shape,
+                                     VarlenInfo *vi) {
+  flare_status st = check_gdn_shape(shape);
+  if (st != FLARE_OK) return st;
+  if (shape->io_dtype == FLARE_F32 && shape->d_k != 16)
+    return fail(FLARE_ERR_UNSUPPORTED, "fp32 io is instantiated for d = 16 only");
+  return check_varlen(varlen, shape->block_size, vi);
+}
+
+extern "C" {
+
+int32_t flare_gdn_chunk_size(void) { return kChunk; }
+
+int32_t flare_version(void) { return kVersion; }
+
+const char *flare_last_error(void) { return last_error(); }
+
+size_t flare_gdn_dual_workspace_size(const flare_varlen *varlen, const flare_gdn_shape *shape,
+                                     int for_bwd) {
+  VarlenInfo vi;
+  if (check_fwd_common(varlen, shape, &vi) != FLARE_OK) return 0;
+  return for_bwd ? bwd_workspace_bytes(vi, shape) : 0;
+}
+
+size_t flare_gdn_dual_ckpt_size(const flare_varlen *varlen, const flare_gdn_shape *shape,
+                                int32_t ckpt_stride_chunks) {
+  VarlenInfo vi;
+  if (ckpt_stride_chunks != 1) return 0;
+  if (check_fwd_common(varlen, shape, &vi) != FLARE_OK) return 0;
+  return (size_t)ckpt_num_slots(vi, ckpt_stride_chunks) * shape->num_heads * shape->d_k *
+         shape->d_v * sizeof(float);
+}
+
+int64_t flare_gdn_ckpt_slot(int32_t cu_seqlens_i, int32_t doc_index, int32_t chunk_index,
+                            int32_t ckpt_stride_chunks) {
+  if (ckpt_stride_chunks <= 0) return -1;
+  return ckpt_slot(cu_seqlens_i, doc_index, chunk_index, ckpt_stride_chunks);
+}
+
+flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shape *shape,
+                                const void *q, const void *k, const void *v, const float *alpha,
+                                const float *beta, const void *qn, const void *kn, const void *vn,
+                                const float *alpha_n, const float *beta_n, const float *h0,
+                                void *o, void *on, float *h_final, float *ckpt,
+                                int32_t ckpt_stride_chunks, void *stream) {
+  clear_error();
+  VarlenInfo vi;
+  flare_status st = check_fwd_common(varlen, shape, &vi);
+  if (st != FLARE_OK) return st;
+  if (ckpt && ckpt_stride_chunks != 1)
+    return fail(FLARE_ERR_UNSUPPORTED, "checkpoint stride %d (only 1 is built)", ckpt_stride_chunks);
+  if (vi.total_tokens > 0 &&
+      (!q || !k || !v || !alpha || !beta || !qn || !kn || !vn || !alpha_n || !beta_n || !o || !on))
+    return fail(FLARE_ERR_NULL, "gdn_dual_fwd: a required pointer is NULL");
+  FwdArgs a{};
+  a.num_docs = varlen->num_docs;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.B = shape->block_size;
+  a.flags = shape->flags;
+  a.bf16 = shape->io_dtype == FLARE_BF16;
+  a.ckpt_stride = ckpt ? ckpt_stride_chunks : 1;
+  a.scale = resolve_scale(shape);
+  a.cu = varlen->cu_seqlens;
+  a.plen = varlen->prompt_lens;
+  a.q = q; a.k = k; a.v = v; a.qn = qn; a.kn = kn; a.vn = vn;
+  a.alpha = alpha; a.beta = beta; a.alpha_n = alpha_n; a.beta_n = beta_n;
+  a.h0 = h0; a.o = o; a.on = on; a.h_final = h_final; a.ckpt = ckpt;
+  return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd launch");
+}
+
+flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shape *shape,
+                                const void *q, const void *k, const void *v, const float *alpha,
+                                const float *beta, const void *qn, const void *kn, const void *vn,
+                                const float *alpha_n, const float *beta_n, const float *h0,
+                                const float *ckpt, int32_t ckpt_stride_chunks, const void *d_o,
+                                const void *d_on, const float *dh_final, void *dq, void *dk,
+                                void *dv, float *dalpha, float *dbeta, void *dqn, void *dkn,
+                                void *dvn, float *dalpha_n, float *dbeta_n, float *dh0,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  VarlenInfo vi;
+  flare_status st = check_fwd_common(varlen, shape, &vi);
+  if (st != FLARE_OK) return st;
+  if (ckpt_stride_chunks != 1)
+    return fail(FLARE_ERR_UNSUPPORTED, "checkpoint stride %d (only 1 is built)", ckpt_stride_chunks);
+  if (vi.total_tokens > 0 &&
+      (!q || !k || !v || !alpha || !beta || !qn || !kn || !vn || !alpha_n || !beta_n || !ckpt ||
+       !d_o || !d_on || !dq || !dk || !dv || !dalpha || !dbeta || !dqn || !dkn || !dvn ||
+       !dalpha_n || !dbeta_n))
+    return fail(FLARE_ERR_NULL, "gdn_dual_bwd: a required pointer is NULL");
+  const size_t need = bwd_workspace_bytes(vi, shape);
+  if (vi.total_tokens > 0 && (!workspace || workspace_bytes < need))
+    return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  BwdArgs a{};
+  a.f.num_docs = varlen->num_docs;
+  a.f.H = shape->num_heads;
+  a.f.D = shape->d_k;
+  a.f.B = shape->block_size;
+  a.f.flags = shape->flags;
+  a.f.bf16 = shape->io_dtype == FLARE_BF16;
+  a.f.ckpt_stride = ckpt_stride_chunks;
+  a.f.scale = resolve_scale(shape);
+  a.f.cu = varlen->cu_seqlens;
+  a.f.plen = varlen->prompt_lens;
+  a.f.q = q; a.f.k = k; a.f.v = v; a.f.qn = qn; a.f.kn = kn; a.f.vn = vn;
+  a.f.alpha = alpha; a.f.beta = beta; a.f.alpha_n = alpha_n; a.f.beta_n = beta_n;
+  a.f.h0 = h0;
+  a.ckpt_in = ckpt;
+  a.d_o = d_o; a.d_on = d_on; a.dh_final = dh_final;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dqn = dqn; a.dkn = dkn; a.dvn = dvn;
+  a.dalpha = dalpha; a.dbeta = dbeta; a.dalpha_n = dalpha_n; a.dbeta_n = dbeta_n; a.dh0 = dh0;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.T = vi.total_tokens;
+  return hip_status(launch_gdn_bwd(a, (hipStream_t)stream), "gdn_dual_bwd launch");
+}
+
+flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
+                                  const int32_t *slot_idx_host, float *state_pool,
+                                  int32_t num_slots, const flare_gdn_shape *shape, const void *q,
+                                  const void *k, const void *v, const float *alpha,
+                                  const float *beta, void *o, int32_t mode, void *stream) {
+  clear_error();
+  flare_status st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape,
+                                     q, k, v, alpha, beta, o, mode);
+  if (st != FLARE_OK) return st;
+  BlockStepArgs a{};
+  a.num_req = num_req;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.B = shape->block_size;
+  a.mode = mode;
+  a.bf16 = shape->io_dtype == FLARE_BF16;
+  a.scale = resolve_scale(shape);
+  a.slot_idx = slot_idx;
+  a.pool = state_pool;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+  return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_block_step launch");
+}
+
+flare_status flare_shortconv_dual(const flare_varlen *varlen, int32_t block_size, int32_t channels,
+                                  int32_t width, int32_t io_dtype, const void *x, const void *xn,
+                                  const float *weight, const float *bias, int32_t activation,
+                                  void *y, void *yn, void *stream) {
+  clear_error();
+  VarlenInfo vi;
+  flare_status st = check_shortconv(varlen, block_size, channels, width, io_dtype, x, xn, weight,
+                                    activation, y, yn, &vi);
+  if (st != FLARE_OK) return st;
+  ShortConvArgs a{};
+  a.num_docs = varlen->num_docs;
+  a.B = block_size;
+  a.C = channels;
+  a.W = width;
+  a.activation = activation;
+  a.bf16 = io_dtype == FLARE_BF16;
+  a.T = vi.total_tokens;
+  a.cu = varlen->cu_seqlens;
+  a.plen = varlen->prompt_lens;
+  a.x = x; a.xn = xn; a.w = weight; a.bias = bias; a.y = y; a.yn = yn;
+  return hip_status(launch_shortconv(a, (hipStream_t)stream), "shortconv_dual launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels:
+// bf16 <-> fp32 conversion, the 16x16 MFMA tile primitives and the LDS
+// fragment loaders that feed them.
+//
+// MFMA tile conventions (CDNA 16x16 output tiles, wave64):
+//   output/accumulator: lane l holds D[4*(l>>4) + r][l & 15], r = 0..3
+//   v_mfma_f32_16x16x32_bf16: lane l supplies A[l & 15][8*(l>>4) + e] and
+//     B[8*(l>>4) + e][l & 15], e = 0..7 (A and B use the same k assignment, so a
+//     permutation of k inside the hardware cannot change the product)
+//   v_mfma_f32_16x16x4f32:    lane l supplies A[l & 15][l >> 4], B[l >> 4][l & 15]
+// Every product in the kernels is written as D[i][j] = sum_k A[i][k] * Bt[j][k],
+// with A and Bt both row-major in LDS, so both operands are fetched with the
+// same row-fragment loader.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flare {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+struct __align__(16) u16x8 { u16 v[8]; };
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round to nearest, ties to even (the IEEE default); NaN stays NaN.
+__device__ __forceinline__ u16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+template <typename IO> struct io_traits;
+template <> struct io_traits<float> {
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+};
+template <> struct io_traits<u16> {
+  static __device__ __forceinline__ float to_f(u16 x) { return bf2f(x); }
+  static __device__ __forceinline__ u16 from_f(float x) { return f2bf(x); }
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u16x8 &x) {
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ void mma_bf16(floatx4 &acc, const bf16x8 &a, const bf16x8 &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_f32(floatx4 &acc, float a, float b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// ---------------------------------------------------------------- fragments
+// Row fragment of a row-major bf16 matrix: rows row0 + (l & 15), columns
+// k0 + 8*(l>>4) .. +7 (one 16-byte LDS read).
+__device__ __forceinline__ bf16x8 frag_bf16(const u16 *base, int ld, int row0, int k0) {
+  const int l = lane_id();
+  const u16x8 *p = reinterpret_cast<const u16x8 *>(base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
+  return as_bf16x8(*p);
+}
+
+// Row fragment of a row-major fp32 matrix rounded to bf16 (hi part).
+__device__ __forceinline__ bf16x8 frag_f32_hi(const float *base, int ld, int row0, int k0) {
+  const int l = lane_id();
+  const float4 *p = reinterpret_cast<const float4 *>(base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
+  const float4 x0 = p[0], x1 = p[1];
+  u16x8 h;
+  h.v[0] = f2bf(x0.x); h.v[1] = f2bf(x0.y); h.v[2] = f2bf(x0.z); h.v[3] = f2bf(x0.w);
+  h.v[4] = f2bf(x1.x); h.v[5] = f2bf(x1.y); h.v[6] = f2bf(x1.z); h.v[7] = f2bf(x1.w);
+  return as_bf16x8(h);
+}
+
+// Row fragment of a row-major fp32 matrix split as hi + lo, both bf16, with
+// hi = bf16(x) and lo = bf16(x - hi): x is represented to ~2^-16 relative.
+__device__ __forceinline__ void frag_f32_split(const float *base, int ld, int row0, int k0,
+                                               bf16x8 &hi, bf16x8 &lo) {
+  const int l = lane_id();
+  const float4 *p = reinterpret_cast<const float4 *>(base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
+  const float4 x0 = p[0], x1 = p[1];
+  const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  u16x8 h, o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h.v[e] = f2bf(x[e]);
+    o.v[e] = f2bf(x[e] - bf2f(h.v[e]));
+  }
+  hi = as_bf16x8(h);
+  lo = as_bf16x8(o);
+}
+
+// Column-gather fragment: element (r, k) = base[(k0 + 8*(l>>4) + e) * ld + row0 + (l&15)],
+// i.e. the row fragment of the TRANSPOSE of a row-major bf16 matrix.
+__device__ __forceinline__ bf16x8 frag_bf16_T(const u16 *base, int ld, int row0, int k0) {
+  const int l = lane_id();
+  const u16 *p = base + (k0 + 8 * (l >> 4)) * ld + row0 + (l & 15);
+  u16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h.v[e] = p[e * ld];
+  return as_bf16x8(h);
+}
+
+// fp32 MFMA operands (16x16x4): one element per lane.
+__device__ __forceinline__ float frag1_f32(const float *base, int ld, int row0, int k0) {
+  const int l = lane_id();
+  return base[(row0 + (l & 15)) * ld + k0 + (l >> 4)];
+}
+__device__ __forceinline__ float frag1_f32_T(const float *base, int ld, int row0, int k0) {
+  const int l = lane_id();
+  return base[(k0 + (l >> 4)) * ld + row0 + (l & 15)];
+}
+
+// Output element coordinates of accumulator register r for this lane.
+__device__ __forceinline__ int acc_row(int r) { return 4 * (lane_id() >> 4) + r; }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+}  // namespace flare

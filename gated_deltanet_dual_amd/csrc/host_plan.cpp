@@ -1,0 +1,159 @@
+// host_plan.cpp -- validation of the packed-batch description and shapes before
+// any launch (the cu_seqlens guard and block alignment of "FLARE: Diffusion for
+// Hybrid Language Model", papernotes.org notes, Key designs item 3), plus the
+// checkpoint-slot and workspace arithmetic.
+#include "host_plan.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace flare {
+
+namespace {
+thread_local char g_msg[512] = "";
+}
+
+flare_status fail(flare_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_msg[0] = '\0'; }
+const char *last_error() { return g_msg; }
+
+static bool pow2_le32(int32_t b) {
+  return b == 1 || b == 2 || b == 4 || b == 8 || b == 16 || b == 32;
+}
+
+flare_status check_varlen(const flare_varlen *v, int32_t block_size, VarlenInfo *out) {
+  if (!v) return fail(FLARE_ERR_NULL, "varlen is NULL");
+  if (v->num_docs < 0) return fail(FLARE_ERR_SHAPE, "num_docs < 0 (%d)", v->num_docs);
+  if (!v->cu_seqlens_host || !v->prompt_lens_host)
+    return fail(FLARE_ERR_NULL, "cu_seqlens_host / prompt_lens_host must be given");
+  if (v->num_docs > 0 && (!v->cu_seqlens || !v->prompt_lens))
+    return fail(FLARE_ERR_NULL, "device cu_seqlens / prompt_lens must be given");
+  if (block_size <= 0) return fail(FLARE_ERR_SHAPE, "block_size must be positive");
+  const int32_t *cu = v->cu_seqlens_host;
+  const int32_t *pl = v->prompt_lens_host;
+  if (cu[0] != 0) return fail(FLARE_ERR_SHAPE, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  VarlenInfo vi;
+  vi.num_docs = v->num_docs;
+  for (int32_t i = 0; i < v->num_docs; ++i) {
+    const int64_t n = (int64_t)cu[i + 1] - cu[i];
+    if (n < 0) return fail(FLARE_ERR_SHAPE, "cu_seqlens decreases at document %d", i);
+    if (pl[i] < 0 || pl[i] > n)
+      return fail(FLARE_ERR_SHAPE, "prompt_lens[%d] = %d outside [0, %lld]", i, pl[i], (long long)n);
+    if (pl[i] % block_size != 0)
+      return fail(FLARE_ERR_ALIGN, "prompt_lens[%d] = %d is not a multiple of block_size %d", i,
+                  pl[i], block_size);
+    if (n > vi.max_len) vi.max_len = (int32_t)n;
+    vi.total_chunks += (n + kChunk - 1) / kChunk;
+  }
+  vi.total_tokens = cu[v->num_docs];
+  if (out) *out = vi;
+  return FLARE_OK;
+}
+
+flare_status check_gdn_shape(const flare_gdn_shape *s) {
+  if (!s) return fail(FLARE_ERR_NULL, "shape is NULL");
+  if (s->num_heads <= 0) return fail(FLARE_ERR_SHAPE, "num_heads must be positive");
+  if (s->d_k != s->d_v)
+    return fail(FLARE_ERR_UNSUPPORTED, "d_k (%d) != d_v (%d) is not instantiated", s->d_k, s->d_v);
+  if (s->d_k != 16 && s->d_k != 128)
+    return fail(FLARE_ERR_UNSUPPORTED, "head dim %d not instantiated (16, 128)", s->d_k);
+  if (!pow2_le32(s->block_size))
+    return fail(FLARE_ERR_UNSUPPORTED, "block_size %d not in {1,2,4,8,16,32}", s->block_size);
+  if (kChunk % s->block_size != 0)
+    return fail(FLARE_ERR_ALIGN, "block_size %d does not divide the chunk %d", s->block_size, kChunk);
+  if (s->io_dtype != FLARE_F32 && s->io_dtype != FLARE_BF16)
+    return fail(FLARE_ERR_UNSUPPORTED, "io_dtype %d unknown", s->io_dtype);
+  if (s->flags & ~FLARE_QK_L2NORM) return fail(FLARE_ERR_UNSUPPORTED, "unknown flags 0x%x", s->flags);
+  return FLARE_OK;
+}
+
+float resolve_scale(const flare_gdn_shape *s) {
+  if (s->scale > 0.0f) return s->scale;
+  return 1.0f / __builtin_sqrtf((float)s->d_k);
+}
+
+int64_t ckpt_slot(int32_t cu_i, int32_t doc, int32_t chunk, int32_t stride) {
+  const int64_t span = (int64_t)kChunk * stride;
+  return (int64_t)cu_i / span + doc + chunk / stride;
+}
+
+int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride) {
+  const int64_t span = (int64_t)kChunk * stride;
+  return vi.total_tokens / span + vi.num_docs;
+}
+
+size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
+  // dq and dk (and their noisy twins) are reduced over the d_v tiles: one fp32
+  // partial per tile, [tiles, T, H, d_k] x 4 tensors, plus 256 bytes of slack.
+  const int tiles = s->d_v > 32 ? s->d_v / 32 : 1;
+  const size_t per = (size_t)vi.total_tokens * s->num_heads * s->d_k * sizeof(float);
+  return per * tiles * 4 + 256;
+}
+
+flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
+                              const int32_t *slot_idx_host, const float *pool,
+                              int32_t num_slots, const flare_gdn_shape *s,
+                              const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, const void *o,
+                              int32_t mode) {
+  flare_status st = check_gdn_shape(s);
+  if (st != FLARE_OK) return st;
+  if (num_req < 0) return fail(FLARE_ERR_SHAPE, "num_req < 0");
+  if (num_slots < 0) return fail(FLARE_ERR_SHAPE, "num_slots < 0");
+  if (mode != FLARE_BLOCK_EVAL && mode != FLARE_BLOCK_COMMIT)
+    return fail(FLARE_ERR_SHAPE, "mode %d is neither EVAL nor COMMIT", mode);
+  if (num_req == 0) return FLARE_OK;
+  if (num_req > num_slots) return fail(FLARE_ERR_SHAPE, "num_req %d > num_slots %d", num_req, num_slots);
+  if (!slot_idx || !pool || !q || !k || !v || !alpha || !beta)
+    return fail(FLARE_ERR_NULL, "block_step: a required pointer is NULL");
+  if (mode == FLARE_BLOCK_EVAL && !o) return fail(FLARE_ERR_NULL, "EVAL needs an output buffer");
+  if (slot_idx_host) {
+    // distinct and in range: counting sort over the slot range
+    if (num_slots > (1 << 26)) return fail(FLARE_ERR_SHAPE, "num_slots too large to check");
+    unsigned char *seen = new unsigned char[(size_t)num_slots]();
+    for (int32_t r = 0; r < num_req; ++r) {
+      const int32_t sl = slot_idx_host[r];
+      if (sl < 0 || sl >= num_slots) {
+        delete[] seen;
+        return fail(FLARE_ERR_SHAPE, "slot_idx[%d] = %d outside [0, %d)", r, sl, num_slots);
+      }
+      if (seen[sl]) {
+        delete[] seen;
+        return fail(FLARE_ERR_SHAPE, "slot %d used by two requests", sl);
+      }
+      seen[sl] = 1;
+    }
+    delete[] seen;
+  }
+  return FLARE_OK;
+}
+
+flare_status check_shortconv(const flare_varlen *v, int32_t block_size, int32_t channels,
+                             int32_t width, int32_t io_dtype, const void *x, const void *xn,
+                             const float *w, int32_t activation, const void *y, const void *yn,
+                             VarlenInfo *out) {
+  flare_status st = check_varlen(v, block_size, out);
+  if (st != FLARE_OK) return st;
+  if (channels <= 0) return fail(FLARE_ERR_SHAPE, "channels must be positive");
+  if (width < 1 || width > 8) return fail(FLARE_ERR_UNSUPPORTED, "width %d not in [1, 8]", width);
+  if (io_dtype != FLARE_F32 && io_dtype != FLARE_BF16)
+    return fail(FLARE_ERR_UNSUPPORTED, "io_dtype %d unknown", io_dtype);
+  const int vec = io_dtype == FLARE_BF16 ? 8 : 4;
+  if (channels % vec != 0)
+    return fail(FLARE_ERR_ALIGN, "channels %d must be a multiple of %d", channels, vec);
+  if (activation != 0 && activation != 1)
+    return fail(FLARE_ERR_UNSUPPORTED, "activation %d unknown", activation);
+  if (out->total_tokens > 0 && (!x || !xn || !w || !y || !yn))
+    return fail(FLARE_ERR_NULL, "shortconv: a required pointer is NULL");
+  return FLARE_OK;
+}
+
+}  // namespace flare

@@ -1,0 +1,59 @@
+// host_plan.h -- host-side validation and launch planning for the flare_gdn
+// C ABI.  Pure C++ (no HIP types) so it is unit-testable on a machine without a
+// GPU; the HIP entry points call these before enqueuing anything.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/flare_gdn.h"
+
+namespace flare {
+
+constexpr int kChunk = 32;          // tokens per chunk of the chunk-parallel scan
+constexpr int kVersion = 100;       // 0.1.0
+
+// Records a message for flare_last_error() and returns the status.
+flare_status fail(flare_status st, const char *fmt, ...);
+void clear_error();
+const char *last_error();
+
+// Summary of a validated packed batch.
+struct VarlenInfo {
+  int32_t num_docs = 0;
+  int64_t total_tokens = 0;
+  int32_t max_len = 0;
+  int64_t total_chunks = 0;  // sum over documents of ceil(n_i / kChunk)
+};
+
+// Checks a flare_varlen: non-NULL host and device arrays (device arrays may be
+// NULL only when num_docs == 0 and nothing is launched), cu[0] == 0,
+// non-decreasing, 0 <= P_i <= n_i and P_i % block_size == 0.
+flare_status check_varlen(const flare_varlen *v, int32_t block_size, VarlenInfo *out);
+
+// Checks a flare_gdn_shape for the GDN entry points: heads > 0, d_k == d_v in
+// {16, 128}, block_size in {1,2,4,8,16,32} (divides kChunk), io dtype, flags.
+flare_status check_gdn_shape(const flare_gdn_shape *s);
+
+float resolve_scale(const flare_gdn_shape *s);
+
+int64_t ckpt_slot(int32_t cu_i, int32_t doc, int32_t chunk, int32_t stride);
+int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride);
+
+// Bytes of bwd workspace (partial dq/dk reductions over d_v tiles).
+size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
+
+// Serving step: slots distinct and in range when the host copy is given.
+flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
+                              const int32_t *slot_idx_host, const float *pool,
+                              int32_t num_slots, const flare_gdn_shape *s,
+                              const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, const void *o,
+                              int32_t mode);
+
+flare_status check_shortconv(const flare_varlen *v, int32_t block_size, int32_t channels,
+                             int32_t width, int32_t io_dtype, const void *x, const void *xn,
+                             const float *w, int32_t activation, const void *y, const void *yn,
+                             VarlenInfo *out);
+
+}  // namespace flare

@@ -1,0 +1,54 @@
+// kernels.h -- argument blocks and launchers of the gfx950 kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flare {
+
+struct BlockStepArgs {
+  int num_req, H, D, B, mode, bf16;
+  float scale;
+  const int32_t *slot_idx;
+  float *pool;
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  void *o;
+};
+hipError_t launch_block_step(const BlockStepArgs &a, hipStream_t st);
+
+struct ShortConvArgs {
+  int num_docs, B, C, W, activation, bf16;
+  int64_t T;
+  const int32_t *cu, *plen;
+  const void *x, *xn;
+  const float *w, *bias;
+  void *y, *yn;
+};
+hipError_t launch_shortconv(const ShortConvArgs &a, hipStream_t st);
+
+struct FwdArgs {
+  int num_docs, H, D, B, flags, bf16, ckpt_stride;
+  float scale;
+  const int32_t *cu, *plen;
+  const void *q, *k, *v, *qn, *kn, *vn;
+  const float *alpha, *beta, *alpha_n, *beta_n, *h0;
+  void *o, *on;
+  float *h_final, *ckpt;
+};
+hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
+
+struct BwdArgs {
+  FwdArgs f;
+  const float *ckpt_in;
+  const void *d_o, *d_on;
+  const float *dh_final;
+  void *dq, *dk, *dv, *dqn, *dkn, *dvn;
+  float *dalpha, *dbeta, *dalpha_n, *dbeta_n, *dh0;
+  void *workspace;
+  size_t workspace_bytes;
+  int64_t T;
+};
+hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
+
+}  // namespace flare

@@ -1,0 +1,215 @@
+/*
+ * flare_gdn.h -- C ABI of the MI355X (gfx950) dual-stream Gated DeltaNet
+ * library: the clean causal stream, the block-wise noisy stream, their reverse
+ * mode, the serving block step and the dual-source causal ShortConv.
+ *
+ * Source of the method: "FLARE: Diffusion for Hybrid Language Model"
+ * (papernotes.org notes on arXiv 2606.01774):
+ *   - Overall framework: the prompt is clean causal context only; the response
+ *     is cut into consecutive blocks of B tokens (default 4).
+ *   - Key designs, item 2: gated delta rule
+ *       S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,
+ *     the noisy block b starts from the clean boundary state S_{e(b-1)} and
+ *     every position of the block reads the block-end state, scaled by
+ *     1/sqrt(d_k); only strided clean checkpoints are kept, and the block
+ *     gradients flow into the causal chain.
+ *   - Key designs, item 3: ShortConv of width W before the GDN layer, whose
+ *     taps before the block start read the clean input; cu_seqlens guards and
+ *     block-aligned document boundaries, per-document state reset.
+ *   - Key designs, item 4: denoising forwards read the global causal state pool
+ *     but never write it; a causal replay writes it once the block is fixed.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work is enqueued on it; no entry point synchronises, allocates or
+ *     frees device memory.
+ *   - The caller owns every buffer.  Host arrays are read during the call only.
+ *   - Outputs are fully overwritten (rows that are zero by definition are
+ *     written as zeros); nothing is accumulated into.  Outputs must not alias
+ *     inputs.
+ *   - All arguments are validated on the host before anything is launched; a
+ *     non-OK status means nothing was enqueued.  flare_last_error() returns a
+ *     thread-local message for the last non-OK status of the calling thread.
+ *   - Layouts are row-major with the last dimension contiguous.  T is the total
+ *     number of packed tokens (cu_seqlens_host[num_docs]), H the head count.
+ *   - io dtype (q, k, v, outputs and their gradients): FLARE_F32 or FLARE_BF16.
+ *     Gates (alpha, beta), states and checkpoints are always fp32.
+ */
+#ifndef FLARE_GDN_H
+#define FLARE_GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLARE_OK = 0,
+  FLARE_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  FLARE_ERR_SHAPE = 2,       /* inconsistent sizes / lengths / indices          */
+  FLARE_ERR_ALIGN = 3,       /* prompt length or block size not aligned         */
+  FLARE_ERR_UNSUPPORTED = 4, /* a size or dtype this build does not instantiate */
+  FLARE_ERR_WORKSPACE = 5,   /* workspace too small or misaligned              */
+  FLARE_ERR_HIP = 6          /* the HIP runtime reported an error               */
+} flare_status;
+
+enum { FLARE_F32 = 0, FLARE_BF16 = 1 };
+enum { FLARE_BLOCK_EVAL = 0, FLARE_BLOCK_COMMIT = 1 };
+/* shape.flags: divide q, k (and the noisy q~, k~) by sqrt(sum x^2 + 1e-6)
+ * over d_k per (token, head) before use. */
+#define FLARE_QK_L2NORM 1
+
+/* Packed variable-length batch (the cu_seqlens guard of Key designs item 3).
+ * Documents lie back to back; document i covers tokens
+ * [cu_seqlens[i], cu_seqlens[i+1]) and its first prompt_lens[i] tokens are the
+ * clean-only prompt.  Both arrays must be given on the device (read by the
+ * kernels) and on the host (validated and planned before launch), with equal
+ * contents.  Requirements: cu_seqlens[0] == 0, non-decreasing;
+ * 0 <= prompt_lens[i] <= n_i; prompt_lens[i] % block_size == 0. */
+typedef struct {
+  int32_t num_docs;
+  const int32_t *cu_seqlens;       /* device [num_docs+1] */
+  const int32_t *cu_seqlens_host;  /* host   [num_docs+1] */
+  const int32_t *prompt_lens;      /* device [num_docs]   */
+  const int32_t *prompt_lens_host; /* host   [num_docs]   */
+} flare_varlen;
+
+/* Layer shape.  This build instantiates d_k == d_v in {16, 128} and
+ * block_size in {1, 2, 4, 8, 16, 32}.  scale <= 0 selects 1/sqrt(d_k). */
+typedef struct {
+  int32_t num_heads;
+  int32_t d_k;
+  int32_t d_v;
+  int32_t block_size;
+  int32_t io_dtype; /* FLARE_F32 or FLARE_BF16 */
+  int32_t flags;    /* 0 or FLARE_QK_L2NORM     */
+  float scale;
+} flare_gdn_shape;
+
+/* Tokens per chunk of the chunk-parallel scan (documents are chunked locally,
+ * from their own first token). */
+int32_t flare_gdn_chunk_size(void);
+
+/* Bytes of device workspace flare_gdn_dual_bwd needs for this batch (the
+ * forward needs none).  Returns 0 on invalid arguments. */
+size_t flare_gdn_dual_workspace_size(const flare_varlen *varlen,
+                                     const flare_gdn_shape *shape, int for_bwd);
+
+/* Checkpoints.  With C = flare_gdn_chunk_size() and stride s (in chunks), the
+ * checkpoint of document i, local chunk c (c % s == 0) is the clean state at
+ * the start of that chunk, fp32 [H, d_k, d_v], stored at slot
+ *     floor(cu_seqlens[i] / (C*s)) + i + c / s
+ * of a buffer [num_slots, H, d_k, d_v] with num_slots = floor(T / (C*s)) + N.
+ * The slots of different documents never overlap.  This build supports s = 1.
+ * flare_gdn_dual_ckpt_size returns the buffer size in bytes (0 on invalid
+ * arguments); flare_gdn_ckpt_slot is the slot formula above. */
+size_t flare_gdn_dual_ckpt_size(const flare_varlen *varlen,
+                                const flare_gdn_shape *shape,
+                                int32_t ckpt_stride_chunks);
+int64_t flare_gdn_ckpt_slot(int32_t cu_seqlens_i, int32_t doc_index,
+                            int32_t chunk_index, int32_t ckpt_stride_chunks);
+
+/* Dual-stream forward (Key designs item 2; Overall framework).
+ *   q, k       [T, H, d_k] io      clean queries / keys
+ *   v          [T, H, d_v] io      clean values
+ *   alpha,beta [T, H] fp32         clean gates, 0 < alpha <= 1
+ *   qn,kn,vn,alpha_n,beta_n        noisy stream, same shapes; prompt rows are
+ *                                  never read
+ *   h0         [N, H, d_k, d_v] fp32 initial state per document, NULL = 0
+ *   o          [T, H, d_v] io      clean outputs o_t = s S_t^T q_t
+ *   on         [T, H, d_v] io      noisy outputs: every response position of a
+ *                                  block reads the block-end noisy state; prompt
+ *                                  rows are written 0
+ *   h_final    [N, H, d_k, d_v] fp32 clean state after each document, or NULL
+ *   ckpt       chunk-start clean states for the backward (see
+ *              flare_gdn_dual_ckpt_size), or NULL for inference
+ * The clean block-boundary states are never written to memory. */
+flare_status flare_gdn_dual_fwd(const flare_varlen *varlen,
+                                const flare_gdn_shape *shape, const void *q,
+                                const void *k, const void *v,
+                                const float *alpha, const float *beta,
+                                const void *qn, const void *kn, const void *vn,
+                                const float *alpha_n, const float *beta_n,
+                                const float *h0, void *o, void *on,
+                                float *h_final, float *ckpt,
+                                int32_t ckpt_stride_chunks, void *stream);
+
+/* Reverse mode of flare_gdn_dual_fwd (Key designs items 2 and 3): the adjoint
+ * reaching each noisy block start is added to the clean adjoint at that block's
+ * boundary, the adjoint is reset per document, and nothing crosses documents.
+ * Inputs: the forward's inputs, its checkpoints (same stride), the output
+ * gradients d_o, d_on [T, H, d_v] io (prompt rows of d_on ignored) and
+ * dh_final [N, H, d_k, d_v] fp32 or NULL.
+ * Outputs (written, not accumulated): dq, dk [T,H,d_k], dv [T,H,d_v] io;
+ * dalpha, dbeta [T,H] fp32; the same five for the noisy stream (prompt rows 0);
+ * dh0 [N,H,d_k,d_v] fp32 or NULL.  workspace: see
+ * flare_gdn_dual_workspace_size(..., 1), 256-byte aligned. */
+flare_status flare_gdn_dual_bwd(
+    const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q,
+    const void *k, const void *v, const float *alpha, const float *beta,
+    const void *qn, const void *kn, const void *vn, const float *alpha_n,
+    const float *beta_n, const float *h0, const float *ckpt,
+    int32_t ckpt_stride_chunks, const void *d_o, const void *d_on,
+    const float *dh_final, void *dq, void *dk, void *dv, float *dalpha,
+    float *dbeta, void *dqn, void *dkn, void *dvn, float *dalpha_n,
+    float *dbeta_n, float *dh0, void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/* Serving block step over a pool of per-request recurrent states (Key designs
+ * item 4).
+ *   slot_idx      [num_req] int32 device: pool slot of each request; slots must
+ *                 be distinct and in [0, num_slots).  Checked only when
+ *                 slot_idx_host (same contents) is given; otherwise duplicate or
+ *                 out-of-range slots are undefined behaviour.
+ *   state_pool    [num_slots, H, d_k, d_v] fp32
+ *   q, k          [num_req, B, H, d_k] io;  v [num_req, B, H, d_v] io
+ *   alpha, beta   [num_req, B, H] fp32, B = shape->block_size
+ *   o             [num_req, B, H, d_v] io
+ * FLARE_BLOCK_EVAL: a denoising read.  The B noisy updates are applied to a
+ *   private copy of the pooled state and every position reads the block-end
+ *   state.  The pool is not written.
+ * FLARE_BLOCK_COMMIT: causal replay of the committed block.  The B clean
+ *   updates are applied in order, o_t reads the state after token t (o may be
+ *   NULL to skip the outputs), and the final state is written to the pool. */
+flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
+                                  const int32_t *slot_idx_host,
+                                  float *state_pool, int32_t num_slots,
+                                  const flare_gdn_shape *shape, const void *q,
+                                  const void *k, const void *v,
+                                  const float *alpha, const float *beta,
+                                  void *o, int32_t mode, void *stream);
+
+/* Dual-source depthwise causal ShortConv (Key designs item 3).
+ *   x, xn   [T, channels] io        clean / noisy inputs (xn prompt rows unread)
+ *   weight  [channels, width] fp32  weight[c, width-1] multiplies the current
+ *                                   token
+ *   bias    [channels] fp32 or NULL
+ *   activation 0 = none, 1 = SiLU (applied after the bias)
+ *   y       [T, channels] io  y[t] = sum_j weight[c,j] x[t-(width-1)+j], taps
+ *                             before the document start read 0
+ *   yn      [T, channels] io  same taps, but a tap that lies before the start
+ *                             of t's noisy block reads x (clean history) and a
+ *                             tap inside the block reads xn; prompt rows 0
+ * Requirements: 1 <= width <= 8, channels % 8 == 0 for bf16 (% 4 for f32). */
+flare_status flare_shortconv_dual(const flare_varlen *varlen,
+                                  int32_t block_size, int32_t channels,
+                                  int32_t width, int32_t io_dtype,
+                                  const void *x, const void *xn,
+                                  const float *weight, const float *bias,
+                                  int32_t activation, void *y, void *yn,
+                                  void *stream);
+
+/* Thread-local message for the last non-OK status; "" if none. */
+const char *flare_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t flare_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLARE_GDN_H */

@@ -1,0 +1,151 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the
+header declares, and its host-side validation returns the documented status
+before anything is launched.  Device pointers here are dummies; every call is
+built so that validation fails (or the call is a pure size query), so nothing
+is ever dereferenced or launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gated_deltanet_dual_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flare_gdn.h")
+FAKE = ctypes.c_void_p(0x7F0000001000)  # never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(g.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return g.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(flare_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"flare_gdn_dual_fwd", "flare_gdn_dual_bwd", "flare_gdn_block_step",
+            "flare_shortconv_dual"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_constants(L):
+    assert L.flare_gdn_chunk_size() == 32
+    assert L.flare_version() >= 100
+
+
+def varlen(cu, pl, dev=True):
+    cu = np.ascontiguousarray(np.asarray(cu, np.int32))
+    pl = np.ascontiguousarray(np.asarray(pl, np.int32))
+    v = g._Varlen(len(pl), FAKE.value if dev else None, cu.ctypes.data,
+                  FAKE.value if dev else None, pl.ctypes.data)
+    v._keep = (cu, pl)
+    return v
+
+
+def fwd_status(L, v, shape, ckpt=None, stride=1, null_q=False):
+    P = [None if null_q else FAKE] + [FAKE] * 9
+    return L.flare_gdn_dual_fwd(ctypes.byref(v), ctypes.byref(shape), *P, None, FAKE, FAKE, None,
+                                ckpt, stride, None)
+
+
+def test_fwd_validation(L):
+    ok_shape = g.GDNShape(16, 128, 128, 4, g.BF16, 0, 0.0)
+    # cu_seqlens must start at 0
+    assert fwd_status(L, varlen([1, 9], [0]), ok_shape) == 2
+    # decreasing cu_seqlens
+    assert fwd_status(L, varlen([0, 9, 5], [0, 0]), ok_shape) == 2
+    # prompt longer than the document
+    assert fwd_status(L, varlen([0, 8], [12]), ok_shape) == 2
+    # prompt not a multiple of the block size
+    assert fwd_status(L, varlen([0, 16], [6]), ok_shape) == 3
+    # NULL input with tokens present
+    assert fwd_status(L, varlen([0, 16], [8]), ok_shape, null_q=True) == 1
+    # unsupported head dim / unequal dk, dv / block size / dtype / flags
+    for bad in [g.GDNShape(16, 64, 64, 4, g.BF16, 0, 0.0), g.GDNShape(16, 128, 16, 4, g.BF16, 0, 0.0),
+                g.GDNShape(16, 128, 128, 3, g.BF16, 0, 0.0), g.GDNShape(16, 128, 128, 64, g.BF16, 0, 0.0),
+                g.GDNShape(16, 128, 128, 4, 7, 0, 0.0), g.GDNShape(16, 128, 128, 4, g.BF16, 4, 0.0),
+                g.GDNShape(16, 128, 128, 4, g.F32, 0, 0.0)]:
+        assert fwd_status(L, varlen([0, 16], [8]), bad) == 4
+    assert fwd_status(L, varlen([0, 16], [8]), g.GDNShape(0, 128, 128, 4, g.BF16, 0, 0.0)) == 2
+    # checkpoint stride other than 1 is not built
+    assert fwd_status(L, varlen([0, 16], [8]), ok_shape, ckpt=FAKE, stride=2) == 4
+    # missing host copies
+    v = g._Varlen(1, FAKE.value, None, FAKE.value, None)
+    assert fwd_status(L, v, ok_shape) == 1
+    assert b"cu_seqlens" in L.flare_last_error()
+
+
+def test_bwd_workspace_checked_before_launch(L):
+    shape = g.GDNShape(2, 16, 16, 4, g.F32, 0, 0.0)
+    v = varlen([0, 40, 64], [8, 0])
+    need = L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(shape), 1)
+    assert need >= 4 * 64 * 2 * 16 * 4
+    args = [FAKE] * 10 + [None, FAKE, 1, FAKE, FAKE, None] + [FAKE] * 10 + [None]
+    st = L.flare_gdn_dual_bwd(ctypes.byref(v), ctypes.byref(shape), *args, FAKE, need - 1, None)
+    assert st == 5
+    mis = ctypes.c_void_p(FAKE.value + 4)
+    st = L.flare_gdn_dual_bwd(ctypes.byref(v), ctypes.byref(shape), *args, mis, need + 64, None)
+    assert st == 5
+
+
+def test_ckpt_slots_never_overlap(L):
+    rng = np.random.default_rng(0)
+    C = 32
+    for trial in range(20):
+        lens = rng.integers(0, 300, size=rng.integers(1, 12))
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        used = set()
+        for i, n in enumerate(lens):
+            for c in range((n + C - 1) // C):
+                s = L.flare_gdn_ckpt_slot(int(cu[i]), i, c, 1)
+                assert s == cu[i] // C + i + c
+                assert s not in used
+                used.add(s)
+        v = varlen(cu, [0] * len(lens))
+        shape = g.GDNShape(3, 16, 16, 4, g.F32, 0, 0.0)
+        nbytes = L.flare_gdn_dual_ckpt_size(ctypes.byref(v), ctypes.byref(shape), 1)
+        n_slots = nbytes // (3 * 16 * 16 * 4)
+        assert n_slots == cu[-1] // C + len(lens)
+        assert not used or max(used) < n_slots
+
+
+def test_block_step_validation(L):
+    shape = g.GDNShape(16, 128, 128, 4, g.BF16, 0, 0.0)
+    host = np.array([3, 1, 3], np.int32)
+    P = [FAKE] * 5
+    st = L.flare_gdn_block_step(3, FAKE, host.ctypes.data, FAKE, 8, ctypes.byref(shape), *P, FAKE, 0, None)
+    assert st == 2 and b"two requests" in L.flare_last_error()
+    host = np.array([3, 1, 9], np.int32)
+    st = L.flare_gdn_block_step(3, FAKE, host.ctypes.data, FAKE, 8, ctypes.byref(shape), *P, FAKE, 0, None)
+    assert st == 2
+    st = L.flare_gdn_block_step(3, FAKE, None, FAKE, 8, ctypes.byref(shape), *P, None, 0, None)
+    assert st == 1  # EVAL without an output
+    st = L.flare_gdn_block_step(3, FAKE, None, FAKE, 8, ctypes.byref(shape), *P, FAKE, 5, None)
+    assert st == 2  # unknown mode
+    st = L.flare_gdn_block_step(9, FAKE, None, FAKE, 8, ctypes.byref(shape), *P, FAKE, 0, None)
+    assert st == 2  # more requests than slots
+    assert L.flare_gdn_block_step(0, None, None, None, 0, ctypes.byref(shape), *([None] * 6), 0, None) == 0
+
+
+def test_shortconv_validation(L):
+    v = varlen([0, 16], [4])
+    P = [FAKE, FAKE, FAKE, None]
+    assert L.flare_shortconv_dual(ctypes.byref(v), 4, 12, 4, g.BF16, *P, 0, FAKE, FAKE, None) == 3
+    assert L.flare_shortconv_dual(ctypes.byref(v), 4, 16, 9, g.BF16, *P, 0, FAKE, FAKE, None) == 4
+    assert L.flare_shortconv_dual(ctypes.byref(v), 4, 16, 4, g.BF16, *P, 2, FAKE, FAKE, None) == 4
+    assert L.flare_shortconv_dual(ctypes.byref(varlen([0, 16], [6])), 4, 16, 4, g.BF16, *P, 0, FAKE,
+                                  FAKE, None) == 3
+    assert L.flare_shortconv_dual(ctypes.byref(v), 4, 16, 4, g.BF16, None, FAKE, FAKE, None, 0, FAKE,
+                                  FAKE, None) == 1
