@@ -99,14 +99,17 @@ class GDNInputs:
 
 def gdn_inputs(doc_lens, prompt_lens, H, dk, dv, block_size, seed, io="bf16",
                gates="smooth", normalize_qk=True, with_h0=False, with_grads=False,
-               noisy_equals_clean=False):
-    """Draw one packed batch: docs of the given lengths back to back."""
+               noisy_equals_clean=False, round_io=True):
+    """Draw one packed batch: docs of the given lengths back to back.  With
+    round_io=False the bf16 rounding is left to the caller (values are the
+    unrounded float32 draws; converting them to bf16 on the device with
+    round-to-nearest-even gives the same numbers as round_bf16)."""
     rng = np.random.default_rng(seed)
     doc_lens = np.asarray(doc_lens, dtype=np.int64)
     cu = np.zeros(len(doc_lens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(doc_lens)
     T = int(cu[-1])
-    rnd = round_bf16 if io == "bf16" else (lambda x: np.asarray(x, np.float32))
+    rnd = round_bf16 if (io == "bf16" and round_io) else (lambda x: np.asarray(x, np.float32))
 
     def qkv():
         q = rng.standard_normal((T, H, dk), dtype=np.float32)
@@ -150,11 +153,11 @@ def dual_bf16(block_size=4, seed=2, batch=4, seqlen=4096, prompt=1024, H=16, d=1
 
 
 def headline(seed=5, with_grads=True, batch=4, seqlen=8192, prompt=2048, H=16, d=128,
-             block_size=4):
+             block_size=4, round_io=True):
     """4 docs x 8192 tokens (prompt 2048), B=4, H=16, d=128, bf16 q/k/v,
     upstream output gradients ~ N(0,1)."""
     return gdn_inputs([seqlen] * batch, [prompt] * batch, H, d, d, block_size, seed,
-                      with_grads=with_grads)
+                      with_grads=with_grads, round_io=round_io)
 
 
 def packed_doc_lengths(total, n_docs, block, seed, min_len=64):
@@ -176,7 +179,7 @@ def packed_doc_lengths(total, n_docs, block, seed, min_len=64):
     return lens.astype(np.int32), prompts.astype(np.int32)
 
 
-def packed_conv(seed=3, total=32768, n_docs=8, H=32, d=128, block_size=4, width=4):
+def packed_conv(seed=3, total=32768, n_docs=8, H=32, d=128, block_size=4, width=4, round_io=True):
     """One packed row of `total` tokens, n_docs Dirichlet-split documents, ShortConv
     inputs over the q/k/v channels (3*H*d) for both streams, conv weights
     ~ U(-1/2, 1/2) [C, width], then GDN gates for both streams."""
@@ -184,8 +187,9 @@ def packed_conv(seed=3, total=32768, n_docs=8, H=32, d=128, block_size=4, width=
     rng = np.random.default_rng(seed + 1000)
     C = 3 * H * d
     T = int(lens.sum())
-    x = round_bf16(rng.standard_normal((T, C), dtype=np.float32))
-    xn = round_bf16(rng.standard_normal((T, C), dtype=np.float32))
+    rnd = round_bf16 if round_io else (lambda x: x)
+    x = rnd(rng.standard_normal((T, C), dtype=np.float32))
+    xn = rnd(rng.standard_normal((T, C), dtype=np.float32))
     w = rng.uniform(-0.5, 0.5, (C, width)).astype(np.float32)
     a, b = _gates_smooth(rng, (T, H))
     an, bn = _gates_smooth(rng, (T, H))
