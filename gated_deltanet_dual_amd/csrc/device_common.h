@@ -27,12 +27,17 @@ struct __align__(16) u16x8 { u16 v[8]; };
 // ---------------------------------------------------------------- bf16 bits
 __device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Round to nearest, ties to even (the IEEE default); NaN stays NaN.
-__device__ __forceinline__ u16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (u16)(u >> 16);
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Round to nearest, ties to even, on the gfx950 conversion unit
+// (v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ u16 f2bf(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+// Two values rounded by one instruction: lo in bits 0..15, hi in bits 16..31.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2v v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename IO> struct io_traits;
@@ -73,10 +78,9 @@ __device__ __forceinline__ bf16x8 frag_f32_hi(const float *base, int ld, int row
   const int l = lane_id();
   const float4 *p = reinterpret_cast<const float4 *>(base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
   const float4 x0 = p[0], x1 = p[1];
-  u16x8 h;
-  h.v[0] = f2bf(x0.x); h.v[1] = f2bf(x0.y); h.v[2] = f2bf(x0.z); h.v[3] = f2bf(x0.w);
-  h.v[4] = f2bf(x1.x); h.v[5] = f2bf(x1.y); h.v[6] = f2bf(x1.z); h.v[7] = f2bf(x1.w);
-  return as_bf16x8(h);
+  const uint4 h = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
+                             pack_bf16x2(x1.z, x1.w));
+  return __builtin_bit_cast(bf16x8, h);
 }
 
 // Row fragment of a row-major fp32 matrix split as hi + lo, both bf16, with
@@ -87,14 +91,16 @@ __device__ __forceinline__ void frag_f32_split(const float *base, int ld, int ro
   const float4 *p = reinterpret_cast<const float4 *>(base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
   const float4 x0 = p[0], x1 = p[1];
   const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  u16x8 h, o;
+  uint32_t h[4], o[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h.v[e] = f2bf(x[e]);
-    o.v[e] = f2bf(x[e] - bf2f(h.v[e]));
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    const float r0 = x[2 * e] - __uint_as_float(h[e] << 16);
+    const float r1 = x[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u);
+    o[e] = pack_bf16x2(r0, r1);
   }
-  hi = as_bf16x8(h);
-  lo = as_bf16x8(o);
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
 // Column-gather fragment: element (r, k) = base[(k0 + 8*(l>>4) + e) * ld + row0 + (l&15)],
@@ -116,6 +122,14 @@ __device__ __forceinline__ float frag1_f32(const float *base, int ld, int row0, 
 __device__ __forceinline__ float frag1_f32_T(const float *base, int ld, int row0, int k0) {
   const int l = lane_id();
   return base[(k0 + (l >> 4)) * ld + row0 + (l & 15)];
+}
+
+// Workgroup barrier for LDS traffic only: waits until this wave's LDS operations
+// have completed, then meets the other waves.  Unlike __syncthreads() it does
+// not wait for outstanding global loads, so a prefetch of the next tile stays in
+// flight across it.  Global memory written before it is NOT made visible.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Output element coordinates of accumulator register r for this lane.

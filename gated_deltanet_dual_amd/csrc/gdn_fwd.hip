@@ -17,7 +17,15 @@
 //   document's chunks of C = 32 tokens in order; the clean state tile
 //   (d_k x 32, fp32) lives in MFMA accumulator registers for the whole document.
 //   The next chunk's inputs are prefetched into registers while the current one
-//   is computed.  Per chunk, with G_i = exp(cumulative log a) inside the chunk:
+//   is computed.  The waves are specialised so that each dependency chain of a
+//   chunk stays inside one wave (LDS traffic of one wave is ordered, so it needs
+//   no barrier) and the chunk needs four workgroup barriers:
+//     wave 0: A Gram -> T solve ; K S_c -> rhs -> U, DU      (clean chain)
+//     wave 1: Mo Gram ; Q S_c (registers) -> o
+//     wave 2: Mq, M~ Grams ; q~ S_c (registers) -> r_q -> o~
+//     wave 3: Mk, A~ Grams -> T~ solve ; k~ S_c -> r_k -> rhs~ -> u~
+//   and every wave updates its quarter of the state with K^T DU.
+//   Per chunk, with G_i = exp(cumulative log a) inside the chunk:
 //     A   = strictly-lower((K K^T) o G_i/G_j) diag(b),  T = (I + A)^-1
 //     U   = T (V - diag(G) K S_c)                         (WY/UT form)
 //     o   = s (diag(G) Q S_c + tril((Q K^T) o G_i/G_j) diag(b) U)
@@ -48,6 +56,7 @@ template <typename IO, int D> struct FwdCfg {
   static constexpr int NT = 64 * NW;           // threads
   static constexpr int DV = D >= 32 ? 32 : D;  // d_v columns per workgroup
   static constexpr int NTILE = D / DV;
+  static constexpr int CT = DV / 16;           // 16-column tiles of d_v
   static constexpr int LDX = D + 8;            // q/k tile pitch (elements)
   static constexpr int LDM = C + 4;            // C x C and [DV][C] fp32 pitch
   static constexpr int LDV = DV + 4;           // value tile pitch (fp32)
@@ -57,8 +66,8 @@ template <typename IO, int D> struct FwdCfg {
   static constexpr int UX = 4 * PU / NT;       // q/k units per thread
   static constexpr int PV = C * DV * ES / 16;  // units per value tile
   static constexpr int RV = DV * ES / 16;      // units per value row
-  static constexpr int NST = (D / 16) * (DV / 16);        // 16x16 state tiles
-  static constexpr int SPW = (NST + NW - 1) / NW;         // state tiles per wave
+  static constexpr int NST = (D / 16) * CT;    // 16x16 state tiles
+  static constexpr int SPW = (NST + NW - 1) / NW;  // state tiles per wave
   static_assert(4 * PU % NT == 0, "q/k tile units must divide the threads");
   static_assert(2 * PV <= NT, "at most one value unit per thread");
 };
@@ -67,44 +76,72 @@ template <typename IO, int D> struct FwdSmem {
   using Cfg = FwdCfg<IO, D>;
   static constexpr int C = Cfg::C, DV = Cfg::DV, LDX = Cfg::LDX, LDM = Cfg::LDM, LDV = Cfg::LDV;
   using ST = typename std::conditional<Cfg::BF, u16, float>::type;  // S^T storage
-  alignas(16) IO x[4][C][LDX];           // 0 q, 1 k, 2 q~, 3 k~
-  alignas(16) ST st[DV][LDX];            // S_c^T (bf16 hi, or fp32)
-  alignas(16) float v[2][C][LDV];        // v, v~ tiles (fp32)
-  alignas(16) float cc[8][C][LDM];       // 0 A, 1 T, 2 Mo, 3 Mq, 4 Mk, 5 A~, 6 T~, 7 M~
-  alignas(16) float vt[7][DV][LDM];      // 0 rhs, 1 QS, 2 rq, 3 rk/rhs~, 4 U, 5 DU, 6 u~
-  alignas(16) float tmp[2][16][17];      // off-diagonal block solve scratch
-  alignas(16) IO out[2][C][DV];          // o, o~ staging
-  alignas(16) float rawg[4][C];          // a, b, a~, b~ of the chunk
-  alignas(16) float lg[C], beta[C], lgn[C], betan[C];
-  alignas(16) float nrm[4][C];  // 1/|x| per row (1 without the L2 flag)
+  alignas(16) IO x[4][C][LDX];      // 0 q, 1 k, 2 q~, 3 k~
+  alignas(16) ST st[DV][LDX];       // S_c^T (bf16 hi, or fp32)
+  alignas(16) float v[2][C][LDV];   // v, v~ tiles (fp32)
+  alignas(16) float cc[8][C][LDM];  // A^T, T, Mo, Mq, Mk, A~^T, T~, M~
+  alignas(16) float vt[5][DV][LDM]; // rhs^T, U^T, DU^T, rhs~^T, u~^T
+  alignas(16) float tmp[2][16][17]; // off-diagonal block solve scratch
+  alignas(16) IO out[2][C][DV];     // o, o~ staging
+  alignas(16) float lg[C];          // cumulative log a inside the chunk
+  alignas(16) float beta[C];
+  alignas(16) float lgn[C];         // cumulative log a~ inside each noisy block
+  alignas(16) float betan[C];
+  alignas(16) float nrm[4][C];      // 1/|x| per row (1 without the L2 flag)
 };
 
-enum { CC_A = 0, CC_T, CC_MO, CC_MQ, CC_MK, CC_AN, CC_TN, CC_MN };
-enum { VT_RHS = 0, VT_QS, VT_RQ, VT_RK, VT_U, VT_DU, VT_UN };
+enum { CC_AT = 0, CC_T, CC_MO, CC_MQ, CC_MK, CC_ANT, CC_TN, CC_MN };
+enum { VT_RHS = 0, VT_U, VT_DU, VT_RHSN, VT_UN };
 
 // ------------------------------------------------------------------ products
-// All compute acc[i][j] += sum_k A[ra + i][k] * Bt[rb + j][k] for one 16x16 tile.
-template <int K>
-__device__ __forceinline__ void mm_u16(floatx4 &acc, const u16 *A, int lda, int ra, const u16 *Bt,
-                                       int ldb, int rb) {
-  if constexpr (K % 32 == 0) {
+// Register-cached row fragments of a 32-row (or DV-row) LDS tile over a K-deep
+// contraction: f[h][ks] covers rows 16h..16h+15 and k-step ks.
+template <bool BF, int K, int NH> struct Frags {
+  static constexpr int KS = BF ? (K >= 32 ? K / 32 : 1) : K / 4;
+  using F = typename std::conditional<BF, bf16x8, float>::type;
+  F f[NH][KS];
+};
+
+template <bool BF, int K, int NH, typename T>
+__device__ __forceinline__ void load_frags(Frags<BF, K, NH> &fr, const T *base, int ld) {
+  using FR = Frags<BF, K, NH>;
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 32) mma_bf16(acc, frag_bf16(A, lda, ra, k0), frag_bf16(Bt, ldb, rb, k0));
-  } else {
-    static_assert(K == 16, "a contraction shorter than one MFMA step must be 16 deep");
-    // one 32-deep step whose upper half (lanes 32..63 carry k = 16..31) is zero
-    const bool live = lane_id() < 32;
-    const bf16x8 z = as_bf16x8(u16x8{});
-    mma_bf16(acc, live ? frag_bf16(A, lda, ra, 0) : z, live ? frag_bf16(Bt, ldb, rb, 0) : z);
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int ks = 0; ks < FR::KS; ++ks) {
+      if constexpr (BF) {
+        if constexpr (K >= 32) {
+          fr.f[h][ks] = frag_bf16(reinterpret_cast<const u16 *>(base), ld, 16 * h, 32 * ks);
+        } else {
+          // a 16-deep contraction: lanes 32..63 carry k = 16..31 and must be zero
+          const bf16x8 z = as_bf16x8(u16x8{});
+          fr.f[h][ks] = lane_id() < 32 ? frag_bf16(reinterpret_cast<const u16 *>(base), ld, 16 * h, 0) : z;
+        }
+      } else {
+        fr.f[h][ks] = frag1_f32(reinterpret_cast<const float *>(base), ld, 16 * h, 4 * ks);
+      }
+    }
+}
+
+// acc[i][j] += sum_k a[ha][i][k] * b[hb][j][k]
+template <bool BF, int K, int NA, int NB>
+__device__ __forceinline__ void mma_frags(floatx4 &acc, const Frags<BF, K, NA> &a, int ha,
+                                          const Frags<BF, K, NB> &b, int hb) {
+#pragma unroll
+  for (int ks = 0; ks < Frags<BF, K, NA>::KS; ++ks) {
+    if constexpr (BF) mma_bf16(acc, a.f[ha][ks], b.f[hb][ks]);
+    else mma_f32(acc, a.f[ha][ks], b.f[hb][ks]);
   }
 }
+
+// Products of two fp32 LDS matrices, acc[i][j] += sum_k A[ra+i][k] Bt[rb+j][k].
 template <int K>
 __device__ __forceinline__ void mm_f32(floatx4 &acc, const float *A, int lda, int ra, const float *Bt,
                                        int ldb, int rb) {
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += 4) mma_f32(acc, frag1_f32(A, lda, ra, k0), frag1_f32(Bt, ldb, rb, k0));
 }
-// A fp32 -> bf16 hi, Bt fp32 -> hi + lo   (2 MFMA per k-step)
+// A -> bf16 hi, Bt -> hi + lo   (2 MFMA per k-step)
 template <int K>
 __device__ __forceinline__ void mm_split2(floatx4 &acc, const float *A, int lda, int ra,
                                           const float *Bt, int ldb, int rb) {
@@ -117,7 +154,7 @@ __device__ __forceinline__ void mm_split2(floatx4 &acc, const float *A, int lda,
     mma_bf16(acc, a, bl);
   }
 }
-// A, Bt fp32 -> hi + lo each; hi*hi + hi*lo + lo*hi   (3 MFMA per k-step)
+// A, Bt -> hi + lo each; hi*hi + hi*lo + lo*hi   (3 MFMA per k-step)
 template <int K>
 __device__ __forceinline__ void mm_split3(floatx4 &acc, const float *A, int lda, int ra,
                                           const float *Bt, int ldb, int rb) {
@@ -131,8 +168,6 @@ __device__ __forceinline__ void mm_split3(floatx4 &acc, const float *A, int lda,
     mma_bf16(acc, al, bh);
   }
 }
-
-// dispatch on the io precision: "exact-ish" product of two fp32 LDS matrices
 template <bool BF, int K, int TERMS>
 __device__ __forceinline__ void mm_ff(floatx4 &acc, const float *A, int lda, int ra, const float *Bt,
                                       int ldb, int rb) {
@@ -146,15 +181,66 @@ __device__ __forceinline__ void mm_ff(floatx4 &acc, const float *A, int lda, int
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// T = (I + A)^-1 for a 32 x 32 unit-lower-triangular system given as A^T
+// (strictly lower A; A^T row j holds column j of A), written row-major to Tm.
+// One wave: lanes 0..31 solve the two diagonal 16 x 16 blocks, one column per
+// lane, by right-looking substitution kept in registers; the off-diagonal block
+// T_10 = -T_11 A_10 T_00 then runs on fp32 MFMA in the same wave (the wave's
+// LDS operations complete in order, so no barrier is needed).
+template <int LDM>
+__device__ __forceinline__ void solve_unit_lower(const float *At, float *Tm, float *tmp, bool offdiag) {
+  const int lane = lane_id();
+  if (lane < 32) {
+    const int r0 = 16 * (lane >> 4), cl = lane & 15;
+    // the whole 16 x 16 block of A^T is loaded first (independent of x), so
+    // the substitution below never waits on LDS
+    float at[16][16];
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v4 = *reinterpret_cast<const float4 *>(At + (r0 + ii) * LDM + r0 + 4 * q4);
+        at[ii][4 * q4] = v4.x; at[ii][4 * q4 + 1] = v4.y; at[ii][4 * q4 + 2] = v4.z; at[ii][4 * q4 + 3] = v4.w;
+      }
+    float x[16];
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) x[ii] = ii == cl ? 1.f : 0.f;
+#pragma unroll
+    for (int ii = 0; ii < 15; ++ii) {
+      const float xi = x[ii];
+#pragma unroll
+      for (int jj = ii + 1; jj < 16; ++jj) x[jj] -= at[ii][jj] * xi;  // at[ii][jj] = A[r0+jj][r0+ii]
+    }
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) Tm[(r0 + ii) * LDM + r0 + cl] = x[ii];
+  }
+  if (offdiag) {
+    floatx4 xa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 4)  // X = A_10 T_00, A_10[i][k] = A^T[k][16 + i]
+      mma_f32(xa, frag1_f32_T(At, LDM, 16, k0), frag1_f32_T(Tm, LDM, 0, k0));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tmp[acc_row(r) * 17 + acc_col()] = xa[r];
+    floatx4 ta = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 4)  // T_10 = -T_11 X
+      mma_f32(ta, frag1_f32(Tm + 16 * LDM + 16, LDM, 0, k0), frag1_f32_T(tmp, 17, 0, k0));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Tm[(16 + acc_row(r)) * LDM + acc_col()] = -ta[r];
+  }
+}
+
 template <typename IO, int D>
 __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
   using Cfg = FwdCfg<IO, D>;
   using Sm = FwdSmem<IO, D>;
   constexpr bool BF = Cfg::BF;
-  constexpr int C = Cfg::C, NW = Cfg::NW, NT = Cfg::NT, DV = Cfg::DV, NTILE = Cfg::NTILE;
-  constexpr int LDX = Cfg::LDX, LDM = Cfg::LDM, LDV = Cfg::LDV;
+  constexpr int C = Cfg::C, NT = Cfg::NT, DV = Cfg::DV, NTILE = Cfg::NTILE, CT = Cfg::CT;
+  constexpr int LDX = Cfg::LDX, LDM = Cfg::LDM;
   constexpr int SPW = Cfg::SPW, NST = Cfg::NST;
   using ST = typename Sm::ST;
+  using XF = Frags<BF, D, 2>;   // 32 rows of q/k/q~/k~ over d_k
+  using SF = Frags<BF, D, CT>;  // DV rows of S^T over d_k
 
   __shared__ Sm sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -176,23 +262,28 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
   const float scale = a.scale;
   const bool l2 = (a.flags & 1) != 0;
 
-  const IO *gx[4] = {reinterpret_cast<const IO *>(a.q), reinterpret_cast<const IO *>(a.k),
-                     reinterpret_cast<const IO *>(a.qn), reinterpret_cast<const IO *>(a.kn)};
-  const IO *gv[2] = {reinterpret_cast<const IO *>(a.v), reinterpret_cast<const IO *>(a.vn)};
-  const float *gg[4] = {a.alpha, a.beta, a.alpha_n, a.beta_n};
+  // Input pointers copied to (uniform) locals first: selecting among them per
+  // lane is then a register select, not a per-lane load from the argument block.
+  const IO *const pq = reinterpret_cast<const IO *>(a.q), *const pk = reinterpret_cast<const IO *>(a.k);
+  const IO *const pqn = reinterpret_cast<const IO *>(a.qn), *const pkn = reinterpret_cast<const IO *>(a.kn);
+  const IO *const pv = reinterpret_cast<const IO *>(a.v), *const pvn = reinterpret_cast<const IO *>(a.vn);
+  const float *const pa = a.alpha, *const pb = a.beta, *const pan = a.alpha_n, *const pbn = a.beta_n;
+  auto gx = [=](int m) { return m == 0 ? pq : m == 1 ? pk : m == 2 ? pqn : pkn; };
+  auto gv = [=](int m) { return m == 0 ? pv : pvn; };
+  auto gg = [=](int g) { return g == 0 ? pa : g == 1 ? pb : g == 2 ? pan : pbn; };
 
-  // ---- one-time LDS init: zero all C x C matrices (upper blocks stay zero)
+  // ---- one-time LDS init: zero all C x C matrices (blocks never written stay zero)
   for (int e = tid; e < 8 * C * LDM; e += NT) (&sm.cc[0][0][0])[e] = 0.f;
   for (int e = tid; e < 4 * C; e += NT) (&sm.nrm[0][0])[e] = 1.f;
 
-  // ---- state tiles owned by this wave: tile q -> rows 16*(q / (DV/16)), cols 16*(q % (DV/16))
+  // ---- state tiles owned by this wave: tile q -> rows 16*(q / CT), cols 16*(q % CT)
   floatx4 S[SPW];
 #pragma unroll
   for (int e = 0; e < SPW; ++e) {
     const int q = wave * SPW + e;
     S[e] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (q < NST && a.h0) {
-      const int rt = q / (DV / 16), ct = q % (DV / 16);
+      const int rt = q / CT, ct = q % CT;
       const float *src = a.h0 + ((size_t)doc * H + h) * D * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[e][r] = src[(size_t)(16 * rt + acc_row(r)) * D + dv0 + 16 * ct + acc_col()];
@@ -203,12 +294,12 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
     for (int e = 0; e < SPW; ++e) {
       const int q = wave * SPW + e;
       if (q < NST) {
-        const int rt = q / (DV / 16), ct = q % (DV / 16);
+        const int rt = q / CT, ct = q % CT;
         ST *dst = &sm.st[16 * ct + acc_col()][16 * rt + acc_row(0)];
         if constexpr (BF) {
           uint2 w;
-          w.x = (uint32_t)f2bf(S[e][0]) | ((uint32_t)f2bf(S[e][1]) << 16);
-          w.y = (uint32_t)f2bf(S[e][2]) | ((uint32_t)f2bf(S[e][3]) << 16);
+          w.x = pack_bf16x2(S[e][0], S[e][1]);
+          w.y = pack_bf16x2(S[e][2], S[e][3]);
           *reinterpret_cast<uint2 *>(dst) = w;
         } else {
           *reinterpret_cast<float4 *>(dst) = make_float4(S[e][0], S[e][1], S[e][2], S[e][3]);
@@ -221,7 +312,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
     for (int e = 0; e < SPW; ++e) {
       const int q = wave * SPW + e;
       if (q < NST) {
-        const int rt = q / (DV / 16), ct = q % (DV / 16);
+        const int rt = q / CT, ct = q % CT;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           dst_base[(size_t)(16 * rt + acc_row(r)) * D + dv0 + 16 * ct + acc_col()] = S[e][r];
@@ -246,7 +337,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
       if (m >= 2) ok = ok && tpos >= P;
       pfx[e] = make_uint4(0u, 0u, 0u, 0u);
       if (ok)
-        pfx[e] = *reinterpret_cast<const uint4 *>(gx[m] + ((t0g + tpos) * H + h) * D + cu16 * (16 / Cfg::ES));
+        pfx[e] = *reinterpret_cast<const uint4 *>(gx(m) + ((t0g + tpos) * H + h) * D + cu16 * (16 / Cfg::ES));
     }
     if (tid < 2 * Cfg::PV) {
       const int m = tid / Cfg::PV, r = tid % Cfg::PV;
@@ -256,18 +347,19 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
       if (m == 1) ok = ok && tpos >= P;
       pfv = make_uint4(0u, 0u, 0u, 0u);
       if (ok)
-        pfv = *reinterpret_cast<const uint4 *>(gv[m] + ((t0g + tpos) * H + h) * D + dv0 + cu16 * (16 / Cfg::ES));
+        pfv = *reinterpret_cast<const uint4 *>(gv(m) + ((t0g + tpos) * H + h) * D + dv0 + cu16 * (16 / Cfg::ES));
     }
     if (tid < 4 * C) {
       const int g = tid / C, i = tid % C;
       const int tpos = c0 + i;
       bool ok = tpos < n;
       if (g >= 2) ok = ok && tpos >= P;
-      const bool is_alpha = (g & 1) == 0;
-      pfg = is_alpha ? 1.f : 0.f;
-      if (ok) pfg = gg[g][(t0g + tpos) * H + h];
+      pfg = (g & 1) == 0 ? 1.f : 0.f;
+      if (ok) pfg = gg(g)[(t0g + tpos) * H + h];
     }
   };
+  // prefetch registers -> LDS; the gates are scanned straight from registers:
+  // wave 0 lanes 0..31 hold alpha, 32..63 beta; wave 1 the noisy pair.
   auto store_prefetch = [&]() {
 #pragma unroll
     for (int e = 0; e < Cfg::UX; ++e) {
@@ -275,6 +367,24 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
       const int m = u / Cfg::PU, r = u % Cfg::PU;
       const int row = r / Cfg::RU, cu16 = r % Cfg::RU;
       *reinterpret_cast<uint4 *>(&sm.x[m][row][cu16 * (16 / Cfg::ES)]) = pfx[e];
+      if (l2) {
+        // sum of squares of this 16-byte unit, reduced over the RU lanes of the row
+        const uint32_t w[4] = {pfx[e].x, pfx[e].y, pfx[e].z, pfx[e].w};
+        float ss = 0.f;
+        if constexpr (BF) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+            ss += lo * lo + hi * hi;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ss += __uint_as_float(w[i]) * __uint_as_float(w[i]);
+        }
+#pragma unroll
+        for (int off = 1; off < Cfg::RU; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        if (cu16 == 0) sm.nrm[m][row] = rsqrtf(ss + 1e-6f);
+      }
     }
     if (tid < 2 * Cfg::PV) {
       const int m = tid / Cfg::PV, r = tid % Cfg::PV;
@@ -292,257 +402,257 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
         dst[2] = __uint_as_float(pfv.z); dst[3] = __uint_as_float(pfv.w);
       }
     }
-    if (tid < 4 * C) sm.rawg[tid / C][tid % C] = pfg;
+    if (tid < 4 * C) {
+      const int g = tid / C, i = tid % C;
+      if (g == 0 || g == 2) {
+        float la = __logf(pfg);
+        if (g == 0) {
+#pragma unroll
+          for (int off = 1; off < C; off <<= 1) {
+            const float y = __shfl_up(la, off, C);
+            if (i >= off) la += y;
+          }
+          sm.lg[i] = la;
+        } else {
+          // segmented scan inside blocks of B tokens (blocks are B-aligned in the chunk)
+          for (int off = 1; off < B; off <<= 1) {
+            const float y = __shfl_up(la, off, B);
+            if ((i % B) >= off) la += y;
+          }
+          sm.lgn[i] = la;
+        }
+      } else {
+        (g == 1 ? sm.beta : sm.betan)[i] = pfg;
+      }
+    }
+  };
+  // staged o, o~ rows of chunk cprev -> global (16-byte stores)
+  auto store_outputs = [&](int cprev, bool noisy_prev) {
+    constexpr int UPR = DV * Cfg::ES / 16;  // 16-byte units per row
+    IO *go[2] = {reinterpret_cast<IO *>(a.o), reinterpret_cast<IO *>(a.on)};
+    for (int e = tid; e < 2 * C * UPR; e += NT) {
+      const int m = e / (C * UPR), rr = e % (C * UPR);
+      const int row = rr / UPR, cu16 = rr % UPR;
+      const int tpos = cprev * C + row;
+      if (tpos >= n) continue;
+      uint4 val = *reinterpret_cast<const uint4 *>(&sm.out[m][row][cu16 * (16 / Cfg::ES)]);
+      if (m == 1 && !noisy_prev) val = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(go[m] + ((t0g + tpos) * H + h) * D + dv0 + cu16 * (16 / Cfg::ES)) = val;
+    }
   };
 
   if (nchunks > 0) prefetch(0);
   const int64_t ck_base = a.ckpt ? (int64_t)(t0g / ((int64_t)C * a.ckpt_stride)) + doc : 0;
+  bool prev_noisy = false;
 
   for (int c = 0; c < nchunks; ++c) {
     const int c0 = c * C;
     const bool has_noisy = (c0 + C > P) && (P < n);
 
-    // ---------------------------------------------------------- [A] inputs
-    __syncthreads();
+    // ============================================================ [A] inputs
+    lds_barrier();                                       // B0
+    if (c > 0) store_outputs(c - 1, prev_noisy);
     store_prefetch();
     if (c + 1 < nchunks) prefetch(c + 1);
     if (a.ckpt && (c % a.ckpt_stride) == 0)
       write_state_global(a.ckpt + ((ck_base + c / a.ckpt_stride) * H + h) * (size_t)D * D);
-    __syncthreads();
+    lds_barrier();                                       // B1
 
-    // ---------------------------------------------------------- [B] gates, norms
+    // ============================================================ [P1] Grams, X S_c, solves
+    // Floating-point io helpers for the row-side factors used in the epilogues.
+    const int g4 = 4 * (lane >> 4);  // accumulator row offset of this lane
+    const int cl = lane & 15;        // accumulator column of this lane
+    floatx4 xs[2][CT];               // q S_c (wave 1), q~ S_c -> r_q (wave 2), k~ S_c -> r_k (wave 3)
     if (wave == 0) {
-      const int i = lane & 31;
-      const bool noisy = lane >= 32;
-      float la = __logf(sm.rawg[noisy ? 2 : 0][i]);
-      const float be = sm.rawg[noisy ? 3 : 1][i];
-      if (!noisy) {
+      XF kf;
+      SF sf;
+      load_frags(kf, &sm.x[1][0][0], LDX);
+      load_frags(sf, &sm.st[0][0], LDX);
+      // A^T: non-transposed Gram tiles G[i = 16ti + g4 + r][j = 16tj + cl] of K K^T
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) {
-          const float y = __shfl_up(la, off, 32);
-          if (i >= off) la += y;
-        }
-        sm.lg[i] = la;
-        sm.beta[i] = be;
-      } else {
-        // segmented scan inside blocks of B tokens (blocks are B-aligned in the chunk)
-        for (int off = 1; off < B; off <<= 1) {
-          const float y = __shfl_up(la, off, B);
-          if ((i % B) >= off) la += y;
-        }
-        sm.lgn[i] = la;
-        sm.betan[i] = be;
-      }
-    }
-    if (l2 && tid < 4 * C) {
-      const int m = tid / C, row = tid % C;
-      float ss = 0.f;
-      for (int e = 0; e < D; ++e) {
-        const float xv = io_traits<IO>::to_f(sm.x[m][row][e]);
-        ss += xv * xv;
-      }
-      sm.nrm[m][row] = rsqrtf(ss + 1e-6f);
-    }
-    __syncthreads();
-
-    // ---------------------------------------------------------- [C1] Gram matrices
-    {
-      // job list: (kind, ti, tj); kinds 0 A, 1 Mo, 2 Mq, 3 Mk use tiles (0,0),(1,0),(1,1);
-      // 4 A~ and 5 M~ use the diagonal tiles, plus (1,0) [and (0,1) for M~] when B > 16.
-      const int nclean = 6;
-      const int nnoisy = has_noisy ? (6 + (B > 16 ? 7 : 4)) : 0;
-      for (int job = wave; job < nclean + nnoisy; job += NW) {
-        int kind, tsub;
-        if (job < 6) { kind = job / 3; tsub = job % 3; }
-        else if (job < 12) { kind = 2 + (job - 6) / 3; tsub = (job - 6) % 3; }
-        else { const int jj = job - 12; const int na = B > 16 ? 3 : 2;
-               if (jj < na) { kind = 4; tsub = jj; } else { kind = 5; tsub = jj - na; } }
-        int ti, tj;
-        if (kind < 4) { ti = tsub == 0 ? 0 : 1; tj = tsub == 2 ? 1 : 0; }
-        else if (kind == 4) { ti = tsub == 0 ? 0 : (tsub == 1 ? 1 : 1); tj = tsub == 2 ? 0 : ti; }
-        else { const int na = B > 16 ? 4 : 2;
-               if (na == 2) { ti = tsub; tj = tsub; }
-               else { ti = tsub >> 1; tj = tsub & 1; } }
-        // X (rows i) and Y (rows j) for G[i][j] = x_i . y_j
-        const int xm = kind == 0 ? 1 : kind == 1 ? 0 : kind == 2 ? 2 : kind == 3 ? 3 : kind == 4 ? 3 : 2;
-        const int ym = kind <= 3 ? 1 : 3;
+      for (int t = 0; t < 3; ++t) {
+        const int ti = t == 0 ? 0 : 1, tj = t == 2 ? 1 : 0;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BF) mm_u16<D>(acc, &sm.x[ym][0][0], LDX, 16 * tj, &sm.x[xm][0][0], LDX, 16 * ti);
-        else mm_f32<D>(acc, &sm.x[ym][0][0], LDX, 16 * tj, &sm.x[xm][0][0], LDX, 16 * ti);
-        // acc[r] = G^T[j][i] with j = 16 tj + acc_row(r), i = 16 ti + acc_col()
-        const int i = 16 * ti + acc_col();
-        const int pi = i - (i % B);  // chunk-local start of i's block
-        const int tpos = c0 + i;
-        const bool resp = tpos < n && tpos >= P;
-        float outv[4];
+        mma_frags(acc, kf, ti, kf, tj);
+        const int j = 16 * tj + cl;
+        const float lgj = sm.lg[j], bj = sm.beta[j] * sm.nrm[1][j];
+        float o4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = 16 * tj + acc_row(r);
-          const float g = acc[r] * sm.nrm[xm][i] * sm.nrm[ym][j];
-          float val = 0.f;
-          if (kind == 0) {
-            if (j < i) val = g * fast_exp(sm.lg[i] - sm.lg[j]) * sm.beta[j];
-          } else if (kind == 1) {
-            if (j <= i) val = g * fast_exp(sm.lg[i] - sm.lg[j]) * sm.beta[j];
-          } else if (kind <= 3) {
-            if (resp && j < pi) val = g * fast_exp(sm.lg[pi - 1] - sm.lg[j]) * sm.beta[j];
-          } else if (kind == 4) {
-            if (resp && j < i && j >= pi) val = g * fast_exp(sm.lgn[i] - sm.lgn[j]) * sm.betan[j];
-          } else {
-            if (resp && j >= pi && j < pi + B) val = g * fast_exp(sm.lgn[pi + B - 1] - sm.lgn[j]) * sm.betan[j];
-          }
-          outv[r] = val;
+          const int i = 16 * ti + g4 + r;
+          o4[r] = j < i ? acc[r] * sm.nrm[1][i] * fast_exp(sm.lg[i] - lgj) * bj : 0.f;
         }
-        const int cc = kind == 0 ? CC_A : kind == 1 ? CC_MO : kind == 2 ? CC_MQ : kind == 3 ? CC_MK
-                     : kind == 4 ? CC_AN : CC_MN;
-        *reinterpret_cast<float4 *>(&sm.cc[cc][i][16 * tj + acc_row(0)]) =
-            make_float4(outv[0], outv[1], outv[2], outv[3]);
+        *reinterpret_cast<float4 *>(&sm.cc[CC_AT][j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
       }
-    }
-    __syncthreads();
-
-    // ---------------------------------------------------------- [C2] X S_c (waves 1..) | diagonal solves (wave 0)
-    if (wave == 0) {
-      // lanes: (matrix m = lane >> 5: 0 clean, 1 noisy), (block bb = (lane >> 4) & 1), column cl
-      const int m = lane >> 5, bb = (lane >> 4) & 1, cl = lane & 15;
-      if (m == 0 || has_noisy) {
-        const float(*Am)[LDM] = sm.cc[m ? CC_AN : CC_A];
-        float(*Tm)[LDM] = sm.cc[m ? CC_TN : CC_T];
-        const int r0 = 16 * bb;
-        for (int ii = 0; ii < 16; ++ii) {
-          float x = 0.f;
-          if (ii == cl) {
-            x = 1.f;
-          } else if (ii > cl) {
-            float acc0 = 0.f, acc1 = 0.f;
-            int mm = cl;
-            for (; mm + 1 < ii; mm += 2) {
-              acc0 += Am[r0 + ii][r0 + mm] * Tm[r0 + mm][r0 + cl];
-              acc1 += Am[r0 + ii][r0 + mm + 1] * Tm[r0 + mm + 1][r0 + cl];
-            }
-            if (mm < ii) acc0 += Am[r0 + ii][r0 + mm] * Tm[r0 + mm][r0 + cl];
-            x = -(acc0 + acc1);
-          }
-          Tm[r0 + ii][r0 + cl] = x;
-        }
-      }
-    } else {
-      constexpr int CT = DV / 16;             // column tiles
-      constexpr int JOBS_PER_X = 2 * CT;      // (C/16) row tiles x CT
-      const int nx = has_noisy ? 4 : 2;
-      for (int job = wave - 1; job < nx * JOBS_PER_X; job += NW - 1) {
-        const int xsel = job / JOBS_PER_X;    // 0 K, 1 Q, 2 K~, 3 Q~
-        const int jr = job % JOBS_PER_X;
-        const int tr = jr / CT, tc = jr % CT;
-        const int xm = xsel == 0 ? 1 : xsel == 1 ? 0 : xsel == 2 ? 3 : 2;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BF) mm_u16<D>(acc, &sm.x[xm][0][0], LDX, 16 * tr, &sm.st[0][0], LDX, 16 * tc);
-        else mm_f32<D>(acc, &sm.x[xm][0][0], LDX, 16 * tr, &sm.st[0][0], LDX, 16 * tc);
-        // acc[r] = (X S)[tok][dv], tok = 16 tr + acc_row(r), dv = 16 tc + acc_col()
-        const int dv = 16 * tc + acc_col();
-        const int tok0 = 16 * tr + acc_row(0);
-        float out4[4];
+      // rhs = V - diag(G) K S_c  ->  rhs^T
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = tok0 + r;
-          const float xs = acc[r] * sm.nrm[xm][tok];
-          if (xsel == 0) {
-            out4[r] = sm.v[0][tok][dv] - fast_exp(sm.lg[tok]) * xs;
-          } else if (xsel == 1) {
-            out4[r] = xs;
-          } else {
-            const int pt = tok - (tok % B);
-            out4[r] = (pt > 0 ? fast_exp(sm.lg[pt - 1]) : 1.f) * xs;
-          }
-        }
-        const int vt = xsel == 0 ? VT_RHS : xsel == 1 ? VT_QS : xsel == 2 ? VT_RK : VT_RQ;
-        *reinterpret_cast<float4 *>(&sm.vt[vt][dv][tok0]) = make_float4(out4[0], out4[1], out4[2], out4[3]);
-      }
-    }
-    __syncthreads();
-
-    // ---------------------------------------------------------- [D] off-diagonal block T_10 = -T_11 A_10 T_00
-    {
-      const int nm = (has_noisy && B > 16) ? 2 : 1;
-      for (int e = tid; e < nm * 256; e += NT) {
-        const int m = e >> 8, ii = (e >> 4) & 15, cl = e & 15;
-        const float(*Am)[LDM] = sm.cc[m ? CC_AN : CC_A];
-        const float(*Tm)[LDM] = sm.cc[m ? CC_TN : CC_T];
-        float acc = 0.f;
-        for (int mm = cl; mm < 16; ++mm) acc += Am[16 + ii][mm] * Tm[mm][cl];
-        sm.tmp[m][ii][cl] = acc;
-      }
-      __syncthreads();
-      for (int e = tid; e < nm * 256; e += NT) {
-        const int m = e >> 8, ii = (e >> 4) & 15, cl = e & 15;
-        float(*Tm)[LDM] = sm.cc[m ? CC_TN : CC_T];
-        float acc = 0.f;
-        for (int mm = 0; mm <= ii; ++mm) acc += Tm[16 + ii][16 + mm] * sm.tmp[m][mm][cl];
-        Tm[16 + ii][cl] = -acc;
-      }
-    }
-    __syncthreads();
-
-    // ---------------------------------------------------------- [E] U = T rhs, DU
-    {
-      constexpr int CT = DV / 16;
-      const float lgC = sm.lg[C - 1];
-      for (int job = wave; job < 2 * CT; job += NW) {
-        const int tr = job / CT, tc = job % CT;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        mm_ff<BF, C, 2>(acc, &sm.cc[CC_T][0][0], LDM, 16 * tr, &sm.vt[VT_RHS][0][0], LDM, 16 * tc);
-        const int dv = 16 * tc + acc_col();
-        const int i0 = 16 * tr + acc_row(0);
-        float du[4];
+      for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = i0 + r;
-          du[r] = acc[r] * sm.beta[i] * fast_exp(lgC - sm.lg[i]) * sm.nrm[1][i];
-        }
-        *reinterpret_cast<float4 *>(&sm.vt[VT_U][dv][i0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<float4 *>(&sm.vt[VT_DU][dv][i0]) = make_float4(du[0], du[1], du[2], du[3]);
-      }
-    }
-    __syncthreads();
-
-    // ---------------------------------------------------------- [F] outputs, noisy reads, state update
-    {
-      constexpr int CT = DV / 16;
-      const int njobs = 2 * CT * (has_noisy ? 3 : 1);
-      for (int job = wave; job < njobs; job += NW) {
-        const int kind = job / (2 * CT);  // 0 o, 1 r_q, 2 r_k
-        const int jr = job % (2 * CT);
-        const int tr = jr / CT, tc = jr % CT;
-        const int dv = 16 * tc + acc_col();
-        const int i0 = 16 * tr + acc_row(0);
-        const int src = kind == 0 ? VT_QS : kind == 1 ? VT_RQ : VT_RK;
-        const float4 init = *reinterpret_cast<const float4 *>(&sm.vt[src][dv][i0]);
-        floatx4 acc = {init.x, init.y, init.z, init.w};
-        if (kind == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] *= fast_exp(sm.lg[i0 + r]);
-        }
-        const int cc = kind == 0 ? CC_MO : kind == 1 ? CC_MQ : CC_MK;
-        mm_ff<BF, C, 3>(acc, &sm.cc[cc][0][0], LDM, 16 * tr, &sm.vt[VT_U][0][0], LDM, 16 * tc);
-        if (kind == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.out[0][i0 + r][dv] = io_traits<IO>::from_f(scale * acc[r]);
-        } else if (kind == 1) {
-          *reinterpret_cast<float4 *>(&sm.vt[VT_RQ][dv][i0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        } else {
+        for (int tc = 0; tc < CT; ++tc) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          mma_frags(acc, kf, tr, sf, tc);
+          const int dv = 16 * tc + cl;
           float o4[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = sm.v[1][i0 + r][dv] - fast_exp(sm.lgn[i0 + r]) * acc[r];
-          *reinterpret_cast<float4 *>(&sm.vt[VT_RK][dv][i0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * tr + g4 + r;
+            o4[r] = sm.v[0][tok][dv] - fast_exp(sm.lg[tok]) * sm.nrm[1][tok] * acc[r];
+          }
+          *reinterpret_cast<float4 *>(&sm.vt[VT_RHS][dv][16 * tr + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
         }
+      solve_unit_lower<LDM>(&sm.cc[CC_AT][0][0], &sm.cc[CC_T][0][0], &sm.tmp[0][0][0], true);
+      // U = T rhs ; DU = diag(b G_C / G) U (the K row norm folded in)
+      const float lgC = sm.lg[C - 1];
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int tc = 0; tc < CT; ++tc) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          mm_ff<BF, C, 2>(acc, &sm.cc[CC_T][0][0], LDM, 16 * tr, &sm.vt[VT_RHS][0][0], LDM, 16 * tc);
+          const int dv = 16 * tc + cl, i0 = 16 * tr + g4;
+          float du[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            du[r] = acc[r] * sm.beta[i0 + r] * fast_exp(lgC - sm.lg[i0 + r]) * sm.nrm[1][i0 + r];
+          *reinterpret_cast<float4 *>(&sm.vt[VT_U][dv][i0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          *reinterpret_cast<float4 *>(&sm.vt[VT_DU][dv][i0]) = make_float4(du[0], du[1], du[2], du[3]);
+        }
+    } else if (wave == 1) {
+      XF kf, qf;
+      SF sf;
+      load_frags(kf, &sm.x[1][0][0], LDX);
+      load_frags(qf, &sm.x[0][0][0], LDX);
+      load_frags(sf, &sm.st[0][0], LDX);
+      // Mo[i][j] = (q_i.k_j) G_i/G_j b_j, j <= i  (transposed Gram tiles: lane holds Mo[i][j0..j0+3])
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const int ti = t == 0 ? 0 : 1, tj = t == 2 ? 1 : 0;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma_frags(acc, kf, tj, qf, ti);
+        const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+        const float lgi = sm.lg[i], ni = sm.nrm[0][i];
+        float o4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + r;
+          o4[r] = j <= i ? acc[r] * ni * sm.nrm[1][j] * fast_exp(lgi - sm.lg[j]) * sm.beta[j] : 0.f;
+        }
+        *reinterpret_cast<float4 *>(&sm.cc[CC_MO][i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
       }
-      // state update on the wave's own tiles: S <- G_C S + K^T (DU)
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int tc = 0; tc < CT; ++tc) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          mma_frags(acc, qf, tr, sf, tc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * tr + g4 + r;
+            acc[r] *= sm.nrm[0][tok] * fast_exp(sm.lg[tok]);
+          }
+          xs[tr][tc] = acc;
+        }
+    } else if (has_noisy) {
+      // waves 2 (q~ side) and 3 (k~ side)
+      const bool qside = wave == 2;
+      const int xm = qside ? 2 : 3;
+      XF kf, xf, knf;
+      SF sf;
+      load_frags(kf, &sm.x[1][0][0], LDX);
+      load_frags(xf, &sm.x[xm][0][0], LDX);
+      load_frags(sf, &sm.st[0][0], LDX);
+      if (qside) load_frags(knf, &sm.x[3][0][0], LDX);
+      // Mq / Mk[i][j] = (x~_i.k_j) (G_p(i)/G_j) b_j for j < p(i), x~ in {q~, k~}
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const int ti = t == 0 ? 0 : 1, tj = t == 2 ? 1 : 0;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma_frags(acc, kf, tj, xf, ti);
+        const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+        const int pi = i - (i % B);
+        const bool resp = c0 + i < n && c0 + i >= P;
+        const float lgp = pi > 0 ? sm.lg[pi - 1] : 0.f;
+        const float ni = sm.nrm[xm][i];
+        float o4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + r;
+          o4[r] = (resp && j < pi) ? acc[r] * ni * sm.nrm[1][j] * fast_exp(lgp - sm.lg[j]) * sm.beta[j] : 0.f;
+        }
+        *reinterpret_cast<float4 *>(&sm.cc[qside ? CC_MQ : CC_MK][i][j0]) =
+            make_float4(o4[0], o4[1], o4[2], o4[3]);
+      }
+      if (qside) {
+        // M~[i][j] = (q~_i.k~_j) (G~_e/G~_j) b~_j for j in i's block (transposed Gram tiles)
+        const int nt = B > 16 ? 4 : 2;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {  // tiles (0,0), (1,1), then (0,1), (1,0) when B > 16
+          if (t >= nt) break;
+          const int ti = (t == 0 || t == 2) ? 0 : 1, tj = (t == 0 || t == 3) ? 0 : 1;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          mma_frags(acc, knf, tj, xf, ti);
+          const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+          const int pi = i - (i % B);
+          const bool resp = c0 + i < n && c0 + i >= P;
+          const float lge = sm.lgn[pi + B - 1], ni = sm.nrm[2][i];
+          float o4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            o4[r] = (resp && j >= pi && j < pi + B)
+                        ? acc[r] * ni * sm.nrm[3][j] * fast_exp(lge - sm.lgn[j]) * sm.betan[j] : 0.f;
+          }
+          *reinterpret_cast<float4 *>(&sm.cc[CC_MN][i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+        }
+      } else {
+        // A~^T: non-transposed Gram tiles of K~ K~^T inside blocks, then T~ = (I + A~)^-1
+        const int nt = B > 16 ? 3 : 2;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {  // tiles (0,0), (1,1), then (1,0) when B > 16
+          if (t >= nt) break;
+          const int ti = t == 0 ? 0 : 1, tj = t == 1 ? 1 : 0;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          mma_frags(acc, xf, ti, xf, tj);
+          const int j = 16 * tj + cl;
+          const int pj = j - (j % B);
+          const float lgj = sm.lgn[j], bj = sm.betan[j] * sm.nrm[3][j];
+          float o4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ti + g4 + r;
+            const bool resp = c0 + i < n && c0 + i >= P;
+            o4[r] = (resp && j < i && i - (i % B) == pj) ? acc[r] * sm.nrm[3][i] * fast_exp(sm.lgn[i] - lgj) * bj : 0.f;
+          }
+          *reinterpret_cast<float4 *>(&sm.cc[CC_ANT][j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+        }
+        solve_unit_lower<LDM>(&sm.cc[CC_ANT][0][0], &sm.cc[CC_TN][0][0], &sm.tmp[1][0][0], B > 16);
+      }
+      // x~ S_c, scaled by G_p: the S_c part of S_p^T x~
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int tc = 0; tc < CT; ++tc) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          mma_frags(acc, xf, tr, sf, tc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * tr + g4 + r;
+            const int pt = tok - (tok % B);
+            acc[r] *= sm.nrm[xm][tok] * (pt > 0 ? fast_exp(sm.lg[pt - 1]) : 1.f);
+          }
+          xs[tr][tc] = acc;
+        }
+    }
+    lds_barrier();                                       // B2
+
+    // ============================================================ [P2] state, o, r_q, r_k -> u~
+    {
       const float gC = fast_exp(sm.lg[C - 1]);
 #pragma unroll
       for (int e = 0; e < SPW; ++e) {
         const int q = wave * SPW + e;
         if (q < NST) {
-          const int rt = q / (DV / 16), ct = q % (DV / 16);
+          const int rt = q / CT, ct = q % CT;
 #pragma unroll
           for (int r = 0; r < 4; ++r) S[e][r] *= gC;
           if constexpr (BF) {
@@ -560,60 +670,82 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
       }
       write_state_t();
     }
-    __syncthreads();
-
-    if (has_noisy) {
-      // -------------------------------------------------------- [G] u~ = T~ rhs~
-      constexpr int CT = DV / 16;
-      for (int job = wave; job < 2 * CT; job += NW) {
-        const int tr = job / CT, tc = job % CT;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        mm_ff<BF, C, 2>(acc, &sm.cc[CC_TN][0][0], LDM, 16 * tr, &sm.vt[VT_RK][0][0], LDM, 16 * tc);
-        const int dv = 16 * tc + acc_col();
-        const int i0 = 16 * tr + acc_row(0);
-        *reinterpret_cast<float4 *>(&sm.vt[VT_UN][dv][i0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      }
-      __syncthreads();
-      // -------------------------------------------------------- [H] o~ = s (G~_e r_q + M~ u~)
-      for (int job = wave; job < 2 * CT; job += NW) {
-        const int tr = job / CT, tc = job % CT;
-        const int dv = 16 * tc + acc_col();
-        const int i0 = 16 * tr + acc_row(0);
-        const float4 init = *reinterpret_cast<const float4 *>(&sm.vt[VT_RQ][dv][i0]);
-        floatx4 acc = {init.x, init.y, init.z, init.w};
+    if (wave == 1) {
+      // o = s (G q S_c + Mo U)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = i0 + r;
-          const int pi = i - (i % B);
-          acc[r] *= fast_exp(sm.lgn[pi + B - 1]);
-        }
-        mm_ff<BF, C, 3>(acc, &sm.cc[CC_MN][0][0], LDM, 16 * tr, &sm.vt[VT_UN][0][0], LDM, 16 * tc);
+      for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tpos = c0 + i0 + r;
-          const bool resp = tpos < n && tpos >= P;
-          sm.out[1][i0 + r][dv] = io_traits<IO>::from_f(resp ? scale * acc[r] : 0.f);
+        for (int tc = 0; tc < CT; ++tc) {
+          floatx4 acc = xs[tr][tc];
+          mm_ff<BF, C, 3>(acc, &sm.cc[CC_MO][0][0], LDM, 16 * tr, &sm.vt[VT_U][0][0], LDM, 16 * tc);
+          const int dv = 16 * tc + cl;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.out[0][16 * tr + g4 + r][dv] = io_traits<IO>::from_f(scale * acc[r]);
         }
-      }
+    } else if (has_noisy && wave == 2) {
+      // r_q = S_p^T q~ = G_p q~ S_c + Mq U   (kept in registers for [P3])
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int tc = 0; tc < CT; ++tc)
+          mm_ff<BF, C, 3>(xs[tr][tc], &sm.cc[CC_MQ][0][0], LDM, 16 * tr, &sm.vt[VT_U][0][0], LDM, 16 * tc);
+    } else if (has_noisy && wave == 3) {
+      // r_k = S_p^T k~ ; rhs~ = v~ - diag(G~) r_k ; u~ = T~ rhs~
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int tc = 0; tc < CT; ++tc) {
+          floatx4 acc = xs[tr][tc];
+          mm_ff<BF, C, 3>(acc, &sm.cc[CC_MK][0][0], LDM, 16 * tr, &sm.vt[VT_U][0][0], LDM, 16 * tc);
+          const int dv = 16 * tc + cl;
+          float o4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * tr + g4 + r;
+            o4[r] = sm.v[1][tok][dv] - fast_exp(sm.lgn[tok]) * acc[r];
+          }
+          *reinterpret_cast<float4 *>(&sm.vt[VT_RHSN][dv][16 * tr + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+        }
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int tc = 0; tc < CT; ++tc) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          mm_ff<BF, C, 2>(acc, &sm.cc[CC_TN][0][0], LDM, 16 * tr, &sm.vt[VT_RHSN][0][0], LDM, 16 * tc);
+          *reinterpret_cast<float4 *>(&sm.vt[VT_UN][16 * tc + cl][16 * tr + g4]) =
+              make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
     }
-    __syncthreads();
+    lds_barrier();                                       // B3
 
-    // ---------------------------------------------------------- [I] write o, o~
-    {
-      constexpr int UPR = DV * Cfg::ES / 16;  // 16-byte units per row
-      IO *go[2] = {reinterpret_cast<IO *>(a.o), reinterpret_cast<IO *>(a.on)};
-      for (int e = tid; e < 2 * C * UPR; e += NT) {
-        const int m = e / (C * UPR), rr = e % (C * UPR);
-        const int row = rr / UPR, cu16 = rr % UPR;
-        const int tpos = c0 + row;
-        if (tpos >= n) continue;
-        uint4 val = *reinterpret_cast<const uint4 *>(&sm.out[m][row][cu16 * (16 / Cfg::ES)]);
-        if (m == 1 && !has_noisy) val = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4 *>(go[m] + ((t0g + tpos) * H + h) * D + dv0 + cu16 * (16 / Cfg::ES)) = val;
-      }
+    // ============================================================ [P3] o~ = s (G~_e r_q + M~ u~)
+    if (has_noisy && wave == 2) {
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int tc = 0; tc < CT; ++tc) {
+          floatx4 acc = xs[tr][tc];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * tr + g4 + r;
+            acc[r] *= fast_exp(sm.lgn[i - (i % B) + B - 1]);
+          }
+          mm_ff<BF, C, 3>(acc, &sm.cc[CC_MN][0][0], LDM, 16 * tr, &sm.vt[VT_UN][0][0], LDM, 16 * tc);
+          const int dv = 16 * tc + cl;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * tr + g4 + r;
+            const bool resp = c0 + i < n && c0 + i >= P;
+            sm.out[1][i][dv] = io_traits<IO>::from_f(resp ? scale * acc[r] : 0.f);
+          }
+        }
     }
+    prev_noisy = has_noisy;
   }
-
+  if (nchunks > 0) {
+    lds_barrier();
+    store_outputs(nchunks - 1, prev_noisy);
+  }
   if (a.h_final) write_state_global(a.h_final + ((size_t)doc * H + h) * D * D);
 }
 

@@ -38,7 +38,7 @@ template <> struct ConvVec<u16> {
     uint4 r;
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(f[2 * i]) | ((uint32_t)f2bf(f[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     r.x = w[0]; r.y = w[1]; r.z = w[2]; r.w = w[3];
     *reinterpret_cast<uint4 *>(p) = r;
   }
