@@ -192,21 +192,24 @@ __device__ __forceinline__ void solve_unit_lower(const float *At, float *Tm, flo
   const int lane = lane_id();
   if (lane < 32) {
     const int r0 = 16 * (lane >> 4), cl = lane & 15;
-    // the whole 16 x 16 block of A^T is loaded first (independent of x), so
-    // the substitution below never waits on LDS
+    // rows of A^T are fetched four substitution steps ahead (independent of
+    // x), so the substitution rarely waits on LDS; about five rows are live
     float at[16][16];
-#pragma unroll
-    for (int ii = 0; ii < 16; ++ii)
+    auto fetch_row = [&](int ii) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const float4 v4 = *reinterpret_cast<const float4 *>(At + (r0 + ii) * LDM + r0 + 4 * q4);
         at[ii][4 * q4] = v4.x; at[ii][4 * q4 + 1] = v4.y; at[ii][4 * q4 + 2] = v4.z; at[ii][4 * q4 + 3] = v4.w;
       }
+    };
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) fetch_row(ii);
     float x[16];
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) x[ii] = ii == cl ? 1.f : 0.f;
 #pragma unroll
     for (int ii = 0; ii < 15; ++ii) {
+      if (ii + 4 < 15) fetch_row(ii + 4);
       const float xi = x[ii];
 #pragma unroll
       for (int jj = ii + 1; jj < 16; ++jj) x[jj] -= at[ii][jj] * xi;  // at[ii][jj] = A[r0+jj][r0+ii]
