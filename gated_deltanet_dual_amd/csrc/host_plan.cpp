@@ -91,11 +91,9 @@ int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride) {
 }
 
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
-  // dq and dk (and their noisy twins) are reduced over the d_v tiles: one fp32
-  // partial per tile, [tiles, T, H, d_k] x 4 tensors, plus 256 bytes of slack.
-  const int tiles = s->d_v > 32 ? s->d_v / 32 : 1;
-  const size_t per = (size_t)vi.total_tokens * s->num_heads * s->d_k * sizeof(float);
-  return per * tiles * 4 + 256;
+  // the end-state adjoint of every chunk, fp32, in the checkpoint slot layout
+  // (stride 1), written by the reverse scan and read by the per-chunk pass
+  return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * s->d_k * s->d_v * sizeof(float) + 256;
 }
 
 flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
