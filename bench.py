@@ -18,6 +18,7 @@ Overall framework and Key designs items 2-4.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -35,14 +36,30 @@ METRIC = "dual-stream GDN tokens/s (H=16,d=128,B=4,L=8K) + % of MFMA/HBM rooflin
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
-# Algorithmic bytes per (token, head) of the forward at d = 128, bf16 io:
-# q, k, v read (3 x 256 B), alpha, beta (8 B), o written (256 B); the noisy
-# stream moves the same per response token.  Checkpoints are excluded.
+# Algorithmic bytes per (token, head) at d = 128, bf16 io, fp32 gates; every
+# input read once and every output written once; the noisy stream moves the
+# same per response token.
+#   forward : q, k, v (3 x 256) + alpha, beta (8) + o (256)             = 1032
+#   backward: q, k, v, do (4 x 256) + alpha, beta (8)
+#             + dq, dk, dv (3 x 256) + dalpha, dbeta (8)                = 1808
+# The chunk-start states the training forward saves (fp32 d x d per chunk
+# slot) are written once by the forward and read once by the backward.
 FWD_BYTES_PER_TH = 3 * 256 + 8 + 256
-# Algorithmic flops per (token, head), triangular halves only, chunk C:
-#   clean 6 d^2 + 5 C d + C^2/3 ;  noisy 4 d^2 + 4 C d + 8 B d
+BWD_BYTES_PER_TH = 4 * 256 + 8 + 3 * 256 + 8
+# the reverse scan needs q, k, do and the gates of both streams (not v)
+SCAN_BYTES_PER_TH = 3 * 256 + 8
+
+
 def fwd_flops_per_th(d, C, B, noisy):
+    """Triangular halves only, chunk C: clean 6d^2 + 5Cd + C^2/3, noisy
+    4d^2 + 4Cd + 8Bd."""
     return (4 * d * d + 4 * C * d + 8 * B * d) if noisy else (6 * d * d + 5 * C * d + C * C / 3)
+
+
+def bwd_flops_per_th(d, C, noisy):
+    """Contractions of the chunked backward, same rule: clean 16d^2 + 12Cd,
+    noisy 10d^2 + 8Cd."""
+    return (10 * d * d + 8 * C * d) if noisy else (16 * d * d + 12 * C * d)
 
 
 def log(*a):
@@ -56,14 +73,16 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
-    p.add_argument("--only", choices=["fwd", "step", "serve", "conv"], default=None)
+    p.add_argument("--only", choices=["step", "infer", "serve", "conv", "copy"], default=None,
+                   help="run one part only (copy: a plain 1 GiB device copy, the reference "
+                        "transfer for HBM byte counters)")
     p.add_argument("--json-out", default=None)
     return p.parse_args()
 
 
 class Timer:
-    """HIP-event timing of one kernel call on the current stream (the library
-    launches on the caller's current stream)."""
+    """HIP-event timing of one library call on torch's current stream, which
+    is the stream the binding passes to the library."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -88,18 +107,37 @@ class Timer:
         self.times = {}
 
 
-def traffic_for(kernel_file, kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, valid only if
-    the kernel source is unchanged since the counters were taken."""
+def traffic_for(kernel, workload):
+    """Calibrated HBM bytes per launch from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain
+    1 GiB copy), valid only while the kernel's sources are unchanged since the
+    counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(kernel, {})
-    src = os.path.join(ROOT, "gated_deltanet_dual_amd", "csrc", kernel_file)
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if rec.get("source_sha") != sha or rec.get("workload") != workload:
+    rec = json.load(open(path)).get(kernel)
+    if not rec or rec.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for f in rec["source_files"].split("+"):
+        src = os.path.join(ROOT, "gated_deltanet_dual_amd", "csrc", f)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if rec.get("source_sha") != h.hexdigest()[:16]:
         return None
     return rec.get("bytes_per_launch")
+
+
+def device_copy(torch, dev, args):
+    """A plain 1 GiB device-to-device copy: 1 GiB read + 1 GiB written per
+    launch, the calibration transfer for FETCH_SIZE / WRITE_SIZE."""
+    x = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(max(args.steps, 3)):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": x.numel() * 4, "launches": max(args.steps, 3)}), flush=True)
 
 
 def main():
@@ -115,6 +153,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.only == "copy":
+        device_copy(torch, dev, args)
+        return
     g.lib()
     timer = Timer(torch)
     bf = torch.bfloat16
@@ -133,57 +174,91 @@ def main():
              qn=up(inp.qn, True), kn=up(inp.kn, True), vn=up(inp.vn, True), an=up(inp.alpha_n),
              bn=up(inp.beta_n))
     args10 = [X[k] for k in ("q", "k", "v", "a", "b", "qn", "kn", "vn", "an", "bn")]
+    do, don = up(inp.do, True), up(inp.don, True)
     o = torch.empty((T, H, d), dtype=bf, device=dev)
     on = torch.empty_like(o)
-    hf = torch.empty((vl.num_docs, H, d, d), dtype=torch.float32, device=dev)
+    C = g.chunk_size()
+    n_slots = T // C + vl.num_docs
+    ckpt = torch.empty((n_slots, H, d, d), dtype=torch.float32, device=dev)
+    g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False)
+    ws = torch.empty((g.lib().flare_gdn_dual_workspace_size(vl.ref(), ctypes.byref(g._shape(H, d, B, g.BF16)), 1),),
+                     dtype=torch.uint8, device=dev)
+    grads = g.gdn_dual_bwd(vl, *args10, B, ckpt, do, don, workspace=ws)
     torch.cuda.synchronize()
     n_resp = int(sum(inp.cu_seqlens[i + 1] - inp.cu_seqlens[i] - inp.prompt_lens[i]
                      for i in range(vl.num_docs)))
-    C = g.chunk_size()
+    th_total, th_resp = T * H, n_resp * H
+    ckpt_bytes = n_slots * H * d * d * 4
 
     def step():
-        timer.run("gdn_dual_fwd", lambda: g.gdn_dual_fwd(vl, *args10, B, out=(o, on)))
+        g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False)
+        g.gdn_dual_bwd(vl, *args10, B, ckpt, do, don, out=grads, workspace=ws)
 
     result = {}
-    if args.only in (None, "fwd", "step"):
+    if args.only in (None, "step"):
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        timer.clear()
+        g.timing_reset()
+        g.timing_enable(True)
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            step()
+            timer.run("step", step)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms_step = 1e3 * wall / args.steps
-        fwd_ms = timer.avg_ms("gdn_dual_fwd")
-        th_total = T * H
-        th_resp = n_resp * H
-        alg_bytes = FWD_BYTES_PER_TH * (th_total + th_resp)
-        alg_flops = (fwd_flops_per_th(d, C, B, False) * th_total + fwd_flops_per_th(d, C, B, True) * th_resp)
-        gbs = alg_bytes / (fwd_ms * 1e-3) / 1e9
-        tflops = alg_flops / (fwd_ms * 1e-3) / 1e12
-        workload = "gdn_dual_fwd 4x8192 p2048 B4 H16 d128 bf16"
+        g.timing_enable(False)
+        ms_step = timer.avg_ms("step")
+        kern = {}
+        for name in ("gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel"):
+            ms, n = g.timing_avg_ms(name)
+            kern[name] = {"ms": ms, "launches": n}
+        g.timing_reset()
+        alg = {
+            "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
+            "gdn_bwd_scan_kernel": SCAN_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
+            "gdn_bwd_chunk_kernel": BWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
+        }
+        fwd_flops = fwd_flops_per_th(d, C, B, False) * th_total + fwd_flops_per_th(d, C, B, True) * th_resp
+        bwd_flops = bwd_flops_per_th(d, C, False) * th_total + bwd_flops_per_th(d, C, True) * th_resp
+        step_bytes = (FWD_BYTES_PER_TH + BWD_BYTES_PER_TH) * (th_total + th_resp) + 2 * ckpt_bytes
+        step_flops = fwd_flops + bwd_flops
+        t_roof = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+        dom = max(kern, key=lambda k: kern[k]["ms"] or 0.0)
+        kms = kern[dom]["ms"]
+        gbs = alg[dom] / (kms * 1e-3) / 1e9
+        workload = "fwd(ckpt)+bwd 4x8192 p2048 B4 H16 d128 bf16"
         result.update({
             "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic (seeded normal q/k/v, L2-normalised q/k, smooth gates)",
-            "config": {"workload": "dual-stream GDN layer forward, 4 docs x 8192 tokens, prompt 2048, "
-                                   "B=4, H=16, d_k=d_v=128, bf16 io, fp32 gates/state",
+            "data": "synthetic (seeded normal q/k/v, L2-normalised q/k, smooth gates, normal upstream grads)",
+            "config": {"workload": "dual-stream GDN layer forward (training, chunk-start states saved) + "
+                                   "backward, 4 docs x 8192 tokens, prompt 2048, B=4, H=16, d_k=d_v=128, "
+                                   "bf16 io, fp32 gates/state",
                        "global_batch": 4, "seq_len": 8192, "block_size": B, "heads": H, "head_dim": d,
-                       "parallelism": "single GPU", "step": "fwd"},
-            "roofline": {"kernel": "gdn_dual_fwd_kernel<bf16,128>", "bound": "hbm", "achieved": gbs,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": traffic_for("gdn_fwd.hip", "gdn_dual_fwd_kernel", workload),
-                         "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
-                         "kernel_ms": fwd_ms, "mfma_alg_tflops": tflops,
-                         "mfma_alg_frac": tflops / MFMA_BF16_PEAK_TFLOPS},
+                       "parallelism": "single GPU", "step": "fwd+bwd"},
+            "roofline": {"kernel": dom, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": traffic_for(dom, workload),
+                         "alg_bytes_per_launch": alg[dom], "kernel_ms": kms},
+            "kernels": {k: dict(v, alg_bytes=alg[k],
+                                alg_gbs=(alg[k] / (v["ms"] * 1e-3) / 1e9) if v["ms"] else None)
+                        for k, v in kern.items()},
+            "step_roofline": {"alg_bytes": step_bytes, "alg_flops": step_flops, "t_roof_ms": 1e3 * t_roof,
+                              "frac": 1e3 * t_roof / ms_step,
+                              "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "mfma_alg_frac": step_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                              "wall_ms_per_step": 1e3 * wall / args.steps},
         })
-        log("bench: fwd %.3f ms/launch, %.1f GB/s alg (%.1f%% of HBM), %.1f TFLOP/s alg"
-            % (fwd_ms, gbs, 100 * gbs / HBM_PEAK_GBS, tflops))
+        log("bench: step %.3f ms (%s), roofline frac %.3f"
+            % (ms_step, ", ".join("%s %.3f ms" % (k, v["ms"] or -1) for k, v in kern.items()),
+               1e3 * t_roof / ms_step))
 
     comps = {}
+    if not args.no_components and args.only in (None, "infer"):
+        comps["fwd_inference"] = bench_infer(torch, g, vl, args10, B, o, on, timer, args,
+                                             th_total, th_resp, fwd_flops_per_th(d, C, B, False) * th_total
+                                             + fwd_flops_per_th(d, C, B, True) * th_resp)
     if not args.no_components and args.only in (None, "serve"):
         comps["serving"] = bench_serving(torch, g, wl, dev, timer, up, args)
     if not args.no_components and args.only in (None, "conv"):
@@ -199,6 +274,24 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(line + "\n")
+
+
+def bench_infer(torch, g, vl, args10, B, o, on, timer, args, th_total, th_resp, flops):
+    """The forward alone, inference mode (nothing saved)."""
+    log("bench: forward, inference mode")
+    for _ in range(args.warmup):
+        g.gdn_dual_fwd(vl, *args10, B, out=(o, on), want_h_final=False)
+    torch.cuda.synchronize()
+    timer.clear()
+    for _ in range(args.steps):
+        timer.run("infer", lambda: g.gdn_dual_fwd(vl, *args10, B, out=(o, on), want_h_final=False))
+    torch.cuda.synchronize()
+    ms = timer.avg_ms("infer")
+    alg = FWD_BYTES_PER_TH * (th_total + th_resp)
+    return {"workload": "dual-stream GDN forward, inference, 4 x 8192 tokens, B=4, H=16, d=128, bf16",
+            "ms": ms, "tokens_per_s": vl.total_tokens / (ms * 1e-3), "alg_bytes": alg, "alg_flops": flops,
+            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_alg_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
 def bench_serving(torch, g, wl, dev, timer, up, args):
@@ -268,32 +361,39 @@ def bench_conv(torch, g, wl, dev, timer, up, args):
 
 
 def cpu_baseline(inp):
-    """The fp64 oracle, as is, on a bounded sample of the same workload: all
-    4 documents at full length for 4 of the 16 heads (scaled to the full head
-    count in the reported rate)."""
+    """The fp64 oracle, as is, on the same step: forward then backward of the
+    whole headline batch (4 documents x 8192 tokens, all 16 heads), on the
+    bf16-rounded values the GPU sees, threads over (document, head)."""
     import oracle
-    heads = [0, 1, 2, 3]
-    sub = {name: np.ascontiguousarray(getattr(inp, name)[:, heads])
-           for name in ("q", "k", "v", "alpha", "beta", "qn", "kn", "vn", "alpha_n", "beta_n")}
+    from gated_deltanet_dual_amd.workloads import round_bf16
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
     threads = min(cores, 16)
-    # bf16 values as the GPU sees them
-    from gated_deltanet_dual_amd.workloads import round_bf16
-    for name in ("q", "k", "v", "qn", "kn", "vn"):
-        sub[name] = round_bf16(sub[name])
+    x = {n: getattr(inp, n) for n in ("q", "k", "v", "alpha", "beta", "qn", "kn", "vn", "alpha_n", "beta_n",
+                                      "do", "don")}
+    for n in ("q", "k", "v", "qn", "kn", "vn", "do", "don"):
+        x[n] = round_bf16(x[n])
+    clean = [x[n] for n in ("q", "k", "v", "alpha", "beta")]
+    noisy = [x[n] for n in ("qn", "kn", "vn", "alpha_n", "beta_n")]
     t0 = time.perf_counter()
-    oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, sub["q"], sub["k"], sub["v"], sub["alpha"],
-                        sub["beta"], sub["qn"], sub["kn"], sub["vn"], sub["alpha_n"], sub["beta_n"],
-                        inp.block_size, threads=threads)
-    dt = time.perf_counter() - t0
-    T = inp.T
-    frac = len(heads) / inp.H
-    return {"value": T * frac / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "fwd, all 4 docs x 8192 tokens, heads 0-3 of 16 (rate scaled to 16 heads); "
-                      "%.1f s on %d threads (%s)" % (dt, threads, platform.processor() or platform.machine())}
+    oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, *clean, *noisy, inp.block_size, threads=threads)
+    t1 = time.perf_counter()
+    oracle.gdn_dual_bwd(inp.cu_seqlens, inp.prompt_lens, *clean, *noisy, inp.block_size, x["do"], x["don"],
+                        threads=threads)
+    t2 = time.perf_counter()
+    cpu = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": inp.T / (t2 - t0), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole step: fp64 forward (%.1f s) + backward (%.1f s) of 4 docs x 8192 tokens, "
+                      "16 heads, %d threads on %s" % (t1 - t0, t2 - t1, threads, cpu)}
 
 
 if __name__ == "__main__":

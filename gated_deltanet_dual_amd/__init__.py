@@ -83,6 +83,12 @@ def lib():
     L.flare_gdn_block_step.restype = ctypes.c_int
     L.flare_shortconv_dual.argtypes = [VP, I32, I32, I32, I32, P, P, P, P, I32, P, P, P]
     L.flare_shortconv_dual.restype = ctypes.c_int
+    L.flare_timing_enable.argtypes = [I32]
+    L.flare_timing_enable.restype = I32
+    L.flare_timing_avg_ms.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64)]
+    L.flare_timing_avg_ms.restype = ctypes.c_double
+    L.flare_timing_reset.argtypes = []
+    L.flare_timing_reset.restype = None
     _lib = L
     return L
 
@@ -164,9 +170,11 @@ def ckpt_slots(varlen: Varlen, H: int, d: int, B: int, io: int, stride: int = 1)
 
 
 def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,
-                 h0=None, scale=0.0, flags=0, want_h_final=True, want_ckpt=False, out=None):
+                 h0=None, scale=0.0, flags=0, want_h_final=True, want_ckpt=False, out=None, ckpt=None):
     """Dual-stream forward.  q,k,qn,kn [T,H,d]; v,vn [T,H,d]; gates [T,H] fp32;
-    h0 [N,H,d,d] fp32 or None.  Returns (o, on, h_final, ckpt)."""
+    h0 [N,H,d,d] fp32 or None.  `out` = (o, on) reuses output buffers, `ckpt`
+    a buffer for the chunk-start states (implies saving them).  Returns
+    (o, on, h_final, ckpt)."""
     torch = _torch()
     T, H, d = q.shape
     io = _io_of(q)
@@ -177,8 +185,8 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
     else:
         o, on = out
     hf = torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=q.device) if want_h_final else None
-    ck = None
-    if want_ckpt:
+    ck = ckpt
+    if ck is None and want_ckpt:
         nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1)
         if nbytes == 0:
             raise FlareError(2, "invalid arguments for the checkpoint size")
@@ -192,8 +200,10 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
 
 def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,
                  ckpt, d_o, d_on, h0=None, dh_final=None, scale=0.0, flags=0, want_dh0=True,
-                 workspace=None):
-    """Reverse mode.  Returns a dict of gradients (same names as the oracle)."""
+                 workspace=None, out=None):
+    """Reverse mode.  Returns a dict of gradients (same names as the oracle);
+    `out` = such a dict reuses its buffers, `workspace` a uint8 device buffer of
+    at least flare_gdn_dual_workspace_size() bytes."""
     torch = _torch()
     T, H, d = q.shape
     io = _io_of(q)
@@ -202,7 +212,7 @@ def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
     ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 1)
     if workspace is None:
         workspace = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
-    g = {
+    g = out if out is not None else {
         "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
         "dalpha": torch.empty_like(alpha), "dbeta": torch.empty_like(beta),
         "dqn": torch.empty_like(qn), "dkn": torch.empty_like(kn), "dvn": torch.empty_like(vn),
@@ -253,3 +263,21 @@ def shortconv_dual(varlen: Varlen, block_size, x, xn, weight, bias=None, activat
                                       _ptr(weight), _ptr(bias), int(activation), _ptr(y), _ptr(yn),
                                       _stream(x.device)))
     return y, yn
+
+
+def timing_enable(on: bool = True) -> bool:
+    """Bracket every kernel launch of the library with HIP events on its
+    stream (flare_timing_enable); returns the previous state."""
+    return bool(lib().flare_timing_enable(1 if on else 0))
+
+
+def timing_avg_ms(kernel: str):
+    """(mean duration in ms, launches) of the recorded launches of `kernel`
+    (flare_timing_avg_ms); waits for them to finish."""
+    n = ctypes.c_int64(0)
+    ms = lib().flare_timing_avg_ms(kernel.encode(), ctypes.byref(n))
+    return (ms if n.value > 0 else None), n.value
+
+
+def timing_reset() -> None:
+    lib().flare_timing_reset()

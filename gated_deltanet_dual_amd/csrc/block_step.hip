@@ -21,6 +21,7 @@
 // below the MI355X fp32 ridge, so the kernel is bound by HBM bandwidth.
 #include "device_common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace flare {
 
@@ -210,6 +211,7 @@ template <typename IO, int D>
 static hipError_t launch_step_d(const BlockStepArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)(a.num_req * a.H));
   const dim3 block(StepCfg<D>::NT);
+  TimedLaunch tl(K_BLOCK_STEP, st);
   if (a.B <= 4)
     hipLaunchKernelGGL((block_step_kernel<IO, D, 4>), grid, block, 0, st, a);
   else if (a.B <= 8)

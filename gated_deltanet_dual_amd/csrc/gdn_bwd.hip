@@ -39,6 +39,7 @@
 #include "gemm_lds.h"
 #include "host_plan.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace flare {
 
@@ -1001,12 +1002,18 @@ static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   const FwdArgs &f = a.f;
   const int pairs = f.num_docs * f.H;
   const int groups = (pairs + 7) / 8;
-  hipLaunchKernelGGL((gdn_bwd_scan_kernel<IO, D>), dim3((unsigned)(groups * 8 * Cfg::NTILE)), dim3(256), 0, st, a);
+  {
+    TimedLaunch tl(K_BWD_SCAN, st);
+    hipLaunchKernelGGL((gdn_bwd_scan_kernel<IO, D>), dim3((unsigned)(groups * 8 * Cfg::NTILE)), dim3(256), 0,
+                       st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t slots = a.T / Cfg::C + f.num_docs;
-  if (slots > 0)
+  if (slots > 0) {
+    TimedLaunch tl(K_BWD_CHUNK, st);
     hipLaunchKernelGGL((gdn_bwd_chunk_kernel<IO, D>), dim3((unsigned)(slots * f.H)), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

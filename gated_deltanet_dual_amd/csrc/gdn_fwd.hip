@@ -47,6 +47,7 @@
 #include "chunk_common.h"
 #include "device_common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace flare {
 
@@ -707,6 +708,7 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
   const int pairs = a.num_docs * a.H;
   const int groups = (pairs + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * Cfg::NTILE));
+  TimedLaunch tl(K_FWD, st);
   hipLaunchKernelGGL((gdn_dual_fwd_kernel<IO, D>), grid, dim3(Cfg::NT), 0, st, a);
   return hipGetLastError();
 }

@@ -15,6 +15,7 @@
 // kernel is a pure streaming kernel: bound by HBM bandwidth.
 #include "device_common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace flare {
 
@@ -171,6 +172,7 @@ hipError_t launch_shortconv(const ShortConvArgs &a, hipStream_t st) {
   const int64_t vecs = a.C / N;
   const dim3 grid((unsigned)((vecs + kConvThreads - 1) / kConvThreads),
                   (unsigned)((a.T + kConvRun - 1) / kConvRun));
+  TimedLaunch tl(K_SHORTCONV, st);
   if (a.bf16)
     hipLaunchKernelGGL(shortconv_dual_kernel<u16>, grid, dim3(kConvThreads), 0, st, a);
   else

@@ -208,6 +208,23 @@ const char *flare_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t flare_version(void);
 
+/* ---- per-launch timing (measurement aid; no passage of the method) -------
+ * While enabled, every kernel launch made by the entry points above is
+ * bracketed by two HIP events recorded on the launch's own stream, so the
+ * duration of each kernel is known even when one entry point launches several
+ * (the backward launches the reverse scan, then the per-chunk kernel).
+ * Kernel names: "gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel",
+ * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel".
+ * flare_timing_enable(1) turns it on (events are created lazily, host side
+ * only; no device memory is allocated), (0) off.  Returns the previous state.
+ * flare_timing_avg_ms() blocks until the recorded launches of that kernel
+ * have finished and returns their mean duration in ms (-1 if none), writing
+ * the launch count to *launches when non-NULL.  flare_timing_reset() drops
+ * every record.  Process-wide, guarded by a mutex. */
+int32_t flare_timing_enable(int32_t on);
+double flare_timing_avg_ms(const char *kernel, int64_t *launches);
+void flare_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif
