@@ -98,3 +98,14 @@ def test_bwd_headline_full_size_sampled_heads(g, dev):
     want = ref_bwd(sub)
     got = {k: (v[:, heads] if k != "dh0" else v[:, heads]) for k, v in gr.items()}
     check(sub, got, want, TOL_BF16, "bwd_headline")
+
+
+def test_bwd_packed_full_size_sampled_heads(g, dev):
+    """One packed row of 32768 tokens, 8 Dirichlet-length documents, 32 heads,
+    d=128, bf16 (q/k pre-normalised); the oracle checks heads 7 and 24."""
+    lens, prompts = wl.packed_doc_lengths(32768, 8, 4, seed=3)
+    inp = wl.gdn_inputs(lens, prompts, 32, 128, 128, 4, seed=13, with_grads=True)
+    gr = run_bwd(g, inp, dev)
+    heads = [7, 24]
+    sub = sub_heads(inp, heads)
+    check(sub, {k: v[:, heads] for k, v in gr.items()}, ref_bwd(sub), TOL_BF16, "bwd_packed")

@@ -163,3 +163,26 @@ def test_headline_full_size_sampled_heads(g, dev):
     want = ref(sub)
     got = (o[:, heads], on[:, heads], hf[:, heads])
     check(sub, got, want, TOL_BF16, "headline")
+
+
+@pytest.mark.parametrize("B", [4, 8, 16, 32])
+def test_dual_bf16_full_size_block_sweep(g, dev, B):
+    """4 docs x 4096 tokens (prompt 1024), 16 heads, d=128, bf16, block sizes
+    4..32 at full size; the oracle checks two heads at full length."""
+    inp = wl.dual_bf16(block_size=B)
+    o, on, hf, _ = run(g, inp, dev)
+    heads = [B % 16, 15 - B % 16]
+    sub = sub_heads(inp, heads)
+    check(sub, (o[:, heads], on[:, heads], hf[:, heads]), ref(sub), TOL_BF16, "dual_bf16_B%d" % B)
+
+
+def test_packed_l2norm_full_size(g, dev):
+    """One packed row of 32768 tokens holding 8 Dirichlet-length documents
+    (prompt fraction U[0.1,0.5]), 32 heads, d=128, bf16, q/k normalised by the
+    forward's L2 flag; the oracle checks heads 5 and 30."""
+    lens, prompts = wl.packed_doc_lengths(32768, 8, 4, seed=3)
+    inp = wl.gdn_inputs(lens, prompts, 32, 128, 128, 4, seed=3, normalize_qk=False)
+    o, on, hf, _ = run(g, inp, dev, flags=g.QK_L2NORM)
+    heads = [5, 30]
+    sub = sub_heads(inp, heads)
+    check(sub, (o[:, heads], on[:, heads], hf[:, heads]), ref(sub, flags=oracle.FLAG_QK_L2NORM), TOL_BF16, "packed_l2")
