@@ -1,0 +1,155 @@
+// bwd_common.h -- pieces shared by the two per-chunk backward kernels: the
+// per-chunk gate load / scan and the masked Gram matrices of a chunk.
+#pragma once
+
+#include "device_common.h"
+#include "gemm_lds.h"
+#include "kernels.h"
+
+namespace flare {
+
+enum { CC_AT = 0, CC_T, CC_MO, CC_MQ, CC_MK, CC_ANT, CC_TN, CC_MN };
+
+// Per-chunk gates: lg = cumulative log a, lgn = cumulative log a~ inside each
+// noisy block (padded tokens: a = 1, b = 0; noisy prompt tokens likewise).
+__device__ __forceinline__ void load_gates(const FwdArgs &f, int64_t t0g, int c0, int n, int P, int h, int B,
+                                           float *lg, float *beta, float *lgn, float *betan) {
+  const int tid = threadIdx.x;
+  if (tid < 128) {
+    const int g = tid / 32, i = tid % 32;
+    const int tpos = c0 + i;
+    bool ok = tpos < n;
+    if (g >= 2) ok = ok && tpos >= P;
+    const float *src = g == 0 ? f.alpha : g == 1 ? f.beta : g == 2 ? f.alpha_n : f.beta_n;
+    float val = (g & 1) == 0 ? 1.f : 0.f;
+    if (ok) val = src[(t0g + tpos) * f.H + h];
+    if (g == 0 || g == 2) {
+      float la = __logf(val);
+      if (g == 0) {
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
+          const float y = __shfl_up(la, off, 32);
+          if (i >= off) la += y;
+        }
+        lg[i] = la;
+      } else {
+        for (int off = 1; off < B; off <<= 1) {
+          const float y = __shfl_up(la, off, B);
+          if ((i % B) >= off) la += y;
+        }
+        lgn[i] = la;
+      }
+    } else {
+      (g == 1 ? beta : betan)[i] = val;
+    }
+  }
+}
+
+// Gram tiles of one chunk (norm factors 1).  With fold_w the write strengths
+// (b, b~) are multiplied in (pass 1); otherwise they are left out (pass 2,
+// which needs the unweighted products for the gate gradients).  A and A~ are
+// stored transposed (row j = column j of A) for the solve.
+//   wave 0: A^T        wave 1: Mo        wave 2: Mq, M~        wave 3: Mk, A~^T
+template <bool BF, int D, int LDX, int LDM, typename IO>
+__device__ __forceinline__ void chunk_grams(IO (*x)[32][LDX], float (*cc)[32][LDM], const float *lg,
+                                            const float *beta, const float *lgn, const float *betan, int c0,
+                                            int n, int P, int B, bool has_noisy, bool fold_w) {
+  constexpr int XL = BF ? RowU16 : RowF32;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int g4 = 4 * (lane >> 4), cl = lane & 15;
+  if (wave == 0) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {  // non-transposed tiles: acc[r] = G[16ti + g4 + r][16tj + cl]
+      const int ti = t == 0 ? 0 : 1, tj = t == 2 ? 1 : 0;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      gemm_tile<BF, D, XL, XL>(acc, &x[1][0][0], LDX, 16 * ti, &x[1][0][0], LDX, 16 * tj);
+      const int j = 16 * tj + cl;
+      const float wj = fold_w ? beta[j] : 1.f;
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + g4 + r;
+        o4[r] = j < i ? acc[r] * __expf(lg[i] - lg[j]) * wj : 0.f;
+      }
+      *reinterpret_cast<float4 *>(&cc[CC_AT][j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    }
+  } else if (wave == 1) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {  // transposed tiles: lane holds Mo[i][j0..j0+3]
+      const int ti = t == 0 ? 0 : 1, tj = t == 2 ? 1 : 0;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      gemm_tile<BF, D, XL, XL>(acc, &x[1][0][0], LDX, 16 * tj, &x[0][0][0], LDX, 16 * ti);
+      const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r;
+        o4[r] = j <= i ? acc[r] * __expf(lg[i] - lg[j]) * (fold_w ? beta[j] : 1.f) : 0.f;
+      }
+      *reinterpret_cast<float4 *>(&cc[CC_MO][i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    }
+  } else if (has_noisy) {
+    const bool qside = wave == 2;
+    const int xm = qside ? 2 : 3;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int ti = t == 0 ? 0 : 1, tj = t == 2 ? 1 : 0;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      gemm_tile<BF, D, XL, XL>(acc, &x[1][0][0], LDX, 16 * tj, &x[xm][0][0], LDX, 16 * ti);
+      const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+      const int pi = i - (i % B);
+      const bool resp = c0 + i < n && c0 + i >= P;
+      const float lgp = pi > 0 ? lg[pi - 1] : 0.f;
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r;
+        o4[r] = (resp && j < pi) ? acc[r] * __expf(lgp - lg[j]) * (fold_w ? beta[j] : 1.f) : 0.f;
+      }
+      *reinterpret_cast<float4 *>(&cc[qside ? CC_MQ : CC_MK][i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    }
+    if (qside) {
+      const int nt = B > 16 ? 4 : 2;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t >= nt) break;
+        const int ti = (t == 0 || t == 2) ? 0 : 1, tj = (t == 0 || t == 3) ? 0 : 1;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        gemm_tile<BF, D, XL, XL>(acc, &x[3][0][0], LDX, 16 * tj, &x[2][0][0], LDX, 16 * ti);
+        const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+        const int pi = i - (i % B);
+        const bool resp = c0 + i < n && c0 + i >= P;
+        const float lge = lgn[pi + B - 1];
+        float o4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + r;
+          o4[r] = (resp && j >= pi && j < pi + B) ? acc[r] * __expf(lge - lgn[j]) * (fold_w ? betan[j] : 1.f) : 0.f;
+        }
+        *reinterpret_cast<float4 *>(&cc[CC_MN][i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+      }
+    } else {
+      const int nt = B > 16 ? 3 : 2;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        if (t >= nt) break;
+        const int ti = t == 0 ? 0 : 1, tj = t == 1 ? 1 : 0;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        gemm_tile<BF, D, XL, XL>(acc, &x[3][0][0], LDX, 16 * ti, &x[3][0][0], LDX, 16 * tj);
+        const int j = 16 * tj + cl;
+        const int pj = j - (j % B);
+        const float wj = fold_w ? betan[j] : 1.f;
+        float o4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ti + g4 + r;
+          const bool resp = c0 + i < n && c0 + i >= P;
+          o4[r] = (resp && j < i && i - (i % B) == pj) ? acc[r] * __expf(lgn[i] - lgn[j]) * wj : 0.f;
+        }
+        *reinterpret_cast<float4 *>(&cc[CC_ANT][j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+      }
+    }
+  }
+}
+
+}  // namespace flare

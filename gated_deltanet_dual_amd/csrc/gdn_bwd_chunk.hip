@@ -1,0 +1,628 @@
+// gdn_bwd_chunk.hip -- per-chunk gradient kernel of the dual-stream backward
+// for bf16 io at d_k = d_v = 128 (the other shapes use the generic kernel in
+// gdn_bwd.hip).  The algebra is the one written out at the top of gdn_bwd.hip;
+// only the schedule differs.
+//
+// One workgroup of 8 waves per (chunk slot, head), fully parallel over chunks.
+//   phase 0  q, k, q~, k~ rows and gates -> LDS; the six masked Gram matrices
+//            (waves 0-3) and the two unit-triangular solves (waves 0, 1).
+//   phase 1  wave w owns d_v columns [16w, 16w + 16).  Every C x 16 quantity of
+//            the chunk -- K S_c, U, the noisy reads r_q, r_k, u~, the noisy
+//            adjoints, dU, drhs -- is computed in MFMA accumulator registers and
+//            fed straight back into the next product (slab.h), so the whole
+//            column-separable chain runs without LDS round trips or barriers.
+//            S_c and dS' columns come straight from global memory as B
+//            fragments; dv and dv~ are stored from registers.
+//   phase 2  the products that reduce over d_v: wave w takes three 16 x 16
+//            tiles of the six Gram adjoints and the 16-column d_k tile w of
+//            dq, dk, dq~, dk~, with U, u~, drhs, drhs~ shared through LDS.
+//   phase 3  Gram adjoints -> Gram-weight gradients, their contractions with
+//            the q/k rows, gate gradients, stores.
+// Nothing is reduced across workgroups, so the result is deterministic.
+#include "bwd_common.h"
+#include "chunk_common.h"
+#include "device_common.h"
+#include "gemm_lds.h"
+#include "kernels.h"
+#include "slab.h"
+#include "timing.h"
+
+namespace flare {
+
+namespace {
+
+constexpr int kC = 32, kD = 128, kNW = 8, kNT = 64 * kNW;
+constexpr int kLDX = kD + 8, kLDM = kC + 4, kLDA = kD + 4;
+enum { P_G = 0, P_GN, P_B, P_BN, P_GP, P_GE, P_C, P_NUM };
+enum { A_U = 0, A_UN, A_DRHS, A_DRN };
+
+struct Chunk2Smem {
+  alignas(16) u16 x[4][kC][kLDX];       // q, k, q~, k~ ; at the end the staging of dq, dk, dq~, dk~
+  alignas(16) float cc[8][kC][kLDM];    // unweighted masked Grams (A, A~ transposed), T, T~; later dG
+  alignas(16) float arr[4][kC][kLDA];   // U, u~, drhs, drhs~ for the d_v reductions
+  alignas(16) float tmp[2][16][17];
+  alignas(16) float lg[kC], beta[kC], lgn[kC], betan[kC];
+  alignas(16) float part[kNW][P_NUM][kC];  // per-wave gate-gradient partials
+  alignas(16) float plgc[kNW];
+  alignas(16) float gsum[2][kC];
+};
+
+// 16-byte row fragment of a [T, H, D] bf16 tensor straight from global memory:
+// rows c0 + row0 + (l & 15), columns k0 + 8 (l >> 4) .. +7; rows past the
+// document end (or noisy prompt rows when noisy) read as zero.
+__device__ __forceinline__ bf16x8 gfrag_rows(const u16 *src, int H, int h, int64_t t0g, int c0, int n, int P,
+                                             bool noisy, int row0, int k0) {
+  const int l = lane_id();
+  const int tpos = c0 + row0 + (l & 15);
+  const bool ok = tpos < n && (!noisy || tpos >= P);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) v = *reinterpret_cast<const uint4 *>(src + ((t0g + tpos) * H + h) * kD + k0 + 8 * (l >> 4));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Slab (accumulator layout) of columns [col0, col0 + 16) of a [T, H, D] bf16 tensor.
+__device__ __forceinline__ Slab gslab(const u16 *src, int H, int h, int64_t t0g, int c0, int n, int P, bool noisy,
+                                      int col0) {
+  Slab s;
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tpos = c0 + slab_row(tr, r);
+      const bool ok = tpos < n && (!noisy || tpos >= P);
+      s.t[tr][r] = ok ? bf2f(src[((t0g + tpos) * H + h) * kD + col0 + acc_col()]) : 0.f;
+    }
+  return s;
+}
+
+// fp32 row fragment of a [D][D] state straight from global memory: rows
+// row0 + (l & 15), columns k0 + 8 (l >> 4) .. +7, split hi + lo.
+__device__ __forceinline__ void gstate_rows(const float *S, int row0, int k0, bf16x8 &hi, bf16x8 &lo) {
+  const int l = lane_id();
+  const float4 *p = reinterpret_cast<const float4 *>(S + (size_t)(row0 + (l & 15)) * kD + k0 + 8 * (l >> 4));
+  const float4 a = p[0], b = p[1];
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  split8(x, hi, lo);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
+  constexpr int C = kC, D = kD, NT = kNT, LDX = kLDX, LDM = kLDM, LDA = kLDA;
+  __shared__ Chunk2Smem sm;
+  const FwdArgs &f = a.f;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = 4 * (lane >> 4), cl = lane & 15;
+  const int H = f.H;
+  const int slot = blockIdx.x / H, h = blockIdx.x % H;
+
+  // slot -> (document, chunk): slots of document i start at floor(cu_i / C) + i
+  int lo = 0, hi = f.num_docs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)f.cu[mid] / C + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int doc = lo;
+  const int64_t t0g = f.cu[doc];
+  const int n = f.cu[doc + 1] - f.cu[doc];
+  const int c = slot - (int)(t0g / C) - doc;
+  if (c < 0 || c * C >= n) return;
+  const int P = f.plen[doc];
+  const int B = f.B;
+  const int c0 = c * C;
+  const bool has_noisy = (c0 + C > P) && (P < n);
+  const float s = f.scale;
+  const float *Sc = a.ckpt_in + ((int64_t)slot * H + h) * (size_t)D * D;
+  const float *dSn = reinterpret_cast<const float *>(a.workspace) + ((int64_t)slot * H + h) * (size_t)D * D;
+  const u16 *const pq = reinterpret_cast<const u16 *>(f.q), *const pk = reinterpret_cast<const u16 *>(f.k);
+  const u16 *const pqn = reinterpret_cast<const u16 *>(f.qn), *const pkn = reinterpret_cast<const u16 *>(f.kn);
+  const u16 *const pv = reinterpret_cast<const u16 *>(f.v), *const pvn = reinterpret_cast<const u16 *>(f.vn);
+  const u16 *const pdo = reinterpret_cast<const u16 *>(a.d_o), *const pdon = reinterpret_cast<const u16 *>(a.d_on);
+  const int col0 = 16 * wave;  // this wave's d_v slab (phase 1) and d_k tile (phase 2)
+
+  // ================================================================ phase 0
+  for (int e = tid; e < 8 * C * LDM; e += NT) (&sm.cc[0][0][0])[e] = 0.f;
+  for (int e = tid; e < kNW * P_NUM * C; e += NT) (&sm.part[0][0][0])[e] = 0.f;
+  {
+    constexpr int RU = D / 8, PU = C * RU;  // 16-byte units per row / per tile
+    for (int u = tid; u < 4 * PU; u += NT) {
+      const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
+      const int tpos = c0 + row;
+      const bool ok = tpos < n && (m < 2 || tpos >= P);
+      const u16 *src = m == 0 ? pq : m == 1 ? pk : m == 2 ? pqn : pkn;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) val = *reinterpret_cast<const uint4 *>(src + ((t0g + tpos) * H + h) * D + cu16 * 8);
+      *reinterpret_cast<uint4 *>(&sm.x[m][row][cu16 * 8]) = val;
+    }
+  }
+  load_gates(f, t0g, c0, n, P, h, B, sm.lg, sm.beta, sm.lgn, sm.betan);
+
+  // this wave's slab inputs (global -> registers, in flight during the Grams)
+  const Slab V = gslab(pv, H, h, t0g, c0, n, P, false, col0);
+  const Slab VN = gslab(pvn, H, h, t0g, c0, n, P, true, col0);
+  const Slab DO = gslab(pdo, H, h, t0g, c0, n, P, false, col0);
+  const Slab DON = gslab(pdon, H, h, t0g, c0, n, P, true, col0);
+  // S_c and dS' columns of the slab (k = 32 ks + 8 g + e over d_k), loaded now
+  // and converted to B fragments after the Gram phase, so the loads overlap it
+  float xs[4][8], xd[4][8];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const size_t off = (size_t)(32 * ks + 2 * g4 + e) * D + col0 + cl;
+      xs[ks][e] = Sc[off];
+      xd[ks][e] = dSn[off];
+    }
+  lds_barrier();
+  if (wave < 4)
+    chunk_grams<true, D, LDX, LDM>(sm.x, sm.cc, sm.lg, sm.beta, sm.lgn, sm.betan, c0, n, P, B, has_noisy, false);
+  lds_barrier();
+
+  const float lgC = sm.lg[C - 1];
+  auto Gm = [&](int i) { return __expf(sm.lg[i]); };
+  auto Gp = [&](int i) { const int pi = i - (i % B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
+  auto Ge = [&](int i) { const int pi = i - (i % B); return __expf(sm.lgn[pi + B - 1]); };
+  auto Dd = [&](int i) { return sm.beta[i] * __expf(lgC - sm.lg[i]); };
+  auto resp_row = [&](int i) { return c0 + i < n && c0 + i >= P; };
+
+  bf16x8 sbh[4], sbl[4], dbh[4], dbl[4];
+  float plg = 0.f;  // <dS', S_c> over this slab, fp32
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) plg += xs[ks][e] * xd[ks][e];
+    split8(xs[ks], sbh[ks], sbl[ks]);
+    split8(xd[ks], dbh[ks], dbl[ks]);
+  }
+
+  // ---- X S_c and K dS' products (need no solve): waves 0, 1 solve first
+  if (wave == 0) solve_unit_lower<LDM>(&sm.cc[CC_AT][0][0], &sm.cc[CC_T][0][0], &sm.tmp[0][0][0], true, sm.beta);
+  if (wave == 1 && has_noisy)
+    solve_unit_lower<LDM>(&sm.cc[CC_ANT][0][0], &sm.cc[CC_TN][0][0], &sm.tmp[1][0][0], B > 16, sm.betan);
+  Slab KS = slab_zero(), QS = slab_zero(), QNS = slab_zero(), KNS = slab_zero(), KD = slab_zero();
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 ak = frag_bf16(&sm.x[1][0][0], LDX, 16 * tr, 32 * ks);
+      const bf16x8 aq = frag_bf16(&sm.x[0][0][0], LDX, 16 * tr, 32 * ks);
+      mma_bf16(KS.t[tr], ak, sbh[ks]);
+      mma_bf16(KS.t[tr], ak, sbl[ks]);
+      mma_bf16(KD.t[tr], ak, dbh[ks]);
+      mma_bf16(KD.t[tr], ak, dbl[ks]);
+      mma_bf16(QS.t[tr], aq, sbh[ks]);
+      if (has_noisy) {
+        const bf16x8 aqn = frag_bf16(&sm.x[2][0][0], LDX, 16 * tr, 32 * ks);
+        const bf16x8 akn = frag_bf16(&sm.x[3][0][0], LDX, 16 * tr, 32 * ks);
+        mma_bf16(QNS.t[tr], aqn, sbh[ks]);
+        mma_bf16(QNS.t[tr], aqn, sbl[ks]);
+        mma_bf16(KNS.t[tr], akn, sbh[ks]);
+        mma_bf16(KNS.t[tr], akn, sbl[ks]);
+      }
+    }
+  lds_barrier();  // T, T~ visible
+
+  // ================================================================ phase 1
+  float pg[2][4], pgn[2][4], pb[2][4], pgp[2][4], pge[2][4], pc[2][4];
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pg[tr][r] = pgn[tr][r] = pb[tr][r] = pgp[tr][r] = pge[tr][r] = pc[tr][r] = 0.f;
+
+  // rhs = v - G K S_c ; U = T rhs
+  Slab rhs;
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = slab_row(tr, r);
+      rhs.t[tr][r] = V.t[tr][r] - Gm(i) * KS.t[tr][r];
+      pg[tr][r] += s * Gm(i) * row_sum16(QS.t[tr][r] * DO.t[tr][r]);  // d gamma_i from o_i = s G_i q_i S_c
+    }
+  Slab U = slab_zero();
+  cc_mul<3, false>(U, &sm.cc[CC_T][0][0], LDM, rhs);
+  Slab BU;
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) BU.t[tr][r] = sm.beta[slab_row(tr, r)] * U.t[tr][r];
+
+  // noisy reads and block: r_q, r_k, u~ ; noisy adjoints dr_q, du~, drhs~, dr_k
+  Slab UN = slab_zero(), DRQ = slab_zero(), DRN = slab_zero(), DUN = slab_zero();
+  if (has_noisy) {
+    Slab RQ, RK, RQ0, RK0;
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = slab_row(tr, r);
+        RQ0.t[tr][r] = Gp(i) * QNS.t[tr][r];
+        RK0.t[tr][r] = Gp(i) * KNS.t[tr][r];
+      }
+    RQ = RQ0;
+    RK = RK0;
+    cc_mul<3, false>(RQ, &sm.cc[CC_MQ][0][0], LDM, BU);
+    cc_mul<3, false>(RK, &sm.cc[CC_MK][0][0], LDM, BU);
+    Slab rhsn;
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rhsn.t[tr][r] = VN.t[tr][r] - __expf(sm.lgn[slab_row(tr, r)]) * RK.t[tr][r];
+    cc_mul<3, false>(UN, &sm.cc[CC_TN][0][0], LDM, rhsn);
+    // du~ = s diag(b~) M~^T do~
+    Slab dun = slab_zero();
+    cc_mul<2, true>(dun, &sm.cc[CC_MN][0][0], LDM, DON);
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = slab_row(tr, r);
+        dun.t[tr][r] *= s * sm.betan[i];
+        DRQ.t[tr][r] = s * Ge(i) * DON.t[tr][r];
+        const float t = row_sum16(DON.t[tr][r] * RQ.t[tr][r]);
+        if (resp_row(i)) pge[tr][r] += s * Ge(i) * t;  // d gamma~ at the block end
+      }
+    // drhs~ = T~^T du~ (response rows only); dr_k = -G~ drhs~
+    cc_mul<3, true>(DRN, &sm.cc[CC_TN][0][0], LDM, dun);
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = slab_row(tr, r);
+        const float drn = resp_row(i) ? DRN.t[tr][r] : 0.f;
+        DRN.t[tr][r] = drn;
+        const float gn = __expf(sm.lgn[i]);
+        pgn[tr][r] -= gn * row_sum16(drn * RK.t[tr][r]);
+        DUN.t[tr][r] = -gn * drn;
+        pgp[tr][r] += row_sum16(DRQ.t[tr][r] * RQ0.t[tr][r] + DUN.t[tr][r] * RK0.t[tr][r]);
+      }
+  }
+
+  // dU = D K dS' + diag(b) (s Mo^T do + Mq^T dr_q + Mk^T dr_k)
+  Slab dU = slab_zero();
+  cc_mul<2, true>(dU, &sm.cc[CC_MO][0][0], LDM, DO);
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr) dU.t[tr] *= s;
+  if (has_noisy) {
+    cc_mul<3, true>(dU, &sm.cc[CC_MQ][0][0], LDM, DRQ);
+    cc_mul<3, true>(dU, &sm.cc[CC_MK][0][0], LDM, DUN);
+  }
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = slab_row(tr, r);
+      const float Di = Dd(i);
+      const float t = row_sum16(KD.t[tr][r] * U.t[tr][r]);  // d D_i
+      pb[tr][r] += t * __expf(lgC - sm.lg[i]);
+      pg[tr][r] -= t * Di;
+      pc[tr][r] += t * Di;
+      dU.t[tr][r] = Di * KD.t[tr][r] + sm.beta[i] * dU.t[tr][r];
+    }
+  // drhs = T^T dU (= dv)
+  Slab DRHS = slab_zero();
+  cc_mul<3, true>(DRHS, &sm.cc[CC_T][0][0], LDM, dU);
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = slab_row(tr, r);
+      pg[tr][r] -= Gm(i) * row_sum16(DRHS.t[tr][r] * KS.t[tr][r]);
+    }
+
+  // ---- dv, dv~ from registers; the four shared C x d_v arrays -> LDS
+  {
+    u16 *gdv = reinterpret_cast<u16 *>(a.dv), *gdvn = reinterpret_cast<u16 *>(a.dvn);
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = slab_row(tr, r);
+        if (c0 + i < n) {
+          const int64_t off = ((t0g + c0 + i) * H + h) * D + col0 + cl;
+          gdv[off] = f2bf(DRHS.t[tr][r]);
+          gdvn[off] = f2bf(has_noisy && resp_row(i) ? DRN.t[tr][r] : 0.f);
+        }
+        sm.arr[A_U][i][col0 + cl] = U.t[tr][r];
+        sm.arr[A_UN][i][col0 + cl] = UN.t[tr][r];
+        sm.arr[A_DRHS][i][col0 + cl] = DRHS.t[tr][r];
+        sm.arr[A_DRN][i][col0 + cl] = DRN.t[tr][r];
+      }
+  }
+  // per-row gate partials of this wave (lanes of column 0 own the row sums)
+  if (cl == 0) {
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = slab_row(tr, r);
+        sm.part[wave][P_G][i] = pg[tr][r];
+        sm.part[wave][P_GN][i] = pgn[tr][r];
+        sm.part[wave][P_B][i] = pb[tr][r];
+        sm.part[wave][P_GP][i] = pgp[tr][r];
+        sm.part[wave][P_GE][i] = pge[tr][r];
+        sm.part[wave][P_C][i] = pc[tr][r];
+      }
+  }
+  {
+    float t = plg;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
+    if (lane == 0) sm.plgc[wave] = __expf(lgC) * t;
+  }
+  lds_barrier();
+
+  // ================================================================ phase 2
+  // Gram adjoints: 6 matrices x 4 tiles, tile t = wave + 8 j -> (m = t / 4, ti, tj)
+  enum { DM_O = 0, DM_Q, DM_K, DM_N, DM_A, DM_AN };
+  floatx4 dM[3];
+#pragma unroll
+  for (int jt = 0; jt < 3; ++jt) {
+    const int t = wave + 8 * jt;
+    const int m = t >> 2, ti = (t >> 1) & 1, tj = t & 1;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    const bool noisy_m = m == DM_Q || m == DM_K || m == DM_N || m == DM_AN;
+    if (!noisy_m || has_noisy) {
+      const int right = (m == DM_N || m == DM_AN) ? A_UN : A_U;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 bh, bl;
+        frag_f32_split(&sm.arr[right][0][0], LDA, 16 * tj, 32 * ks, bh, bl);
+        if (m == DM_O || m == DM_Q || m == DM_N) {  // left operand do / do~ (exact bf16)
+          const bf16x8 ah = gfrag_rows(m == DM_O ? pdo : pdon, H, h, t0g, c0, n, P, m != DM_O, 16 * ti, 32 * ks);
+          mma_bf16(acc, ah, bh);
+          mma_bf16(acc, ah, bl);
+        } else {
+          const int left = m == DM_A ? A_DRHS : A_DRN;
+          bf16x8 ah, al;
+          frag_f32_split(&sm.arr[left][0][0], LDA, 16 * ti, 32 * ks, ah, al);
+          mma_bf16(acc, ah, bh);
+          mma_bf16(acc, ah, bl);
+          mma_bf16(acc, al, bh);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + g4 + r;
+        float sc = 1.f;
+        if (m == DM_O || m == DM_N) sc = s;
+        else if (m == DM_Q) sc = s * Ge(i);
+        else if (m == DM_K) sc = -__expf(sm.lgn[i]);
+        else sc = -1.f;
+        acc[r] *= sc;
+      }
+    }
+    dM[jt] = acc;
+  }
+
+  // d_k tile `wave` of dq, dk, dq~, dk~: the d_v contractions with S_c, dS'
+  floatx4 dq[2], dk[2], dqn[2], dkn[2];
+  {
+    floatx4 a_dq[2], a_dk1[2], a_dk2[2], a_dqn[2], a_dkn[2];
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+      a_dq[tr] = a_dk1[tr] = a_dk2[tr] = a_dqn[tr] = a_dkn[tr] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 sh, sl, dh, dl;
+      gstate_rows(Sc, col0, 32 * ks, sh, sl);
+      gstate_rows(dSn, col0, 32 * ks, dh, dl);
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr) {
+        const bf16x8 ado = gfrag_rows(pdo, H, h, t0g, c0, n, P, false, 16 * tr, 32 * ks);
+        mma_bf16(a_dq[tr], ado, sh);
+        mma_bf16(a_dq[tr], ado, sl);
+        bf16x8 ah, al;
+        frag_f32_split(&sm.arr[A_DRHS][0][0], LDA, 16 * tr, 32 * ks, ah, al);
+        mma_bf16(a_dk1[tr], ah, sh);
+        mma_bf16(a_dk1[tr], ah, sl);
+        mma_bf16(a_dk1[tr], al, sh);
+        frag_f32_split(&sm.arr[A_U][0][0], LDA, 16 * tr, 32 * ks, ah, al);
+        mma_bf16(a_dk2[tr], ah, dh);
+        mma_bf16(a_dk2[tr], ah, dl);
+        mma_bf16(a_dk2[tr], al, dh);
+        if (has_noisy) {
+          const bf16x8 adon = gfrag_rows(pdon, H, h, t0g, c0, n, P, true, 16 * tr, 32 * ks);
+          mma_bf16(a_dqn[tr], adon, sh);
+          mma_bf16(a_dqn[tr], adon, sl);
+          frag_f32_split(&sm.arr[A_DRN][0][0], LDA, 16 * tr, 32 * ks, ah, al);
+          mma_bf16(a_dkn[tr], ah, sh);
+          mma_bf16(a_dkn[tr], ah, sl);
+          mma_bf16(a_dkn[tr], al, sh);
+        }
+      }
+    }
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * tr + g4 + r;
+        dq[tr][r] = s * Gm(i) * a_dq[tr][r];
+        dk[tr][r] = -Gm(i) * a_dk1[tr][r] + Dd(i) * a_dk2[tr][r];
+        dqn[tr][r] = Gp(i) * s * Ge(i) * a_dqn[tr][r];
+        dkn[tr][r] = -Gp(i) * __expf(sm.lgn[i]) * a_dkn[tr][r];
+      }
+  }
+
+  // ================================================================ phase 3
+  // Gram adjoints -> dG (in place over the unweighted Grams) + gate partials
+#pragma unroll
+  for (int jt = 0; jt < 3; ++jt) {
+    const int t = wave + 8 * jt;
+    const int m = t >> 2, ti = (t >> 1) & 1, tj = t & 1;
+    if (!has_noisy && (m == DM_Q || m == DM_K || m == DM_N || m == DM_AN)) continue;
+    const int i0 = 16 * ti + g4, j = 16 * tj + cl;
+    // Mo : w = b, e = lg_i, f = lg_j, mask j <= i
+    // Mq/Mk : w = b, e = lg[p_i - 1], mask j < p_i (resp)
+    // M~ : w = b~, e = lgn[end(i)], f = lgn_j, mask same block (resp)
+    // A^T / A~^T stored transposed: element [j][i]
+    const int ccm = m == DM_O ? CC_MO : m == DM_Q ? CC_MQ : m == DM_K ? CC_MK : m == DM_N ? CC_MN
+                  : m == DM_A ? CC_AT : CC_ANT;
+    const bool tr_store = (m == DM_A || m == DM_AN);
+    const bool noisyw = (m == DM_N || m == DM_AN);
+    const float wj = noisyw ? sm.betan[j] : sm.beta[j];
+    const float fj = noisyw ? sm.lgn[j] : sm.lg[j];
+    float colw = 0.f, colf = 0.f;
+    const int pbase = (m == DM_O || m == DM_A) ? P_G : (m == DM_Q || m == DM_K) ? P_GP : m == DM_N ? P_GE : P_GN;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + r;
+      float *cell = tr_store ? &sm.cc[ccm][j][i] : &sm.cc[ccm][i][j];
+      const float mw = *cell;  // unweighted masked Gram, already zero outside the mask
+      float ei;
+      bool mask;
+      if (m == DM_O) { ei = sm.lg[i]; mask = j <= i; }
+      else if (m == DM_A) { ei = sm.lg[i]; mask = j < i; }
+      else if (m == DM_Q || m == DM_K) {
+        const int pi = i - (i % B);
+        ei = pi > 0 ? sm.lg[pi - 1] : 0.f;
+        mask = resp_row(i) && j < pi;
+      } else if (m == DM_N) {
+        const int pi = i - (i % B);
+        ei = sm.lgn[pi + B - 1];
+        mask = resp_row(i) && j >= pi && j < pi + B;
+      } else {
+        const int pi = i - (i % B);
+        ei = sm.lgn[i];
+        mask = resp_row(i) && j < i && j >= pi;
+      }
+      const float dm = dM[jt][r];
+      const float E = mask ? __expf(ei - fj) : 0.f;
+      const float mfull = mw * wj;
+      *cell = dm * E * wj;  // dG
+      const float dd = dm * mfull;
+      const float rs = row_sum16(dd);
+      if (cl == 0) sm.part[wave][pbase][i] += rs;  // row part d e_i
+      colf += dd;
+      colw += dm * mw;
+    }
+    // column parts: over the 4 row groups of the tile
+    colf += __shfl_xor(colf, 16, 64);
+    colf += __shfl_xor(colf, 32, 64);
+    colw += __shfl_xor(colw, 16, 64);
+    colw += __shfl_xor(colw, 32, 64);
+    if (lane < 16) {
+      if (noisyw) {
+        sm.part[wave][P_GN][j] -= colf;
+        sm.part[wave][P_BN][j] += colw;
+      } else {
+        sm.part[wave][P_G][j] -= colf;
+        sm.part[wave][P_B][j] += colw;
+      }
+    }
+  }
+  lds_barrier();
+
+  // Gram contractions for d_k tile `wave`: B fragments are columns of q, k, q~, k~
+  {
+    const bf16x8 bq = frag_bf16_T(&sm.x[0][0][0], LDX, col0, 0);
+    const bf16x8 bk = frag_bf16_T(&sm.x[1][0][0], LDX, col0, 0);
+    const bf16x8 bqn = frag_bf16_T(&sm.x[2][0][0], LDX, col0, 0);
+    const bf16x8 bkn = frag_bf16_T(&sm.x[3][0][0], LDX, col0, 0);
+    auto gmul = [&](floatx4 &acc, int ccm, bool transposed, int ra, const bf16x8 &b) {
+      bf16x8 ah, al;
+      if (transposed) frag_f32_split_T(&sm.cc[ccm][0][0], LDM, ra, 0, ah, al);
+      else frag_f32_split(&sm.cc[ccm][0][0], LDM, ra, 0, ah, al);
+      mma_bf16(acc, ah, b);
+      mma_bf16(acc, al, b);
+    };
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr) {
+      const int ra = 16 * tr;
+      gmul(dq[tr], CC_MO, false, ra, bk);   // dq += dGo k
+      gmul(dk[tr], CC_MO, true, ra, bq);    // dk += dGo^T q + dGA k + dGA^T k
+      gmul(dk[tr], CC_AT, true, ra, bk);
+      gmul(dk[tr], CC_AT, false, ra, bk);
+      if (has_noisy) {
+        gmul(dk[tr], CC_MQ, true, ra, bqn);   // + dGq^T q~ + dGk^T k~
+        gmul(dk[tr], CC_MK, true, ra, bkn);
+        gmul(dqn[tr], CC_MQ, false, ra, bk);  // dq~ += dGq k + dG~ k~
+        gmul(dqn[tr], CC_MN, false, ra, bkn);
+        gmul(dkn[tr], CC_MK, false, ra, bk);  // dk~ += dGk k + dGA~ k~ + dGA~^T k~ + dG~^T q~
+        gmul(dkn[tr], CC_ANT, true, ra, bkn);
+        gmul(dkn[tr], CC_ANT, false, ra, bkn);
+        gmul(dkn[tr], CC_MN, true, ra, bqn);
+      }
+    }
+  }
+  lds_barrier();
+  // ---- stage the four d_k-side gradients in the (now free) q/k tiles, then store rows
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * tr + g4 + r;
+      const bool rs = resp_row(i);
+      sm.x[0][i][col0 + cl] = f2bf(dq[tr][r]);
+      sm.x[1][i][col0 + cl] = f2bf(dk[tr][r]);
+      sm.x[2][i][col0 + cl] = f2bf(rs ? dqn[tr][r] : 0.f);
+      sm.x[3][i][col0 + cl] = f2bf(rs ? dkn[tr][r] : 0.f);
+    }
+  // ---- gates: reduce the per-wave partials in a fixed order and move the
+  // boundary terms to the positions they belong to
+  if (tid < 2 * C) {
+    const int i = tid & (C - 1);
+    float v = 0.f;
+    if (tid < C) {  // clean d gamma_i
+      for (int w = 0; w < kNW; ++w) v += sm.part[w][P_G][i];
+      if (((i + 1) % B) == 0 && i + 1 < C)  // boundary p = i + 1: reads of the block starting there
+        for (int m = i + 1; m < i + 1 + B; ++m)
+          for (int w = 0; w < kNW; ++w) v += sm.part[w][P_GP][m];
+      if (i == C - 1) {
+        for (int w = 0; w < kNW; ++w) v += sm.plgc[w];
+        for (int m = 0; m < C; ++m)
+          for (int w = 0; w < kNW; ++w) v += sm.part[w][P_C][m];
+      }
+    } else {  // noisy d gamma~_i
+      for (int w = 0; w < kNW; ++w) v += sm.part[w][P_GN][i];
+      if (((i + 1) % B) == 0)
+        for (int m = i + 1 - B; m <= i; ++m)
+          for (int w = 0; w < kNW; ++w) v += sm.part[w][P_GE][m];
+    }
+    sm.gsum[tid / C][i] = v;
+  }
+  lds_barrier();
+  {
+    constexpr int RU = D / 8;
+    u16 *outp[4] = {reinterpret_cast<u16 *>(a.dq), reinterpret_cast<u16 *>(a.dk), reinterpret_cast<u16 *>(a.dqn),
+                    reinterpret_cast<u16 *>(a.dkn)};
+    for (int u = tid; u < 4 * C * RU; u += NT) {
+      const int m = u / (C * RU), rr = u % (C * RU), row = rr / RU, cu16 = rr % RU;
+      if (c0 + row >= n) continue;
+      u16 *dst = m == 0 ? outp[0] : m == 1 ? outp[1] : m == 2 ? outp[2] : outp[3];
+      *reinterpret_cast<uint4 *>(dst + ((t0g + c0 + row) * H + h) * D + cu16 * 8) =
+          *reinterpret_cast<const uint4 *>(&sm.x[m][row][cu16 * 8]);
+    }
+  }
+  if (tid < 2 * C) {
+    const int i = tid & (C - 1);
+    const bool noisy = tid >= C;
+    float dg = 0.f, db = 0.f;
+    if (!noisy) {
+      for (int m = i; m < C; ++m) dg += sm.gsum[0][m];
+      for (int w = 0; w < kNW; ++w) db += sm.part[w][P_B][i];
+    } else {
+      const int end = i - (i % B) + B;
+      for (int m = i; m < end; ++m) dg += sm.gsum[1][m];
+      for (int w = 0; w < kNW; ++w) db += sm.part[w][P_BN][i];
+    }
+    const int64_t gi = (t0g + c0 + i) * H + h;
+    if (c0 + i < n) {
+      if (!noisy) {
+        a.dalpha[gi] = dg / f.alpha[gi];
+        a.dbeta[gi] = db;
+      } else {
+        const bool rsp = c0 + i >= P;
+        a.dalpha_n[gi] = rsp ? dg / f.alpha_n[gi] : 0.f;
+        a.dbeta_n[gi] = rsp ? db : 0.f;
+      }
+    }
+  }
+}
+
+hipError_t launch_bwd_chunk_d128(const BwdArgs &a, hipStream_t st, int64_t slots) {
+  hipLaunchKernelGGL(gdn_bwd_chunk_d128_kernel, dim3((unsigned)(slots * a.f.H)), dim3(kNT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace flare

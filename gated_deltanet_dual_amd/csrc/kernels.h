@@ -50,5 +50,7 @@ struct BwdArgs {
   int64_t T;
 };
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
+// per-chunk backward kernel for bf16 io at d = 128 (gdn_bwd_chunk.hip)
+hipError_t launch_bwd_chunk_d128(const BwdArgs &a, hipStream_t st, int64_t slots);
 
 }  // namespace flare
