@@ -10,6 +10,63 @@ namespace flare {
 
 enum { CC_AT = 0, CC_T, CC_MO, CC_MQ, CC_MK, CC_ANT, CC_TN, CC_MN };
 
+// The gate value thread tid < 128 of a chunk reads: group g = tid / 32 of
+// (a, b, a~, b~), position i = tid % 32 (padded tokens and noisy prompt tokens:
+// a = 1, b = 0).
+__device__ __forceinline__ float gate_load(const FwdArgs &f, int64_t t0g, int c0, int n, int P, int h, int tid) {
+  const int g = tid / 32, i = tid % 32;
+  const int tpos = c0 + i;
+  bool ok = tpos < n;
+  if (g >= 2) ok = ok && tpos >= P;
+  // the four pointers are read into registers first: selecting among the
+  // argument block's fields per lane would load the pointer itself per lane
+  const float *const p0 = f.alpha, *const p1 = f.beta, *const p2 = f.alpha_n, *const p3 = f.beta_n;
+  const float *src = g == 0 ? p0 : g == 1 ? p1 : g == 2 ? p2 : p3;
+  // unconditional load from a row clamped into the document, masked afterwards
+  const float v = src[(t0g + min(tpos, n - 1)) * f.H + h];
+  return ok ? v : ((g & 1) == 0 ? 1.f : 0.f);
+}
+
+// The same load, split: the raw value now (no use of it, so nothing waits),
+// the mask and padding applied by gate_fix when the value is consumed.
+__device__ __forceinline__ float gate_load_raw(const FwdArgs &f, int64_t t0g, int c0, int n, int h, int tid) {
+  const int g = tid / 32, i = tid % 32;
+  const float *const p0 = f.alpha, *const p1 = f.beta, *const p2 = f.alpha_n, *const p3 = f.beta_n;
+  const float *src = g == 0 ? p0 : g == 1 ? p1 : g == 2 ? p2 : p3;
+  return src[(t0g + min(c0 + i, n - 1)) * f.H + h];
+}
+__device__ __forceinline__ float gate_fix(float raw, int c0, int n, int P, int tid) {
+  const int g = tid / 32, tpos = c0 + tid % 32;
+  const bool ok = tpos < n && (g < 2 || tpos >= P);
+  return ok ? raw : ((g & 1) == 0 ? 1.f : 0.f);
+}
+
+// The scan of gate_load's value (threads tid < 128): cumulative log a over the
+// chunk, cumulative log a~ inside each noisy block of B.
+__device__ __forceinline__ void gate_scan(float val, int B, int tid, float *lg, float *beta, float *lgn,
+                                          float *betan) {
+  const int g = tid / 32, i = tid % 32;
+  if (g == 0 || g == 2) {
+    float la = __logf(val);
+    if (g == 0) {
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float y = __shfl_up(la, off, 32);
+        if (i >= off) la += y;
+      }
+      lg[i] = la;
+    } else {
+      for (int off = 1; off < B; off <<= 1) {
+        const float y = __shfl_up(la, off, B);
+        if ((i % B) >= off) la += y;
+      }
+      lgn[i] = la;
+    }
+  } else {
+    (g == 1 ? beta : betan)[i] = val;
+  }
+}
+
 // Per-chunk gates: lg = cumulative log a, lgn = cumulative log a~ inside each
 // noisy block (padded tokens: a = 1, b = 0; noisy prompt tokens likewise).
 __device__ __forceinline__ void load_gates(const FwdArgs &f, int64_t t0g, int c0, int n, int P, int h, int B,
@@ -149,6 +206,67 @@ __device__ __forceinline__ void chunk_grams(IO (*x)[32][LDX], float (*cc)[32][LD
         *reinterpret_cast<float4 *>(&cc[CC_ANT][j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
       }
     }
+  }
+}
+
+// Chunk slot -> (document, chunk index); returns false for a slot past the end
+// of its document.  Slots of document i start at floor(cu_i / 32) + i.
+__device__ __forceinline__ bool slot_to_chunk(const FwdArgs &f, int slot, int &doc, int &c) {
+  int lo = 0, hi = f.num_docs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)f.cu[mid] / 32 + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  doc = lo;
+  c = slot - (int)(f.cu[doc] / 32) - doc;
+  const int n = f.cu[doc + 1] - f.cu[doc];
+  return c >= 0 && c * 32 < n;
+}
+
+// A^T of the chunk (one wave): A_ij = (k_i . k_j) exp(lg_i - lg_j) for j < i,
+// without the write strengths, stored transposed (row j = column j of A).
+template <int D, int LDX, int LDM>
+__device__ __forceinline__ void gram_at(const u16 (*k)[LDX], float (*at)[LDM], const float *lg) {
+  const int lane = lane_id(), g4 = 4 * (lane >> 4), cl = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int ti = t == 0 ? 0 : 1, tj = t == 2 ? 1 : 0;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    gemm_tile<true, D, RowU16, RowU16>(acc, &k[0][0], LDX, 16 * ti, &k[0][0], LDX, 16 * tj);
+    const int j = 16 * tj + cl;
+    float o4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + g4 + r;
+      o4[r] = j < i ? acc[r] * __expf(lg[i] - lg[j]) : 0.f;
+    }
+    *reinterpret_cast<float4 *>(&at[j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+  }
+}
+
+// A~^T (one wave): A~_ij = (k~_i . k~_j) exp(lgn_i - lgn_j) for j < i inside
+// one noisy block of a response row, stored transposed.
+template <int D, int LDX, int LDM>
+__device__ __forceinline__ void gram_ant(const u16 (*kn)[LDX], float (*at)[LDM], const float *lgn, int c0, int n,
+                                         int P, int B) {
+  const int lane = lane_id(), g4 = 4 * (lane >> 4), cl = lane & 15;
+  const int nt = B > 16 ? 3 : 2;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    if (t >= nt) break;
+    const int ti = t == 0 ? 0 : 1, tj = t == 1 ? 1 : 0;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    gemm_tile<true, D, RowU16, RowU16>(acc, &kn[0][0], LDX, 16 * ti, &kn[0][0], LDX, 16 * tj);
+    const int j = 16 * tj + cl;
+    const int pj = j - (j % B);
+    float o4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + g4 + r;
+      const bool resp = c0 + i < n && c0 + i >= P;
+      o4[r] = (resp && j < i && i - (i % B) == pj) ? acc[r] * __expf(lgn[i] - lgn[j]) : 0.f;
+    }
+    *reinterpret_cast<float4 *>(&at[j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
 }
 

@@ -132,6 +132,24 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// x from another lane of the same 16-lane row through the DPP network (no LDS
+// traffic): CTRL is a gfx9 DPP control code.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of x over the 16 lanes of this lane's DPP row (lanes 16q .. 16q + 15);
+// every lane of the row gets the total.  xor 1 and xor 2 inside each quad
+// (quad_perm), then the mirrored quad and the mirrored half-row.
+__device__ __forceinline__ float dpp_sum16(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror: quad 0 <-> quad 1, quad 2 <-> quad 3
+  x += dpp_f32<0x140>(x);  // row_mirror: lanes 0-7 <-> 15-8
+  return x;
+}
+
 // Output element coordinates of accumulator register r for this lane.
 __device__ __forceinline__ int acc_row(int r) { return 4 * (lane_id() >> 4) + r; }
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }

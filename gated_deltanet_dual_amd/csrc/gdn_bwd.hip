@@ -854,19 +854,33 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_kernel(BwdArgs a) {
 }
 
 template <typename IO, int D>
-static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
+static hipError_t launch_bwd_t(const BwdArgs &a_in, hipStream_t st) {
   using Cfg = BwdCfg<IO, D>;
+  BwdArgs a = a_in;
   const FwdArgs &f = a.f;
   const int pairs = f.num_docs * f.H;
   const int groups = (pairs + 7) / 8;
+  const int64_t slots = a.T / Cfg::C + f.num_docs;
+  a.tri = reinterpret_cast<float *>(a.workspace) + (size_t)slots * f.H * D * D;
+  if constexpr (std::is_same<IO, u16>::value && D == 128) {
+    if (slots > 0) {
+      TimedLaunch tl(K_BWD_TRI, st);
+      hipError_t e0 = launch_tri_d128(a, st, slots);
+      if (e0 != hipSuccess) return e0;
+    }
+  }
   {
     TimedLaunch tl(K_BWD_SCAN, st);
-    hipLaunchKernelGGL((gdn_bwd_scan_kernel<IO, D>), dim3((unsigned)(groups * 8 * Cfg::NTILE)), dim3(256), 0,
-                       st, a);
+    if constexpr (std::is_same<IO, u16>::value && D == 128) {
+      hipError_t e1 = launch_bwd_scan_d128(a, st);
+      if (e1 != hipSuccess) return e1;
+    } else {
+      hipLaunchKernelGGL((gdn_bwd_scan_kernel<IO, D>), dim3((unsigned)(groups * 8 * Cfg::NTILE)), dim3(256), 0,
+                         st, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t slots = a.T / Cfg::C + f.num_docs;
   if (slots > 0) {
     TimedLaunch tl(K_BWD_CHUNK, st);
     if constexpr (std::is_same<IO, u16>::value && D == 128) return launch_bwd_chunk_d128(a, st, slots);

@@ -40,7 +40,6 @@ struct Chunk2Smem {
   alignas(16) u16 x[4][kC][kLDX];       // q, k, q~, k~ ; at the end the staging of dq, dk, dq~, dk~
   alignas(16) float cc[8][kC][kLDM];    // unweighted masked Grams (A, A~ transposed), T, T~; later dG
   alignas(16) float arr[4][kC][kLDA];   // U, u~, drhs, drhs~ for the d_v reductions
-  alignas(16) float tmp[2][16][17];
   alignas(16) float lg[kC], beta[kC], lgn[kC], betan[kC];
   alignas(16) float part[kNW][P_NUM][kC];  // per-wave gate-gradient partials
   alignas(16) float plgc[kNW];
@@ -48,21 +47,34 @@ struct Chunk2Smem {
 };
 
 // 16-byte row fragment of a [T, H, D] bf16 tensor straight from global memory:
-// rows c0 + row0 + (l & 15), columns k0 + 8 (l >> 4) .. +7; rows past the
-// document end (or noisy prompt rows when noisy) read as zero.
-__device__ __forceinline__ bf16x8 gfrag_rows(const u16 *src, int H, int h, int64_t t0g, int c0, int n, int P,
-                                             bool noisy, int row0, int k0) {
+// rows c0 + row0 + (l & 15), columns k0 + 8 (l >> 4) .. +7.  The load is
+// unconditional, from a row clamped into the document, and its value is left
+// untouched (no wait); frag_mask zeroes rows past the document end (and noisy
+// prompt rows when noisy) when it is consumed.
+__device__ __forceinline__ uint4 gfrag_raw(const u16 *src, int H, int h, int64_t t0g, int c0, int n, int row0,
+                                          int k0) {
   const int l = lane_id();
   const int tpos = c0 + row0 + (l & 15);
+  return *reinterpret_cast<const uint4 *>(src + ((t0g + min(tpos, n - 1)) * H + h) * kD + k0 + 8 * (l >> 4));
+}
+__device__ __forceinline__ bf16x8 frag_mask(const uint4 &v, int c0, int n, int P, bool noisy, int row0) {
+  const int tpos = c0 + row0 + (lane_id() & 15);
   const bool ok = tpos < n && (!noisy || tpos >= P);
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (ok) v = *reinterpret_cast<const uint4 *>(src + ((t0g + tpos) * H + h) * kD + k0 + 8 * (l >> 4));
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(bf16x8, ok ? v : make_uint4(0u, 0u, 0u, 0u));
 }
 
-// Slab (accumulator layout) of columns [col0, col0 + 16) of a [T, H, D] bf16 tensor.
-__device__ __forceinline__ Slab gslab(const u16 *src, int H, int h, int64_t t0g, int c0, int n, int P, bool noisy,
-                                      int col0) {
+// Slab (accumulator layout) of columns [col0, col0 + 16) of a [T, H, D] bf16
+// tensor: raw bits loaded from rows clamped into the document, then masked and
+// converted by slab_mask when consumed.
+__device__ __forceinline__ void gslab_raw(u16 (&dst)[2][4], const u16 *src, int H, int h, int64_t t0g, int c0,
+                                          int n, int col0) {
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dst[tr][r] = src[((t0g + min(c0 + slab_row(tr, r), n - 1)) * H + h) * kD + col0 + acc_col()];
+}
+__device__ __forceinline__ Slab slab_mask(const u16 (&raw)[2][4], int c0, int n, int P, bool noisy) {
   Slab s;
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
@@ -70,19 +82,9 @@ __device__ __forceinline__ Slab gslab(const u16 *src, int H, int h, int64_t t0g,
     for (int r = 0; r < 4; ++r) {
       const int tpos = c0 + slab_row(tr, r);
       const bool ok = tpos < n && (!noisy || tpos >= P);
-      s.t[tr][r] = ok ? bf2f(src[((t0g + tpos) * H + h) * kD + col0 + acc_col()]) : 0.f;
+      s.t[tr][r] = ok ? bf2f(raw[tr][r]) : 0.f;
     }
   return s;
-}
-
-// fp32 row fragment of a [D][D] state straight from global memory: rows
-// row0 + (l & 15), columns k0 + 8 (l >> 4) .. +7, split hi + lo.
-__device__ __forceinline__ void gstate_rows(const float *S, int row0, int k0, bf16x8 &hi, bf16x8 &lo) {
-  const int l = lane_id();
-  const float4 *p = reinterpret_cast<const float4 *>(S + (size_t)(row0 + (l & 15)) * kD + k0 + 8 * (l >> 4));
-  const float4 a = p[0], b = p[1];
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  split8(x, hi, lo);
 }
 
 }  // namespace
@@ -96,17 +98,10 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   const int H = f.H;
   const int slot = blockIdx.x / H, h = blockIdx.x % H;
 
-  // slot -> (document, chunk): slots of document i start at floor(cu_i / C) + i
-  int lo = 0, hi = f.num_docs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)f.cu[mid] / C + mid <= slot) lo = mid; else hi = mid - 1;
-  }
-  const int doc = lo;
+  int doc, c;
+  if (!slot_to_chunk(f, slot, doc, c)) return;
   const int64_t t0g = f.cu[doc];
   const int n = f.cu[doc + 1] - f.cu[doc];
-  const int c = slot - (int)(t0g / C) - doc;
-  if (c < 0 || c * C >= n) return;
   const int P = f.plen[doc];
   const int B = f.B;
   const int c0 = c * C;
@@ -121,29 +116,31 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   const int col0 = 16 * wave;  // this wave's d_v slab (phase 1) and d_k tile (phase 2)
 
   // ================================================================ phase 0
-  for (int e = tid; e < 8 * C * LDM; e += NT) (&sm.cc[0][0][0])[e] = 0.f;
-  for (int e = tid; e < kNW * P_NUM * C; e += NT) (&sm.part[0][0][0])[e] = 0.f;
-  {
-    constexpr int RU = D / 8, PU = C * RU;  // 16-byte units per row / per tile
-    for (int u = tid; u < 4 * PU; u += NT) {
-      const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
-      const int tpos = c0 + row;
-      const bool ok = tpos < n && (m < 2 || tpos >= P);
-      const u16 *src = m == 0 ? pq : m == 1 ? pk : m == 2 ? pqn : pkn;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) val = *reinterpret_cast<const uint4 *>(src + ((t0g + tpos) * H + h) * D + cu16 * 8);
-      *reinterpret_cast<uint4 *>(&sm.x[m][row][cu16 * 8]) = val;
-    }
+  // every global load of the phase first, so they are all in flight together:
+  // q, k, q~, k~ rows (4 16-byte units per thread), gates, T and T~ (one float4
+  // per thread), this wave's v, v~, do, do~ columns and S_c, dS' columns.
+  constexpr int RU = D / 8, PU = C * RU, UX = 4 * PU / NT;
+  uint4 xr[UX];
+#pragma unroll
+  for (int e = 0; e < UX; ++e) {
+    const int u = e * NT + tid;
+    const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
+    const int tpos = c0 + row;
+    const bool ok = tpos < n && (m < 2 || tpos >= P);
+    const u16 *src = m == 0 ? pq : m == 1 ? pk : m == 2 ? pqn : pkn;
+    const uint4 v = *reinterpret_cast<const uint4 *>(src + ((t0g + min(tpos, n - 1)) * H + h) * D + cu16 * 8);
+    xr[e] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
   }
-  load_gates(f, t0g, c0, n, P, h, B, sm.lg, sm.beta, sm.lgn, sm.betan);
-
-  // this wave's slab inputs (global -> registers, in flight during the Grams)
-  const Slab V = gslab(pv, H, h, t0g, c0, n, P, false, col0);
-  const Slab VN = gslab(pvn, H, h, t0g, c0, n, P, true, col0);
-  const Slab DO = gslab(pdo, H, h, t0g, c0, n, P, false, col0);
-  const Slab DON = gslab(pdon, H, h, t0g, c0, n, P, true, col0);
-  // S_c and dS' columns of the slab (k = 32 ks + 8 g + e over d_k), loaded now
-  // and converted to B fragments after the Gram phase, so the loads overlap it
+  const float gval = tid < 4 * C ? gate_load(f, t0g, c0, n, P, h, tid) : 0.f;
+  const float4 tri4 =
+      *reinterpret_cast<const float4 *>(a.tri + ((size_t)slot * H + h) * 2 * C * C + 4 * tid);  // 2 C^2 = 4 NT
+  u16 rv[2][4], rvn[2][4], rdo[2][4], rdon[2][4];
+  gslab_raw(rv, pv, H, h, t0g, c0, n, col0);
+  gslab_raw(rvn, pvn, H, h, t0g, c0, n, col0);
+  gslab_raw(rdo, pdo, H, h, t0g, c0, n, col0);
+  gslab_raw(rdon, pdon, H, h, t0g, c0, n, col0);
+  // S_c and dS' columns of the slab (k = 32 ks + 8 g + e over d_k), converted to
+  // B fragments after the Gram phase
   float xs[4][8], xd[4][8];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -153,10 +150,24 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       xs[ks][e] = Sc[off];
       xd[ks][e] = dSn[off];
     }
+  // LDS: zero the Gram matrices and partials, then the loaded rows, T, T~, gates
+  for (int e = tid; e < 8 * C * LDM; e += NT) (&sm.cc[0][0][0])[e] = 0.f;
+  for (int e = tid; e < kNW * P_NUM * C; e += NT) (&sm.part[0][0][0])[e] = 0.f;
+  lds_barrier();
+#pragma unroll
+  for (int e = 0; e < UX; ++e) {
+    const int u = e * NT + tid;
+    const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
+    *reinterpret_cast<uint4 *>(&sm.x[m][row][cu16 * 8]) = xr[e];
+  }
+  {
+    const int which = tid / (C * C / 4), rr = tid % (C * C / 4), row = rr / (C / 4), c4 = rr % (C / 4);
+    *reinterpret_cast<float4 *>(&sm.cc[which ? CC_TN : CC_T][row][4 * c4]) = tri4;
+  }
+  if (tid < 4 * C) gate_scan(gval, B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   lds_barrier();
   if (wave < 4)
     chunk_grams<true, D, LDX, LDM>(sm.x, sm.cc, sm.lg, sm.beta, sm.lgn, sm.betan, c0, n, P, B, has_noisy, false);
-  lds_barrier();
 
   const float lgC = sm.lg[C - 1];
   auto Gm = [&](int i) { return __expf(sm.lg[i]); };
@@ -165,6 +176,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   auto Dd = [&](int i) { return sm.beta[i] * __expf(lgC - sm.lg[i]); };
   auto resp_row = [&](int i) { return c0 + i < n && c0 + i >= P; };
 
+  const Slab V = slab_mask(rv, c0, n, P, false), VN = slab_mask(rvn, c0, n, P, true);
+  const Slab DO = slab_mask(rdo, c0, n, P, false), DON = slab_mask(rdon, c0, n, P, true);
   bf16x8 sbh[4], sbl[4], dbh[4], dbl[4];
   float plg = 0.f;  // <dS', S_c> over this slab, fp32
 #pragma unroll
@@ -175,10 +188,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     split8(xd[ks], dbh[ks], dbl[ks]);
   }
 
-  // ---- X S_c and K dS' products (need no solve): waves 0, 1 solve first
-  if (wave == 0) solve_unit_lower<LDM>(&sm.cc[CC_AT][0][0], &sm.cc[CC_T][0][0], &sm.tmp[0][0][0], true, sm.beta);
-  if (wave == 1 && has_noisy)
-    solve_unit_lower<LDM>(&sm.cc[CC_ANT][0][0], &sm.cc[CC_TN][0][0], &sm.tmp[1][0][0], B > 16, sm.betan);
+  // ---- X S_c and K dS' products
   Slab KS = slab_zero(), QS = slab_zero(), QNS = slab_zero(), KNS = slab_zero(), KD = slab_zero();
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
@@ -200,7 +210,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         mma_bf16(KNS.t[tr], akn, sbl[ks]);
       }
     }
-  lds_barrier();  // T, T~ visible
+  lds_barrier();  // the Gram matrices visible
 
   // ================================================================ phase 1
   float pg[2][4], pgn[2][4], pb[2][4], pgp[2][4], pge[2][4], pc[2][4];
@@ -350,9 +360,39 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
     if (lane == 0) sm.plgc[wave] = __expf(lgC) * t;
   }
+  // ---- phase 2's do, do~ row fragments (rows 16 tr .., k-step ks over d_v),
+  // issued after the phase-1 values are stored, so they arrive during the barrier
+  uint4 rfdo[2][4], rfdon[2][4];
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      rfdo[tr][ks] = gfrag_raw(pdo, H, h, t0g, c0, n, 16 * tr, 32 * ks);
+      rfdon[tr][ks] = gfrag_raw(pdon, H, h, t0g, c0, n, 16 * tr, 32 * ks);
+    }
+
+  // rows [16 wave, 16 wave + 16) of S_c and dS' for the d_k tile of dq..dk~,
+  // raw fp32, in flight during the Gram adjoints
+  float4 rsc[4][2], rds[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const size_t off = (size_t)(col0 + cl) * D + 32 * ks + 2 * g4;
+    rsc[ks][0] = *reinterpret_cast<const float4 *>(Sc + off);
+    rsc[ks][1] = *reinterpret_cast<const float4 *>(Sc + off + 4);
+    rds[ks][0] = *reinterpret_cast<const float4 *>(dSn + off);
+    rds[ks][1] = *reinterpret_cast<const float4 *>(dSn + off + 4);
+  }
   lds_barrier();
 
   // ================================================================ phase 2
+  bf16x8 fdo[2][4], fdon[2][4];
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      fdo[tr][ks] = frag_mask(rfdo[tr][ks], c0, n, P, false, 16 * tr);
+      fdon[tr][ks] = frag_mask(rfdon[tr][ks], c0, n, P, true, 16 * tr);
+    }
   // Gram adjoints: 6 matrices x 4 tiles, tile t = wave + 8 j -> (m = t / 4, ti, tj)
   enum { DM_O = 0, DM_Q, DM_K, DM_N, DM_A, DM_AN };
   floatx4 dM[3];
@@ -369,7 +409,10 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         bf16x8 bh, bl;
         frag_f32_split(&sm.arr[right][0][0], LDA, 16 * tj, 32 * ks, bh, bl);
         if (m == DM_O || m == DM_Q || m == DM_N) {  // left operand do / do~ (exact bf16)
-          const bf16x8 ah = gfrag_rows(m == DM_O ? pdo : pdon, H, h, t0g, c0, n, P, m != DM_O, 16 * ti, 32 * ks);
+          // ti is wave-dependent: select between registers, never index them
+          const bf16x8 a0 = m == DM_O ? fdo[0][ks] : fdon[0][ks];
+          const bf16x8 a1 = m == DM_O ? fdo[1][ks] : fdon[1][ks];
+          const bf16x8 ah = ti == 0 ? a0 : a1;
           mma_bf16(acc, ah, bh);
           mma_bf16(acc, ah, bl);
         } else {
@@ -405,11 +448,17 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 sh, sl, dh, dl;
-      gstate_rows(Sc, col0, 32 * ks, sh, sl);
-      gstate_rows(dSn, col0, 32 * ks, dh, dl);
+      {
+        const float x0[8] = {rsc[ks][0].x, rsc[ks][0].y, rsc[ks][0].z, rsc[ks][0].w,
+                             rsc[ks][1].x, rsc[ks][1].y, rsc[ks][1].z, rsc[ks][1].w};
+        const float x1[8] = {rds[ks][0].x, rds[ks][0].y, rds[ks][0].z, rds[ks][0].w,
+                             rds[ks][1].x, rds[ks][1].y, rds[ks][1].z, rds[ks][1].w};
+        split8(x0, sh, sl);
+        split8(x1, dh, dl);
+      }
 #pragma unroll
       for (int tr = 0; tr < 2; ++tr) {
-        const bf16x8 ado = gfrag_rows(pdo, H, h, t0g, c0, n, P, false, 16 * tr, 32 * ks);
+        const bf16x8 ado = fdo[tr][ks];
         mma_bf16(a_dq[tr], ado, sh);
         mma_bf16(a_dq[tr], ado, sl);
         bf16x8 ah, al;
@@ -422,7 +471,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         mma_bf16(a_dk2[tr], ah, dl);
         mma_bf16(a_dk2[tr], al, dh);
         if (has_noisy) {
-          const bf16x8 adon = gfrag_rows(pdon, H, h, t0g, c0, n, P, true, 16 * tr, 32 * ks);
+          const bf16x8 adon = fdon[tr][ks];
           mma_bf16(a_dqn[tr], adon, sh);
           mma_bf16(a_dqn[tr], adon, sl);
           frag_f32_split(&sm.arr[A_DRN][0][0], LDA, 16 * tr, 32 * ks, ah, al);

@@ -101,10 +101,6 @@ __device__ __forceinline__ void gemm_tile(floatx4 &acc, const void *A, int lda, 
 
 // Sum of x over the 16 lanes that share an accumulator row group (the 16
 // columns of a 16x16 tile); every lane of the group gets the total.
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
+__device__ __forceinline__ float sum16(float x) { return dpp_sum16(x); }
 
 }  // namespace flare

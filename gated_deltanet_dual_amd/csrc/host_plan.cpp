@@ -91,9 +91,12 @@ int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride) {
 }
 
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
-  // the end-state adjoint of every chunk, fp32, in the checkpoint slot layout
-  // (stride 1), written by the reverse scan and read by the per-chunk pass
-  return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * s->d_k * s->d_v * sizeof(float) + 256;
+  // per chunk slot and head, fp32, in the checkpoint slot layout (stride 1):
+  // the chunk's end-state adjoint (d_k x d_v), written by the reverse scan and
+  // read by the per-chunk pass, then the two unit-triangular inverses T, T~
+  // (kChunk x kChunk each), written by the solve pass and read by both
+  const size_t per = (size_t)s->d_k * s->d_v + 2 * kChunk * kChunk;
+  return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float) + 256;
 }
 
 flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,

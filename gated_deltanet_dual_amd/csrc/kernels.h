@@ -45,12 +45,17 @@ struct BwdArgs {
   const float *dh_final;
   void *dq, *dk, *dv, *dqn, *dkn, *dvn;
   float *dalpha, *dbeta, *dalpha_n, *dbeta_n, *dh0;
-  void *workspace;
+  void *workspace;       // end-state adjoints [slots][H][D][D], then `tri`
   size_t workspace_bytes;
   int64_t T;
+  float *tri;            // T, T~ per slot and head [slots][H][2][32][32] (set by the launcher)
 };
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
 // per-chunk backward kernel for bf16 io at d = 128 (gdn_bwd_chunk.hip)
 hipError_t launch_bwd_chunk_d128(const BwdArgs &a, hipStream_t st, int64_t slots);
+// reverse scan of the state adjoint for bf16 io at d = 128 (gdn_bwd_scan.hip)
+hipError_t launch_bwd_scan_d128(const BwdArgs &a, hipStream_t st);
+// the chunk solves T, T~ into a.tri for bf16 io at d = 128 (gdn_tri.hip)
+hipError_t launch_tri_d128(const BwdArgs &a, hipStream_t st, int64_t slots);
 
 }  // namespace flare

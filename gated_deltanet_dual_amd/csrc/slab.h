@@ -101,10 +101,6 @@ __device__ __forceinline__ void cc_mul(Slab &out, const float *M, int ld, const 
 }
 
 // Sum of x over the 16 lanes that share an accumulator row group.
-__device__ __forceinline__ float row_sum16(float x) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
+__device__ __forceinline__ float row_sum16(float x) { return dpp_sum16(x); }
 
 }  // namespace flare

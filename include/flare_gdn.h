@@ -214,7 +214,8 @@ int32_t flare_version(void);
  * duration of each kernel is known even when one entry point launches several
  * (the backward launches the reverse scan, then the per-chunk kernel).
  * Kernel names: "gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel",
- * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel".
+ * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel",
+ * "gdn_tri_kernel" (the backward's chunk solves, bf16 io at d = 128).
  * flare_timing_enable(1) turns it on (events are created lazily, host side
  * only; no device memory is allocated), (0) off.  Returns the previous state.
  * flare_timing_avg_ms() blocks until the recorded launches of that kernel
