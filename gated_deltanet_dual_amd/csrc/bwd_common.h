@@ -270,4 +270,77 @@ __device__ __forceinline__ void gram_ant(const u16 (*kn)[LDX], float (*at)[LDM],
   }
 }
 
+// The weighted masked Grams of a chunk (write strengths folded in), split over
+// two waves: wave 0 Mwo and Mwq, wave 1 Mwk and Mw~.  x holds the rows of q, k,
+// q~, k~; tiles that stay zero (above the diagonal, across noisy blocks) are
+// not written, so the outputs must start zeroed.
+//   Mwo[i][j] = (q_i . k_j) G_i / G_j b_j              j <= i
+//   Mwq[i][j] = (q~_i . k_j) G_{p_i - 1} / G_j b_j     j < p_i, response row i
+//   Mwk[i][j] = (k~_i . k_j) G_{p_i - 1} / G_j b_j     j < p_i, response row i
+//   Mw~[i][j] = (q~_i . k~_j) G~_e(i) / G~_j b~_j       j in the block of i, response row i
+template <int D, int LDX, int LDM>
+__device__ __forceinline__ void grams_weighted(int wave, const u16 (*x)[32][LDX], float (*mo)[LDM],
+                                               float (*mq)[LDM], float (*mk)[LDM], float (*mn)[LDM],
+                                               const float *lg, const float *beta, const float *lgn,
+                                               const float *betan, int c0, int n, int P, int B, bool has_noisy) {
+  const int lane = lane_id(), g4 = 4 * (lane >> 4), cl = lane & 15;
+  const int ti_t[3] = {0, 1, 1}, tj_t[3] = {0, 0, 1};
+  if (wave == 0) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int ti = ti_t[t], tj = tj_t[t];
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      gemm_tile<true, D, RowU16, RowU16>(acc, &x[1][0][0], LDX, 16 * tj, &x[0][0][0], LDX, 16 * ti);
+      const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r;
+        o4[r] = j <= i ? acc[r] * __expf(lg[i] - lg[j]) * beta[j] : 0.f;
+      }
+      *reinterpret_cast<float4 *>(&mo[i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    }
+  }
+  if (!has_noisy) return;
+  const int xm = wave == 0 ? 2 : 3;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int ti = ti_t[t], tj = tj_t[t];
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    gemm_tile<true, D, RowU16, RowU16>(acc, &x[1][0][0], LDX, 16 * tj, &x[xm][0][0], LDX, 16 * ti);
+    const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+    const int pi = i - (i % B);
+    const bool resp = c0 + i < n && c0 + i >= P;
+    const float lgp = pi > 0 ? lg[pi - 1] : 0.f;
+    float o4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + r;
+      o4[r] = (resp && j < pi) ? acc[r] * __expf(lgp - lg[j]) * beta[j] : 0.f;
+    }
+    *reinterpret_cast<float4 *>(&(wave == 0 ? mq : mk)[i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+  }
+  if (wave == 1) {
+    const int nt = B > 16 ? 4 : 2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t >= nt) break;
+      const int ti = (t == 0 || t == 2) ? 0 : 1, tj = (t == 0 || t == 3) ? 0 : 1;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      gemm_tile<true, D, RowU16, RowU16>(acc, &x[3][0][0], LDX, 16 * tj, &x[2][0][0], LDX, 16 * ti);
+      const int i = 16 * ti + cl, j0 = 16 * tj + g4;
+      const int pi = i - (i % B);
+      const bool resp = c0 + i < n && c0 + i >= P;
+      const float lge = lgn[pi + B - 1];
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r;
+        o4[r] = (resp && j >= pi && j < pi + B) ? acc[r] * __expf(lge - lgn[j]) * betan[j] : 0.f;
+      }
+      *reinterpret_cast<float4 *>(&mn[i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    }
+  }
+}
+
 }  // namespace flare

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   }
   const float gval = tid < 4 * C ? gate_load(f, t0g, c0, n, P, h, tid) : 0.f;
   const float4 tri4 =
-      *reinterpret_cast<const float4 *>(a.tri + ((size_t)slot * H + h) * 2 * C * C + 4 * tid);  // 2 C^2 = 4 NT
+      *reinterpret_cast<const float4 *>(a.tri + ((size_t)slot * H + h) * 6 * C * C + 4 * tid);  // T, T~: 4 NT
   u16 rv[2][4], rvn[2][4], rdo[2][4], rdon[2][4];
   gslab_raw(rv, pv, H, h, t0g, c0, n, col0);
   gslab_raw(rvn, pvn, H, h, t0g, c0, n, col0);

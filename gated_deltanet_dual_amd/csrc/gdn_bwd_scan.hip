@@ -14,9 +14,10 @@
 // every C x 16 quantity of a chunk is a register slab (slab.h).  K dS' takes
 // dS straight from the accumulators as its B operand; dS += X^T Y takes X^T
 // from a transposed copy of the chunk's q/k rows kept in LDS.  T and T~ come
-// precomputed from the chunk-solve kernel, so no triangular solve sits on the
-// sequential chain, and the next chunk's rows, T, T~, gates and do/do~
-// columns are fetched into registers while the current chunk computes.
+// precomputed, with the weighted Gram matrices, by the chunk-matrix kernel
+// (gdn_tri.hip), so neither a solve nor a Gram sits on the sequential chain;
+// the next chunk's rows, those six matrices, gates and do/do~ columns are
+// fetched into registers while the current chunk computes.
 #include "bwd_common.h"
 #include "device_common.h"
 #include "gemm_lds.h"
@@ -28,13 +29,13 @@ namespace flare {
 namespace {
 
 constexpr int sC = 32, sD = 128, sNW = 2, sNT = 64 * sNW, sQ = 4;  // quarters per (doc, head)
-constexpr int sLDX = sD + 8, sLDT = sC + 8, sLDM = sC + 4;
-enum { SC_MO = 0, SC_MQ, SC_MK, SC_MN, SC_T, SC_TN };
+constexpr int sLDX = sD + 8, sLDT = sC + 4, sLDM = sC + 4;
+enum { SC_T = 0, SC_TN, SC_MO, SC_MQ, SC_MK, SC_MN };  // the chunk-matrix pass's order
 
 struct ScanSmem2 {
   alignas(16) u16 xr[4][sC][sLDX];  // q, k, q~, k~ rows
   alignas(16) u16 xt[4][sD][sLDT];  // the same, transposed ([d_k][chunk row])
-  alignas(16) float cc[6][sC][sLDM];  // Mwo, Mwq, Mwk, Mw~ (b folded), T, T~
+  alignas(16) float cc[6][sC][sLDM];  // T, T~, Mwo, Mwq, Mwk, Mw~ (b folded)
   alignas(16) float lg[sC], beta[sC], lgn[sC], betan[sC];
 };
 
@@ -43,8 +44,8 @@ struct ScanSmem2 {
 // instruction touches a loaded register before the next chunk (and nothing
 // waits for the loads early).
 struct ScanPrefetch {
-  uint4 x[4][4];  // [array][row rr]: rows 4 (t / 16) + rr, 16-byte unit t % 16
-  float4 tri[4];
+  uint4 x[4][4];  // [array][row rr]: rows 4 (t % 8) + rr, 16-byte unit t / 8
+  float4 tri[12];
   float gate;
   u16 dO[2][4], dOn[2][4];  // slab layout, bf16 bits
 };
@@ -98,7 +99,9 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
   };
 
   // ---- prefetch of chunk c into registers
-  const int prow = 4 * (tid >> 4), pu = tid & 15;  // 4 rows x one 16-byte unit per array
+  // 4 rows x one 16-byte unit per array; neighbouring lanes take neighbouring
+  // rows, so the transposed 8-byte LDS writes spread over the banks
+  const int prow = 4 * (tid & 7), pu = tid >> 3;
   // Loads are unconditional, from a row clamped into the document (always in
   // bounds), and masked afterwards: a load under a branch would make the
   // compiler wait for it, and for every load issued before it.
@@ -128,9 +131,9 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         pf.x[m][rr] = *reinterpret_cast<const uint4 *>(px[m] + ((t0g + min(c0 + prow + rr, n - 1)) * H + h) * D + 8 * pu);
-    const float *tri = a.tri + ((size_t)(ck_base + c) * H + h) * 2 * C * C;
+    const float *tri = a.tri + ((size_t)(ck_base + c) * H + h) * 6 * C * C;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pf.tri[j] = *reinterpret_cast<const float4 *>(tri + 4 * (j * NT + tid));
+    for (int j = 0; j < 12; ++j) pf.tri[j] = *reinterpret_cast<const float4 *>(tri + 4 * (j * NT + tid));
     pf.gate = gate_load_raw(f, t0g, c0, n, h, tid);
     slab_raw(pf.dO, pdo, c0);
     slab_raw(pf.dOn, pdon, c0);
@@ -160,17 +163,12 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 12; ++j) {
       const int u = j * NT + tid, which = u / (C * C / 4), rr = u % (C * C / 4);
-      *reinterpret_cast<float4 *>(&sm.cc[which ? SC_TN : SC_T][rr / (C / 4)][4 * (rr % (C / 4))]) = pf.tri[j];
+      *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = pf.tri[j];
     }
     gate_scan(gate_fix(pf.gate, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   };
-
-  // tiles of the Gram matrices that no chunk writes (above the diagonal, and
-  // across noisy blocks) must read as zero: clear them once (ordered before
-  // their first use by the loop's first barrier)
-  for (int e = tid; e < 4 * C * LDM; e += NT) (&sm.cc[0][0][0])[e] = 0.f;
 
   ScanPrefetch pf;
   if (nchunks > 0) prefetch(pf, nchunks - 1);
@@ -184,71 +182,6 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
     if (c > 0) prefetch(pf, c - 1);
     // the adjoint of this chunk's end state, for the per-chunk pass
     store_dS(ws + ((ck_base + c) * H + h) * (size_t)D * D);
-    lds_barrier();
-
-    // ---- weighted masked Grams: wave 0 Mwo, Mwq; wave 1 Mwk, Mw~
-    {
-      const int ti_t[3] = {0, 1, 1}, tj_t[3] = {0, 0, 1};
-      if (wave == 0) {
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {  // Mwo[i][j] = (q_i . k_j) G_i / G_j b_j, j <= i
-          const int ti = ti_t[t], tj = tj_t[t];
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-          gemm_tile<true, D, RowU16, RowU16>(acc, &sm.xr[1][0][0], LDX, 16 * tj, &sm.xr[0][0][0], LDX, 16 * ti);
-          const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-          float o4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            o4[r] = j <= i ? acc[r] * __expf(sm.lg[i] - sm.lg[j]) * sm.beta[j] : 0.f;
-          }
-          *reinterpret_cast<float4 *>(&sm.cc[SC_MO][i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
-        }
-      }
-      if (has_noisy) {
-        // wave 0: Mwq (x = q~), wave 1: Mwk (x = k~): [i][j] = (x_i . k_j) G_{p-1} / G_j b_j, j < p_i
-        const int xm = wave == 0 ? 2 : 3;
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          const int ti = ti_t[t], tj = tj_t[t];
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-          gemm_tile<true, D, RowU16, RowU16>(acc, &sm.xr[1][0][0], LDX, 16 * tj, &sm.xr[xm][0][0], LDX, 16 * ti);
-          const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-          const int pi = i - (i % B);
-          const bool resp = c0 + i < n && c0 + i >= P;
-          const float lgp = pi > 0 ? sm.lg[pi - 1] : 0.f;
-          float o4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            o4[r] = (resp && j < pi) ? acc[r] * __expf(lgp - sm.lg[j]) * sm.beta[j] : 0.f;
-          }
-          *reinterpret_cast<float4 *>(&sm.cc[wave == 0 ? SC_MQ : SC_MK][i][j0]) =
-              make_float4(o4[0], o4[1], o4[2], o4[3]);
-        }
-        if (wave == 1) {  // Mw~[i][j] = (q~_i . k~_j) G~_e / G~_j b~_j, same block
-          const int nt = B > 16 ? 4 : 2;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if (t >= nt) break;
-            const int ti = (t == 0 || t == 2) ? 0 : 1, tj = (t == 0 || t == 3) ? 0 : 1;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            gemm_tile<true, D, RowU16, RowU16>(acc, &sm.xr[3][0][0], LDX, 16 * tj, &sm.xr[2][0][0], LDX, 16 * ti);
-            const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-            const int pi = i - (i % B);
-            const bool resp = c0 + i < n && c0 + i >= P;
-            const float lge = sm.lgn[pi + B - 1];
-            float o4[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int j = j0 + r;
-              o4[r] = (resp && j >= pi && j < pi + B) ? acc[r] * __expf(lge - sm.lgn[j]) * sm.betan[j] : 0.f;
-            }
-            *reinterpret_cast<float4 *>(&sm.cc[SC_MN][i][j0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
-          }
-        }
-      }
-    }
     lds_barrier();
 
     const float lgC = sm.lg[C - 1];

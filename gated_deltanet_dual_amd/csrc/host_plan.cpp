@@ -93,9 +93,10 @@ int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride) {
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   // per chunk slot and head, fp32, in the checkpoint slot layout (stride 1):
   // the chunk's end-state adjoint (d_k x d_v), written by the reverse scan and
-  // read by the per-chunk pass, then the two unit-triangular inverses T, T~
-  // (kChunk x kChunk each), written by the solve pass and read by both
-  const size_t per = (size_t)s->d_k * s->d_v + 2 * kChunk * kChunk;
+  // read by the per-chunk pass, then six kChunk x kChunk chunk matrices (the
+  // triangular inverses T, T~ and four weighted Gram matrices), written by the
+  // chunk-matrix pass and read by both
+  const size_t per = (size_t)s->d_k * s->d_v + 6 * kChunk * kChunk;
   return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float) + 256;
 }
 

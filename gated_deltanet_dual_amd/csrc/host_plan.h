@@ -41,7 +41,7 @@ int64_t ckpt_slot(int32_t cu_i, int32_t doc, int32_t chunk, int32_t stride);
 int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride);
 
 // Bytes of bwd workspace: per chunk slot and head, the end-state adjoint and
-// the two triangular inverses T, T~ (checkpoint slot layout).
+// six chunk matrices (checkpoint slot layout).
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
 
 // Serving step: slots distinct and in range when the host copy is given.

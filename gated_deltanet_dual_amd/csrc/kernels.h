@@ -48,7 +48,7 @@ struct BwdArgs {
   void *workspace;       // end-state adjoints [slots][H][D][D], then `tri`
   size_t workspace_bytes;
   int64_t T;
-  float *tri;            // T, T~ per slot and head [slots][H][2][32][32] (set by the launcher)
+  float *tri;            // per slot and head [slots][H][6][32][32]: T, T~, Mwo, Mwq, Mwk, Mw~ (set by the launcher)
 };
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
 // per-chunk backward kernel for bf16 io at d = 128 (gdn_bwd_chunk.hip)

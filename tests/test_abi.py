@@ -92,8 +92,8 @@ def test_bwd_workspace_checked_before_launch(L):
     v = varlen([0, 40, 64], [8, 0])
     need = L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(shape), 1)
     # per chunk slot ((T/32 + N) slots) and head, fp32: the end-state adjoint
-    # (d x d) and the two 32 x 32 triangular inverses
-    assert need == (64 // 32 + 2) * 2 * (16 * 16 + 2 * 32 * 32) * 4 + 256
+    # (d x d) and six 32 x 32 chunk matrices
+    assert need == (64 // 32 + 2) * 2 * (16 * 16 + 6 * 32 * 32) * 4 + 256
     args = [FAKE] * 10 + [None, FAKE, 1, FAKE, FAKE, None] + [FAKE] * 10 + [None]
     st = L.flare_gdn_dual_bwd(ctypes.byref(v), ctypes.byref(shape), *args, FAKE, need - 1, None)
     assert st == 5
