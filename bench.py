@@ -48,6 +48,10 @@ FWD_BYTES_PER_TH = 3 * 256 + 8 + 256
 BWD_BYTES_PER_TH = 4 * 256 + 8 + 3 * 256 + 8
 # the reverse scan needs q, k, do and the gates of both streams (not v)
 SCAN_BYTES_PER_TH = 3 * 256 + 8
+# the chunk-matrix pass reads q, k and the gates of both streams and writes six
+# 32 x 32 fp32 matrices per (chunk slot, head)
+TRI_BYTES_PER_TH = 2 * 256 + 8
+TRI_BYTES_PER_SLOT_HEAD = 6 * 32 * 32 * 4
 
 
 def fwd_flops_per_th(d, C, B, noisy):
@@ -180,7 +184,8 @@ def main():
     C = g.chunk_size()
     n_slots = T // C + vl.num_docs
     ckpt = torch.empty((n_slots, H, d, d), dtype=torch.float32, device=dev)
-    g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False)
+    fws = torch.empty((max(g.workspace_bytes(vl, H, d, B, g.BF16), 256),), dtype=torch.uint8, device=dev)
+    g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
     ws = torch.empty((g.lib().flare_gdn_dual_workspace_size(vl.ref(), ctypes.byref(g._shape(H, d, B, g.BF16)), 1),),
                      dtype=torch.uint8, device=dev)
     grads = g.gdn_dual_bwd(vl, *args10, B, ckpt, do, don, workspace=ws)
@@ -191,7 +196,7 @@ def main():
     ckpt_bytes = n_slots * H * d * d * 4
 
     def step():
-        g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False)
+        g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
         g.gdn_dual_bwd(vl, *args10, B, ckpt, do, don, out=grads, workspace=ws)
 
     result = {}
@@ -209,13 +214,14 @@ def main():
         g.timing_enable(False)
         ms_step = timer.avg_ms("step")
         kern = {}
-        for name in ("gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel"):
+        for name in ("gdn_dual_fwd_kernel", "gdn_tri_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel"):
             ms, n = g.timing_avg_ms(name)
             kern[name] = {"ms": ms, "launches": n}
         g.timing_reset()
         alg = {
             "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
-            "gdn_bwd_scan_kernel": SCAN_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
+            "gdn_tri_kernel": TRI_BYTES_PER_TH * (th_total + th_resp) + TRI_BYTES_PER_SLOT_HEAD * n_slots * H,
+            "gdn_bwd_scan_kernel": SCAN_BYTES_PER_TH * (th_total + th_resp),
             "gdn_bwd_chunk_kernel": BWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
         }
         fwd_flops = fwd_flops_per_th(d, C, B, False) * th_total + fwd_flops_per_th(d, C, B, True) * th_resp
@@ -256,7 +262,7 @@ def main():
 
     comps = {}
     if not args.no_components and args.only in (None, "infer"):
-        comps["fwd_inference"] = bench_infer(torch, g, vl, args10, B, o, on, timer, args,
+        comps["fwd_inference"] = bench_infer(torch, g, vl, args10, B, o, on, fws, timer, args,
                                              th_total, th_resp, fwd_flops_per_th(d, C, B, False) * th_total
                                              + fwd_flops_per_th(d, C, B, True) * th_resp)
     if not args.no_components and args.only in (None, "serve"):
@@ -276,15 +282,15 @@ def main():
             f.write(line + "\n")
 
 
-def bench_infer(torch, g, vl, args10, B, o, on, timer, args, th_total, th_resp, flops):
+def bench_infer(torch, g, vl, args10, B, o, on, fws, timer, args, th_total, th_resp, flops):
     """The forward alone, inference mode (nothing saved)."""
     log("bench: forward, inference mode")
     for _ in range(args.warmup):
-        g.gdn_dual_fwd(vl, *args10, B, out=(o, on), want_h_final=False)
+        g.gdn_dual_fwd(vl, *args10, B, out=(o, on), want_h_final=False, workspace=fws)
     torch.cuda.synchronize()
     timer.clear()
     for _ in range(args.steps):
-        timer.run("infer", lambda: g.gdn_dual_fwd(vl, *args10, B, out=(o, on), want_h_final=False))
+        timer.run("infer", lambda: g.gdn_dual_fwd(vl, *args10, B, out=(o, on), want_h_final=False, workspace=fws))
     torch.cuda.synchronize()
     ms = timer.avg_ms("infer")
     alg = FWD_BYTES_PER_TH * (th_total + th_resp)

@@ -75,7 +75,7 @@ def lib():
     L.flare_gdn_dual_ckpt_size.restype = SZ
     L.flare_gdn_ckpt_slot.argtypes = [I32, I32, I32, I32]
     L.flare_gdn_ckpt_slot.restype = ctypes.c_int64
-    L.flare_gdn_dual_fwd.argtypes = [VP, SP] + [P] * 10 + [P, P, P, P, P, I32, P]
+    L.flare_gdn_dual_fwd.argtypes = [VP, SP] + [P] * 10 + [P, P, P, P, P, I32, P, SZ, P]
     L.flare_gdn_dual_fwd.restype = ctypes.c_int
     L.flare_gdn_dual_bwd.argtypes = [VP, SP] + [P] * 10 + [P, P, I32, P, P, P] + [P] * 11 + [P, SZ, P]
     L.flare_gdn_dual_bwd.restype = ctypes.c_int
@@ -170,10 +170,13 @@ def ckpt_slots(varlen: Varlen, H: int, d: int, B: int, io: int, stride: int = 1)
 
 
 def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,
-                 h0=None, scale=0.0, flags=0, want_h_final=True, want_ckpt=False, out=None, ckpt=None):
+                 h0=None, scale=0.0, flags=0, want_h_final=True, want_ckpt=False, out=None, ckpt=None,
+                 workspace=None):
     """Dual-stream forward.  q,k,qn,kn [T,H,d]; v,vn [T,H,d]; gates [T,H] fp32;
     h0 [N,H,d,d] fp32 or None.  `out` = (o, on) reuses output buffers, `ckpt`
-    a buffer for the chunk-start states (implies saving them).  Returns
+    a buffer for the chunk-start states (implies saving them), `workspace` a
+    uint8 device buffer of at least flare_gdn_dual_workspace_size(..., 0)
+    bytes (allocated here when needed and not given).  Returns
     (o, on, h_final, ckpt)."""
     torch = _torch()
     T, H, d = q.shape
@@ -191,10 +194,14 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
         if nbytes == 0:
             raise FlareError(2, "invalid arguments for the checkpoint size")
         ck = torch.empty((nbytes // (H * d * d * 4), H, d, d), dtype=torch.float32, device=q.device)
+    ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 0)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
     _check(lib().flare_gdn_dual_fwd(varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(alpha), _ptr(beta), _ptr(qn), _ptr(kn), _ptr(vn),
                                     _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(o), _ptr(on),
-                                    _ptr(hf), _ptr(ck), 1, _stream(q.device)))
+                                    _ptr(hf), _ptr(ck), 1, _ptr(workspace),
+                                    workspace.numel() if workspace is not None else 0, _stream(q.device)))
     return o, on, hf, ck
 
 
@@ -263,6 +270,13 @@ def shortconv_dual(varlen: Varlen, block_size, x, xn, weight, bias=None, activat
                                       _ptr(weight), _ptr(bias), int(activation), _ptr(y), _ptr(yn),
                                       _stream(x.device)))
     return y, yn
+
+
+def workspace_bytes(varlen: Varlen, H: int, d: int, block_size: int, io: int, flags: int = 0,
+                    for_bwd: bool = False) -> int:
+    """flare_gdn_dual_workspace_size for this batch and shape."""
+    return int(lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(_shape(H, d, block_size, io, flags)),
+                                                   1 if for_bwd else 0))
 
 
 def timing_enable(on: bool = True) -> bool:

@@ -34,7 +34,7 @@ size_t flare_gdn_dual_workspace_size(const flare_varlen *varlen, const flare_gdn
                                      int for_bwd) {
   VarlenInfo vi;
   if (check_fwd_common(varlen, shape, &vi) != FLARE_OK) return 0;
-  return for_bwd ? bwd_workspace_bytes(vi, shape) : 0;
+  return for_bwd ? bwd_workspace_bytes(vi, shape) : fwd_workspace_bytes(vi, shape);
 }
 
 size_t flare_gdn_dual_ckpt_size(const flare_varlen *varlen, const flare_gdn_shape *shape,
@@ -57,7 +57,8 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shap
                                 const float *beta, const void *qn, const void *kn, const void *vn,
                                 const float *alpha_n, const float *beta_n, const float *h0,
                                 void *o, void *on, float *h_final, float *ckpt,
-                                int32_t ckpt_stride_chunks, void *stream) {
+                                int32_t ckpt_stride_chunks, void *workspace, size_t workspace_bytes,
+                                void *stream) {
   clear_error();
   VarlenInfo vi;
   flare_status st = check_fwd_common(varlen, shape, &vi);
@@ -67,6 +68,11 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shap
   if (vi.total_tokens > 0 &&
       (!q || !k || !v || !alpha || !beta || !qn || !kn || !vn || !alpha_n || !beta_n || !o || !on))
     return fail(FLARE_ERR_NULL, "gdn_dual_fwd: a required pointer is NULL");
+  const size_t need = fwd_workspace_bytes(vi, shape);
+  if (vi.total_tokens > 0 && need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   FwdArgs a{};
   a.num_docs = varlen->num_docs;
   a.H = shape->num_heads;
@@ -81,6 +87,8 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shap
   a.q = q; a.k = k; a.v = v; a.qn = qn; a.kn = kn; a.vn = vn;
   a.alpha = alpha; a.beta = beta; a.alpha_n = alpha_n; a.beta_n = beta_n;
   a.h0 = h0; a.o = o; a.on = on; a.h_final = h_final; a.ckpt = ckpt;
+  a.workspace = need > 0 ? reinterpret_cast<float *>(workspace) : nullptr;
+  a.T = vi.total_tokens;
   return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd launch");
 }
 
@@ -125,6 +133,7 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
   a.f.q = q; a.f.k = k; a.f.v = v; a.f.qn = qn; a.f.kn = kn; a.f.vn = vn;
   a.f.alpha = alpha; a.f.beta = beta; a.f.alpha_n = alpha_n; a.f.beta_n = beta_n;
   a.f.h0 = h0;
+  a.f.T = vi.total_tokens;
   a.ckpt_in = ckpt;
   a.d_o = d_o; a.d_on = d_on; a.dh_final = dh_final;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dqn = dqn; a.dkn = dkn; a.dvn = dvn;

@@ -864,7 +864,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a_in, hipStream_t st) {
   a.tri = reinterpret_cast<float *>(a.workspace) + (size_t)slots * f.H * D * D;
   if constexpr (std::is_same<IO, u16>::value && D == 128) {
     if (slots > 0) {
-      TimedLaunch tl(K_BWD_TRI, st);
+      TimedLaunch tl(K_TRI, st);
       hipError_t e0 = launch_tri_d128(a, st, slots);
       if (e0 != hipSuccess) return e0;
     }

@@ -36,6 +36,8 @@ struct ScanSmem2 {
   alignas(16) u16 xr[4][sC][sLDX];  // q, k, q~, k~ rows
   alignas(16) u16 xt[4][sD][sLDT];  // the same, transposed ([d_k][chunk row])
   alignas(16) float cc[6][sC][sLDM];  // T, T~, Mwo, Mwq, Mwk, Mw~ (b folded)
+  alignas(16) u16 dob[2][sC][32 + 8];  // do, do~ columns of this quarter
+  alignas(16) float dst[sNW][sD][16 + 4];  // per-wave staging of the dS slab for 16-byte stores
   alignas(16) float lg[sC], beta[sC], lgn[sC], betan[sC];
 };
 
@@ -47,7 +49,7 @@ struct ScanPrefetch {
   uint4 x[4][4];  // [array][row rr]: rows 4 (t % 8) + rr, 16-byte unit t / 8
   float4 tri[12];
   float gate;
-  u16 dO[2][4], dOn[2][4];  // slab layout, bf16 bits
+  uint4 dob[2];  // do / do~ rows: unit (j * 128 + t) -> array, row, 16-byte unit of the quarter
 };
 
 }  // namespace
@@ -91,11 +93,20 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) dS[kt][r] = src[(size_t)(16 * kt + g4 + r) * D + dv0 + cl];
     }
   }
+  // the dS slab -> global through this wave's own LDS staging rows, so it
+  // leaves as 8 16-byte stores per lane instead of 32 scalar ones (few enough
+  // vector-memory operations in flight for the prefetch to be tracked exactly)
   auto store_dS = [&](float *dst) {
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kt + g4 + r) * D + dv0 + cl] = dS[kt][r];
+      for (int r = 0; r < 4; ++r) sm.dst[wave][16 * kt + g4 + r][cl] = dS[kt][r];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int u = j * 64 + lane, row = u >> 2, c4 = u & 3;
+      *reinterpret_cast<float4 *>(dst + (size_t)row * D + dv0 + 4 * c4) =
+          *reinterpret_cast<const float4 *>(&sm.dst[wave][row][4 * c4]);
+    }
   };
 
   // ---- prefetch of chunk c into registers
@@ -105,23 +116,13 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
   // Loads are unconditional, from a row clamped into the document (always in
   // bounds), and masked afterwards: a load under a branch would make the
   // compiler wait for it, and for every load issued before it.
-  auto slab_raw = [&](u16 (&dst)[2][4], const u16 *src, int c0) {
-#pragma unroll
-    for (int tr = 0; tr < 2; ++tr)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dst[tr][r] = src[((t0g + min(c0 + slab_row(tr, r), n - 1)) * H + h) * D + dv0 + cl];
-  };
-  auto slab_fix = [&](const u16 (&raw)[2][4], int c0, bool noisy) {
+  // do / do~ slab of this wave from the quarter's LDS rows
+  auto slab_lds = [&](int m) {
     Slab sl;
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tpos = c0 + slab_row(tr, r);
-        const bool ok = tpos < n && (!noisy || tpos >= P);
-        sl.t[tr][r] = ok ? bf2f(raw[tr][r]) : 0.f;
-      }
+      for (int r = 0; r < 4; ++r) sl.t[tr][r] = bf2f(sm.dob[m][slab_row(tr, r)][16 * wave + cl]);
     return sl;
   };
   auto prefetch = [&](ScanPrefetch &pf, int c) {
@@ -135,8 +136,12 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 12; ++j) pf.tri[j] = *reinterpret_cast<const float4 *>(tri + 4 * (j * NT + tid));
     pf.gate = gate_load_raw(f, t0g, c0, n, h, tid);
-    slab_raw(pf.dO, pdo, c0);
-    slab_raw(pf.dOn, pdon, c0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = (tid >> 2), un = tid & 3;
+      pf.dob[j] = *reinterpret_cast<const uint4 *>((j == 0 ? pdo : pdon) +
+                                                   ((t0g + min(c0 + row, n - 1)) * H + h) * D + 32 * quarter + 8 * un);
+    }
   };
   auto fill_lds = [&](const ScanPrefetch &pf, int c0) {
 #pragma unroll
@@ -168,6 +173,12 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
       *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = pf.tri[j];
     }
     gate_scan(gate_fix(pf.gate, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = tid >> 2, un = tid & 3, tpos = c0 + row;
+      const bool ok = tpos < n && (j == 0 || tpos >= P);
+      *reinterpret_cast<uint4 *>(&sm.dob[j][row][8 * un]) = ok ? pf.dob[j] : make_uint4(0u, 0u, 0u, 0u);
+    }
   };
 
   ScanPrefetch pf;
@@ -178,11 +189,12 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
     const bool has_noisy = (c0 + C > P) && (P < n);
     lds_barrier();  // every wave is done with the previous chunk's LDS
     fill_lds(pf, c0);
-    const Slab DO = slab_fix(pf.dO, c0, false), DON = slab_fix(pf.dOn, c0, true);
-    if (c > 0) prefetch(pf, c - 1);
-    // the adjoint of this chunk's end state, for the per-chunk pass
+    // the adjoint of this chunk's end state, for the per-chunk pass (issued
+    // before the next prefetch, so waiting for that prefetch never waits on it)
     store_dS(ws + ((ck_base + c) * H + h) * (size_t)D * D);
+    if (c > 0) prefetch(pf, c - 1);
     lds_barrier();
+    const Slab DO = slab_lds(0), DON = slab_lds(1);
 
     const float lgC = sm.lg[C - 1];
     // ---- the column-separable chain of this slab
@@ -266,19 +278,31 @@ __global__ __launch_bounds__(sNT) void gdn_bwd_scan_d128_kernel(BwdArgs a) {
       slab_b_split(Y2, yh[2], yl[2]);
       slab_b_split(Y3, yh[3], yl[3]);
     }
+    // A = X^T from the transposed rows (k-slots in the slab permutation); the
+    // noisy terms in a loop of their own, so each loop is one basic block
+    auto xt_frag = [&](int xm, int kt) {
+      const u16 *col = &sm.xt[xm][16 * kt + cl][0];
+      const uint2 lo4 = *reinterpret_cast<const uint2 *>(col + g4);
+      const uint2 hi4 = *reinterpret_cast<const uint2 *>(col + 16 + g4);
+      return __builtin_bit_cast(bf16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+    };
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       dS[kt] *= gC;
+      const bf16x8 aq = xt_frag(0, kt), ak = xt_frag(1, kt);  // Y1 <- q, Y4 <- k
+      mma_bf16(dS[kt], aq, yh[0]);
+      mma_bf16(dS[kt], aq, yl[0]);
+      mma_bf16(dS[kt], ak, yh[1]);
+      mma_bf16(dS[kt], ak, yl[1]);
+    }
+    if (has_noisy) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (m >= 2 && !has_noisy) continue;
-        const int xm = m == 0 ? 0 : m == 1 ? 1 : m;  // Y1 <- q, Y4 <- k, Y2 <- q~, Y3 <- k~
-        const u16 *col = &sm.xt[xm][16 * kt + cl][0];
-        const uint2 lo4 = *reinterpret_cast<const uint2 *>(col + g4);
-        const uint2 hi4 = *reinterpret_cast<const uint2 *>(col + 16 + g4);
-        const bf16x8 ax = __builtin_bit_cast(bf16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-        mma_bf16(dS[kt], ax, yh[m]);
-        mma_bf16(dS[kt], ax, yl[m]);
+      for (int kt = 0; kt < 8; ++kt) {
+        const bf16x8 aqn = xt_frag(2, kt), akn = xt_frag(3, kt);  // Y2 <- q~, Y3 <- k~
+        mma_bf16(dS[kt], aqn, yh[2]);
+        mma_bf16(dS[kt], aqn, yl[2]);
+        mma_bf16(dS[kt], akn, yh[3]);
+        mma_bf16(dS[kt], akn, yl[3]);
       }
     }
   }

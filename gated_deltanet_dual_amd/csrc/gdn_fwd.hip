@@ -715,6 +715,21 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
 
 hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st) {
   if (a.num_docs == 0) return hipSuccess;
+  if (a.workspace) {
+    // bf16, d = 128, no flags: chunk matrices in parallel, then the march
+    const int64_t slots = a.T / 32 + a.num_docs;
+    BwdArgs b{};
+    b.f = a;
+    b.T = a.T;
+    b.tri = a.workspace;
+    if (slots > 0) {
+      TimedLaunch tl(K_TRI, st);
+      hipError_t e = launch_tri_d128(b, st, slots);
+      if (e != hipSuccess) return e;
+    }
+    TimedLaunch tl(K_FWD, st);
+    return launch_fwd_march_d128(a, a.workspace, st);
+  }
   // fp32 io is instantiated at d = 16 only (the fp32 tiles at d = 128 exceed the LDS budget)
   if (a.bf16) return a.D == 128 ? launch_fwd_t<u16, 128>(a, st) : launch_fwd_t<u16, 16>(a, st);
   return a.D == 16 ? launch_fwd_t<float, 16>(a, st) : hipErrorInvalidValue;

@@ -100,6 +100,15 @@ size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float) + 256;
 }
 
+bool fwd_uses_chunk_matrices(const flare_gdn_shape *s) {
+  return s->io_dtype == FLARE_BF16 && s->d_k == 128 && s->d_v == 128 && s->flags == 0;
+}
+
+size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
+  if (!fwd_uses_chunk_matrices(s)) return 0;
+  return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * 6 * kChunk * kChunk * sizeof(float) + 256;
+}
+
 flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
                               const int32_t *slot_idx_host, const float *pool,
                               int32_t num_slots, const flare_gdn_shape *s,

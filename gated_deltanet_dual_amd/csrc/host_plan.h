@@ -44,6 +44,11 @@ int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride);
 // six chunk matrices (checkpoint slot layout).
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
 
+// Bytes of fwd workspace: six chunk matrices per chunk slot and head when the
+// forward runs its chunk-matrix pass (bf16 io, d = 128, no flags), else 0.
+size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
+bool fwd_uses_chunk_matrices(const flare_gdn_shape *s);
+
 // Serving step: slots distinct and in range when the host copy is given.
 flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
                               const int32_t *slot_idx_host, const float *pool,

@@ -35,8 +35,13 @@ struct FwdArgs {
   const float *alpha, *beta, *alpha_n, *beta_n, *h0;
   void *o, *on;
   float *h_final, *ckpt;
+  float *workspace;  // the forward's chunk matrices (bf16, d = 128, no flags)
+  int64_t T;
 };
 hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
+// forward march for bf16 io at d = 128 without flags (gdn_fwd_march.hip);
+// cmat: the chunk matrices of every (slot, head)
+hipError_t launch_fwd_march_d128(const FwdArgs &a, const float *cmat, hipStream_t st);
 
 struct BwdArgs {
   FwdArgs f;

@@ -93,8 +93,12 @@ typedef struct {
  * from their own first token). */
 int32_t flare_gdn_chunk_size(void);
 
-/* Bytes of device workspace flare_gdn_dual_bwd needs for this batch (the
- * forward needs none).  Returns 0 on invalid arguments. */
+/* Bytes of device workspace flare_gdn_dual_fwd (for_bwd = 0) or
+ * flare_gdn_dual_bwd (for_bwd = 1) needs for this batch; 0 when the
+ * configuration needs none (the forward needs workspace only for bf16 io at
+ * d = 128 without flags) and on invalid arguments.  The workspace holds, per
+ * chunk slot (checkpoint slot layout, stride 1) and head, six 32 x 32 fp32
+ * chunk matrices, and for the backward also the chunk's end-state adjoint. */
 size_t flare_gdn_dual_workspace_size(const flare_varlen *varlen,
                                      const flare_gdn_shape *shape, int for_bwd);
 
@@ -126,6 +130,8 @@ int64_t flare_gdn_ckpt_slot(int32_t cu_seqlens_i, int32_t doc_index,
  *   h_final    [N, H, d_k, d_v] fp32 clean state after each document, or NULL
  *   ckpt       chunk-start clean states for the backward (see
  *              flare_gdn_dual_ckpt_size), or NULL for inference
+ *   workspace  device scratch of flare_gdn_dual_workspace_size(..., 0) bytes,
+ *              256-byte aligned; may be NULL when that size is 0
  * The clean block-boundary states are never written to memory. */
 flare_status flare_gdn_dual_fwd(const flare_varlen *varlen,
                                 const flare_gdn_shape *shape, const void *q,
@@ -135,7 +141,8 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen,
                                 const float *alpha_n, const float *beta_n,
                                 const float *h0, void *o, void *on,
                                 float *h_final, float *ckpt,
-                                int32_t ckpt_stride_chunks, void *stream);
+                                int32_t ckpt_stride_chunks, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Reverse mode of flare_gdn_dual_fwd (Key designs items 2 and 3): the adjoint
  * reaching each noisy block start is added to the clean adjoint at that block's
@@ -215,7 +222,8 @@ int32_t flare_version(void);
  * (the backward launches the reverse scan, then the per-chunk kernel).
  * Kernel names: "gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel",
  * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel",
- * "gdn_tri_kernel" (the backward's chunk solves, bf16 io at d = 128).
+ * "gdn_tri_kernel" (the chunk-matrix pass of the forward and backward, bf16
+ * io at d = 128; "gdn_dual_fwd_kernel" then names the forward march).
  * flare_timing_enable(1) turns it on (events are created lazily, host side
  * only; no device memory is allocated), (0) off.  Returns the previous state.
  * flare_timing_avg_ms() blocks until the recorded launches of that kernel

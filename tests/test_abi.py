@@ -57,7 +57,7 @@ def varlen(cu, pl, dev=True):
 def fwd_status(L, v, shape, ckpt=None, stride=1, null_q=False):
     P = [None if null_q else FAKE] + [FAKE] * 9
     return L.flare_gdn_dual_fwd(ctypes.byref(v), ctypes.byref(shape), *P, None, FAKE, FAKE, None,
-                                ckpt, stride, None)
+                                ckpt, stride, None, 0, None)
 
 
 def test_fwd_validation(L):
@@ -85,6 +85,24 @@ def test_fwd_validation(L):
     v = g._Varlen(1, FAKE.value, None, FAKE.value, None)
     assert fwd_status(L, v, ok_shape) == 1
     assert b"cu_seqlens" in L.flare_last_error()
+
+
+def test_fwd_workspace_checked_before_launch(L):
+    shape = g.GDNShape(4, 128, 128, 4, g.BF16, 0, 0.0)
+    v = varlen([0, 100, 164], [20, 0])
+    need = L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(shape), 0)
+    # six 32 x 32 fp32 chunk matrices per chunk slot and head
+    assert need == (164 // 32 + 2) * 4 * 6 * 32 * 32 * 4 + 256
+    P = [FAKE] * 10
+    st = L.flare_gdn_dual_fwd(ctypes.byref(v), ctypes.byref(shape), *P, None, FAKE, FAKE, None, None, 1,
+                              FAKE, need - 1, None)
+    assert st == 5
+    st = L.flare_gdn_dual_fwd(ctypes.byref(v), ctypes.byref(shape), *P, None, FAKE, FAKE, None, None, 1,
+                              None, 0, None)
+    assert st == 5
+    # configurations served by the fused kernel need none
+    for other in (g.GDNShape(4, 16, 16, 4, g.BF16, 0, 0.0), g.GDNShape(4, 128, 128, 4, g.BF16, 1, 0.0)):
+        assert L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(other), 0) == 0
 
 
 def test_bwd_workspace_checked_before_launch(L):
