@@ -7,8 +7,11 @@
 // gated delta rule of Key designs item 2.
 //
 // One workgroup per (request, head).  The whole d x d fp32 state of the pair is
-// read once with 16-byte loads and kept in registers: thread t owns columns
-// 4*(t % (D/4)) .. +3 of a group of rows.  The B updates are applied in their
+// read once with 16-byte loads and kept in registers: the threads of one
+// 4-column quad are adjacent lanes, each holding every NRG-th row, so the sums
+// over rows are DPP reductions across those lanes with no LDS partials.  The
+// small B x B work (dot products, the unit-triangular solve) runs while the
+// state is still arriving.  The B updates are applied in their
 // chunked (UT) form so the state is touched by exactly one reduction pass:
 //   w_j = S^T k_j, r_l = S^T q_l                      (one pass over S)
 //   A_ij = (G_i/G_j) b_j k_i.k_j (j < i), T = (I + A)^-1
@@ -28,181 +31,266 @@ namespace flare {
 template <int D> struct StepCfg {
   static constexpr int NT = D >= 128 ? 256 : 64;  // threads
   static constexpr int NCQ = D / 4;               // column quads
-  static constexpr int NRG = NT / NCQ;            // row groups
-  static constexpr int RPG = D / NRG;             // rows per group
-  static constexpr int G = 8;                     // vectors reduced per pass
+  static constexpr int NRG = NT / NCQ;            // row groups: adjacent lanes of one quad
+  static constexpr int RPG = D / NRG;             // rows per group (rows rg * RPG + i)
+  static constexpr int G = D >= 128 ? 2 : 8;      // vectors per pass (few: registers, occupancy)
+  static_assert(NRG == 8 || NRG == 16, "row groups are reduced over 8 or 16 lanes");
 };
+
+// Sum over the NRG adjacent lanes of a row group (a DPP row or half-row).
+template <int NRG>
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  x += dpp_f32<0xB1>(x);   // xor 1
+  x += dpp_f32<0x4E>(x);   // xor 2
+  x += dpp_f32<0x141>(x);  // the other quad of the half-row
+  if constexpr (NRG == 16) x += dpp_f32<0x140>(x);  // the other half-row
+  return x;
+}
 
 template <typename IO, int D, int BMAX>
 __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArgs a) {
   using Cfg = StepCfg<D>;
-  constexpr int NT = Cfg::NT, NCQ = Cfg::NCQ, NRG = Cfg::NRG, RPG = Cfg::RPG, G = Cfg::G;
-  constexpr int NV = 2 * BMAX;  // k vectors then q vectors
+  constexpr int NT = Cfg::NT, NRG = Cfg::NRG, RPG = Cfg::RPG, G = Cfg::G;
+  constexpr int NV = 2 * BMAX;           // k vectors then q vectors
+  constexpr int EPU = 16 / sizeof(IO);   // io elements per 16 bytes
+  constexpr int UPR = D / EPU;           // 16-byte units per row
   const int B = a.B;
   const int t = threadIdx.x;
+  const int rg = t % NRG, cq = t / NRG;
   const int req = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const int cq = t % NCQ, rg = t / NCQ;
 
-  __shared__ float sX[NV][D];          // k_0..k_{B-1}, q_0..q_{B-1} (fp32)
-  __shared__ float sVv[BMAX][D];       // values
-  __shared__ float sW[NV][D];          // S^T x for every x in sX
-  __shared__ __align__(16) float sPart[NRG][G][D];
-  __shared__ float sU[BMAX][D];
-  __shared__ float sKK[BMAX][BMAX], sQK[BMAX][BMAX], sT[BMAX][BMAX];
+  __shared__ __align__(16) float sX[NV][D];   // k_0..k_{B-1} at 0.., q_0..q_{B-1} at BMAX..
+  __shared__ __align__(16) float sV[BMAX][D];
+  __shared__ __align__(16) float sW[NV][D];   // S^T x for every x in sX
+  __shared__ __align__(16) float sU[BMAX][D];
+  __shared__ float sKK[BMAX][BMAX + 1], sQK[BMAX][BMAX + 1], sT[BMAX][BMAX + 1];
   __shared__ float sG[BMAX], sBeta[BMAX];
 
-  const int slot = a.slot_idx[req];
-  float *S = a.pool + ((size_t)slot * a.H + h) * D * D;
+  const IO *const pk = reinterpret_cast<const IO *>(a.k), *const pq = reinterpret_cast<const IO *>(a.q);
+  const IO *const pv = reinterpret_cast<const IO *>(a.v);
+  const float *const pal = a.alpha, *const pbe = a.beta;
 
-  // 1. stream the state into registers (16-byte loads, all issued up front)
+  float *S = a.pool + ((size_t)a.slot_idx[req] * a.H + h) * D * D;
   float4 s4[RPG];
+  {
+    // 0. the block inputs first (16-byte loads into registers), then the
+    //    state: vector-memory results return in issue order, so the small B x B
+    //    work below waits only for the inputs while the state is in flight
+    constexpr int IU = (3 * BMAX * UPR + NT - 1) / NT;  // input units per thread
+    uint4 in_raw[IU];
 #pragma unroll
-  for (int i = 0; i < RPG; ++i)
-    s4[i] = *reinterpret_cast<const float4 *>(S + (size_t)(rg * RPG + i) * D + 4 * cq);
-
-  // 2. block inputs -> LDS as fp32
-  const IO *q = reinterpret_cast<const IO *>(a.q);
-  const IO *k = reinterpret_cast<const IO *>(a.k);
-  const IO *v = reinterpret_cast<const IO *>(a.v);
-  for (int e = t; e < B * D; e += NT) {
-    const int j = e / D, c = e % D;
-    const size_t row = (((size_t)req * B + j) * a.H + h) * D + c;
-    sX[j][c] = io_traits<IO>::to_f(k[row]);
-    sX[BMAX + j][c] = io_traits<IO>::to_f(q[row]);
-    sVv[j][c] = io_traits<IO>::to_f(v[row]);
-  }
-  if (t < 64) {
-    // gates: inclusive scan of log(alpha) over the block (one wave)
-    const int j = t;
+    for (int e = 0; e < IU; ++e) {
+      const int u = e * NT + t;
+      in_raw[e] = make_uint4(0u, 0u, 0u, 0u);
+      if (u < 3 * B * UPR) {
+        const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
+        const IO *src = which == 0 ? pk : which == 1 ? pq : pv;
+        in_raw[e] = *reinterpret_cast<const uint4 *>(src + (((size_t)req * B + r) * a.H + h) * D + cu * EPU);
+      }
+    }
     float la = 0.f, be = 0.f;
-    if (j < B) {
-      const size_t gi = ((size_t)req * B + j) * a.H + h;
-      la = __logf(a.alpha[gi]);
-      be = a.beta[gi];
+    if (t < B) {
+      const size_t gi = ((size_t)req * B + t) * a.H + h;
+      la = __logf(pal[gi]);
+      be = pbe[gi];
     }
+    // the state: thread (rg, cq) holds rows rg * RPG .. + RPG - 1, columns
+    // 4 cq .. 4 cq + 3 (a wave reads whole 128-byte row segments); nothing
+    // waits for it until the reduction
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(la, off, 64);
-      if (j >= off) la += y;
-    }
-    if (j < B) {
-      sG[j] = la;
-      sBeta[j] = be;
-    }
-  }
-  __syncthreads();
+    for (int i = 0; i < RPG; ++i)
+      s4[i] = *reinterpret_cast<const float4 *>(S + (size_t)(rg * RPG + i) * D + 4 * cq);
 
-  // 3. one reduction pass: W[x] = S^T x for the 2B vectors, G at a time
-  for (int v0 = 0; v0 < 2 * B; v0 += G) {
-    float4 acc[G];
+    // 1. block inputs -> LDS as fp32
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = 0; e < IU; ++e) {
+      const int u = e * NT + t;
+      if (u < 3 * B * UPR) {
+        const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
+        float *dst = which == 0 ? &sX[r][cu * EPU] : which == 1 ? &sX[BMAX + r][cu * EPU] : &sV[r][cu * EPU];
+        const uint4 raw = in_raw[e];
+        if constexpr (sizeof(IO) == 2) {
+          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+          float4 lo, hi;
+          lo.x = __uint_as_float(w[0] << 16); lo.y = __uint_as_float(w[0] & 0xffff0000u);
+          lo.z = __uint_as_float(w[1] << 16); lo.w = __uint_as_float(w[1] & 0xffff0000u);
+          hi.x = __uint_as_float(w[2] << 16); hi.y = __uint_as_float(w[2] & 0xffff0000u);
+          hi.z = __uint_as_float(w[3] << 16); hi.w = __uint_as_float(w[3] & 0xffff0000u);
+          reinterpret_cast<float4 *>(dst)[0] = lo;
+          reinterpret_cast<float4 *>(dst)[1] = hi;
+        } else {
+          *reinterpret_cast<uint4 *>(dst) = raw;
+        }
+      }
+    }
+    if (t < 64) {
+      // gates: inclusive scan of log(alpha) over the block (one wave)
+      const int j = t;
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const int row = rg * RPG + i;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(la, off, 64);
+        if (j >= off) la += y;
+      }
+      if (j < B) {
+        sG[j] = la;
+        sBeta[j] = be;
+      }
+    }
+    __syncthreads();
+
+    // 2. B x B dot products k_i.k_j and q_l.k_j, 16 lanes per dot (a DPP row),
+    //    while the state is still in flight
+    {
+      constexpr int GROUPS = NT / 16, PER = D / 16;
+      const int grp = t / 16, sub = t % 16;
+      const int ndots = 2 * B * B;
+      for (int d0 = 0; d0 < ndots; d0 += GROUPS) {  // uniform trip count: every lane joins the DPP sums
+        const int dd = d0 + grp;
+        const bool valid = dd < ndots;
+        const int which = valid ? dd / (B * B) : 0, ij = valid ? dd % (B * B) : 0;
+        const int i = ij / B, j = ij % B;
+        const float *x = sX[which ? BMAX + i : i];
+        const float *y = sX[j];
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) p += x[sub * PER + e] * y[sub * PER + e];
+        p = dpp_sum16(p);
+        if (valid && sub == 0) {
+          if (which) sQK[i][j] = p; else sKK[i][j] = p;
+        }
+      }
+    }
+    __syncthreads();
+
+    // 3. T = (I + A)^-1 by forward substitution, one lane per column (the other
+    //    threads go on to the reduction); the column lives in sT and is read
+    //    back only by the thread that wrote it.
+    if (t < B) {
+      const int c = t;
+      for (int i = 0; i < B; ++i) {
+        float x = 0.f;
+        if (i == c) {
+          x = 1.f;
+        } else if (i > c) {
+          float acc = 0.f;
+          for (int m = c; m < i; ++m) acc += __expf(sG[i] - sG[m]) * sBeta[m] * sKK[i][m] * sT[m][c];
+          x = -acc;
+        }
+        sT[i][c] = x;
+      }
+    }
+
+    // 4. one pass over the state: W[x] = S^T x for the 2B vectors, G at a time;
+    //    the row-group partials are summed across adjacent lanes (DPP)
+    for (int v0 = 0; v0 < 2 * B; v0 += G) {
+      float4 acc[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int vi = v0 + g;
-        const int src = min(vi < B ? vi : BMAX + (vi - B), NV - 1);
-        const float x = (vi < 2 * B) ? sX[src][row] : 0.f;
-        acc[g].x += x * s4[i].x;
-        acc[g].y += x * s4[i].y;
-        acc[g].z += x * s4[i].z;
-        acc[g].w += x * s4[i].w;
-      }
-    }
+        const int src = vi < B ? vi : BMAX + min(vi - B, BMAX - 1);
+        const bool live = vi < 2 * B;
+        if constexpr (RPG % 4 == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) *reinterpret_cast<float4 *>(&sPart[rg][g][4 * cq]) = acc[g];
-    __syncthreads();
-    for (int e = t; e < G * NCQ; e += NT) {
-      const int g = e / NCQ, c4 = e % NCQ;
-      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-      for (int r = 0; r < NRG; ++r) {
-        const float4 p = *reinterpret_cast<const float4 *>(&sPart[r][g][4 * c4]);
-        sum.x += p.x; sum.y += p.y; sum.z += p.z; sum.w += p.w;
+          for (int i4 = 0; i4 < RPG; i4 += 4) {  // four rows of x per 16-byte LDS read
+            float4 x4 = *reinterpret_cast<const float4 *>(&sX[src][rg * RPG + i4]);
+            if (!live) x4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              acc[g].x += xs[ii] * s4[i4 + ii].x;
+              acc[g].y += xs[ii] * s4[i4 + ii].y;
+              acc[g].z += xs[ii] * s4[i4 + ii].z;
+              acc[g].w += xs[ii] * s4[i4 + ii].w;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < RPG; ++i) {
+            const float x = live ? sX[src][rg * RPG + i] : 0.f;
+            acc[g].x += x * s4[i].x;
+            acc[g].y += x * s4[i].y;
+            acc[g].z += x * s4[i].z;
+            acc[g].w += x * s4[i].w;
+          }
+        }
       }
-      const int vi = v0 + g;
-      if (vi < 2 * B) {
-        const int dst = vi < B ? vi : BMAX + (vi - B);
-        *reinterpret_cast<float4 *>(&sW[dst][4 * c4]) = sum;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float4 r4;
+        r4.x = rowgroup_sum<NRG>(acc[g].x);
+        r4.y = rowgroup_sum<NRG>(acc[g].y);
+        r4.z = rowgroup_sum<NRG>(acc[g].z);
+        r4.w = rowgroup_sum<NRG>(acc[g].w);
+        const int vi = v0 + g;
+        if (rg == 0 && vi < 2 * B) {
+          const int dst = vi < B ? vi : BMAX + (vi - B);
+          *reinterpret_cast<float4 *>(&sW[dst][4 * cq]) = r4;
+        }
       }
     }
     __syncthreads();
-  }
 
-  // 4. B x B dot products k_i.k_j and q_l.k_j
-  for (int e = t; e < 2 * B * B; e += NT) {
-    const int which = e / (B * B), ij = e % (B * B);
-    const int i = ij / B, j = ij % B;
-    const float *x = sX[which ? BMAX + i : i];
-    const float *y = sX[j];
-    float d = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) d += x[c] * y[c];
-    if (which) sQK[i][j] = d; else sKK[i][j] = d;
-  }
-  __syncthreads();
-
-  // 5. T = (I + A)^-1 by forward substitution, one lane per column; the
-  //    column lives in sT and is read back only by the thread that wrote it.
-  if (t < B) {
-    const int c = t;
-    for (int i = 0; i < B; ++i) {
-      float x = 0.f;
-      if (i == c) {
-        x = 1.f;
-      } else if (i > c) {
-        float acc = 0.f;
-        for (int m = c; m < i; ++m) acc += __expf(sG[i] - sG[m]) * sBeta[m] * sKK[i][m] * sT[m][c];
-        x = -acc;
-      }
-      sT[i][c] = x;
-    }
-  }
-  __syncthreads();
-
-  // 6. U = T (V - diag(G) W_k)
-  for (int e = t; e < B * D; e += NT) {
-    const int i = e / D, c = e % D;
-    float u = 0.f;
-    for (int m = 0; m <= i; ++m) u += sT[i][m] * (sVv[m][c] - __expf(sG[m]) * sW[m][c]);
-    sU[i][c] = u;
-  }
-  __syncthreads();
-
-  // 7. outputs
-  const float s = a.scale;
-  const int last = B - 1;
-  if (a.o) {
-    IO *o = reinterpret_cast<IO *>(a.o);
+    // 5. U = T (V - diag(G) W_k)
     for (int e = t; e < B * D; e += NT) {
-      const int l = e / D, c = e % D;
-      const int end = a.mode == 0 ? last : l;  // EVAL reads the block end
-      float acc = __expf(sG[end]) * sW[BMAX + l][c];
-      for (int j = 0; j <= end; ++j) acc += __expf(sG[end] - sG[j]) * sBeta[j] * sQK[l][j] * sU[j][c];
-      o[(((size_t)req * B + l) * a.H + h) * D + c] = io_traits<IO>::from_f(s * acc);
+      const int i = e / D, c = e % D;
+      float u = 0.f;
+      for (int m = 0; m <= i; ++m) u += sT[i][m] * (sV[m][c] - __expf(sG[m]) * sW[m][c]);
+      sU[i][c] = u;
     }
-  }
+    __syncthreads();
 
-  // 8. COMMIT: rank-B update of the register-resident state, written back
-  if (a.mode == 1) {
-    const float ge = __expf(sG[last]);
-    float wj[BMAX];
+    // 6. outputs, EPU consecutive columns per work item (one 16-byte store)
+    const float s = a.scale;
+    const int last = B - 1;
+    if (a.o) {
+      IO *o = reinterpret_cast<IO *>(a.o);
+      for (int e = t; e < B * UPR; e += NT) {
+        const int l = e / UPR, c0 = (e % UPR) * EPU;
+        const int end = a.mode == 0 ? last : l;  // EVAL reads the block end
+        const float ge = __expf(sG[end]);
+        float acc[EPU];
 #pragma unroll
-    for (int j = 0; j < BMAX; ++j) wj[j] = j < B ? __expf(sG[last] - sG[j]) * sBeta[j] : 0.f;
+        for (int c = 0; c < EPU; ++c) acc[c] = ge * sW[BMAX + l][c0 + c];
+        for (int j = 0; j <= end; ++j) {
+          const float wq = __expf(sG[end] - sG[j]) * sBeta[j] * sQK[l][j];
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const int row = rg * RPG + i;
-      float4 n = make_float4(ge * s4[i].x, ge * s4[i].y, ge * s4[i].z, ge * s4[i].w);
-#pragma unroll
-      for (int j = 0; j < BMAX; ++j) {
-        if (j >= B) break;
-        const float kk = sX[j][row] * wj[j];
-        const float4 u = *reinterpret_cast<const float4 *>(&sU[j][4 * cq]);
-        n.x += kk * u.x; n.y += kk * u.y; n.z += kk * u.z; n.w += kk * u.w;
+          for (int c = 0; c < EPU; ++c) acc[c] += wq * sU[j][c0 + c];
+        }
+        IO *dst = o + (((size_t)req * B + l) * a.H + h) * D + c0;
+        if constexpr (sizeof(IO) == 2) {
+          uint4 w;
+          w.x = pack_bf16x2(s * acc[0], s * acc[1]);
+          w.y = pack_bf16x2(s * acc[2], s * acc[3]);
+          w.z = pack_bf16x2(s * acc[4], s * acc[5]);
+          w.w = pack_bf16x2(s * acc[6], s * acc[7]);
+          *reinterpret_cast<uint4 *>(dst) = w;
+        } else {
+          *reinterpret_cast<float4 *>(dst) = make_float4(s * acc[0], s * acc[1], s * acc[2], s * acc[3]);
+        }
       }
-      *reinterpret_cast<float4 *>(S + (size_t)row * D + 4 * cq) = n;
+    }
+
+    // 7. COMMIT: rank-B update of the register-resident state, written back
+    if (a.mode == 1) {
+      const float ge = __expf(sG[last]);
+      float wj[BMAX];
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j) wj[j] = j < B ? __expf(sG[last] - sG[j]) * sBeta[j] : 0.f;
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const int row = rg * RPG + i;
+        float4 n = make_float4(ge * s4[i].x, ge * s4[i].y, ge * s4[i].z, ge * s4[i].w);
+#pragma unroll
+        for (int j = 0; j < BMAX; ++j) {
+          if (j >= B) break;
+          const float kk = sX[j][row] * wj[j];
+          const float4 u = *reinterpret_cast<const float4 *>(&sU[j][4 * cq]);
+          n.x += kk * u.x; n.y += kk * u.y; n.z += kk * u.z; n.w += kk * u.w;
+        }
+        *reinterpret_cast<float4 *>(S + (size_t)row * D + 4 * cq) = n;
+      }
     }
   }
 }
