@@ -168,6 +168,31 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
         return t.to(bf) if to_bf16 else t
 
+    result = {}
+    comps = {}
+    need_headline = args.only in (None, "step", "infer")
+    if need_headline:
+        result, comps, inp = run_headline(torch, g, wl, dev, timer, up, args)
+    if not args.no_components and args.only in (None, "serve"):
+        comps["serving"] = bench_serving(torch, g, wl, dev, timer, up, args)
+    if not args.no_components and args.only in (None, "conv"):
+        comps["shortconv"] = bench_conv(torch, g, wl, dev, timer, up, args)
+    if comps:
+        result["components"] = comps
+
+    if not args.no_cpu_baseline and args.only is None:
+        result["cpu_baseline"] = cpu_baseline(inp)
+
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+def run_headline(torch, g, wl, dev, timer, up, args):
+    """The headline step (fwd with checkpoints + bwd) and the inference forward."""
+    bf = torch.bfloat16
     # ------------------------------------------------------------ headline inputs
     log("bench: generating the headline workload (4 x 8192 tokens, H=16, d=128)")
     inp = wl.headline(with_grads=True, round_io=False)
@@ -197,9 +222,10 @@ def main():
 
     def step():
         g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
-        g.gdn_dual_bwd(vl, *args10, B, ckpt, do, don, out=grads, workspace=ws)
+        g.gdn_dual_bwd(vl, *args10, B, ckpt, do, don, out=grads, workspace=ws, fwd_workspace=fws)
 
     result = {}
+    comps = {}
     if args.only in (None, "step"):
         for _ in range(args.warmup):
             step()
@@ -260,26 +286,11 @@ def main():
             % (ms_step, ", ".join("%s %.3f ms" % (k, v["ms"] or -1) for k, v in kern.items()),
                1e3 * t_roof / ms_step))
 
-    comps = {}
     if not args.no_components and args.only in (None, "infer"):
         comps["fwd_inference"] = bench_infer(torch, g, vl, args10, B, o, on, fws, timer, args,
                                              th_total, th_resp, fwd_flops_per_th(d, C, B, False) * th_total
                                              + fwd_flops_per_th(d, C, B, True) * th_resp)
-    if not args.no_components and args.only in (None, "serve"):
-        comps["serving"] = bench_serving(torch, g, wl, dev, timer, up, args)
-    if not args.no_components and args.only in (None, "conv"):
-        comps["shortconv"] = bench_conv(torch, g, wl, dev, timer, up, args)
-    if comps:
-        result["components"] = comps
-
-    if not args.no_cpu_baseline and args.only is None:
-        result["cpu_baseline"] = cpu_baseline(inp)
-
-    line = json.dumps(result)
-    print(line, flush=True)
-    if args.json_out:
-        with open(args.json_out, "w") as f:
-            f.write(line + "\n")
+    return result, comps, inp
 
 
 def bench_infer(torch, g, vl, args10, B, o, on, fws, timer, args, th_total, th_resp, flops):

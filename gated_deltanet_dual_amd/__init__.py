@@ -77,7 +77,7 @@ def lib():
     L.flare_gdn_ckpt_slot.restype = ctypes.c_int64
     L.flare_gdn_dual_fwd.argtypes = [VP, SP] + [P] * 10 + [P, P, P, P, P, I32, P, SZ, P]
     L.flare_gdn_dual_fwd.restype = ctypes.c_int
-    L.flare_gdn_dual_bwd.argtypes = [VP, SP] + [P] * 10 + [P, P, I32, P, P, P] + [P] * 11 + [P, SZ, P]
+    L.flare_gdn_dual_bwd.argtypes = [VP, SP] + [P] * 10 + [P, P, I32, P, P, P, P] + [P] * 11 + [P, SZ, P]
     L.flare_gdn_dual_bwd.restype = ctypes.c_int
     L.flare_gdn_block_step.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, I32, P]
     L.flare_gdn_block_step.restype = ctypes.c_int
@@ -207,10 +207,12 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
 
 def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,
                  ckpt, d_o, d_on, h0=None, dh_final=None, scale=0.0, flags=0, want_dh0=True,
-                 workspace=None, out=None):
+                 workspace=None, out=None, fwd_workspace=None):
     """Reverse mode.  Returns a dict of gradients (same names as the oracle);
     `out` = such a dict reuses its buffers, `workspace` a uint8 device buffer of
-    at least flare_gdn_dual_workspace_size() bytes."""
+    at least flare_gdn_dual_workspace_size() bytes, `fwd_workspace` the
+    workspace of the forward call that produced `ckpt` (its chunk matrices are
+    then reused)."""
     torch = _torch()
     T, H, d = q.shape
     io = _io_of(q)
@@ -229,7 +231,7 @@ def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
     _check(lib().flare_gdn_dual_bwd(
         varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
         _ptr(qn), _ptr(kn), _ptr(vn), _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(ckpt), 1,
-        _ptr(d_o), _ptr(d_on), _ptr(dh_final), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+        _ptr(fwd_workspace), _ptr(d_o), _ptr(d_on), _ptr(dh_final), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
         _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g["dqn"]), _ptr(g["dkn"]), _ptr(g["dvn"]),
         _ptr(g["dalpha_n"]), _ptr(g["dbeta_n"]), _ptr(g["dh0"]), _ptr(workspace),
         workspace.numel(), _stream(dev)))

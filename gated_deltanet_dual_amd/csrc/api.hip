@@ -96,7 +96,8 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
                                 const void *q, const void *k, const void *v, const float *alpha,
                                 const float *beta, const void *qn, const void *kn, const void *vn,
                                 const float *alpha_n, const float *beta_n, const float *h0,
-                                const float *ckpt, int32_t ckpt_stride_chunks, const void *d_o,
+                                const float *ckpt, int32_t ckpt_stride_chunks, const void *fwd_workspace,
+                                const void *d_o,
                                 const void *d_on, const float *dh_final, void *dq, void *dk,
                                 void *dv, float *dalpha, float *dbeta, void *dqn, void *dkn,
                                 void *dvn, float *dalpha_n, float *dbeta_n, float *dh0,
@@ -135,6 +136,9 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
   a.f.h0 = h0;
   a.f.T = vi.total_tokens;
   a.ckpt_in = ckpt;
+  // the forward's chunk matrices, when its workspace held them
+  a.fwd_cm = (fwd_workspace && fwd_workspace_bytes(vi, shape) > 0) ? reinterpret_cast<const float *>(fwd_workspace)
+                                                                      : nullptr;
   a.d_o = d_o; a.d_on = d_on; a.dh_final = dh_final;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dqn = dqn; a.dkn = dkn; a.dvn = dvn;
   a.dalpha = dalpha; a.dbeta = dbeta; a.dalpha_n = dalpha_n; a.dbeta_n = dbeta_n; a.dh0 = dh0;

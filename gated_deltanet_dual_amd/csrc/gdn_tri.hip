@@ -4,10 +4,10 @@
 // the noisy blocks, and the four weighted masked Gram matrices Mwo, Mwq, Mwk,
 // Mw~ (bwd_common.h).  They depend only on q, k, q~, k~ and the gates, so they
 // are formed here once, fully in parallel over (chunk, head), instead of on
-// the sequential reverse scan's critical path.  One workgroup of 2 waves per
-// (chunk slot, head): wave 0 solves T and forms Mwo, Mwq; wave 1 solves T~
-// and forms Mwk, Mw~.  Output per (slot, head): [T, T~, Mwo, Mwq, Mwk, Mw~],
-// each 32 x 32 fp32 row-major.
+// the sequential reverse scan's critical path.  One workgroup of 4 waves per
+// (chunk slot, head), all four in parallel: wave 0 solves T, wave 1 T~,
+// wave 2 forms Mwo and Mwq, wave 3 Mwk and Mw~.  Output per (slot, head):
+// [T, T~, Mwo, Mwq, Mwk, Mw~], each 32 x 32 fp32 row-major.
 #include "bwd_common.h"
 #include "chunk_common.h"
 #include "device_common.h"
@@ -17,7 +17,7 @@
 namespace flare {
 
 namespace {
-constexpr int tC = 32, tD = 128, tNT = 128, tLDX = tD + 8, tLDM = tC + 4;
+constexpr int tC = 32, tD = 128, tNT = 256, tLDX = tD + 8, tLDM = tC + 4;
 struct TriSmem {
   alignas(16) u16 x[4][tC][tLDX];     // q, k, q~, k~
   alignas(16) float at[2][tC][tLDM];  // A^T, A~^T (gated, without b)
@@ -46,8 +46,8 @@ __global__ __launch_bounds__(tNT) void gdn_tri_d128_kernel(BwdArgs a) {
                             reinterpret_cast<const u16 *>(f.qn), reinterpret_cast<const u16 *>(f.kn)};
 
   // all global loads first (unconditional, rows clamped into the document):
-  // gates and the q, k, q~, k~ rows (16 16-byte units per thread)
-  const float graw = gate_load_raw(f, t0g, c0, n, h, tid);
+  // gates and the q, k, q~, k~ rows (8 16-byte units per thread)
+  const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
   constexpr int RU = D / 8, PU = C * RU, UX = 4 * PU / NT;
   uint4 xr[UX];
 #pragma unroll
@@ -65,25 +65,27 @@ __global__ __launch_bounds__(tNT) void gdn_tri_d128_kernel(BwdArgs a) {
     const bool ok = tpos < n && (m < 2 || tpos >= P);
     *reinterpret_cast<uint4 *>(&sm.x[m][row][cu16 * 8]) = ok ? xr[e] : make_uint4(0u, 0u, 0u, 0u);
   }
-  gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
+  if (tid < 4 * C) gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   lds_barrier();
 
-  // each wave's Gram, solve and store touch only its own LDS (ordered per wave)
+  // each wave forms and stores only matrices it wrote itself (ordered per wave)
   if (wave == 0) {
     gram_at<D, LDX, LDM>(sm.x[1], sm.at[0], sm.lg);
     solve_unit_lower<LDM>(&sm.at[0][0][0], &sm.tm[0][0][0], &sm.tmp[0][0][0], true, sm.beta);
-  } else if (has_noisy) {
-    gram_ant<D, LDX, LDM>(sm.x[3], sm.at[1], sm.lgn, c0, n, P, B);
-    solve_unit_lower<LDM>(&sm.at[1][0][0], &sm.tm[1][0][0], &sm.tmp[1][0][0], B > 16, sm.betan);
+  } else if (wave == 1) {
+    if (has_noisy) {
+      gram_ant<D, LDX, LDM>(sm.x[3], sm.at[1], sm.lgn, c0, n, P, B);
+      solve_unit_lower<LDM>(&sm.at[1][0][0], &sm.tm[1][0][0], &sm.tmp[1][0][0], B > 16, sm.betan);
+    }
+  } else {
+    grams_weighted<D, LDX, LDM>(wave - 2, sm.x, sm.tm[2], sm.tm[3], sm.tm[4], sm.tm[5], sm.lg, sm.beta, sm.lgn,
+                                sm.betan, c0, n, P, B, has_noisy);
   }
-  grams_weighted<D, LDX, LDM>(wave, sm.x, sm.tm[2], sm.tm[3], sm.tm[4], sm.tm[5], sm.lg, sm.beta, sm.lgn,
-                              sm.betan, c0, n, P, B, has_noisy);
-  // wave 0 wrote T, Mwo, Mwq (0, 2, 3); wave 1 T~, Mwk, Mw~ (1, 4, 5): each
-  // stores its own three
+  // wave 0 wrote T (0), wave 1 T~ (1), wave 2 Mwo, Mwq (2, 3), wave 3 Mwk, Mw~ (4, 5)
   float *dst = a.tri + ((size_t)slot * H + h) * 6 * C * C;
-#pragma unroll
-  for (int mi = 0; mi < 3; ++mi) {
-    const int mtx = mi == 0 ? wave : mi == 1 ? (wave == 0 ? 2 : 4) : (wave == 0 ? 3 : 5);
+  const int nm = wave < 2 ? 1 : 2;
+  for (int mi = 0; mi < nm; ++mi) {
+    const int mtx = wave < 2 ? wave : (wave == 2 ? 2 : 4) + mi;
 #pragma unroll
     for (int e = 0; e < C * C / 4 / 64; ++e) {
       const int u = e * 64 + lane, row = u / (C / 4), c4 = u % (C / 4);

@@ -54,6 +54,7 @@ struct BwdArgs {
   size_t workspace_bytes;
   int64_t T;
   float *tri;            // per slot and head [slots][H][6][32][32]: T, T~, Mwo, Mwq, Mwk, Mw~ (set by the launcher)
+  const float *fwd_cm;   // the same matrices from the forward's workspace, or NULL
 };
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
 // per-chunk backward kernel for bf16 io at d = 128 (gdn_bwd_chunk.hip)

@@ -153,13 +153,17 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen,
  * Outputs (written, not accumulated): dq, dk [T,H,d_k], dv [T,H,d_v] io;
  * dalpha, dbeta [T,H] fp32; the same five for the noisy stream (prompt rows 0);
  * dh0 [N,H,d_k,d_v] fp32 or NULL.  workspace: see
- * flare_gdn_dual_workspace_size(..., 1), 256-byte aligned. */
+ * flare_gdn_dual_workspace_size(..., 1), 256-byte aligned.
+ * fwd_workspace: NULL, or the workspace of the flare_gdn_dual_fwd call that
+ * produced ckpt, still holding what that call wrote there (same inputs, shape
+ * and batch): its chunk matrices are then read instead of formed again.  The
+ * result is the same either way. */
 flare_status flare_gdn_dual_bwd(
     const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q,
     const void *k, const void *v, const float *alpha, const float *beta,
     const void *qn, const void *kn, const void *vn, const float *alpha_n,
     const float *beta_n, const float *h0, const float *ckpt,
-    int32_t ckpt_stride_chunks, const void *d_o, const void *d_on,
+    int32_t ckpt_stride_chunks, const void *fwd_workspace, const void *d_o, const void *d_on,
     const float *dh_final, void *dq, void *dk, void *dv, float *dalpha,
     float *dbeta, void *dqn, void *dkn, void *dvn, float *dalpha_n,
     float *dbeta_n, float *dh0, void *workspace, size_t workspace_bytes,

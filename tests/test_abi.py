@@ -112,7 +112,7 @@ def test_bwd_workspace_checked_before_launch(L):
     # per chunk slot ((T/32 + N) slots) and head, fp32: the end-state adjoint
     # (d x d) and six 32 x 32 chunk matrices
     assert need == (64 // 32 + 2) * 2 * (16 * 16 + 6 * 32 * 32) * 4 + 256
-    args = [FAKE] * 10 + [None, FAKE, 1, FAKE, FAKE, None] + [FAKE] * 10 + [None]
+    args = [FAKE] * 10 + [None, FAKE, 1, None, FAKE, FAKE, None] + [FAKE] * 10 + [None]
     st = L.flare_gdn_dual_bwd(ctypes.byref(v), ctypes.byref(shape), *args, FAKE, need - 1, None)
     assert st == 5
     mis = ctypes.c_void_p(FAKE.value + 4)

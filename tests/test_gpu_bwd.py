@@ -109,3 +109,20 @@ def test_bwd_packed_full_size_sampled_heads(g, dev):
     heads = [7, 24]
     sub = sub_heads(inp, heads)
     check(sub, {k: v[:, heads] for k, v in gr.items()}, ref_bwd(sub), TOL_BF16, "bwd_packed")
+
+
+def test_bwd_reusing_forward_chunk_matrices_is_identical(g, dev):
+    """Passing the forward's workspace lets the backward read its chunk
+    matrices instead of forming them again; the gradients are bit-identical."""
+    import torch
+    inp = wl.gdn_inputs([130, 64, 96], [32, 0, 48], 2, 128, 128, 4, seed=74, with_grads=True)
+    vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+    args = fwd_args(inp, dev)
+    fws = torch.empty((g.workspace_bytes(vl, 2, 128, 4, g.BF16),), dtype=torch.uint8, device=dev)
+    _, _, _, ck = g.gdn_dual_fwd(vl, *args, 4, want_ckpt=True, workspace=fws)
+    do, don = to_dev(inp.do, dev, True), to_dev(inp.don, dev, True)
+    g1 = g.gdn_dual_bwd(vl, *args, 4, ck, do, don)
+    g2 = g.gdn_dual_bwd(vl, *args, 4, ck, do, don, fwd_workspace=fws)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert torch.equal(g1[k], g2[k]), k
