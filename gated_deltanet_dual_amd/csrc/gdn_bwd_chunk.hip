@@ -32,14 +32,18 @@ namespace flare {
 namespace {
 
 constexpr int kC = 32, kD = 128, kNW = 8, kNT = 64 * kNW;
-constexpr int kLDX = kD + 8, kLDM = kC + 4, kLDA = kD + 4;
+constexpr int kLDX = kD + 8, kLDM = kC + 4, kLDP = kD + 8, kLDG = kC + 8;
 enum { P_G = 0, P_GN, P_B, P_BN, P_GP, P_GE, P_C, P_NUM };
 enum { A_U = 0, A_UN, A_DRHS, A_DRN };
+static_assert(6 * 2 * 2 * kC * kLDG <= 4 * 2 * kC * kLDP, "dG planes must fit in the d_v arrays");
 
 struct Chunk2Smem {
   alignas(16) u16 x[4][kC][kLDX];       // q, k, q~, k~ ; at the end the staging of dq, dk, dq~, dk~
   alignas(16) float cc[8][kC][kLDM];    // unweighted masked Grams (A, A~ transposed), T, T~; later dG
-  alignas(16) float arr[4][kC][kLDA];   // U, u~, drhs, drhs~ for the d_v reductions
+  // U, u~, drhs, drhs~ for the d_v reductions as bf16 hi / lo planes (each
+  // value split once, by the wave that computed it); after those reductions
+  // the same bytes hold the Gram-weight gradients dG, [6][orientation][hi, lo][kC][kLDG]
+  alignas(16) u16 arrp[4][2][kC][kLDP];
   alignas(16) float lg[kC], beta[kC], lgn[kC], betan[kC];
   alignas(16) float part[kNW][P_NUM][kC];  // per-wave gate-gradient partials
   alignas(16) float plgc[kNW];
@@ -90,7 +94,7 @@ __device__ __forceinline__ Slab slab_mask(const u16 (&raw)[2][4], int c0, int n,
 }  // namespace
 
 __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
-  constexpr int C = kC, D = kD, NT = kNT, LDX = kLDX, LDM = kLDM, LDA = kLDA;
+  constexpr int C = kC, D = kD, NT = kNT, LDX = kLDX, LDM = kLDM, LDP = kLDP, LDG = kLDG;
   __shared__ Chunk2Smem sm;
   const FwdArgs &f = a.f;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -333,10 +337,13 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
           gdv[off] = f2bf(DRHS.t[tr][r]);
           gdvn[off] = f2bf(has_noisy && resp_row(i) ? DRN.t[tr][r] : 0.f);
         }
-        sm.arr[A_U][i][col0 + cl] = U.t[tr][r];
-        sm.arr[A_UN][i][col0 + cl] = UN.t[tr][r];
-        sm.arr[A_DRHS][i][col0 + cl] = DRHS.t[tr][r];
-        sm.arr[A_DRN][i][col0 + cl] = DRN.t[tr][r];
+        const float vals[4] = {U.t[tr][r], UN.t[tr][r], DRHS.t[tr][r], DRN.t[tr][r]};
+#pragma unroll
+        for (int ai = 0; ai < 4; ++ai) {
+          const u16 hb = f2bf(vals[ai]);
+          sm.arrp[ai][0][i][col0 + cl] = hb;
+          sm.arrp[ai][1][i][col0 + cl] = f2bf(vals[ai] - bf2f(hb));
+        }
       }
   }
   // per-row gate partials of this wave (lanes of column 0 own the row sums)
@@ -406,8 +413,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       const int right = (m == DM_N || m == DM_AN) ? A_UN : A_U;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 bh, bl;
-        frag_f32_split(&sm.arr[right][0][0], LDA, 16 * tj, 32 * ks, bh, bl);
+        const bf16x8 bh = frag_bf16(&sm.arrp[right][0][0][0], LDP, 16 * tj, 32 * ks);
+        const bf16x8 bl = frag_bf16(&sm.arrp[right][1][0][0], LDP, 16 * tj, 32 * ks);
         if (m == DM_O || m == DM_Q || m == DM_N) {  // left operand do / do~ (exact bf16)
           // ti is wave-dependent: select between registers, never index them
           const bf16x8 a0 = m == DM_O ? fdo[0][ks] : fdon[0][ks];
@@ -417,8 +424,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
           mma_bf16(acc, ah, bl);
         } else {
           const int left = m == DM_A ? A_DRHS : A_DRN;
-          bf16x8 ah, al;
-          frag_f32_split(&sm.arr[left][0][0], LDA, 16 * ti, 32 * ks, ah, al);
+          const bf16x8 ah = frag_bf16(&sm.arrp[left][0][0][0], LDP, 16 * ti, 32 * ks);
+          const bf16x8 al = frag_bf16(&sm.arrp[left][1][0][0], LDP, 16 * ti, 32 * ks);
           mma_bf16(acc, ah, bh);
           mma_bf16(acc, ah, bl);
           mma_bf16(acc, al, bh);
@@ -461,12 +468,13 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         const bf16x8 ado = fdo[tr][ks];
         mma_bf16(a_dq[tr], ado, sh);
         mma_bf16(a_dq[tr], ado, sl);
-        bf16x8 ah, al;
-        frag_f32_split(&sm.arr[A_DRHS][0][0], LDA, 16 * tr, 32 * ks, ah, al);
+        bf16x8 ah = frag_bf16(&sm.arrp[A_DRHS][0][0][0], LDP, 16 * tr, 32 * ks);
+        bf16x8 al = frag_bf16(&sm.arrp[A_DRHS][1][0][0], LDP, 16 * tr, 32 * ks);
         mma_bf16(a_dk1[tr], ah, sh);
         mma_bf16(a_dk1[tr], ah, sl);
         mma_bf16(a_dk1[tr], al, sh);
-        frag_f32_split(&sm.arr[A_U][0][0], LDA, 16 * tr, 32 * ks, ah, al);
+        ah = frag_bf16(&sm.arrp[A_U][0][0][0], LDP, 16 * tr, 32 * ks);
+        al = frag_bf16(&sm.arrp[A_U][1][0][0], LDP, 16 * tr, 32 * ks);
         mma_bf16(a_dk2[tr], ah, dh);
         mma_bf16(a_dk2[tr], ah, dl);
         mma_bf16(a_dk2[tr], al, dh);
@@ -474,7 +482,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
           const bf16x8 adon = fdon[tr][ks];
           mma_bf16(a_dqn[tr], adon, sh);
           mma_bf16(a_dqn[tr], adon, sl);
-          frag_f32_split(&sm.arr[A_DRN][0][0], LDA, 16 * tr, 32 * ks, ah, al);
+          ah = frag_bf16(&sm.arrp[A_DRN][0][0][0], LDP, 16 * tr, 32 * ks);
+          al = frag_bf16(&sm.arrp[A_DRN][1][0][0], LDP, 16 * tr, 32 * ks);
           mma_bf16(a_dkn[tr], ah, sh);
           mma_bf16(a_dkn[tr], ah, sl);
           mma_bf16(a_dkn[tr], al, sh);
@@ -494,7 +503,12 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   }
 
   // ================================================================ phase 3
-  // Gram adjoints -> dG (in place over the unweighted Grams) + gate partials
+  // Gram adjoints -> dG as bf16 hi / lo planes in both orientations (in the
+  // bytes of the d_v arrays, which every wave is done with) + gate partials
+  lds_barrier();
+  auto dgp = [&](int mtx, int orient, int plane) {  // [32][LDG] u16
+    return reinterpret_cast<u16 *>(&sm.arrp[0][0][0][0]) + (((size_t)mtx * 2 + orient) * 2 + plane) * C * LDG;
+  };
 #pragma unroll
   for (int jt = 0; jt < 3; ++jt) {
     const int t = wave + 8 * jt;
@@ -512,12 +526,12 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const float wj = noisyw ? sm.betan[j] : sm.beta[j];
     const float fj = noisyw ? sm.lgn[j] : sm.lg[j];
     float colw = 0.f, colf = 0.f;
+    float dgv[4];
     const int pbase = (m == DM_O || m == DM_A) ? P_G : (m == DM_Q || m == DM_K) ? P_GP : m == DM_N ? P_GE : P_GN;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + r;
-      float *cell = tr_store ? &sm.cc[ccm][j][i] : &sm.cc[ccm][i][j];
-      const float mw = *cell;  // unweighted masked Gram, already zero outside the mask
+      const float mw = tr_store ? sm.cc[ccm][j][i] : sm.cc[ccm][i][j];  // unweighted masked Gram (0 off the mask)
       float ei;
       bool mask;
       if (m == DM_O) { ei = sm.lg[i]; mask = j <= i; }
@@ -538,12 +552,29 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       const float dm = dM[jt][r];
       const float E = mask ? __expf(ei - fj) : 0.f;
       const float mfull = mw * wj;
-      *cell = dm * E * wj;  // dG
+      dgv[r] = dm * E * wj;  // dG[i][j]
       const float dd = dm * mfull;
       const float rs = row_sum16(dd);
       if (cl == 0) sm.part[wave][pbase][i] += rs;  // row part d e_i
       colf += dd;
       colw += dm * mw;
+    }
+    // dG[i0 .. i0+3][j]: orientation 0 rows i (scalar halves), orientation 1
+    // rows j (the four i are adjacent: one 8-byte write per plane)
+    {
+      uint32_t hw[2], lw[2];
+      u16 hb[4], lb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hb[r] = f2bf(dgv[r]);
+        lb[r] = f2bf(dgv[r] - bf2f(hb[r]));
+        dgp(m, 0, 0)[(i0 + r) * LDG + j] = hb[r];
+        dgp(m, 0, 1)[(i0 + r) * LDG + j] = lb[r];
+      }
+      hw[0] = hb[0] | ((uint32_t)hb[1] << 16); hw[1] = hb[2] | ((uint32_t)hb[3] << 16);
+      lw[0] = lb[0] | ((uint32_t)lb[1] << 16); lw[1] = lb[2] | ((uint32_t)lb[3] << 16);
+      *reinterpret_cast<uint2 *>(dgp(m, 1, 0) + j * LDG + i0) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2 *>(dgp(m, 1, 1) + j * LDG + i0) = make_uint2(lw[0], lw[1]);
     }
     // column parts: over the 4 row groups of the tile
     colf += __shfl_xor(colf, 16, 64);
@@ -568,29 +599,29 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const bf16x8 bk = frag_bf16_T(&sm.x[1][0][0], LDX, col0, 0);
     const bf16x8 bqn = frag_bf16_T(&sm.x[2][0][0], LDX, col0, 0);
     const bf16x8 bkn = frag_bf16_T(&sm.x[3][0][0], LDX, col0, 0);
-    auto gmul = [&](floatx4 &acc, int ccm, bool transposed, int ra, const bf16x8 &b) {
-      bf16x8 ah, al;
-      if (transposed) frag_f32_split_T(&sm.cc[ccm][0][0], LDM, ra, 0, ah, al);
-      else frag_f32_split(&sm.cc[ccm][0][0], LDM, ra, 0, ah, al);
+    // A = dG (orientation 0) or dG^T (orientation 1) rows ra .. ra + 15
+    auto gmul = [&](floatx4 &acc, int mtx, int orient, int ra, const bf16x8 &b) {
+      const bf16x8 ah = frag_bf16(dgp(mtx, orient, 0), LDG, ra, 0);
+      const bf16x8 al = frag_bf16(dgp(mtx, orient, 1), LDG, ra, 0);
       mma_bf16(acc, ah, b);
       mma_bf16(acc, al, b);
     };
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr) {
       const int ra = 16 * tr;
-      gmul(dq[tr], CC_MO, false, ra, bk);   // dq += dGo k
-      gmul(dk[tr], CC_MO, true, ra, bq);    // dk += dGo^T q + dGA k + dGA^T k
-      gmul(dk[tr], CC_AT, true, ra, bk);
-      gmul(dk[tr], CC_AT, false, ra, bk);
+      gmul(dq[tr], DM_O, 0, ra, bk);   // dq += dGo k
+      gmul(dk[tr], DM_O, 1, ra, bq);   // dk += dGo^T q + dGA k + dGA^T k
+      gmul(dk[tr], DM_A, 0, ra, bk);
+      gmul(dk[tr], DM_A, 1, ra, bk);
       if (has_noisy) {
-        gmul(dk[tr], CC_MQ, true, ra, bqn);   // + dGq^T q~ + dGk^T k~
-        gmul(dk[tr], CC_MK, true, ra, bkn);
-        gmul(dqn[tr], CC_MQ, false, ra, bk);  // dq~ += dGq k + dG~ k~
-        gmul(dqn[tr], CC_MN, false, ra, bkn);
-        gmul(dkn[tr], CC_MK, false, ra, bk);  // dk~ += dGk k + dGA~ k~ + dGA~^T k~ + dG~^T q~
-        gmul(dkn[tr], CC_ANT, true, ra, bkn);
-        gmul(dkn[tr], CC_ANT, false, ra, bkn);
-        gmul(dkn[tr], CC_MN, true, ra, bqn);
+        gmul(dk[tr], DM_Q, 1, ra, bqn);   // + dGq^T q~ + dGk^T k~
+        gmul(dk[tr], DM_K, 1, ra, bkn);
+        gmul(dqn[tr], DM_Q, 0, ra, bk);   // dq~ += dGq k + dG~ k~
+        gmul(dqn[tr], DM_N, 0, ra, bkn);
+        gmul(dkn[tr], DM_K, 0, ra, bk);   // dk~ += dGk k + dGA~ k~ + dGA~^T k~ + dG~^T q~
+        gmul(dkn[tr], DM_AN, 0, ra, bkn);
+        gmul(dkn[tr], DM_AN, 1, ra, bkn);
+        gmul(dkn[tr], DM_N, 1, ra, bqn);
       }
     }
   }
