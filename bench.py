@@ -46,8 +46,15 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # slot) are written once by the forward and read once by the backward.
 FWD_BYTES_PER_TH = 3 * 256 + 8 + 256
 BWD_BYTES_PER_TH = 4 * 256 + 8 + 3 * 256 + 8
-# the reverse scan needs q, k, do and the gates of both streams (not v)
-SCAN_BYTES_PER_TH = 3 * 256 + 8
+# the backward pre-pass reads q, k, do and the gates of both streams (not v)
+# and the six chunk matrices, and hands the reverse scan, per (chunk slot,
+# head), R (128 x 128 fp32), W (hi + lo bf16), two fragment sets of K and the
+# chunk decay; the scan reads that and writes the chunk's end-state adjoint
+# (128 x 128 fp32) for the per-chunk pass
+PRE_BYTES_PER_TH = 3 * 256 + 8
+PACK_BYTES_PER_SLOT_HEAD = (128 * 128 + 1024 + 2048 + 2048 + 64) * 4
+PRE_BYTES_PER_SLOT_HEAD = 6 * 32 * 32 * 4 + PACK_BYTES_PER_SLOT_HEAD
+SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4
 # the chunk-matrix pass reads q, k and the gates of both streams and writes six
 # 32 x 32 fp32 matrices per (chunk slot, head)
 TRI_BYTES_PER_TH = 2 * 256 + 8
@@ -219,6 +226,8 @@ def run_headline(torch, g, wl, dev, timer, up, args):
                      for i in range(vl.num_docs)))
     th_total, th_resp = T * H, n_resp * H
     ckpt_bytes = n_slots * H * d * d * 4
+    n_chunk_heads = H * sum((int(inp.cu_seqlens[i + 1] - inp.cu_seqlens[i]) + C - 1) // C
+                            for i in range(vl.num_docs))
 
     def step():
         g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
@@ -240,14 +249,16 @@ def run_headline(torch, g, wl, dev, timer, up, args):
         g.timing_enable(False)
         ms_step = timer.avg_ms("step")
         kern = {}
-        for name in ("gdn_dual_fwd_kernel", "gdn_tri_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel"):
+        for name in ("gdn_dual_fwd_kernel", "gdn_tri_kernel", "gdn_bwd_pre_kernel", "gdn_bwd_scan_kernel",
+                     "gdn_bwd_chunk_kernel"):
             ms, n = g.timing_avg_ms(name)
             kern[name] = {"ms": ms, "launches": n}
         g.timing_reset()
         alg = {
             "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
             "gdn_tri_kernel": TRI_BYTES_PER_TH * (th_total + th_resp) + TRI_BYTES_PER_SLOT_HEAD * n_slots * H,
-            "gdn_bwd_scan_kernel": SCAN_BYTES_PER_TH * (th_total + th_resp),
+            "gdn_bwd_pre_kernel": PRE_BYTES_PER_TH * (th_total + th_resp) + PRE_BYTES_PER_SLOT_HEAD * n_chunk_heads,
+            "gdn_bwd_scan_kernel": SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_bwd_chunk_kernel": BWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
         }
         fwd_flops = fwd_flops_per_th(d, C, B, False) * th_total + fwd_flops_per_th(d, C, B, True) * th_resp

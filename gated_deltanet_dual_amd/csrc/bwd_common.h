@@ -5,10 +5,56 @@
 #include "device_common.h"
 #include "gemm_lds.h"
 #include "kernels.h"
+#include "slab.h"
 
 namespace flare {
 
+// Slab (accumulator layout) of columns [col0, col0 + 16) of a [T, H, D] bf16
+// tensor: raw bits loaded from rows clamped into the document, then masked and
+// converted by slab_mask when consumed.
+template <int D>
+__device__ __forceinline__ void gslab_raw(u16 (&dst)[2][4], const u16 *src, int H, int h, int64_t t0g, int c0,
+                                          int n, int col0) {
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dst[tr][r] = src[((t0g + min(c0 + slab_row(tr, r), n - 1)) * H + h) * D + col0 + acc_col()];
+}
+// rows past the document end, and prompt rows of the noisy stream, read as 0
+__device__ __forceinline__ Slab slab_mask(const u16 (&raw)[2][4], int c0, int n, int P, bool noisy) {
+  Slab s;
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tpos = c0 + slab_row(tr, r);
+      const bool ok = tpos < n && (!noisy || tpos >= P);
+      s.t[tr][r] = ok ? bf2f(raw[tr][r]) : 0.f;
+    }
+  return s;
+}
+
 enum { CC_AT = 0, CC_T, CC_MO, CC_MQ, CC_MK, CC_ANT, CC_TN, CC_MN };
+
+// The hand-over from the backward pre-pass to the reverse scan, per (chunk
+// slot, head), in fp32 words (bf16 io, d = 128).  With the end-state adjoint
+// dS' of the chunk the scan's step is
+//   dS_c = g_C dS' + R + K^T (W (K dS')),
+// R the 128 x 128 state-independent right-hand side and W the 32 x 32 chain
+// matrix W_ij = -exp(lg_i) T_ji b_j exp(lg_C - lg_j).  Every operand is stored
+// in the register order of the wave that consumes it (16-byte units, lane
+// fastest), so the scan reads each with plain coalesced loads:
+//   R  [slab 8][tile 8][lane 64][4]  accumulator tile of d_v slab w, d_k tile kt
+//   W  [tile 2][hi/lo 2][lane 64][8 bf16]  A fragment rows 16 tr + (l & 15),
+//        columns in the slab k-permutation (slab.h)
+//   KA [ks 4][tile 2][lane 64][8 bf16]  A fragments of K (rows: chunk tokens,
+//        columns: d_k 32 ks + the slab k-permutation)
+//   KT [tile 8][lane 64][8 bf16]  A fragments of K^T (rows: d_k 16 kt + (l & 15),
+//        columns: chunk tokens in the slab k-permutation)
+//   G  g_C = exp(lg_C) in word 0
+constexpr int kPackR = 0, kPackW = kPackR + 16384, kPackKA = kPackW + 1024, kPackKT = kPackKA + 2048,
+              kPackG = kPackKT + 2048, kPackWords = kPackG + 64;
 
 // The gate value thread tid < 128 of a chunk reads: group g = tid / 32 of
 // (a, b, a~, b~), position i = tid % 32 (padded tokens and noisy prompt tokens:

@@ -863,11 +863,17 @@ static hipError_t launch_bwd_t(const BwdArgs &a_in, hipStream_t st) {
   const int64_t slots = a.T / Cfg::C + f.num_docs;
   a.tri = reinterpret_cast<float *>(a.workspace) + (size_t)slots * f.H * D * D;
   if constexpr (std::is_same<IO, u16>::value && D == 128) {
+    a.pack = a.tri + (size_t)slots * f.H * 6 * Cfg::C * Cfg::C;
     if (a.fwd_cm) {
       a.tri = const_cast<float *>(a.fwd_cm);  // read only from here on
     } else if (slots > 0) {
       TimedLaunch tl(K_TRI, st);
       hipError_t e0 = launch_tri_d128(a, st, slots);
+      if (e0 != hipSuccess) return e0;
+    }
+    if (slots > 0) {
+      TimedLaunch tl(K_BWD_PRE, st);
+      hipError_t e0 = launch_bwd_pre_d128(a, st, slots);
       if (e0 != hipSuccess) return e0;
     }
   }

@@ -67,30 +67,6 @@ __device__ __forceinline__ bf16x8 frag_mask(const uint4 &v, int c0, int n, int P
   return __builtin_bit_cast(bf16x8, ok ? v : make_uint4(0u, 0u, 0u, 0u));
 }
 
-// Slab (accumulator layout) of columns [col0, col0 + 16) of a [T, H, D] bf16
-// tensor: raw bits loaded from rows clamped into the document, then masked and
-// converted by slab_mask when consumed.
-__device__ __forceinline__ void gslab_raw(u16 (&dst)[2][4], const u16 *src, int H, int h, int64_t t0g, int c0,
-                                          int n, int col0) {
-#pragma unroll
-  for (int tr = 0; tr < 2; ++tr)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      dst[tr][r] = src[((t0g + min(c0 + slab_row(tr, r), n - 1)) * H + h) * kD + col0 + acc_col()];
-}
-__device__ __forceinline__ Slab slab_mask(const u16 (&raw)[2][4], int c0, int n, int P, bool noisy) {
-  Slab s;
-#pragma unroll
-  for (int tr = 0; tr < 2; ++tr)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tpos = c0 + slab_row(tr, r);
-      const bool ok = tpos < n && (!noisy || tpos >= P);
-      s.t[tr][r] = ok ? bf2f(raw[tr][r]) : 0.f;
-    }
-  return s;
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
@@ -139,10 +115,10 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   const float4 tri4 =
       *reinterpret_cast<const float4 *>(a.tri + ((size_t)slot * H + h) * 6 * C * C + 4 * tid);  // T, T~: 4 NT
   u16 rv[2][4], rvn[2][4], rdo[2][4], rdon[2][4];
-  gslab_raw(rv, pv, H, h, t0g, c0, n, col0);
-  gslab_raw(rvn, pvn, H, h, t0g, c0, n, col0);
-  gslab_raw(rdo, pdo, H, h, t0g, c0, n, col0);
-  gslab_raw(rdon, pdon, H, h, t0g, c0, n, col0);
+  gslab_raw<kD>(rv, pv, H, h, t0g, c0, n, col0);
+  gslab_raw<kD>(rvn, pvn, H, h, t0g, c0, n, col0);
+  gslab_raw<kD>(rdo, pdo, H, h, t0g, c0, n, col0);
+  gslab_raw<kD>(rdon, pdon, H, h, t0g, c0, n, col0);
   // S_c and dS' columns of the slab (k = 32 ks + 8 g + e over d_k), converted to
   // B fragments after the Gram phase
   float xs[4][8], xd[4][8];

@@ -95,9 +95,15 @@ size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   // the chunk's end-state adjoint (d_k x d_v), written by the reverse scan and
   // read by the per-chunk pass, then six kChunk x kChunk chunk matrices (the
   // triangular inverses T, T~ and four weighted Gram matrices), written by the
-  // chunk-matrix pass and read by both
-  const size_t per = (size_t)s->d_k * s->d_v + 6 * kChunk * kChunk;
+  // chunk-matrix pass and read by both; for bf16 io at d = 128 then the
+  // pre-pass's hand-over to the reverse scan
+  size_t per = (size_t)s->d_k * s->d_v + 6 * kChunk * kChunk;
+  if (bwd_uses_scan_pack(s)) per += kScanPackFloats;
   return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float) + 256;
+}
+
+bool bwd_uses_scan_pack(const flare_gdn_shape *s) {
+  return s->io_dtype == FLARE_BF16 && s->d_k == 128 && s->d_v == 128;
 }
 
 bool fwd_uses_chunk_matrices(const flare_gdn_shape *s) {

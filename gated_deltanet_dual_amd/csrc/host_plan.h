@@ -12,6 +12,11 @@ namespace flare {
 
 constexpr int kChunk = 32;          // tokens per chunk of the chunk-parallel scan
 constexpr int kVersion = 100;       // 0.1.0
+// fp32 words per (chunk slot, head) of the backward's hand-over from its
+// state-independent pre-pass to its reverse scan (bf16 io, d = 128): the
+// 128 x 128 right-hand side, the 32 x 32 chain matrix as hi / lo bf16
+// fragments, the chunk's k rows as two sets of bf16 fragments, the chunk decay
+constexpr int kScanPackFloats = 16384 + 1024 + 2048 + 2048 + 64;
 
 // Records a message for flare_last_error() and returns the status.
 flare_status fail(flare_status st, const char *fmt, ...);
@@ -41,8 +46,10 @@ int64_t ckpt_slot(int32_t cu_i, int32_t doc, int32_t chunk, int32_t stride);
 int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride);
 
 // Bytes of bwd workspace: per chunk slot and head, the end-state adjoint and
-// six chunk matrices (checkpoint slot layout).
+// six chunk matrices (checkpoint slot layout), and for bf16 io at d = 128 the
+// scan hand-over (kScanPackFloats).
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
+bool bwd_uses_scan_pack(const flare_gdn_shape *s);
 
 // Bytes of fwd workspace: six chunk matrices per chunk slot and head when the
 // forward runs its chunk-matrix pass (bf16 io, d = 128, no flags), else 0.

@@ -55,6 +55,7 @@ struct BwdArgs {
   int64_t T;
   float *tri;            // per slot and head [slots][H][6][32][32]: T, T~, Mwo, Mwq, Mwk, Mw~ (set by the launcher)
   const float *fwd_cm;   // the same matrices from the forward's workspace, or NULL
+  float *pack;           // bf16, d = 128: the pre-pass's hand-over to the scan, per slot and head (set by the launcher)
 };
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
 // per-chunk backward kernel for bf16 io at d = 128 (gdn_bwd_chunk.hip)
@@ -63,5 +64,8 @@ hipError_t launch_bwd_chunk_d128(const BwdArgs &a, hipStream_t st, int64_t slots
 hipError_t launch_bwd_scan_d128(const BwdArgs &a, hipStream_t st);
 // the chunk solves T, T~ into a.tri for bf16 io at d = 128 (gdn_tri.hip)
 hipError_t launch_tri_d128(const BwdArgs &a, hipStream_t st, int64_t slots);
+// the state-independent part of the reverse scan's chunk step into a.pack
+// (gdn_bwd_pre.hip)
+hipError_t launch_bwd_pre_d128(const BwdArgs &a, hipStream_t st, int64_t slots);
 
 }  // namespace flare

@@ -227,7 +227,9 @@ int32_t flare_version(void);
  * Kernel names: "gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel",
  * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel",
  * "gdn_tri_kernel" (the chunk-matrix pass of the forward and backward, bf16
- * io at d = 128; "gdn_dual_fwd_kernel" then names the forward march).
+ * io at d = 128; "gdn_dual_fwd_kernel" then names the forward march),
+ * "gdn_bwd_pre_kernel" (the backward's state-independent pre-pass, bf16 io at
+ * d = 128, run before the reverse scan).
  * flare_timing_enable(1) turns it on (events are created lazily, host side
  * only; no device memory is allocated), (0) off.  Returns the previous state.
  * flare_timing_avg_ms() blocks until the recorded launches of that kernel

@@ -118,6 +118,13 @@ def test_bwd_workspace_checked_before_launch(L):
     mis = ctypes.c_void_p(FAKE.value + 4)
     st = L.flare_gdn_dual_bwd(ctypes.byref(v), ctypes.byref(shape), *args, mis, need + 64, None)
     assert st == 5
+    # bf16 io at d = 128 adds the pre-pass's hand-over to the reverse scan:
+    # (fp32 words): R (128 x 128 fp32), W (32 x 32 as hi and lo bf16), K twice
+    # (32 x 128 bf16 each), the chunk decay padded to 64 words
+    big = g.GDNShape(2, 128, 128, 4, g.BF16, 0, 0.0)
+    need = L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(big), 1)
+    pack = 128 * 128 + 2 * 32 * 32 // 2 + 2 * (32 * 128 // 2) + 64
+    assert need == (64 // 32 + 2) * 2 * (128 * 128 + 6 * 32 * 32 + pack) * 4 + 256
 
 
 def test_ckpt_slots_never_overlap(L):
