@@ -55,6 +55,12 @@ PRE_BYTES_PER_TH = 3 * 256 + 8
 PACK_BYTES_PER_SLOT_HEAD = (128 * 128 + 1024 + 2048 + 2048 + 64) * 4
 PRE_BYTES_PER_SLOT_HEAD = 6 * 32 * 32 * 4 + PACK_BYTES_PER_SLOT_HEAD
 SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4
+# the forward pre-pass reads k, v and the clean gates and T, and writes the
+# hand-over; the forward scan reads that and writes the chunk-start states;
+# the output pass reads the layer's inputs, the six chunk matrices and the
+# chunk-start states and writes o, o~ (FWD_BYTES_PER_TH plus the states)
+FWD_PRE_BYTES_PER_TH = 2 * 256 + 8
+FWD_PRE_BYTES_PER_SLOT_HEAD = 32 * 32 * 4 + PACK_BYTES_PER_SLOT_HEAD
 # the chunk-matrix pass reads q, k and the gates of both streams and writes six
 # 32 x 32 fp32 matrices per (chunk slot, head)
 TRI_BYTES_PER_TH = 2 * 256 + 8
@@ -249,13 +255,16 @@ def run_headline(torch, g, wl, dev, timer, up, args):
         g.timing_enable(False)
         ms_step = timer.avg_ms("step")
         kern = {}
-        for name in ("gdn_dual_fwd_kernel", "gdn_tri_kernel", "gdn_bwd_pre_kernel", "gdn_bwd_scan_kernel",
-                     "gdn_bwd_chunk_kernel"):
+        for name in ("gdn_tri_kernel", "gdn_fwd_pre_kernel", "gdn_fwd_scan_kernel", "gdn_dual_fwd_kernel",
+                     "gdn_bwd_pre_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel"):
             ms, n = g.timing_avg_ms(name)
             kern[name] = {"ms": ms, "launches": n}
         g.timing_reset()
         alg = {
-            "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
+            "gdn_fwd_pre_kernel": FWD_PRE_BYTES_PER_TH * th_total + FWD_PRE_BYTES_PER_SLOT_HEAD * n_chunk_heads,
+            "gdn_fwd_scan_kernel": SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
+            "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes
+                                   + TRI_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_tri_kernel": TRI_BYTES_PER_TH * (th_total + th_resp) + TRI_BYTES_PER_SLOT_HEAD * n_slots * H,
             "gdn_bwd_pre_kernel": PRE_BYTES_PER_TH * (th_total + th_resp) + PRE_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_bwd_scan_kernel": SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,

@@ -880,7 +880,15 @@ static hipError_t launch_bwd_t(const BwdArgs &a_in, hipStream_t st) {
   {
     TimedLaunch tl(K_BWD_SCAN, st);
     if constexpr (std::is_same<IO, u16>::value && D == 128) {
-      hipError_t e1 = launch_bwd_scan_d128(a, st);
+      ScanArgs sa{};
+      sa.num_docs = f.num_docs;
+      sa.H = f.H;
+      sa.cu = f.cu;
+      sa.pack = a.pack;
+      sa.init = a.dh_final;
+      sa.final_out = a.dh0;
+      sa.states = reinterpret_cast<float *>(a.workspace);
+      hipError_t e1 = launch_scan_d128(sa, true, st);
       if (e1 != hipSuccess) return e1;
     } else {
       hipLaunchKernelGGL((gdn_bwd_scan_kernel<IO, D>), dim3((unsigned)(groups * 8 * Cfg::NTILE)), dim3(256), 0,

@@ -46,6 +46,7 @@
 
 #include "chunk_common.h"
 #include "device_common.h"
+#include "host_plan.h"
 #include "kernels.h"
 #include "timing.h"
 
@@ -716,19 +717,44 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
 hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st) {
   if (a.num_docs == 0) return hipSuccess;
   if (a.workspace) {
-    // bf16, d = 128, no flags: chunk matrices in parallel, then the march
-    const int64_t slots = a.T / 32 + a.num_docs;
-    BwdArgs b{};
-    b.f = a;
-    b.T = a.T;
-    b.tri = a.workspace;
+    // bf16, d = 128, no flags: chunk matrices and the scan hand-over in
+    // parallel, the state recurrence (chunk-start states -> ckpt, or the
+    // workspace when no checkpoints are asked for), then the outputs in parallel
+    const int64_t slots = a.T / kChunk + a.num_docs;
+    const size_t per = (size_t)slots * a.H;
+    float *const cmat = a.workspace;
+    float *const pack = cmat + per * 6 * kChunk * kChunk;
+    float *const states = a.ckpt ? a.ckpt : pack + per * kScanPackFloats;
     if (slots > 0) {
-      TimedLaunch tl(K_TRI, st);
-      hipError_t e = launch_tri_d128(b, st, slots);
+      BwdArgs b{};
+      b.f = a;
+      b.T = a.T;
+      b.tri = cmat;
+      {
+        TimedLaunch tl(K_TRI, st);
+        hipError_t e = launch_tri_d128(b, st, slots);
+        if (e != hipSuccess) return e;
+      }
+      TimedLaunch tl(K_FWD_PRE, st);
+      hipError_t e = launch_fwd_pre_d128(a, cmat, pack, st, slots);
       if (e != hipSuccess) return e;
     }
+    {
+      ScanArgs sa{};
+      sa.num_docs = a.num_docs;
+      sa.H = a.H;
+      sa.cu = a.cu;
+      sa.pack = pack;
+      sa.init = a.h0;
+      sa.final_out = a.h_final;
+      sa.states = states;
+      TimedLaunch tl(K_FWD_SCAN, st);
+      hipError_t e = launch_scan_d128(sa, false, st);
+      if (e != hipSuccess) return e;
+    }
+    if (slots == 0) return hipSuccess;
     TimedLaunch tl(K_FWD, st);
-    return launch_fwd_march_d128(a, a.workspace, st);
+    return launch_fwd_out_d128(a, cmat, states, st, slots);
   }
   // fp32 io is instantiated at d = 16 only (the fp32 tiles at d = 128 exceed the LDS budget)
   if (a.bf16) return a.D == 128 ? launch_fwd_t<u16, 128>(a, st) : launch_fwd_t<u16, 16>(a, st);

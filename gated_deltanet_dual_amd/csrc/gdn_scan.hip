@@ -1,0 +1,201 @@
+// gdn_scan.hip -- the sequential part of the chunked recurrence, forward
+// (the clean state) and reverse (the state adjoint), for bf16 io at
+// d_k = d_v = 128.
+//
+// A pre-pass (gdn_fwd_pre.hip, gdn_bwd_pre.hip) reduces every chunk's step to
+//   X <- g_C X + R + K^T (W (K X))
+// (R: 128 x 128 right-hand side, W: 32 x 32 chain matrix, K: the chunk's keys,
+// g_C: the chunk's decay), forward for the state S over the chunks of a
+// document, in reverse for the adjoint dS; so what stays sequential is three
+// small products per chunk.  The carried value before each chunk's step is
+// stored at that chunk's slot: the chunk-start states S_c (the checkpoints)
+// forward, the chunk end-state adjoints dS' in reverse.
+//
+// Every column of X evolves on its own, so a wave owns a 16-column slab of
+// d_v: its 128 x 16 slab of X lives in MFMA accumulators for the whole
+// document (8 tiles over d_k).  Every operand arrives in register order (the
+// pre-pass stores it so): a wave's R slab and its half of the operands all
+// slabs share (W and two fragment sets of K) are loaded four chunks ahead
+// into a register ring with 16-byte coalesced loads; the shared half is
+// published to the other wave through a double-buffered LDS area, one barrier
+// per chunk.  Four workgroups of two waves per (document, head), on one XCD so
+// the operands they share stay in that XCD's L2.
+#include "bwd_common.h"
+#include "device_common.h"
+#include "kernels.h"
+#include "slab.h"
+
+namespace flare {
+
+namespace {
+
+constexpr int sC = 32, sD = 128, sNW = 2, sNQ = sD / (16 * sNW);  // waves per workgroup, workgroups per (doc, head)
+constexpr int sRING = 4;                                            // register ring depth (chunks)
+// the operands every slab needs (W, then K and K^T fragments: contiguous in the
+// hand-over), in 1 KB units of 64 lanes x 16 bytes, split between the waves
+constexpr int sSH = (kPackKT + 2048 - kPackW) / 256, sSHW = sSH / sNW;
+static_assert(kPackKA == kPackW + 1024 && kPackKT == kPackKA + 2048, "shared operands must be contiguous");
+static_assert(sSH == 20 && sSH % sNW == 0, "shared units");
+
+// one chunk's loads for one wave: its R slab and its half of the shared units
+struct ScanRing {
+  uint4 r[8];
+  uint4 sh[sSHW];
+  float gc;  // g_C
+};
+
+struct ScanSmem {
+  alignas(16) uint4 sh[2][sSH][64];          // shared units, double-buffered by chunk parity
+  alignas(16) float stage[sNW][sD][16 + 4];  // per-wave staging of the carried slab for 16-byte stores
+};
+
+}  // namespace
+
+template <bool REVERSE>
+__global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
+  constexpr int C = sC, D = sD;
+  __shared__ ScanSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = 4 * (lane >> 4), cl = lane & 15;
+
+  // ---- workgroup -> (document, head, quarter); the quarters of a pair share an XCD
+  const int L = blockIdx.x;
+  const int grp = L / (8 * sNQ), rem = L % (8 * sNQ);
+  const int quarter = rem / 8;
+  const int pair = grp * 8 + (rem % 8);
+  if (pair >= a.num_docs * a.H) return;
+  const int doc = pair / a.H, h = pair % a.H;
+  const int H = a.H;
+  const int64_t t0g = a.cu[doc];
+  const int n = a.cu[doc + 1] - a.cu[doc];
+  const int nchunks = (n + C - 1) / C;
+  const int slab = sNW * quarter + wave;
+  const int dv0 = 16 * slab;
+  const int64_t ck_base = (int64_t)(t0g / C) + doc;
+
+  // ---- X slab: tile kt holds rows 16 kt + 4 g + r (d_k), column dv0 + cl
+  floatx4 X[8];
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    X[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (a.init) {
+      const float *src = a.init + ((size_t)doc * H + h) * D * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[kt][r] = src[(size_t)(16 * kt + g4 + r) * D + dv0 + cl];
+    }
+  }
+  // the X slab -> global, row-major [d_k][d_v], through this wave's LDS:
+  // 8 16-byte stores per lane instead of 32 scalar ones
+  auto store_X = [&](float *dst) {
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.stage[wave][16 * kt + g4 + r][cl] = X[kt][r];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int u = j * 64 + lane, row = u >> 2, c4 = u & 3;
+      *reinterpret_cast<float4 *>(dst + (size_t)row * D + dv0 + 4 * c4) =
+          *reinterpret_cast<const float4 *>(&sm.stage[wave][row][4 * c4]);
+    }
+  };
+  // Loads are unconditional (the chunk index is clamped into the document:
+  // an empty document still owns one slot), so no load sits under a branch:
+  // the compiler would otherwise wait for every load issued before it.
+  auto load_ring = [&](ScanRing &p, int c) {
+    c = max(0, min(c, nchunks - 1));
+    const float *pk = a.pack + ((size_t)(ck_base + c) * H + h) * kPackWords;
+    const uint4 *pr = reinterpret_cast<const uint4 *>(pk + kPackR) + (size_t)slab * 8 * 64;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) p.r[kt] = pr[kt * 64 + lane];
+    const uint4 *ps = reinterpret_cast<const uint4 *>(pk + kPackW) + (size_t)wave * sSHW * 64;
+#pragma unroll
+    for (int j = 0; j < sSHW; ++j) p.sh[j] = ps[j * 64 + lane];
+    p.gc = pk[kPackG];
+  };
+  auto bf = [](const uint4 &v) { return __builtin_bit_cast(bf16x8, v); };
+  // one chunk: store the carried X at the chunk's slot, publish this wave's
+  // half of the shared operands, then the step; the ring slot is refilled
+  // with chunk `refill` once R is used
+  auto step = [&](ScanRing &p, int c, int refill) {
+    store_X(a.states + ((ck_base + c) * H + h) * (size_t)D * D);
+    uint4 (*sh)[64] = sm.sh[c & 1];
+#pragma unroll
+    for (int j = 0; j < sSHW; ++j) sh[wave * sSHW + j][lane] = p.sh[j];
+    lds_barrier();
+    // KX = K X (X from the accumulators: k-slots of step ks are d_k rows
+    // 32 ks + 4 g + e (e < 4) and 32 ks + 16 + 4 g + e - 4, split hi + lo)
+    Slab KX = slab_zero();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float xv[8] = {X[2 * ks][0], X[2 * ks][1], X[2 * ks][2], X[2 * ks][3],
+                           X[2 * ks + 1][0], X[2 * ks + 1][1], X[2 * ks + 1][2], X[2 * ks + 1][3]};
+      bf16x8 bh, bl;
+      split8(xv, bh, bl);
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr) {
+        const bf16x8 ak = bf(sh[4 + 2 * ks + tr][lane]);
+        mma_bf16(KX.t[tr], ak, bh);
+        mma_bf16(KX.t[tr], ak, bl);
+      }
+    }
+    // Y = W KX
+    bf16x8 xh, xl;
+    slab_b_split(KX, xh, xl);
+    Slab Y = slab_zero();
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr) {
+      const bf16x8 wh = bf(sh[2 * tr][lane]), wl = bf(sh[2 * tr + 1][lane]);
+      mma_bf16(Y.t[tr], wh, xh);
+      mma_bf16(Y.t[tr], wh, xl);
+      mma_bf16(Y.t[tr], wl, xh);
+    }
+    // X <- g_C X + R + K^T Y
+    bf16x8 yh, yl;
+    slab_b_split(Y, yh, yl);
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      const float4 rv = __builtin_bit_cast(float4, p.r[kt]);
+      X[kt] = p.gc * X[kt] + floatx4{rv.x, rv.y, rv.z, rv.w};
+      mma_bf16(X[kt], bf(sh[12 + kt][lane]), yh);
+      mma_bf16(X[kt], bf(sh[12 + kt][lane]), yl);
+    }
+    load_ring(p, refill);
+  };
+
+  // step i handles chunk at(i); sRING operand sets in rotation, sRING - 1
+  // chunks in flight while one computes
+  auto at = [&](int i) { return REVERSE ? nchunks - 1 - i : i; };
+  ScanRing p0, p1, p2, p3;
+  static_assert(sRING == 4, "the rotation below names four sets");
+  load_ring(p0, at(0));
+  load_ring(p1, at(1));
+  load_ring(p2, at(2));
+  load_ring(p3, at(3));
+  for (int i = 0; i < nchunks; i += 4) {
+    step(p0, at(i), at(i + 4));
+    if (i + 1 >= nchunks) break;
+    step(p1, at(i + 1), at(i + 5));
+    if (i + 2 >= nchunks) break;
+    step(p2, at(i + 2), at(i + 6));
+    if (i + 3 >= nchunks) break;
+    step(p3, at(i + 3), at(i + 7));
+  }
+  if (a.final_out) {
+    float *dst = a.final_out + ((size_t)doc * H + h) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kt + g4 + r) * D + dv0 + cl] = X[kt][r];
+  }
+}
+
+hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st) {
+  const int pairs = a.num_docs * a.H;
+  const int groups = (pairs + 7) / 8;
+  const dim3 grid((unsigned)(groups * 8 * sNQ)), block(64 * sNW);
+  if (reverse) hipLaunchKernelGGL(gdn_scan_d128_kernel<true>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(gdn_scan_d128_kernel<false>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace flare

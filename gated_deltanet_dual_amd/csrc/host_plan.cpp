@@ -112,7 +112,10 @@ bool fwd_uses_chunk_matrices(const flare_gdn_shape *s) {
 
 size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   if (!fwd_uses_chunk_matrices(s)) return 0;
-  return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * 6 * kChunk * kChunk * sizeof(float) + 256;
+  // per chunk slot and head, fp32: the six chunk matrices, the scan hand-over,
+  // and room for the chunk-start state when no checkpoints are asked for
+  const size_t per = 6 * kChunk * kChunk + kScanPackFloats + (size_t)s->d_k * s->d_v;
+  return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float) + 256;
 }
 
 flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,

@@ -51,8 +51,9 @@ int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride);
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
 bool bwd_uses_scan_pack(const flare_gdn_shape *s);
 
-// Bytes of fwd workspace: six chunk matrices per chunk slot and head when the
-// forward runs its chunk-matrix pass (bf16 io, d = 128, no flags), else 0.
+// Bytes of fwd workspace when the forward runs its chunked passes (bf16 io,
+// d = 128, no flags), else 0: per chunk slot and head the six chunk matrices,
+// the scan hand-over and a chunk-start state.
 size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
 bool fwd_uses_chunk_matrices(const flare_gdn_shape *s);
 

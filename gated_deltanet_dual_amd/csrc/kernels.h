@@ -39,9 +39,24 @@ struct FwdArgs {
   int64_t T;
 };
 hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
-// forward march for bf16 io at d = 128 without flags (gdn_fwd_march.hip);
-// cmat: the chunk matrices of every (slot, head)
-hipError_t launch_fwd_march_d128(const FwdArgs &a, const float *cmat, hipStream_t st);
+// bf16 io at d = 128 without flags: the forward's pre-pass (chunk matrices
+// `cmat` -> scan hand-over `pack`, gdn_fwd_pre.hip) and its output pass
+// (chunk-start states -> o, o~, gdn_fwd_out.hip)
+hipError_t launch_fwd_pre_d128(const FwdArgs &a, const float *cmat, float *pack, hipStream_t st, int64_t slots);
+hipError_t launch_fwd_out_d128(const FwdArgs &a, const float *cmat, const float *states, hipStream_t st,
+                               int64_t slots);
+
+// The sequential chunk recurrence X <- g_C X + R + K^T (W (K X)) over the chunks
+// of each document (gdn_scan.hip), forward or in reverse.
+struct ScanArgs {
+  int num_docs, H;
+  const int32_t *cu;
+  const float *pack;   // per (chunk slot, head): the pre-pass's hand-over
+  const float *init;   // [N, H, 128, 128] X before the first step, or NULL (zero)
+  float *final_out;    // [N, H, 128, 128] X after the last step, or NULL
+  float *states;       // [slots, H, 128, 128]: X before the step of chunk c, at chunk c's slot
+};
+hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st);
 
 struct BwdArgs {
   FwdArgs f;
@@ -60,8 +75,6 @@ struct BwdArgs {
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
 // per-chunk backward kernel for bf16 io at d = 128 (gdn_bwd_chunk.hip)
 hipError_t launch_bwd_chunk_d128(const BwdArgs &a, hipStream_t st, int64_t slots);
-// reverse scan of the state adjoint for bf16 io at d = 128 (gdn_bwd_scan.hip)
-hipError_t launch_bwd_scan_d128(const BwdArgs &a, hipStream_t st);
 // the chunk solves T, T~ into a.tri for bf16 io at d = 128 (gdn_tri.hip)
 hipError_t launch_tri_d128(const BwdArgs &a, hipStream_t st, int64_t slots);
 // the state-independent part of the reverse scan's chunk step into a.pack

@@ -5,7 +5,9 @@
 
 namespace flare {
 
-enum KernelId { K_FWD = 0, K_BWD_SCAN, K_BWD_CHUNK, K_BLOCK_STEP, K_SHORTCONV, K_TRI, K_BWD_PRE, K_COUNT };
+enum KernelId {
+  K_FWD = 0, K_BWD_SCAN, K_BWD_CHUNK, K_BLOCK_STEP, K_SHORTCONV, K_TRI, K_BWD_PRE, K_FWD_PRE, K_FWD_SCAN, K_COUNT
+};
 
 // Records a start event on construction and a stop event on destruction, on
 // `st`, when timing is enabled; does nothing otherwise.

@@ -98,7 +98,10 @@ int32_t flare_gdn_chunk_size(void);
  * configuration needs none (the forward needs workspace only for bf16 io at
  * d = 128 without flags) and on invalid arguments.  The workspace holds, per
  * chunk slot (checkpoint slot layout, stride 1) and head, six 32 x 32 fp32
- * chunk matrices, and for the backward also the chunk's end-state adjoint. */
+ * chunk matrices first; for the backward also the chunk's end-state adjoint;
+ * at bf16 io and d = 128 also the hand-over between a chunk pre-pass and the
+ * sequential scan (86272 bytes), and for the forward room for the chunk-start
+ * state (used when no checkpoints are asked for). */
 size_t flare_gdn_dual_workspace_size(const flare_varlen *varlen,
                                      const flare_gdn_shape *shape, int for_bwd);
 
@@ -226,10 +229,12 @@ int32_t flare_version(void);
  * (the backward launches the reverse scan, then the per-chunk kernel).
  * Kernel names: "gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel",
  * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel",
- * "gdn_tri_kernel" (the chunk-matrix pass of the forward and backward, bf16
- * io at d = 128; "gdn_dual_fwd_kernel" then names the forward march),
- * "gdn_bwd_pre_kernel" (the backward's state-independent pre-pass, bf16 io at
- * d = 128, run before the reverse scan).
+ * and, for bf16 io at d = 128, the chunked passes: "gdn_tri_kernel" (the
+ * chunk matrices, forward and backward), "gdn_fwd_pre_kernel" and
+ * "gdn_bwd_pre_kernel" (the state-independent parts of the chunk steps),
+ * "gdn_fwd_scan_kernel" (the forward state recurrence; "gdn_dual_fwd_kernel"
+ * then names the forward's output pass) and "gdn_bwd_scan_kernel" (the
+ * reverse recurrence).
  * flare_timing_enable(1) turns it on (events are created lazily, host side
  * only; no device memory is allocated), (0) off.  Returns the previous state.
  * flare_timing_avg_ms() blocks until the recorded launches of that kernel

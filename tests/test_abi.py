@@ -91,8 +91,12 @@ def test_fwd_workspace_checked_before_launch(L):
     shape = g.GDNShape(4, 128, 128, 4, g.BF16, 0, 0.0)
     v = varlen([0, 100, 164], [20, 0])
     need = L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(shape), 0)
-    # six 32 x 32 fp32 chunk matrices per chunk slot and head
-    assert need == (164 // 32 + 2) * 4 * 6 * 32 * 32 * 4 + 256
+    # per chunk slot and head (fp32 words): six 32 x 32 chunk matrices, the
+    # pre-pass's hand-over to the scan (R 128 x 128 fp32, W 32 x 32 as hi and
+    # lo bf16, K twice as 32 x 128 bf16, the decay padded to 64 words), and a
+    # 128 x 128 chunk-start state
+    pack = 128 * 128 + 2 * 32 * 32 // 2 + 2 * (32 * 128 // 2) + 64
+    assert need == (164 // 32 + 2) * 4 * (6 * 32 * 32 + pack + 128 * 128) * 4 + 256
     P = [FAKE] * 10
     st = L.flare_gdn_dual_fwd(ctypes.byref(v), ctypes.byref(shape), *P, None, FAKE, FAKE, None, None, 1,
                               FAKE, need - 1, None)
