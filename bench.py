@@ -59,8 +59,12 @@ SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4
 # hand-over; the forward scan reads that and writes the chunk-start states;
 # the output pass reads the layer's inputs, the six chunk matrices and the
 # chunk-start states and writes o, o~ (FWD_BYTES_PER_TH plus the states)
+# (the forward's hand-over carries Z = diag(D) T V, 32 x 128 fp32, in place
+# of the backward's 128 x 128 R)
 FWD_PRE_BYTES_PER_TH = 2 * 256 + 8
-FWD_PRE_BYTES_PER_SLOT_HEAD = 32 * 32 * 4 + PACK_BYTES_PER_SLOT_HEAD
+FWD_PACK_BYTES_PER_SLOT_HEAD = (32 * 128 + 1024 + 2048 + 2048 + 64) * 4
+FWD_PRE_BYTES_PER_SLOT_HEAD = 32 * 32 * 4 + FWD_PACK_BYTES_PER_SLOT_HEAD
+FWD_SCAN_BYTES_PER_SLOT_HEAD = FWD_PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4
 # the chunk-matrix pass reads q, k and the gates of both streams and writes six
 # 32 x 32 fp32 matrices per (chunk slot, head)
 TRI_BYTES_PER_TH = 2 * 256 + 8
@@ -262,7 +266,7 @@ def run_headline(torch, g, wl, dev, timer, up, args):
         g.timing_reset()
         alg = {
             "gdn_fwd_pre_kernel": FWD_PRE_BYTES_PER_TH * th_total + FWD_PRE_BYTES_PER_SLOT_HEAD * n_chunk_heads,
-            "gdn_fwd_scan_kernel": SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
+            "gdn_fwd_scan_kernel": FWD_SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes
                                    + TRI_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_tri_kernel": TRI_BYTES_PER_TH * (th_total + th_resp) + TRI_BYTES_PER_SLOT_HEAD * n_slots * H,

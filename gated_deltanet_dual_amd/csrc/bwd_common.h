@@ -46,6 +46,8 @@ enum { CC_AT = 0, CC_T, CC_MO, CC_MQ, CC_MK, CC_ANT, CC_TN, CC_MN };
 // in the register order of the wave that consumes it (16-byte units, lane
 // fastest), so the scan reads each with plain coalesced loads:
 //   R  [slab 8][tile 8][lane 64][4]  accumulator tile of d_v slab w, d_k tile kt
+//        (the forward, whose R is K^T Z, stores the C x d_v matrix Z here
+//        instead: [slab 8][tile 2][lane 64][4])
 //   W  [tile 2][hi/lo 2][lane 64][8 bf16]  A fragment rows 16 tr + (l & 15),
 //        columns in the slab k-permutation (slab.h)
 //   KA [ks 4][tile 2][lane 64][8 bf16]  A fragments of K (rows: chunk tokens,

@@ -8,14 +8,14 @@
 // matrices from the chunk-matrix pass (gdn_tri.hip),
 //   U    = T (V - diag(G) K S_c),   S_{c+1} = G_C S_c + K^T diag(D) U,
 // D_i = b_i G_C / G_i.  Only K S_c carries the state, so
-//   S_{c+1} = G_C S_c + R + K^T (W (K S_c)),
-//   R = K^T (diag(D) T V),   W = -diag(D) T diag(G),
-// the same step as the backward's reverse scan.  This kernel forms R, W, G_C
-// and the two fragment sets of K in the order the scan consumes them
-// (bwd_common.h).
+//   S_{c+1} = G_C S_c + K^T (Z + W (K S_c)),
+//   Z = diag(D) T V,   W = -diag(D) T diag(G),
+// the backward's reverse step with its right-hand side R = K^T Z.  This
+// kernel forms Z, W, G_C and the two fragment sets of K in the order the scan
+// consumes them (bwd_common.h; Z in the R area as [slab 8][tile 2][lane 64][4]).
 //
 // One workgroup of 8 waves per (chunk slot, head); wave w owns d_v columns
-// [16 w, 16 w + 16) of R (a register slab, slab.h) and one fragment set.
+// [16 w, 16 w + 16) of Z (a register slab, slab.h) and one fragment set.
 #include "bwd_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -129,28 +129,18 @@ __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const 
   }
   if (tid == 0) pack[kPackG] = __expf(lgC);
 
-  // ---- R = K^T (diag(D) T V) for this wave's slab
+  // ---- Z = diag(D) T V for this wave's slab (R = K^T Z: the scan adds Z to
+  // W (K S_c) ahead of its K^T product), stored as [slab][tile][lane][4]
   const Slab V = slab_mask(rv, c0, n, P, false);
-  Slab TV = slab_zero();
-  cc_mul<2, false>(TV, &sm.tm[0][0], LDM, V);
+  Slab Z = slab_zero();
+  cc_mul<2, false>(Z, &sm.tm[0][0], LDM, V);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) TV.t[tr][r] *= Dd(slab_row(tr, r));
-  bf16x8 yh, yl;
-  slab_b_split(TV, yh, yl);
-  float4 *rdst = reinterpret_cast<float4 *>(pack + kPackR) + (size_t)wave * 8 * 64;
+    for (int r = 0; r < 4; ++r) Z.t[tr][r] *= Dd(slab_row(tr, r));
+  float4 *zdst = reinterpret_cast<float4 *>(pack + kPackR) + (size_t)wave * 2 * 64;
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    const u16 *col = &sm.kt[16 * kt + cl][0];
-    const uint2 lo4 = *reinterpret_cast<const uint2 *>(col + g4);
-    const uint2 hi4 = *reinterpret_cast<const uint2 *>(col + 16 + g4);
-    const bf16x8 ak = __builtin_bit_cast(bf16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma_bf16(acc, ak, yh);
-    mma_bf16(acc, ak, yl);
-    rdst[kt * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  }
+  for (int tr = 0; tr < 2; ++tr) zdst[tr * 64 + lane] = make_float4(Z.t[tr][0], Z.t[tr][1], Z.t[tr][2], Z.t[tr][3]);
 }
 
 hipError_t launch_fwd_pre_d128(const FwdArgs &a, const float *cmat, float *pack, hipStream_t st, int64_t slots) {

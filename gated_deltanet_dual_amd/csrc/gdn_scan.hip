@@ -4,6 +4,8 @@
 //
 // A pre-pass (gdn_fwd_pre.hip, gdn_bwd_pre.hip) reduces every chunk's step to
 //   X <- g_C X + R + K^T (W (K X))
+// (forward: R = K^T Z with Z only C x d_v, so the scan adds Z to W (K X) and
+// reads a quarter of the bytes)
 // (R: 128 x 128 right-hand side, W: 32 x 32 chain matrix, K: the chunk's keys,
 // g_C: the chunk's decay), forward for the state S over the chunks of a
 // document, in reverse for the adjoint dS; so what stays sequential is three
@@ -14,12 +16,12 @@
 // Every column of X evolves on its own, so a wave owns a 16-column slab of
 // d_v: its 128 x 16 slab of X lives in MFMA accumulators for the whole
 // document (8 tiles over d_k).  Every operand arrives in register order (the
-// pre-pass stores it so): a wave's R slab and its half of the operands all
-// slabs share (W and two fragment sets of K) are loaded four chunks ahead
-// into a register ring with 16-byte coalesced loads; the shared half is
-// published to the other wave through a double-buffered LDS area, one barrier
-// per chunk.  Four workgroups of two waves per (document, head), on one XCD so
-// the operands they share stay in that XCD's L2.
+// pre-pass stores it so): a wave's R slab and its share of the operands all
+// slabs need (W and two fragment sets of K) are loaded four chunks ahead into
+// a register ring with 16-byte coalesced loads; the shared operands are
+// published to the other waves through a double-buffered LDS area, one
+// barrier per chunk.  Two slabs form a workgroup, four workgroups per
+// (document, head), on one XCD so the operands they share stay in its L2.
 #include "bwd_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -32,14 +34,16 @@ namespace {
 constexpr int sC = 32, sD = 128, sNW = 2, sNQ = sD / (16 * sNW);  // waves per workgroup, workgroups per (doc, head)
 constexpr int sRING = 4;                                            // register ring depth (chunks)
 // the operands every slab needs (W, then K and K^T fragments: contiguous in the
-// hand-over), in 1 KB units of 64 lanes x 16 bytes, split between the waves
-constexpr int sSH = (kPackKT + 2048 - kPackW) / 256, sSHW = sSH / sNW;
+// hand-over), in 1 KB units of 64 lanes x 16 bytes, dealt round-robin to the waves
+constexpr int sSH = (kPackKT + 2048 - kPackW) / 256, sSHW = (sSH + sNW - 1) / sNW;
 static_assert(kPackKA == kPackW + 1024 && kPackKT == kPackKA + 2048, "shared operands must be contiguous");
-static_assert(sSH == 20 && sSH % sNW == 0, "shared units");
+static_assert(sSH == 20, "shared units");
 
-// one chunk's loads for one wave: its R slab and its half of the shared units
+// one chunk's loads for one wave: its right-hand side (the R slab, or the Z
+// slab when the right-hand side is K^T Z) and its half of the shared units
+template <bool ZRHS>
 struct ScanRing {
-  uint4 r[8];
+  uint4 r[ZRHS ? 2 : 8];
   uint4 sh[sSHW];
   float gc;  // g_C
 };
@@ -51,8 +55,12 @@ struct ScanSmem {
 
 }  // namespace
 
-template <bool REVERSE>
+// ZRHS: the right-hand side is K^T Z with Z a C x d_v matrix (stored as
+// slabs, [slab 8][tile 2][lane 64][4], in the R area of the hand-over), added
+// to W (K X) before the K^T product; else a full 128 x 128 R.
+template <bool REVERSE, bool ZRHS>
 __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
+  using ScanRing = ScanRing<ZRHS>;
   constexpr int C = sC, D = sD;
   __shared__ ScanSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -104,12 +112,15 @@ __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
   auto load_ring = [&](ScanRing &p, int c) {
     c = max(0, min(c, nchunks - 1));
     const float *pk = a.pack + ((size_t)(ck_base + c) * H + h) * kPackWords;
-    const uint4 *pr = reinterpret_cast<const uint4 *>(pk + kPackR) + (size_t)slab * 8 * 64;
+    constexpr int NR = ZRHS ? 2 : 8;
+    const uint4 *pr = reinterpret_cast<const uint4 *>(pk + kPackR) + (size_t)slab * NR * 64;
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) p.r[kt] = pr[kt * 64 + lane];
-    const uint4 *ps = reinterpret_cast<const uint4 *>(pk + kPackW) + (size_t)wave * sSHW * 64;
+    for (int j = 0; j < NR; ++j) p.r[j] = pr[j * 64 + lane];
+    // shared unit j * sNW + wave (clamped: the last round is partial, and
+    // its surplus loads are repeats that are never published)
+    const uint4 *ps = reinterpret_cast<const uint4 *>(pk + kPackW);
 #pragma unroll
-    for (int j = 0; j < sSHW; ++j) p.sh[j] = ps[j * 64 + lane];
+    for (int j = 0; j < sSHW; ++j) p.sh[j] = ps[min(j * sNW + wave, sSH - 1) * 64 + lane];
     p.gc = pk[kPackG];
   };
   auto bf = [](const uint4 &v) { return __builtin_bit_cast(bf16x8, v); };
@@ -120,7 +131,8 @@ __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
     store_X(a.states + ((ck_base + c) * H + h) * (size_t)D * D);
     uint4 (*sh)[64] = sm.sh[c & 1];
 #pragma unroll
-    for (int j = 0; j < sSHW; ++j) sh[wave * sSHW + j][lane] = p.sh[j];
+    for (int j = 0; j < sSHW; ++j)
+      if (j * sNW + wave < sSH) sh[j * sNW + wave][lane] = p.sh[j];
     lds_barrier();
     // KX = K X (X from the accumulators: k-slots of step ks are d_k rows
     // 32 ks + 4 g + e (e < 4) and 32 ks + 16 + 4 g + e - 4, split hi + lo)
@@ -149,13 +161,24 @@ __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
       mma_bf16(Y.t[tr], wh, xl);
       mma_bf16(Y.t[tr], wl, xh);
     }
-    // X <- g_C X + R + K^T Y
+    // X <- g_C X + R + K^T Y, or g_C X + K^T (Y + Z)
+    if constexpr (ZRHS) {
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr) {
+        const float4 zv = __builtin_bit_cast(float4, p.r[tr]);
+        Y.t[tr] += floatx4{zv.x, zv.y, zv.z, zv.w};
+      }
+    }
     bf16x8 yh, yl;
     slab_b_split(Y, yh, yl);
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
-      const float4 rv = __builtin_bit_cast(float4, p.r[kt]);
-      X[kt] = p.gc * X[kt] + floatx4{rv.x, rv.y, rv.z, rv.w};
+      if constexpr (ZRHS) {
+        X[kt] = p.gc * X[kt];
+      } else {
+        const float4 rv = __builtin_bit_cast(float4, p.r[kt]);
+        X[kt] = p.gc * X[kt] + floatx4{rv.x, rv.y, rv.z, rv.w};
+      }
       mma_bf16(X[kt], bf(sh[12 + kt][lane]), yh);
       mma_bf16(X[kt], bf(sh[12 + kt][lane]), yl);
     }
@@ -193,8 +216,9 @@ hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st) {
   const int pairs = a.num_docs * a.H;
   const int groups = (pairs + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * sNQ)), block(64 * sNW);
-  if (reverse) hipLaunchKernelGGL(gdn_scan_d128_kernel<true>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(gdn_scan_d128_kernel<false>, grid, block, 0, st, a);
+  // the reverse recurrence carries a full R, the forward one K^T Z
+  if (reverse) hipLaunchKernelGGL((gdn_scan_d128_kernel<true, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((gdn_scan_d128_kernel<false, true>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
