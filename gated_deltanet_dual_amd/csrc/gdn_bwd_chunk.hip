@@ -4,20 +4,23 @@
 // only the schedule differs.
 //
 // One workgroup of 8 waves per (chunk slot, head), fully parallel over chunks.
-//   phase 0  q, k, q~, k~ rows and gates -> LDS; the six masked Gram matrices
-//            (waves 0-3) and the two unit-triangular solves (waves 0, 1).
+//   phase 0  q, k, q~, k~ rows, gates and the chunk matrices of the
+//            chunk-matrix pass (T, T~ and the weighted masked Grams Mwo, Mwq,
+//            Mwk, Mw~, gdn_tri.hip) -> LDS.
 //   phase 1  wave w owns d_v columns [16w, 16w + 16).  Every C x 16 quantity of
 //            the chunk -- K S_c, U, the noisy reads r_q, r_k, u~, the noisy
 //            adjoints, dU, drhs -- is computed in MFMA accumulator registers and
 //            fed straight back into the next product (slab.h), so the whole
 //            column-separable chain runs without LDS round trips or barriers.
 //            S_c and dS' columns come straight from global memory as B
-//            fragments; dv and dv~ are stored from registers.
+//            fragments; v, v~, do, do~ rows are staged through LDS.
 //   phase 2  the products that reduce over d_v: wave w takes three 16 x 16
 //            tiles of the six Gram adjoints and the 16-column d_k tile w of
 //            dq, dk, dq~, dk~, with U, u~, drhs, drhs~ shared through LDS.
-//   phase 3  Gram adjoints -> Gram-weight gradients, their contractions with
-//            the q/k rows, gate gradients, stores.
+//   phase 3  Gram adjoints -> Gram-weight gradients (each wave recomputes the
+//            raw q/k products of its three tiles with MFMA, instead of keeping
+//            six unweighted Gram matrices in LDS), their contractions with the
+//            q/k rows, gate gradients, stores.
 // Nothing is reduced across workgroups, so the result is deterministic.
 #include "bwd_common.h"
 #include "chunk_common.h"
@@ -35,11 +38,12 @@ constexpr int kC = 32, kD = 128, kNW = 8, kNT = 64 * kNW;
 constexpr int kLDX = kD + 8, kLDM = kC + 4, kLDP = kD + 8, kLDG = kC + 8;
 enum { P_G = 0, P_GN, P_B, P_BN, P_GP, P_GE, P_C, P_NUM };
 enum { A_U = 0, A_UN, A_DRHS, A_DRN };
+enum { KC_T = 0, KC_TN, KC_MWO, KC_MWQ, KC_MWK, KC_MWN };  // the chunk-matrix pass's order
 static_assert(6 * 2 * 2 * kC * kLDG <= 4 * 2 * kC * kLDP, "dG planes must fit in the d_v arrays");
 
 struct Chunk2Smem {
   alignas(16) u16 x[4][kC][kLDX];       // q, k, q~, k~ ; at the end the staging of dq, dk, dq~, dk~
-  alignas(16) float cc[8][kC][kLDM];    // unweighted masked Grams (A, A~ transposed), T, T~; later dG
+  alignas(16) float cc[6][kC][kLDM];    // T, T~ and the weighted masked Grams Mwo, Mwq, Mwk, Mw~
   // U, u~, drhs, drhs~ for the d_v reductions as bf16 hi / lo planes (each
   // value split once, by the wave that computed it); after those reductions
   // the same bytes hold the Gram-weight gradients dG, [6][orientation][hi, lo][kC][kLDG]
@@ -97,8 +101,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
 
   // ================================================================ phase 0
   // every global load of the phase first, so they are all in flight together:
-  // q, k, q~, k~ rows (4 16-byte units per thread), gates, T and T~ (one float4
-  // per thread), this wave's v, v~, do, do~ columns and S_c, dS' columns.
+  // q, k, q~, k~ rows and v, v~, do, do~ rows (4 + 4 16-byte units per
+  // thread), gates, T and T~ (one float4 per thread), S_c and dS' columns.
   constexpr int RU = D / 8, PU = C * RU, UX = 4 * PU / NT;
   uint4 xr[UX];
 #pragma unroll
@@ -112,13 +116,21 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     xr[e] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
   }
   const float gval = tid < 4 * C ? gate_load(f, t0g, c0, n, P, h, tid) : 0.f;
-  const float4 tri4 =
-      *reinterpret_cast<const float4 *>(a.tri + ((size_t)slot * H + h) * 6 * C * C + 4 * tid);  // T, T~: 4 NT
-  u16 rv[2][4], rvn[2][4], rdo[2][4], rdon[2][4];
-  gslab_raw<kD>(rv, pv, H, h, t0g, c0, n, col0);
-  gslab_raw<kD>(rvn, pvn, H, h, t0g, c0, n, col0);
-  gslab_raw<kD>(rdo, pdo, H, h, t0g, c0, n, col0);
-  gslab_raw<kD>(rdon, pdon, H, h, t0g, c0, n, col0);
+  float4 tri4[3];  // the six chunk matrices
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    tri4[j] = reinterpret_cast<const float4 *>(a.tri + ((size_t)slot * H + h) * 6 * C * C)[j * NT + tid];
+  // v, v~, do, do~ rows: staged through LDS (the bytes of the d_v arrays, which
+  // phase 1 fills only after every wave has taken its slab from them)
+  uint4 vr[UX];
+#pragma unroll
+  for (int e = 0; e < UX; ++e) {
+    const int u = e * NT + tid;
+    const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
+    const u16 *src = m == 0 ? pv : m == 1 ? pvn : m == 2 ? pdo : pdon;
+    vr[e] = *reinterpret_cast<const uint4 *>(src + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu16 * 8);
+  }
+  u16 (*const vst)[C][LDX] = reinterpret_cast<u16 (*)[C][LDX]>(&sm.arrp[0][0][0][0]);
   // S_c and dS' columns of the slab (k = 32 ks + 8 g + e over d_k), converted to
   // B fragments after the Gram phase
   float xs[4][8], xd[4][8];
@@ -130,8 +142,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       xs[ks][e] = Sc[off];
       xd[ks][e] = dSn[off];
     }
-  // LDS: zero the Gram matrices and partials, then the loaded rows, T, T~, gates
-  for (int e = tid; e < 8 * C * LDM; e += NT) (&sm.cc[0][0][0])[e] = 0.f;
+  // LDS: zero the partials, then the loaded rows, the chunk matrices, gates
   for (int e = tid; e < kNW * P_NUM * C; e += NT) (&sm.part[0][0][0])[e] = 0.f;
   lds_barrier();
 #pragma unroll
@@ -139,15 +150,18 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const int u = e * NT + tid;
     const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
     *reinterpret_cast<uint4 *>(&sm.x[m][row][cu16 * 8]) = xr[e];
+    // v, v~, do, do~: rows past the document end, and the noisy ones' prompt rows, read 0
+    const int tpos = c0 + row;
+    const bool ok = tpos < n && ((m & 1) == 0 || tpos >= P);
+    *reinterpret_cast<uint4 *>(&vst[m][row][cu16 * 8]) = ok ? vr[e] : make_uint4(0u, 0u, 0u, 0u);
   }
-  {
-    const int which = tid / (C * C / 4), rr = tid % (C * C / 4), row = rr / (C / 4), c4 = rr % (C / 4);
-    *reinterpret_cast<float4 *>(&sm.cc[which ? CC_TN : CC_T][row][4 * c4]) = tri4;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int u = j * NT + tid, which = u / (C * C / 4), rr = u % (C * C / 4);
+    *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = tri4[j];
   }
   if (tid < 4 * C) gate_scan(gval, B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   lds_barrier();
-  if (wave < 4)
-    chunk_grams<true, D, LDX, LDM>(sm.x, sm.cc, sm.lg, sm.beta, sm.lgn, sm.betan, c0, n, P, B, has_noisy, false);
 
   const float lgC = sm.lg[C - 1];
   auto Gm = [&](int i) { return __expf(sm.lg[i]); };
@@ -156,8 +170,6 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   auto Dd = [&](int i) { return sm.beta[i] * __expf(lgC - sm.lg[i]); };
   auto resp_row = [&](int i) { return c0 + i < n && c0 + i >= P; };
 
-  const Slab V = slab_mask(rv, c0, n, P, false), VN = slab_mask(rvn, c0, n, P, true);
-  const Slab DO = slab_mask(rdo, c0, n, P, false), DON = slab_mask(rdon, c0, n, P, true);
   bf16x8 sbh[4], sbl[4], dbh[4], dbl[4];
   float plg = 0.f;  // <dS', S_c> over this slab, fp32
 #pragma unroll
@@ -190,6 +202,17 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         mma_bf16(KNS.t[tr], akn, sbl[ks]);
       }
     }
+  // this wave's v, v~, do, do~ slabs (taken before the barrier: after it, waves
+  // write the d_v arrays over the staged rows)
+  auto slab_of = [&](int m) {
+    Slab sl;
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sl.t[tr][r] = bf2f(vst[m][slab_row(tr, r)][col0 + cl]);
+    return sl;
+  };
+  const Slab V = slab_of(0), VN = slab_of(1), DO = slab_of(2), DON = slab_of(3);
   lds_barrier();  // the Gram matrices visible
 
   // ================================================================ phase 1
@@ -210,12 +233,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       pg[tr][r] += s * Gm(i) * row_sum16(QS.t[tr][r] * DO.t[tr][r]);  // d gamma_i from o_i = s G_i q_i S_c
     }
   Slab U = slab_zero();
-  cc_mul<3, false>(U, &sm.cc[CC_T][0][0], LDM, rhs);
-  Slab BU;
-#pragma unroll
-  for (int tr = 0; tr < 2; ++tr)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) BU.t[tr][r] = sm.beta[slab_row(tr, r)] * U.t[tr][r];
+  cc_mul<3, false>(U, &sm.cc[KC_T][0][0], LDM, rhs);
 
   // noisy reads and block: r_q, r_k, u~ ; noisy adjoints dr_q, du~, drhs~, dr_k
   Slab UN = slab_zero(), DRQ = slab_zero(), DRN = slab_zero(), DUN = slab_zero();
@@ -231,29 +249,29 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       }
     RQ = RQ0;
     RK = RK0;
-    cc_mul<3, false>(RQ, &sm.cc[CC_MQ][0][0], LDM, BU);
-    cc_mul<3, false>(RK, &sm.cc[CC_MK][0][0], LDM, BU);
+    cc_mul<3, false>(RQ, &sm.cc[KC_MWQ][0][0], LDM, U);  // + Mq diag(b) U
+    cc_mul<3, false>(RK, &sm.cc[KC_MWK][0][0], LDM, U);
     Slab rhsn;
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
       for (int r = 0; r < 4; ++r) rhsn.t[tr][r] = VN.t[tr][r] - __expf(sm.lgn[slab_row(tr, r)]) * RK.t[tr][r];
-    cc_mul<3, false>(UN, &sm.cc[CC_TN][0][0], LDM, rhsn);
-    // du~ = s diag(b~) M~^T do~
+    cc_mul<3, false>(UN, &sm.cc[KC_TN][0][0], LDM, rhsn);
+    // du~ = s diag(b~) M~^T do~ = s Mw~^T do~
     Slab dun = slab_zero();
-    cc_mul<2, true>(dun, &sm.cc[CC_MN][0][0], LDM, DON);
+    cc_mul<2, true>(dun, &sm.cc[KC_MWN][0][0], LDM, DON);
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = slab_row(tr, r);
-        dun.t[tr][r] *= s * sm.betan[i];
+        dun.t[tr][r] *= s;
         DRQ.t[tr][r] = s * Ge(i) * DON.t[tr][r];
         const float t = row_sum16(DON.t[tr][r] * RQ.t[tr][r]);
         if (resp_row(i)) pge[tr][r] += s * Ge(i) * t;  // d gamma~ at the block end
       }
     // drhs~ = T~^T du~ (response rows only); dr_k = -G~ drhs~
-    cc_mul<3, true>(DRN, &sm.cc[CC_TN][0][0], LDM, dun);
+    cc_mul<3, true>(DRN, &sm.cc[KC_TN][0][0], LDM, dun);
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -269,13 +287,14 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   }
 
   // dU = D K dS' + diag(b) (s Mo^T do + Mq^T dr_q + Mk^T dr_k)
+  //    = D K dS' + s Mwo^T do + Mwq^T dr_q + Mwk^T dr_k
   Slab dU = slab_zero();
-  cc_mul<2, true>(dU, &sm.cc[CC_MO][0][0], LDM, DO);
+  cc_mul<2, true>(dU, &sm.cc[KC_MWO][0][0], LDM, DO);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr) dU.t[tr] *= s;
   if (has_noisy) {
-    cc_mul<3, true>(dU, &sm.cc[CC_MQ][0][0], LDM, DRQ);
-    cc_mul<3, true>(dU, &sm.cc[CC_MK][0][0], LDM, DUN);
+    cc_mul<3, true>(dU, &sm.cc[KC_MWQ][0][0], LDM, DRQ);
+    cc_mul<3, true>(dU, &sm.cc[KC_MWK][0][0], LDM, DUN);
   }
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
@@ -287,11 +306,11 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       pb[tr][r] += t * __expf(lgC - sm.lg[i]);
       pg[tr][r] -= t * Di;
       pc[tr][r] += t * Di;
-      dU.t[tr][r] = Di * KD.t[tr][r] + sm.beta[i] * dU.t[tr][r];
+      dU.t[tr][r] = Di * KD.t[tr][r] + dU.t[tr][r];
     }
   // drhs = T^T dU (= dv)
   Slab DRHS = slab_zero();
-  cc_mul<3, true>(DRHS, &sm.cc[CC_T][0][0], LDM, dU);
+  cc_mul<3, true>(DRHS, &sm.cc[KC_T][0][0], LDM, dU);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -300,19 +319,15 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       pg[tr][r] -= Gm(i) * row_sum16(DRHS.t[tr][r] * KS.t[tr][r]);
     }
 
-  // ---- dv, dv~ from registers; the four shared C x d_v arrays -> LDS
+  // ---- the four shared C x d_v arrays -> LDS as bf16 hi / lo planes; the hi
+  // planes of drhs and drhs~ are dv and dv~ rounded to bf16, stored from there
+  // as 16-byte rows once every wave has written its slab
   {
-    u16 *gdv = reinterpret_cast<u16 *>(a.dv), *gdvn = reinterpret_cast<u16 *>(a.dvn);
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = slab_row(tr, r);
-        if (c0 + i < n) {
-          const int64_t off = ((t0g + c0 + i) * H + h) * D + col0 + cl;
-          gdv[off] = f2bf(DRHS.t[tr][r]);
-          gdvn[off] = f2bf(has_noisy && resp_row(i) ? DRN.t[tr][r] : 0.f);
-        }
         const float vals[4] = {U.t[tr][r], UN.t[tr][r], DRHS.t[tr][r], DRN.t[tr][r]};
 #pragma unroll
         for (int ai = 0; ai < 4; ++ai) {
@@ -366,7 +381,6 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     rds[ks][1] = *reinterpret_cast<const float4 *>(dSn + off + 4);
   }
   lds_barrier();
-
   // ================================================================ phase 2
   bf16x8 fdo[2][4], fdon[2][4];
 #pragma unroll
@@ -478,6 +492,20 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       }
   }
 
+  // dv, dv~ rows from the hi planes (drhs~ is zero outside the response rows),
+  // before phase 3 reuses the planes' bytes
+  {
+    u16 *const gdv = reinterpret_cast<u16 *>(a.dv), *const gdvn = reinterpret_cast<u16 *>(a.dvn);
+#pragma unroll
+    for (int e = 0; e < 2 * PU / NT; ++e) {
+      const int u = e * NT + tid;
+      const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
+      if (c0 + row < n)
+        *reinterpret_cast<uint4 *>((m == 0 ? gdv : gdvn) + ((t0g + c0 + row) * H + h) * D + cu16 * 8) =
+            *reinterpret_cast<const uint4 *>(&sm.arrp[m == 0 ? A_DRHS : A_DRN][0][row][cu16 * 8]);
+    }
+  }
+
   // ================================================================ phase 3
   // Gram adjoints -> dG as bf16 hi / lo planes in both orientations (in the
   // bytes of the d_v arrays, which every wave is done with) + gate partials
@@ -491,13 +519,19 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const int m = t >> 2, ti = (t >> 1) & 1, tj = t & 1;
     if (!has_noisy && (m == DM_Q || m == DM_K || m == DM_N || m == DM_AN)) continue;
     const int i0 = 16 * ti + g4, j = 16 * tj + cl;
-    // Mo : w = b, e = lg_i, f = lg_j, mask j <= i
-    // Mq/Mk : w = b, e = lg[p_i - 1], mask j < p_i (resp)
-    // M~ : w = b~, e = lgn[end(i)], f = lgn_j, mask same block (resp)
-    // A^T / A~^T stored transposed: element [j][i]
-    const int ccm = m == DM_O ? CC_MO : m == DM_Q ? CC_MQ : m == DM_K ? CC_MK : m == DM_N ? CC_MN
-                  : m == DM_A ? CC_AT : CC_ANT;
-    const bool tr_store = (m == DM_A || m == DM_AN);
+    // the raw products x_i . y_j of this tile (bf16 rows, exact products):
+    //   Mo: q.k   Mq: q~.k   Mk: k~.k   M~: q~.k~   A: k.k   A~: k~.k~
+    // gated and masked below:
+    //   Mo : w = b, e = lg_i, f = lg_j, mask j <= i
+    //   Mq/Mk : w = b, e = lg[p_i - 1], mask j < p_i (resp)
+    //   M~ : w = b~, e = lgn[end(i)], f = lgn_j, mask same block (resp)
+    //   A : e = lg_i, mask j < i ;  A~ : e = lgn_i, mask j < i in the block of i (resp)
+    const int xl = m == DM_O ? 0 : m == DM_Q || m == DM_N ? 2 : m == DM_A ? 1 : 3;
+    const int xr_ = m == DM_O || m == DM_Q || m == DM_K || m == DM_A ? 1 : 3;
+    floatx4 raw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      mma_bf16(raw, frag_bf16(&sm.x[xl][0][0], LDX, 16 * ti, 32 * ks), frag_bf16(&sm.x[xr_][0][0], LDX, 16 * tj, 32 * ks));
     const bool noisyw = (m == DM_N || m == DM_AN);
     const float wj = noisyw ? sm.betan[j] : sm.beta[j];
     const float fj = noisyw ? sm.lgn[j] : sm.lg[j];
@@ -507,7 +541,6 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + r;
-      const float mw = tr_store ? sm.cc[ccm][j][i] : sm.cc[ccm][i][j];  // unweighted masked Gram (0 off the mask)
       float ei;
       bool mask;
       if (m == DM_O) { ei = sm.lg[i]; mask = j <= i; }
@@ -527,6 +560,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       }
       const float dm = dM[jt][r];
       const float E = mask ? __expf(ei - fj) : 0.f;
+      const float mw = raw[r] * E;  // the unweighted masked Gram
       const float mfull = mw * wj;
       dgv[r] = dm * E * wj;  // dG[i][j]
       const float dd = dm * mfull;
