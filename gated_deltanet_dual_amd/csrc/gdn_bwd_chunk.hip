@@ -39,6 +39,10 @@ constexpr int kLDX = kD + 8, kLDM = kC + 4, kLDP = kD + 8, kLDG = kC + 8;
 enum { P_G = 0, P_GN, P_B, P_BN, P_GP, P_GE, P_C, P_NUM };
 enum { A_U = 0, A_UN, A_DRHS, A_DRN };
 enum { KC_T = 0, KC_TN, KC_MWO, KC_MWQ, KC_MWK, KC_MWN };  // the chunk-matrix pass's order
+// per-row gate factors, formed once per chunk:
+//   GF_M = G_i, GF_P = G_{p_i - 1} (1 at p_i = 0), GF_E = G~ at the end of i's
+//   block, GF_C = G_C / G_i, GF_D = b_i G_C / G_i, GF_N = G~_i
+enum { GF_M = 0, GF_P, GF_E, GF_C, GF_D, GF_N, GF_NUM };
 static_assert(6 * 2 * 2 * kC * kLDG <= 4 * 2 * kC * kLDP, "dG planes must fit in the d_v arrays");
 
 struct Chunk2Smem {
@@ -52,6 +56,7 @@ struct Chunk2Smem {
   alignas(16) float part[kNW][P_NUM][kC];  // per-wave gate-gradient partials
   alignas(16) float plgc[kNW];
   alignas(16) float gsum[2][kC];
+  alignas(16) float gf[GF_NUM][kC];
 };
 
 // 16-byte row fragment of a [T, H, D] bf16 tensor straight from global memory:
@@ -164,10 +169,21 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   lds_barrier();
 
   const float lgC = sm.lg[C - 1];
-  auto Gm = [&](int i) { return __expf(sm.lg[i]); };
-  auto Gp = [&](int i) { const int pi = i - (i % B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
-  auto Ge = [&](int i) { const int pi = i - (i % B); return __expf(sm.lgn[pi + B - 1]); };
-  auto Dd = [&](int i) { return sm.beta[i] * __expf(lgC - sm.lg[i]); };
+  if (tid < C) {  // the gate factor table, visible after the next barrier
+    const int i = tid, pi = i - (i % B);
+    const float ec = __expf(lgC - sm.lg[i]);
+    sm.gf[GF_M][i] = __expf(sm.lg[i]);
+    sm.gf[GF_P][i] = pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f;
+    sm.gf[GF_E][i] = __expf(sm.lgn[pi + B - 1]);
+    sm.gf[GF_C][i] = ec;
+    sm.gf[GF_D][i] = sm.beta[i] * ec;
+    sm.gf[GF_N][i] = __expf(sm.lgn[i]);
+  }
+  auto Gm = [&](int i) { return sm.gf[GF_M][i]; };
+  auto Gp = [&](int i) { return sm.gf[GF_P][i]; };
+  auto Ge = [&](int i) { return sm.gf[GF_E][i]; };
+  auto Dd = [&](int i) { return sm.gf[GF_D][i]; };
+  auto Gn = [&](int i) { return sm.gf[GF_N][i]; };
   auto resp_row = [&](int i) { return c0 + i < n && c0 + i >= P; };
 
   bf16x8 sbh[4], sbl[4], dbh[4], dbl[4];
@@ -255,7 +271,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rhsn.t[tr][r] = VN.t[tr][r] - __expf(sm.lgn[slab_row(tr, r)]) * RK.t[tr][r];
+      for (int r = 0; r < 4; ++r) rhsn.t[tr][r] = VN.t[tr][r] - Gn(slab_row(tr, r)) * RK.t[tr][r];
     cc_mul<3, false>(UN, &sm.cc[KC_TN][0][0], LDM, rhsn);
     // du~ = s diag(b~) M~^T do~ = s Mw~^T do~
     Slab dun = slab_zero();
@@ -279,7 +295,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         const int i = slab_row(tr, r);
         const float drn = resp_row(i) ? DRN.t[tr][r] : 0.f;
         DRN.t[tr][r] = drn;
-        const float gn = __expf(sm.lgn[i]);
+        const float gn = Gn(i);
         pgn[tr][r] -= gn * row_sum16(drn * RK.t[tr][r]);
         DUN.t[tr][r] = -gn * drn;
         pgp[tr][r] += row_sum16(DRQ.t[tr][r] * RQ0.t[tr][r] + DUN.t[tr][r] * RK0.t[tr][r]);
@@ -303,7 +319,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       const int i = slab_row(tr, r);
       const float Di = Dd(i);
       const float t = row_sum16(KD.t[tr][r] * U.t[tr][r]);  // d D_i
-      pb[tr][r] += t * __expf(lgC - sm.lg[i]);
+      pb[tr][r] += t * sm.gf[GF_C][i];
       pg[tr][r] -= t * Di;
       pc[tr][r] += t * Di;
       dU.t[tr][r] = Di * KD.t[tr][r] + dU.t[tr][r];
@@ -427,7 +443,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         float sc = 1.f;
         if (m == DM_O || m == DM_N) sc = s;
         else if (m == DM_Q) sc = s * Ge(i);
-        else if (m == DM_K) sc = -__expf(sm.lgn[i]);
+        else if (m == DM_K) sc = -Gn(i);
         else sc = -1.f;
         acc[r] *= sc;
       }
@@ -488,7 +504,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         dq[tr][r] = s * Gm(i) * a_dq[tr][r];
         dk[tr][r] = -Gm(i) * a_dk1[tr][r] + Dd(i) * a_dk2[tr][r];
         dqn[tr][r] = Gp(i) * s * Ge(i) * a_dqn[tr][r];
-        dkn[tr][r] = -Gp(i) * __expf(sm.lgn[i]) * a_dkn[tr][r];
+        dkn[tr][r] = -Gp(i) * Gn(i) * a_dkn[tr][r];
       }
   }
 
