@@ -35,10 +35,12 @@ namespace flare {
 namespace {
 
 constexpr int kC = 32, kD = 128, kNW = 8, kNT = 64 * kNW;
-constexpr int kLDX = kD + 8, kLDM = kC + 4, kLDP = kD + 8, kLDG = kC + 8;
+constexpr int kLDX = kD + 8, kLDP = kD + 8, kLDG = kC + 8, kLDQ = kC + 4;
 enum { P_G = 0, P_GN, P_B, P_BN, P_GP, P_GE, P_C, P_NUM };
 enum { A_U = 0, A_UN, A_DRHS, A_DRN };
-enum { KC_T = 0, KC_TN, KC_MWO, KC_MWQ, KC_MWK, KC_MWN };  // the chunk-matrix pass's order
+// the chunk matrices (T, T~, Mwo, Mwq, Mwk, Mw~) as bf16 hi / lo planes in the
+// orientation each product reads them (_N as stored, _T transposed)
+enum { Q_T_N = 0, Q_T_T, Q_TN_N, Q_TN_T, Q_MWO_T, Q_MWQ_N, Q_MWQ_T, Q_MWK_N, Q_MWK_T, Q_MWN_T, Q_NUM };
 // per-row gate factors, formed once per chunk:
 //   GF_M = G_i, GF_P = G_{p_i - 1} (1 at p_i = 0), GF_E = G~ at the end of i's
 //   block, GF_C = G_C / G_i, GF_D = b_i G_C / G_i, GF_N = G~_i
@@ -47,7 +49,7 @@ static_assert(6 * 2 * 2 * kC * kLDG <= 4 * 2 * kC * kLDP, "dG planes must fit in
 
 struct Chunk2Smem {
   alignas(16) u16 x[4][kC][kLDX];       // q, k, q~, k~ ; at the end the staging of dq, dk, dq~, dk~
-  alignas(16) float cc[6][kC][kLDM];    // T, T~ and the weighted masked Grams Mwo, Mwq, Mwk, Mw~
+  alignas(16) u16 cq[Q_NUM][2][kC][kLDQ];  // T, T~ and the weighted masked Grams, bf16 hi / lo planes
   // U, u~, drhs, drhs~ for the d_v reductions as bf16 hi / lo planes (each
   // value split once, by the wave that computed it); after those reductions
   // the same bytes hold the Gram-weight gradients dG, [6][orientation][hi, lo][kC][kLDG]
@@ -79,7 +81,7 @@ __device__ __forceinline__ bf16x8 frag_mask(const uint4 &v, int c0, int n, int P
 }  // namespace
 
 __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
-  constexpr int C = kC, D = kD, NT = kNT, LDX = kLDX, LDM = kLDM, LDP = kLDP, LDG = kLDG;
+  constexpr int C = kC, D = kD, NT = kNT, LDX = kLDX, LDP = kLDP, LDG = kLDG, LDQ = kLDQ;
   __shared__ Chunk2Smem sm;
   const FwdArgs &f = a.f;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -160,10 +162,34 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const bool ok = tpos < n && ((m & 1) == 0 || tpos >= P);
     *reinterpret_cast<uint4 *>(&vst[m][row][cu16 * 8]) = ok ? vr[e] : make_uint4(0u, 0u, 0u, 0u);
   }
+  // the chunk matrices -> hi / lo planes: 4 consecutive entries of a row per
+  // thread, one 8-byte write per plane as stored, four 2-byte writes per plane
+  // transposed (the matrix index is the same across a wave)
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int u = j * NT + tid, which = u / (C * C / 4), rr = u % (C * C / 4);
-    *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = tri4[j];
+    const int row = rr / (C / 4), col = 4 * (rr % (C / 4));
+    const float x4[4] = {tri4[j].x, tri4[j].y, tri4[j].z, tri4[j].w};
+    u16 hb[4], lb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hb[e] = f2bf(x4[e]);
+      lb[e] = f2bf(x4[e] - bf2f(hb[e]));
+    }
+    const int qn = which == 0 ? Q_T_N : which == 1 ? Q_TN_N : which == 3 ? Q_MWQ_N : which == 4 ? Q_MWK_N : -1;
+    const int qt = which == 0 ? Q_T_T : which == 1 ? Q_TN_T : which == 2 ? Q_MWO_T : which == 3 ? Q_MWQ_T
+                 : which == 4 ? Q_MWK_T : Q_MWN_T;
+    if (qn >= 0) {
+      *reinterpret_cast<uint2 *>(&sm.cq[qn][0][row][col]) =
+          make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
+      *reinterpret_cast<uint2 *>(&sm.cq[qn][1][row][col]) =
+          make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm.cq[qt][0][col + e][row] = hb[e];
+      sm.cq[qt][1][col + e][row] = lb[e];
+    }
   }
   if (tid < 4 * C) gate_scan(gval, B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   lds_barrier();
@@ -249,7 +275,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       pg[tr][r] += s * Gm(i) * row_sum16(QS.t[tr][r] * DO.t[tr][r]);  // d gamma_i from o_i = s G_i q_i S_c
     }
   Slab U = slab_zero();
-  cc_mul<3, false>(U, &sm.cc[KC_T][0][0], LDM, rhs);
+  cc_mul_planes<3>(U, &sm.cq[Q_T_N][0][0][0], &sm.cq[Q_T_N][1][0][0], LDQ, rhs);
 
   // noisy reads and block: r_q, r_k, u~ ; noisy adjoints dr_q, du~, drhs~, dr_k
   Slab UN = slab_zero(), DRQ = slab_zero(), DRN = slab_zero(), DUN = slab_zero();
@@ -265,17 +291,17 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       }
     RQ = RQ0;
     RK = RK0;
-    cc_mul<3, false>(RQ, &sm.cc[KC_MWQ][0][0], LDM, U);  // + Mq diag(b) U
-    cc_mul<3, false>(RK, &sm.cc[KC_MWK][0][0], LDM, U);
+    cc_mul_planes<3>(RQ, &sm.cq[Q_MWQ_N][0][0][0], &sm.cq[Q_MWQ_N][1][0][0], LDQ, U);  // + Mq diag(b) U
+    cc_mul_planes<3>(RK, &sm.cq[Q_MWK_N][0][0][0], &sm.cq[Q_MWK_N][1][0][0], LDQ, U);
     Slab rhsn;
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
       for (int r = 0; r < 4; ++r) rhsn.t[tr][r] = VN.t[tr][r] - Gn(slab_row(tr, r)) * RK.t[tr][r];
-    cc_mul<3, false>(UN, &sm.cc[KC_TN][0][0], LDM, rhsn);
+    cc_mul_planes<3>(UN, &sm.cq[Q_TN_N][0][0][0], &sm.cq[Q_TN_N][1][0][0], LDQ, rhsn);
     // du~ = s diag(b~) M~^T do~ = s Mw~^T do~
     Slab dun = slab_zero();
-    cc_mul<2, true>(dun, &sm.cc[KC_MWN][0][0], LDM, DON);
+    cc_mul_planes<2>(dun, &sm.cq[Q_MWN_T][0][0][0], &sm.cq[Q_MWN_T][1][0][0], LDQ, DON);
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -287,7 +313,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         if (resp_row(i)) pge[tr][r] += s * Ge(i) * t;  // d gamma~ at the block end
       }
     // drhs~ = T~^T du~ (response rows only); dr_k = -G~ drhs~
-    cc_mul<3, true>(DRN, &sm.cc[KC_TN][0][0], LDM, dun);
+    cc_mul_planes<3>(DRN, &sm.cq[Q_TN_T][0][0][0], &sm.cq[Q_TN_T][1][0][0], LDQ, dun);
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -305,12 +331,12 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   // dU = D K dS' + diag(b) (s Mo^T do + Mq^T dr_q + Mk^T dr_k)
   //    = D K dS' + s Mwo^T do + Mwq^T dr_q + Mwk^T dr_k
   Slab dU = slab_zero();
-  cc_mul<2, true>(dU, &sm.cc[KC_MWO][0][0], LDM, DO);
+  cc_mul_planes<2>(dU, &sm.cq[Q_MWO_T][0][0][0], &sm.cq[Q_MWO_T][1][0][0], LDQ, DO);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr) dU.t[tr] *= s;
   if (has_noisy) {
-    cc_mul<3, true>(dU, &sm.cc[KC_MWQ][0][0], LDM, DRQ);
-    cc_mul<3, true>(dU, &sm.cc[KC_MWK][0][0], LDM, DUN);
+    cc_mul_planes<3>(dU, &sm.cq[Q_MWQ_T][0][0][0], &sm.cq[Q_MWQ_T][1][0][0], LDQ, DRQ);
+    cc_mul_planes<3>(dU, &sm.cq[Q_MWK_T][0][0][0], &sm.cq[Q_MWK_T][1][0][0], LDQ, DUN);
   }
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
@@ -326,7 +352,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     }
   // drhs = T^T dU (= dv)
   Slab DRHS = slab_zero();
-  cc_mul<3, true>(DRHS, &sm.cc[KC_T][0][0], LDM, dU);
+  cc_mul_planes<3>(DRHS, &sm.cq[Q_T_T][0][0][0], &sm.cq[Q_T_T][1][0][0], LDQ, dU);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
 #pragma unroll

@@ -100,6 +100,34 @@ __device__ __forceinline__ void cc_mul(Slab &out, const float *M, int ld, const 
   }
 }
 
+// A fragment of rows m0 .. m0+15 of a C x C bf16 plane in LDS (row-major,
+// pitch ld elements, a multiple of 4), columns in the slab's k-permutation:
+// two 8-byte reads, no conversion.
+__device__ __forceinline__ bf16x8 plane_a(const u16 *P, int ld, int m0) {
+  const int l = lane_id(), g = l >> 4;
+  const u16 *p = P + (m0 + (l & 15)) * ld + 4 * g;
+  const uint2 lo4 = *reinterpret_cast<const uint2 *>(p);
+  const uint2 hi4 = *reinterpret_cast<const uint2 *>(p + 16);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+}
+
+// out += A * in, A (C x C) given as its bf16 hi and lo planes, already in the
+// orientation of the product (a transposed operand is stored transposed).
+// TERMS as for cc_mul.
+template <int TERMS>
+__device__ __forceinline__ void cc_mul_planes(Slab &out, const u16 *Ah, const u16 *Al, int ld, const Slab &in) {
+  bf16x8 bh, bl;
+  if constexpr (TERMS == 3) slab_b_split(in, bh, bl);
+  else bh = slab_b_hi(in);
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr) {
+    const bf16x8 ah = plane_a(Ah, ld, 16 * tr), al = plane_a(Al, ld, 16 * tr);
+    mma_bf16(out.t[tr], ah, bh);
+    if constexpr (TERMS == 3) mma_bf16(out.t[tr], ah, bl);
+    mma_bf16(out.t[tr], al, bh);
+  }
+}
+
 // Sum of x over the 16 lanes that share an accumulator row group.
 __device__ __forceinline__ float row_sum16(float x) { return dpp_sum16(x); }
 
