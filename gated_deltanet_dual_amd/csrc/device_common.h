@@ -150,6 +150,19 @@ __device__ __forceinline__ float dpp_sum16(float x) {
   return x;
 }
 
+// x + x of lane l ^ 16, and x + x of lane l ^ 32: sums across the 16-lane rows
+// with the gfx950 permlane swaps (VALU, no LDS traffic).  A swap of a value
+// with itself leaves each lane holding its own value in one output and its
+// partner's in the other.
+__device__ __forceinline__ float xsum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Output element coordinates of accumulator register r for this lane.
 __device__ __forceinline__ int acc_row(int r) { return 4 * (lane_id() >> 4) + r; }
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }

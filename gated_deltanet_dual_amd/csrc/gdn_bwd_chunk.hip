@@ -395,9 +395,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       }
   }
   {
-    float t = plg;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
+    const float t = xsum32(xsum16(dpp_sum16(plg)));
     if (lane == 0) sm.plgc[wave] = __expf(lgC) * t;
   }
   // ---- phase 2's do, do~ row fragments (rows 16 tr .., k-step ks over d_v),
@@ -578,7 +576,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const float wj = noisyw ? sm.betan[j] : sm.beta[j];
     const float fj = noisyw ? sm.lgn[j] : sm.lg[j];
     float colw = 0.f, colf = 0.f;
-    float dgv[4];
+    float dgv[4], rsum[4];
     const int pbase = (m == DM_O || m == DM_A) ? P_G : (m == DM_Q || m == DM_K) ? P_GP : m == DM_N ? P_GE : P_GN;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -606,8 +604,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       const float mfull = mw * wj;
       dgv[r] = dm * E * wj;  // dG[i][j]
       const float dd = dm * mfull;
-      const float rs = row_sum16(dd);
-      if (cl == 0) sm.part[wave][pbase][i] += rs;  // row part d e_i
+      rsum[r] = row_sum16(dd);  // row part d e_i
       colf += dd;
       colw += dm * mw;
     }
@@ -628,11 +625,15 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       *reinterpret_cast<uint2 *>(dgp(m, 1, 0) + j * LDG + i0) = make_uint2(hw[0], hw[1]);
       *reinterpret_cast<uint2 *>(dgp(m, 1, 1) + j * LDG + i0) = make_uint2(lw[0], lw[1]);
     }
+    // row parts of the tile's 4 rows of this lane group, one read-modify-write
+    if (cl == 0) {
+      float4 *pp = reinterpret_cast<float4 *>(&sm.part[wave][pbase][i0]);
+      const float4 o = *pp;
+      *pp = make_float4(o.x + rsum[0], o.y + rsum[1], o.z + rsum[2], o.w + rsum[3]);
+    }
     // column parts: over the 4 row groups of the tile
-    colf += __shfl_xor(colf, 16, 64);
-    colf += __shfl_xor(colf, 32, 64);
-    colw += __shfl_xor(colw, 16, 64);
-    colw += __shfl_xor(colw, 32, 64);
+    colf = xsum32(xsum16(colf));
+    colw = xsum32(xsum16(colw));
     if (lane < 16) {
       if (noisyw) {
         sm.part[wave][P_GN][j] -= colf;
