@@ -74,6 +74,17 @@ def test_bwd_bf16(g, dev, B):
     check(inp, run_bwd(g, inp, dev), ref_bwd(inp), TOL_BF16, "bwd_bf16_B%d" % B)
 
 
+def test_bwd_bf16_edge_documents(g, dev):
+    """The chunked d = 128 path on the degenerate documents: empty, shorter
+    than a chunk, exactly one chunk, all prompt, no prompt, a ragged tail;
+    with h0, dh_final and an explicit scale."""
+    lens, plens = [0, 5, 31, 32, 0, 64, 97, 40], [0, 4, 28, 32, 0, 0, 64, 40]
+    inp = wl.gdn_inputs(lens, plens, 2, 128, 128, 4, seed=73, with_h0=True, with_grads=True)
+    dhf = (np.random.default_rng(74).standard_normal((len(lens), 2, 128, 128)) / 16).astype(np.float32)
+    check(inp, run_bwd(g, inp, dev, dhf=dhf, scale=0.2), ref_bwd(inp, dhf=dhf, scale=0.2), TOL_BF16,
+          "bwd_bf16_edge")
+
+
 def test_bwd_bf16_h0(g, dev):
     inp = wl.gdn_inputs([100, 37], [20, 0], 2, 128, 128, 4, seed=70, with_h0=True, with_grads=True)
     dhf = (np.random.default_rng(71).standard_normal((2, 2, 128, 128)) / 16).astype(np.float32)

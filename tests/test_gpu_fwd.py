@@ -104,6 +104,29 @@ def test_checkpoints_are_chunk_start_states(g, dev):
             assert rel_rms(ck[slot], hf[0]) <= TOL_F32, (i, c)
 
 
+def test_checkpoints_chunked_path(g, dev):
+    """bf16 io at d = 128 (chunk pre-pass + state scan + output pass): every
+    checkpoint slot holds the clean state after 32c tokens of its document
+    (empty and sub-chunk documents included), and the outputs are the same
+    bits whether checkpoints are asked for or not."""
+    import torch
+    inp = wl.gdn_inputs([100, 0, 64, 7, 45], [0, 0, 32, 4, 44], 2, 128, 128, 4, seed=35, with_h0=True)
+    o1, on1, hf1, ck = run(g, inp, dev, want_ckpt=True)
+    o2, on2, hf2, _ = run(g, inp, dev)
+    assert torch.equal(o1, o2) and torch.equal(on1, on2) and torch.equal(hf1, hf2)
+    ck = to_np(ck)
+    cu = inp.cu_seqlens
+    for i in range(len(inp.prompt_lens)):
+        n = cu[i + 1] - cu[i]
+        for c in range((n + 31) // 32):
+            L = 32 * c
+            sl = slice(cu[i], cu[i] + L)
+            pre = [x[sl] for x in inp.clean_args() + inp.noisy_args()]
+            _, _, hf = oracle.gdn_dual_fwd([0, L], [L], *pre, 4, h0=inp.h0[i:i + 1])
+            slot = cu[i] // 32 + i + c
+            assert rel_rms(ck[slot], hf[0]) <= TOL_F32, (i, c, rel_rms(ck[slot], hf[0]))
+
+
 def test_exact_tags_bit_identical(g, dev):
     """fp32, a = b = 1, standard-basis keys and small-integer values: every
     intermediate is an exact small integer, so GPU and oracle agree bit for bit,
