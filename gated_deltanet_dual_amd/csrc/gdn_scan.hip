@@ -22,6 +22,9 @@
 // published to the other waves through a double-buffered LDS area, one
 // barrier per chunk.  Two slabs form a workgroup, four workgroups per
 // (document, head), on one XCD so the operands they share stay in its L2.
+// A third wave per workgroup only stores: the compute waves stage each
+// chunk's carried slabs in LDS and it writes them out, so the stores never sit
+// in the compute waves' (in-order) memory counters ahead of their loads.
 #include "bwd_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -49,8 +52,8 @@ struct ScanRing {
 };
 
 struct ScanSmem {
-  alignas(16) uint4 sh[2][sSH][64];          // shared units, double-buffered by chunk parity
-  alignas(16) float stage[sNW][sD][16 + 4];  // per-wave staging of the carried slab for 16-byte stores
+  alignas(16) uint4 sh[2][sSH][64];             // shared units, double-buffered by chunk parity
+  alignas(16) float stage[2][sNW][sD][16 + 4];  // the carried slabs for the store wave, by chunk parity
 };
 
 }  // namespace
@@ -59,7 +62,7 @@ struct ScanSmem {
 // slabs, [slab 8][tile 2][lane 64][4], in the R area of the hand-over), added
 // to W (K X) before the K^T product; else a full 128 x 128 R.
 template <bool REVERSE, bool ZRHS>
-__global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
+__global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs a) {
   using ScanRing = ScanRing<ZRHS>;
   constexpr int C = sC, D = sD;
   __shared__ ScanSmem sm;
@@ -77,9 +80,33 @@ __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
   const int64_t t0g = a.cu[doc];
   const int n = a.cu[doc + 1] - a.cu[doc];
   const int nchunks = (n + C - 1) / C;
+  const int64_t ck_base = (int64_t)(t0g / C) + doc;
+  // step i handles chunk at(i)
+  auto at = [&](int i) { return REVERSE ? nchunks - 1 - i : i; };
+
+  // ---- the store wave: after each chunk's barrier, the carried slabs the
+  // compute waves staged for that chunk -> global, row-major [d_k][d_v], as
+  // 16-byte stores.  Its stores never hold up the compute waves' loads (each
+  // wave's memory counter is in order).  Same barrier count as the compute
+  // waves: one per chunk.
+  if (wave == sNW) {
+    for (int i = 0; i < nchunks; ++i) {
+      const int c = at(i);
+      lds_barrier();
+      float *dst = a.states + ((ck_base + c) * H + h) * (size_t)D * D;
+#pragma unroll
+      for (int w = 0; w < sNW; ++w)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int u = j * 64 + lane, row = u >> 2, c4 = u & 3;
+          *reinterpret_cast<float4 *>(dst + (size_t)row * D + 16 * (sNW * quarter + w) + 4 * c4) =
+              *reinterpret_cast<const float4 *>(&sm.stage[c & 1][w][row][4 * c4]);
+        }
+    }
+    return;
+  }
   const int slab = sNW * quarter + wave;
   const int dv0 = 16 * slab;
-  const int64_t ck_base = (int64_t)(t0g / C) + doc;
 
   // ---- X slab: tile kt holds rows 16 kt + 4 g + r (d_k), column dv0 + cl
   floatx4 X[8];
@@ -92,19 +119,12 @@ __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
       for (int r = 0; r < 4; ++r) X[kt][r] = src[(size_t)(16 * kt + g4 + r) * D + dv0 + cl];
     }
   }
-  // the X slab -> global, row-major [d_k][d_v], through this wave's LDS:
-  // 8 16-byte stores per lane instead of 32 scalar ones
-  auto store_X = [&](float *dst) {
+  // the X slab -> the store wave's staging area for chunk parity `par`
+  auto stage_X = [&](int par) {
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.stage[wave][16 * kt + g4 + r][cl] = X[kt][r];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int u = j * 64 + lane, row = u >> 2, c4 = u & 3;
-      *reinterpret_cast<float4 *>(dst + (size_t)row * D + dv0 + 4 * c4) =
-          *reinterpret_cast<const float4 *>(&sm.stage[wave][row][4 * c4]);
-    }
+      for (int r = 0; r < 4; ++r) sm.stage[par][wave][16 * kt + g4 + r][cl] = X[kt][r];
   };
   // Loads are unconditional (the chunk index is clamped into the document:
   // an empty document still owns one slot), so no load sits under a branch:
@@ -124,11 +144,11 @@ __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
     p.gc = pk[kPackG];
   };
   auto bf = [](const uint4 &v) { return __builtin_bit_cast(bf16x8, v); };
-  // one chunk: store the carried X at the chunk's slot, publish this wave's
-  // half of the shared operands, then the step; the ring slot is refilled
-  // with chunk `refill` once R is used
+  // one chunk: stage the carried X for the store wave (it goes to the chunk's
+  // slot), publish this wave's half of the shared operands, then the step;
+  // the ring slot is refilled with chunk `refill` once R is used
   auto step = [&](ScanRing &p, int c, int refill) {
-    store_X(a.states + ((ck_base + c) * H + h) * (size_t)D * D);
+    stage_X(c & 1);
     uint4 (*sh)[64] = sm.sh[c & 1];
 #pragma unroll
     for (int j = 0; j < sSHW; ++j)
@@ -185,9 +205,7 @@ __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
     load_ring(p, refill);
   };
 
-  // step i handles chunk at(i); sRING operand sets in rotation, sRING - 1
-  // chunks in flight while one computes
-  auto at = [&](int i) { return REVERSE ? nchunks - 1 - i : i; };
+  // sRING operand sets in rotation, sRING - 1 chunks in flight while one computes
   ScanRing p0, p1, p2, p3;
   static_assert(sRING == 4, "the rotation below names four sets");
   load_ring(p0, at(0));
@@ -215,7 +233,7 @@ __global__ __launch_bounds__(64 * sNW) void gdn_scan_d128_kernel(ScanArgs a) {
 hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st) {
   const int pairs = a.num_docs * a.H;
   const int groups = (pairs + 7) / 8;
-  const dim3 grid((unsigned)(groups * 8 * sNQ)), block(64 * sNW);
+  const dim3 grid((unsigned)(groups * 8 * sNQ)), block(64 * (sNW + 1));
   // the reverse recurrence carries a full R, the forward one K^T Z
   if (reverse) hipLaunchKernelGGL((gdn_scan_d128_kernel<true, false>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((gdn_scan_d128_kernel<false, true>), grid, block, 0, st, a);
