@@ -17,6 +17,8 @@ What each entry computes, with its source:
 * ``block_step`` -- serving EVAL (no pool write) and COMMIT (causal replay that
   writes the pool), Key designs item 4.
 * ``shortconv_dual`` -- the dual-source causal ShortConv, Key designs item 3.
+* ``shortconv_dual_bwd`` -- its reverse mode (parity pinned by finite
+  differences and the adjoint identity in the CPU tests).
 
 Parity pins (closed forms, brute force, invariants, finite differences and a
 hand-worked example) are in the CPU tests; see ``tests/test_oracle_*.py``.
@@ -65,6 +67,8 @@ def _load():
     lib.oracle_block_step.restype = i32
     lib.oracle_shortconv_dual.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, i32, P, P, i32]
     lib.oracle_shortconv_dual.restype = i32
+    lib.oracle_shortconv_dual_bwd.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, P, i32]
+    lib.oracle_shortconv_dual_bwd.restype = i32
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = i32
     _lib = lib
@@ -178,3 +182,25 @@ def shortconv_dual(cu_seqlens, prompt_lens, block_size, x, xn, weight,
                                        _p(y), _p(yn), int(threads))
     _check(rc, "shortconv_dual")
     return y, yn
+
+
+def shortconv_dual_bwd(cu_seqlens, prompt_lens, block_size, x, xn, weight, dy, dyn,
+                       bias=None, activation=0, threads=0):
+    """Reverse mode of shortconv_dual: x, xn, dy, dyn [T,C]; weight [C,W];
+    bias [C] or None.  Returns (dx, dxn, dweight, dbias); dxn's prompt rows are
+    0 and dyn's prompt rows are ignored."""
+    cu, pl = _i32(cu_seqlens), _i32(prompt_lens)
+    x, xn, w, bias = _f64(x), _f64(xn), _f64(weight), _f64(bias)
+    dy, dyn = _f64(dy), _f64(dyn)
+    T, C = x.shape
+    W = w.shape[1]
+    dx = np.zeros((T, C))
+    dxn = np.zeros((T, C))
+    dw = np.zeros((C, W))
+    db = np.zeros(C)
+    rc = _load().oracle_shortconv_dual_bwd(len(pl), _p(cu), _p(pl), int(block_size), C, W,
+                                           _p(x), _p(xn), _p(w), _p(bias), int(activation),
+                                           _p(dy), _p(dyn), _p(dx), _p(dxn), _p(dw), _p(db),
+                                           int(threads))
+    _check(rc, "shortconv_dual_bwd")
+    return dx, dxn, dw, db

@@ -1,7 +1,8 @@
 /*
  * flare_oracle.c -- plain fp64 CPU oracle for the dual-stream Gated DeltaNet
  * layer (clean causal stream + block-wise noisy stream), its reverse mode,
- * the serving block step and the dual-source causal ShortConv.
+ * the serving block step and the dual-source causal ShortConv with its
+ * reverse mode.
  *
  * THIS IS TEST INFRASTRUCTURE.  Only the test-suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load it.  It shares no code, header,
@@ -644,6 +645,94 @@ static void conv_unit(void *vctx, int doc, void *scratch) {
       c->yn[(size_t)(start + t) * C + ch] = blk >= 0 ? act(acc_n, c->activation) : 0.0;
     }
   }
+}
+
+/* Reverse mode of the ShortConv above: with z the pre-activation sums and
+ * g = dy * act'(z) (g~ = dy~ * act'(z~) on response rows, 0 on prompt rows),
+ * every tap that read input element m passes w[j] * g to that element's
+ * gradient -- the clean input's, or the noisy input's when the noisy tap read
+ * x~ -- and w[j] receives g times the value the tap read; the bias receives g.
+ * One unit per channel, so each unit owns its dw row, its dbias entry and its
+ * column of dx, dx~. */
+typedef struct {
+  int num_docs, B, C, W, activation;
+  const int32_t *cu, *plen;
+  const double *x, *xn, *w, *bias, *dy, *dyn;
+  double *dx, *dxn, *dw, *db;
+} convb_ctx;
+
+static double act_grad(double z, int activation) {
+  if (activation != 1) return 1.0;
+  const double sg = 1.0 / (1.0 + exp(-z));
+  return sg * (1.0 + z * (1.0 - sg));
+}
+
+static void convb_unit(void *vctx, int ch, void *scratch) {
+  (void)scratch;
+  convb_ctx *c = (convb_ctx *)vctx;
+  const int C = c->C, W = c->W, B = c->B;
+  const double *wr = c->w + (size_t)ch * W;
+  double *dwr = c->dw + (size_t)ch * W;
+  for (int j = 0; j < W; ++j) dwr[j] = 0.0;
+  double db = 0.0;
+  for (int doc = 0; doc < c->num_docs; ++doc) {
+    const int start = c->cu[doc], n = c->cu[doc + 1] - c->cu[doc];
+    const int P = c->plen[doc];
+    for (int t = 0; t < n; ++t) {
+      c->dx[(size_t)(start + t) * C + ch] = 0.0;
+      c->dxn[(size_t)(start + t) * C + ch] = 0.0;
+    }
+    for (int t = 0; t < n; ++t) {
+      const int blk = (t >= P) ? P + ((t - P) / B) * B : -1;
+      /* the forward sums again, for the activation's derivative */
+      double zc = c->bias ? c->bias[ch] : 0.0, zn = zc;
+      for (int j = 0; j < W; ++j) {
+        const int m = t - (W - 1) + j;
+        if (m < 0) continue;
+        const double xc = c->x[(size_t)(start + m) * C + ch];
+        zc += wr[j] * xc;
+        if (blk >= 0) zn += wr[j] * (m < blk ? xc : c->xn[(size_t)(start + m) * C + ch]);
+      }
+      const double gc = c->dy[(size_t)(start + t) * C + ch] * act_grad(zc, c->activation);
+      const double gn = blk >= 0 ? c->dyn[(size_t)(start + t) * C + ch] * act_grad(zn, c->activation) : 0.0;
+      db += gc + gn;
+      for (int j = 0; j < W; ++j) {
+        const int m = t - (W - 1) + j;
+        if (m < 0) continue;
+        const size_t at = (size_t)(start + m) * C + ch;
+        c->dx[at] += wr[j] * gc;
+        dwr[j] += gc * c->x[at];
+        if (blk >= 0) {
+          if (m < blk) {
+            c->dx[at] += wr[j] * gn;
+            dwr[j] += gn * c->x[at];
+          } else {
+            c->dxn[at] += wr[j] * gn;
+            dwr[j] += gn * c->xn[at];
+          }
+        }
+      }
+    }
+  }
+  if (c->db) c->db[ch] = db;
+}
+
+int oracle_shortconv_dual_bwd(int num_docs, const int32_t *cu_seqlens,
+                              const int32_t *prompt_lens, int B, int channels,
+                              int width, const double *x, const double *xn,
+                              const double *weight, const double *bias,
+                              int activation, const double *dy, const double *dyn,
+                              double *dx, double *dxn, double *dweight,
+                              double *dbias, int nthreads) {
+  if (num_docs < 0 || B <= 0 || channels <= 0 || width <= 0) return 2;
+  for (int i = 0; i < num_docs; ++i) {
+    const int n = cu_seqlens[i + 1] - cu_seqlens[i];
+    if (n < 0 || prompt_lens[i] < 0 || prompt_lens[i] > n) return 2;
+  }
+  convb_ctx c = {num_docs, B, channels, width, activation, cu_seqlens, prompt_lens,
+                 x, xn, weight, bias, dy, dyn, dx, dxn, dweight, dbias};
+  run_units(convb_unit, &c, channels, 0, nthreads);
+  return 0;
 }
 
 int oracle_shortconv_dual(int num_docs, const int32_t *cu_seqlens,
