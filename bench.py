@@ -193,7 +193,7 @@ def main():
     if not args.no_components and args.only in (None, "serve"):
         comps["serving"] = bench_serving(torch, g, wl, dev, timer, up, args)
     if not args.no_components and args.only in (None, "conv"):
-        comps["shortconv"] = bench_conv(torch, g, wl, dev, timer, up, args)
+        comps["shortconv"], comps["shortconv_bwd"] = bench_conv(torch, g, wl, dev, timer, up, args)
     if comps:
         result["components"] = comps
 
@@ -396,9 +396,38 @@ def bench_conv(torch, g, wl, dev, timer, up, args):
     T, C = x.shape
     n_resp = int(sum(p["cu_seqlens"][i + 1] - p["cu_seqlens"][i] - p["prompt_lens"][i] for i in range(8)))
     alg = 2 * C * (T + n_resp + 2 * T)  # read x (all), xn (response), write y, yn
-    return {"workload": "dual ShortConv, 1 packed row of 32768 tokens, 8 docs, 3x32x128 channels, W=4, bf16",
-            "ms": ms, "gbs": alg / (ms * 1e-3) / 1e9, "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "alg_bytes": alg, "tokens_per_s": T / (ms * 1e-3), "bound": "hbm"}
+    fwd = {"workload": "dual ShortConv, 1 packed row of 32768 tokens, 8 docs, 3x32x128 channels, W=4, bf16",
+           "ms": ms, "gbs": alg / (ms * 1e-3) / 1e9, "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "alg_bytes": alg, "tokens_per_s": T / (ms * 1e-3), "bound": "hbm"}
+    # ---- reverse mode on the same inputs; output gradients ~ N(0, 1) drawn on
+    # the device from a seeded generator
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    dy = torch.randn(x.shape, generator=gen, device=dev).to(torch.bfloat16)
+    dyn = torch.randn(x.shape, generator=gen, device=dev).to(torch.bfloat16)
+    W = w.shape[1]
+    dx, dxn = torch.empty_like(x), torch.empty_like(x)
+    dw = torch.empty((C, W), dtype=torch.float32, device=dev)
+    db = torch.empty((C,), dtype=torch.float32, device=dev)
+    ws = torch.empty((g.shortconv_dual_bwd_workspace_bytes(vl, p["block_size"], C, W),), dtype=torch.uint8,
+                     device=dev)
+
+    def bwd():
+        return g.shortconv_dual_bwd(vl, p["block_size"], x, xn, w, dy, dyn, workspace=ws, out=(dx, dxn, dw, db))
+
+    for _ in range(max(args.warmup, 2)):
+        bwd()
+    torch.cuda.synchronize()
+    for _ in range(n):
+        timer.run("conv_bwd", bwd)
+    torch.cuda.synchronize()
+    bms = timer.avg_ms("conv_bwd")
+    # read x, dy (all rows), xn, dyn (response rows); write dx, dxn
+    balg = 2 * C * (4 * T + 2 * n_resp)
+    bwd_d = {"workload": "dual ShortConv reverse mode, same row and shape, bf16 (dx, dx~, dweight, dbias)",
+             "ms": bms, "gbs": balg / (bms * 1e-3) / 1e9, "hbm_frac": balg / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "alg_bytes": balg, "tokens_per_s": T / (bms * 1e-3), "bound": "hbm"}
+    return fwd, bwd_d
 
 
 def cpu_baseline(inp):

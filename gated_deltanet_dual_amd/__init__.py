@@ -17,7 +17,7 @@ import os
 import numpy as np
 
 __all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_bwd",
-           "block_step", "shortconv_dual", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
+           "block_step", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
            "QK_L2NORM", "F32", "BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +83,10 @@ def lib():
     L.flare_gdn_block_step.restype = ctypes.c_int
     L.flare_shortconv_dual.argtypes = [VP, I32, I32, I32, I32, P, P, P, P, I32, P, P, P]
     L.flare_shortconv_dual.restype = ctypes.c_int
+    L.flare_shortconv_dual_bwd_workspace_size.argtypes = [VP, I32, I32, I32]
+    L.flare_shortconv_dual_bwd_workspace_size.restype = SZ
+    L.flare_shortconv_dual_bwd.argtypes = [VP, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, P, P, P, SZ, P]
+    L.flare_shortconv_dual_bwd.restype = ctypes.c_int
     L.flare_timing_enable.argtypes = [I32]
     L.flare_timing_enable.restype = I32
     L.flare_timing_avg_ms.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64)]
@@ -272,6 +276,36 @@ def shortconv_dual(varlen: Varlen, block_size, x, xn, weight, bias=None, activat
                                       _ptr(weight), _ptr(bias), int(activation), _ptr(y), _ptr(yn),
                                       _stream(x.device)))
     return y, yn
+
+
+def shortconv_dual_bwd_workspace_bytes(varlen: Varlen, block_size, channels, width) -> int:
+    """flare_shortconv_dual_bwd_workspace_size for this batch and shape."""
+    return int(lib().flare_shortconv_dual_bwd_workspace_size(varlen.ref(), int(block_size), int(channels),
+                                                             int(width)))
+
+
+def shortconv_dual_bwd(varlen: Varlen, block_size, x, xn, weight, dy, dyn, bias=None, activation=0,
+                       workspace=None, out=None, want_dbias=True):
+    """Reverse mode of shortconv_dual.  Returns (dx, dxn, dweight, dbias);
+    dbias is None when want_dbias is False."""
+    torch = _torch()
+    T, C = x.shape
+    W = weight.shape[1]
+    if out is None:
+        dx, dxn = torch.empty_like(x), torch.empty_like(x)
+        dw = torch.empty((C, W), dtype=torch.float32, device=x.device)
+        db = torch.empty((C,), dtype=torch.float32, device=x.device) if want_dbias else None
+    else:
+        dx, dxn, dw, db = out
+    need = shortconv_dual_bwd_workspace_bytes(varlen, block_size, C, W)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().flare_shortconv_dual_bwd(varlen.ref(), int(block_size), C, W, _io_of(x), _ptr(x), _ptr(xn),
+                                          _ptr(weight), _ptr(bias), int(activation), _ptr(dy), _ptr(dyn),
+                                          _ptr(dx), _ptr(dxn), _ptr(dw), _ptr(db), _ptr(workspace), nbytes,
+                                          _stream(x.device)))
+    return dx, dxn, dw, db
 
 
 def workspace_bytes(varlen: Varlen, H: int, d: int, block_size: int, io: int, flags: int = 0,

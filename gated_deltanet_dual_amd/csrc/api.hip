@@ -194,4 +194,46 @@ flare_status flare_shortconv_dual(const flare_varlen *varlen, int32_t block_size
   return hip_status(launch_shortconv(a, (hipStream_t)stream), "shortconv_dual launch");
 }
 
+size_t flare_shortconv_dual_bwd_workspace_size(const flare_varlen *varlen, int32_t block_size,
+                                               int32_t channels, int32_t width) {
+  VarlenInfo vi;
+  if (check_varlen(varlen, block_size, &vi) != FLARE_OK || channels <= 0 || width < 1 || width > 8) return 0;
+  return shortconv_bwd_workspace_bytes(vi, channels, width);
+}
+
+flare_status flare_shortconv_dual_bwd(const flare_varlen *varlen, int32_t block_size, int32_t channels,
+                                      int32_t width, int32_t io_dtype, const void *x, const void *xn,
+                                      const float *weight, const float *bias, int32_t activation,
+                                      const void *dy, const void *dyn, void *dx, void *dxn,
+                                      float *dweight, float *dbias, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  clear_error();
+  VarlenInfo vi;
+  flare_status st = check_shortconv(varlen, block_size, channels, width, io_dtype, x, xn, weight,
+                                    activation, dx, dxn, &vi);
+  if (st != FLARE_OK) return st;
+  if (!dweight) return fail(FLARE_ERR_NULL, "shortconv_dual_bwd: dweight is NULL");
+  if (vi.total_tokens > 0 && (!dy || !dyn))
+    return fail(FLARE_ERR_NULL, "shortconv_dual_bwd: dy or dyn is NULL");
+  const size_t need = shortconv_bwd_workspace_bytes(vi, channels, width);
+  if (vi.total_tokens > 0 && (!workspace || workspace_bytes < need))
+    return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  ShortConvBwdArgs a{};
+  a.num_docs = varlen->num_docs;
+  a.B = block_size;
+  a.C = channels;
+  a.W = width;
+  a.activation = activation;
+  a.bf16 = io_dtype == FLARE_BF16;
+  a.T = vi.total_tokens;
+  a.cu = varlen->cu_seqlens;
+  a.plen = varlen->prompt_lens;
+  a.x = x; a.xn = xn; a.dy = dy; a.dyn = dyn; a.w = weight; a.bias = bias;
+  a.dx = dx; a.dxn = dxn; a.dw = dweight; a.dbias = dbias;
+  a.part = reinterpret_cast<float *>(workspace);
+  return hip_status(launch_shortconv_bwd(a, (hipStream_t)stream), "shortconv_dual_bwd launch");
+}
+
 }  // extern "C"

@@ -156,6 +156,11 @@ flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
   return FLARE_OK;
 }
 
+size_t shortconv_bwd_workspace_bytes(const VarlenInfo &vi, int32_t channels, int32_t width) {
+  const int64_t runs = (vi.total_tokens + kConvBwdRun - 1) / kConvBwdRun;
+  return (size_t)runs * channels * (width + 1) * sizeof(float) + 256;
+}
+
 flare_status check_shortconv(const flare_varlen *v, int32_t block_size, int32_t channels,
                              int32_t width, int32_t io_dtype, const void *x, const void *xn,
                              const float *w, int32_t activation, const void *y, const void *yn,

@@ -11,6 +11,7 @@
 namespace flare {
 
 constexpr int kChunk = 32;          // tokens per chunk of the chunk-parallel scan
+constexpr int kConvBwdRun = 32;     // tokens per thread run of the ShortConv backward
 constexpr int kVersion = 100;       // 0.1.0
 // fp32 words per (chunk slot, head) of the backward's hand-over from its
 // state-independent pre-pass to its reverse scan (bf16 io, d = 128): the
@@ -64,6 +65,10 @@ flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
                               const void *q, const void *k, const void *v,
                               const float *alpha, const float *beta, const void *o,
                               int32_t mode);
+
+// Bytes of ShortConv-backward workspace: the per-run partials of the weight
+// and bias gradients, ceil(T / 32) runs x channels x (width + 1) fp32.
+size_t shortconv_bwd_workspace_bytes(const VarlenInfo &vi, int32_t channels, int32_t width);
 
 flare_status check_shortconv(const flare_varlen *v, int32_t block_size, int32_t channels,
                              int32_t width, int32_t io_dtype, const void *x, const void *xn,

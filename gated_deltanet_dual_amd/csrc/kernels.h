@@ -27,6 +27,19 @@ struct ShortConvArgs {
 };
 hipError_t launch_shortconv(const ShortConvArgs &a, hipStream_t st);
 
+// reverse mode of the ShortConv (shortconv_bwd.hip)
+struct ShortConvBwdArgs {
+  int num_docs, B, C, W, activation, bf16;
+  int64_t T;
+  const int32_t *cu, *plen;
+  const void *x, *xn, *dy, *dyn;
+  const float *w, *bias;
+  void *dx, *dxn;
+  float *dw, *dbias;
+  float *part;  // workspace: [ceil(T / 32)][C][W + 1] run partials of dweight, dbias
+};
+hipError_t launch_shortconv_bwd(const ShortConvBwdArgs &a, hipStream_t st);
+
 struct FwdArgs {
   int num_docs, H, D, B, flags, bf16, ckpt_stride;
   float scale;

@@ -6,7 +6,8 @@
 namespace flare {
 
 enum KernelId {
-  K_FWD = 0, K_BWD_SCAN, K_BWD_CHUNK, K_BLOCK_STEP, K_SHORTCONV, K_TRI, K_BWD_PRE, K_FWD_PRE, K_FWD_SCAN, K_COUNT
+  K_FWD = 0, K_BWD_SCAN, K_BWD_CHUNK, K_BLOCK_STEP, K_SHORTCONV, K_TRI, K_BWD_PRE, K_FWD_PRE, K_FWD_SCAN, K_SHORTCONV_BWD,
+  K_COUNT
 };
 
 // Records a start event on construction and a stop event on destruction, on

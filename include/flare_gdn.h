@@ -216,6 +216,34 @@ flare_status flare_shortconv_dual(const flare_varlen *varlen,
                                   int32_t activation, void *y, void *yn,
                                   void *stream);
 
+/* Reverse mode of flare_shortconv_dual (Key designs item 3: the gradient of a
+ * noisy output reaches the clean input through its taps before the block start
+ * and the noisy input through its taps inside the block).  Same varlen,
+ * block_size, channels, width, io_dtype, x, xn, weight, bias and activation as
+ * the forward call, plus
+ *   dy, dyn  [T, channels] io   gradients of y and yn (dyn prompt rows ignored)
+ *   dx, dxn  [T, channels] io   written: gradients of x and xn (dxn prompt rows 0)
+ *   dweight  [channels, width] fp32  written
+ *   dbias    [channels] fp32 or NULL  written when given (the sum of the
+ *            pre-activation gradients, whether or not the forward had a bias)
+ *   workspace  flare_shortconv_dual_bwd_workspace_size bytes, 256-byte aligned
+ *            (per-run partial sums of dweight and dbias, reduced in a fixed
+ *            order: the result is run-to-run identical)
+ * Requirements as for the forward. */
+size_t flare_shortconv_dual_bwd_workspace_size(const flare_varlen *varlen,
+                                               int32_t block_size, int32_t channels,
+                                               int32_t width);
+flare_status flare_shortconv_dual_bwd(const flare_varlen *varlen,
+                                      int32_t block_size, int32_t channels,
+                                      int32_t width, int32_t io_dtype,
+                                      const void *x, const void *xn,
+                                      const float *weight, const float *bias,
+                                      int32_t activation, const void *dy,
+                                      const void *dyn, void *dx, void *dxn,
+                                      float *dweight, float *dbias,
+                                      void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
 /* Thread-local message for the last non-OK status; "" if none. */
 const char *flare_last_error(void);
 
@@ -229,6 +257,7 @@ int32_t flare_version(void);
  * (the backward launches the reverse scan, then the per-chunk kernel).
  * Kernel names: "gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel",
  * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel",
+ * "shortconv_dual_bwd_kernel" (both kernels of flare_shortconv_dual_bwd),
  * and, for bf16 io at d = 128, the chunked passes: "gdn_tri_kernel" (the
  * chunk matrices, forward and backward), "gdn_fwd_pre_kernel" and
  * "gdn_bwd_pre_kernel" (the state-independent parts of the chunk steps),

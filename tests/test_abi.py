@@ -180,3 +180,33 @@ def test_shortconv_validation(L):
                                   FAKE, None) == 3
     assert L.flare_shortconv_dual(ctypes.byref(v), 4, 16, 4, g.BF16, None, FAKE, FAKE, None, 0, FAKE,
                                   FAKE, None) == 1
+
+
+def test_shortconv_bwd_workspace_and_validation(L):
+    cu, pl = [0, 37, 37, 100], [8, 0, 4]
+    v = varlen(cu, pl)
+    runs = (100 + 31) // 32
+    for C, W in ((16, 4), (48, 1), (64, 8)):
+        assert L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, C, W) == runs * C * (W + 1) * 4 + 256
+    assert L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, 16, 9) == 0
+    assert L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, 0, 4) == 0
+    need = L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, 16, 4)
+    ok = [FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+
+    def call(C=16, W=4, io=g.BF16, args=ok, ws=FAKE, nbytes=need):
+        return L.flare_shortconv_dual_bwd(ctypes.byref(v), 4, C, W, io, *args, ws, nbytes, None)
+
+    assert call(C=12) == 3                                   # bf16 needs channels % 8
+    assert call(W=9) == 4
+    assert call(io=7) == 4
+    bad = list(ok); bad[4] = 2
+    assert call(args=bad) == 4                               # unknown activation
+    bad = list(ok); bad[5] = None
+    assert call(args=bad) == 1                               # dy NULL
+    bad = list(ok); bad[9] = None
+    assert call(args=bad) == 1                               # dweight NULL
+    assert call(nbytes=need - 1) == 5
+    assert call(ws=None) == 5
+    assert call(ws=ctypes.c_void_p(FAKE.value + 16)) == 5    # misaligned
+    assert L.flare_shortconv_dual_bwd(ctypes.byref(varlen([0, 16], [6])), 4, 16, 4, g.BF16, *ok, FAKE, need,
+                                      None) == 3
