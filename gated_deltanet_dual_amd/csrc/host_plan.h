@@ -11,7 +11,7 @@
 namespace flare {
 
 constexpr int kChunk = 32;          // tokens per chunk of the chunk-parallel scan
-constexpr int kConvBwdRun = 32;     // tokens per thread run of the ShortConv backward
+constexpr int kConvBwdRun = 256;  // tokens per row of the ShortConv reverse-mode partials
 constexpr int kVersion = 100;       // 0.1.0
 // fp32 words per (chunk slot, head) of the backward's hand-over from its
 // state-independent pre-pass to its reverse scan (bf16 io, d = 128): the

@@ -15,15 +15,27 @@
 //   dbias  = sum_t g(t) + g~(t)
 // with in(t) = t - (start of t's block) (-1 on prompt rows).
 //
-// Layout: [T, C] with channels contiguous.  A thread owns N channels (16 or 8
-// bytes) and a run of R tokens, walking positions in order with three sliding
-// register windows of WM rows: the inputs (to rebuild z and for dwl), the
-// output gradients g, g~ with each row's in(t) (dx(m) needs the W rows
-// m .. m + W - 1, so it is emitted W - 1 steps after m), and the per-lag
-// weight-gradient partials of the run.  Those partials go to a workspace
-// [run][C][W + 1] (taps, then bias) and a second kernel sums them over the
-// runs in a fixed order, so the result is deterministic.  Streaming: bound by
-// HBM bandwidth.
+// Layout: [T, C] with channels contiguous.  A lane owns an 8-byte slice of
+// channels (4 bytes for W > 4) and walks a run of 64 tokens; the four waves of
+// a workgroup take four consecutive runs over the same channels.  Scatter form:
+// at step t the lane turns g(t), g~(t) into their contributions to the pending
+// dx, dx~ rows t - L, L < W; row t - W + 1 is then complete and stored.  Since
+// t is uniform over the wave, which lags are noisy (L <= in(t)) and which still
+// lie in the document (L <= t - doc start) are uniform branches, not selects.
+//
+// Registers are indexed by step modulo U (U = max(W, 4); the loop is unrolled
+// by U, so no window ever shifts), and the four input rows of step t + U - 1
+// are loaded at step t.  Every load and store of the loop is unconditional
+// (rows clamped into the batch, rows that are not needed redirected to the
+// clean input row of the same step, which the same step loads anyway), so the
+// compiler's wait counts never have to assume a skipped access and U - 1 steps
+// of loads stay in flight.  The per-lag weight-gradient partials of the four
+// runs are summed in LDS in a fixed order and written to a workspace
+// [256-token block][C][W + 1] (taps, then bias); a second kernel sums them
+// over the blocks in order, so the result is run-to-run identical.  Streaming:
+// bound by HBM bandwidth.
+#include <utility>
+
 #include "device_common.h"
 #include "host_plan.h"
 #include "kernels.h"
@@ -33,28 +45,16 @@ namespace flare {
 
 namespace {
 
-constexpr int kBRun = kConvBwdRun;  // tokens per thread (the workspace is sized by it)
-constexpr int kBThreads = 256;
+constexpr int kBWaves = 4;                       // runs per workgroup
+constexpr int kBRun = kConvBwdRun / kBWaves;     // tokens per wave (64)
+static_assert(kBRun * kBWaves == kConvBwdRun, "workspace rows must be whole workgroups");
 
-template <typename IO, int N> struct BVec;
-template <> struct BVec<u16, 8> {
-  static __device__ __forceinline__ void load(const u16 *p, float *f) {
-    const uint4 r = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-  static __device__ __forceinline__ void store(u16 *p, const float *f) {
-    *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                               pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
-  }
-};
-template <> struct BVec<u16, 4> {
-  static __device__ __forceinline__ void load(const u16 *p, float *f) {
-    const uint2 r = *reinterpret_cast<const uint2 *>(p);
+// A lane's slice of one row: N channels of type IO, loaded as one word.
+template <typename IO, int N> struct Slice;
+template <> struct Slice<u16, 4> {
+  using Raw = uint2;
+  static __device__ __forceinline__ Raw load(const u16 *p) { return *reinterpret_cast<const uint2 *>(p); }
+  static __device__ __forceinline__ void cvt(Raw r, float *f) {
     f[0] = __uint_as_float(r.x << 16);
     f[1] = __uint_as_float(r.x & 0xffff0000u);
     f[2] = __uint_as_float(r.y << 16);
@@ -64,14 +64,30 @@ template <> struct BVec<u16, 4> {
     *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
   }
 };
-template <> struct BVec<float, 4> {
-  static __device__ __forceinline__ void load(const float *p, float *f) {
-    const float4 r = *reinterpret_cast<const float4 *>(p);
-    f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
+template <> struct Slice<u16, 2> {
+  using Raw = uint32_t;
+  static __device__ __forceinline__ Raw load(const u16 *p) { return *reinterpret_cast<const uint32_t *>(p); }
+  static __device__ __forceinline__ void cvt(Raw r, float *f) {
+    f[0] = __uint_as_float(r << 16);
+    f[1] = __uint_as_float(r & 0xffff0000u);
   }
+  static __device__ __forceinline__ void store(u16 *p, const float *f) {
+    *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(f[0], f[1]);
+  }
+};
+template <> struct Slice<float, 2> {
+  using Raw = float2;
+  static __device__ __forceinline__ Raw load(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+  static __device__ __forceinline__ void cvt(Raw r, float *f) { f[0] = r.x; f[1] = r.y; }
   static __device__ __forceinline__ void store(float *p, const float *f) {
-    *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float2 *>(p) = make_float2(f[0], f[1]);
   }
+};
+template <> struct Slice<float, 1> {
+  using Raw = float;
+  static __device__ __forceinline__ Raw load(const float *p) { return *p; }
+  static __device__ __forceinline__ void cvt(Raw r, float *f) { f[0] = r; }
+  static __device__ __forceinline__ void store(float *p, const float *f) { *p = f[0]; }
 };
 
 __device__ __forceinline__ float silu_grad(float z) {
@@ -79,246 +95,269 @@ __device__ __forceinline__ float silu_grad(float z) {
   return sg * (1.f + z * (1.f - sg));
 }
 
-// the document containing position t (uniform: every thread of a workgroup
-// walks the same positions), advanced monotonically
-struct DocCursor {
-  int doc;
-  int64_t ds, de, P;
-  __device__ __forceinline__ void seek(const ShortConvBwdArgs &a, int64_t t) {
-    int lo = 0, hi = a.num_docs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.cu[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    doc = lo;
-    ds = a.cu[doc];
-    de = a.cu[doc + 1];
-    P = a.plen[doc];
-  }
-  // true when t starts a new document (also past empty ones)
-  __device__ __forceinline__ bool advance(const ShortConvBwdArgs &a, int64_t t) {
-    bool moved = false;
-    while (t >= de && doc + 1 < a.num_docs) {
-      ++doc;
-      ds = a.cu[doc];
-      de = a.cu[doc + 1];
-      P = a.plen[doc];
-      moved = true;
-    }
-    return moved || t == ds;
-  }
+template <typename IO, int W> struct BwdCfg {
+  static constexpr int N = (W <= 4 ? 8 : 4) / (int)sizeof(IO);  // channels per lane
+  static constexpr int U = W < 4 ? 4 : W;                        // ring slots
+  static constexpr int RED = 64 * N * (W + 1);                   // partials per wave
 };
+
+// f(integral_constant<int, J>) for J = 0, 1, ... in order (static slot indices)
+template <typename F, int... J>
+__device__ __forceinline__ void for_each_slot(std::integer_sequence<int, J...>, F &&f) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
 
 }  // namespace
 
-template <typename IO, int W, int N>
-__global__ __launch_bounds__(kBThreads) void shortconv_dual_bwd_kernel(ShortConvBwdArgs a) {
-  constexpr int WM = W;
-  using V = BVec<IO, N>;
-  const int64_t c0 = ((int64_t)blockIdx.y * kBThreads + threadIdx.x) * N;
-  if (c0 >= a.C) return;
-  const int run = blockIdx.x;
-  const int64_t t_begin = (int64_t)run * kBRun;
-  const int64_t t_end = min(t_begin + kBRun, a.T);
-  const IO *x = reinterpret_cast<const IO *>(a.x), *xn = reinterpret_cast<const IO *>(a.xn);
-  const IO *dy = reinterpret_cast<const IO *>(a.dy), *dyn = reinterpret_cast<const IO *>(a.dyn);
-  IO *dx = reinterpret_cast<IO *>(a.dx), *dxn = reinterpret_cast<IO *>(a.dxn);
+template <typename IO, int W, bool ACT>
+__global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(
+    ShortConvBwdArgs a, const int32_t *__restrict__ cu, const int32_t *__restrict__ plen,
+    const IO *__restrict__ x, const IO *__restrict__ xn, const IO *__restrict__ dy, const IO *__restrict__ dyn,
+    IO *__restrict__ dx, IO *__restrict__ dxn, float *__restrict__ part) {
+  using Cfg = BwdCfg<IO, W>;
+  constexpr int N = Cfg::N, U = Cfg::U;
+  using S = Slice<IO, N>;
+  using Raw = typename S::Raw;
+  __shared__ float red[kBWaves][Cfg::RED];
 
-  float wl[WM][N];
-#pragma unroll
-  for (int L = 0; L < WM; ++L)
-#pragma unroll
-    for (int c = 0; c < N; ++c) wl[L][c] = a.w[(c0 + c) * W + (W - 1 - L)];
-  float bias[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) bias[c] = a.bias ? a.bias[c0 + c] : 0.f;
+  // the wave index through readfirstlane: everything derived from it (the
+  // run, the documents, the per-step lag counts) is then known to be uniform
+  // and lives in scalar registers.  Positions are 32-bit (the entry point
+  // checks T < 2^31).
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t C = a.C;
+  const int T = (int)a.T;
+  const int64_t cb = (int64_t)blockIdx.y * 64 * N;
+  // lanes past the last channel repeat the last slice: same inputs, same
+  // results, same addresses -- their stores are harmless duplicates
+  const int64_t cl = min(cb + (int64_t)lane * N, C - N);
+  const uint32_t lo = (uint32_t)(cl * (int64_t)sizeof(IO));  // byte offset in a row
+  const int tb = (int)blockIdx.x * kConvBwdRun + wave * kBRun;
+  const int te = min(tb + kBRun, T);
+  auto at = [&](const IO *row) { return S::load(reinterpret_cast<const IO *>(reinterpret_cast<const char *>(row) + lo)); };
 
-  // windows: inputs at t - L, output gradients at t - L (row L = 0 newest)
-  float hx[WM][N], hn[WM][N], gc[WM][N], gn[WM][N];
-  int ins[WM];
-#pragma unroll
-  for (int L = 0; L < WM; ++L) {
-    ins[L] = -1;
-#pragma unroll
-    for (int c = 0; c < N; ++c) hx[L][c] = hn[L][c] = gc[L][c] = gn[L][c] = 0.f;
-  }
-  float dwl[WM][N], db[N];
+  float dwl[W][N], db[N];
 #pragma unroll
   for (int c = 0; c < N; ++c) {
     db[c] = 0.f;
 #pragma unroll
-    for (int L = 0; L < WM; ++L) dwl[L][c] = 0.f;
+    for (int L = 0; L < W; ++L) dwl[L][c] = 0.f;
   }
 
-  const int64_t t_lo = max((int64_t)0, t_begin - (W - 1));
-  const int64_t t_hi = t_end + (W - 1);
-  DocCursor dt, dm;
-  dt.seek(a, t_lo);
-  dm.seek(a, t_begin);
+  if (te > tb) {
+    float wl[W][N], bias[N];
+#pragma unroll
+    for (int L = 0; L < W; ++L)
+#pragma unroll
+      for (int c = 0; c < N; ++c) wl[L][c] = a.w[(cl + c) * W + (W - 1 - L)];
+#pragma unroll
+    for (int c = 0; c < N; ++c) bias[c] = ACT && a.bias ? a.bias[cl + c] : 0.f;
 
-  for (int64_t t = t_lo; t < t_hi; ++t) {
-    const bool valid = t < a.T;
-    // ---- inputs at t (a new document starts with an empty history)
-    if (valid && dt.advance(a, t)) {
-#pragma unroll
-      for (int L = 0; L < WM; ++L)
-#pragma unroll
-        for (int c = 0; c < N; ++c) hx[L][c] = hn[L][c] = 0.f;
-    }
-    const int64_t tp = t - dt.ds;
-    const bool resp = valid && tp >= dt.P;
-#pragma unroll
-    for (int L = WM - 1; L > 0; --L) {
-      ins[L] = ins[L - 1];
-#pragma unroll
-      for (int c = 0; c < N; ++c) {
-        hx[L][c] = hx[L - 1][c];
-        hn[L][c] = hn[L - 1][c];
-        gc[L][c] = gc[L - 1][c];
-        gn[L][c] = gn[L - 1][c];
+    // steps t in [t0, te + W - 1), a whole number of U-step groups: output
+    // m = t - W + 1 is complete at step t; the first steps only fill the
+    // windows (their stores go to row tb, which its own step rewrites later)
+    const int nsteps = (te - tb + 2 * (W - 1) + U - 1) / U * U;
+    const int t0 = te + W - 1 - nsteps;
+    // documents of the computed step (dc) and of the loaded one (dl)
+    int dc = 0;
+    {
+      const int t1 = max(t0, 0);
+      int hi = a.num_docs - 1;
+      while (dc < hi) {
+        const int mid = (dc + hi + 1) >> 1;
+        if (cu[mid] <= t1) dc = mid; else hi = mid - 1;
       }
     }
+    int cds = cu[dc], cde = cu[dc + 1], cP = plen[dc];
+    int dl = dc, lds_ = cds, lde = cde, lP = cP;
+    // position in the block at the step before the first valid one; stepped
+    // after (blocks start at the prompt end, prompts are whole blocks)
+    int inb = 0;
+    {
+      const int tp1 = max(t0, 0) - cds;
+      if (tp1 > cP) inb = (tp1 - 1 - cP) % a.B;
+    }
+
+    Raw rx[U], rn[U], rg[U], rgn[U];
+    // windows start at zero: the first steps read slots no step has filled
+    // yet, with zero weight (0 * garbage could be NaN)
+    float hx[U][N], hn[U][N], ax[U][N], an[U][N];
 #pragma unroll
-    for (int c = 0; c < N; ++c) hx[0][c] = hn[0][c] = gc[0][c] = gn[0][c] = 0.f;
-    ins[0] = -1;
-    if (valid) V::load(x + t * a.C + c0, hx[0]);
-    if (resp) V::load(xn + t * a.C + c0, hn[0]);
-    // ---- output gradients at t (needed from t_begin on)
-    if (valid && t >= t_begin) {
-      const int64_t inside = resp ? tp - (dt.P + ((tp - dt.P) / a.B) * a.B) : -1;
-      ins[0] = (int)inside;
-      float g[N], gv[N];
-      V::load(dy + t * a.C + c0, g);
-      if (a.activation == 1) {
-        float z[N];
+    for (int j = 0; j < U; ++j)
 #pragma unroll
-        for (int c = 0; c < N; ++c) z[c] = bias[c];
-#pragma unroll
-        for (int L = 0; L < WM; ++L)
-#pragma unroll
-          for (int c = 0; c < N; ++c) z[c] += wl[L][c] * hx[L][c];
-#pragma unroll
-        for (int c = 0; c < N; ++c) g[c] *= silu_grad(z[c]);
+      for (int c = 0; c < N; ++c) hx[j][c] = hn[j][c] = ax[j][c] = an[j][c] = 0.f;
+    auto issue = [&](int slot, int t) {
+      const int tc = min(max(t, 0), T - 1);
+      while (tc >= lde && dl + 1 < a.num_docs) {
+        ++dl;
+        lds_ = cu[dl];
+        lde = cu[dl + 1];
+        lP = plen[dl];
       }
+      const bool resp = t >= 0 && t < T && tc - lds_ >= lP;
+      const bool grad = t >= tb && t < T;
+      const int64_t o = (int64_t)tc * C;
+      rx[slot] = at(x + o);
+      rn[slot] = at((resp ? xn : x) + o);
+      rg[slot] = at((grad ? dy : x) + o);
+      rgn[slot] = at((grad && resp ? dyn : x) + o);
+    };
 #pragma unroll
-      for (int c = 0; c < N; ++c) gv[c] = 0.f;
-      if (resp) {
-        V::load(dyn + t * a.C + c0, gv);
-        if (a.activation == 1) {
-          float z[N];
+    for (int j = 0; j < U - 1; ++j) issue(j, t0 + j);
+
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+      for_each_slot(std::make_integer_sequence<int, U>{}, [&](auto jc) {
+        constexpr int J = decltype(jc)::value;
+        const int t = t0 + s0 + J;
+        float g[N], gn[N];
+        S::cvt(rx[J], hx[J]);
+        S::cvt(rn[J], hn[J]);
+        S::cvt(rg[J], g);
+        S::cvt(rgn[J], gn);
+        issue((J + U - 1) % U, t + U - 1);
+        const bool valid = t >= 0 && t < T;
+        if (valid) {
+          while (t >= cde && dc + 1 < a.num_docs) {
+            ++dc;
+            cds = cu[dc];
+            cde = cu[dc + 1];
+            cP = plen[dc];
+          }
+        }
+        const int tp = t - cds;
+        const bool resp = valid && tp >= cP;
+        if (resp) inb = tp == cP || inb + 1 == a.B ? 0 : inb + 1;
+        // lags L < nb read inside the document, L < na inside the block
+        // (noisy); no gradient before the run or past the batch
+        const bool grad = valid && t >= tb;
+        const int nb = grad ? min(tp + 1, W) : 0;
+        const int na = grad && resp ? min(inb + 1, W) : 0;
+        const bool own = grad && t < te;
+        if (ACT) {
+          float z[N], zn[N];
 #pragma unroll
-          for (int c = 0; c < N; ++c) z[c] = bias[c];
+          for (int c = 0; c < N; ++c) z[c] = zn[c] = bias[c];
 #pragma unroll
-          for (int L = 0; L < WM; ++L) {
-            const bool noisy = L <= inside;
+          for (int L = 0; L < W; ++L) {
+            const int r = (J - L + U * W) % U;
 #pragma unroll
-            for (int c = 0; c < N; ++c) z[c] += wl[L][c] * (noisy ? hn[L][c] : hx[L][c]);
+            for (int c = 0; c < N; ++c) {
+              const float hxu = L < nb ? hx[r][c] : 0.f;
+              z[c] = fmaf(wl[L][c], hxu, z[c]);
+              zn[c] = fmaf(wl[L][c], L < na ? hn[r][c] : hxu, zn[c]);
+            }
           }
 #pragma unroll
-          for (int c = 0; c < N; ++c) gv[c] *= silu_grad(z[c]);
+          for (int c = 0; c < N; ++c) {
+            g[c] *= silu_grad(z[c]);
+            gn[c] *= silu_grad(zn[c]);
+          }
         }
-      }
+        float gs[N];
 #pragma unroll
-      for (int c = 0; c < N; ++c) {
-        gc[0][c] = g[c];
-        gn[0][c] = gv[c];
-      }
-      // ---- weight and bias partials over this run's outputs
-      if (t < t_end) {
+        for (int c = 0; c < N; ++c) gs[c] = na > 0 ? g[c] + gn[c] : g[c];
 #pragma unroll
-        for (int L = 0; L < WM; ++L) {
-          const bool noisy = L <= inside;
+        for (int L = 0; L < W; ++L) {
+          const int r = (J - L + U * W) % U;
+          const bool live = L < nb, noisy = L < na;
 #pragma unroll
-          for (int c = 0; c < N; ++c) dwl[L][c] += g[c] * hx[L][c] + gv[c] * (noisy ? hn[L][c] : hx[L][c]);
+          for (int c = 0; c < N; ++c) {
+            // the part of the output gradient that reads x (q) and x~ (p)
+            const float q = noisy ? g[c] : live ? gs[c] : 0.f;
+            const float p = noisy ? gn[c] : 0.f;
+            dwl[L][c] = fmaf(own ? q : 0.f, hx[r][c], dwl[L][c]);
+            dwl[L][c] = fmaf(own ? p : 0.f, hn[r][c], dwl[L][c]);
+            if (L == 0) {
+              ax[J][c] = wl[0][c] * q;
+              an[J][c] = wl[0][c] * p;
+            } else {
+              ax[r][c] = fmaf(wl[L][c], q, ax[r][c]);
+              an[r][c] = fmaf(wl[L][c], p, an[r][c]);
+            }
+          }
         }
 #pragma unroll
-        for (int c = 0; c < N; ++c) db[c] += g[c] + gv[c];
-      }
-    }
-    // ---- dx(m), dx~(m) for m = t - (W - 1): rows m + L sit in window row W - 1 - L
-    const int64_t m = t - (W - 1);
-    if (m >= t_begin && m < t_end) {
-      dm.advance(a, m);
-      float ox[N], on[N];
-#pragma unroll
-      for (int c = 0; c < N; ++c) ox[c] = on[c] = 0.f;
-#pragma unroll
-      for (int L = 0; L < W; ++L) {
-        const int r = W - 1 - L;  // window row of output m + L
-        // outputs of m's document only
-        const bool in_doc = m + L < dm.de;
-        const bool noisy = L <= ins[r];
-#pragma unroll
-        for (int c = 0; c < N; ++c) {
-          const float gcr = in_doc ? gc[r][c] : 0.f, gnr = in_doc ? gn[r][c] : 0.f;
-          ox[c] += wl[L][c] * (gcr + (noisy ? 0.f : gnr));
-          on[c] += noisy ? wl[L][c] * gnr : 0.f;
-        }
-      }
-      V::store(dx + m * a.C + c0, ox);
-      V::store(dxn + m * a.C + c0, on);
+        for (int c = 0; c < N; ++c) db[c] += own ? gs[c] : 0.f;
+        // row t - W + 1 has all its contributions
+        constexpr int r = (J - (W - 1) + U * W) % U;
+        const int64_t m = (int64_t)max(t - (W - 1), tb) * C;
+        S::store(reinterpret_cast<IO *>(reinterpret_cast<char *>(dx + m) + lo), ax[r]);
+        S::store(reinterpret_cast<IO *>(reinterpret_cast<char *>(dxn + m) + lo), an[r]);
+      });
     }
   }
-  // ---- partials: [run][C][W + 1], taps by index j = W - 1 - L, then the bias
-  float *part = a.part + ((size_t)run * a.C + c0) * (W + 1);
+
+  // ---- weight and bias partials of the four runs, summed in wave order
+  float *mine = red[wave] + lane * N * (W + 1);
 #pragma unroll
   for (int c = 0; c < N; ++c) {
 #pragma unroll
-    for (int L = 0; L < W; ++L) part[(size_t)c * (W + 1) + (W - 1 - L)] = dwl[L][c];
-    part[(size_t)c * (W + 1) + W] = db[c];
+    for (int L = 0; L < W; ++L) mine[c * (W + 1) + (W - 1 - L)] = dwl[L][c];
+    mine[c * (W + 1) + W] = db[c];
   }
+  __syncthreads();
+  const int nel = (int)min((int64_t)64 * N, C - cb) * (W + 1);
+  float *dst = part + ((size_t)blockIdx.x * C + cb) * (W + 1);
+  for (int e = threadIdx.x; e < nel; e += 256) dst[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
 }
 
-// dweight[c][j] and dbias[c]: the run partials summed in run order
-__global__ __launch_bounds__(256) void shortconv_bwd_reduce_kernel(ShortConvBwdArgs a, int runs) {
+// dweight[c][j] and dbias[c]: the block partials summed in block order
+__global__ __launch_bounds__(256) void shortconv_bwd_reduce_kernel(ShortConvBwdArgs a, int blocks) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int W1 = a.W + 1;
   if (i >= (int64_t)a.C * W1) return;
   float s = 0.f;
-  for (int r = 0; r < runs; ++r) s += a.part[(size_t)r * a.C * W1 + i];
+  for (int r = 0; r < blocks; ++r) s += a.part[(size_t)r * a.C * W1 + i];
   const int64_t c = i / W1, j = i % W1;
   if (j < a.W) a.dw[c * a.W + j] = s;
   else if (a.dbias) a.dbias[c] = s;
 }
 
 template <typename IO, int W>
-static hipError_t launch_bwd_w(const ShortConvBwdArgs &a, int runs, hipStream_t st) {
-  // up to 4 taps 16-byte rows of channels per thread; wider windows take half
-  // as many channels, so the four windows still fit in registers
-  constexpr int N = (sizeof(IO) == 2 && W <= 4) ? 8 : 4;
-  // runs on x (no 65535 limit there), channel groups on y
-  const dim3 grid((unsigned)runs, (unsigned)((a.C / N + kBThreads - 1) / kBThreads));
+static hipError_t launch_bwd_w(const ShortConvBwdArgs &a, int blocks, hipStream_t st) {
+  constexpr int N = BwdCfg<IO, W>::N;
+  // token blocks on x (no 65535 limit there), channel groups on y
+  const dim3 grid((unsigned)blocks, (unsigned)((a.C + 64 * N - 1) / (64 * N)));
   if (grid.y > 65535u) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((shortconv_dual_bwd_kernel<IO, W, N>), grid, dim3(kBThreads), 0, st, a);
+  const IO *x = reinterpret_cast<const IO *>(a.x), *xn = reinterpret_cast<const IO *>(a.xn);
+  const IO *dy = reinterpret_cast<const IO *>(a.dy), *dyn = reinterpret_cast<const IO *>(a.dyn);
+  IO *dx = reinterpret_cast<IO *>(a.dx), *dxn = reinterpret_cast<IO *>(a.dxn);
+  if (a.activation == 1)
+    hipLaunchKernelGGL((shortconv_dual_bwd_kernel<IO, W, true>), grid, dim3(256), 0, st, a, a.cu, a.plen, x, xn,
+                       dy, dyn, dx, dxn, a.part);
+  else
+    hipLaunchKernelGGL((shortconv_dual_bwd_kernel<IO, W, false>), grid, dim3(256), 0, st, a, a.cu, a.plen, x, xn,
+                       dy, dyn, dx, dxn, a.part);
   return hipGetLastError();
 }
 
 template <typename IO>
-static hipError_t launch_bwd_io(const ShortConvBwdArgs &a, int runs, hipStream_t st) {
+static hipError_t launch_bwd_io(const ShortConvBwdArgs &a, int blocks, hipStream_t st) {
   switch (a.W) {
-    case 1: return launch_bwd_w<IO, 1>(a, runs, st);
-    case 2: return launch_bwd_w<IO, 2>(a, runs, st);
-    case 3: return launch_bwd_w<IO, 3>(a, runs, st);
-    case 4: return launch_bwd_w<IO, 4>(a, runs, st);
-    case 5: return launch_bwd_w<IO, 5>(a, runs, st);
-    case 6: return launch_bwd_w<IO, 6>(a, runs, st);
-    case 7: return launch_bwd_w<IO, 7>(a, runs, st);
-    case 8: return launch_bwd_w<IO, 8>(a, runs, st);
+    case 1: return launch_bwd_w<IO, 1>(a, blocks, st);
+    case 2: return launch_bwd_w<IO, 2>(a, blocks, st);
+    case 3: return launch_bwd_w<IO, 3>(a, blocks, st);
+    case 4: return launch_bwd_w<IO, 4>(a, blocks, st);
+    case 5: return launch_bwd_w<IO, 5>(a, blocks, st);
+    case 6: return launch_bwd_w<IO, 6>(a, blocks, st);
+    case 7: return launch_bwd_w<IO, 7>(a, blocks, st);
+    case 8: return launch_bwd_w<IO, 8>(a, blocks, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_shortconv_bwd(const ShortConvBwdArgs &a, hipStream_t st) {
-  const int runs = (int)((a.T + kBRun - 1) / kBRun);
+  const int blocks = (int)((a.T + kConvBwdRun - 1) / kConvBwdRun);
   if (a.C <= 0) return hipSuccess;
   TimedLaunch tl(K_SHORTCONV_BWD, st);
-  if (runs > 0) {
-    hipError_t e = a.bf16 ? launch_bwd_io<u16>(a, runs, st) : launch_bwd_io<float>(a, runs, st);
+  if (blocks > 0) {
+    hipError_t e = a.bf16 ? launch_bwd_io<u16>(a, blocks, st) : launch_bwd_io<float>(a, blocks, st);
     if (e != hipSuccess) return e;
   }
-  // with no tokens (runs = 0) this writes the zero sums
+  // with no tokens (blocks = 0) this writes the zero sums
   const int64_t outs = (int64_t)a.C * (a.W + 1);
-  hipLaunchKernelGGL(shortconv_bwd_reduce_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st, a, runs);
+  hipLaunchKernelGGL(shortconv_bwd_reduce_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st, a,
+                     blocks);
   return hipGetLastError();
 }
 

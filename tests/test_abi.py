@@ -185,9 +185,11 @@ def test_shortconv_validation(L):
 def test_shortconv_bwd_workspace_and_validation(L):
     cu, pl = [0, 37, 37, 100], [8, 0, 4]
     v = varlen(cu, pl)
-    runs = (100 + 31) // 32
+    blocks = (100 + 255) // 256  # weight-gradient partials per 256-token block
     for C, W in ((16, 4), (48, 1), (64, 8)):
-        assert L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, C, W) == runs * C * (W + 1) * 4 + 256
+        assert L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, C, W) == blocks * C * (W + 1) * 4 + 256
+    v2 = varlen([0, 300, 600], [0, 0])
+    assert L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v2), 4, 16, 4) == 3 * 16 * 5 * 4 + 256
     assert L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, 16, 9) == 0
     assert L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, 0, 4) == 0
     need = L.flare_shortconv_dual_bwd_workspace_size(ctypes.byref(v), 4, 16, 4)

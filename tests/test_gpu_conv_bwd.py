@@ -5,8 +5,8 @@ inputs.
   * exact: small-integer inputs, weights and output gradients (fp32 and bf16
     io), so every sum is exact and any misplaced tap, source or document boundary shows as a
     nonzero difference;
-  * ragged documents (empty, shorter than the window, across the 32-token runs)
-    for every width 1..8, both io dtypes, with and without SiLU and bias;
+  * ragged documents (empty, shorter than the window, across the 64-token runs
+    and the 256-token blocks of the weight-gradient partials) for widths 1..8, both io dtypes, with and without SiLU and bias;
   * the full packed row (32768 tokens, 8 documents, 3*32*128 channels, W=4,
     bf16) on 512 sampled channels;
   * no tokens: the weight and bias gradients are written as zeros;
@@ -36,8 +36,10 @@ def g():
     return g
 
 
-LENS = [37, 0, 3, 70, 5, 96, 1]
-PROMPTS = [12, 0, 0, 20, 4, 32, 0]
+# 302 tokens: runs of 64 tokens, a second 256-token block with a partial run
+# and two empty ones
+LENS = [37, 0, 3, 70, 5, 96, 1, 90]
+PROMPTS = [12, 0, 0, 20, 4, 32, 0, 40]
 
 
 def _cu(lens):
@@ -57,7 +59,8 @@ def _run(g, dev, cu, prompts, B, x, xn, w, dy, dyn, bias=None, act=0, bf16=False
 
 @pytest.mark.parametrize("W,bf16", [(1, False), (2, True), (4, False), (4, True), (5, False), (8, True)])
 def test_conv_bwd_exact_integers(g, dev, W, bf16):
-    """|dx| <= 8 taps * 3 * 8 = 192 < 256: exact in bf16 as well."""
+    """|dx| <= 8 taps * 3 * 8 = 192 < 256: exact in bf16 as well; the weight
+    sums stay below 2^24."""
     rng = np.random.default_rng(70 + W)
     cu, B, C = _cu(LENS), 4, 8
     T = int(cu[-1])
