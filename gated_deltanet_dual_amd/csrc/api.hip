@@ -213,9 +213,6 @@ flare_status flare_shortconv_dual_bwd(const flare_varlen *varlen, int32_t block_
                                     activation, dx, dxn, &vi);
   if (st != FLARE_OK) return st;
   if (!dweight) return fail(FLARE_ERR_NULL, "shortconv_dual_bwd: dweight is NULL");
-  if (vi.total_tokens > INT32_MAX - 4096)
-    return fail(FLARE_ERR_UNSUPPORTED, "shortconv_dual_bwd: %lld tokens, at most 2^31 - 4097",
-                (long long)vi.total_tokens);
   if (vi.total_tokens > 0 && (!dy || !dyn))
     return fail(FLARE_ERR_NULL, "shortconv_dual_bwd: dy or dyn is NULL");
   const size_t need = shortconv_bwd_workspace_bytes(vi, channels, width);

@@ -178,6 +178,10 @@ flare_status check_shortconv(const flare_varlen *v, int32_t block_size, int32_t 
     return fail(FLARE_ERR_UNSUPPORTED, "activation %d unknown", activation);
   if (out->total_tokens > 0 && (!x || !xn || !w || !y || !yn))
     return fail(FLARE_ERR_NULL, "shortconv: a required pointer is NULL");
+  // token positions are 32-bit in the kernels, with room for a run past the end
+  if (out->total_tokens > INT32_MAX - 4096)
+    return fail(FLARE_ERR_UNSUPPORTED, "shortconv: %lld tokens, at most 2^31 - 4097",
+                (long long)out->total_tokens);
   return FLARE_OK;
 }
 

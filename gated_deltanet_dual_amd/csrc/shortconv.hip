@@ -8,176 +8,208 @@
 // the document start read zero (cu_seqlens guard).  Clean taps always read the
 // clean input.  Noisy prompt rows are written as zeros.
 //
-// Layout: x, xn, y, yn are [T, C] with channels contiguous.  Each thread owns
-// 16 bytes of channels (8 bf16 or 4 fp32) and walks a run of R consecutive
-// tokens, keeping the last WMAX rows of both streams in registers, so every
-// input row is fetched from HBM about once (plus a W-1 row halo per run).  The
-// kernel is a pure streaming kernel: bound by HBM bandwidth.
+// Layout: x, xn, y, yn are [T, C] with channels contiguous.  A lane owns an
+// 8-byte slice of channels (4 bytes for W > 4) and walks a run of 64 tokens,
+// keeping the last W rows of both inputs in registers, so every input row is
+// read from HBM about once (plus a W - 1 row halo per run); the four waves of
+// a workgroup take four consecutive runs.  Since the step's position is
+// uniform over the wave, which taps lie inside the document and which inside
+// the block are wave-uniform masks.  The input rows of step t + U - 1 are
+// loaded at step t into a register ring of U = max(W, 4) slots (the loop is
+// unrolled by U, so slots are static), and every load and store is
+// unconditional -- rows clamped into the batch, the noisy row of a prompt
+// position redirected to the clean row the step loads anyway -- so U - 1
+// steps of loads stay in flight.  A pure streaming kernel: bound by HBM
+// bandwidth.
+#include "conv_common.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "timing.h"
 
 namespace flare {
 
-constexpr int kConvRun = 32;   // tokens per thread
-constexpr int kConvWMax = 8;   // largest supported width
-constexpr int kConvThreads = 256;
+using conv::Slice;
+using conv::for_each_slot;
 
-template <typename IO> struct ConvVec;
-template <> struct ConvVec<u16> {
-  static constexpr int N = 8;
-  static __device__ __forceinline__ void load(const u16 *p, float *f) {
-    const uint4 r = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+namespace {
+
+constexpr int kConvWaves = 4;   // runs per workgroup
+constexpr int kConvRun = 64;    // tokens per wave
+
+template <typename IO, int W> struct FwdCfg {
+  static constexpr int N = (W <= 4 ? 8 : 4) / (int)sizeof(IO);  // channels per lane
+  static constexpr int U = W < 4 ? 4 : W;                        // ring slots
+};
+
+}  // namespace
+
+template <typename IO, int W, bool ACT>
+__global__ __launch_bounds__(256) void shortconv_dual_kernel(ShortConvArgs a, const int32_t *__restrict__ cu,
+                                                             const int32_t *__restrict__ plen,
+                                                             const IO *__restrict__ x, const IO *__restrict__ xn,
+                                                             IO *__restrict__ y, IO *__restrict__ yn) {
+  using Cfg = FwdCfg<IO, W>;
+  constexpr int N = Cfg::N, U = Cfg::U;
+  using S = Slice<IO, N>;
+  using Raw = typename S::Raw;
+
+  // the wave index through readfirstlane: the run, its documents and the
+  // per-step tap masks are then uniform (scalar registers)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t C = a.C;
+  const int T = (int)a.T;
+  const int64_t cb = (int64_t)blockIdx.y * 64 * N;
+  // lanes past the last channel repeat the last slice (duplicate stores of
+  // identical values)
+  const int64_t cl = min(cb + (int64_t)lane * N, C - N);
+  const uint32_t lo = (uint32_t)(cl * (int64_t)sizeof(IO));
+  const int tb = (int)blockIdx.x * (kConvWaves * kConvRun) + wave * kConvRun;
+  const int te = min(tb + kConvRun, T);
+  if (te <= tb) return;
+  auto at = [&](const IO *row) { return S::load(reinterpret_cast<const IO *>(reinterpret_cast<const char *>(row) + lo)); };
+
+  // weights by lag: wl[L] multiplies the input L tokens back
+  float wl[W][N], bias[N];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  for (int L = 0; L < W; ++L)
+#pragma unroll
+    for (int c = 0; c < N; ++c) wl[L][c] = a.w[(cl + c) * W + (W - 1 - L)];
+#pragma unroll
+  for (int c = 0; c < N; ++c) bias[c] = a.bias ? a.bias[cl + c] : 0.f;
+
+  // steps t in [t0, te), a whole number of U-step groups; the first W - 1 (or
+  // more) only fill the window, and their stores go to row tb, which its own
+  // step rewrites later
+  const int nsteps = (te - tb + W - 1 + U - 1) / U * U;
+  const int t0 = te - nsteps;
+  int dc = 0;
+  {
+    const int t1 = max(t0, 0);
+    int hi = a.num_docs - 1;
+    while (dc < hi) {
+      const int mid = (dc + hi + 1) >> 1;
+      if (cu[mid] <= t1) dc = mid; else hi = mid - 1;
     }
   }
-  static __device__ __forceinline__ void store(u16 *p, const float *f) {
-    uint4 r;
-    uint32_t w[4];
+  int cds = cu[dc], cde = cu[dc + 1], cP = plen[dc];
+  int dl = dc, lds_ = cds, lde = cde, lP = cP;
+  // position in the block at the step before the first valid one, stepped
+  // after (blocks start at the prompt end; prompts are whole blocks)
+  int inb = 0;
+  {
+    const int tp1 = max(t0, 0) - cds;
+    if (tp1 > cP) inb = (tp1 - 1 - cP) % a.B;
+  }
+
+  Raw rx[U], rn[U];
+  float hx[U][N], hn[U][N];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
-    r.x = w[0]; r.y = w[1]; r.z = w[2]; r.w = w[3];
-    *reinterpret_cast<uint4 *>(p) = r;
+  for (int j = 0; j < U; ++j)
+#pragma unroll
+    for (int c = 0; c < N; ++c) hx[j][c] = hn[j][c] = 0.f;
+  auto issue = [&](int slot, int t) {
+    const int tc = min(max(t, 0), T - 1);
+    while (tc >= lde && dl + 1 < a.num_docs) {
+      ++dl;
+      lds_ = cu[dl];
+      lde = cu[dl + 1];
+      lP = plen[dl];
+    }
+    const bool resp = t >= 0 && t < T && tc - lds_ >= lP;
+    const int64_t o = (int64_t)tc * C;
+    rx[slot] = at(x + o);
+    rn[slot] = at((resp ? xn : x) + o);
+  };
+#pragma unroll
+  for (int j = 0; j < U - 1; ++j) issue(j, t0 + j);
+
+  for (int s0 = 0; s0 < nsteps; s0 += U) {
+    for_each_slot(std::make_integer_sequence<int, U>{}, [&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      const int t = t0 + s0 + J;
+      S::cvt(rx[J], hx[J]);
+      S::cvt(rn[J], hn[J]);
+      issue((J + U - 1) % U, t + U - 1);
+      const bool valid = t >= 0;  // t < te <= T always
+      if (valid) {
+        while (t >= cde && dc + 1 < a.num_docs) {
+          ++dc;
+          cds = cu[dc];
+          cde = cu[dc + 1];
+          cP = plen[dc];
+        }
+      }
+      const int tp = t - cds;
+      const bool resp = valid && tp >= cP;
+      if (resp) inb = tp == cP || inb + 1 == a.B ? 0 : inb + 1;
+      // taps L < nb read inside the document (earlier ones read zero), taps
+      // L < na inside the block (the noisy input)
+      const int nb = valid ? min(tp + 1, W) : 0;
+      const int na = resp ? min(inb + 1, W) : 0;
+      float yc[N], ynv[N];
+#pragma unroll
+      for (int c = 0; c < N; ++c) yc[c] = ynv[c] = bias[c];
+#pragma unroll
+      for (int L = 0; L < W; ++L) {
+        const int r = (J - L + U * W) % U;
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+          const float hxu = L < nb ? hx[r][c] : 0.f;
+          yc[c] = fmaf(wl[L][c], hxu, yc[c]);
+          ynv[c] = fmaf(wl[L][c], L < na ? hn[r][c] : hxu, ynv[c]);
+        }
+      }
+      if (ACT) {
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+          yc[c] = yc[c] / (1.f + __expf(-yc[c]));
+          ynv[c] = ynv[c] / (1.f + __expf(-ynv[c]));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < N; ++c) ynv[c] = resp ? ynv[c] : 0.f;  // noisy prompt rows are zero
+      const int64_t m = (int64_t)max(t, tb) * C;
+      S::store(reinterpret_cast<IO *>(reinterpret_cast<char *>(y + m) + lo), yc);
+      S::store(reinterpret_cast<IO *>(reinterpret_cast<char *>(yn + m) + lo), ynv);
+    });
   }
-};
-template <> struct ConvVec<float> {
-  static constexpr int N = 4;
-  static __device__ __forceinline__ void load(const float *p, float *f) {
-    const float4 r = *reinterpret_cast<const float4 *>(p);
-    f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
-  }
-  static __device__ __forceinline__ void store(float *p, const float *f) {
-    *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
-  }
-};
+}
+
+template <typename IO, int W>
+static hipError_t launch_fwd_w(const ShortConvArgs &a, hipStream_t st) {
+  constexpr int N = FwdCfg<IO, W>::N;
+  // token blocks on x (no 65535 limit there), channel groups on y
+  const dim3 grid((unsigned)((a.T + kConvWaves * kConvRun - 1) / (kConvWaves * kConvRun)),
+                  (unsigned)((a.C + 64 * N - 1) / (64 * N)));
+  if (grid.y > 65535u) return hipErrorInvalidValue;
+  const IO *x = reinterpret_cast<const IO *>(a.x), *xn = reinterpret_cast<const IO *>(a.xn);
+  IO *y = reinterpret_cast<IO *>(a.y), *yn = reinterpret_cast<IO *>(a.yn);
+  if (a.activation == 1)
+    hipLaunchKernelGGL((shortconv_dual_kernel<IO, W, true>), grid, dim3(256), 0, st, a, a.cu, a.plen, x, xn, y, yn);
+  else
+    hipLaunchKernelGGL((shortconv_dual_kernel<IO, W, false>), grid, dim3(256), 0, st, a, a.cu, a.plen, x, xn, y, yn);
+  return hipGetLastError();
+}
 
 template <typename IO>
-__global__ __launch_bounds__(kConvThreads) void shortconv_dual_kernel(ShortConvArgs a) {
-  using V = ConvVec<IO>;
-  constexpr int N = V::N;
-  const int64_t c0 = ((int64_t)blockIdx.x * kConvThreads + threadIdx.x) * N;
-  if (c0 >= a.C) return;
-  const int64_t t_begin = (int64_t)blockIdx.y * kConvRun;
-  const int64_t t_end = min(t_begin + kConvRun, a.T);
-  const int W = a.W;
-  const IO *x = reinterpret_cast<const IO *>(a.x);
-  const IO *xn = reinterpret_cast<const IO *>(a.xn);
-  IO *y = reinterpret_cast<IO *>(a.y);
-  IO *yn = reinterpret_cast<IO *>(a.yn);
-
-  // weights by lag: wl[L][c] multiplies x[t - L]; lags >= W are zero
-  float wl[kConvWMax][N];
-#pragma unroll
-  for (int L = 0; L < kConvWMax; ++L)
-#pragma unroll
-    for (int c = 0; c < N; ++c) wl[L][c] = L < W ? a.w[(c0 + c) * W + (W - 1 - L)] : 0.f;
-  float bias[N];
-#pragma unroll
-  for (int c = 0; c < N; ++c) bias[c] = a.bias ? a.bias[c0 + c] : 0.f;
-
-  // start W-1 tokens early to fill the history window
-  const int64_t ts = max((int64_t)0, t_begin - (W - 1));
-  // document containing ts (binary search over cu_seqlens)
-  int lo = 0, hi = a.num_docs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.cu[mid] <= ts) lo = mid; else hi = mid - 1;
-  }
-  int doc = lo;
-  int64_t ds = a.cu[doc], de = a.cu[doc + 1];
-  int64_t P = a.plen[doc];
-
-  float hx[kConvWMax][N], hn[kConvWMax][N];
-#pragma unroll
-  for (int L = 0; L < kConvWMax; ++L)
-#pragma unroll
-    for (int c = 0; c < N; ++c) hx[L][c] = hn[L][c] = 0.f;
-
-  for (int64_t t = ts; t < t_end; ++t) {
-    while (t >= de) {  // next document: reset the history (taps before its start read 0)
-      ++doc;
-      ds = a.cu[doc];
-      de = a.cu[doc + 1];
-      P = a.plen[doc];
-#pragma unroll
-      for (int L = 0; L < kConvWMax; ++L)
-#pragma unroll
-        for (int c = 0; c < N; ++c) hx[L][c] = hn[L][c] = 0.f;
-    }
-    if (t == ds) {
-#pragma unroll
-      for (int L = 0; L < kConvWMax; ++L)
-#pragma unroll
-        for (int c = 0; c < N; ++c) hx[L][c] = hn[L][c] = 0.f;
-    }
-    const int64_t tp = t - ds;  // position inside the document
-    const bool resp = tp >= P;
-#pragma unroll
-    for (int L = kConvWMax - 1; L > 0; --L)
-#pragma unroll
-      for (int c = 0; c < N; ++c) {
-        hx[L][c] = hx[L - 1][c];
-        hn[L][c] = hn[L - 1][c];
-      }
-    V::load(x + t * a.C + c0, hx[0]);
-    if (resp) V::load(xn + t * a.C + c0, hn[0]);
-    else {
-#pragma unroll
-      for (int c = 0; c < N; ++c) hn[0][c] = 0.f;
-    }
-    if (t < t_begin) continue;
-    float yc[N], ynv[N];
-#pragma unroll
-    for (int c = 0; c < N; ++c) yc[c] = bias[c];
-#pragma unroll
-    for (int L = 0; L < kConvWMax; ++L)
-#pragma unroll
-      for (int c = 0; c < N; ++c) yc[c] += wl[L][c] * hx[L][c];
-    if (resp) {
-      // taps at lag L <= tp - blk lie inside the block and read the noisy input
-      const int64_t blk = P + ((tp - P) / a.B) * a.B;
-      const int64_t inside = tp - blk;
-#pragma unroll
-      for (int c = 0; c < N; ++c) ynv[c] = bias[c];
-#pragma unroll
-      for (int L = 0; L < kConvWMax; ++L) {
-        const bool noisy = L <= inside;
-#pragma unroll
-        for (int c = 0; c < N; ++c) ynv[c] += wl[L][c] * (noisy ? hn[L][c] : hx[L][c]);
-      }
-    }
-    if (a.activation == 1) {
-#pragma unroll
-      for (int c = 0; c < N; ++c) {
-        yc[c] = yc[c] / (1.f + __expf(-yc[c]));
-        ynv[c] = ynv[c] / (1.f + __expf(-ynv[c]));
-      }
-    }
-    if (!resp) {
-#pragma unroll
-      for (int c = 0; c < N; ++c) ynv[c] = 0.f;
-    }
-    V::store(y + t * a.C + c0, yc);
-    V::store(yn + t * a.C + c0, ynv);
+static hipError_t launch_fwd_io(const ShortConvArgs &a, hipStream_t st) {
+  switch (a.W) {
+    case 1: return launch_fwd_w<IO, 1>(a, st);
+    case 2: return launch_fwd_w<IO, 2>(a, st);
+    case 3: return launch_fwd_w<IO, 3>(a, st);
+    case 4: return launch_fwd_w<IO, 4>(a, st);
+    case 5: return launch_fwd_w<IO, 5>(a, st);
+    case 6: return launch_fwd_w<IO, 6>(a, st);
+    case 7: return launch_fwd_w<IO, 7>(a, st);
+    case 8: return launch_fwd_w<IO, 8>(a, st);
+    default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_shortconv(const ShortConvArgs &a, hipStream_t st) {
-  if (a.T == 0) return hipSuccess;
-  const int N = a.bf16 ? 8 : 4;
-  const int64_t vecs = a.C / N;
-  const dim3 grid((unsigned)((vecs + kConvThreads - 1) / kConvThreads),
-                  (unsigned)((a.T + kConvRun - 1) / kConvRun));
+  if (a.T == 0 || a.C <= 0) return hipSuccess;
   TimedLaunch tl(K_SHORTCONV, st);
-  if (a.bf16)
-    hipLaunchKernelGGL(shortconv_dual_kernel<u16>, grid, dim3(kConvThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(shortconv_dual_kernel<float>, grid, dim3(kConvThreads), 0, st, a);
-  return hipGetLastError();
+  return a.bf16 ? launch_fwd_io<u16>(a, st) : launch_fwd_io<float>(a, st);
 }
 
 }  // namespace flare

@@ -102,11 +102,13 @@ def test_block_step_sizes(g, dev, B, d, io):
 
 # ------------------------------------------------------------------ ShortConv
 
-def test_shortconv_position_tags_exact(g, dev):
+@pytest.mark.parametrize("W", [1, 2, 4, 5, 8])
+def test_shortconv_position_tags_exact(g, dev, W):
     """fp32 x[t] = doc*1000 + t, x~ = -x - 1, one-hot weights: every tap's
-    source and position is read back exactly."""
+    source and position is read back exactly (documents across the 64-token
+    runs and 256-token blocks of the kernel, one shorter than the window)."""
     import torch
-    lens, prompts, B, W, C = [37, 8, 0, 51], [12, 0, 0, 4], 4, 4, 8
+    lens, prompts, B, C = [37, 8, 0, 51, 3, 230], [12, 0, 0, 4, 0, 100], 4, 8
     T = sum(lens)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     pos = np.concatenate([np.arange(L) + 1000 * i for i, L in enumerate(lens)]).astype(np.float32)
