@@ -378,6 +378,9 @@ def bench_serving(torch, g, wl, dev, timer, up, args):
             "alg_bytes": {"eval": ev_bytes, "commit": cm_bytes}}
 
 
+CONV_WORKLOAD = "packed conv 32768 tokens 8 docs 12288 ch W4 bf16"
+
+
 def bench_conv(torch, g, wl, dev, timer, up, args):
     log("bench: packed ShortConv (32768 tokens, 8 docs, 12288 channels, W=4)")
     p = wl.packed_conv(round_io=False)
@@ -398,7 +401,8 @@ def bench_conv(torch, g, wl, dev, timer, up, args):
     alg = 2 * C * (T + n_resp + 2 * T)  # read x (all), xn (response), write y, yn
     fwd = {"workload": "dual ShortConv, 1 packed row of 32768 tokens, 8 docs, 3x32x128 channels, W=4, bf16",
            "ms": ms, "gbs": alg / (ms * 1e-3) / 1e9, "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-           "alg_bytes": alg, "tokens_per_s": T / (ms * 1e-3), "bound": "hbm"}
+           "alg_bytes": alg, "tokens_per_s": T / (ms * 1e-3), "bound": "hbm",
+           "traffic": traffic_for("shortconv_dual_kernel", CONV_WORKLOAD)}
     # ---- reverse mode on the same inputs; output gradients ~ N(0, 1) drawn on
     # the device from a seeded generator
     gen = torch.Generator(device=dev)
@@ -426,7 +430,8 @@ def bench_conv(torch, g, wl, dev, timer, up, args):
     balg = 2 * C * (4 * T + 2 * n_resp)
     bwd_d = {"workload": "dual ShortConv reverse mode, same row and shape, bf16 (dx, dx~, dweight, dbias)",
              "ms": bms, "gbs": balg / (bms * 1e-3) / 1e9, "hbm_frac": balg / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-             "alg_bytes": balg, "tokens_per_s": T / (bms * 1e-3), "bound": "hbm"}
+             "alg_bytes": balg, "tokens_per_s": T / (bms * 1e-3), "bound": "hbm",
+             "traffic": traffic_for("shortconv_dual_bwd_kernel", CONV_WORKLOAD)}
     return fwd, bwd_d
 
 

@@ -32,7 +32,7 @@
 // of loads stay in flight.  The per-lag weight-gradient partials of the four
 // runs are summed in LDS in a fixed order and written to a workspace
 // [256-token block][C][W + 1] (taps, then bias); a second kernel sums them
-// over the blocks in order, so the result is run-to-run identical.  Streaming:
+// over the blocks in a fixed order, so the result is run-to-run identical.  Streaming:
 // bound by HBM bandwidth.
 #include "conv_common.h"
 #include "device_common.h"
@@ -256,16 +256,35 @@ __global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(
   for (int e = threadIdx.x; e < nel; e += 256) dst[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
 }
 
-// dweight[c][j] and dbias[c]: the block partials summed in block order
+// dweight[c][j] and dbias[c]: the block partials summed in a fixed order.
+// A workgroup owns 64 consecutive outputs; wave w sums the blocks r = w mod 4
+// (eight loads in flight per lane), then the four sums are added in wave order.
 __global__ __launch_bounds__(256) void shortconv_bwd_reduce_kernel(ShortConvBwdArgs a, int blocks) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float sums[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int W1 = a.W + 1;
-  if (i >= (int64_t)a.C * W1) return;
+  const int64_t n = (int64_t)a.C * W1;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t ic = min(i, n - 1);
+  const size_t stride = (size_t)n;
   float s = 0.f;
-  for (int r = 0; r < blocks; ++r) s += a.part[(size_t)r * a.C * W1 + i];
-  const int64_t c = i / W1, j = i % W1;
-  if (j < a.W) a.dw[c * a.W + j] = s;
-  else if (a.dbias) a.dbias[c] = s;
+  int r = wave;
+  for (; r + 28 < blocks; r += 32) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = a.part[(size_t)(r + 4 * k) * stride + ic];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+  for (; r < blocks; r += 4) s += a.part[(size_t)r * stride + ic];
+  sums[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && i < n) {
+    const float t = ((sums[0][lane] + sums[1][lane]) + sums[2][lane]) + sums[3][lane];
+    const int64_t c = i / W1, j = i % W1;
+    if (j < a.W) a.dw[c * a.W + j] = t;
+    else if (a.dbias) a.dbias[c] = t;
+  }
 }
 
 template <typename IO, int W>
@@ -311,8 +330,7 @@ hipError_t launch_shortconv_bwd(const ShortConvBwdArgs &a, hipStream_t st) {
   }
   // with no tokens (blocks = 0) this writes the zero sums
   const int64_t outs = (int64_t)a.C * (a.W + 1);
-  hipLaunchKernelGGL(shortconv_bwd_reduce_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st, a,
-                     blocks);
+  hipLaunchKernelGGL(shortconv_bwd_reduce_kernel, dim3((unsigned)((outs + 63) / 64)), dim3(256), 0, st, a, blocks);
   return hipGetLastError();
 }
 
