@@ -160,7 +160,7 @@ __device__ __forceinline__ void chunk_grams(IO (*x)[32][LDX], float (*cc)[32][LD
                                             const float *beta, const float *lgn, const float *betan, int c0,
                                             int n, int P, int B, bool has_noisy, bool fold_w) {
   constexpr int XL = BF ? RowU16 : RowF32;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
   if (wave == 0) {
 #pragma unroll

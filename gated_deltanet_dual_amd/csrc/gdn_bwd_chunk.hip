@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   constexpr int C = kC, D = kD, NT = kNT, LDX = kLDX, LDP = kLDP, LDG = kLDG, LDQ = kLDQ;
   __shared__ Chunk2Smem sm;
   const FwdArgs &f = a.f;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
   const int H = f.H;
   const int slot = blockIdx.x / H, h = blockIdx.x % H;

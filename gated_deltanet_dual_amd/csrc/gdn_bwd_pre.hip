@@ -45,7 +45,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
   constexpr int C = pC, D = pD, NT = pNT, LDM = pLDM;
   __shared__ PreSmem sm;
   const FwdArgs &f = a.f;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
   const int H = f.H;
   const int slot = blockIdx.x / H, h = blockIdx.x % H;

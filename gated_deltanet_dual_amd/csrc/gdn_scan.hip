@@ -66,7 +66,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   using ScanRing = ScanRing<ZRHS>;
   constexpr int C = sC, D = sD;
   __shared__ ScanSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
 
   // ---- workgroup -> (document, head, quarter); the quarters of a pair share an XCD

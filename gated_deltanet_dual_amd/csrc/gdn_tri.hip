@@ -31,7 +31,7 @@ __global__ __launch_bounds__(tNT) void gdn_tri_d128_kernel(BwdArgs a) {
   constexpr int C = tC, D = tD, NT = tNT, LDX = tLDX, LDM = tLDM;
   __shared__ TriSmem sm;
   const FwdArgs &f = a.f;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = f.H;
   const int slot = blockIdx.x / H, h = blockIdx.x % H;
   int doc, c;
