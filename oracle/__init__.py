@@ -19,6 +19,11 @@ What each entry computes, with its source:
 * ``shortconv_dual`` -- the dual-source causal ShortConv, Key designs item 3.
 * ``shortconv_dual_bwd`` -- its reverse mode (parity pinned by finite
   differences and the adjoint identity in the CPU tests).
+* ``qkv_prologue`` / ``qkv_prologue_bwd`` -- the GDN layer's input prologue:
+  the ShortConv above on each of the q, k, v projections of both streams,
+  optionally SiLU, then (a reading: the pages do not mention it) q and k
+  divided per (token, head) by sqrt(sum x^2 + 1e-6); and its reverse mode.
+  Plain numpy around the C ShortConv.
 
 Parity pins (closed forms, brute force, invariants, finite differences and a
 hand-worked example) are in the CPU tests; see ``tests/test_oracle_*.py``.
@@ -204,3 +209,61 @@ def shortconv_dual_bwd(cu_seqlens, prompt_lens, block_size, x, xn, weight, dy, d
                                            int(threads))
     _check(rc, "shortconv_dual_bwd")
     return dx, dxn, dw, db
+
+
+L2_EPS = 1e-6
+
+
+def _l2_heads(y, d):
+    """Divide every (token, head) row of d values by sqrt(sum y^2 + eps)."""
+    T = y.shape[0]
+    r = y.reshape(T, -1, d)
+    n = np.sqrt(np.sum(r * r, axis=2, keepdims=True) + L2_EPS)
+    return (r / n).reshape(y.shape)
+
+
+def _l2_heads_bwd(y, dyhat, d):
+    """Gradient w.r.t. y of sum(dyhat * y / n), n = sqrt(|y|^2 + eps) per row:
+    dyhat / n - y (y . dyhat) / n^3."""
+    T = y.shape[0]
+    r = y.reshape(T, -1, d)
+    g = dyhat.reshape(T, -1, d)
+    n = np.sqrt(np.sum(r * r, axis=2, keepdims=True) + L2_EPS)
+    dot = np.sum(r * g, axis=2, keepdims=True)
+    return (g / n - r * dot / n ** 3).reshape(y.shape)
+
+
+def qkv_prologue(cu_seqlens, prompt_lens, block_size, head_dim, xs, xns, weights, activation=0, l2=True,
+                 threads=0):
+    """ShortConv -> optional SiLU -> per-head L2 norm of q and k.
+    xs, xns: the clean and noisy (q, k, v) projections, each [T, H*head_dim];
+    weights: their conv weights, each [H*head_dim, W].  Returns (ys, yns), the
+    GDN-ready (q, k, v) of both streams (noisy prompt rows 0)."""
+    ys, yns = [], []
+    for sec in range(3):
+        y, yn = shortconv_dual(cu_seqlens, prompt_lens, block_size, xs[sec], xns[sec], weights[sec],
+                               activation=activation, threads=threads)
+        if l2 and sec < 2:
+            y, yn = _l2_heads(y, head_dim), _l2_heads(yn, head_dim)
+        ys.append(y)
+        yns.append(yn)
+    return ys, yns
+
+
+def qkv_prologue_bwd(cu_seqlens, prompt_lens, block_size, head_dim, xs, xns, weights, dys, dyns,
+                     activation=0, l2=True, threads=0):
+    """Reverse mode of qkv_prologue: dys, dyns are the gradients of its
+    outputs (noisy prompt rows ignored).  Returns (dxs, dxns, dws)."""
+    dxs, dxns, dws = [], [], []
+    for sec in range(3):
+        dy, dyn = _f64(dys[sec]), _f64(dyns[sec])
+        if l2 and sec < 2:
+            y, yn = shortconv_dual(cu_seqlens, prompt_lens, block_size, xs[sec], xns[sec], weights[sec],
+                                   activation=activation, threads=threads)
+            dy, dyn = _l2_heads_bwd(y, dy, head_dim), _l2_heads_bwd(yn, dyn, head_dim)
+        dx, dxn, dw, _ = shortconv_dual_bwd(cu_seqlens, prompt_lens, block_size, xs[sec], xns[sec],
+                                            weights[sec], dy, dyn, activation=activation, threads=threads)
+        dxs.append(dx)
+        dxns.append(dxn)
+        dws.append(dw)
+    return dxs, dxns, dws
