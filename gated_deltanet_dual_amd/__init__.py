@@ -17,7 +17,8 @@ import os
 import numpy as np
 
 __all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_bwd",
-           "block_step", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
+           "block_step", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
+           "qkv_prologue_bwd", "qkv_prologue_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
            "QK_L2NORM", "F32", "BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,14 @@ def lib():
     L.flare_shortconv_dual_bwd_workspace_size.restype = SZ
     L.flare_shortconv_dual_bwd.argtypes = [VP, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, P, P, P, SZ, P]
     L.flare_shortconv_dual_bwd.restype = ctypes.c_int
+    A3 = ctypes.c_void_p * 3
+    L.flare_qkv_prologue.argtypes = [VP, I32, I32, I32, I32, I32, A3, A3, A3, I32, I32, A3, A3, P]
+    L.flare_qkv_prologue.restype = ctypes.c_int
+    L.flare_qkv_prologue_bwd_workspace_size.argtypes = [VP, I32, I32, I32, I32]
+    L.flare_qkv_prologue_bwd_workspace_size.restype = SZ
+    L.flare_qkv_prologue_bwd.argtypes = [VP, I32, I32, I32, I32, I32, A3, A3, A3, I32, I32, A3, A3, A3, A3, A3,
+                                         P, SZ, P]
+    L.flare_qkv_prologue_bwd.restype = ctypes.c_int
     L.flare_timing_enable.argtypes = [I32]
     L.flare_timing_enable.restype = I32
     L.flare_timing_avg_ms.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64)]
@@ -306,6 +315,57 @@ def shortconv_dual_bwd(varlen: Varlen, block_size, x, xn, weight, dy, dyn, bias=
                                           _ptr(dx), _ptr(dxn), _ptr(dw), _ptr(db), _ptr(workspace), nbytes,
                                           _stream(x.device)))
     return dx, dxn, dw, db
+
+
+def _a3(ts):
+    return (ctypes.c_void_p * 3)(*[_ptr(t) for t in ts])
+
+
+def qkv_prologue(varlen: Varlen, block_size, head_dim, xs, xns, weights, activation=0, qk_l2norm=True, out=None):
+    """The GDN layer's fused input prologue: ShortConv on the clean and noisy
+    q, k, v projections (xs, xns: three [T, H*head_dim] io tensors each;
+    weights: three [H*head_dim, W] fp32), optional SiLU, per-head L2 norm of
+    q and k.  Returns (ys, yns), lists of three tensors shaped like xs."""
+    torch = _torch()
+    T, C = xs[0].shape
+    W = weights[0].shape[1]
+    if out is None:
+        ys, yns = [torch.empty_like(x) for x in xs], [torch.empty_like(x) for x in xs]
+    else:
+        ys, yns = out
+    _check(lib().flare_qkv_prologue(varlen.ref(), int(block_size), C // int(head_dim), int(head_dim), W,
+                                    _io_of(xs[0]), _a3(xs), _a3(xns), _a3(weights), int(activation),
+                                    1 if qk_l2norm else 0, _a3(ys), _a3(yns), _stream(xs[0].device)))
+    return ys, yns
+
+
+def qkv_prologue_bwd_workspace_bytes(varlen: Varlen, block_size, heads, head_dim, width) -> int:
+    """flare_qkv_prologue_bwd_workspace_size for this batch and shape."""
+    return int(lib().flare_qkv_prologue_bwd_workspace_size(varlen.ref(), int(block_size), int(heads),
+                                                           int(head_dim), int(width)))
+
+
+def qkv_prologue_bwd(varlen: Varlen, block_size, head_dim, xs, xns, weights, dys, dyns, activation=0,
+                     qk_l2norm=True, workspace=None, out=None):
+    """Reverse mode of qkv_prologue.  Returns (dxs, dxns, dws), lists of three."""
+    torch = _torch()
+    T, C = xs[0].shape
+    W = weights[0].shape[1]
+    H = C // int(head_dim)
+    if out is None:
+        dxs, dxns = [torch.empty_like(x) for x in xs], [torch.empty_like(x) for x in xs]
+        dws = [torch.empty((C, W), dtype=torch.float32, device=xs[0].device) for _ in range(3)]
+    else:
+        dxs, dxns, dws = out
+    need = qkv_prologue_bwd_workspace_bytes(varlen, block_size, H, head_dim, W)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=xs[0].device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().flare_qkv_prologue_bwd(varlen.ref(), int(block_size), H, int(head_dim), W, _io_of(xs[0]),
+                                        _a3(xs), _a3(xns), _a3(weights), int(activation), 1 if qk_l2norm else 0,
+                                        _a3(dys), _a3(dyns), _a3(dxs), _a3(dxns), _a3(dws), _ptr(workspace),
+                                        nbytes, _stream(xs[0].device)))
+    return dxs, dxns, dws
 
 
 def workspace_bytes(varlen: Varlen, H: int, d: int, block_size: int, io: int, flags: int = 0,

@@ -187,10 +187,11 @@ flare_status flare_shortconv_dual(const flare_varlen *varlen, int32_t block_size
   a.W = width;
   a.activation = activation;
   a.bf16 = io_dtype == FLARE_BF16;
+  a.nsec = 1;
   a.T = vi.total_tokens;
   a.cu = varlen->cu_seqlens;
   a.plen = varlen->prompt_lens;
-  a.x = x; a.xn = xn; a.w = weight; a.bias = bias; a.y = y; a.yn = yn;
+  a.x[0] = x; a.xn[0] = xn; a.w[0] = weight; a.bias = bias; a.y[0] = y; a.yn[0] = yn;
   return hip_status(launch_shortconv(a, (hipStream_t)stream), "shortconv_dual launch");
 }
 
@@ -227,13 +228,95 @@ flare_status flare_shortconv_dual_bwd(const flare_varlen *varlen, int32_t block_
   a.W = width;
   a.activation = activation;
   a.bf16 = io_dtype == FLARE_BF16;
+  a.nsec = 1;
   a.T = vi.total_tokens;
   a.cu = varlen->cu_seqlens;
   a.plen = varlen->prompt_lens;
-  a.x = x; a.xn = xn; a.dy = dy; a.dyn = dyn; a.w = weight; a.bias = bias;
-  a.dx = dx; a.dxn = dxn; a.dw = dweight; a.dbias = dbias;
+  a.x[0] = x; a.xn[0] = xn; a.dy[0] = dy; a.dyn[0] = dyn; a.w[0] = weight; a.bias = bias;
+  a.dx[0] = dx; a.dxn[0] = dxn; a.dw[0] = dweight; a.dbias = dbias;
   a.part = reinterpret_cast<float *>(workspace);
   return hip_status(launch_shortconv_bwd(a, (hipStream_t)stream), "shortconv_dual_bwd launch");
+}
+
+flare_status flare_qkv_prologue(const flare_varlen *varlen, int32_t block_size, int32_t heads, int32_t head_dim,
+                                int32_t width, int32_t io_dtype, const void *const x[3], const void *const xn[3],
+                                const float *const weight[3], int32_t activation, int32_t qk_l2norm,
+                                void *const y[3], void *const yn[3], void *stream) {
+  clear_error();
+  VarlenInfo vi;
+  flare_status st = check_qkv_prologue(varlen, block_size, heads, head_dim, width, io_dtype, x, xn, weight,
+                                       activation, qk_l2norm, (const void *const *)y, (const void *const *)yn, &vi);
+  if (st != FLARE_OK) return st;
+  ShortConvArgs a{};
+  a.num_docs = varlen->num_docs;
+  a.B = block_size;
+  a.C = heads * head_dim;
+  a.W = width;
+  a.activation = activation;
+  a.bf16 = io_dtype == FLARE_BF16;
+  a.nsec = 3;
+  a.nnorm = qk_l2norm ? 2 : 0;
+  a.hd = head_dim;
+  a.T = vi.total_tokens;
+  a.cu = varlen->cu_seqlens;
+  a.plen = varlen->prompt_lens;
+  for (int s = 0; s < 3; ++s) {
+    a.x[s] = x[s]; a.xn[s] = xn[s]; a.w[s] = weight[s]; a.y[s] = y[s]; a.yn[s] = yn[s];
+  }
+  return hip_status(launch_shortconv(a, (hipStream_t)stream), "qkv_prologue launch");
+}
+
+size_t flare_qkv_prologue_bwd_workspace_size(const flare_varlen *varlen, int32_t block_size, int32_t heads,
+                                             int32_t head_dim, int32_t width) {
+  VarlenInfo vi;
+  if (check_varlen(varlen, block_size, &vi) != FLARE_OK || heads <= 0 || head_dim <= 0 || width < 1 || width > 8 ||
+      (int64_t)heads * head_dim > INT32_MAX)
+    return 0;
+  return shortconv_bwd_workspace_bytes(vi, heads * head_dim, width, 3);
+}
+
+flare_status flare_qkv_prologue_bwd(const flare_varlen *varlen, int32_t block_size, int32_t heads, int32_t head_dim,
+                                    int32_t width, int32_t io_dtype, const void *const x[3],
+                                    const void *const xn[3], const float *const weight[3], int32_t activation,
+                                    int32_t qk_l2norm, const void *const dy[3], const void *const dyn[3],
+                                    void *const dx[3], void *const dxn[3], float *const dweight[3], void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  clear_error();
+  VarlenInfo vi;
+  flare_status st = check_qkv_prologue(varlen, block_size, heads, head_dim, width, io_dtype, x, xn, weight,
+                                       activation, qk_l2norm, (const void *const *)dx, (const void *const *)dxn, &vi);
+  if (st != FLARE_OK) return st;
+  if (!dy || !dyn || !dweight) return fail(FLARE_ERR_NULL, "qkv_prologue_bwd: a pointer array is NULL");
+  for (int s = 0; s < 3; ++s) {
+    if (!dweight[s]) return fail(FLARE_ERR_NULL, "qkv_prologue_bwd: dweight[%d] is NULL", s);
+    if (vi.total_tokens > 0 && (!dy[s] || !dyn[s]))
+      return fail(FLARE_ERR_NULL, "qkv_prologue_bwd: dy[%d] or dyn[%d] is NULL", s, s);
+  }
+  const int C = heads * head_dim;
+  const size_t need = shortconv_bwd_workspace_bytes(vi, C, width, 3);
+  if (vi.total_tokens > 0 && (!workspace || workspace_bytes < need))
+    return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  ShortConvBwdArgs a{};
+  a.num_docs = varlen->num_docs;
+  a.B = block_size;
+  a.C = C;
+  a.W = width;
+  a.activation = activation;
+  a.bf16 = io_dtype == FLARE_BF16;
+  a.nsec = 3;
+  a.nnorm = qk_l2norm ? 2 : 0;
+  a.hd = head_dim;
+  a.T = vi.total_tokens;
+  a.cu = varlen->cu_seqlens;
+  a.plen = varlen->prompt_lens;
+  for (int s = 0; s < 3; ++s) {
+    a.x[s] = x[s]; a.xn[s] = xn[s]; a.dy[s] = dy[s]; a.dyn[s] = dyn[s]; a.w[s] = weight[s];
+    a.dx[s] = dx[s]; a.dxn[s] = dxn[s]; a.dw[s] = dweight[s];
+  }
+  a.part = reinterpret_cast<float *>(workspace);
+  return hip_status(launch_shortconv_bwd(a, (hipStream_t)stream), "qkv_prologue_bwd launch");
 }
 
 }  // extern "C"

@@ -51,6 +51,33 @@ template <> struct Slice<float, 1> {
   static __device__ __forceinline__ void store(float *p, const float *f) { *p = f[0]; }
 };
 
+// Sum of x over aligned groups of G consecutive lanes (G a power of two, at
+// most 64, wave-uniform); every lane of a group gets its group's total.  xor 1
+// and xor 2 inside quads, then mirrored quads (8), mirrored half-rows (16), and
+// the permlane swaps across rows (32, 64).  The steps past G are switched off
+// by 0/1 factors (GroupSum::f, formed once) rather than by branches, so a loop
+// that calls it holds six scalars instead of a mask per call.
+// Each step adds the partner lane's value in an order both lanes share, so all
+// lanes of a group hold the same bits.
+struct GroupSum {
+  float f[6], g4, g5;  // f: step on (1) or off (0); g4, g5 = 1 - f[4], 1 - f[5]
+  __device__ __forceinline__ explicit GroupSum(int G) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) f[i] = G >= (2 << i) ? 1.f : 0.f;
+    g4 = 1.f - f[4];
+    g5 = 1.f - f[5];
+  }
+  __device__ __forceinline__ float operator()(float x) const {
+    x = fmaf(f[0], dpp_f32<0xB1>(x), x);   // quad_perm [1,0,3,2]
+    x = fmaf(f[1], dpp_f32<0x4E>(x), x);   // quad_perm [2,3,0,1]
+    x = fmaf(f[2], dpp_f32<0x141>(x), x);  // row_half_mirror
+    x = fmaf(f[3], dpp_f32<0x140>(x), x);  // row_mirror
+    x = fmaf(f[4], xsum16(x), g4 * x);     // rows 2k + 2k+1 (even row's value first in both)
+    x = fmaf(f[5], xsum32(x), g5 * x);     // halves of the wave
+    return x;
+  }
+};
+
 // f(integral_constant<int, J>) for J = 0, 1, ... in order (static slot indices)
 template <typename F, int... J>
 __device__ __forceinline__ void for_each_slot(std::integer_sequence<int, J...>, F &&f) {

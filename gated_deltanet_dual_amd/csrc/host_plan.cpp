@@ -156,9 +156,32 @@ flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
   return FLARE_OK;
 }
 
-size_t shortconv_bwd_workspace_bytes(const VarlenInfo &vi, int32_t channels, int32_t width) {
-  const int64_t runs = (vi.total_tokens + kConvBwdRun - 1) / kConvBwdRun;
-  return (size_t)runs * channels * (width + 1) * sizeof(float) + 256;
+size_t shortconv_bwd_workspace_bytes(const VarlenInfo &vi, int32_t channels, int32_t width, int32_t sections) {
+  const int64_t blocks = (vi.total_tokens + kConvBwdRun - 1) / kConvBwdRun;
+  return (size_t)sections * blocks * channels * (width + 1) * sizeof(float) + 256;
+}
+
+flare_status check_qkv_prologue(const flare_varlen *v, int32_t block_size, int32_t heads, int32_t head_dim,
+                                int32_t width, int32_t io_dtype, const void *const x[3], const void *const xn[3],
+                                const float *const w[3], int32_t activation, int32_t qk_l2norm,
+                                const void *const y[3], const void *const yn[3], VarlenInfo *out) {
+  if (heads <= 0 || head_dim <= 0) return fail(FLARE_ERR_SHAPE, "heads and head_dim must be positive");
+  if ((int64_t)heads * head_dim > INT32_MAX) return fail(FLARE_ERR_SHAPE, "heads * head_dim too large");
+  if (qk_l2norm != 0 && qk_l2norm != 1) return fail(FLARE_ERR_UNSUPPORTED, "qk_l2norm %d unknown", qk_l2norm);
+  if (!x || !xn || !w || !y || !yn) return fail(FLARE_ERR_NULL, "qkv prologue: a pointer array is NULL");
+  for (int s = 0; s < 3; ++s) {
+    const flare_status st = check_shortconv(v, block_size, heads * head_dim, width, io_dtype, x[s], xn[s], w[s],
+                                            activation, y[s], yn[s], out);
+    if (st != FLARE_OK) return st;
+  }
+  if (qk_l2norm) {
+    const int n = conv_lane_channels(io_dtype, width);
+    const int g = head_dim / n;
+    if (head_dim % n != 0 || g > 64 || (g & (g - 1)) != 0)
+      return fail(FLARE_ERR_UNSUPPORTED, "qk_l2norm needs head_dim / %d to be a power of two <= 64 (head_dim %d)", n,
+                  head_dim);
+  }
+  return FLARE_OK;
 }
 
 flare_status check_shortconv(const flare_varlen *v, int32_t block_size, int32_t channels,

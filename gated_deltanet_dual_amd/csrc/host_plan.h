@@ -66,9 +66,25 @@ flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
                               const float *alpha, const float *beta, const void *o,
                               int32_t mode);
 
-// Bytes of ShortConv-backward workspace: the per-run partials of the weight
-// and bias gradients, ceil(T / 32) runs x channels x (width + 1) fp32.
-size_t shortconv_bwd_workspace_bytes(const VarlenInfo &vi, int32_t channels, int32_t width);
+// Bytes of ShortConv-backward workspace: per section, the per-block partials
+// of the weight and bias gradients, ceil(T / 256) blocks x channels x
+// (width + 1) fp32.
+size_t shortconv_bwd_workspace_bytes(const VarlenInfo &vi, int32_t channels, int32_t width, int32_t sections = 1);
+
+// Channels a lane of the ShortConv kernels holds (8 bytes of a row, 4 bytes
+// for widths above 4).
+inline int conv_lane_channels(int32_t io_dtype, int32_t width) {
+  return (width <= 4 ? 8 : 4) / (io_dtype == FLARE_BF16 ? 2 : 4);
+}
+
+// The QKV prologue: each of the three sections is a ShortConv over
+// heads * head_dim channels; with qk_l2norm the head rows of q and k are
+// normalised inside the kernel, which needs head_dim / conv_lane_channels to
+// be a power of two of at most 64 lanes.
+flare_status check_qkv_prologue(const flare_varlen *v, int32_t block_size, int32_t heads, int32_t head_dim,
+                                int32_t width, int32_t io_dtype, const void *const x[3], const void *const xn[3],
+                                const float *const w[3], int32_t activation, int32_t qk_l2norm,
+                                const void *const y[3], const void *const yn[3], VarlenInfo *out);
 
 flare_status check_shortconv(const flare_varlen *v, int32_t block_size, int32_t channels,
                              int32_t width, int32_t io_dtype, const void *x, const void *xn,

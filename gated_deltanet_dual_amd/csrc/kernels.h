@@ -17,26 +17,35 @@ struct BlockStepArgs {
 };
 hipError_t launch_block_step(const BlockStepArgs &a, hipStream_t st);
 
+// ShortConv over up to three sections of channels sharing one document
+// layout (the q, k, v projections of the GDN layer's input prologue; one
+// section for a plain ShortConv).  Each section is [T, C] with its own
+// tensors and weights; the first nnorm sections are L2-normalised after the
+// convolution (and activation) per group of hd consecutive channels (a head).
 struct ShortConvArgs {
   int num_docs, B, C, W, activation, bf16;
+  int nsec, nnorm, hd;
   int64_t T;
   const int32_t *cu, *plen;
-  const void *x, *xn;
-  const float *w, *bias;
-  void *y, *yn;
+  const void *x[3], *xn[3];
+  const float *w[3], *bias;  // bias: plain ShortConv (one section) only
+  void *y[3], *yn[3];
 };
 hipError_t launch_shortconv(const ShortConvArgs &a, hipStream_t st);
 
 // reverse mode of the ShortConv (shortconv_bwd.hip)
 struct ShortConvBwdArgs {
   int num_docs, B, C, W, activation, bf16;
+  int nsec, nnorm, hd;
   int64_t T;
   const int32_t *cu, *plen;
-  const void *x, *xn, *dy, *dyn;
-  const float *w, *bias;
-  void *dx, *dxn;
-  float *dw, *dbias;
-  float *part;  // workspace: [ceil(T / 32)][C][W + 1] run partials of dweight, dbias
+  const void *x[3], *xn[3], *dy[3], *dyn[3];
+  const float *w[3], *bias;
+  void *dx[3], *dxn[3];
+  float *dw[3], *dbias;
+  // workspace: per section [ceil(T / 256)][C][W + 1] block partials of
+  // dweight and dbias
+  float *part;
 };
 hipError_t launch_shortconv_bwd(const ShortConvBwdArgs &a, hipStream_t st);
 

@@ -30,6 +30,7 @@ namespace flare {
 
 using conv::Slice;
 using conv::for_each_slot;
+using conv::GroupSum;
 
 namespace {
 
@@ -43,11 +44,11 @@ template <typename IO, int W> struct FwdCfg {
 
 }  // namespace
 
-template <typename IO, int W, bool ACT>
+// NRM: the section's outputs are L2-normalised per group of a.hd channels
+// (sections sec0 + blockIdx.z, all with or all without the normalisation)
+template <typename IO, int W, bool ACT, bool NRM>
 __global__ __launch_bounds__(256) void shortconv_dual_kernel(ShortConvArgs a, const int32_t *__restrict__ cu,
-                                                             const int32_t *__restrict__ plen,
-                                                             const IO *__restrict__ x, const IO *__restrict__ xn,
-                                                             IO *__restrict__ y, IO *__restrict__ yn) {
+                                                             const int32_t *__restrict__ plen, int sec0) {
   using Cfg = FwdCfg<IO, W>;
   constexpr int N = Cfg::N, U = Cfg::U;
   using S = Slice<IO, N>;
@@ -56,12 +57,20 @@ __global__ __launch_bounds__(256) void shortconv_dual_kernel(ShortConvArgs a, co
   // the wave index through readfirstlane: the run, its documents and the
   // per-step tap masks are then uniform (scalar registers)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sec = sec0 + (int)blockIdx.z;
+  const IO *const x = reinterpret_cast<const IO *>(a.x[sec]), *const xn = reinterpret_cast<const IO *>(a.xn[sec]);
+  IO *const y = reinterpret_cast<IO *>(a.y[sec]), *const yn = reinterpret_cast<IO *>(a.yn[sec]);
+  const float *const wsec = a.w[sec];
   const int64_t C = a.C;
   const int T = (int)a.T;
   const int64_t cb = (int64_t)blockIdx.y * 64 * N;
-  // lanes past the last channel repeat the last slice (duplicate stores of
-  // identical values)
-  const int64_t cl = min(cb + (int64_t)lane * N, C - N);
+  // lanes past the last channel repeat the matching lanes of the last group
+  // (head) of channels: same inputs, same results, duplicate stores of
+  // identical values, and group sums that never mix live and repeated lanes
+  const int64_t grp = NRM ? a.hd : N;
+  const int64_t c0 = cb + (int64_t)lane * N;
+  const int64_t cl = c0 < C ? c0 : C - grp + c0 % grp;
+  const GroupSum group_sum((int)(grp / N));  // sums over the lanes of a group
   const uint32_t lo = (uint32_t)(cl * (int64_t)sizeof(IO));
   const int tb = (int)blockIdx.x * (kConvWaves * kConvRun) + wave * kConvRun;
   const int te = min(tb + kConvRun, T);
@@ -73,7 +82,7 @@ __global__ __launch_bounds__(256) void shortconv_dual_kernel(ShortConvArgs a, co
 #pragma unroll
   for (int L = 0; L < W; ++L)
 #pragma unroll
-    for (int c = 0; c < N; ++c) wl[L][c] = a.w[(cl + c) * W + (W - 1 - L)];
+    for (int c = 0; c < N; ++c) wl[L][c] = wsec[(cl + c) * W + (W - 1 - L)];
 #pragma unroll
   for (int c = 0; c < N; ++c) bias[c] = a.bias ? a.bias[cl + c] : 0.f;
 
@@ -168,6 +177,21 @@ __global__ __launch_bounds__(256) void shortconv_dual_kernel(ShortConvArgs a, co
       }
 #pragma unroll
       for (int c = 0; c < N; ++c) ynv[c] = resp ? ynv[c] : 0.f;  // noisy prompt rows are zero
+      if (NRM) {
+        // divide each head's row by sqrt(sum y^2 + 1e-6) (zero rows stay zero)
+        float ss = 0.f, ssn = 0.f;
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+          ss = fmaf(yc[c], yc[c], ss);
+          ssn = fmaf(ynv[c], ynv[c], ssn);
+        }
+        const float r = rsqrtf(group_sum(ss) + 1e-6f), rn = rsqrtf(group_sum(ssn) + 1e-6f);
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+          yc[c] *= r;
+          ynv[c] *= rn;
+        }
+      }
       const int64_t m = (int64_t)max(t, tb) * C;
       S::store(reinterpret_cast<IO *>(reinterpret_cast<char *>(y + m) + lo), yc);
       S::store(reinterpret_cast<IO *>(reinterpret_cast<char *>(yn + m) + lo), ynv);
@@ -175,20 +199,29 @@ __global__ __launch_bounds__(256) void shortconv_dual_kernel(ShortConvArgs a, co
   }
 }
 
+template <typename IO, int W, bool NRM>
+static hipError_t launch_fwd_wn(const ShortConvArgs &a, int sec0, int nsec, hipStream_t st) {
+  constexpr int N = FwdCfg<IO, W>::N;
+  // token blocks on x (no 65535 limit there), channel groups on y, sections on z
+  const dim3 grid((unsigned)((a.T + kConvWaves * kConvRun - 1) / (kConvWaves * kConvRun)),
+                  (unsigned)((a.C + 64 * N - 1) / (64 * N)), (unsigned)nsec);
+  if (grid.y > 65535u) return hipErrorInvalidValue;
+  if (a.activation == 1)
+    hipLaunchKernelGGL((shortconv_dual_kernel<IO, W, true, NRM>), grid, dim3(256), 0, st, a, a.cu, a.plen, sec0);
+  else
+    hipLaunchKernelGGL((shortconv_dual_kernel<IO, W, false, NRM>), grid, dim3(256), 0, st, a, a.cu, a.plen, sec0);
+  return hipGetLastError();
+}
+
 template <typename IO, int W>
 static hipError_t launch_fwd_w(const ShortConvArgs &a, hipStream_t st) {
-  constexpr int N = FwdCfg<IO, W>::N;
-  // token blocks on x (no 65535 limit there), channel groups on y
-  const dim3 grid((unsigned)((a.T + kConvWaves * kConvRun - 1) / (kConvWaves * kConvRun)),
-                  (unsigned)((a.C + 64 * N - 1) / (64 * N)));
-  if (grid.y > 65535u) return hipErrorInvalidValue;
-  const IO *x = reinterpret_cast<const IO *>(a.x), *xn = reinterpret_cast<const IO *>(a.xn);
-  IO *y = reinterpret_cast<IO *>(a.y), *yn = reinterpret_cast<IO *>(a.yn);
-  if (a.activation == 1)
-    hipLaunchKernelGGL((shortconv_dual_kernel<IO, W, true>), grid, dim3(256), 0, st, a, a.cu, a.plen, x, xn, y, yn);
-  else
-    hipLaunchKernelGGL((shortconv_dual_kernel<IO, W, false>), grid, dim3(256), 0, st, a, a.cu, a.plen, x, xn, y, yn);
-  return hipGetLastError();
+  // the normalised sections first, then the others
+  if (a.nnorm > 0) {
+    const hipError_t e = launch_fwd_wn<IO, W, true>(a, 0, a.nnorm, st);
+    if (e != hipSuccess) return e;
+  }
+  if (a.nsec > a.nnorm) return launch_fwd_wn<IO, W, false>(a, a.nnorm, a.nsec - a.nnorm, st);
+  return hipSuccess;
 }
 
 template <typename IO>

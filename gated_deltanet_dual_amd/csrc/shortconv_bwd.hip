@@ -44,6 +44,7 @@ namespace flare {
 
 using conv::Slice;
 using conv::for_each_slot;
+using conv::GroupSum;
 
 namespace {
 
@@ -64,11 +65,12 @@ template <typename IO, int W> struct BwdCfg {
 
 }  // namespace
 
-template <typename IO, int W, bool ACT>
-__global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(
-    ShortConvBwdArgs a, const int32_t *__restrict__ cu, const int32_t *__restrict__ plen,
-    const IO *__restrict__ x, const IO *__restrict__ xn, const IO *__restrict__ dy, const IO *__restrict__ dyn,
-    IO *__restrict__ dx, IO *__restrict__ dxn, float *__restrict__ part) {
+// NRM: the forward L2-normalised the section's outputs per group of a.hd
+// channels, so the incoming gradients are w.r.t. the normalised rows
+template <typename IO, int W, bool ACT, bool NRM>
+__global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(ShortConvBwdArgs a, const int32_t *__restrict__ cu,
+                                                                 const int32_t *__restrict__ plen, int sec0,
+                                                                 int64_t part_stride) {
   using Cfg = BwdCfg<IO, W>;
   constexpr int N = Cfg::N, U = Cfg::U;
   using S = Slice<IO, N>;
@@ -80,12 +82,23 @@ __global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(
   // and lives in scalar registers.  Positions are 32-bit (the entry point
   // checks T < 2^31).
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sec = sec0 + (int)blockIdx.z;
+  const IO *const x = reinterpret_cast<const IO *>(a.x[sec]), *const xn = reinterpret_cast<const IO *>(a.xn[sec]);
+  const IO *const dy = reinterpret_cast<const IO *>(a.dy[sec]);
+  const IO *const dyn = reinterpret_cast<const IO *>(a.dyn[sec]);
+  IO *const dx = reinterpret_cast<IO *>(a.dx[sec]), *const dxn = reinterpret_cast<IO *>(a.dxn[sec]);
+  const float *const wsec = a.w[sec];
+  float *const part = a.part + sec * part_stride;
   const int64_t C = a.C;
   const int T = (int)a.T;
   const int64_t cb = (int64_t)blockIdx.y * 64 * N;
-  // lanes past the last channel repeat the last slice: same inputs, same
-  // results, same addresses -- their stores are harmless duplicates
-  const int64_t cl = min(cb + (int64_t)lane * N, C - N);
+  // lanes past the last channel repeat the matching lanes of the last group
+  // (head) of channels: same inputs, same results, duplicate stores of
+  // identical values, group sums that never mix live and repeated lanes
+  const int64_t grp = NRM ? a.hd : N;
+  const int64_t c0 = cb + (int64_t)lane * N;
+  const int64_t cl = c0 < C ? c0 : C - grp + c0 % grp;
+  const GroupSum group_sum((int)(grp / N));  // sums over the lanes of a group
   const uint32_t lo = (uint32_t)(cl * (int64_t)sizeof(IO));  // byte offset in a row
   const int tb = (int)blockIdx.x * kConvBwdRun + wave * kBRun;
   const int te = min(tb + kBRun, T);
@@ -104,7 +117,7 @@ __global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(
 #pragma unroll
     for (int L = 0; L < W; ++L)
 #pragma unroll
-      for (int c = 0; c < N; ++c) wl[L][c] = a.w[(cl + c) * W + (W - 1 - L)];
+      for (int c = 0; c < N; ++c) wl[L][c] = wsec[(cl + c) * W + (W - 1 - L)];
 #pragma unroll
     for (int c = 0; c < N; ++c) bias[c] = ACT && a.bias ? a.bias[cl + c] : 0.f;
 
@@ -188,7 +201,8 @@ __global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(
         const int nb = grad ? min(tp + 1, W) : 0;
         const int na = grad && resp ? min(inb + 1, W) : 0;
         const bool own = grad && t < te;
-        if (ACT) {
+        if (ACT || NRM) {
+          // the forward's pre-activation sums of row t
           float z[N], zn[N];
 #pragma unroll
           for (int c = 0; c < N; ++c) z[c] = zn[c] = bias[c];
@@ -202,10 +216,32 @@ __global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(
               zn[c] = fmaf(wl[L][c], L < na ? hn[r][c] : hxu, zn[c]);
             }
           }
+          if (NRM) {
+            // through y / sqrt(|y|^2 + 1e-6) per head: dy = r dyhat - y r^3 (y . dyhat)
+            float yv[N], yvn[N], ss = 0.f, ssn = 0.f, dt = 0.f, dtn = 0.f;
 #pragma unroll
-          for (int c = 0; c < N; ++c) {
-            g[c] *= silu_grad(z[c]);
-            gn[c] *= silu_grad(zn[c]);
+            for (int c = 0; c < N; ++c) {
+              yv[c] = ACT ? z[c] / (1.f + __expf(-z[c])) : z[c];
+              yvn[c] = ACT ? zn[c] / (1.f + __expf(-zn[c])) : zn[c];
+              ss = fmaf(yv[c], yv[c], ss);
+              ssn = fmaf(yvn[c], yvn[c], ssn);
+              dt = fmaf(yv[c], g[c], dt);
+              dtn = fmaf(yvn[c], gn[c], dtn);
+            }
+            const float r = rsqrtf(group_sum(ss) + 1e-6f), rn = rsqrtf(group_sum(ssn) + 1e-6f);
+            const float k3 = r * r * r * group_sum(dt), k3n = rn * rn * rn * group_sum(dtn);
+#pragma unroll
+            for (int c = 0; c < N; ++c) {
+              g[c] = r * g[c] - yv[c] * k3;
+              gn[c] = rn * gn[c] - yvn[c] * k3n;
+            }
+          }
+          if (ACT) {
+#pragma unroll
+            for (int c = 0; c < N; ++c) {
+              g[c] *= silu_grad(z[c]);
+              gn[c] *= silu_grad(zn[c]);
+            }
           }
         }
         float gs[N];
@@ -259,8 +295,11 @@ __global__ __launch_bounds__(256) void shortconv_dual_bwd_kernel(
 // dweight[c][j] and dbias[c]: the block partials summed in a fixed order.
 // A workgroup owns 64 consecutive outputs; wave w sums the blocks r = w mod 4
 // (eight loads in flight per lane), then the four sums are added in wave order.
-__global__ __launch_bounds__(256) void shortconv_bwd_reduce_kernel(ShortConvBwdArgs a, int blocks) {
+__global__ __launch_bounds__(256) void shortconv_bwd_reduce_kernel(ShortConvBwdArgs a, int blocks,
+                                                                   int64_t part_stride) {
   __shared__ float sums[4][64];
+  const int sec = (int)blockIdx.y;
+  const float *const part = a.part + sec * part_stride;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int W1 = a.W + 1;
   const int64_t n = (int64_t)a.C * W1;
@@ -272,37 +311,46 @@ __global__ __launch_bounds__(256) void shortconv_bwd_reduce_kernel(ShortConvBwdA
   for (; r + 28 < blocks; r += 32) {
     float v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = a.part[(size_t)(r + 4 * k) * stride + ic];
+    for (int k = 0; k < 8; ++k) v[k] = part[(size_t)(r + 4 * k) * stride + ic];
 #pragma unroll
     for (int k = 0; k < 8; ++k) s += v[k];
   }
-  for (; r < blocks; r += 4) s += a.part[(size_t)r * stride + ic];
+  for (; r < blocks; r += 4) s += part[(size_t)r * stride + ic];
   sums[wave][lane] = s;
   __syncthreads();
   if (wave == 0 && i < n) {
     const float t = ((sums[0][lane] + sums[1][lane]) + sums[2][lane]) + sums[3][lane];
     const int64_t c = i / W1, j = i % W1;
-    if (j < a.W) a.dw[c * a.W + j] = t;
-    else if (a.dbias) a.dbias[c] = t;
+    if (j < a.W) a.dw[sec][c * a.W + j] = t;
+    else if (a.dbias) a.dbias[c] = t;  // one section only
   }
+}
+
+template <typename IO, int W, bool NRM>
+static hipError_t launch_bwd_wn(const ShortConvBwdArgs &a, int blocks, int64_t part_stride, int sec0, int nsec,
+                                hipStream_t st) {
+  constexpr int N = BwdCfg<IO, W>::N;
+  // token blocks on x (no 65535 limit there), channel groups on y, sections on z
+  const dim3 grid((unsigned)blocks, (unsigned)((a.C + 64 * N - 1) / (64 * N)), (unsigned)nsec);
+  if (grid.y > 65535u) return hipErrorInvalidValue;
+  if (a.activation == 1)
+    hipLaunchKernelGGL((shortconv_dual_bwd_kernel<IO, W, true, NRM>), grid, dim3(256), 0, st, a, a.cu, a.plen, sec0,
+                       part_stride);
+  else
+    hipLaunchKernelGGL((shortconv_dual_bwd_kernel<IO, W, false, NRM>), grid, dim3(256), 0, st, a, a.cu, a.plen,
+                       sec0, part_stride);
+  return hipGetLastError();
 }
 
 template <typename IO, int W>
 static hipError_t launch_bwd_w(const ShortConvBwdArgs &a, int blocks, hipStream_t st) {
-  constexpr int N = BwdCfg<IO, W>::N;
-  // token blocks on x (no 65535 limit there), channel groups on y
-  const dim3 grid((unsigned)blocks, (unsigned)((a.C + 64 * N - 1) / (64 * N)));
-  if (grid.y > 65535u) return hipErrorInvalidValue;
-  const IO *x = reinterpret_cast<const IO *>(a.x), *xn = reinterpret_cast<const IO *>(a.xn);
-  const IO *dy = reinterpret_cast<const IO *>(a.dy), *dyn = reinterpret_cast<const IO *>(a.dyn);
-  IO *dx = reinterpret_cast<IO *>(a.dx), *dxn = reinterpret_cast<IO *>(a.dxn);
-  if (a.activation == 1)
-    hipLaunchKernelGGL((shortconv_dual_bwd_kernel<IO, W, true>), grid, dim3(256), 0, st, a, a.cu, a.plen, x, xn,
-                       dy, dyn, dx, dxn, a.part);
-  else
-    hipLaunchKernelGGL((shortconv_dual_bwd_kernel<IO, W, false>), grid, dim3(256), 0, st, a, a.cu, a.plen, x, xn,
-                       dy, dyn, dx, dxn, a.part);
-  return hipGetLastError();
+  const int64_t part_stride = (int64_t)blocks * a.C * (W + 1);
+  if (a.nnorm > 0) {
+    const hipError_t e = launch_bwd_wn<IO, W, true>(a, blocks, part_stride, 0, a.nnorm, st);
+    if (e != hipSuccess) return e;
+  }
+  if (a.nsec > a.nnorm) return launch_bwd_wn<IO, W, false>(a, blocks, part_stride, a.nnorm, a.nsec - a.nnorm, st);
+  return hipSuccess;
 }
 
 template <typename IO>
@@ -330,7 +378,8 @@ hipError_t launch_shortconv_bwd(const ShortConvBwdArgs &a, hipStream_t st) {
   }
   // with no tokens (blocks = 0) this writes the zero sums
   const int64_t outs = (int64_t)a.C * (a.W + 1);
-  hipLaunchKernelGGL(shortconv_bwd_reduce_kernel, dim3((unsigned)((outs + 63) / 64)), dim3(256), 0, st, a, blocks);
+  hipLaunchKernelGGL(shortconv_bwd_reduce_kernel, dim3((unsigned)((outs + 63) / 64), (unsigned)a.nsec), dim3(256), 0,
+                     st, a, blocks, (int64_t)blocks * outs);
   return hipGetLastError();
 }
 

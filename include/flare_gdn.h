@@ -244,6 +244,58 @@ flare_status flare_shortconv_dual_bwd(const flare_varlen *varlen,
                                       void *workspace, size_t workspace_bytes,
                                       void *stream);
 
+/* The GDN layer's input prologue, fused: the dual-source ShortConv of
+ * flare_shortconv_dual (Key designs item 3) on each of the q, k, v projections
+ * of both streams in one launch, an optional SiLU, and -- with qk_l2norm -- q
+ * and k divided per (token, head) by sqrt(sum x^2 + 1e-6) (not on the pages:
+ * the usual q/k normalisation in front of a gated delta rule, the same
+ * reading as FLARE_QK_L2NORM).  The outputs are ready for flare_gdn_dual_fwd
+ * without flags.
+ *   heads, head_dim   each projection is [T, heads * head_dim] io, channels
+ *                     contiguous (the [T, H, d] layout of q, k, v)
+ *   x[3], xn[3]       clean / noisy projections (q, k, v); noisy prompt rows
+ *                     are never read
+ *   weight[3]         fp32 [heads * head_dim, width] per projection, tap
+ *                     width-1 on the current token; no bias
+ *   y[3], yn[3]       written: the prologue outputs (noisy prompt rows 0)
+ * Requirements as for flare_shortconv_dual per projection, plus with qk_l2norm
+ * head_dim / (8 / sizeof(io) channels, 4 / sizeof(io) for width > 4) a power of
+ * two of at most 64 (FLARE_ERR_UNSUPPORTED otherwise).  The arrays are host
+ * arrays of device pointers, read during the call. */
+flare_status flare_qkv_prologue(const flare_varlen *varlen, int32_t block_size,
+                                int32_t heads, int32_t head_dim, int32_t width,
+                                int32_t io_dtype, const void *const x[3],
+                                const void *const xn[3],
+                                const float *const weight[3],
+                                int32_t activation, int32_t qk_l2norm,
+                                void *const y[3], void *const yn[3],
+                                void *stream);
+
+/* Reverse mode of flare_qkv_prologue: the same inputs, plus
+ *   dy[3], dyn[3]     gradients of y, yn (dyn prompt rows ignored)
+ *   dx[3], dxn[3]     written: gradients of the projections (dxn prompt rows 0)
+ *   dweight[3]        written: fp32 [heads * head_dim, width]
+ *   workspace         flare_qkv_prologue_bwd_workspace_size bytes, 256-byte
+ *                     aligned (per-block weight partials, reduced in a fixed
+ *                     order: results are run-to-run identical)
+ * The L2 step's gradient is taken inside the kernel from the recomputed
+ * convolution outputs. */
+size_t flare_qkv_prologue_bwd_workspace_size(const flare_varlen *varlen,
+                                             int32_t block_size, int32_t heads,
+                                             int32_t head_dim, int32_t width);
+flare_status flare_qkv_prologue_bwd(const flare_varlen *varlen,
+                                    int32_t block_size, int32_t heads,
+                                    int32_t head_dim, int32_t width,
+                                    int32_t io_dtype, const void *const x[3],
+                                    const void *const xn[3],
+                                    const float *const weight[3],
+                                    int32_t activation, int32_t qk_l2norm,
+                                    const void *const dy[3],
+                                    const void *const dyn[3], void *const dx[3],
+                                    void *const dxn[3], float *const dweight[3],
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
 /* Thread-local message for the last non-OK status; "" if none. */
 const char *flare_last_error(void);
 
@@ -257,7 +309,8 @@ int32_t flare_version(void);
  * (the backward launches the reverse scan, then the per-chunk kernel).
  * Kernel names: "gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel",
  * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel",
- * "shortconv_dual_bwd_kernel" (both kernels of flare_shortconv_dual_bwd),
+ * "shortconv_dual_bwd_kernel" (both kernels of flare_shortconv_dual_bwd;
+ * flare_qkv_prologue and its reverse mode are timed under the ShortConv names),
  * and, for bf16 io at d = 128, the chunked passes: "gdn_tri_kernel" (the
  * chunk matrices, forward and backward), "gdn_fwd_pre_kernel" and
  * "gdn_bwd_pre_kernel" (the state-independent parts of the chunk steps),

@@ -212,3 +212,24 @@ def test_shortconv_bwd_workspace_and_validation(L):
     assert call(ws=ctypes.c_void_p(FAKE.value + 16)) == 5    # misaligned
     assert L.flare_shortconv_dual_bwd(ctypes.byref(varlen([0, 16], [6])), 4, 16, 4, g.BF16, *ok, FAKE, need,
                                       None) == 3
+
+
+def test_qkv_prologue_validation(L):
+    v = varlen([0, 300, 600], [0, 0])
+    A3 = ctypes.c_void_p * 3
+    P3 = A3(FAKE, FAKE, FAKE)
+    # three sections of partials
+    assert L.flare_qkv_prologue_bwd_workspace_size(ctypes.byref(v), 4, 4, 32, 4) == 3 * 3 * 128 * 5 * 4 + 256
+    assert L.flare_qkv_prologue_bwd_workspace_size(ctypes.byref(v), 4, 0, 32, 4) == 0
+
+    def fwd(H=4, d=32, W=4, io=g.BF16, l2=1, x=P3, y=P3):
+        return L.flare_qkv_prologue(ctypes.byref(v), 4, H, d, W, io, x, P3, P3, 0, l2, y, P3, None)
+
+    assert fwd(H=3, d=12) == 3            # bf16 channels (36) must be a multiple of 8
+    assert fwd(d=8 * 68) == 4             # 136 lanes per head: too wide for the in-wave L2 sum
+    assert fwd(d=24) == 4                 # 6 lanes per head: not a power of two
+    assert fwd(l2=2) == 4
+    assert fwd(x=A3(FAKE, None, FAKE)) == 1
+    assert fwd(y=A3(FAKE, FAKE, None)) == 1
+    # without the L2 step the head size is free
+    assert fwd(d=24, l2=0, x=A3(FAKE, None, FAKE)) == 1
