@@ -1,7 +1,7 @@
 """Benchmark of the dual-stream Gated DeltaNet layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-components] [--only fwd|step|serve|conv] [--json-out PATH]
+                    [--no-components] [--only step|infer|serve|conv|layer|copy] [--json-out PATH]
 
 A step is one pass of the layer's hot path over one batch of the headline
 workload -- 4 documents x 8192 tokens (prompt 2048, response in blocks of
@@ -94,7 +94,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
-    p.add_argument("--only", choices=["step", "infer", "serve", "conv", "copy"], default=None,
+    p.add_argument("--only", choices=["step", "infer", "serve", "conv", "layer", "copy"], default=None,
                    help="run one part only (copy: a plain 1 GiB device copy, the reference "
                         "transfer for HBM byte counters)")
     p.add_argument("--json-out", default=None)
@@ -194,6 +194,8 @@ def main():
         comps["serving"] = bench_serving(torch, g, wl, dev, timer, up, args)
     if not args.no_components and args.only in (None, "conv"):
         comps["shortconv"], comps["shortconv_bwd"] = bench_conv(torch, g, wl, dev, timer, up, args)
+    if not args.no_components and args.only in (None, "layer"):
+        comps["packed_layer"] = bench_packed_layer(torch, g, wl, dev, timer, up, args)
     if comps:
         result["components"] = comps
 
@@ -433,6 +435,95 @@ def bench_conv(torch, g, wl, dev, timer, up, args):
              "alg_bytes": balg, "tokens_per_s": T / (bms * 1e-3), "bound": "hbm",
              "traffic": traffic_for("shortconv_dual_bwd_kernel", CONV_WORKLOAD)}
     return fwd, bwd_d
+
+
+def bench_packed_layer(torch, g, wl, dev, timer, up, args):
+    """The layer's whole input side on the packed row (32768 tokens, 8 docs,
+    32 heads x 128, W=4, bf16): ShortConv on q, k, v of both streams, q/k L2
+    norm, dual GDN.  Unfused: three flare_shortconv_dual calls, then the GDN
+    forward with its q/k L2 flag.  Fused: flare_qkv_prologue, then the GDN
+    forward without flags.  Training: the fused forward with chunk-start
+    states, the GDN backward and the prologue's reverse mode."""
+    log("bench: packed layer (32768 tokens, 8 docs, 32 heads x 128, ShortConv W=4 + L2 + dual GDN)")
+    bf = torch.bfloat16
+    p = wl.packed_conv(round_io=False)
+    B, H, d = p["block_size"], p["H"], p["d"]
+    vl = g.Varlen(p["cu_seqlens"], p["prompt_lens"], dev)
+    x, xn, w = up(p["x"], True), up(p["xn"], True), up(p["weight"])
+    T, C3 = x.shape
+    C = C3 // 3
+    xs = [x[:, s * C:(s + 1) * C].contiguous() for s in range(3)]
+    xns = [xn[:, s * C:(s + 1) * C].contiguous() for s in range(3)]
+    ws_ = [w[s * C:(s + 1) * C].contiguous() for s in range(3)]
+    del x, xn
+    gates = [up(p[k]) for k in ("alpha", "beta", "alpha_n", "beta_n")]
+    ys, yns = [torch.empty_like(t) for t in xs], [torch.empty_like(t) for t in xs]
+    hv = lambda t: t.view(T, H, d)
+    o = torch.empty((T, H, d), dtype=bf, device=dev)
+    on = torch.empty_like(o)
+    fws = torch.empty((max(g.workspace_bytes(vl, H, d, B, g.BF16, g.QK_L2NORM),
+                           g.workspace_bytes(vl, H, d, B, g.BF16), 256),), dtype=torch.uint8, device=dev)
+
+    def gdn_args(q, k, v, qn, kn, vn):
+        return [hv(q), hv(k), hv(v), gates[0], gates[1], hv(qn), hv(kn), hv(vn), gates[2], gates[3]]
+
+    def unfused():
+        for s in range(3):
+            g.shortconv_dual(vl, B, xs[s], xns[s], ws_[s], out=(ys[s], yns[s]))
+        g.gdn_dual_fwd(vl, *gdn_args(*ys, *yns), B, flags=g.QK_L2NORM, out=(o, on), want_h_final=False,
+                       workspace=fws)
+
+    def fused():
+        g.qkv_prologue(vl, B, d, xs, xns, ws_, out=(ys, yns))
+        g.gdn_dual_fwd(vl, *gdn_args(*ys, *yns), B, out=(o, on), want_h_final=False, workspace=fws)
+
+    n = max(args.steps // 2, 3)
+    res = {}
+    for name, fn in (("unfused_fwd", unfused), ("fused_fwd", fused)):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(n):
+            timer.run(name, fn)
+        torch.cuda.synchronize()
+        res[name] = timer.avg_ms(name)
+    # training: fused prologue -> GDN forward with states -> GDN backward -> prologue reverse mode
+    Cs = g.chunk_size()
+    ckpt = torch.empty((T // Cs + vl.num_docs, H, d, d), dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(33)
+    do = torch.randn((T, H, d), generator=gen, device=dev).to(bf)
+    don = torch.randn((T, H, d), generator=gen, device=dev).to(bf)
+    bws = torch.empty((g.lib().flare_gdn_dual_workspace_size(vl.ref(), ctypes.byref(g._shape(H, d, B, g.BF16)), 1),),
+                      dtype=torch.uint8, device=dev)
+    pws = torch.empty((g.qkv_prologue_bwd_workspace_bytes(vl, B, H, d, ws_[0].shape[1]),), dtype=torch.uint8,
+                      device=dev)
+    g.qkv_prologue(vl, B, d, xs, xns, ws_, out=(ys, yns))
+    g.gdn_dual_fwd(vl, *gdn_args(*ys, *yns), B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
+    grads = g.gdn_dual_bwd(vl, *gdn_args(*ys, *yns), B, ckpt, do, don, workspace=bws, fwd_workspace=fws)
+    dxs, dxns = [torch.empty_like(t) for t in xs], [torch.empty_like(t) for t in xs]
+    dws = [torch.empty_like(t) for t in ws_]
+    flat = lambda t: t.view(T, H * d)
+
+    def train():
+        g.qkv_prologue(vl, B, d, xs, xns, ws_, out=(ys, yns))
+        g.gdn_dual_fwd(vl, *gdn_args(*ys, *yns), B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
+        g.gdn_dual_bwd(vl, *gdn_args(*ys, *yns), B, ckpt, do, don, out=grads, workspace=bws, fwd_workspace=fws)
+        g.qkv_prologue_bwd(vl, B, d, xs, xns, ws_, [flat(grads[k]) for k in ("dq", "dk", "dv")],
+                           [flat(grads[k]) for k in ("dqn", "dkn", "dvn")], workspace=pws, out=(dxs, dxns, dws))
+
+    for _ in range(max(args.warmup, 1)):
+        train()
+    torch.cuda.synchronize()
+    for _ in range(n):
+        timer.run("train", train)
+    torch.cuda.synchronize()
+    res["train"] = timer.avg_ms("train")
+    out = {"workload": "packed row 32768 tokens, 8 docs, H=32, d=128, B=4, ShortConv W=4 on q/k/v + q/k L2 + dual GDN, bf16"}
+    for k, ms in res.items():
+        out[k] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
+    out["fused_speedup_fwd"] = res["unfused_fwd"] / res["fused_fwd"]
+    return out
 
 
 def cpu_baseline(inp):
