@@ -16,6 +16,10 @@ What each entry computes, with its source:
   adjoint added to the clean adjoint at the block boundary (same item).
 * ``block_step`` -- serving EVAL (no pool write) and COMMIT (causal replay that
   writes the pool), Key designs item 4.
+* ``gdn_verify`` / ``gdn_scatter`` -- AR-Trust (same page, Key designs item
+  4): the clean stream verifies K drafted tokens in one causal pass from the
+  pool state, keeping the state after every token as a candidate; once r
+  tokens are accepted, candidate r is copied into the pool.
 * ``shortconv_dual`` -- the dual-source causal ShortConv, Key designs item 3.
 * ``shortconv_dual_bwd`` -- its reverse mode (parity pinned by finite
   differences and the adjoint identity in the CPU tests).
@@ -70,6 +74,8 @@ def _load():
     lib.oracle_gdn_dual_bwd.restype = i32
     lib.oracle_block_step.argtypes = [i32, P, P, i32, i32, i32, i32, i32, f64] + [P] * 6 + [i32, i32]
     lib.oracle_block_step.restype = i32
+    lib.oracle_gdn_verify.argtypes = [i32, P, P, i32, i32, i32, i32, i32, f64] + [P] * 7 + [i32]
+    lib.oracle_gdn_verify.restype = i32
     lib.oracle_shortconv_dual.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, i32, P, P, i32]
     lib.oracle_shortconv_dual.restype = i32
     lib.oracle_shortconv_dual_bwd.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, P, i32]
@@ -171,6 +177,35 @@ def block_step(slot_idx, pool, q, k, v, alpha, beta, mode, scale=0.0, threads=0)
                                    _p(o), int(mode), int(threads))
     _check(rc, "block_step")
     return o
+
+
+def gdn_verify(slot_idx, pool, q, k, v, alpha, beta, scale=0.0, threads=0):
+    """AR-Trust verify: the clean causal pass over K drafted tokens per request
+    from its pool state.  q,k [R,K,H,dk], v [R,K,H,dv], gates [R,K,H].
+    Returns (o [R,K,H,dv], cand [R,K,H,dk,dv]); the pool is not modified."""
+    slot = _i32(slot_idx)
+    pool = _f64(pool)
+    q, k, v, a, b = map(_f64, (q, k, v, alpha, beta))
+    R, K, H, dk = q.shape
+    dv = v.shape[3]
+    o = np.zeros((R, K, H, dv))
+    cand = np.zeros((R, K, H, dk, dv))
+    rc = _load().oracle_gdn_verify(R, _p(slot), _p(pool), pool.shape[0], H, dk, dv, K, float(scale),
+                                   _p(q), _p(k), _p(v), _p(a), _p(b), _p(o), _p(cand), int(threads))
+    _check(rc, "gdn_verify")
+    return o, cand
+
+
+def gdn_scatter(slot_idx, accepted, cand, pool):
+    """AR-Trust rollback: for each request with r = accepted count clamped to
+    [0, K], r >= 1 writes candidate r (the state after r tokens) into its pool
+    slot; r = 0 leaves the slot as it was.  pool is updated in place."""
+    K = cand.shape[1]
+    for i, sl in enumerate(np.asarray(slot_idx)):
+        r = min(max(int(accepted[i]), 0), K)
+        if r >= 1:
+            pool[sl] = cand[i, r - 1]
+    return pool
 
 
 def shortconv_dual(cu_seqlens, prompt_lens, block_size, x, xn, weight,

@@ -557,6 +557,7 @@ typedef struct {
   double *pool;
   const double *q, *k, *v, *a, *b;
   double *o;
+  double *cand; /* VERIFY: [num_req, B, H, dk, dv] states after each token */
 } step_ctx;
 
 /* mode 0 (EVAL): apply the B noisy updates to a private copy of the pooled
@@ -575,8 +576,10 @@ static void step_unit(void *vctx, int unit, void *scratch) {
   for (int l = 0; l < B; ++l) {
     const size_t row = ((size_t)r * B + l) * H + h;
     delta_step(S, dk, dv, c->k + row * dk, c->v + row * dv, c->a[row], c->b[row], tmp);
-    if (c->mode == 1 && c->o) read_state(S, dk, dv, c->q + row * dk, c->s, c->o + row * dv);
+    if (c->mode >= 1 && c->o) read_state(S, dk, dv, c->q + row * dk, c->s, c->o + row * dv);
+    if (c->mode == 2) memcpy(c->cand + row * SS, S, SS * sizeof(double));
   }
+  if (c->mode == 2) return; /* VERIFY leaves the pool as it was */
   if (c->mode == 0) {
     for (int l = 0; l < B; ++l) {
       const size_t row = ((size_t)r * B + l) * H + h;
@@ -600,7 +603,27 @@ int oracle_block_step(int num_req, const int32_t *slot_idx, double *pool,
       if (slot_idx[j] == slot_idx[r]) return 2;
   }
   step_ctx c = {num_req, H, dk, dv, B, mode, resolve_scale(scale, dk),
-                slot_idx, pool, q, k, v, a, b, o};
+                slot_idx, pool, q, k, v, a, b, o, NULL};
+  run_units(step_unit, &c, num_req * H, ((size_t)dk * dv + dv) * sizeof(double), nthreads);
+  return 0;
+}
+
+/* AR-Trust verify [KD4]: the clean causal pass over K drafted tokens from the
+ * pool state, as COMMIT (per-token outputs o_t = s S_t^T q_t), except that the
+ * state after every token goes to cand[r][t] and the pool is not written. */
+int oracle_gdn_verify(int num_req, const int32_t *slot_idx, double *pool,
+                      int num_slots, int H, int dk, int dv, int K,
+                      double scale, const double *q, const double *k,
+                      const double *v, const double *a, const double *b,
+                      double *o, double *cand, int nthreads) {
+  if (num_req < 0 || H <= 0 || dk <= 0 || dv <= 0 || K <= 0 || !cand) return 2;
+  for (int r = 0; r < num_req; ++r) {
+    if (slot_idx[r] < 0 || slot_idx[r] >= num_slots) return 2;
+    for (int j = 0; j < r; ++j)
+      if (slot_idx[j] == slot_idx[r]) return 2;
+  }
+  step_ctx c = {num_req, H, dk, dv, K, 2, resolve_scale(scale, dk),
+                slot_idx, pool, q, k, v, a, b, o, cand};
   run_units(step_unit, &c, num_req * H, ((size_t)dk * dv + dv) * sizeof(double), nthreads);
   return 0;
 }
