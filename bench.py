@@ -371,13 +371,44 @@ def bench_serving(torch, g, wl, dev, timer, up, args):
     state = R * H * d * d * 4
     io_tok = R * Bs * H * (3 * d * 2 + 8 + d * 2)
     ev_bytes, cm_bytes = state + io_tok, 2 * state + io_tok
+
+    # AR-Trust: verify K = 4 drafted tokens (the state after each kept as a
+    # candidate), then scatter the accepted one; accepted counts ~ U{0..K},
+    # seeded, on the device
+    K = Bs
+    cand = torch.empty((R, K, H, d, d), dtype=torch.float32, device=dev)
+    gen = np.random.default_rng(45)
+    acc = [up(gen.integers(0, K + 1, R).astype(np.int32)) for _ in range(n_rot)]
+    n_acc = [int(np.count_nonzero(a.cpu().numpy())) for a in acc]
+
+    def ar_cycle(i):
+        slot, pool, blocks = sets[i % n_rot]
+        timer.run("verify", lambda: g.gdn_verify(slot, pool, *blocks[4], o=o, cand=cand))
+        timer.run("scatter", lambda: g.gdn_scatter(slot, acc[i % n_rot], cand, pool))
+
+    for i in range(max(args.warmup, 3)):
+        ar_cycle(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        ar_cycle(i)
+    torch.cuda.synchronize()
+    ar_wall = time.perf_counter() - t0
+    vf, sc = timer.avg_ms("verify"), timer.avg_ms("scatter")
+    vf_bytes = state + io_tok + K * state  # pool read, block io, K candidate states written
+    sc_bytes = 2 * float(np.mean(n_acc)) * H * d * d * 4  # accepted candidates read, slots written
     return {"workload": "serving block step, 256 requests x 16 heads, fp32 128x128 states, B=4",
             "eval_ms": ev, "commit_ms": cm, "cycle_ms": 1e3 * wall / n,
             "eval_gbs": ev_bytes / (ev * 1e-3) / 1e9, "commit_gbs": cm_bytes / (cm * 1e-3) / 1e9,
             "eval_hbm_frac": ev_bytes / (ev * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "commit_hbm_frac": cm_bytes / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": R * Bs * 5 / (wall / n), "bound": "hbm",
-            "alg_bytes": {"eval": ev_bytes, "commit": cm_bytes}}
+            "alg_bytes": {"eval": ev_bytes, "commit": cm_bytes, "verify": vf_bytes, "scatter": sc_bytes},
+            "ar_trust": {"verify_ms": vf, "scatter_ms": sc, "cycle_ms": 1e3 * ar_wall / n,
+                         "verify_gbs": vf_bytes / (vf * 1e-3) / 1e9, "scatter_gbs": sc_bytes / (sc * 1e-3) / 1e9,
+                         "verify_hbm_frac": vf_bytes / (vf * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "scatter_hbm_frac": sc_bytes / (sc * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "drafted_tokens_per_s": R * K / (ar_wall / n)}}
 
 
 CONV_WORKLOAD = "packed conv 32768 tokens 8 docs 12288 ch W4 bf16"

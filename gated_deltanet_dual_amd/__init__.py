@@ -17,7 +17,7 @@ import os
 import numpy as np
 
 __all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_bwd",
-           "block_step", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
+           "block_step", "gdn_verify", "gdn_scatter", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
            "qkv_prologue_bwd", "qkv_prologue_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
            "QK_L2NORM", "F32", "BF16"]
 
@@ -82,6 +82,10 @@ def lib():
     L.flare_gdn_dual_bwd.restype = ctypes.c_int
     L.flare_gdn_block_step.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, I32, P]
     L.flare_gdn_block_step.restype = ctypes.c_int
+    L.flare_gdn_verify.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, P, P]
+    L.flare_gdn_verify.restype = ctypes.c_int
+    L.flare_gdn_scatter.argtypes = [I32, P, P, P, P, P, I32, SP, P]
+    L.flare_gdn_scatter.restype = ctypes.c_int
     L.flare_shortconv_dual.argtypes = [VP, I32, I32, I32, I32, P, P, P, P, I32, P, P, P]
     L.flare_shortconv_dual.restype = ctypes.c_int
     L.flare_shortconv_dual_bwd_workspace_size.argtypes = [VP, I32, I32, I32]
@@ -270,6 +274,39 @@ def block_step(slot_idx, pool, q, k, v, alpha, beta, mode, scale=0.0, slot_idx_h
                                       _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), int(mode),
                                       _stream(q.device)))
     return o
+
+
+def gdn_verify(slot_idx, pool, q, k, v, alpha, beta, scale=0.0, slot_idx_host=None, o=None, cand=None):
+    """AR-Trust verify of K drafted tokens per request (q,k,v [R,K,H,d];
+    gates [R,K,H]) from the pool states (read only).  Returns (o [R,K,H,d],
+    cand [R,K,H,d,d] fp32: the state after every token)."""
+    torch = _torch()
+    R, K, H, d = q.shape
+    shp = _shape(H, d, K, _io_of(q), 0, scale)
+    if o is None:
+        o = torch.empty((R, K, H, d), dtype=q.dtype, device=q.device)
+    if cand is None:
+        cand = torch.empty((R, K, H, d, d), dtype=torch.float32, device=q.device)
+    host = None
+    if slot_idx_host is not None:
+        host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
+    _check(lib().flare_gdn_verify(R, _ptr(slot_idx), None if host is None else host.ctypes.data, _ptr(pool),
+                                  pool.shape[0], ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                  _ptr(beta), _ptr(o), _ptr(cand), _stream(q.device)))
+    return o, cand
+
+
+def gdn_scatter(slot_idx, accepted, cand, pool, slot_idx_host=None):
+    """AR-Trust rollback: pool[slot_idx[r]] = cand[r, accepted[r] - 1] for the
+    device int32 counts accepted [R], clamped to [0, K] (0 leaves the slot)."""
+    R, K, H, d, _ = cand.shape
+    shp = _shape(H, d, K, BF16, 0, 0.0)
+    host = None
+    if slot_idx_host is not None:
+        host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
+    _check(lib().flare_gdn_scatter(R, _ptr(slot_idx), None if host is None else host.ctypes.data, _ptr(accepted),
+                                   _ptr(cand), _ptr(pool), pool.shape[0], ctypes.byref(shp), _stream(cand.device)))
+    return pool
 
 
 def shortconv_dual(varlen: Varlen, block_size, x, xn, weight, bias=None, activation=0, out=None):

@@ -171,6 +171,59 @@ flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
   return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_block_step launch");
 }
 
+flare_status flare_gdn_verify(int32_t num_req, const int32_t *slot_idx, const int32_t *slot_idx_host,
+                              const float *state_pool, int32_t num_slots, const flare_gdn_shape *shape,
+                              const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                              void *o, float *cand, void *stream) {
+  clear_error();
+  // the same inputs as a COMMIT of the K = block_size drafted tokens
+  flare_status st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape, q, k, v,
+                                     alpha, beta, o, FLARE_BLOCK_COMMIT);
+  if (st != FLARE_OK) return st;
+  if (num_req > 0 && (!o || !cand)) return fail(FLARE_ERR_NULL, "verify needs the outputs and the candidate buffer");
+  BlockStepArgs a{};
+  a.num_req = num_req;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.B = shape->block_size;
+  a.mode = 2;
+  a.bf16 = shape->io_dtype == FLARE_BF16;
+  a.scale = resolve_scale(shape);
+  a.slot_idx = slot_idx;
+  a.pool = const_cast<float *>(state_pool);  // read only in this mode
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+  a.cand = cand;
+  return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_verify launch");
+}
+
+flare_status flare_gdn_scatter(int32_t num_req, const int32_t *slot_idx, const int32_t *slot_idx_host,
+                               const int32_t *accepted, const float *cand, float *state_pool, int32_t num_slots,
+                               const flare_gdn_shape *shape, void *stream) {
+  clear_error();
+  flare_status st = check_gdn_shape(shape);
+  if (st != FLARE_OK) return st;
+  if (num_req < 0 || num_slots < 0) return fail(FLARE_ERR_SHAPE, "negative count");
+  if (num_req == 0) return FLARE_OK;
+  if (num_req > num_slots) return fail(FLARE_ERR_SHAPE, "num_req %d > num_slots %d", num_req, num_slots);
+  if (!slot_idx || !accepted || !cand || !state_pool) return fail(FLARE_ERR_NULL, "scatter: a required pointer is NULL");
+  if (slot_idx_host) {
+    // same slot checks as the block step (no inputs are read for them)
+    st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape, cand, cand, cand, cand,
+                          cand, cand, FLARE_BLOCK_COMMIT);
+    if (st != FLARE_OK) return st;
+  }
+  ScatterArgs a{};
+  a.num_req = num_req;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.K = shape->block_size;
+  a.slot_idx = slot_idx;
+  a.accepted = accepted;
+  a.cand = cand;
+  a.pool = state_pool;
+  return hip_status(launch_gdn_scatter(a, (hipStream_t)stream), "gdn_scatter launch");
+}
+
 flare_status flare_shortconv_dual(const flare_varlen *varlen, int32_t block_size, int32_t channels,
                                   int32_t width, int32_t io_dtype, const void *x, const void *xn,
                                   const float *weight, const float *bias, int32_t activation,

@@ -19,6 +19,11 @@
 //   EVAL:   o_l = s (G_e r_l + sum_j (G_e/G_j) b_j (q_l.k_j) u_j)   for every l
 //   COMMIT: o_t = s (G_t r_t + sum_{j<=t} (G_t/G_j) b_j (q_t.k_j) u_j),
 //           S  <- G_e S + sum_j (G_e/G_j) b_j k_j u_j^T            (written back)
+//   VERIFY (AR-Trust, Key designs item 4): COMMIT's outputs for K drafted
+//           tokens, and the state after every token, S_t = a_t S_{t-1} +
+//           b_t k_t u_t^T, written to a candidate buffer; the pool is not
+//           written.  A later scatter copies candidate r into the pool once r
+//           tokens are accepted.
 // with G_i = prod_{m<=i} a_m taken as exp of a cumulative sum of log a.
 // Everything is fp32 on the VALU: the step moves ~4 flop per byte of state, far
 // below the MI355X fp32 ridge, so the kernel is bound by HBM bandwidth.
@@ -272,7 +277,36 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
       }
     }
 
-    // 7. COMMIT: rank-B update of the register-resident state, written back
+    // 7. VERIFY: the state after every token, S_t = a_t S_{t-1} + b_t k_t u_t^T,
+    //    into the candidate buffer (same per-thread rows and columns as COMMIT)
+    if (a.mode == 2) {
+      float al[BMAX], bt[BMAX];
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j) {
+        al[j] = j < B ? __expf(sG[j] - (j > 0 ? sG[j - 1] : 0.f)) : 0.f;
+        bt[j] = j < B ? sBeta[j] : 0.f;
+      }
+      float *cand = a.cand + ((size_t)req * B * a.H + h) * D * D;
+      const size_t tstride = (size_t)a.H * D * D;
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const int row = rg * RPG + i;
+        float4 n = s4[i];
+#pragma unroll
+        for (int j = 0; j < BMAX; ++j) {
+          if (j >= B) break;
+          const float kk = sX[j][row] * bt[j];
+          const float4 u = *reinterpret_cast<const float4 *>(&sU[j][4 * cq]);
+          n.x = al[j] * n.x + kk * u.x;
+          n.y = al[j] * n.y + kk * u.y;
+          n.z = al[j] * n.z + kk * u.z;
+          n.w = al[j] * n.w + kk * u.w;
+          *reinterpret_cast<float4 *>(cand + j * tstride + (size_t)row * D + 4 * cq) = n;
+        }
+      }
+    }
+
+    // 8. COMMIT: rank-B update of the register-resident state, written back
     if (a.mode == 1) {
       const float ge = __expf(sG[last]);
       float wj[BMAX];
@@ -306,6 +340,50 @@ static hipError_t launch_step_d(const BlockStepArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((block_step_kernel<IO, D, 8>), grid, block, 0, st, a);
   else
     hipLaunchKernelGGL((block_step_kernel<IO, D, 32>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// One workgroup per (request, head): the accepted candidate's d x d state into
+// the request's pool slot, 16-byte loads and stores.  The count is clamped to
+// [0, K]; 0 leaves the slot as it was.
+template <int D>
+__global__ __launch_bounds__(256) void gdn_scatter_kernel(ScatterArgs a, const int32_t *__restrict__ accepted,
+                                                          const int32_t *__restrict__ slot_idx) {
+  const int req = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int r = min(max(accepted[req], 0), a.K);
+  if (r == 0) return;
+  // the candidate buffer and the pool never overlap (restrict), so the
+  // unrolled copy issues its loads ahead of its stores
+  typedef float v4f __attribute__((ext_vector_type(4)));  // a native vector: stays in registers
+  const v4f *__restrict__ src =
+      reinterpret_cast<const v4f *>(a.cand + (((size_t)req * a.K + (r - 1)) * a.H + h) * D * D);
+  v4f *__restrict__ dst = reinterpret_cast<v4f *>(a.pool + ((size_t)slot_idx[req] * a.H + h) * D * D);
+  constexpr int NV = D * D / 4;
+  if constexpr (NV >= 256) {
+    // all sixteen 16-byte loads of a thread in flight, then their stores
+    constexpr int PER = NV / 256, GRP = PER < 16 ? PER : 16;
+    static_assert(PER % GRP == 0, "whole groups");
+#pragma unroll
+    for (int e0 = 0; e0 < PER; e0 += GRP) {
+      v4f v[GRP];
+#pragma unroll
+      for (int e = 0; e < GRP; ++e) v[e] = src[(e0 + e) * 256 + threadIdx.x];
+#pragma unroll
+      for (int e = 0; e < GRP; ++e) dst[(e0 + e) * 256 + threadIdx.x] = v[e];
+    }
+  } else {
+    if ((int)threadIdx.x < NV) dst[threadIdx.x] = src[threadIdx.x];
+  }
+}
+
+hipError_t launch_gdn_scatter(const ScatterArgs &a, hipStream_t st) {
+  if (a.num_req == 0) return hipSuccess;
+  TimedLaunch tl(K_SCATTER, st);
+  const dim3 grid((unsigned)(a.num_req * a.H));
+  if (a.D == 128)
+    hipLaunchKernelGGL(gdn_scatter_kernel<128>, grid, dim3(256), 0, st, a, a.accepted, a.slot_idx);
+  else
+    hipLaunchKernelGGL(gdn_scatter_kernel<16>, grid, dim3(256), 0, st, a, a.accepted, a.slot_idx);
   return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@
 
 namespace flare {
 
+// mode 0 EVAL, 1 COMMIT, 2 VERIFY (COMMIT's outputs; the state after every
+// token written to cand [num_req][B][H][D][D] instead of the last to the pool)
 struct BlockStepArgs {
   int num_req, H, D, B, mode, bf16;
   float scale;
@@ -14,8 +16,19 @@ struct BlockStepArgs {
   const void *q, *k, *v;
   const float *alpha, *beta;
   void *o;
+  float *cand;
 };
 hipError_t launch_block_step(const BlockStepArgs &a, hipStream_t st);
+
+// AR-Trust rollback: pool[slot[r]] = cand[r][accepted[r] - 1] for accepted
+// counts clamped to [0, K] (0 leaves the slot)
+struct ScatterArgs {
+  int num_req, H, D, K;
+  const int32_t *slot_idx, *accepted;
+  const float *cand;
+  float *pool;
+};
+hipError_t launch_gdn_scatter(const ScatterArgs &a, hipStream_t st);
 
 // ShortConv over up to three sections of channels sharing one document
 // layout (the q, k, v projections of the GDN layer's input prologue; one

@@ -7,6 +7,7 @@ namespace flare {
 
 enum KernelId {
   K_FWD = 0, K_BWD_SCAN, K_BWD_CHUNK, K_BLOCK_STEP, K_SHORTCONV, K_TRI, K_BWD_PRE, K_FWD_PRE, K_FWD_SCAN, K_SHORTCONV_BWD,
+  K_SCATTER,
   K_COUNT
 };
 

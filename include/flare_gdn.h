@@ -196,6 +196,39 @@ flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
                                   const float *alpha, const float *beta,
                                   void *o, int32_t mode, void *stream);
 
+/* AR-Trust (Key designs item 4: the noisy stream drafts K tokens, the clean
+ * stream verifies them in one parallel pass, and a partial acceptance of the
+ * first r < K tokens is rolled back without recomputation by keeping the K
+ * intermediate states and scattering the accepted one).
+ *
+ * flare_gdn_verify: for each request r and head, from S = pool[slot_idx[r]]
+ * (read only), the K = shape->block_size clean causal updates of the drafted
+ * tokens with per-token outputs o_t = s S_t^T q_t (as COMMIT), and the state
+ * after every token written to
+ *   cand   [num_req, K, H, d_k, d_v] fp32, cand[r][t] = state after token t+1
+ * Arguments as flare_gdn_block_step (q, k, v, alpha, beta, o: [num_req, K, H, .]);
+ * o and cand are required.  The pool is not written.
+ *
+ * flare_gdn_scatter: for each request r, with a = accepted[r] (device int32,
+ * clamped to [0, K]), a >= 1 copies cand[r][a-1] into pool[slot_idx[r]] and
+ * a = 0 leaves the slot as it was.  cand as written by flare_gdn_verify with
+ * the same shape; slot_idx_host (optional) as for flare_gdn_block_step.  The
+ * accepted counts stay on the device: the caller's acceptance test never
+ * round-trips through the host. */
+flare_status flare_gdn_verify(int32_t num_req, const int32_t *slot_idx,
+                              const int32_t *slot_idx_host,
+                              const float *state_pool, int32_t num_slots,
+                              const flare_gdn_shape *shape, const void *q,
+                              const void *k, const void *v, const float *alpha,
+                              const float *beta, void *o, float *cand,
+                              void *stream);
+flare_status flare_gdn_scatter(int32_t num_req, const int32_t *slot_idx,
+                               const int32_t *slot_idx_host,
+                               const int32_t *accepted, const float *cand,
+                               float *state_pool, int32_t num_slots,
+                               const flare_gdn_shape *shape, void *stream);
+
+
 /* Dual-source depthwise causal ShortConv (Key designs item 3).
  *   x, xn   [T, channels] io        clean / noisy inputs (xn prompt rows unread)
  *   weight  [channels, width] fp32  weight[c, width-1] multiplies the current
@@ -310,7 +343,8 @@ int32_t flare_version(void);
  * Kernel names: "gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel",
  * "gdn_bwd_chunk_kernel", "block_step_kernel", "shortconv_dual_kernel",
  * "shortconv_dual_bwd_kernel" (both kernels of flare_shortconv_dual_bwd;
- * flare_qkv_prologue and its reverse mode are timed under the ShortConv names),
+ * flare_qkv_prologue and its reverse mode are timed under the ShortConv names;
+ * flare_gdn_verify under "block_step_kernel"), "gdn_scatter_kernel",
  * and, for bf16 io at d = 128, the chunked passes: "gdn_tri_kernel" (the
  * chunk matrices, forward and backward), "gdn_fwd_pre_kernel" and
  * "gdn_bwd_pre_kernel" (the state-independent parts of the chunk steps),

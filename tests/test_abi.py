@@ -233,3 +233,20 @@ def test_qkv_prologue_validation(L):
     assert fwd(y=A3(FAKE, FAKE, None)) == 1
     # without the L2 step the head size is free
     assert fwd(d=24, l2=0, x=A3(FAKE, None, FAKE)) == 1
+
+
+def test_verify_scatter_validation(L):
+    shape = g._shape(2, 16, 4, g.F32)
+    host = np.array([3, 1], np.int32)
+    args = [FAKE] * 5
+    # verify: the COMMIT checks plus required outputs and candidates
+    assert L.flare_gdn_verify(2, FAKE, host.ctypes.data, FAKE, 8, ctypes.byref(shape), *args, FAKE, None, None) == 1
+    assert L.flare_gdn_verify(2, FAKE, host.ctypes.data, FAKE, 8, ctypes.byref(shape), *args, None, FAKE, None) == 1
+    dup = np.array([3, 3], np.int32)
+    assert L.flare_gdn_verify(2, FAKE, dup.ctypes.data, FAKE, 8, ctypes.byref(shape), *args, FAKE, FAKE, None) == 2
+    assert L.flare_gdn_verify(0, None, None, None, 0, ctypes.byref(shape), *([None] * 7), None) == 0
+    # scatter
+    assert L.flare_gdn_scatter(2, FAKE, host.ctypes.data, None, FAKE, FAKE, 8, ctypes.byref(shape), None) == 1
+    assert L.flare_gdn_scatter(2, FAKE, dup.ctypes.data, FAKE, FAKE, FAKE, 8, ctypes.byref(shape), None) == 2
+    assert L.flare_gdn_scatter(9, FAKE, None, FAKE, FAKE, FAKE, 8, ctypes.byref(shape), None) == 2
+    assert L.flare_gdn_scatter(0, None, None, None, None, None, 0, ctypes.byref(shape), None) == 0
