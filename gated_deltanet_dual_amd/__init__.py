@@ -16,7 +16,7 @@ import os
 
 import numpy as np
 
-__all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_bwd",
+__all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_fwd_pool", "gdn_dual_bwd",
            "block_step", "gdn_verify", "gdn_scatter", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
            "qkv_prologue_bwd", "qkv_prologue_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
            "QK_L2NORM", "F32", "BF16"]
@@ -82,6 +82,8 @@ def lib():
     L.flare_gdn_dual_bwd.restype = ctypes.c_int
     L.flare_gdn_block_step.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, I32, P]
     L.flare_gdn_block_step.restype = ctypes.c_int
+    L.flare_gdn_dual_fwd_pool.argtypes = [VP, SP] + [P] * 10 + [P, P, P, I32, I32, P, P, P, I32, P, SZ, P]
+    L.flare_gdn_dual_fwd_pool.restype = ctypes.c_int
     L.flare_gdn_verify.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, P, P]
     L.flare_gdn_verify.restype = ctypes.c_int
     L.flare_gdn_scatter.argtypes = [I32, P, P, P, P, P, I32, SP, P]
@@ -220,6 +222,34 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
                                     _ptr(hf), _ptr(ck), 1, _ptr(workspace),
                                     workspace.numel() if workspace is not None else 0, _stream(q.device)))
     return o, on, hf, ck
+
+
+def gdn_dual_fwd_pool(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size, doc_slot,
+                      pool, read_initial=False, doc_slot_host=None, scale=0.0, flags=0, out=None, workspace=None):
+    """Prefill into a state pool: the dual forward with document i starting
+    from pool[doc_slot[i]] (read_initial) or zero, and its final state written
+    to pool[doc_slot[i]].  doc_slot: device int32 [N].  Returns (o, on)."""
+    torch = _torch()
+    T, H, d = q.shape
+    shp = _shape(H, d, block_size, _io_of(q), flags, scale)
+    if out is None:
+        o = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+        on = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    else:
+        o, on = out
+    ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 0)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    host = None
+    if doc_slot_host is not None:
+        host = np.ascontiguousarray(np.asarray(doc_slot_host, dtype=np.int32))
+    _check(lib().flare_gdn_dual_fwd_pool(varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                         _ptr(beta), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(alpha_n), _ptr(beta_n),
+                                         _ptr(doc_slot), None if host is None else host.ctypes.data, _ptr(pool),
+                                         pool.shape[0], 1 if read_initial else 0, _ptr(o), _ptr(on), None, 1,
+                                         _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                         _stream(q.device)))
+    return o, on
 
 
 def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,

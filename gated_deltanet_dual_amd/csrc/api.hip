@@ -52,14 +52,11 @@ int64_t flare_gdn_ckpt_slot(int32_t cu_seqlens_i, int32_t doc_index, int32_t chu
   return ckpt_slot(cu_seqlens_i, doc_index, chunk_index, ckpt_stride_chunks);
 }
 
-flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shape *shape,
-                                const void *q, const void *k, const void *v, const float *alpha,
-                                const float *beta, const void *qn, const void *kn, const void *vn,
-                                const float *alpha_n, const float *beta_n, const float *h0,
-                                void *o, void *on, float *h_final, float *ckpt,
-                                int32_t ckpt_stride_chunks, void *workspace, size_t workspace_bytes,
-                                void *stream) {
-  clear_error();
+static flare_status fwd_impl(const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q, const void *k,
+                             const void *v, const float *alpha, const float *beta, const void *qn, const void *kn,
+                             const void *vn, const float *alpha_n, const float *beta_n, const float *h0, void *o,
+                             void *on, float *h_final, const int32_t *state_slot, float *ckpt,
+                             int32_t ckpt_stride_chunks, void *workspace, size_t workspace_bytes, void *stream) {
   VarlenInfo vi;
   flare_status st = check_fwd_common(varlen, shape, &vi);
   if (st != FLARE_OK) return st;
@@ -87,9 +84,49 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shap
   a.q = q; a.k = k; a.v = v; a.qn = qn; a.kn = kn; a.vn = vn;
   a.alpha = alpha; a.beta = beta; a.alpha_n = alpha_n; a.beta_n = beta_n;
   a.h0 = h0; a.o = o; a.on = on; a.h_final = h_final; a.ckpt = ckpt;
+  a.state_slot = state_slot;
   a.workspace = need > 0 ? reinterpret_cast<float *>(workspace) : nullptr;
   a.T = vi.total_tokens;
   return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd launch");
+}
+
+flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shape *shape,
+                                const void *q, const void *k, const void *v, const float *alpha,
+                                const float *beta, const void *qn, const void *kn, const void *vn,
+                                const float *alpha_n, const float *beta_n, const float *h0,
+                                void *o, void *on, float *h_final, float *ckpt,
+                                int32_t ckpt_stride_chunks, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  clear_error();
+  return fwd_impl(varlen, shape, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0, o, on, h_final, nullptr,
+                  ckpt, ckpt_stride_chunks, workspace, workspace_bytes, stream);
+}
+
+flare_status flare_gdn_dual_fwd_pool(const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q,
+                                     const void *k, const void *v, const float *alpha, const float *beta,
+                                     const void *qn, const void *kn, const void *vn, const float *alpha_n,
+                                     const float *beta_n, const int32_t *doc_slot, const int32_t *doc_slot_host,
+                                     float *state_pool, int32_t num_slots, int32_t read_initial, void *o, void *on,
+                                     float *ckpt, int32_t ckpt_stride_chunks, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  clear_error();
+  if (!varlen) return fail(FLARE_ERR_NULL, "varlen is NULL");
+  if (read_initial != 0 && read_initial != 1) return fail(FLARE_ERR_SHAPE, "read_initial %d is not 0 or 1", read_initial);
+  if (varlen->num_docs > 0) {
+    if (!doc_slot || !state_pool) return fail(FLARE_ERR_NULL, "gdn_dual_fwd_pool: doc_slot or state_pool is NULL");
+    if (varlen->num_docs > num_slots)
+      return fail(FLARE_ERR_SHAPE, "%d documents > %d pool slots", varlen->num_docs, num_slots);
+    if (doc_slot_host) {
+      // distinct slots in range: the same check as the serving step's
+      flare_status st = check_block_step(varlen->num_docs, doc_slot, doc_slot_host, state_pool, num_slots, shape,
+                                         state_pool, state_pool, state_pool, state_pool, state_pool, state_pool,
+                                         FLARE_BLOCK_COMMIT);
+      if (st != FLARE_OK) return st;
+    }
+  }
+  return fwd_impl(varlen, shape, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n,
+                  read_initial ? state_pool : nullptr, o, on, state_pool, doc_slot, ckpt, ckpt_stride_chunks,
+                  workspace, workspace_bytes, stream);
 }
 
 flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shape *shape,

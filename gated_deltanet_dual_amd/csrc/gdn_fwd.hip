@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
     S[e] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (q < NST && a.h0) {
       const int rt = q / CT, ct = q % CT;
-      const float *src = a.h0 + ((size_t)doc * H + h) * D * D;
+      const float *src = a.h0 + ((size_t)(a.state_slot ? a.state_slot[doc] : doc) * H + h) * D * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[e][r] = src[(size_t)(16 * rt + acc_row(r)) * D + dv0 + 16 * ct + acc_col()];
     }
@@ -700,7 +700,8 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
     lds_barrier();
     store_outputs(nchunks - 1, prev_noisy);
   }
-  if (a.h_final) write_state_global(a.h_final + ((size_t)doc * H + h) * D * D);
+  if (a.h_final)
+    write_state_global(a.h_final + ((size_t)(a.state_slot ? a.state_slot[doc] : doc) * H + h) * D * D);
 }
 
 template <typename IO, int D>
@@ -747,6 +748,7 @@ hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st) {
       sa.pack = pack;
       sa.init = a.h0;
       sa.final_out = a.h_final;
+      sa.slot = a.state_slot;
       sa.states = states;
       TimedLaunch tl(K_FWD_SCAN, st);
       hipError_t e = launch_scan_d128(sa, false, st);

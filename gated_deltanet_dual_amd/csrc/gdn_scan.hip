@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   for (int kt = 0; kt < 8; ++kt) {
     X[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (a.init) {
-      const float *src = a.init + ((size_t)doc * H + h) * D * D;
+      const float *src = a.init + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) X[kt][r] = src[(size_t)(16 * kt + g4 + r) * D + dv0 + cl];
     }
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     step(p3, at(i + 3), at(i + 7));
   }
   if (a.final_out) {
-    float *dst = a.final_out + ((size_t)doc * H + h) * D * D;
+    float *dst = a.final_out + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll

@@ -72,6 +72,10 @@ struct FwdArgs {
   float *h_final, *ckpt;
   float *workspace;  // the forward's chunk matrices (bf16, d = 128, no flags)
   int64_t T;
+  // NULL, or per document the index of its state in h0 / h_final (a state
+  // pool): document i starts from h0[state_slot[i]] and ends in
+  // h_final[state_slot[i]]
+  const int32_t *state_slot;
 };
 hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
 // bf16 io at d = 128 without flags: the forward's pre-pass (chunk matrices
@@ -90,6 +94,7 @@ struct ScanArgs {
   const float *init;   // [N, H, 128, 128] X before the first step, or NULL (zero)
   float *final_out;    // [N, H, 128, 128] X after the last step, or NULL
   float *states;       // [slots, H, 128, 128]: X before the step of chunk c, at chunk c's slot
+  const int32_t *slot; // NULL, or per document the index of its init / final_out state
 };
 hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st);
 

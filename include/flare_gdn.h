@@ -147,6 +147,35 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen,
                                 int32_t ckpt_stride_chunks, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* Prefill into the serving pool (Key designs item 4: the serving pool holds
+ * one causal state per request): flare_gdn_dual_fwd with every document's
+ * state kept in a pool slot instead of the h0 / h_final arrays.
+ *   doc_slot       device int32 [N]: the pool slot of each document
+ *   doc_slot_host  optional host copy, checked for range and duplicates
+ *                  (FLARE_ERR_SHAPE) as in flare_gdn_block_step
+ *   state_pool     fp32 [num_slots, H, d_k, d_v]; document i's final clean
+ *                  state is written to state_pool[doc_slot[i]], every other
+ *                  slot is untouched
+ *   read_initial   1: document i starts from state_pool[doc_slot[i]] (read
+ *                  before it is overwritten); 0: from zero
+ * All other arguments, requirements and the workspace are those of
+ * flare_gdn_dual_fwd.  The pool can then be served by flare_gdn_block_step
+ * and flare_gdn_verify without a copy. */
+flare_status flare_gdn_dual_fwd_pool(const flare_varlen *varlen,
+                                     const flare_gdn_shape *shape,
+                                     const void *q, const void *k, const void *v,
+                                     const float *alpha, const float *beta,
+                                     const void *qn, const void *kn,
+                                     const void *vn, const float *alpha_n,
+                                     const float *beta_n,
+                                     const int32_t *doc_slot,
+                                     const int32_t *doc_slot_host,
+                                     float *state_pool, int32_t num_slots,
+                                     int32_t read_initial, void *o, void *on,
+                                     float *ckpt, int32_t ckpt_stride_chunks,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 /* Reverse mode of flare_gdn_dual_fwd (Key designs items 2 and 3): the adjoint
  * reaching each noisy block start is added to the clean adjoint at that block's
  * boundary, the adjoint is reset per document, and nothing crosses documents.

@@ -250,3 +250,23 @@ def test_verify_scatter_validation(L):
     assert L.flare_gdn_scatter(2, FAKE, dup.ctypes.data, FAKE, FAKE, FAKE, 8, ctypes.byref(shape), None) == 2
     assert L.flare_gdn_scatter(9, FAKE, None, FAKE, FAKE, FAKE, 8, ctypes.byref(shape), None) == 2
     assert L.flare_gdn_scatter(0, None, None, None, None, None, 0, ctypes.byref(shape), None) == 0
+
+
+def test_fwd_pool_validation(L):
+    v = varlen([0, 40, 80], [8, 8])
+    shape = g._shape(1, 16, 4, g.F32)
+    P10 = [FAKE] * 10
+    host = np.array([1, 3], np.int32)
+    dup = np.array([3, 3], np.int32)
+
+    def call(slot=FAKE, slot_host=host, pool=FAKE, n_slots=4, read=1):
+        return L.flare_gdn_dual_fwd_pool(ctypes.byref(v), ctypes.byref(shape), *P10, slot,
+                                         None if slot_host is None else slot_host.ctypes.data, pool, n_slots, read,
+                                         FAKE, FAKE, None, 1, FAKE, 1 << 20, None)
+
+    assert call(slot=None) == 1
+    assert call(pool=None) == 1
+    assert call(slot_host=dup) == 2
+    assert call(n_slots=1) == 2          # two documents, one slot
+    assert call(read=2) == 2
+    assert call(slot_host=np.array([1, 4], np.int32)) == 2  # slot out of range
