@@ -20,6 +20,10 @@ What each entry computes, with its source:
   4): the clean stream verifies K drafted tokens in one causal pass from the
   pool state, keeping the state after every token as a candidate; once r
   tokens are accepted, candidate r is copied into the pool.
+* ``block_step_conv`` / ``conv_cache_fill`` -- the serving step with the
+  ShortConv in front: each request keeps its last W-1 clean projection rows,
+  so a block's taps before its start read that clean history and taps inside
+  read the block itself; the prefill fills the history from the prompt.
 * ``shortconv_dual`` -- the dual-source causal ShortConv, Key designs item 3.
 * ``shortconv_dual_bwd`` -- its reverse mode (parity pinned by finite
   differences and the adjoint identity in the CPU tests).
@@ -302,3 +306,54 @@ def qkv_prologue_bwd(cu_seqlens, prompt_lens, block_size, head_dim, xs, xns, wei
         dxns.append(dxn)
         dws.append(dw)
     return dxs, dxns, dws
+
+
+def conv_cache_fill(cu_seqlens, xs, width, doc_slot, cache):
+    """The clean history of each document after a prefill: cache[slot_i][j, s]
+    = xs[s][end_i - (W-1) + j] (zero before the document start).  cache:
+    [n_slots, W-1, 3, C], updated in place."""
+    W1 = width - 1
+    for i, sl in enumerate(doc_slot):
+        a, e = int(cu_seqlens[i]), int(cu_seqlens[i + 1])
+        for j in range(W1):
+            t = e - W1 + j
+            for sec in range(3):
+                cache[sl, j, sec] = xs[sec][t] if t >= a else 0.0
+    return cache
+
+
+def block_step_conv(slot_idx, pool, cache, head_dim, xs, weights, alpha, beta, mode, activation=0, l2=True,
+                    scale=0.0):
+    """Serving step whose q, k, v come from raw projections xs (three
+    [R, B, H*d]) through the ShortConv: request r's block is preceded by its
+    clean history cache[slot_r] ([W-1, 3, H*d]) -- a one-document batch whose
+    prompt is the history and whose one block is the drafted / fixed block.
+    EVAL reads the block as the noisy stream (outputs at the block end), COMMIT
+    as the clean stream and then keeps the last W-1 clean rows as the new
+    history.  pool and cache are updated in place for COMMIT."""
+    xs = [_f64(x) for x in xs]
+    R, B, C = xs[0].shape
+    W1 = cache.shape[1]
+    H = C // head_dim
+    q, k, v = (np.zeros((R, B, H, head_dim)) for _ in range(3))
+    for r, sl in enumerate(slot_idx):
+        n = W1 + B
+        hist = [cache[sl, :, sec] for sec in range(3)]
+        blk = [xs[sec][r] for sec in range(3)]
+        if mode == EVAL:
+            x = [np.concatenate([hist[sec], np.zeros((B, C))]) for sec in range(3)]
+            xn = [np.concatenate([np.zeros((W1, C)), blk[sec]]) for sec in range(3)]
+        else:
+            x = [np.concatenate([hist[sec], blk[sec]]) for sec in range(3)]
+            xn = x
+        ys, yns = qkv_prologue([0, n], [W1], B, head_dim, x, xn, weights, activation=activation, l2=l2)
+        out = yns if mode == EVAL else ys
+        for sec, dst in enumerate((q, k, v)):
+            dst[r] = out[sec][W1:].reshape(B, H, head_dim)
+    o = block_step(slot_idx, pool, q, k, v, alpha, beta, EVAL if mode == EVAL else COMMIT, scale=scale)
+    if mode != EVAL:
+        for r, sl in enumerate(slot_idx):
+            full = [np.concatenate([cache[sl, :, sec], xs[sec][r]]) for sec in range(3)]
+            for sec in range(3):
+                cache[sl, :, sec] = full[sec][B:]
+    return o
