@@ -395,6 +395,32 @@ def bench_serving(torch, g, wl, dev, timer, up, args):
     torch.cuda.synchronize()
     ar_wall = time.perf_counter() - t0
     vf, sc = timer.avg_ms("verify"), timer.avg_ms("scatter")
+
+    # the same EVAL / COMMIT with the ShortConv in front: raw bf16 projections,
+    # W = 4 clean histories per slot, SiLU, q/k L2 norm
+    Wc = 4
+    crng = np.random.default_rng(46)
+    cws = [up(crng.uniform(-0.5, 0.5, (H * d, Wc)).astype(np.float32)) for _ in range(3)]
+    caches = [torch.randn((512, Wc - 1, 3, H * d), generator=torch.Generator(device=dev).manual_seed(47 + r),
+                          device=dev).to(torch.bfloat16) for r in range(n_rot)]
+
+    def conv_cycle(i):
+        slot, pool, blocks = sets[i % n_rot]
+        for e in range(4):
+            timer.run("eval_conv", lambda: g.block_step_conv(slot, pool, caches[i % n_rot], cws, *blocks[e], g.EVAL,
+                                                             activation=1, o=o))
+        timer.run("commit_conv", lambda: g.block_step_conv(slot, pool, caches[i % n_rot], cws, *blocks[4], g.COMMIT,
+                                                           activation=1, o=o))
+
+    for i in range(max(args.warmup, 3)):
+        conv_cycle(i)
+    torch.cuda.synchronize()
+    for i in range(n):
+        conv_cycle(i)
+    torch.cuda.synchronize()
+    evc, cmc = timer.avg_ms("eval_conv"), timer.avg_ms("commit_conv")
+    hist = R * H * (Wc - 1) * 3 * d * 2  # the histories read (and written back by COMMIT)
+    evc_bytes, cmc_bytes = ev_bytes + hist, cm_bytes + 2 * hist
     vf_bytes = state + io_tok + K * state  # pool read, block io, K candidate states written
     sc_bytes = 2 * float(np.mean(n_acc)) * H * d * d * 4  # accepted candidates read, slots written
     return {"workload": "serving block step, 256 requests x 16 heads, fp32 128x128 states, B=4",
@@ -404,6 +430,11 @@ def bench_serving(torch, g, wl, dev, timer, up, args):
             "commit_hbm_frac": cm_bytes / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": R * Bs * 5 / (wall / n), "bound": "hbm",
             "alg_bytes": {"eval": ev_bytes, "commit": cm_bytes, "verify": vf_bytes, "scatter": sc_bytes},
+            "with_conv": {"eval_ms": evc, "commit_ms": cmc, "eval_gbs": evc_bytes / (evc * 1e-3) / 1e9,
+                          "commit_gbs": cmc_bytes / (cmc * 1e-3) / 1e9,
+                          "eval_hbm_frac": evc_bytes / (evc * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "commit_hbm_frac": cmc_bytes / (cmc * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "alg_bytes": {"eval": evc_bytes, "commit": cmc_bytes}},
             "ar_trust": {"verify_ms": vf, "scatter_ms": sc, "cycle_ms": 1e3 * ar_wall / n,
                          "verify_gbs": vf_bytes / (vf * 1e-3) / 1e9, "scatter_gbs": sc_bytes / (sc * 1e-3) / 1e9,
                          "verify_hbm_frac": vf_bytes / (vf * 1e-3) / 1e9 / HBM_PEAK_GBS,

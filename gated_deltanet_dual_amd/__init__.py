@@ -17,7 +17,7 @@ import os
 import numpy as np
 
 __all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_fwd_pool", "gdn_dual_bwd",
-           "block_step", "gdn_verify", "gdn_scatter", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
+           "block_step", "block_step_conv", "conv_cache_fill", "gdn_verify", "gdn_scatter", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
            "qkv_prologue_bwd", "qkv_prologue_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
            "QK_L2NORM", "F32", "BF16"]
 
@@ -67,6 +67,7 @@ def lib():
     _check_single_hip_runtime()
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     VP, SP = ctypes.POINTER(_Varlen), ctypes.POINTER(GDNShape)
+    A3 = ctypes.c_void_p * 3  # host arrays of three device pointers
     L.flare_gdn_chunk_size.restype = I32
     L.flare_version.restype = I32
     L.flare_last_error.restype = ctypes.c_char_p
@@ -84,6 +85,10 @@ def lib():
     L.flare_gdn_block_step.restype = ctypes.c_int
     L.flare_gdn_dual_fwd_pool.argtypes = [VP, SP] + [P] * 10 + [P, P, P, I32, I32, P, P, P, I32, P, SZ, P]
     L.flare_gdn_dual_fwd_pool.restype = ctypes.c_int
+    L.flare_gdn_block_step_conv.argtypes = [I32, P, P, P, P, I32, SP, I32, A3, I32, I32, P, P, P, P, P, P, I32, P]
+    L.flare_gdn_block_step_conv.restype = ctypes.c_int
+    L.flare_conv_cache_fill.argtypes = [VP, I32, I32, I32, I32, A3, P, P, P, I32, P]
+    L.flare_conv_cache_fill.restype = ctypes.c_int
     L.flare_gdn_verify.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, P, P]
     L.flare_gdn_verify.restype = ctypes.c_int
     L.flare_gdn_scatter.argtypes = [I32, P, P, P, P, P, I32, SP, P]
@@ -94,7 +99,6 @@ def lib():
     L.flare_shortconv_dual_bwd_workspace_size.restype = SZ
     L.flare_shortconv_dual_bwd.argtypes = [VP, I32, I32, I32, I32, P, P, P, P, I32, P, P, P, P, P, P, P, SZ, P]
     L.flare_shortconv_dual_bwd.restype = ctypes.c_int
-    A3 = ctypes.c_void_p * 3
     L.flare_qkv_prologue.argtypes = [VP, I32, I32, I32, I32, I32, A3, A3, A3, I32, I32, A3, A3, P]
     L.flare_qkv_prologue.restype = ctypes.c_int
     L.flare_qkv_prologue_bwd_workspace_size.argtypes = [VP, I32, I32, I32, I32]
@@ -304,6 +308,44 @@ def block_step(slot_idx, pool, q, k, v, alpha, beta, mode, scale=0.0, slot_idx_h
                                       _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), int(mode),
                                       _stream(q.device)))
     return o
+
+
+def block_step_conv(slot_idx, pool, cache, weights, xq, xk, xv, alpha, beta, mode, activation=0, qk_l2norm=True,
+                    scale=0.0, slot_idx_host=None, o=None):
+    """The serving step with the ShortConv in front: xq, xk, xv [R,B,H,d] raw
+    projections; cache [n_slots, W-1, 3, H*d] io clean histories (None for
+    W = 1); weights: three [H*d, W] fp32.  Returns o [R,B,H,d]."""
+    torch = _torch()
+    R, B, H, d = xq.shape
+    W = weights[0].shape[1]
+    shp = _shape(H, d, B, _io_of(xq), 0, scale)
+    if o is None:
+        o = torch.empty((R, B, H, d), dtype=xq.dtype, device=xq.device)
+    elif o is False:
+        o = None
+    host = None
+    if slot_idx_host is not None:
+        host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
+    _check(lib().flare_gdn_block_step_conv(R, _ptr(slot_idx), None if host is None else host.ctypes.data,
+                                           _ptr(pool), _ptr(cache), pool.shape[0], ctypes.byref(shp), W,
+                                           _a3(weights), int(activation), 1 if qk_l2norm else 0, _ptr(xq),
+                                           _ptr(xk), _ptr(xv), _ptr(alpha), _ptr(beta), _ptr(o), int(mode),
+                                           _stream(xq.device)))
+    return o
+
+
+def conv_cache_fill(varlen: Varlen, head_dim, width, xs, doc_slot, cache, doc_slot_host=None):
+    """Each document's clean history (its last W-1 projection rows, zero
+    before its start) into cache[doc_slot[i]]; xs: three [T, H*d] io."""
+    T, C = xs[0].shape
+    host = None
+    if doc_slot_host is not None:
+        host = np.ascontiguousarray(np.asarray(doc_slot_host, dtype=np.int32))
+    _check(lib().flare_conv_cache_fill(varlen.ref(), C // int(head_dim), int(head_dim), int(width), _io_of(xs[0]),
+                                       _a3(xs), _ptr(doc_slot), None if host is None else host.ctypes.data,
+                                       _ptr(cache), cache.shape[0] if cache is not None else 0,
+                                       _stream(xs[0].device)))
+    return cache
 
 
 def gdn_verify(slot_idx, pool, q, k, v, alpha, beta, scale=0.0, slot_idx_host=None, o=None, cand=None):

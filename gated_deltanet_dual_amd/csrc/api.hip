@@ -116,13 +116,8 @@ flare_status flare_gdn_dual_fwd_pool(const flare_varlen *varlen, const flare_gdn
     if (!doc_slot || !state_pool) return fail(FLARE_ERR_NULL, "gdn_dual_fwd_pool: doc_slot or state_pool is NULL");
     if (varlen->num_docs > num_slots)
       return fail(FLARE_ERR_SHAPE, "%d documents > %d pool slots", varlen->num_docs, num_slots);
-    if (doc_slot_host) {
-      // distinct slots in range: the same check as the serving step's
-      flare_status st = check_block_step(varlen->num_docs, doc_slot, doc_slot_host, state_pool, num_slots, shape,
-                                         state_pool, state_pool, state_pool, state_pool, state_pool, state_pool,
-                                         FLARE_BLOCK_COMMIT);
-      if (st != FLARE_OK) return st;
-    }
+    const flare_status st = check_slots_host(varlen->num_docs, doc_slot_host, num_slots);
+    if (st != FLARE_OK) return st;
   }
   return fwd_impl(varlen, shape, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n,
                   read_initial ? state_pool : nullptr, o, on, state_pool, doc_slot, ckpt, ckpt_stride_chunks,
@@ -208,6 +203,82 @@ flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
   return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_block_step launch");
 }
 
+flare_status flare_gdn_block_step_conv(int32_t num_req, const int32_t *slot_idx, const int32_t *slot_idx_host,
+                                       float *state_pool, void *conv_cache, int32_t num_slots,
+                                       const flare_gdn_shape *shape, int32_t width, const float *const weight[3],
+                                       int32_t activation, int32_t qk_l2norm, const void *xq, const void *xk,
+                                       const void *xv, const float *alpha, const float *beta, void *o, int32_t mode,
+                                       void *stream) {
+  clear_error();
+  flare_status st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape, xq, xk, xv,
+                                     alpha, beta, o, mode);
+  if (st != FLARE_OK) return st;
+  if (shape->flags != 0) return fail(FLARE_ERR_UNSUPPORTED, "block_step_conv: the L2 step is its own argument");
+  if (width < 1 || width > 8) return fail(FLARE_ERR_UNSUPPORTED, "width %d not in [1, 8]", width);
+  if (shape->block_size > 8)
+    return fail(FLARE_ERR_UNSUPPORTED, "block_step_conv is built for blocks of up to 8 tokens (got %d)",
+                shape->block_size);
+  if (activation != 0 && activation != 1) return fail(FLARE_ERR_UNSUPPORTED, "activation %d unknown", activation);
+  if (qk_l2norm != 0 && qk_l2norm != 1) return fail(FLARE_ERR_UNSUPPORTED, "qk_l2norm %d unknown", qk_l2norm);
+  if (num_req > 0) {
+    if (!weight || !weight[0] || !weight[1] || !weight[2])
+      return fail(FLARE_ERR_NULL, "block_step_conv: a weight pointer is NULL");
+    if (width > 1 && !conv_cache) return fail(FLARE_ERR_NULL, "block_step_conv: conv_cache is NULL");
+  }
+  BlockStepArgs a{};
+  a.num_req = num_req;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.B = shape->block_size;
+  a.mode = mode;
+  a.bf16 = shape->io_dtype == FLARE_BF16;
+  a.scale = resolve_scale(shape);
+  a.slot_idx = slot_idx;
+  a.pool = state_pool;
+  a.q = xq; a.k = xk; a.v = xv; a.alpha = alpha; a.beta = beta; a.o = o;
+  a.conv = 1;
+  a.W = width;
+  a.act = activation;
+  a.l2 = qk_l2norm;
+  a.cache = conv_cache;
+  for (int s = 0; s < 3; ++s) a.cw[s] = num_req > 0 ? weight[s] : nullptr;
+  return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_block_step_conv launch");
+}
+
+flare_status flare_conv_cache_fill(const flare_varlen *varlen, int32_t heads, int32_t head_dim, int32_t width,
+                                   int32_t io_dtype, const void *const x[3], const int32_t *doc_slot,
+                                   const int32_t *doc_slot_host, void *conv_cache, int32_t num_slots,
+                                   void *stream) {
+  clear_error();
+  VarlenInfo vi;
+  flare_status st = check_varlen(varlen, 1, &vi);
+  if (st != FLARE_OK) return st;
+  if (heads <= 0 || head_dim <= 0 || (int64_t)heads * head_dim > INT32_MAX)
+    return fail(FLARE_ERR_SHAPE, "heads and head_dim must be positive");
+  if (width < 1 || width > 8) return fail(FLARE_ERR_UNSUPPORTED, "width %d not in [1, 8]", width);
+  if (io_dtype != FLARE_F32 && io_dtype != FLARE_BF16) return fail(FLARE_ERR_UNSUPPORTED, "io_dtype %d unknown", io_dtype);
+  const int C = heads * head_dim;
+  if (C % (io_dtype == FLARE_BF16 ? 8 : 4) != 0)
+    return fail(FLARE_ERR_ALIGN, "heads * head_dim = %d must be a multiple of 16 bytes", C);
+  const int N = varlen->num_docs;
+  if (N == 0 || width == 1) return FLARE_OK;
+  if (N > num_slots) return fail(FLARE_ERR_SHAPE, "%d documents > %d slots", N, num_slots);
+  if (!x || !x[0] || !x[1] || !x[2] || !doc_slot || !conv_cache)
+    return fail(FLARE_ERR_NULL, "conv_cache_fill: a required pointer is NULL");
+  st = check_slots_host(N, doc_slot_host, num_slots);
+  if (st != FLARE_OK) return st;
+  ConvCacheArgs a{};
+  a.num_docs = N;
+  a.C = C;
+  a.W = width;
+  a.bf16 = io_dtype == FLARE_BF16;
+  a.cu = varlen->cu_seqlens;
+  a.slot = doc_slot;
+  for (int s = 0; s < 3; ++s) a.x[s] = x[s];
+  a.cache = conv_cache;
+  return hip_status(launch_conv_cache_fill(a, (hipStream_t)stream), "conv_cache_fill launch");
+}
+
 flare_status flare_gdn_verify(int32_t num_req, const int32_t *slot_idx, const int32_t *slot_idx_host,
                               const float *state_pool, int32_t num_slots, const flare_gdn_shape *shape,
                               const void *q, const void *k, const void *v, const float *alpha, const float *beta,
@@ -243,12 +314,8 @@ flare_status flare_gdn_scatter(int32_t num_req, const int32_t *slot_idx, const i
   if (num_req == 0) return FLARE_OK;
   if (num_req > num_slots) return fail(FLARE_ERR_SHAPE, "num_req %d > num_slots %d", num_req, num_slots);
   if (!slot_idx || !accepted || !cand || !state_pool) return fail(FLARE_ERR_NULL, "scatter: a required pointer is NULL");
-  if (slot_idx_host) {
-    // same slot checks as the block step (no inputs are read for them)
-    st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape, cand, cand, cand, cand,
-                          cand, cand, FLARE_BLOCK_COMMIT);
-    if (st != FLARE_OK) return st;
-  }
+  st = check_slots_host(num_req, slot_idx_host, num_slots);
+  if (st != FLARE_OK) return st;
   ScatterArgs a{};
   a.num_req = num_req;
   a.H = shape->num_heads;

@@ -52,13 +52,18 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
   return x;
 }
 
-template <typename IO, int D, int BMAX>
+// CONV: the block inputs are raw projections that go through the serving
+// ShortConv first (the request's W - 1 clean history rows, then the block;
+// SiLU; q/k L2 norm) -- see BlockStepArgs
+template <typename IO, int D, int BMAX, bool CONV>
 __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArgs a) {
   using Cfg = StepCfg<D>;
   constexpr int NT = Cfg::NT, NRG = Cfg::NRG, RPG = Cfg::RPG, G = Cfg::G;
   constexpr int NV = 2 * BMAX;           // k vectors then q vectors
   constexpr int EPU = 16 / sizeof(IO);   // io elements per 16 bytes
   constexpr int UPR = D / EPU;           // 16-byte units per row
+  constexpr int WM1 = 7;                 // most history rows (W <= 8)
+  constexpr int NRAW = CONV ? WM1 + BMAX : 1;
   const int B = a.B;
   const int t = threadIdx.x;
   const int rg = t % NRG, cq = t / NRG;
@@ -70,6 +75,10 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
   __shared__ __align__(16) float sU[BMAX][D];
   __shared__ float sKK[BMAX][BMAX + 1], sQK[BMAX][BMAX + 1], sT[BMAX][BMAX + 1];
   __shared__ float sG[BMAX], sBeta[BMAX];
+  // CONV: the raw rows of q, k, v (history, then the block) as fp32, and the
+  // head's conv weights [projection][channel * W + tap]
+  __shared__ __align__(16) float sRaw[CONV ? 3 : 1][NRAW][CONV ? D : 4];
+  __shared__ __align__(16) float sCW[CONV ? 3 : 1][CONV ? D * (WM1 + 1) : 4];
 
   const IO *const pk = reinterpret_cast<const IO *>(a.k), *const pq = reinterpret_cast<const IO *>(a.q);
   const IO *const pv = reinterpret_cast<const IO *>(a.v);
@@ -81,16 +90,45 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
     // 0. the block inputs first (16-byte loads into registers), then the
     //    state: vector-memory results return in issue order, so the small B x B
     //    work below waits only for the inputs while the state is in flight
-    constexpr int IU = (3 * BMAX * UPR + NT - 1) / NT;  // input units per thread
+    constexpr int IU = ((CONV ? 3 * NRAW : 3 * BMAX) * UPR + NT - 1) / NT;  // input units per thread
     uint4 in_raw[IU];
+    const int W1 = CONV ? a.W - 1 : 0;  // history rows
+    const int NR = W1 + B;              // raw rows per projection (CONV)
+    const size_t C = (size_t)a.H * D;
+    const IO *const hist = reinterpret_cast<const IO *>(a.cache);
+    const int slot = a.slot_idx[req];
 #pragma unroll
     for (int e = 0; e < IU; ++e) {
       const int u = e * NT + t;
       in_raw[e] = make_uint4(0u, 0u, 0u, 0u);
-      if (u < 3 * B * UPR) {
+      if constexpr (CONV) {
+        // projection-major [q, k, v][history rows, block rows][16-byte units]
+        if (u < 3 * NR * UPR) {
+          const int sec = u / (NR * UPR), row = (u / UPR) % NR, cu = u % UPR;
+          const IO *src = row < W1 ? hist + (((size_t)slot * W1 + row) * 3 + sec) * C + (size_t)h * D
+                                   : (sec == 0 ? pq : sec == 1 ? pk : pv) +
+                                         (((size_t)req * B + (row - W1)) * a.H + h) * D;
+          in_raw[e] = *reinterpret_cast<const uint4 *>(src + cu * EPU);
+        }
+      } else if (u < 3 * B * UPR) {
         const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
         const IO *src = which == 0 ? pk : which == 1 ? pq : pv;
         in_raw[e] = *reinterpret_cast<const uint4 *>(src + (((size_t)req * B + r) * a.H + h) * D + cu * EPU);
+      }
+    }
+    // CONV: the head's weights, loaded with the inputs (float4 units)
+    constexpr int WUMAX = CONV ? (3 * D * (WM1 + 1) / 4 + NT - 1) / NT : 1;
+    float4 cw4[WUMAX];
+    if constexpr (CONV) {
+      const int per = D * a.W / 4;  // float4 units per projection
+#pragma unroll
+      for (int e = 0; e < WUMAX; ++e) {
+        const int u = e * NT + t;
+        cw4[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (u < 3 * per) {
+          const int sec = u / per, off = u % per;
+          cw4[e] = *reinterpret_cast<const float4 *>(a.cw[sec] + (size_t)h * D * a.W + 4 * off);
+        }
       }
     }
     float la = 0.f, be = 0.f;
@@ -106,13 +144,19 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
     for (int i = 0; i < RPG; ++i)
       s4[i] = *reinterpret_cast<const float4 *>(S + (size_t)(rg * RPG + i) * D + 4 * cq);
 
-    // 1. block inputs -> LDS as fp32
+    // 1. block inputs -> LDS as fp32 (CONV: the raw rows, convolved below)
 #pragma unroll
     for (int e = 0; e < IU; ++e) {
       const int u = e * NT + t;
-      if (u < 3 * B * UPR) {
-        const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
-        float *dst = which == 0 ? &sX[r][cu * EPU] : which == 1 ? &sX[BMAX + r][cu * EPU] : &sV[r][cu * EPU];
+      if (u < (CONV ? 3 * NR : 3 * B) * UPR) {
+        float *dst;
+        if constexpr (CONV) {
+          const int sec = u / (NR * UPR), row = (u / UPR) % NR, cu = u % UPR;
+          dst = &sRaw[sec][row][cu * EPU];
+        } else {
+          const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
+          dst = which == 0 ? &sX[r][cu * EPU] : which == 1 ? &sX[BMAX + r][cu * EPU] : &sV[r][cu * EPU];
+        }
         const uint4 raw = in_raw[e];
         if constexpr (sizeof(IO) == 2) {
           const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -126,6 +170,14 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
         } else {
           *reinterpret_cast<uint4 *>(dst) = raw;
         }
+      }
+    }
+    if constexpr (CONV) {
+      const int per = D * a.W / 4;
+#pragma unroll
+      for (int e = 0; e < WUMAX; ++e) {
+        const int u = e * NT + t;
+        if (u < 3 * per) *reinterpret_cast<float4 *>(&sCW[u / per][4 * (u % per)]) = cw4[e];
       }
     }
     if (t < 64) {
@@ -142,6 +194,54 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
       }
     }
     __syncthreads();
+
+    if constexpr (CONV) {
+      // COMMIT: the new clean history is the last W - 1 raw rows
+      if (a.mode == 1) {
+        IO *const hw = reinterpret_cast<IO *>(a.cache);
+        for (int u = t; u < 3 * W1 * UPR; u += NT) {
+          const int sec = u / (W1 * UPR), row = (u / UPR) % W1, cu = u % UPR;
+          const float *src = &sRaw[sec][B + row][cu * EPU];
+          IO *dst = hw + (((size_t)slot * W1 + row) * 3 + sec) * C + (size_t)h * D + cu * EPU;
+          if constexpr (sizeof(IO) == 2) {
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(pack_bf16x2(src[0], src[1]), pack_bf16x2(src[2], src[3]),
+                                                         pack_bf16x2(src[4], src[5]), pack_bf16x2(src[6], src[7]));
+          } else {
+            *reinterpret_cast<float4 *>(dst) = *reinterpret_cast<const float4 *>(src);
+          }
+        }
+      }
+      // the convolution: block row j, tap i reads raw row j + i (history first)
+      for (int e = t; e < 3 * B * D; e += NT) {
+        const int sec = e / (B * D), j = (e / D) % B, c = e % D;
+        const float *w = &sCW[sec][c * a.W];
+        float y = 0.f;
+        for (int i = 0; i < a.W; ++i) y = fmaf(w[i], sRaw[sec][j + i][c], y);
+        if (a.act) y = y / (1.f + __expf(-y));
+        float *dst = sec == 0 ? &sX[BMAX + j][c] : sec == 1 ? &sX[j][c] : &sV[j][c];
+        *dst = y;
+      }
+      __syncthreads();
+      if (a.l2) {
+        // q and k rows divided by sqrt(sum y^2 + 1e-6), 16 lanes per row
+        constexpr int GROUPS = NT / 16, PER = D / 16;
+        const int grp = t / 16, sub = t % 16;
+        for (int r0 = 0; r0 < 2 * B; r0 += GROUPS) {  // uniform trip count: every lane joins the DPP sums
+          const int rr = r0 + grp;
+          const bool valid = rr < 2 * B;
+          float *row = sX[valid ? (rr < B ? rr : BMAX + rr - B) : 0];
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) ss = fmaf(row[sub * PER + e], row[sub * PER + e], ss);
+          const float sc = rsqrtf(dpp_sum16(ss) + 1e-6f);
+          if (valid) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) row[sub * PER + e] *= sc;
+          }
+        }
+        __syncthreads();
+      }
+    }
 
     // 2. B x B dot products k_i.k_j and q_l.k_j, 16 lanes per dot (a DPP row),
     //    while the state is still in flight
@@ -334,12 +434,48 @@ static hipError_t launch_step_d(const BlockStepArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)(a.num_req * a.H));
   const dim3 block(StepCfg<D>::NT);
   TimedLaunch tl(K_BLOCK_STEP, st);
-  if (a.B <= 4)
-    hipLaunchKernelGGL((block_step_kernel<IO, D, 4>), grid, block, 0, st, a);
-  else if (a.B <= 8)
-    hipLaunchKernelGGL((block_step_kernel<IO, D, 8>), grid, block, 0, st, a);
+  if (a.conv) {
+    // the serving ShortConv is built for blocks of up to 8 tokens
+    if (a.B <= 4)
+      hipLaunchKernelGGL((block_step_kernel<IO, D, 4, true>), grid, block, 0, st, a);
+    else if (a.B <= 8)
+      hipLaunchKernelGGL((block_step_kernel<IO, D, 8, true>), grid, block, 0, st, a);
+    else
+      return hipErrorInvalidValue;
+  } else if (a.B <= 4) {
+    hipLaunchKernelGGL((block_step_kernel<IO, D, 4, false>), grid, block, 0, st, a);
+  } else if (a.B <= 8) {
+    hipLaunchKernelGGL((block_step_kernel<IO, D, 8, false>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((block_step_kernel<IO, D, 32, false>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+// One workgroup per (document, history row, projection): the row W - 1 - j
+// before the document end, or zeros before its start, into the slot.
+template <typename IO>
+__global__ __launch_bounds__(256) void conv_cache_fill_kernel(ConvCacheArgs a) {
+  const int W1 = a.W - 1;
+  const int doc = blockIdx.x / (W1 * 3), j = (blockIdx.x / 3) % W1, sec = blockIdx.x % 3;
+  const int s = a.cu[doc], e = a.cu[doc + 1];
+  const int t = e - W1 + j;
+  constexpr int EPU = 16 / sizeof(IO);
+  const IO *src = reinterpret_cast<const IO *>(a.x[sec]) + (size_t)max(t, 0) * a.C;
+  IO *dst = reinterpret_cast<IO *>(a.cache) + (((size_t)a.slot[doc] * W1 + j) * 3 + sec) * a.C;
+  for (int u = threadIdx.x; u < a.C / EPU; u += 256) {
+    const uint4 v = t >= s ? reinterpret_cast<const uint4 *>(src)[u] : make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4 *>(dst)[u] = v;
+  }
+}
+
+hipError_t launch_conv_cache_fill(const ConvCacheArgs &a, hipStream_t st) {
+  if (a.num_docs == 0 || a.W <= 1) return hipSuccess;
+  const dim3 grid((unsigned)(a.num_docs * (a.W - 1) * 3));
+  if (a.bf16)
+    hipLaunchKernelGGL(conv_cache_fill_kernel<u16>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((block_step_kernel<IO, D, 32>), grid, block, 0, st, a);
+    hipLaunchKernelGGL(conv_cache_fill_kernel<float>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -135,24 +135,27 @@ flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
   if (!slot_idx || !pool || !q || !k || !v || !alpha || !beta)
     return fail(FLARE_ERR_NULL, "block_step: a required pointer is NULL");
   if (mode == FLARE_BLOCK_EVAL && !o) return fail(FLARE_ERR_NULL, "EVAL needs an output buffer");
-  if (slot_idx_host) {
-    // distinct and in range: counting sort over the slot range
-    if (num_slots > (1 << 26)) return fail(FLARE_ERR_SHAPE, "num_slots too large to check");
-    unsigned char *seen = new unsigned char[(size_t)num_slots]();
-    for (int32_t r = 0; r < num_req; ++r) {
-      const int32_t sl = slot_idx_host[r];
-      if (sl < 0 || sl >= num_slots) {
-        delete[] seen;
-        return fail(FLARE_ERR_SHAPE, "slot_idx[%d] = %d outside [0, %d)", r, sl, num_slots);
-      }
-      if (seen[sl]) {
-        delete[] seen;
-        return fail(FLARE_ERR_SHAPE, "slot %d used by two requests", sl);
-      }
-      seen[sl] = 1;
+  return check_slots_host(num_req, slot_idx_host, num_slots);
+}
+
+flare_status check_slots_host(int32_t n, const int32_t *slot_host, int32_t num_slots) {
+  if (!slot_host) return FLARE_OK;
+  // distinct and in range: counting sort over the slot range
+  if (num_slots > (1 << 26)) return fail(FLARE_ERR_SHAPE, "num_slots too large to check");
+  unsigned char *seen = new unsigned char[(size_t)num_slots]();
+  for (int32_t r = 0; r < n; ++r) {
+    const int32_t sl = slot_host[r];
+    if (sl < 0 || sl >= num_slots) {
+      delete[] seen;
+      return fail(FLARE_ERR_SHAPE, "slot_idx[%d] = %d outside [0, %d)", r, sl, num_slots);
     }
-    delete[] seen;
+    if (seen[sl]) {
+      delete[] seen;
+      return fail(FLARE_ERR_SHAPE, "slot %d used by two requests", sl);
+    }
+    seen[sl] = 1;
   }
+  delete[] seen;
   return FLARE_OK;
 }
 

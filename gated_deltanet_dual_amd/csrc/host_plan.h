@@ -58,6 +58,9 @@ bool bwd_uses_scan_pack(const flare_gdn_shape *s);
 size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
 bool fwd_uses_chunk_matrices(const flare_gdn_shape *s);
 
+// Slots distinct and in [0, num_slots) (no check when slot_host is NULL).
+flare_status check_slots_host(int32_t n, const int32_t *slot_host, int32_t num_slots);
+
 // Serving step: slots distinct and in range when the host copy is given.
 flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,
                               const int32_t *slot_idx_host, const float *pool,

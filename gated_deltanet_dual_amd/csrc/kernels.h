@@ -17,8 +17,26 @@ struct BlockStepArgs {
   const float *alpha, *beta;
   void *o;
   float *cand;
+  // conv != 0: q, k, v are the raw projections; each goes through the
+  // width-W ShortConv whose W - 1 earlier rows come from the request's clean
+  // history cache [n_slots][W - 1][3][H * D] (io), then SiLU (act) and, for q
+  // and k, the per-row L2 norm (l2); COMMIT keeps the last W - 1 raw rows as
+  // the new history
+  int conv, W, act, l2;
+  void *cache;
+  const float *cw[3];  // [H * D][W] per projection (q, k, v)
 };
 hipError_t launch_block_step(const BlockStepArgs &a, hipStream_t st);
+
+// the clean history of each document after a prefill: cache[slot_i][j][s] =
+// x_s[end_i - (W - 1) + j] (zero before the document start)
+struct ConvCacheArgs {
+  int num_docs, C, W, bf16;
+  const int32_t *cu, *slot;
+  const void *x[3];
+  void *cache;
+};
+hipError_t launch_conv_cache_fill(const ConvCacheArgs &a, hipStream_t st);
 
 // AR-Trust rollback: pool[slot[r]] = cand[r][accepted[r] - 1] for accepted
 // counts clamped to [0, K] (0 leaves the slot)

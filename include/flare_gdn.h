@@ -225,6 +225,49 @@ flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
                                   const float *alpha, const float *beta,
                                   void *o, int32_t mode, void *stream);
 
+/* The serving step with the ShortConv in front (Key designs item 3 for the
+ * convolution, item 4 for the pool): flare_gdn_block_step whose q, k, v are
+ * the raw projections xq, xk, xv [num_req, B, H, d] io.  Each request keeps
+ * its clean history -- the last width-1 clean projection rows -- in
+ *   conv_cache   io [num_slots, width-1, 3 (q, k, v), H * d], slot slot_idx[r]
+ *                (may be NULL when width = 1)
+ * so the block's taps before its start read that clean history and the taps
+ * inside read the block itself (EVAL: the noisy draft; COMMIT: the fixed
+ * block), then SiLU (activation = 1) and, with qk_l2norm, q and k divided per
+ * (token, head) by sqrt(sum x^2 + 1e-6).  COMMIT also replaces the history
+ * with the last width-1 raw rows of history + block; EVAL writes neither the
+ * state pool nor the cache.
+ *   weight[3]    fp32 [H * d, width] per projection, tap width-1 on the
+ *                current token (as flare_shortconv_dual); no bias
+ * Requirements: as flare_gdn_block_step, shape->flags = 0, width in [1, 8],
+ * block_size <= 8 (FLARE_ERR_UNSUPPORTED otherwise). */
+flare_status flare_gdn_block_step_conv(int32_t num_req, const int32_t *slot_idx,
+                                       const int32_t *slot_idx_host,
+                                       float *state_pool, void *conv_cache,
+                                       int32_t num_slots,
+                                       const flare_gdn_shape *shape,
+                                       int32_t width,
+                                       const float *const weight[3],
+                                       int32_t activation, int32_t qk_l2norm,
+                                       const void *xq, const void *xk,
+                                       const void *xv, const float *alpha,
+                                       const float *beta, void *o, int32_t mode,
+                                       void *stream);
+
+/* After a prefill (flare_gdn_dual_fwd_pool): each document's clean history,
+ * conv_cache[doc_slot[i]][j][s] = x[s][end_i - (width-1) + j], zero for rows
+ * before the document start.  x[3]: the clean q, k, v projections
+ * [T, heads * head_dim] io of the prefilled batch; doc_slot: device int32
+ * [N]; doc_slot_host optional (range and duplicates checked).  Nothing to do
+ * for width = 1. */
+flare_status flare_conv_cache_fill(const flare_varlen *varlen, int32_t heads,
+                                   int32_t head_dim, int32_t width,
+                                   int32_t io_dtype, const void *const x[3],
+                                   const int32_t *doc_slot,
+                                   const int32_t *doc_slot_host,
+                                   void *conv_cache, int32_t num_slots,
+                                   void *stream);
+
 /* AR-Trust (Key designs item 4: the noisy stream drafts K tokens, the clean
  * stream verifies them in one parallel pass, and a partial acceptance of the
  * first r < K tokens is rolled back without recomputation by keeping the K

@@ -270,3 +270,30 @@ def test_fwd_pool_validation(L):
     assert call(n_slots=1) == 2          # two documents, one slot
     assert call(read=2) == 2
     assert call(slot_host=np.array([1, 4], np.int32)) == 2  # slot out of range
+
+
+def test_block_step_conv_and_cache_fill_validation(L):
+    A3 = ctypes.c_void_p * 3
+    W3 = A3(FAKE, FAKE, FAKE)
+    host = np.array([3, 1], np.int32)
+
+    def step(B=4, width=4, flags=0, act=0, l2=1, cache=FAKE, w=W3):
+        shape = g._shape(2, 16, B, g.F32, flags)
+        return L.flare_gdn_block_step_conv(2, FAKE, host.ctypes.data, FAKE, cache, 8, ctypes.byref(shape), width, w,
+                                           act, l2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None)
+
+    assert step(B=16) == 4               # blocks of up to 8 tokens with the conv
+    assert step(width=9) == 4
+    assert step(flags=1) == 4            # the L2 step is its own argument
+    assert step(act=3) == 4
+    assert step(l2=2) == 4
+    assert step(cache=None) == 1         # a history is needed for width > 1
+    assert step(w=A3(FAKE, None, FAKE)) == 1
+    v = varlen([0, 10, 30], [4, 8])
+    dup = np.array([2, 2], np.int32)
+    fill = lambda **k: L.flare_conv_cache_fill(ctypes.byref(v), k.get("H", 2), 16, k.get("W", 4), g.BF16, W3, FAKE,
+                                               k.get("host", host).ctypes.data, FAKE, k.get("slots", 8), None)
+    assert fill(host=dup) == 2
+    assert fill(slots=1) == 2
+    assert fill(W=0) == 4
+    assert L.flare_conv_cache_fill(ctypes.byref(v), 2, 16, 1, g.BF16, W3, FAKE, None, None, 8, None) == 0  # W = 1
