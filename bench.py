@@ -1,7 +1,7 @@
 """Benchmark of the dual-stream Gated DeltaNet layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-components] [--only step|infer|serve|conv|layer|copy] [--json-out PATH]
+                    [--no-components] [--only step|infer|serve|conv|layer|routes|copy] [--json-out PATH]
 
 A step is one pass of the layer's hot path over one batch of the headline
 workload -- 4 documents x 8192 tokens (prompt 2048, response in blocks of
@@ -94,7 +94,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
-    p.add_argument("--only", choices=["step", "infer", "serve", "conv", "layer", "copy"], default=None,
+    p.add_argument("--only", choices=["step", "infer", "serve", "conv", "layer", "routes", "copy"], default=None,
                    help="run one part only (copy: a plain 1 GiB device copy, the reference "
                         "transfer for HBM byte counters)")
     p.add_argument("--json-out", default=None)
@@ -196,6 +196,8 @@ def main():
         comps["shortconv"], comps["shortconv_bwd"] = bench_conv(torch, g, wl, dev, timer, up, args)
     if not args.no_components and args.only in (None, "layer"):
         comps["packed_layer"] = bench_packed_layer(torch, g, wl, dev, timer, up, args)
+    if not args.no_components and args.only in (None, "routes"):
+        comps["routes"] = bench_routes(torch, g, wl, dev, timer, up, args)
     if comps:
         result["components"] = comps
 
@@ -585,6 +587,53 @@ def bench_packed_layer(torch, g, wl, dev, timer, up, args):
     for k, ms in res.items():
         out[k] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
     out["fused_speedup_fwd"] = res["unfused_fwd"] / res["fused_fwd"]
+    return out
+
+
+def bench_routes(torch, g, wl, dev, timer, up, args):
+    """The two ways to give every noisy block its clean boundary state, at the
+    dual workload (4 x 4096 tokens, prompt 1024, H=16, d=128, bf16), blocks of
+    4 to 32: the masked route (flare_gdn_dual_fwd: boundary states rebuilt on
+    chip from chunk-start states, none stored) against chunk-then-refine
+    (flare_gdn_dual_fwd_route1: every boundary state stored, then every noisy
+    block refined from it).  Both inference forwards; route I also writes the
+    chunk-start states it needs."""
+    log("bench: masked route vs chunk-then-refine, 4 x 4096 tokens, H=16, d=128, B = 4..32")
+    bf = torch.bfloat16
+    out = {"workload": "dual-stream GDN forward, 4 x 4096 tokens (prompt 1024), H=16, d=128, bf16"}
+    n = max(args.steps // 2, 3)
+    for B in (4, 8, 16, 32):
+        inp = wl.dual_bf16(block_size=B)
+        H, d, T = inp.H, 128, inp.T
+        vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+        a10 = [up(inp.q, True), up(inp.k, True), up(inp.v, True), up(inp.alpha), up(inp.beta),
+               up(inp.qn, True), up(inp.kn, True), up(inp.vn, True), up(inp.alpha_n), up(inp.beta_n)]
+        o = torch.empty((T, H, d), dtype=bf, device=dev)
+        on = torch.empty_like(o)
+        fws = torch.empty((max(g.workspace_bytes(vl, H, d, B, g.BF16), 256),), dtype=torch.uint8, device=dev)
+        shp = g._shape(H, d, B, g.BF16)
+        r1_bytes = int(g.lib().flare_gdn_route1_workspace_size(vl.ref(), ctypes.byref(shp)))
+        rws = torch.empty((r1_bytes,), dtype=torch.uint8, device=dev)
+        ckpt = torch.empty((T // g.chunk_size() + vl.num_docs, H, d, d), dtype=torch.float32, device=dev)
+        masked = lambda: g.gdn_dual_fwd(vl, *a10, B, out=(o, on), want_h_final=False, workspace=fws)
+        route1 = lambda: g.gdn_dual_fwd_route1(vl, *a10, B, out=(o, on), ckpt=ckpt, workspace=rws,
+                                               want_h_final=False)
+        row = {}
+        for name, fn in (("masked", masked), ("route1", route1)):
+            for _ in range(max(args.warmup, 1)):
+                fn()
+            torch.cuda.synchronize()
+            key = "%s_B%d" % (name, B)
+            for _ in range(n):
+                timer.run(key, fn)
+            torch.cuda.synchronize()
+            row[name + "_ms"] = timer.avg_ms(key)
+        row["route1_workspace_bytes"] = r1_bytes
+        row["masked_workspace_bytes"] = int(fws.numel())
+        row["route1_over_masked"] = row["route1_ms"] / row["masked_ms"]
+        out["B%d" % B] = row
+        del a10, o, on, fws, rws, ckpt
+        torch.cuda.empty_cache()
     return out
 
 

@@ -16,7 +16,7 @@ import os
 
 import numpy as np
 
-__all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_fwd_pool", "gdn_dual_bwd",
+__all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_fwd_pool", "gdn_dual_fwd_route1", "gdn_dual_bwd",
            "block_step", "block_step_conv", "conv_cache_fill", "gdn_verify", "gdn_scatter", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
            "qkv_prologue_bwd", "qkv_prologue_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
            "QK_L2NORM", "F32", "BF16"]
@@ -83,6 +83,10 @@ def lib():
     L.flare_gdn_dual_bwd.restype = ctypes.c_int
     L.flare_gdn_block_step.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, I32, P]
     L.flare_gdn_block_step.restype = ctypes.c_int
+    L.flare_gdn_route1_workspace_size.argtypes = [VP, SP]
+    L.flare_gdn_route1_workspace_size.restype = SZ
+    L.flare_gdn_dual_fwd_route1.argtypes = [VP, SP] + [P] * 10 + [P, P, P, P, P, P, SZ, P]
+    L.flare_gdn_dual_fwd_route1.restype = ctypes.c_int
     L.flare_gdn_dual_fwd_pool.argtypes = [VP, SP] + [P] * 10 + [P, P, P, I32, I32, P, P, P, I32, P, SZ, P]
     L.flare_gdn_dual_fwd_pool.restype = ctypes.c_int
     L.flare_gdn_block_step_conv.argtypes = [I32, P, P, P, P, I32, SP, I32, A3, I32, I32, P, P, P, P, P, P, I32, P]
@@ -226,6 +230,35 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
                                     _ptr(hf), _ptr(ck), 1, _ptr(workspace),
                                     workspace.numel() if workspace is not None else 0, _stream(q.device)))
     return o, on, hf, ck
+
+
+def gdn_dual_fwd_route1(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size, h0=None,
+                        scale=0.0, out=None, ckpt=None, workspace=None, want_h_final=True):
+    """The chunk-then-refine route for the dual forward: the clean stream with
+    its chunk-start states, every block-boundary state materialised, every
+    noisy block refined from it.  Returns (o, on, h_final, ckpt)."""
+    torch = _torch()
+    T, H, d = q.shape
+    shp = _shape(H, d, block_size, _io_of(q), 0, scale)
+    if out is None:
+        o = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+        on = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    else:
+        o, on = out
+    hf = torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=q.device) if want_h_final else None
+    if ckpt is None:
+        nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1)
+        ckpt = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=q.device)
+    need = int(lib().flare_gdn_route1_workspace_size(varlen.ref(), ctypes.byref(shp)))
+    if need == 0:
+        raise FlareError(4, "route1: unsupported shape")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _check(lib().flare_gdn_dual_fwd_route1(varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                           _ptr(beta), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(alpha_n), _ptr(beta_n),
+                                           _ptr(h0), _ptr(o), _ptr(on), _ptr(hf), _ptr(ckpt), _ptr(workspace),
+                                           workspace.numel(), _stream(q.device)))
+    return o, on, hf, ckpt
 
 
 def gdn_dual_fwd_pool(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size, doc_slot,

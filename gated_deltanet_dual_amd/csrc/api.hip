@@ -102,6 +102,69 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shap
                   ckpt, ckpt_stride_chunks, workspace, workspace_bytes, stream);
 }
 
+size_t flare_gdn_route1_workspace_size(const flare_varlen *varlen, const flare_gdn_shape *shape) {
+  VarlenInfo vi;
+  if (check_fwd_common(varlen, shape, &vi) != FLARE_OK) return 0;
+  if (shape->d_k != shape->d_v || (shape->d_k != 16 && shape->d_k != 128) || shape->flags != 0) return 0;
+  return route1_workspace_bytes(vi, shape, route1_num_blocks(varlen, shape->block_size));
+}
+
+flare_status flare_gdn_dual_fwd_route1(const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q,
+                                       const void *k, const void *v, const float *alpha, const float *beta,
+                                       const void *qn, const void *kn, const void *vn, const float *alpha_n,
+                                       const float *beta_n, const float *h0, void *o, void *on, float *h_final,
+                                       float *ckpt, void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  VarlenInfo vi;
+  flare_status st = check_fwd_common(varlen, shape, &vi);
+  if (st != FLARE_OK) return st;
+  if (shape->flags != 0) return fail(FLARE_ERR_UNSUPPORTED, "route1: no flags (normalise q, k beforehand)");
+  if (shape->d_k != shape->d_v || (shape->d_k != 16 && shape->d_k != 128))
+    return fail(FLARE_ERR_UNSUPPORTED, "route1: d_k = d_v in {16, 128}");
+  if (vi.total_tokens > 0 &&
+      (!q || !k || !v || !alpha || !beta || !qn || !kn || !vn || !alpha_n || !beta_n || !o || !on || !ckpt))
+    return fail(FLARE_ERR_NULL, "gdn_dual_fwd_route1: a required pointer is NULL (the chunk-start states too)");
+  const int64_t nblk = route1_num_blocks(varlen, shape->block_size);
+  const size_t need = route1_workspace_bytes(vi, shape, nblk);
+  if (vi.total_tokens > 0 && (!workspace || workspace_bytes < need))
+    return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (vi.total_tokens == 0) return FLARE_OK;
+  FwdArgs a{};
+  a.num_docs = varlen->num_docs;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.B = shape->block_size;
+  a.flags = 0;
+  a.bf16 = shape->io_dtype == FLARE_BF16;
+  a.ckpt_stride = 1;
+  a.scale = resolve_scale(shape);
+  a.cu = varlen->cu_seqlens;
+  a.plen = varlen->prompt_lens;
+  a.q = q; a.k = k; a.v = v; a.qn = qn; a.kn = kn; a.vn = vn;
+  a.alpha = alpha; a.beta = beta; a.alpha_n = alpha_n; a.beta_n = beta_n;
+  a.h0 = h0; a.o = o; a.on = on; a.h_final = h_final; a.ckpt = ckpt;
+  a.T = vi.total_tokens;
+  // workspace: the forward's, the boundary states, the plan arrays
+  char *w = reinterpret_cast<char *>(workspace);
+  const size_t fwd = fwd_workspace_bytes(vi, shape);
+  a.workspace = fwd > 0 ? reinterpret_cast<float *>(w) : nullptr;
+  w += (fwd + 255) & ~(size_t)255;
+  Route1Plan pl{};
+  pl.n_blocks = nblk;
+  pl.bstates = reinterpret_cast<float *>(w);
+  w += ((size_t)nblk * a.H * a.D * a.D * 4 + 255) & ~(size_t)255;
+  int32_t *ip = reinterpret_cast<int32_t *>(w);
+  pl.boff = ip; ip += a.num_docs;
+  pl.plen_all = ip; ip += a.num_docs;
+  pl.r0m = ip; ip += nblk;
+  pl.cm = ip; ip += nblk;
+  pl.slm = ip; ip += nblk;
+  pl.r0r = ip; ip += nblk;
+  pl.cr = ip;
+  return hip_status(launch_route1(a, pl, (hipStream_t)stream), "gdn_dual_fwd_route1 launch");
+}
+
 flare_status flare_gdn_dual_fwd_pool(const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q,
                                      const void *k, const void *v, const float *alpha, const float *beta,
                                      const void *qn, const void *kn, const void *vn, const float *alpha_n,

@@ -84,7 +84,12 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
   const IO *const pv = reinterpret_cast<const IO *>(a.v);
   const float *const pal = a.alpha, *const pbe = a.beta;
 
-  float *S = a.pool + ((size_t)a.slot_idx[req] * a.H + h) * D * D;
+  const int slot = a.slot_idx ? a.slot_idx[req] : req;
+  float *S = a.pool + ((size_t)slot * a.H + h) * D * D;
+  // table mode: the request's first token row and its number of real tokens
+  const int64_t rbase = a.row0 ? (int64_t)a.row0[req] : (int64_t)req * B;
+  const int cnt = a.count ? a.count[req] : B;
+  auto trow = [&](int r) { return rbase + (r < cnt ? r : max(cnt - 1, 0)); };  // loads stay on real rows
   float4 s4[RPG];
   {
     // 0. the block inputs first (16-byte loads into registers), then the
@@ -96,7 +101,6 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
     const int NR = W1 + B;              // raw rows per projection (CONV)
     const size_t C = (size_t)a.H * D;
     const IO *const hist = reinterpret_cast<const IO *>(a.cache);
-    const int slot = a.slot_idx[req];
 #pragma unroll
     for (int e = 0; e < IU; ++e) {
       const int u = e * NT + t;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
       } else if (u < 3 * B * UPR) {
         const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
         const IO *src = which == 0 ? pk : which == 1 ? pq : pv;
-        in_raw[e] = *reinterpret_cast<const uint4 *>(src + (((size_t)req * B + r) * a.H + h) * D + cu * EPU);
+        in_raw[e] = *reinterpret_cast<const uint4 *>(src + ((size_t)trow(r) * a.H + h) * D + cu * EPU);
       }
     }
     // CONV: the head's weights, loaded with the inputs (float4 units)
@@ -132,8 +136,8 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
       }
     }
     float la = 0.f, be = 0.f;
-    if (t < B) {
-      const size_t gi = ((size_t)req * B + t) * a.H + h;
+    if (t < B && t < cnt) {  // tokens past the count: alpha = 1, beta = 0 (identity)
+      const size_t gi = (size_t)trow(t) * a.H + h;
       la = __logf(pal[gi]);
       be = pbe[gi];
     }
@@ -353,6 +357,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
       IO *o = reinterpret_cast<IO *>(a.o);
       for (int e = t; e < B * UPR; e += NT) {
         const int l = e / UPR, c0 = (e % UPR) * EPU;
+        if (l >= cnt) continue;                  // no output for identity tokens
         const int end = a.mode == 0 ? last : l;  // EVAL reads the block end
         const float ge = __expf(sG[end]);
         float acc[EPU];
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
 #pragma unroll
           for (int c = 0; c < EPU; ++c) acc[c] += wq * sU[j][c0 + c];
         }
-        IO *dst = o + (((size_t)req * B + l) * a.H + h) * D + c0;
+        IO *dst = o + ((size_t)trow(l) * a.H + h) * D + c0;
         if constexpr (sizeof(IO) == 2) {
           uint4 w;
           w.x = pack_bf16x2(s * acc[0], s * acc[1]);
@@ -408,6 +413,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
 
     // 8. COMMIT: rank-B update of the register-resident state, written back
     if (a.mode == 1) {
+      float *const Sdst = a.pool_out ? a.pool_out + ((size_t)req * a.H + h) * D * D : S;
       const float ge = __expf(sG[last]);
       float wj[BMAX];
 #pragma unroll
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
           const float4 u = *reinterpret_cast<const float4 *>(&sU[j][4 * cq]);
           n.x += kk * u.x; n.y += kk * u.y; n.z += kk * u.z; n.w += kk * u.w;
         }
-        *reinterpret_cast<float4 *>(S + (size_t)row * D + 4 * cq) = n;
+        *reinterpret_cast<float4 *>(Sdst + (size_t)row * D + 4 * cq) = n;
       }
     }
   }

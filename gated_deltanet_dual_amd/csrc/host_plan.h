@@ -58,6 +58,12 @@ bool bwd_uses_scan_pack(const flare_gdn_shape *s);
 size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
 bool fwd_uses_chunk_matrices(const flare_gdn_shape *s);
 
+// The chunk-then-refine route: the number of response blocks (from the host
+// copies of the document layout) and its workspace, laid out as the forward's
+// workspace, the block-boundary states, then the int32 plan arrays.
+int64_t route1_num_blocks(const flare_varlen *v, int32_t block_size);
+size_t route1_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s, int64_t n_blocks);
+
 // Slots distinct and in [0, num_slots) (no check when slot_host is NULL).
 flare_status check_slots_host(int32_t n, const int32_t *slot_host, int32_t num_slots);
 

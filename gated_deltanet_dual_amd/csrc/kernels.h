@@ -25,6 +25,13 @@ struct BlockStepArgs {
   int conv, W, act, l2;
   void *cache;
   const float *cw[3];  // [H * D][W] per projection (q, k, v)
+  // table mode (not with conv), all optional: request r's tokens are the rows
+  // row0[r] .. row0[r] + B - 1 of token-major [T, H, D] inputs (gates
+  // [T, H]); only the first count[r] are real (the rest are identity updates,
+  // their outputs not written); slot_idx NULL reads state r; COMMIT writes
+  // the new state to pool_out[r] instead of in place
+  const int32_t *row0, *count;
+  float *pool_out;
 };
 hipError_t launch_block_step(const BlockStepArgs &a, hipStream_t st);
 
@@ -96,6 +103,16 @@ struct FwdArgs {
   const int32_t *state_slot;
 };
 hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
+
+// the chunk-then-refine route (route1.hip): f as for launch_gdn_fwd with the
+// chunk-start states f.ckpt required; the plan's arrays live in the workspace
+struct Route1Plan {
+  int64_t n_blocks;  // response blocks over all documents
+  float *bstates;    // [n_blocks, H, D, D] the block-boundary states
+  int32_t *boff, *plen_all;                   // [N]
+  int32_t *r0m, *cm, *slm, *r0r, *cr;         // [n_blocks]
+};
+hipError_t launch_route1(const FwdArgs &f, const Route1Plan &pl, hipStream_t st);
 // bf16 io at d = 128 without flags: the forward's pre-pass (chunk matrices
 // `cmat` -> scan hand-over `pack`, gdn_fwd_pre.hip) and its output pass
 // (chunk-start states -> o, o~, gdn_fwd_out.hip)

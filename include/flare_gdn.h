@@ -147,6 +147,29 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen,
                                 int32_t ckpt_stride_chunks, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* The chunk-then-refine route for the same forward (Key designs item 2 and
+ * the pages' comparison of the two ways to give every noisy block its clean
+ * boundary state): the clean stream with its chunk-start states (ckpt,
+ * required, flare_gdn_dual_ckpt_size(..., 1) bytes), then every block-boundary
+ * state materialised in the workspace, then every noisy block refined from its
+ * state.  Same results as flare_gdn_dual_fwd (o, on, h_final) at O(L / B)
+ * states of memory; built for comparing the two routes.  Requirements as
+ * flare_gdn_dual_fwd, plus d_k = d_v in {16, 128} and no flags; the
+ * workspace is flare_gdn_route1_workspace_size bytes, 256-byte aligned. */
+size_t flare_gdn_route1_workspace_size(const flare_varlen *varlen,
+                                       const flare_gdn_shape *shape);
+flare_status flare_gdn_dual_fwd_route1(const flare_varlen *varlen,
+                                       const flare_gdn_shape *shape,
+                                       const void *q, const void *k,
+                                       const void *v, const float *alpha,
+                                       const float *beta, const void *qn,
+                                       const void *kn, const void *vn,
+                                       const float *alpha_n,
+                                       const float *beta_n, const float *h0,
+                                       void *o, void *on, float *h_final,
+                                       float *ckpt, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /* Prefill into the serving pool (Key designs item 4: the serving pool holds
  * one causal state per request): flare_gdn_dual_fwd with every document's
  * state kept in a pool slot instead of the h0 / h_final arrays.

@@ -297,3 +297,33 @@ def test_block_step_conv_and_cache_fill_validation(L):
     assert fill(slots=1) == 2
     assert fill(W=0) == 4
     assert L.flare_conv_cache_fill(ctypes.byref(v), 2, 16, 1, g.BF16, W3, FAKE, None, None, 8, None) == 0  # W = 1
+
+
+def test_route1_workspace_and_validation(L):
+    # documents of 40 and 80 tokens with prompts 8 and 8, blocks of 4: 8 + 18
+    # response blocks; the size covers the forward's workspace, one fp32 state
+    # per block and the per-document / per-block tables
+    v = varlen([0, 40, 120], [8, 8])
+    shape = g._shape(2, 16, 4, g.F32)
+    need = L.flare_gdn_route1_workspace_size(ctypes.byref(v), ctypes.byref(shape))
+    fwd = L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(shape), 0)
+    r = lambda x: (x + 255) // 256 * 256
+    assert need == r(fwd) + r(26 * 2 * 16 * 16 * 4) + r((2 * 2 + 5 * 26) * 4) + 256
+    # no response tokens: no block states
+    v0 = varlen([0, 40], [40])
+    need0 = L.flare_gdn_route1_workspace_size(ctypes.byref(v0), ctypes.byref(shape))
+    assert need0 == r(L.flare_gdn_dual_workspace_size(ctypes.byref(v0), ctypes.byref(shape), 0)) + r(2 * 4) + 256
+    # unsupported shapes report 0 and fail the call
+    odd = g._shape(2, 16, 4, g.F32, g.QK_L2NORM)
+    assert L.flare_gdn_route1_workspace_size(ctypes.byref(v), ctypes.byref(odd)) == 0
+    P10 = [FAKE] * 10
+
+    def call(shp=shape, ckpt=FAKE, ws=FAKE, nbytes=need):
+        return L.flare_gdn_dual_fwd_route1(ctypes.byref(v), ctypes.byref(shp), *P10, None, FAKE, FAKE, None, ckpt,
+                                           ws, nbytes, None)
+
+    assert call(ckpt=None) == 1             # the chunk-start states are required
+    assert call(nbytes=need - 1) == 5
+    assert call(ws=None) == 5
+    assert call(ws=ctypes.c_void_p(FAKE.value + 64)) == 5  # misaligned
+    assert call(shp=odd) == 4
