@@ -152,14 +152,18 @@ flare_status flare_gdn_dual_fwd_route1(const flare_varlen *varlen, const flare_g
   w += (fwd + 255) & ~(size_t)255;
   Route1Plan pl{};
   pl.n_blocks = nblk;
+  pl.n_windows = route1_num_windows(varlen);  // at most one per block
   pl.bstates = reinterpret_cast<float *>(w);
   w += ((size_t)nblk * a.H * a.D * a.D * 4 + 255) & ~(size_t)255;
   int32_t *ip = reinterpret_cast<int32_t *>(w);
   pl.boff = ip; ip += a.num_docs;
+  pl.woff = ip; ip += a.num_docs;
   pl.plen_all = ip; ip += a.num_docs;
-  pl.r0m = ip; ip += nblk;
-  pl.cm = ip; ip += nblk;
-  pl.slm = ip; ip += nblk;
+  pl.wrow = ip; ip += nblk;
+  pl.wcnt = ip; ip += nblk;
+  pl.wslot = ip; ip += nblk;
+  pl.wlo = ip; ip += nblk;
+  pl.wg0 = ip; ip += nblk;
   pl.r0r = ip; ip += nblk;
   pl.cr = ip;
   return hip_status(launch_route1(a, pl, (hipStream_t)stream), "gdn_dual_fwd_route1 launch");

@@ -39,6 +39,7 @@ template <int D> struct StepCfg {
   static constexpr int NRG = NT / NCQ;            // row groups: adjacent lanes of one quad
   static constexpr int RPG = D / NRG;             // rows per group (rows rg * RPG + i)
   static constexpr int G = D >= 128 ? 2 : 8;      // vectors per pass (few: registers, occupancy)
+  static constexpr int MINB = D >= 128 ? 4 : 8;   // workgroups per CU the registers must allow
   static_assert(NRG == 8 || NRG == 16, "row groups are reduced over 8 or 16 lanes");
 };
 
@@ -55,7 +56,9 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
 // CONV: the block inputs are raw projections that go through the serving
 // ShortConv first (the request's W - 1 clean history rows, then the block;
 // SiLU; q/k L2 norm) -- see BlockStepArgs
-template <typename IO, int D, int BMAX, bool CONV>
+// KIND: 0 = EVAL, 1 = COMMIT, 2 = the token-wise state writers (VERIFY and
+// BOUNDARIES); the readers carry no state-update registers
+template <typename IO, int D, int BMAX, bool CONV, int KIND>
 __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArgs a) {
   using Cfg = StepCfg<D>;
   constexpr int NT = Cfg::NT, NRG = Cfg::NRG, RPG = Cfg::RPG, G = Cfg::G;
@@ -64,16 +67,21 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
   constexpr int UPR = D / EPU;           // 16-byte units per row
   constexpr int WM1 = 7;                 // most history rows (W <= 8)
   constexpr int NRAW = CONV ? WM1 + BMAX : 1;
-  const int B = a.B;
+  const int req = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  // table mode: the request's number of real tokens; a BOUNDARIES window
+  // runs over exactly the tokens before its last block start (possibly none)
+  const int cnt = a.count ? a.count[req] : a.B;
+  const int B = KIND == 2 && a.mode == 3 ? cnt : a.B;
   const int t = threadIdx.x;
   const int rg = t % NRG, cq = t / NRG;
-  const int req = blockIdx.x / a.H, h = blockIdx.x % a.H;
 
   __shared__ __align__(16) float sX[NV][D];   // k_0..k_{B-1} at 0.., q_0..q_{B-1} at BMAX..
   __shared__ __align__(16) float sV[BMAX][D];
   __shared__ __align__(16) float sW[NV][D];   // S^T x for every x in sX
   __shared__ __align__(16) float sU[BMAX][D];
-  __shared__ float sKK[BMAX][BMAX + 1], sQK[BMAX][BMAX + 1], sT[BMAX][BMAX + 1];
+  // B x B coefficients, rows 16-byte aligned for broadcast reads: k.k then the
+  // UT system A, q.k then the output weights P, the inverse T
+  __shared__ __align__(16) float sKK[BMAX][BMAX], sQK[BMAX][BMAX], sT[BMAX][BMAX];
   __shared__ float sG[BMAX], sBeta[BMAX];
   // CONV: the raw rows of q, k, v (history, then the block) as fp32, and the
   // head's conv weights [projection][channel * W + tap]
@@ -86,9 +94,8 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
 
   const int slot = a.slot_idx ? a.slot_idx[req] : req;
   float *S = a.pool + ((size_t)slot * a.H + h) * D * D;
-  // table mode: the request's first token row and its number of real tokens
+  // table mode: the request's first token row
   const int64_t rbase = a.row0 ? (int64_t)a.row0[req] : (int64_t)req * B;
-  const int cnt = a.count ? a.count[req] : B;
   auto trow = [&](int r) { return rbase + (r < cnt ? r : max(cnt - 1, 0)); };  // loads stay on real rows
   float4 s4[RPG];
   {
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
 
     if constexpr (CONV) {
       // COMMIT: the new clean history is the last W - 1 raw rows
-      if (a.mode == 1) {
+      if constexpr (KIND == 1) {
         IO *const hw = reinterpret_cast<IO *>(a.cache);
         for (int u = t; u < 3 * W1 * UPR; u += NT) {
           const int sec = u / (W1 * UPR), row = (u / UPR) % W1, cu = u % UPR;
@@ -271,21 +278,38 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
     }
     __syncthreads();
 
-    // 3. T = (I + A)^-1 by forward substitution, one lane per column (the other
-    //    threads go on to the reduction); the column lives in sT and is read
-    //    back only by the thread that wrote it.
-    if (t < B) {
+    // 2b. the coefficients, in place and zero outside the block:
+    //     A[i][m] = (G_i / G_m) b_m k_i.k_m for m < i (the UT system) and
+    //     P[l][j] = (G_e / G_j) b_j q_l.k_j for j <= e, e the row the output
+    //     reads (the block end for EVAL, l otherwise)
+    for (int e = t; e < BMAX * BMAX; e += NT) {
+      const int i = e / BMAX, m = e % BMAX;
+      float A = 0.f, P = 0.f;
+      if (i < B && m < B) {
+        const float bm = sBeta[m];
+        if (m < i) A = __expf(sG[i] - sG[m]) * bm * sKK[i][m];
+        const int end = KIND == 0 ? B - 1 : i;
+        if (m <= end) P = __expf(sG[end] - sG[m]) * bm * sQK[i][m];
+      }
+      sKK[i][m] = A;
+      sQK[i][m] = P;
+    }
+    __syncthreads();
+
+    // 3. T = (I + A)^-1 by forward substitution, one lane per column, the
+    //    column in registers (T[m][c] = 0 for m < c, so every row sums over all
+    //    earlier m); columns past the block come out as unit vectors.  The
+    //    other threads go on to the reduction.
+    if (t < BMAX) {
       const int c = t;
-      for (int i = 0; i < B; ++i) {
-        float x = 0.f;
-        if (i == c) {
-          x = 1.f;
-        } else if (i > c) {
-          float acc = 0.f;
-          for (int m = c; m < i; ++m) acc += __expf(sG[i] - sG[m]) * sBeta[m] * sKK[i][m] * sT[m][c];
-          x = -acc;
-        }
-        sT[i][c] = x;
+      float tc[BMAX];
+#pragma unroll
+      for (int i = 0; i < BMAX; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc += sKK[i][m] * tc[m];
+        tc[i] = i == c ? 1.f : (i > c ? -acc : 0.f);
+        sT[i][c] = tc[i];
       }
     }
 
@@ -341,30 +365,106 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
     }
     __syncthreads();
 
-    // 5. U = T (V - diag(G) W_k)
+    // 5. U = T (V - diag(G) W_k): first Y = V - diag(G) W_k in place of V,
+    //    then every NPC-th row of U per thread (T is lower triangular)
     for (int e = t; e < B * D; e += NT) {
-      const int i = e / D, c = e % D;
-      float u = 0.f;
-      for (int m = 0; m <= i; ++m) u += sT[i][m] * (sV[m][c] - __expf(sG[m]) * sW[m][c]);
-      sU[i][c] = u;
+      const int m = e / D, c = e % D;
+      sV[m][c] -= __expf(sG[m]) * sW[m][c];
+    }
+    __syncthreads();
+    {
+      constexpr int NPC = NT / D;  // threads per column
+      const int c = t % D;
+      for (int i = t / D; i < B; i += NPC) {
+        float u = 0.f;
+#pragma unroll 4
+        for (int m = 0; m <= i; ++m) u += sT[i][m] * sV[m][c];
+        sU[i][c] = u;
+      }
     }
     __syncthreads();
 
-    // 6. outputs, EPU consecutive columns per work item (one 16-byte store)
     const float s = a.scale;
     const int last = B - 1;
+
+    // 6. the new state (first: the state registers are free for the outputs),
+    //    token by token or as one rank-B update, for the modes
+    //    that write states; thread (rg, cq) owns rows rg * RPG .. + RPG - 1,
+    //    columns 4 cq .. 4 cq + 3 (the layout it read)
+    //    VERIFY (2): S_t = a_t S_{t-1} + b_t k_t u_t^T after every token, to
+    //      the candidate buffer;
+    //    BOUNDARIES (3): the same recurrence over the window's first count
+    //      tokens; the state before local token q for q = lo, lo + bB, ...
+    //      <= count goes to pool_out[g0 + (q - lo) / bB];
+    //    COMMIT (1): S <- G_e S + sum_j (G_e / G_j) b_j k_j u_j^T, written back
+    //      (or to pool_out)
+    const int toff = rg * RPG * D + 4 * cq;  // the thread's first state element; rows follow at D
+    auto store = [&](float *base, const float4 *n) {
+      float *const p = base + toff;
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) *reinterpret_cast<float4 *>(p + i * D) = n[i];
+    };
+    if constexpr (KIND == 1) {
+      const float ge = __expf(sG[last]);
+      float4 n[RPG];
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) n[i] = make_float4(ge * s4[i].x, ge * s4[i].y, ge * s4[i].z, ge * s4[i].w);
+      for (int j = 0; j < B; ++j) {
+        const float wk = __expf(sG[last] - sG[j]) * sBeta[j];
+        const float4 u = *reinterpret_cast<const float4 *>(&sU[j][4 * cq]);
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) {
+          const float kk = sX[j][rg * RPG + i] * wk;
+          n[i].x += kk * u.x; n[i].y += kk * u.y; n[i].z += kk * u.z; n[i].w += kk * u.w;
+        }
+      }
+      store(a.pool_out ? a.pool_out + ((size_t)req * a.H + h) * D * D : S, n);
+    } else if constexpr (KIND == 2) {
+      const bool bounds = a.mode == 3;
+      const int lo = bounds ? a.blo[req] : 0, g0 = bounds ? a.bg0[req] : 0, bB = bounds ? a.bB : 1;
+      const size_t tstride = (size_t)a.H * D * D;
+      float *const cand = bounds ? nullptr : a.cand + ((size_t)req * B * a.H + h) * D * D;
+      auto bnd = [&](int q) { return a.pool_out + ((size_t)(g0 + (q - lo) / bB) * a.H + h) * D * D; };
+      float4 n[RPG];
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) n[i] = s4[i];
+      if (bounds && lo == 0) store(bnd(0), n);
+      // VERIFY: every token of the block; BOUNDARIES: every token before the
+      // window's last block start
+      for (int j = 0; j < B; ++j) {
+        const float aj = __expf(sG[j] - (j > 0 ? sG[j - 1] : 0.f)), wk = sBeta[j];
+        const float4 u = *reinterpret_cast<const float4 *>(&sU[j][4 * cq]);
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) {
+          const float kk = sX[j][rg * RPG + i] * wk;
+          n[i].x = aj * n[i].x + kk * u.x;
+          n[i].y = aj * n[i].y + kk * u.y;
+          n[i].z = aj * n[i].z + kk * u.z;
+          n[i].w = aj * n[i].w + kk * u.w;
+        }
+        if (!bounds) {
+          store(cand + j * tstride, n);
+        } else {
+          const int q = j + 1;
+          if (q >= lo && (q - lo) % bB == 0) store(bnd(q), n);
+        }
+      }
+    }
+
+    // 7. outputs, EPU consecutive columns per work item (one 16-byte store)
     if (a.o) {
       IO *o = reinterpret_cast<IO *>(a.o);
       for (int e = t; e < B * UPR; e += NT) {
         const int l = e / UPR, c0 = (e % UPR) * EPU;
         if (l >= cnt) continue;                  // no output for identity tokens
-        const int end = a.mode == 0 ? last : l;  // EVAL reads the block end
+        const int end = KIND == 0 ? last : l;  // EVAL reads the block end
         const float ge = __expf(sG[end]);
         float acc[EPU];
 #pragma unroll
         for (int c = 0; c < EPU; ++c) acc[c] = ge * sW[BMAX + l][c0 + c];
+#pragma unroll 4
         for (int j = 0; j <= end; ++j) {
-          const float wq = __expf(sG[end] - sG[j]) * sBeta[j] * sQK[l][j];
+          const float wq = sQK[l][j];
 #pragma unroll
           for (int c = 0; c < EPU; ++c) acc[c] += wq * sU[j][c0 + c];
         }
@@ -381,79 +481,39 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
         }
       }
     }
-
-    // 7. VERIFY: the state after every token, S_t = a_t S_{t-1} + b_t k_t u_t^T,
-    //    into the candidate buffer (same per-thread rows and columns as COMMIT)
-    if (a.mode == 2) {
-      float al[BMAX], bt[BMAX];
-#pragma unroll
-      for (int j = 0; j < BMAX; ++j) {
-        al[j] = j < B ? __expf(sG[j] - (j > 0 ? sG[j - 1] : 0.f)) : 0.f;
-        bt[j] = j < B ? sBeta[j] : 0.f;
-      }
-      float *cand = a.cand + ((size_t)req * B * a.H + h) * D * D;
-      const size_t tstride = (size_t)a.H * D * D;
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        const int row = rg * RPG + i;
-        float4 n = s4[i];
-#pragma unroll
-        for (int j = 0; j < BMAX; ++j) {
-          if (j >= B) break;
-          const float kk = sX[j][row] * bt[j];
-          const float4 u = *reinterpret_cast<const float4 *>(&sU[j][4 * cq]);
-          n.x = al[j] * n.x + kk * u.x;
-          n.y = al[j] * n.y + kk * u.y;
-          n.z = al[j] * n.z + kk * u.z;
-          n.w = al[j] * n.w + kk * u.w;
-          *reinterpret_cast<float4 *>(cand + j * tstride + (size_t)row * D + 4 * cq) = n;
-        }
-      }
-    }
-
-    // 8. COMMIT: rank-B update of the register-resident state, written back
-    if (a.mode == 1) {
-      float *const Sdst = a.pool_out ? a.pool_out + ((size_t)req * a.H + h) * D * D : S;
-      const float ge = __expf(sG[last]);
-      float wj[BMAX];
-#pragma unroll
-      for (int j = 0; j < BMAX; ++j) wj[j] = j < B ? __expf(sG[last] - sG[j]) * sBeta[j] : 0.f;
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        const int row = rg * RPG + i;
-        float4 n = make_float4(ge * s4[i].x, ge * s4[i].y, ge * s4[i].z, ge * s4[i].w);
-#pragma unroll
-        for (int j = 0; j < BMAX; ++j) {
-          if (j >= B) break;
-          const float kk = sX[j][row] * wj[j];
-          const float4 u = *reinterpret_cast<const float4 *>(&sU[j][4 * cq]);
-          n.x += kk * u.x; n.y += kk * u.y; n.z += kk * u.z; n.w += kk * u.w;
-        }
-        *reinterpret_cast<float4 *>(Sdst + (size_t)row * D + 4 * cq) = n;
-      }
-    }
   }
+}
+
+template <typename IO, int D, int BMAX, bool CONV>
+static void launch_kind(const BlockStepArgs &a, dim3 grid, dim3 block, hipStream_t st) {
+  if (a.mode == 0)
+    hipLaunchKernelGGL((block_step_kernel<IO, D, BMAX, CONV, 0>), grid, block, 0, st, a);
+  else if (a.mode == 1)
+    hipLaunchKernelGGL((block_step_kernel<IO, D, BMAX, CONV, 1>), grid, block, 0, st, a);
+  else if constexpr (!CONV)
+    hipLaunchKernelGGL((block_step_kernel<IO, D, BMAX, CONV, 2>), grid, block, 0, st, a);
 }
 
 template <typename IO, int D>
 static hipError_t launch_step_d(const BlockStepArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)(a.num_req * a.H));
   const dim3 block(StepCfg<D>::NT);
+  if (a.conv && a.mode > 1) return hipErrorInvalidValue;  // the ShortConv step evaluates or commits
   TimedLaunch tl(K_BLOCK_STEP, st);
   if (a.conv) {
     // the serving ShortConv is built for blocks of up to 8 tokens
     if (a.B <= 4)
-      hipLaunchKernelGGL((block_step_kernel<IO, D, 4, true>), grid, block, 0, st, a);
+      launch_kind<IO, D, 4, true>(a, grid, block, st);
     else if (a.B <= 8)
-      hipLaunchKernelGGL((block_step_kernel<IO, D, 8, true>), grid, block, 0, st, a);
+      launch_kind<IO, D, 8, true>(a, grid, block, st);
     else
       return hipErrorInvalidValue;
   } else if (a.B <= 4) {
-    hipLaunchKernelGGL((block_step_kernel<IO, D, 4, false>), grid, block, 0, st, a);
+    launch_kind<IO, D, 4, false>(a, grid, block, st);
   } else if (a.B <= 8) {
-    hipLaunchKernelGGL((block_step_kernel<IO, D, 8, false>), grid, block, 0, st, a);
+    launch_kind<IO, D, 8, false>(a, grid, block, st);
   } else {
-    hipLaunchKernelGGL((block_step_kernel<IO, D, 32, false>), grid, block, 0, st, a);
+    launch_kind<IO, D, 32, false>(a, grid, block, st);
   }
   return hipGetLastError();
 }

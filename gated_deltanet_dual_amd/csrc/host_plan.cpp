@@ -128,11 +128,21 @@ int64_t route1_num_blocks(const flare_varlen *v, int32_t block_size) {
   return nb;
 }
 
+int64_t route1_num_windows(const flare_varlen *v) {
+  int64_t nw = 0;
+  for (int32_t i = 0; i < v->num_docs; ++i) {
+    const int64_t n = (int64_t)v->cu_seqlens_host[i + 1] - v->cu_seqlens_host[i];
+    const int64_t P = v->prompt_lens_host[i];
+    if (n > P) nw += (n + kChunk - 1) / kChunk - P / kChunk;
+  }
+  return nw;
+}
+
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t route1_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s, int64_t n_blocks) {
   return round256(fwd_workspace_bytes(vi, s)) + round256((size_t)n_blocks * s->num_heads * s->d_k * s->d_v * 4) +
-         round256((size_t)(2 * vi.num_docs + 5 * n_blocks) * sizeof(int32_t)) + 256;
+         round256((size_t)(3 * vi.num_docs + 7 * n_blocks) * sizeof(int32_t)) + 256;
 }
 
 flare_status check_block_step(int32_t num_req, const int32_t *slot_idx,

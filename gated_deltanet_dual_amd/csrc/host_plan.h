@@ -62,6 +62,8 @@ bool fwd_uses_chunk_matrices(const flare_gdn_shape *s);
 // copies of the document layout) and its workspace, laid out as the forward's
 // workspace, the block-boundary states, then the int32 plan arrays.
 int64_t route1_num_blocks(const flare_varlen *v, int32_t block_size);
+// chunks holding at least one response block start, over all documents
+int64_t route1_num_windows(const flare_varlen *v);
 size_t route1_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s, int64_t n_blocks);
 
 // Slots distinct and in [0, num_slots) (no check when slot_host is NULL).

@@ -32,6 +32,12 @@ struct BlockStepArgs {
   // the new state to pool_out[r] instead of in place
   const int32_t *row0, *count;
   float *pool_out;
+  // mode 3 (table mode): no outputs; request r's window runs over its first
+  // count[r] tokens (count[r] is its last block start, local) and the state
+  // before its local token q, for q = blo[r], blo[r] + bB, ... <= count[r],
+  // goes to pool_out[bg0[r] + (q - blo[r]) / bB]
+  const int32_t *blo, *bg0;
+  int bB;
 };
 hipError_t launch_block_step(const BlockStepArgs &a, hipStream_t st);
 
@@ -107,10 +113,12 @@ hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
 // the chunk-then-refine route (route1.hip): f as for launch_gdn_fwd with the
 // chunk-start states f.ckpt required; the plan's arrays live in the workspace
 struct Route1Plan {
-  int64_t n_blocks;  // response blocks over all documents
-  float *bstates;    // [n_blocks, H, D, D] the block-boundary states
-  int32_t *boff, *plen_all;                   // [N]
-  int32_t *r0m, *cm, *slm, *r0r, *cr;         // [n_blocks]
+  int64_t n_blocks;   // response blocks over all documents
+  int64_t n_windows;  // chunks holding at least one block start
+  float *bstates;     // [n_blocks, H, D, D] the block-boundary states
+  int32_t *boff, *woff, *plen_all;          // [N]
+  int32_t *wrow, *wcnt, *wslot, *wlo, *wg0;  // [n_windows] per chunk window
+  int32_t *r0r, *cr;                         // [n_blocks] per noisy block
 };
 hipError_t launch_route1(const FwdArgs &f, const Route1Plan &pl, hipStream_t st);
 // bf16 io at d = 128 without flags: the forward's pre-pass (chunk matrices

@@ -312,7 +312,7 @@ def test_route1_workspace_and_validation(L):
     # no response tokens: no block states
     v0 = varlen([0, 40], [40])
     need0 = L.flare_gdn_route1_workspace_size(ctypes.byref(v0), ctypes.byref(shape))
-    assert need0 == r(L.flare_gdn_dual_workspace_size(ctypes.byref(v0), ctypes.byref(shape), 0)) + r(2 * 4) + 256
+    assert need0 == r(L.flare_gdn_dual_workspace_size(ctypes.byref(v0), ctypes.byref(shape), 0)) + r(3 * 4) + 256
     # unsupported shapes report 0 and fail the call
     odd = g._shape(2, 16, 4, g.F32, g.QK_L2NORM)
     assert L.flare_gdn_route1_workspace_size(ctypes.byref(v), ctypes.byref(odd)) == 0
