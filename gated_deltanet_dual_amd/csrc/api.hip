@@ -5,6 +5,7 @@
 
 #include "host_plan.h"
 #include "kernels.h"
+#include "serving.h"
 
 using namespace flare;
 

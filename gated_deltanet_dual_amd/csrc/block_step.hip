@@ -29,6 +29,7 @@
 // below the MI355X fp32 ridge, so the kernel is bound by HBM bandwidth.
 #include "device_common.h"
 #include "kernels.h"
+#include "serving.h"
 #include "timing.h"
 
 namespace flare {

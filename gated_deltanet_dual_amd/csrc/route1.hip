@@ -20,6 +20,7 @@
 #include "device_common.h"
 #include "host_plan.h"
 #include "kernels.h"
+#include "serving.h"
 #include "timing.h"
 
 namespace flare {
