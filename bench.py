@@ -398,6 +398,23 @@ def bench_serving(torch, g, wl, dev, timer, up, args):
     ar_wall = time.perf_counter() - t0
     vf, sc = timer.avg_ms("verify"), timer.avg_ms("scatter")
 
+    # the replay form of the same rollback: the causal outputs without
+    # candidates, then the COMMIT of each accepted prefix (same counts)
+    def replay_cycle(i):
+        slot, pool, blocks = sets[i % n_rot]
+        timer.run("verify_out", lambda: g.gdn_verify_outputs(slot, pool, *blocks[4], o=o))
+        timer.run("commit_prefix", lambda: g.gdn_commit_prefix(slot, pool, *blocks[4], acc[i % n_rot]))
+
+    for i in range(max(args.warmup, 3)):
+        replay_cycle(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        replay_cycle(i)
+    torch.cuda.synchronize()
+    rp_wall = time.perf_counter() - t0
+    vo, cp = timer.avg_ms("verify_out"), timer.avg_ms("commit_prefix")
+
     # the same EVAL / COMMIT with the ShortConv in front: raw bf16 projections,
     # W = 4 clean histories per slot, SiLU, q/k L2 norm
     Wc = 4
@@ -425,6 +442,9 @@ def bench_serving(torch, g, wl, dev, timer, up, args):
     evc_bytes, cmc_bytes = ev_bytes + hist, cm_bytes + 2 * hist
     vf_bytes = state + io_tok + K * state  # pool read, block io, K candidate states written
     sc_bytes = 2 * float(np.mean(n_acc)) * H * d * d * 4  # accepted candidates read, slots written
+    # the prefix commit reads and writes the slots with an accepted token, and
+    # the drafted block's io
+    cp_bytes = 2 * float(np.mean(n_acc)) * H * d * d * 4 + io_tok
     return {"workload": "serving block step, 256 requests x 16 heads, fp32 128x128 states, B=4",
             "eval_ms": ev, "commit_ms": cm, "cycle_ms": 1e3 * wall / n,
             "eval_gbs": ev_bytes / (ev * 1e-3) / 1e9, "commit_gbs": cm_bytes / (cm * 1e-3) / 1e9,
@@ -441,7 +461,12 @@ def bench_serving(torch, g, wl, dev, timer, up, args):
                          "verify_gbs": vf_bytes / (vf * 1e-3) / 1e9, "scatter_gbs": sc_bytes / (sc * 1e-3) / 1e9,
                          "verify_hbm_frac": vf_bytes / (vf * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "scatter_hbm_frac": sc_bytes / (sc * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "drafted_tokens_per_s": R * K / (ar_wall / n)}}
+                         "drafted_tokens_per_s": R * K / (ar_wall / n),
+                         "replay": {"verify_outputs_ms": vo, "commit_prefix_ms": cp, "cycle_ms": 1e3 * rp_wall / n,
+                                    "verify_outputs_gbs": ev_bytes / (vo * 1e-3) / 1e9,
+                                    "commit_prefix_gbs": cp_bytes / (cp * 1e-3) / 1e9,
+                                    "alg_bytes": {"verify_outputs": ev_bytes, "commit_prefix": cp_bytes},
+                                    "drafted_tokens_per_s": R * K / (rp_wall / n)}}}
 
 
 CONV_WORKLOAD = "packed conv 32768 tokens 8 docs 12288 ch W4 bf16"

@@ -17,7 +17,7 @@ import os
 import numpy as np
 
 __all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_fwd_pool", "gdn_dual_fwd_route1", "gdn_dual_bwd",
-           "block_step", "block_step_conv", "conv_cache_fill", "gdn_verify", "gdn_scatter", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
+           "block_step", "block_step_conv", "conv_cache_fill", "gdn_verify", "gdn_scatter", "gdn_verify_outputs", "gdn_commit_prefix", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
            "qkv_prologue_bwd", "qkv_prologue_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
            "QK_L2NORM", "F32", "BF16"]
 
@@ -97,6 +97,10 @@ def lib():
     L.flare_gdn_verify.restype = ctypes.c_int
     L.flare_gdn_scatter.argtypes = [I32, P, P, P, P, P, I32, SP, P]
     L.flare_gdn_scatter.restype = ctypes.c_int
+    L.flare_gdn_verify_outputs.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, P]
+    L.flare_gdn_verify_outputs.restype = ctypes.c_int
+    L.flare_gdn_commit_prefix.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, P, P]
+    L.flare_gdn_commit_prefix.restype = ctypes.c_int
     L.flare_shortconv_dual.argtypes = [VP, I32, I32, I32, I32, P, P, P, P, I32, P, P, P]
     L.flare_shortconv_dual.restype = ctypes.c_int
     L.flare_shortconv_dual_bwd_workspace_size.argtypes = [VP, I32, I32, I32]
@@ -411,6 +415,38 @@ def gdn_scatter(slot_idx, accepted, cand, pool, slot_idx_host=None):
         host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
     _check(lib().flare_gdn_scatter(R, _ptr(slot_idx), None if host is None else host.ctypes.data, _ptr(accepted),
                                    _ptr(cand), _ptr(pool), pool.shape[0], ctypes.byref(shp), _stream(cand.device)))
+    return pool
+
+
+def gdn_verify_outputs(slot_idx, pool, q, k, v, alpha, beta, scale=0.0, slot_idx_host=None, o=None):
+    """The causal outputs of gdn_verify without the candidate states (pool
+    read only).  Returns o [R,K,H,d]."""
+    torch = _torch()
+    R, K, H, d = q.shape
+    shp = _shape(H, d, K, _io_of(q), 0, scale)
+    if o is None:
+        o = torch.empty((R, K, H, d), dtype=q.dtype, device=q.device)
+    host = None
+    if slot_idx_host is not None:
+        host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
+    _check(lib().flare_gdn_verify_outputs(R, _ptr(slot_idx), None if host is None else host.ctypes.data, _ptr(pool),
+                                          pool.shape[0], ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                          _ptr(beta), _ptr(o), _stream(q.device)))
+    return o
+
+
+def gdn_commit_prefix(slot_idx, pool, q, k, v, alpha, beta, accepted, scale=0.0, slot_idx_host=None, o=None):
+    """COMMIT of each request's first accepted[r] drafted tokens (device int32,
+    clamped to [0, K]) into its pool slot, in place; 0 leaves the slot.
+    o (optional) receives the causal outputs of the replayed tokens."""
+    R, K, H, d = q.shape
+    shp = _shape(H, d, K, _io_of(q), 0, scale)
+    host = None
+    if slot_idx_host is not None:
+        host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
+    _check(lib().flare_gdn_commit_prefix(R, _ptr(slot_idx), None if host is None else host.ctypes.data, _ptr(pool),
+                                         pool.shape[0], ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                         _ptr(beta), _ptr(accepted), _ptr(o), _stream(q.device)))
     return pool
 
 

@@ -396,6 +396,53 @@ flare_status flare_gdn_scatter(int32_t num_req, const int32_t *slot_idx, const i
   return hip_status(launch_gdn_scatter(a, (hipStream_t)stream), "gdn_scatter launch");
 }
 
+flare_status flare_gdn_verify_outputs(int32_t num_req, const int32_t *slot_idx, const int32_t *slot_idx_host,
+                                      const float *state_pool, int32_t num_slots, const flare_gdn_shape *shape,
+                                      const void *q, const void *k, const void *v, const float *alpha,
+                                      const float *beta, void *o, void *stream) {
+  clear_error();
+  flare_status st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape, q, k, v,
+                                     alpha, beta, o, FLARE_BLOCK_EVAL);
+  if (st != FLARE_OK) return st;
+  BlockStepArgs a{};
+  a.num_req = num_req;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.B = shape->block_size;
+  a.mode = 0;
+  a.causal = 1;
+  a.bf16 = shape->io_dtype == FLARE_BF16;
+  a.scale = resolve_scale(shape);
+  a.slot_idx = slot_idx;
+  a.pool = const_cast<float *>(state_pool);  // read only in this mode
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+  return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_verify_outputs launch");
+}
+
+flare_status flare_gdn_commit_prefix(int32_t num_req, const int32_t *slot_idx, const int32_t *slot_idx_host,
+                                     float *state_pool, int32_t num_slots, const flare_gdn_shape *shape,
+                                     const void *q, const void *k, const void *v, const float *alpha,
+                                     const float *beta, const int32_t *accepted, void *o, void *stream) {
+  clear_error();
+  flare_status st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape, q, k, v,
+                                     alpha, beta, o, FLARE_BLOCK_COMMIT);
+  if (st != FLARE_OK) return st;
+  if (num_req > 0 && !accepted) return fail(FLARE_ERR_NULL, "commit_prefix needs the accepted counts");
+  BlockStepArgs a{};
+  a.num_req = num_req;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.B = shape->block_size;
+  a.mode = 1;
+  a.bf16 = shape->io_dtype == FLARE_BF16;
+  a.scale = resolve_scale(shape);
+  a.slot_idx = slot_idx;
+  a.pool = state_pool;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+  a.count = accepted;  // the first accepted[r] tokens are replayed, the rest are identity
+  return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_commit_prefix launch");
+}
+
 flare_status flare_shortconv_dual(const flare_varlen *varlen, int32_t block_size, int32_t channels,
                                   int32_t width, int32_t io_dtype, const void *x, const void *xn,
                                   const float *weight, const float *bias, int32_t activation,

@@ -71,8 +71,9 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
   const int req = blockIdx.x / a.H, h = blockIdx.x % a.H;
   // table mode: the request's number of real tokens; a BOUNDARIES window
   // runs over exactly the tokens before its last block start (possibly none)
-  const int cnt = a.count ? a.count[req] : a.B;
+  const int cnt = a.count ? min(max(a.count[req], 0), a.B) : a.B;
   const int B = KIND == 2 && a.mode == 3 ? cnt : a.B;
+  if (KIND == 1 && cnt == 0) return;  // a COMMIT of no token leaves the state as it is
   const int t = threadIdx.x;
   const int rg = t % NRG, cq = t / NRG;
 
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
       if (i < B && m < B) {
         const float bm = sBeta[m];
         if (m < i) A = __expf(sG[i] - sG[m]) * bm * sKK[i][m];
-        const int end = KIND == 0 ? B - 1 : i;
+        const int end = KIND == 0 && !a.causal ? B - 1 : i;
         if (m <= end) P = __expf(sG[end] - sG[m]) * bm * sQK[i][m];
       }
       sKK[i][m] = A;
@@ -458,7 +459,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
       for (int e = t; e < B * UPR; e += NT) {
         const int l = e / UPR, c0 = (e % UPR) * EPU;
         if (l >= cnt) continue;                  // no output for identity tokens
-        const int end = KIND == 0 ? last : l;  // EVAL reads the block end
+        const int end = KIND == 0 && !a.causal ? last : l;  // EVAL reads the block end
         const float ge = __expf(sG[end]);
         float acc[EPU];
 #pragma unroll

@@ -28,8 +28,9 @@ struct BlockStepArgs {
   const float *cw[3];  // [H * D][W] per projection (q, k, v)
   // table mode (not with conv), all optional: request r's tokens are the rows
   // row0[r] .. row0[r] + B - 1 of token-major [T, H, D] inputs (gates
-  // [T, H]); only the first count[r] are real (the rest are identity updates,
-  // their outputs not written); slot_idx NULL reads state r; COMMIT writes
+  // [T, H]); only the first count[r] (clamped to [0, B]) are real (the rest
+  // are identity updates, their outputs not written; a COMMIT with none
+  // leaves the state untouched); slot_idx NULL reads state r; COMMIT writes
   // the new state to pool_out[r] instead of in place
   const int32_t *row0, *count;
   float *pool_out;
@@ -39,6 +40,9 @@ struct BlockStepArgs {
   // goes to pool_out[bg0[r] + (q - blo[r]) / bB]
   const int32_t *blo, *bg0;
   int bB;
+  // mode 0 only: causal reads (o_t reads the state after token t, as COMMIT)
+  // instead of block-end reads
+  int causal;
 };
 hipError_t launch_block_step(const BlockStepArgs &a, hipStream_t st);
 

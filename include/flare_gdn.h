@@ -324,6 +324,44 @@ flare_status flare_gdn_scatter(int32_t num_req, const int32_t *slot_idx,
                                const flare_gdn_shape *shape, void *stream);
 
 
+/* AR-Trust without the candidate buffer (Key designs item 4 names the
+ * rollback; this pair reaches the same pool state by replaying the accepted
+ * prefix instead of keeping every intermediate state).  Per (request, head) it
+ * reads the pooled state twice and writes it once, where verify + scatter
+ * write K candidates and copy one.
+ *
+ * flare_gdn_verify_outputs: the per-token causal outputs of flare_gdn_verify
+ * (o_t = s S_t^T q_t after drafted token t), without the candidates.  Arguments
+ * as flare_gdn_verify without cand; o is required; the pool is not written.
+ *
+ * flare_gdn_commit_prefix: for each request r, with a = accepted[r] (device
+ * int32, clamped to [0, K], K = shape->block_size), the COMMIT of the first a
+ * drafted tokens: their clean updates are applied to pool[slot_idx[r]] in
+ * order and the state is written back; a = 0 leaves the slot untouched.  The
+ * resulting slot equals what flare_gdn_scatter writes after flare_gdn_verify
+ * (up to rounding).  q, k, v, alpha, beta [num_req, K, H, .] as for
+ * flare_gdn_verify; o (optional, [num_req, K, H, d_v]) receives the causal
+ * outputs of the first a tokens (rows past a are not written).  Other
+ * arguments and errors as flare_gdn_block_step. */
+flare_status flare_gdn_verify_outputs(int32_t num_req, const int32_t *slot_idx,
+                                      const int32_t *slot_idx_host,
+                                      const float *state_pool,
+                                      int32_t num_slots,
+                                      const flare_gdn_shape *shape,
+                                      const void *q, const void *k,
+                                      const void *v, const float *alpha,
+                                      const float *beta, void *o,
+                                      void *stream);
+flare_status flare_gdn_commit_prefix(int32_t num_req, const int32_t *slot_idx,
+                                     const int32_t *slot_idx_host,
+                                     float *state_pool, int32_t num_slots,
+                                     const flare_gdn_shape *shape,
+                                     const void *q, const void *k,
+                                     const void *v, const float *alpha,
+                                     const float *beta,
+                                     const int32_t *accepted, void *o,
+                                     void *stream);
+
 /* Dual-source depthwise causal ShortConv (Key designs item 3).
  *   x, xn   [T, channels] io        clean / noisy inputs (xn prompt rows unread)
  *   weight  [channels, width] fp32  weight[c, width-1] multiplies the current

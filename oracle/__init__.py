@@ -212,6 +212,25 @@ def gdn_scatter(slot_idx, accepted, cand, pool):
     return pool
 
 
+def gdn_commit_prefix(slot_idx, pool, q, k, v, alpha, beta, accepted, scale=0.0):
+    """AR-Trust rollback by replay: for each request, the COMMIT of its first
+    r drafted tokens (r = accepted count clamped to [0, K]) into its pool slot
+    (the serving step's causal replay, Key designs item 4); r = 0 leaves the
+    slot.  pool is updated in place.  Returns the causal outputs of the
+    replayed tokens, zero past r."""
+    q, k, v, a, b = map(_f64, (q, k, v, alpha, beta))
+    R, K = q.shape[:2]
+    o = np.zeros(v.shape)
+    for i, sl in enumerate(np.asarray(slot_idx)):
+        r = min(max(int(accepted[i]), 0), K)
+        if r == 0:
+            continue
+        part = lambda x: np.ascontiguousarray(x[i:i + 1, :r])
+        o[i, :r] = block_step([0], pool[sl:sl + 1], part(q), part(k), part(v), part(a), part(b), COMMIT,
+                              scale=scale)[0]
+    return o
+
+
 def shortconv_dual(cu_seqlens, prompt_lens, block_size, x, xn, weight,
                    bias=None, activation=0, threads=0):
     """x, xn [T,C]; weight [C,W]; bias [C] or None.  Returns (y, yn)."""

@@ -250,6 +250,17 @@ def test_verify_scatter_validation(L):
     assert L.flare_gdn_scatter(2, FAKE, dup.ctypes.data, FAKE, FAKE, FAKE, 8, ctypes.byref(shape), None) == 2
     assert L.flare_gdn_scatter(9, FAKE, None, FAKE, FAKE, FAKE, 8, ctypes.byref(shape), None) == 2
     assert L.flare_gdn_scatter(0, None, None, None, None, None, 0, ctypes.byref(shape), None) == 0
+    # the replay pair: outputs required for the read, counts for the commit
+    assert L.flare_gdn_verify_outputs(2, FAKE, host.ctypes.data, FAKE, 8, ctypes.byref(shape), *args, None,
+                                      None) == 1
+    assert L.flare_gdn_verify_outputs(2, FAKE, dup.ctypes.data, FAKE, 8, ctypes.byref(shape), *args, FAKE,
+                                      None) == 2
+    assert L.flare_gdn_commit_prefix(2, FAKE, host.ctypes.data, FAKE, 8, ctypes.byref(shape), *args, None, None,
+                                     None) == 1
+    assert L.flare_gdn_commit_prefix(2, FAKE, dup.ctypes.data, FAKE, 8, ctypes.byref(shape), *args, FAKE, None,
+                                     None) == 2
+    assert L.flare_gdn_commit_prefix(0, None, None, None, 0, ctypes.byref(shape), *([None] * 5), None, None,
+                                     None) == 0
 
 
 def test_fwd_pool_validation(L):

@@ -8,6 +8,11 @@ oracle.gdn_scatter):
     candidate lands in its slot bit for bit, every other slot (and a slot whose
     count is 0) is bit-identical to before, and the result matches the oracle's
     scatter of its own candidates;
+  * the replay pair (flare_gdn_verify_outputs, flare_gdn_commit_prefix):
+    causal outputs without candidates, pool untouched; the COMMIT of each
+    request's accepted prefix against the oracle's (oracle.gdn_commit_prefix),
+    a slot with no accepted token bit-identical, other slots untouched, and
+    the slots agree with the GPU's own verify + scatter;
   * the full serving shape: 256 requests x 16 heads, K = 4, d = 128, bf16.
 """
 import numpy as np
@@ -103,3 +108,41 @@ def test_verify_and_scatter_full_serving_shape(g, dev):
     assert rel_rms(newpool[s.slot_idx], rpool[s.slot_idx]) <= TOL_F32
     others = np.setdiff1d(np.arange(s.pool.shape[0]), s.slot_idx)
     assert np.array_equal(newpool[others], s.pool[others])
+
+
+@pytest.mark.parametrize("K,d,bf16", [(4, 16, False), (8, 128, True)])
+def test_replay_pair_small(g, dev, K, d, bf16):
+    import torch
+    R, H, n_slots = 6, 2, 11
+    slots, pool, q, k, v, a, b = draw(30 + K + d, R, K, H, d, n_slots, bf16)
+    accepted = np.array([0, K, 1, K // 2, -3, K + 5], np.int32)
+    gq, gk, gv = to_dev(q, dev, bf16), to_dev(k, dev, bf16), to_dev(v, dev, bf16)
+    ga, gb = to_dev(a, dev), to_dev(b, dev)
+    gslot = to_dev(slots, dev)
+    gpool = to_dev(pool, dev)
+    before = gpool.clone()
+    o = g.gdn_verify_outputs(gslot, gpool, gq, gk, gv, ga, gb, slot_idx_host=slots)
+    torch.cuda.synchronize()
+    assert torch.equal(gpool, before), "the causal read must not write the pool"
+    ro, _ = oracle.gdn_verify(slots, pool.astype(np.float64), q, k, v, a, b)
+    tol = TOL_BF16 if bf16 else TOL_F32
+    assert rel_rms(to_np(o), ro) <= tol
+    # the prefix commit, with its outputs
+    op = torch.zeros_like(o)
+    g.gdn_commit_prefix(gslot, gpool, gq, gk, gv, ga, gb, to_dev(accepted, dev), slot_idx_host=slots, o=op)
+    torch.cuda.synchronize()
+    got = gpool.cpu().numpy()
+    rpool = pool.astype(np.float64).copy()
+    rop = oracle.gdn_commit_prefix(slots, rpool, q, k, v, a, b, accepted)
+    assert rel_rms(got[slots], rpool[slots]) <= TOL_F32
+    assert rel_rms(to_np(op), rop) <= tol
+    for i, sl in enumerate(slots):
+        r = min(max(int(accepted[i]), 0), K)
+        if r == 0:
+            assert np.array_equal(got[sl], pool[sl])
+        assert not to_np(op)[i, r:].any(), "rows past the accepted prefix are not written"
+    others = np.setdiff1d(np.arange(n_slots), slots)
+    assert np.array_equal(got[others], pool[others])
+    # the same slots as the candidate route on the GPU
+    _, _, via_scatter = run(g, dev, (slots, pool, q, k, v, a, b), accepted, bf16)
+    assert rel_rms(got[slots], via_scatter[slots]) <= TOL_F32

@@ -1,5 +1,6 @@
 """Pins of the oracle's AR-Trust verify and scatter (oracle.gdn_verify,
-oracle.gdn_scatter), against the other oracle paths they must agree with:
+oracle.gdn_scatter, and the replay form oracle.gdn_commit_prefix), against
+the other oracle paths they must agree with:
   * every candidate state equals the dual forward's final state over a
     one-document batch of the first t+1 drafted tokens (all clean), started
     from the pool state -- the forward's own document loop, not the step code;
@@ -77,3 +78,27 @@ def test_verify_rejects_duplicate_slots():
     g = np.ones((2, 2, 1))
     with pytest.raises(ValueError):
         oracle.gdn_verify([1, 1], np.zeros((3, 1, 2, 2)), x, x, x, g, g)
+
+
+def test_commit_prefix_equals_verify_then_scatter():
+    """The replay form of the rollback (oracle.gdn_commit_prefix: the step's
+    COMMIT over the first r tokens) lands every slot where the candidate form
+    (oracle.gdn_verify's token-by-token candidates, then oracle.gdn_scatter)
+    does, for r = 0, 1..K and out-of-range counts; its outputs are verify's
+    outputs on the replayed tokens and zero past them; other slots untouched."""
+    R, K, H, dk, dv = 6, 4, 2, 4, 3
+    slots, pool, q, k, v, a, b = draw(5, R, K, H, dk, dv, 9)
+    accepted = [0, 1, 2, K, -2, K + 3]
+    o_ver, cand = oracle.gdn_verify(slots, pool, q, k, v, a, b)
+    via_scatter = oracle.gdn_scatter(slots, accepted, cand, pool.copy())
+    via_replay = pool.copy()
+    o = oracle.gdn_commit_prefix(slots, via_replay, q, k, v, a, b, accepted)
+    np.testing.assert_allclose(via_replay, via_scatter, rtol=1e-12, atol=1e-12)
+    for i in range(R):
+        r = min(max(accepted[i], 0), K)
+        np.testing.assert_allclose(o[i, :r], o_ver[i, :r], rtol=1e-12, atol=1e-12)
+        assert not o[i, r:].any()
+        if r == 0:
+            np.testing.assert_array_equal(via_replay[slots[i]], pool[slots[i]])
+    others = np.setdiff1d(np.arange(pool.shape[0]), slots)
+    np.testing.assert_array_equal(via_replay[others], pool[others])
