@@ -34,14 +34,17 @@
 
 namespace flare {
 
-template <int D> struct StepCfg {
+// DV: the state columns (d_v) one workgroup owns; D / DV workgroups share a
+// (request, head), each with the whole k and q rows and its own columns of v,
+// the state and the outputs
+template <int D, int DV> struct StepCfg {
   static constexpr int NT = D >= 128 ? 256 : 64;  // threads
-  static constexpr int NCQ = D / 4;               // column quads
+  static constexpr int NCQ = DV / 4;              // column quads
   static constexpr int NRG = NT / NCQ;            // row groups: adjacent lanes of one quad
   static constexpr int RPG = D / NRG;             // rows per group (rows rg * RPG + i)
   static constexpr int G = D >= 128 ? 2 : 8;      // vectors per pass (few: registers, occupancy)
-  static constexpr int MINB = D >= 128 ? 4 : 8;   // workgroups per CU the registers must allow
   static_assert(NRG == 8 || NRG == 16, "row groups are reduced over 8 or 16 lanes");
+  static_assert(D % DV == 0 && NT % DV == 0, "whole column splits");
 };
 
 // Sum over the NRG adjacent lanes of a row group (a DPP row or half-row).
@@ -59,16 +62,20 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
 // SiLU; q/k L2 norm) -- see BlockStepArgs
 // KIND: 0 = EVAL, 1 = COMMIT, 2 = the token-wise state writers (VERIFY and
 // BOUNDARIES); the readers carry no state-update registers
-template <typename IO, int D, int BMAX, bool CONV, int KIND>
-__global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArgs a) {
-  using Cfg = StepCfg<D>;
+template <typename IO, int D, int DV, int BMAX, bool CONV, int KIND>
+__global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockStepArgs a) {
+  using Cfg = StepCfg<D, DV>;
+  static_assert(!CONV || DV == D, "the ShortConv step keeps whole rows");
   constexpr int NT = Cfg::NT, NRG = Cfg::NRG, RPG = Cfg::RPG, G = Cfg::G;
+  constexpr int NSPLIT = D / DV;         // workgroups per (request, head)
   constexpr int NV = 2 * BMAX;           // k vectors then q vectors
   constexpr int EPU = 16 / sizeof(IO);   // io elements per 16 bytes
   constexpr int UPR = D / EPU;           // 16-byte units per row
+  constexpr int UPRV = DV / EPU;         // 16-byte units of this workgroup's columns per row
   constexpr int WM1 = 7;                 // most history rows (W <= 8)
   constexpr int NRAW = CONV ? WM1 + BMAX : 1;
-  const int req = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int req = blockIdx.x / (a.H * NSPLIT), h = (blockIdx.x / NSPLIT) % a.H;
+  const int col0 = (blockIdx.x % NSPLIT) * DV;  // this workgroup's first state / value column
   // table mode: the request's number of real tokens; a BOUNDARIES window
   // runs over exactly the tokens before its last block start (possibly none)
   const int cnt = a.count ? min(max(a.count[req], 0), a.B) : a.B;
@@ -78,9 +85,9 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
   const int rg = t % NRG, cq = t / NRG;
 
   __shared__ __align__(16) float sX[NV][D];   // k_0..k_{B-1} at 0.., q_0..q_{B-1} at BMAX..
-  __shared__ __align__(16) float sV[BMAX][D];
-  __shared__ __align__(16) float sW[NV][D];   // S^T x for every x in sX
-  __shared__ __align__(16) float sU[BMAX][D];
+  __shared__ __align__(16) float sV[BMAX][DV];
+  __shared__ __align__(16) float sW[NV][DV];   // S^T x for every x in sX (this workgroup's columns)
+  __shared__ __align__(16) float sU[BMAX][DV];
   // B x B coefficients, rows 16-byte aligned for broadcast reads: k.k then the
   // UT system A, q.k then the output weights P, the inverse T
   __shared__ __align__(16) float sKK[BMAX][BMAX], sQK[BMAX][BMAX], sT[BMAX][BMAX];
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
   const float *const pal = a.alpha, *const pbe = a.beta;
 
   const int slot = a.slot_idx ? a.slot_idx[req] : req;
-  float *S = a.pool + ((size_t)slot * a.H + h) * D * D;
+  float *S = a.pool + ((size_t)slot * a.H + h) * D * D + col0;  // row r of the columns at S + r D
   // table mode: the request's first token row
   const int64_t rbase = a.row0 ? (int64_t)a.row0[req] : (int64_t)req * B;
   auto trow = [&](int r) { return rbase + (r < cnt ? r : max(cnt - 1, 0)); };  // loads stay on real rows
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
     // 0. the block inputs first (16-byte loads into registers), then the
     //    state: vector-memory results return in issue order, so the small B x B
     //    work below waits only for the inputs while the state is in flight
-    constexpr int IU = ((CONV ? 3 * NRAW : 3 * BMAX) * UPR + NT - 1) / NT;  // input units per thread
+    constexpr int IU = ((CONV ? 3 * NRAW * UPR : BMAX * (2 * UPR + UPRV)) + NT - 1) / NT;  // input units per thread
     uint4 in_raw[IU];
     const int W1 = CONV ? a.W - 1 : 0;  // history rows
     const int NR = W1 + B;              // raw rows per projection (CONV)
@@ -123,10 +130,13 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
                                          (((size_t)req * B + (row - W1)) * a.H + h) * D;
           in_raw[e] = *reinterpret_cast<const uint4 *>(src + cu * EPU);
         }
-      } else if (u < 3 * B * UPR) {
+      } else if (u < 2 * B * UPR) {  // k and q rows, whole
         const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
-        const IO *src = which == 0 ? pk : which == 1 ? pq : pv;
-        in_raw[e] = *reinterpret_cast<const uint4 *>(src + ((size_t)trow(r) * a.H + h) * D + cu * EPU);
+        in_raw[e] = *reinterpret_cast<const uint4 *>((which == 0 ? pk : pq) + ((size_t)trow(r) * a.H + h) * D +
+                                                     cu * EPU);
+      } else if (u < B * (2 * UPR + UPRV)) {  // v rows, this workgroup's columns
+        const int uv = u - 2 * B * UPR, r = uv / UPRV, cu = uv % UPRV;
+        in_raw[e] = *reinterpret_cast<const uint4 *>(pv + ((size_t)trow(r) * a.H + h) * D + col0 + cu * EPU);
       }
     }
     // CONV: the head's weights, loaded with the inputs (float4 units)
@@ -161,14 +171,17 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
 #pragma unroll
     for (int e = 0; e < IU; ++e) {
       const int u = e * NT + t;
-      if (u < (CONV ? 3 * NR : 3 * B) * UPR) {
+      if (u < (CONV ? 3 * NR * UPR : B * (2 * UPR + UPRV))) {
         float *dst;
         if constexpr (CONV) {
           const int sec = u / (NR * UPR), row = (u / UPR) % NR, cu = u % UPR;
           dst = &sRaw[sec][row][cu * EPU];
-        } else {
+        } else if (u < 2 * B * UPR) {
           const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
-          dst = which == 0 ? &sX[r][cu * EPU] : which == 1 ? &sX[BMAX + r][cu * EPU] : &sV[r][cu * EPU];
+          dst = which == 0 ? &sX[r][cu * EPU] : &sX[BMAX + r][cu * EPU];
+        } else {
+          const int uv = u - 2 * B * UPR;
+          dst = &sV[uv / UPRV][(uv % UPRV) * EPU];
         }
         const uint4 raw = in_raw[e];
         if constexpr (sizeof(IO) == 2) {
@@ -369,15 +382,15 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
 
     // 5. U = T (V - diag(G) W_k): first Y = V - diag(G) W_k in place of V,
     //    then every NPC-th row of U per thread (T is lower triangular)
-    for (int e = t; e < B * D; e += NT) {
-      const int m = e / D, c = e % D;
+    for (int e = t; e < B * DV; e += NT) {
+      const int m = e / DV, c = e % DV;
       sV[m][c] -= __expf(sG[m]) * sW[m][c];
     }
     __syncthreads();
     {
-      constexpr int NPC = NT / D;  // threads per column
-      const int c = t % D;
-      for (int i = t / D; i < B; i += NPC) {
+      constexpr int NPC = NT / DV;  // threads per column
+      const int c = t % DV;
+      for (int i = t / DV; i < B; i += NPC) {
         float u = 0.f;
 #pragma unroll 4
         for (int m = 0; m <= i; ++m) u += sT[i][m] * sV[m][c];
@@ -420,13 +433,13 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
           n[i].x += kk * u.x; n[i].y += kk * u.y; n[i].z += kk * u.z; n[i].w += kk * u.w;
         }
       }
-      store(a.pool_out ? a.pool_out + ((size_t)req * a.H + h) * D * D : S, n);
+      store(a.pool_out ? a.pool_out + ((size_t)req * a.H + h) * D * D + col0 : S, n);
     } else if constexpr (KIND == 2) {
       const bool bounds = a.mode == 3;
       const int lo = bounds ? a.blo[req] : 0, g0 = bounds ? a.bg0[req] : 0, bB = bounds ? a.bB : 1;
       const size_t tstride = (size_t)a.H * D * D;
-      float *const cand = bounds ? nullptr : a.cand + ((size_t)req * B * a.H + h) * D * D;
-      auto bnd = [&](int q) { return a.pool_out + ((size_t)(g0 + (q - lo) / bB) * a.H + h) * D * D; };
+      float *const cand = bounds ? nullptr : a.cand + ((size_t)req * B * a.H + h) * D * D + col0;
+      auto bnd = [&](int q) { return a.pool_out + ((size_t)(g0 + (q - lo) / bB) * a.H + h) * D * D + col0; };
       float4 n[RPG];
 #pragma unroll
       for (int i = 0; i < RPG; ++i) n[i] = s4[i];
@@ -456,8 +469,8 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
     // 7. outputs, EPU consecutive columns per work item (one 16-byte store)
     if (a.o) {
       IO *o = reinterpret_cast<IO *>(a.o);
-      for (int e = t; e < B * UPR; e += NT) {
-        const int l = e / UPR, c0 = (e % UPR) * EPU;
+      for (int e = t; e < B * UPRV; e += NT) {
+        const int l = e / UPRV, c0 = (e % UPRV) * EPU;
         if (l >= cnt) continue;                  // no output for identity tokens
         const int end = KIND == 0 && !a.causal ? last : l;  // EVAL reads the block end
         const float ge = __expf(sG[end]);
@@ -470,7 +483,7 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
 #pragma unroll
           for (int c = 0; c < EPU; ++c) acc[c] += wq * sU[j][c0 + c];
         }
-        IO *dst = o + ((size_t)trow(l) * a.H + h) * D + c0;
+        IO *dst = o + ((size_t)trow(l) * a.H + h) * D + col0 + c0;
         if constexpr (sizeof(IO) == 2) {
           uint4 w;
           w.x = pack_bf16x2(s * acc[0], s * acc[1]);
@@ -486,36 +499,41 @@ __global__ __launch_bounds__(StepCfg<D>::NT) void block_step_kernel(BlockStepArg
   }
 }
 
-template <typename IO, int D, int BMAX, bool CONV>
-static void launch_kind(const BlockStepArgs &a, dim3 grid, dim3 block, hipStream_t st) {
+template <typename IO, int D, int DV, int BMAX, bool CONV>
+static void launch_kind(const BlockStepArgs &a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.num_req * a.H * (D / DV)));
+  const dim3 block(StepCfg<D, DV>::NT);
   if (a.mode == 0)
-    hipLaunchKernelGGL((block_step_kernel<IO, D, BMAX, CONV, 0>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CONV, 0>), grid, block, 0, st, a);
   else if (a.mode == 1)
-    hipLaunchKernelGGL((block_step_kernel<IO, D, BMAX, CONV, 1>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CONV, 1>), grid, block, 0, st, a);
   else if constexpr (!CONV)
-    hipLaunchKernelGGL((block_step_kernel<IO, D, BMAX, CONV, 2>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CONV, 2>), grid, block, 0, st, a);
 }
 
 template <typename IO, int D>
 static hipError_t launch_step_d(const BlockStepArgs &a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.num_req * a.H));
-  const dim3 block(StepCfg<D>::NT);
+  // the 32-token step splits a d = 128 state's columns over two workgroups
+  // (its LDS then allows two workgroups per CU instead of one); the short
+  // blocks keep whole rows, whose stores cover full 128-byte row segments per
+  // wave (half rows measured slower there)
+  constexpr int DV32 = D >= 128 ? D / 2 : D;
   if (a.conv && a.mode > 1) return hipErrorInvalidValue;  // the ShortConv step evaluates or commits
   TimedLaunch tl(K_BLOCK_STEP, st);
   if (a.conv) {
     // the serving ShortConv is built for blocks of up to 8 tokens
     if (a.B <= 4)
-      launch_kind<IO, D, 4, true>(a, grid, block, st);
+      launch_kind<IO, D, D, 4, true>(a, st);
     else if (a.B <= 8)
-      launch_kind<IO, D, 8, true>(a, grid, block, st);
+      launch_kind<IO, D, D, 8, true>(a, st);
     else
       return hipErrorInvalidValue;
   } else if (a.B <= 4) {
-    launch_kind<IO, D, 4, false>(a, grid, block, st);
+    launch_kind<IO, D, D, 4, false>(a, st);
   } else if (a.B <= 8) {
-    launch_kind<IO, D, 8, false>(a, grid, block, st);
+    launch_kind<IO, D, D, 8, false>(a, st);
   } else {
-    launch_kind<IO, D, 32, false>(a, grid, block, st);
+    launch_kind<IO, D, DV32, 32, false>(a, st);
   }
   return hipGetLastError();
 }
