@@ -62,9 +62,12 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
 // SiLU; q/k L2 norm) -- see BlockStepArgs
 // KIND: 0 = EVAL, 1 = COMMIT, 2 = the token-wise state writers (VERIFY and
 // BOUNDARIES); the readers carry no state-update registers
-template <typename IO, int D, int DV, int BMAX, bool CONV, int KIND>
+// CW: 0 for the plain step, else the widest ShortConv it is built for (its LDS
+// staging holds CW - 1 history rows and CW taps per channel)
+template <typename IO, int D, int DV, int BMAX, int CW, int KIND>
 __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockStepArgs a) {
   using Cfg = StepCfg<D, DV>;
+  constexpr bool CONV = CW > 0;
   static_assert(!CONV || DV == D, "the ShortConv step keeps whole rows");
   constexpr int NT = Cfg::NT, NRG = Cfg::NRG, RPG = Cfg::RPG, G = Cfg::G;
   constexpr int NSPLIT = D / DV;         // workgroups per (request, head)
@@ -72,7 +75,7 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
   constexpr int EPU = 16 / sizeof(IO);   // io elements per 16 bytes
   constexpr int UPR = D / EPU;           // 16-byte units per row
   constexpr int UPRV = DV / EPU;         // 16-byte units of this workgroup's columns per row
-  constexpr int WM1 = 7;                 // most history rows (W <= 8)
+  constexpr int WM1 = CONV ? CW - 1 : 0;  // most history rows
   constexpr int NRAW = CONV ? WM1 + BMAX : 1;
   const int req = blockIdx.x / (a.H * NSPLIT), h = (blockIdx.x / NSPLIT) % a.H;
   const int col0 = (blockIdx.x % NSPLIT) * DV;  // this workgroup's first state / value column
@@ -499,16 +502,16 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
   }
 }
 
-template <typename IO, int D, int DV, int BMAX, bool CONV>
+template <typename IO, int D, int DV, int BMAX, int CW>
 static void launch_kind(const BlockStepArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)(a.num_req * a.H * (D / DV)));
   const dim3 block(StepCfg<D, DV>::NT);
   if (a.mode == 0)
-    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CONV, 0>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CW, 0>), grid, block, 0, st, a);
   else if (a.mode == 1)
-    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CONV, 1>), grid, block, 0, st, a);
-  else if constexpr (!CONV)
-    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CONV, 2>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CW, 1>), grid, block, 0, st, a);
+  else if constexpr (CW == 0)
+    hipLaunchKernelGGL((block_step_kernel<IO, D, DV, BMAX, CW, 2>), grid, block, 0, st, a);
 }
 
 template <typename IO, int D>
@@ -521,19 +524,23 @@ static hipError_t launch_step_d(const BlockStepArgs &a, hipStream_t st) {
   if (a.conv && a.mode > 1) return hipErrorInvalidValue;  // the ShortConv step evaluates or commits
   TimedLaunch tl(K_BLOCK_STEP, st);
   if (a.conv) {
-    // the serving ShortConv is built for blocks of up to 8 tokens
-    if (a.B <= 4)
-      launch_kind<IO, D, D, 4, true>(a, st);
-    else if (a.B <= 8)
-      launch_kind<IO, D, D, 8, true>(a, st);
-    else
-      return hipErrorInvalidValue;
+    // the serving ShortConv is built for blocks of up to 8 tokens and widths
+    // up to 8; widths up to 4 take the smaller LDS staging (one more
+    // workgroup per CU)
+    if (a.B > 8 || a.W > 8) return hipErrorInvalidValue;
+    if (a.W <= 4) {
+      if (a.B <= 4) launch_kind<IO, D, D, 4, 4>(a, st);
+      else launch_kind<IO, D, D, 8, 4>(a, st);
+    } else {
+      if (a.B <= 4) launch_kind<IO, D, D, 4, 8>(a, st);
+      else launch_kind<IO, D, D, 8, 8>(a, st);
+    }
   } else if (a.B <= 4) {
-    launch_kind<IO, D, D, 4, false>(a, st);
+    launch_kind<IO, D, D, 4, 0>(a, st);
   } else if (a.B <= 8) {
-    launch_kind<IO, D, D, 8, false>(a, st);
+    launch_kind<IO, D, D, 8, 0>(a, st);
   } else {
-    launch_kind<IO, D, DV32, 32, false>(a, st);
+    launch_kind<IO, D, DV32, 32, 0>(a, st);
   }
   return hipGetLastError();
 }
