@@ -128,11 +128,12 @@ class Timer:
         self.times = {}
 
 
-def traffic_for(kernel, workload):
+def traffic_for(kernel, workload, field="bytes_per_launch"):
     """Calibrated HBM bytes per launch from the committed rocprofv3 counter
     runs (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain
-    1 GiB copy), valid only while the kernel's sources are unchanged since the
-    counters were taken."""
+    1 GiB copy), or another counter-measured field of the same record (the
+    MFMA busy percentage), valid only while the kernel's sources are unchanged
+    since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -147,7 +148,7 @@ def traffic_for(kernel, workload):
         h.update(open(src, "rb").read())
     if rec.get("source_sha") != h.hexdigest()[:16]:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get(field)
 
 
 def device_copy(torch, dev, args):
@@ -300,9 +301,11 @@ def run_headline(torch, g, wl, dev, timer, up, args):
             "roofline": {"kernel": dom, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": traffic_for(dom, workload),
-                         "alg_bytes_per_launch": alg[dom], "kernel_ms": kms},
+                         "alg_bytes_per_launch": alg[dom], "kernel_ms": kms,
+                         "mfma_busy_pct": traffic_for(dom, workload, "mfma_util_pct")},
             "kernels": {k: dict(v, alg_bytes=alg[k],
-                                alg_gbs=(alg[k] / (v["ms"] * 1e-3) / 1e9) if v["ms"] else None)
+                                alg_gbs=(alg[k] / (v["ms"] * 1e-3) / 1e9) if v["ms"] else None,
+                                mfma_busy_pct=traffic_for(k, workload, "mfma_util_pct"))
                         for k, v in kern.items()},
             "step_roofline": {"alg_bytes": step_bytes, "alg_flops": step_flops, "t_roof_ms": 1e3 * t_roof,
                               "frac": 1e3 * t_roof / ms_step,
