@@ -53,6 +53,30 @@ int64_t flare_gdn_ckpt_slot(int32_t cu_seqlens_i, int32_t doc_index, int32_t chu
   return ckpt_slot(cu_seqlens_i, doc_index, chunk_index, ckpt_stride_chunks);
 }
 
+// The forward's argument block from the validated call (the workspace and the
+// pool slots are set by the caller).
+static FwdArgs fwd_args(const flare_varlen *varlen, const flare_gdn_shape *shape, const VarlenInfo &vi,
+                        const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                        const void *qn, const void *kn, const void *vn, const float *alpha_n, const float *beta_n,
+                        const float *h0, void *o, void *on, float *h_final, float *ckpt, int32_t ckpt_stride) {
+  FwdArgs a{};
+  a.num_docs = varlen->num_docs;
+  a.H = shape->num_heads;
+  a.D = shape->d_k;
+  a.B = shape->block_size;
+  a.flags = shape->flags;
+  a.bf16 = shape->io_dtype == FLARE_BF16;
+  a.ckpt_stride = ckpt ? ckpt_stride : 1;
+  a.scale = resolve_scale(shape);
+  a.cu = varlen->cu_seqlens;
+  a.plen = varlen->prompt_lens;
+  a.q = q; a.k = k; a.v = v; a.qn = qn; a.kn = kn; a.vn = vn;
+  a.alpha = alpha; a.beta = beta; a.alpha_n = alpha_n; a.beta_n = beta_n;
+  a.h0 = h0; a.o = o; a.on = on; a.h_final = h_final; a.ckpt = ckpt;
+  a.T = vi.total_tokens;
+  return a;
+}
+
 static flare_status fwd_impl(const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q, const void *k,
                              const void *v, const float *alpha, const float *beta, const void *qn, const void *kn,
                              const void *vn, const float *alpha_n, const float *beta_n, const float *h0, void *o,
@@ -71,23 +95,10 @@ static flare_status fwd_impl(const flare_varlen *varlen, const flare_gdn_shape *
     return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (((uintptr_t)workspace & 255u) != 0)
     return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  FwdArgs a{};
-  a.num_docs = varlen->num_docs;
-  a.H = shape->num_heads;
-  a.D = shape->d_k;
-  a.B = shape->block_size;
-  a.flags = shape->flags;
-  a.bf16 = shape->io_dtype == FLARE_BF16;
-  a.ckpt_stride = ckpt ? ckpt_stride_chunks : 1;
-  a.scale = resolve_scale(shape);
-  a.cu = varlen->cu_seqlens;
-  a.plen = varlen->prompt_lens;
-  a.q = q; a.k = k; a.v = v; a.qn = qn; a.kn = kn; a.vn = vn;
-  a.alpha = alpha; a.beta = beta; a.alpha_n = alpha_n; a.beta_n = beta_n;
-  a.h0 = h0; a.o = o; a.on = on; a.h_final = h_final; a.ckpt = ckpt;
+  FwdArgs a = fwd_args(varlen, shape, vi, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0, o, on, h_final,
+                       ckpt, ckpt_stride_chunks);
   a.state_slot = state_slot;
   a.workspace = need > 0 ? reinterpret_cast<float *>(workspace) : nullptr;
-  a.T = vi.total_tokens;
   return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd launch");
 }
 
@@ -131,21 +142,8 @@ flare_status flare_gdn_dual_fwd_route1(const flare_varlen *varlen, const flare_g
     return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (((uintptr_t)workspace & 255u) != 0) return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (vi.total_tokens == 0) return FLARE_OK;
-  FwdArgs a{};
-  a.num_docs = varlen->num_docs;
-  a.H = shape->num_heads;
-  a.D = shape->d_k;
-  a.B = shape->block_size;
-  a.flags = 0;
-  a.bf16 = shape->io_dtype == FLARE_BF16;
-  a.ckpt_stride = 1;
-  a.scale = resolve_scale(shape);
-  a.cu = varlen->cu_seqlens;
-  a.plen = varlen->prompt_lens;
-  a.q = q; a.k = k; a.v = v; a.qn = qn; a.kn = kn; a.vn = vn;
-  a.alpha = alpha; a.beta = beta; a.alpha_n = alpha_n; a.beta_n = beta_n;
-  a.h0 = h0; a.o = o; a.on = on; a.h_final = h_final; a.ckpt = ckpt;
-  a.T = vi.total_tokens;
+  FwdArgs a = fwd_args(varlen, shape, vi, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0, o, on, h_final,
+                       ckpt, 1);
   // workspace: the forward's, the boundary states, the plan arrays
   char *w = reinterpret_cast<char *>(workspace);
   const size_t fwd = fwd_workspace_bytes(vi, shape);
@@ -248,15 +246,10 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
   return hip_status(launch_gdn_bwd(a, (hipStream_t)stream), "gdn_dual_bwd launch");
 }
 
-flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
-                                  const int32_t *slot_idx_host, float *state_pool,
-                                  int32_t num_slots, const flare_gdn_shape *shape, const void *q,
-                                  const void *k, const void *v, const float *alpha,
-                                  const float *beta, void *o, int32_t mode, void *stream) {
-  clear_error();
-  flare_status st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape,
-                                     q, k, v, alpha, beta, o, mode);
-  if (st != FLARE_OK) return st;
+// The serving step's argument block for num_req requests of shape's blocks.
+static BlockStepArgs step_args(int32_t num_req, const flare_gdn_shape *shape, int32_t mode,
+                               const int32_t *slot_idx, const float *pool, const void *q, const void *k,
+                               const void *v, const float *alpha, const float *beta, void *o) {
   BlockStepArgs a{};
   a.num_req = num_req;
   a.H = shape->num_heads;
@@ -266,8 +259,21 @@ flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
   a.bf16 = shape->io_dtype == FLARE_BF16;
   a.scale = resolve_scale(shape);
   a.slot_idx = slot_idx;
-  a.pool = state_pool;
+  a.pool = const_cast<float *>(pool);  // written only by the modes that commit
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+  return a;
+}
+
+flare_status flare_gdn_block_step(int32_t num_req, const int32_t *slot_idx,
+                                  const int32_t *slot_idx_host, float *state_pool,
+                                  int32_t num_slots, const flare_gdn_shape *shape, const void *q,
+                                  const void *k, const void *v, const float *alpha,
+                                  const float *beta, void *o, int32_t mode, void *stream) {
+  clear_error();
+  flare_status st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape,
+                                     q, k, v, alpha, beta, o, mode);
+  if (st != FLARE_OK) return st;
+  BlockStepArgs a = step_args(num_req, shape, mode, slot_idx, state_pool, q, k, v, alpha, beta, o);
   return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_block_step launch");
 }
 
@@ -293,17 +299,7 @@ flare_status flare_gdn_block_step_conv(int32_t num_req, const int32_t *slot_idx,
       return fail(FLARE_ERR_NULL, "block_step_conv: a weight pointer is NULL");
     if (width > 1 && !conv_cache) return fail(FLARE_ERR_NULL, "block_step_conv: conv_cache is NULL");
   }
-  BlockStepArgs a{};
-  a.num_req = num_req;
-  a.H = shape->num_heads;
-  a.D = shape->d_k;
-  a.B = shape->block_size;
-  a.mode = mode;
-  a.bf16 = shape->io_dtype == FLARE_BF16;
-  a.scale = resolve_scale(shape);
-  a.slot_idx = slot_idx;
-  a.pool = state_pool;
-  a.q = xq; a.k = xk; a.v = xv; a.alpha = alpha; a.beta = beta; a.o = o;
+  BlockStepArgs a = step_args(num_req, shape, mode, slot_idx, state_pool, xq, xk, xv, alpha, beta, o);
   a.conv = 1;
   a.W = width;
   a.act = activation;
@@ -357,17 +353,7 @@ flare_status flare_gdn_verify(int32_t num_req, const int32_t *slot_idx, const in
                                      alpha, beta, o, FLARE_BLOCK_COMMIT);
   if (st != FLARE_OK) return st;
   if (num_req > 0 && (!o || !cand)) return fail(FLARE_ERR_NULL, "verify needs the outputs and the candidate buffer");
-  BlockStepArgs a{};
-  a.num_req = num_req;
-  a.H = shape->num_heads;
-  a.D = shape->d_k;
-  a.B = shape->block_size;
-  a.mode = 2;
-  a.bf16 = shape->io_dtype == FLARE_BF16;
-  a.scale = resolve_scale(shape);
-  a.slot_idx = slot_idx;
-  a.pool = const_cast<float *>(state_pool);  // read only in this mode
-  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+  BlockStepArgs a = step_args(num_req, shape, 2, slot_idx, state_pool, q, k, v, alpha, beta, o);
   a.cand = cand;
   return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_verify launch");
 }
@@ -404,18 +390,8 @@ flare_status flare_gdn_verify_outputs(int32_t num_req, const int32_t *slot_idx, 
   flare_status st = check_block_step(num_req, slot_idx, slot_idx_host, state_pool, num_slots, shape, q, k, v,
                                      alpha, beta, o, FLARE_BLOCK_EVAL);
   if (st != FLARE_OK) return st;
-  BlockStepArgs a{};
-  a.num_req = num_req;
-  a.H = shape->num_heads;
-  a.D = shape->d_k;
-  a.B = shape->block_size;
-  a.mode = 0;
+  BlockStepArgs a = step_args(num_req, shape, 0, slot_idx, state_pool, q, k, v, alpha, beta, o);
   a.causal = 1;
-  a.bf16 = shape->io_dtype == FLARE_BF16;
-  a.scale = resolve_scale(shape);
-  a.slot_idx = slot_idx;
-  a.pool = const_cast<float *>(state_pool);  // read only in this mode
-  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
   return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_verify_outputs launch");
 }
 
@@ -428,17 +404,7 @@ flare_status flare_gdn_commit_prefix(int32_t num_req, const int32_t *slot_idx, c
                                      alpha, beta, o, FLARE_BLOCK_COMMIT);
   if (st != FLARE_OK) return st;
   if (num_req > 0 && !accepted) return fail(FLARE_ERR_NULL, "commit_prefix needs the accepted counts");
-  BlockStepArgs a{};
-  a.num_req = num_req;
-  a.H = shape->num_heads;
-  a.D = shape->d_k;
-  a.B = shape->block_size;
-  a.mode = 1;
-  a.bf16 = shape->io_dtype == FLARE_BF16;
-  a.scale = resolve_scale(shape);
-  a.slot_idx = slot_idx;
-  a.pool = state_pool;
-  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+  BlockStepArgs a = step_args(num_req, shape, 1, slot_idx, state_pool, q, k, v, alpha, beta, o);
   a.count = accepted;  // the first accepted[r] tokens are replayed, the rest are identity
   return hip_status(launch_block_step(a, (hipStream_t)stream), "gdn_commit_prefix launch");
 }
