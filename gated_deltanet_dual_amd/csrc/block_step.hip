@@ -6,7 +6,8 @@
 // writes the final state into the pool (COMMIT).  The per-token update is the
 // gated delta rule of Key designs item 2.
 //
-// One workgroup per (request, head).  The whole d x d fp32 state of the pair is
+// One workgroup per (request, head) -- two for 32-token blocks, each owning
+// half of the state's columns.  The workgroup's part of the d x d fp32 state is
 // read once with 16-byte loads and kept in registers: the threads of one
 // 4-column quad are adjacent lanes, each holding every NRG-th row, so the sums
 // over rows are DPP reductions across those lanes with no LDS partials.  The
@@ -23,7 +24,12 @@
 //           tokens, and the state after every token, S_t = a_t S_{t-1} +
 //           b_t k_t u_t^T, written to a candidate buffer; the pool is not
 //           written.  A later scatter copies candidate r into the pool once r
-//           tokens are accepted.
+//           tokens are accepted.  The same rollback by replay: EVAL with
+//           causal reads (COMMIT's outputs, nothing written), then a COMMIT
+//           of each request's accepted prefix (per-request token counts).
+//   BOUNDARIES (the chunk-then-refine forward): from a chunk-start state, the
+//           per-token recurrence over a window of clean tokens, writing the
+//           state at every block start it passes.
 // with G_i = prod_{m<=i} a_m taken as exp of a cumulative sum of log a.
 // Everything is fp32 on the VALU: the step moves ~4 flop per byte of state, far
 // below the MI355X fp32 ridge, so the kernel is bound by HBM bandwidth.
@@ -87,7 +93,10 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
   const int t = threadIdx.x;
   const int rg = t % NRG, cq = t / NRG;
 
-  __shared__ __align__(16) float sX[NV][D];   // k_0..k_{B-1} at 0.., q_0..q_{B-1} at BMAX..
+  // k_0..k_{B-1} at 0.., q_0..q_{B-1} at BMAX..; rows padded by 4 floats so the
+  // 16 rows of a matrix-core fragment fall in different LDS banks
+  constexpr int LDXS = D + 4;
+  __shared__ __align__(16) float sX[NV][LDXS];
   __shared__ __align__(16) float sV[BMAX][DV];
   __shared__ __align__(16) float sW[NV][DV];   // S^T x for every x in sX (this workgroup's columns)
   __shared__ __align__(16) float sU[BMAX][DV];
@@ -272,9 +281,28 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
       }
     }
 
-    // 2. B x B dot products k_i.k_j and q_l.k_j, 16 lanes per dot (a DPP row),
-    //    while the state is still in flight
-    {
+    // 2. B x B dot products k_i.k_j and q_l.k_j while the state is still in
+    //    flight: for bf16 io and blocks of up to 32 tokens on the matrix cores
+    //    (the rows are exact in bf16; 16 x 16 tiles of KK^T and QK^T, two per
+    //    wave), otherwise 16 lanes per dot (a DPP row)
+    constexpr bool MFMA_DOTS = sizeof(IO) == 2 && BMAX >= 16 && D % 32 == 0;
+    if constexpr (MFMA_DOTS) {
+      const int nt = (B + 15) / 16;  // tiles in use per side
+      const int wv = __builtin_amdgcn_readfirstlane(t >> 6), ln = t & 63;
+      for (int tt = wv; tt < 8; tt += NT / 64) {  // tile tt: which (KK^T, QK^T), ti, tj
+        const int which = tt >> 2, ti = (tt >> 1) & 1, tj = tt & 1;
+        if (ti >= nt || tj >= nt) continue;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+          mma_bf16(acc, frag_f32_hi(&sX[which ? BMAX : 0][0], LDXS, 16 * ti, 32 * ks),
+                   frag_f32_hi(&sX[0][0], LDXS, 16 * tj, 32 * ks));
+        // accumulator lane layout: rows 4 (lane / 16) + r, column lane % 16
+        float (*dst)[BMAX] = which ? sQK : sKK;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[16 * ti + 4 * (ln >> 4) + r][16 * tj + (ln & 15)] = acc[r];
+      }
+    } else {
       constexpr int GROUPS = NT / 16, PER = D / 16;
       const int grp = t / 16, sub = t % 16;
       const int ndots = 2 * B * B;
