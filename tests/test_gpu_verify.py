@@ -2,8 +2,8 @@
 (through the C-ABI binding) against the fp64 oracle (oracle.gdn_verify,
 oracle.gdn_scatter):
   * verify: per-token outputs and the candidate state after every drafted
-    token, for K in {4, 8}, d in {16 (fp32 io), 128 (bf16 io)}; the pool is
-    bit-identical afterwards;
+    token, for K in {4, 8, 16, 32}, d in {16 (fp32 io), 128 (bf16 io)}; the
+    pool is bit-identical afterwards;
   * scatter: accepted counts 0, 1..K and out of range (clamped); the accepted
     candidate lands in its slot bit for bit, every other slot (and a slot whose
     count is 0) is bit-identical to before, and the result matches the oracle's
@@ -69,7 +69,8 @@ def run(g, dev, case, accepted, bf16):
     return to_np(o), cand_np, gpool.cpu().numpy()
 
 
-@pytest.mark.parametrize("K,d,bf16", [(4, 16, False), (8, 16, False), (4, 128, True), (8, 128, True)])
+@pytest.mark.parametrize("K,d,bf16", [(4, 16, False), (8, 16, False), (4, 128, True), (8, 128, True),
+                                      (16, 128, True), (32, 128, True), (16, 16, False)])
 def test_verify_and_scatter_small(g, dev, K, d, bf16):
     R, H, n_slots = 6, 2, 11
     case = draw(10 + K + d, R, K, H, d, n_slots, bf16)
@@ -110,7 +111,7 @@ def test_verify_and_scatter_full_serving_shape(g, dev):
     assert np.array_equal(newpool[others], s.pool[others])
 
 
-@pytest.mark.parametrize("K,d,bf16", [(4, 16, False), (8, 128, True)])
+@pytest.mark.parametrize("K,d,bf16", [(4, 16, False), (8, 128, True), (32, 128, True)])
 def test_replay_pair_small(g, dev, K, d, bf16):
     import torch
     R, H, n_slots = 6, 2, 11
