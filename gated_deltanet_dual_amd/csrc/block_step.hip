@@ -36,6 +36,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "serving.h"
+#include "slab.h"
 #include "timing.h"
 
 namespace flare {
@@ -118,7 +119,14 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
   // table mode: the request's first token row
   const int64_t rbase = a.row0 ? (int64_t)a.row0[req] : (int64_t)req * B;
   auto trow = [&](int r) { return rbase + (r < cnt ? r : max(cnt - 1, 0)); };  // loads stay on real rows
-  float4 s4[RPG];
+  // MF (bf16 io, 32-token blocks, half-row workgroups): the state's pass runs
+  // on the matrix cores and the state is held in their operand layout -- wave
+  // w's lane (n, g) holds column 16 w + n of its part, rows 32 ks + 8 g + e
+  // (ks, e < 4, 8); otherwise the (rg, cq) layout below
+  constexpr bool MF = sizeof(IO) == 2 && BMAX == 32 && D == 128 && DV == 64;
+  float4 s4[MF ? 1 : RPG];
+  float sf[MF ? 4 : 1][8];
+  const int wvs = __builtin_amdgcn_readfirstlane(t >> 6), n16 = t & 15, kg = (t & 63) >> 4;
   {
     // 0. the block inputs first (16-byte loads into registers), then the
     //    state: vector-memory results return in issue order, so the small B x B
@@ -175,9 +183,17 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
     // the state: thread (rg, cq) holds rows rg * RPG .. + RPG - 1, columns
     // 4 cq .. 4 cq + 3 (a wave reads whole 128-byte row segments); nothing
     // waits for it until the reduction
+    if constexpr (MF) {
+      const float *Sw = S + 16 * wvs + n16;
 #pragma unroll
-    for (int i = 0; i < RPG; ++i)
-      s4[i] = *reinterpret_cast<const float4 *>(S + (size_t)(rg * RPG + i) * D + 4 * cq);
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sf[ks][e] = Sw[(size_t)(32 * ks + 8 * kg + e) * D];
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPG; ++i)
+        s4[i] = *reinterpret_cast<const float4 *>(S + (size_t)(rg * RPG + i) * D + 4 * cq);
+    }
 
     // 1. block inputs -> LDS as fp32 (CONV: the raw rows, convolved below)
 #pragma unroll
@@ -359,8 +375,30 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
       }
     }
 
-    // 4. one pass over the state: W[x] = S^T x for the 2B vectors, G at a time;
-    //    the row-group partials are summed across adjacent lanes (DPP)
+    // 4. one pass over the state: W[x] = S^T x for the 2B vectors.  MF: as
+    //    16 x 16 x 32 bf16 tiles, the k / q rows exact in bf16, S split hi + lo,
+    //    wave w the 16 columns it holds.  Otherwise G vectors at a time, the
+    //    row-group partials summed across adjacent lanes (DPP).
+    if constexpr (MF) {
+      bf16x8 sh[4], sl[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) split8(sf[ks], sh[ks], sl[ks]);
+      const int nt = (B + 15) / 16;  // row tiles in use per half (k, q)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {  // rows 16 mt of sX / sW: k tiles 0, 1, q tiles 2, 3
+        if ((mt & 1) >= nt) continue;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 ax = frag_f32_hi(&sX[0][0], LDXS, 16 * mt, 32 * ks);
+          mma_bf16(acc, ax, sh[ks]);
+          mma_bf16(acc, ax, sl[ks]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sW[16 * mt + 4 * kg + r][16 * wvs + n16] = acc[r];
+      }
+    }
+    if constexpr (!MF)
     for (int v0 = 0; v0 < 2 * B; v0 += G) {
       float4 acc[G];
 #pragma unroll
@@ -450,7 +488,56 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
 #pragma unroll
       for (int i = 0; i < RPG; ++i) *reinterpret_cast<float4 *>(p + i * D) = n[i];
     };
-    if constexpr (KIND == 1) {
+    // MF layout: one token's update n = a n + (b k_j) u_j^T and the stores
+    auto mf_step = [&](float (*nn)[8], int j, float aj, float wk) {
+      const float u = sU[j][16 * wvs + n16];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float4 k0 = *reinterpret_cast<const float4 *>(&sX[j][32 * ks + 8 * kg]);
+        const float4 k1 = *reinterpret_cast<const float4 *>(&sX[j][32 * ks + 8 * kg + 4]);
+        const float kr[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) nn[ks][e] = aj * nn[ks][e] + (kr[e] * wk) * u;
+      }
+    };
+    auto mf_store = [&](float *base, const float (*nn)[8]) {
+      float *const p = base + 16 * wvs + n16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[(size_t)(32 * ks + 8 * kg + e) * D] = nn[ks][e];
+    };
+    if constexpr (MF && KIND == 1) {
+      const float ge = __expf(sG[last]);
+      float nn[4][8];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) nn[ks][e] = ge * sf[ks][e];
+      for (int j = 0; j < B; ++j) mf_step(nn, j, 1.f, __expf(sG[last] - sG[j]) * sBeta[j]);
+      mf_store(a.pool_out ? a.pool_out + ((size_t)req * a.H + h) * D * D + col0 : S, nn);
+    } else if constexpr (MF && KIND == 2) {
+      const bool bounds = a.mode == 3;
+      const int lo = bounds ? a.blo[req] : 0, g0 = bounds ? a.bg0[req] : 0, bB = bounds ? a.bB : 1;
+      const size_t tstride = (size_t)a.H * D * D;
+      float *const cand = bounds ? nullptr : a.cand + ((size_t)req * B * a.H + h) * D * D + col0;
+      auto bnd = [&](int q) { return a.pool_out + ((size_t)(g0 + (q - lo) / bB) * a.H + h) * D * D + col0; };
+      float nn[4][8];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) nn[ks][e] = sf[ks][e];
+      if (bounds && lo == 0) mf_store(bnd(0), nn);
+      for (int j = 0; j < B; ++j) {
+        mf_step(nn, j, __expf(sG[j] - (j > 0 ? sG[j - 1] : 0.f)), sBeta[j]);
+        if (!bounds) {
+          mf_store(cand + j * tstride, nn);
+        } else {
+          const int q = j + 1;
+          if (q >= lo && (q - lo) % bB == 0) mf_store(bnd(q), nn);
+        }
+      }
+    } else if constexpr (KIND == 1) {
       const float ge = __expf(sG[last]);
       float4 n[RPG];
 #pragma unroll
