@@ -74,8 +74,8 @@ def test_eval_repeatable_and_commit_without_outputs(g, dev):
     assert rel_rms(to_np(pool), ref_pool) <= 1e-5
 
 
-@pytest.mark.parametrize("B,d,io", [(1, 128, "bf16"), (8, 128, "bf16"), (32, 128, "bf16"),
-                                    (4, 16, "f32"), (16, 16, "f32")])
+@pytest.mark.parametrize("B,d,io", [(1, 128, "bf16"), (8, 128, "bf16"), (16, 128, "bf16"), (32, 128, "bf16"),
+                                    (4, 16, "f32"), (16, 16, "f32"), (16, 128, "f32"), (32, 128, "f32")])
 def test_block_step_sizes(g, dev, B, d, io):
     import torch
     rng = np.random.default_rng(42 + B + d)
