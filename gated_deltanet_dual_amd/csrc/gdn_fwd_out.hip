@@ -42,7 +42,7 @@ struct OutSmem {
 }  // namespace
 
 __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const float *cmat, const float *states) {
-  constexpr int C = oC, D = oD, NT = oNT, LDX = oLDX, LDM = oLDM;
+  constexpr int C = oC, D = oD, NT = oNT, LDM = oLDM;
   __shared__ OutSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;

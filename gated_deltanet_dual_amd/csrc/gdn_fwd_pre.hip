@@ -37,7 +37,7 @@ struct FwdPreSmem {
 }  // namespace
 
 __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const float *cmat, float *pack_all) {
-  constexpr int C = fC, D = fD, NT = fNT, LDM = fLDM;
+  constexpr int C = fC, D = fD, LDM = fLDM;
   __shared__ FwdPreSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
