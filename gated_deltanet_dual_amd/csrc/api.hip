@@ -141,9 +141,13 @@ flare_status flare_gdn_dual_fwd_route1(const flare_varlen *varlen, const flare_g
   if (vi.total_tokens > 0 && (!workspace || workspace_bytes < need))
     return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (((uintptr_t)workspace & 255u) != 0) return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (vi.total_tokens == 0) return FLARE_OK;
   FwdArgs a = fwd_args(varlen, shape, vi, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0, o, on, h_final,
                        ckpt, 1);
+  if (vi.total_tokens == 0) {
+    // only empty documents: no block, no window; the forward writes h_final
+    a.workspace = nullptr;
+    return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd_route1 launch");
+  }
   // workspace: the forward's, the boundary states, the plan arrays
   char *w = reinterpret_cast<char *>(workspace);
   const size_t fwd = fwd_workspace_bytes(vi, shape);
