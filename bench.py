@@ -6,11 +6,14 @@
 A step is one pass of the layer's hot path over one batch of the headline
 workload -- 4 documents x 8192 tokens (prompt 2048, response in blocks of
 B = 4), 16 heads, d_k = d_v = 128, bf16 q/k/v with fp32 gates and state:
-the dual-stream forward and, once the backward exists, the backward.  Inputs are
-resident in HBM before the timed region.  The serving cycle (256 requests x 16
-heads, four EVALs + one COMMIT) and the packed ShortConv (32768 tokens, 8
-documents, 3x32x128 channels) are timed in the same run and reported under
-"components".  Rank 0 prints one JSON line.
+the dual-stream forward (chunk-start states saved) and the backward.  Inputs are
+resident in HBM before the timed region.  Also timed in the same run and
+reported under "components": the inference forward; the serving cycle (256
+requests x 16 heads, four EVALs + one COMMIT), AR-Trust (verify + scatter, and
+the replay pair), the serving conv step; the packed ShortConv and its reverse
+mode (32768 tokens, 8 documents, 3x32x128 channels); the packed layer
+(unfused, fused, training); the masked route against chunk-then-refine at
+blocks of 4 to 32.  One JSON line is printed.
 
 Method: "FLARE: Diffusion for Hybrid Language Model" (papernotes.org notes),
 Overall framework and Key designs items 2-4.

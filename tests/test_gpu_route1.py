@@ -73,7 +73,7 @@ def check(inp, r1, want, tol, name):
         assert not np.any(on[a:a + p]), "noisy prompt rows must be written as 0"
 
 
-@pytest.mark.parametrize("B", [4, 16, 32])
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32])
 def test_route1_fp32_ragged(g, dev, B):
     # prompts are multiples of B; 48 does not start a chunk at B = 16
     P = [B, 0, 2 * B, 0, 3 * B]
