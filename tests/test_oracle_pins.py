@@ -415,3 +415,29 @@ def test_shortconv_bias_and_silu():
     zn = yn0[4:] + bias
     np.testing.assert_allclose(yn1[4:], zn / (1 + np.exp(-zn)), rtol=1e-13)
     np.testing.assert_array_equal(yn1[:4], 0.0)
+
+
+def test_shortconv_silu_and_bias_special_values():
+    """SiLU and the bias pinned by values the sigmoid fixes in closed form:
+    sigma(ln 3) = 3/4 and sigma(-ln 3) = 1/4, so silu(ln 3) = (3/4) ln 3 and
+    silu(-ln 3) = -(1/4) ln 3; silu(0) = 0; silu(x) -> x for large x.  A
+    one-hot current tap passes x through; zero taps leave only the bias, on
+    every row including the first rows of a document."""
+    l3 = np.log(3.0)
+    vals = np.array([0.0, l3, -l3, 40.0])
+    x = np.repeat(vals[:, None], 2, axis=1)  # one document of 4 tokens, 2 channels
+    w = np.zeros((2, 4))
+    w[:, 3] = 1.0  # tap W - 1 multiplies the current token
+    y, _ = oracle.shortconv_dual([0, 4], [4], 4, x, x, w, activation=1)
+    want = np.array([0.0, 0.75 * l3, -0.25 * l3, 40.0])
+    np.testing.assert_allclose(y[:, 0], want, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(y[:, 1], want, rtol=1e-15, atol=1e-15)
+    # zero taps: the activated bias alone, on every row
+    yb, _ = oracle.shortconv_dual([0, 4], [4], 4, x, x, np.zeros((2, 4)), bias=np.array([l3, -l3]),
+                                  activation=1)
+    np.testing.assert_allclose(yb[:, 0], 0.75 * l3, rtol=1e-15)
+    np.testing.assert_allclose(yb[:, 1], -0.25 * l3, rtol=1e-15)
+    # without the activation the bias is a plain shift
+    y0, _ = oracle.shortconv_dual([0, 4], [4], 4, x, x, w)
+    y1, _ = oracle.shortconv_dual([0, 4], [4], 4, x, x, w, bias=np.array([0.5, -2.0]))
+    np.testing.assert_allclose(y1 - y0, np.tile([0.5, -2.0], (4, 1)), rtol=0, atol=1e-15)
