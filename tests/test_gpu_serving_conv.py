@@ -1,7 +1,8 @@
 """GPU parity of the serving step with the ShortConv in front
 (flare_gdn_block_step_conv, flare_conv_cache_fill) through the C-ABI binding,
 against the fp64 oracle (oracle.block_step_conv, oracle.conv_cache_fill):
-  * EVAL and COMMIT from random pools and clean histories, widths 1, 4 and 8,
+  * EVAL and COMMIT from random pools and clean histories, widths 1 to 8
+    (both LDS sizings: up to 4 and up to 8),
     blocks of 4 and 8, fp32 (d = 16) and bf16 (d = 128) io, with and without
     SiLU; EVAL leaves the pool and the history cache bit-identical, COMMIT's
     new history is the exact last W-1 raw rows;
@@ -40,7 +41,8 @@ def _round(x, bf16):
 
 
 @pytest.mark.parametrize("d,io,W,B,act", [(16, "f32", 4, 4, 0), (16, "f32", 1, 8, 1), (128, "bf16", 4, 4, 1),
-                                          (128, "bf16", 8, 8, 0), (128, "bf16", 4, 8, 1)])
+                                          (128, "bf16", 8, 8, 0), (128, "bf16", 4, 8, 1), (16, "f32", 5, 4, 1),
+                                          (128, "bf16", 3, 8, 0), (128, "bf16", 2, 4, 1), (128, "bf16", 6, 4, 1)])
 def test_block_step_conv_modes(g, dev, d, io, W, B, act):
     import torch
     bf16 = io == "bf16"
