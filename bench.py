@@ -1,7 +1,7 @@
 """Benchmark of the dual-stream Gated DeltaNet layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-components] [--only step|infer|serve|conv|layer|routes|copy] [--json-out PATH]
+                    [--no-components] [--only step|infer|serve|serve_sweep|conv|layer|routes|copy] [--json-out PATH]
 
 A step is one pass of the layer's hot path over one batch of the headline
 workload -- 4 documents x 8192 tokens (prompt 2048, response in blocks of
@@ -97,7 +97,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
-    p.add_argument("--only", choices=["step", "infer", "serve", "conv", "layer", "routes", "copy"], default=None,
+    p.add_argument("--only", choices=["step", "infer", "serve", "serve_sweep", "conv", "layer", "routes", "copy"], default=None,
                    help="run one part only (copy: a plain 1 GiB device copy, the reference "
                         "transfer for HBM byte counters)")
     p.add_argument("--json-out", default=None)
@@ -200,6 +200,8 @@ def main():
         comps["shortconv"], comps["shortconv_bwd"] = bench_conv(torch, g, wl, dev, timer, up, args)
     if not args.no_components and args.only in (None, "layer"):
         comps["packed_layer"] = bench_packed_layer(torch, g, wl, dev, timer, up, args)
+    if args.only == "serve_sweep":
+        comps["serving_sweep"] = bench_serving_sweep(torch, g, dev, args)
     if not args.no_components and args.only in (None, "routes"):
         comps["routes"] = bench_routes(torch, g, wl, dev, timer, up, args)
     if comps:
@@ -651,6 +653,53 @@ def bench_packed_layer(torch, g, wl, dev, timer, up, args):
     for k, ms in res.items():
         out[k] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
     out["fused_speedup_fwd"] = res["unfused_fwd"] / res["fused_fwd"]
+    return out
+
+
+def bench_serving_sweep(torch, g, dev, args):
+    """The serving step's efficiency against the number of requests (64 to
+    2048 requests x 16 heads, d = 128, B = 4, bf16): EVAL and COMMIT each
+    timed alone over three rotating pools of 2R random fp32 states, so no
+    call finds its states in the last-level cache.  Not part of the default
+    run."""
+    log("bench: serving step against the request count")
+    H, d, B = 16, 128, 4
+    out = {"workload": "serving block step, R requests x 16 heads, fp32 128x128 states, B=4, bf16, uncached pools"}
+    for R in (64, 128, 256, 512, 1024, 2048):
+        sets = []
+        for r in range(3):
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(10 + r)
+            pool = torch.randn((2 * R, H, d, d), generator=gen, device=dev) / d ** 0.5
+            slot = torch.randperm(2 * R, device=dev)[:R].to(torch.int32)
+            blk = [torch.randn((R, B, H, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(3)]
+            a = torch.rand((R, B, H), generator=gen, device=dev) * 0.15 + 0.85
+            b = torch.rand((R, B, H), generator=gen, device=dev) * 0.8 + 0.1
+            sets.append((slot, pool, blk, a, b))
+        o = torch.empty((R, B, H, d), dtype=torch.bfloat16, device=dev)
+        row = {}
+        state = R * H * d * d * 4
+        io = R * B * H * (3 * d * 2 + 8 + d * 2)
+        for mode, name in ((g.EVAL, "eval"), (g.COMMIT, "commit")):
+            call = lambda s_: g.block_step(s_[0], s_[1], *s_[2], s_[3], s_[4], mode, o=o)
+            for i in range(3):
+                call(sets[i % 3])
+            torch.cuda.synchronize()
+            ev = []
+            for i in range(max(args.steps, 12)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call(sets[i % 3])
+                e1.record()
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+            alg = (state if mode == g.EVAL else 2 * state) + io
+            row[name + "_us"] = 1e3 * ms
+            row[name + "_gbs"] = alg / (ms * 1e-3) / 1e9
+        out["R%d" % R] = row
+        del sets
+        torch.cuda.empty_cache()
     return out
 
 
