@@ -254,14 +254,16 @@ def gdn_dual_fwd_route1(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_
         nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1)
         ckpt = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=q.device)
     need = int(lib().flare_gdn_route1_workspace_size(varlen.ref(), ctypes.byref(shp)))
-    if need == 0:
+    call = lambda ws, nbytes: lib().flare_gdn_dual_fwd_route1(
+        varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(qn), _ptr(kn),
+        _ptr(vn), _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(o), _ptr(on), _ptr(hf), _ptr(ckpt), ws, nbytes,
+        _stream(q.device))
+    if need == 0:  # the size query rejected the call: the entry point names the reason
+        _check(call(None, 0))
         raise FlareError(4, "route1: unsupported shape")
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
-    _check(lib().flare_gdn_dual_fwd_route1(varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                           _ptr(beta), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(alpha_n), _ptr(beta_n),
-                                           _ptr(h0), _ptr(o), _ptr(on), _ptr(hf), _ptr(ckpt), _ptr(workspace),
-                                           workspace.numel(), _stream(q.device)))
+    _check(call(_ptr(workspace), workspace.numel()))
     return o, on, hf, ckpt
 
 
