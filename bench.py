@@ -1,7 +1,7 @@
 """Benchmark of the dual-stream Gated DeltaNet layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-components] [--only step|infer|serve|serve_sweep|conv|layer|routes|copy] [--json-out PATH]
+                    [--no-components] [--only step|step_sweep|infer|serve|serve_sweep|conv|layer|routes|copy] [--json-out PATH]
 
 A step is one pass of the layer's hot path over one batch of the headline
 workload -- 4 documents x 8192 tokens (prompt 2048, response in blocks of
@@ -97,7 +97,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
-    p.add_argument("--only", choices=["step", "infer", "serve", "serve_sweep", "conv", "layer", "routes", "copy"], default=None,
+    p.add_argument("--only", choices=["step", "step_sweep", "infer", "serve", "serve_sweep", "conv", "layer", "routes", "copy"], default=None,
                    help="run one part only (copy: a plain 1 GiB device copy, the reference "
                         "transfer for HBM byte counters)")
     p.add_argument("--json-out", default=None)
@@ -200,6 +200,8 @@ def main():
         comps["shortconv"], comps["shortconv_bwd"] = bench_conv(torch, g, wl, dev, timer, up, args)
     if not args.no_components and args.only in (None, "layer"):
         comps["packed_layer"] = bench_packed_layer(torch, g, wl, dev, timer, up, args)
+    if args.only == "step_sweep":
+        comps["step_sweep"] = bench_step_sweep(torch, g, wl, dev, up, args)
     if args.only == "serve_sweep":
         comps["serving_sweep"] = bench_serving_sweep(torch, g, dev, args)
     if not args.no_components and args.only in (None, "routes"):
@@ -653,6 +655,61 @@ def bench_packed_layer(torch, g, wl, dev, timer, up, args):
     for k, ms in res.items():
         out[k] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
     out["fused_speedup_fwd"] = res["unfused_fwd"] / res["fused_fwd"]
+    return out
+
+
+STEP_KERNELS = ("gdn_tri_kernel", "gdn_fwd_pre_kernel", "gdn_fwd_scan_kernel", "gdn_dual_fwd_kernel",
+                "gdn_bwd_pre_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel")
+
+
+def bench_step_sweep(torch, g, wl, dev, up, args):
+    """The headline step (forward with chunk-start states, backward) at the same
+    32768 tokens packed as 4 x 8192, 8 x 4096, 32 x 1024, 128 x 256 and one
+    document of 32768 (prompt a quarter of each document, B = 4, 16 heads,
+    d = 128, bf16), with per-kernel times.  Not part of the default run."""
+    log("bench: training step against the packing of 32768 tokens")
+    H, d, B = 16, 128, 4
+    out = {"workload": "dual-stream GDN fwd (states) + bwd, 32768 tokens in N documents, H=16, d=128, B=4, bf16"}
+    for ndoc, L in ((4, 8192), (8, 4096), (32, 1024), (128, 256), (1, 32768)):
+        inp = wl.gdn_inputs([L] * ndoc, [L // 4] * ndoc, H, d, d, B, seed=5, with_grads=True, round_io=False)
+        a10 = [up(inp.q, True), up(inp.k, True), up(inp.v, True), up(inp.alpha), up(inp.beta), up(inp.qn, True),
+               up(inp.kn, True), up(inp.vn, True), up(inp.alpha_n), up(inp.beta_n)]
+        do, don = up(inp.do, True), up(inp.don, True)
+        vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+        T = inp.T
+        o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+        on = torch.empty_like(o)
+        ckpt = torch.empty((T // g.chunk_size() + ndoc, H, d, d), dtype=torch.float32, device=dev)
+        fws = torch.empty((max(g.workspace_bytes(vl, H, d, B, g.BF16), 256),), dtype=torch.uint8, device=dev)
+        ws = torch.empty((g.lib().flare_gdn_dual_workspace_size(vl.ref(), ctypes.byref(g._shape(H, d, B, g.BF16)),
+                                                                 1),), dtype=torch.uint8, device=dev)
+        g.gdn_dual_fwd(vl, *a10, B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
+        grads = g.gdn_dual_bwd(vl, *a10, B, ckpt, do, don, workspace=ws, fwd_workspace=fws)
+
+        def step():
+            g.gdn_dual_fwd(vl, *a10, B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
+            g.gdn_dual_bwd(vl, *a10, B, ckpt, do, don, out=grads, workspace=ws, fwd_workspace=fws)
+
+        for _ in range(max(args.warmup, 2)):
+            step()
+        torch.cuda.synchronize()
+        g.timing_reset()
+        g.timing_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(args.steps, 5)
+        e0.record()
+        for _ in range(n):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        row = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
+        for k in STEP_KERNELS:
+            row[k] = g.timing_avg_ms(k)[0]
+        g.timing_enable(False)
+        out["%dx%d" % (ndoc, L)] = row
+        del a10, do, don, o, on, ckpt, fws, ws, grads
+        torch.cuda.empty_cache()
     return out
 
 

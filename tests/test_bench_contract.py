@@ -22,5 +22,5 @@ def test_more_than_one_gpu_is_refused():
 def test_help_lists_the_sections():
     r = run("--help")
     assert r.returncode == 0
-    for name in ("step", "infer", "serve", "serve_sweep", "conv", "layer", "routes", "copy"):
+    for name in ("step", "step_sweep", "infer", "serve", "serve_sweep", "conv", "layer", "routes", "copy"):
         assert name in r.stdout
