@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from gated_deltanet_dual_amd import workloads as wl
-from gpu_util import TOL_BF16, TOL_F32, fwd_args, rel_rms, sub_heads, to_dev, to_np
+from gpu_util import TOL_BF16, TOL_F32, fwd_args, rel_rms, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -99,27 +99,47 @@ def test_bwd_deterministic(g, dev):
         assert torch.equal(g1[k], g2[k]), k
 
 
-def test_bwd_headline_full_size_sampled_heads(g, dev):
+def test_bwd_headline_full_size_all_heads(g, dev):
     """4 docs x 8192 tokens (prompt 2048), B=4, H=16, d=128, bf16; the oracle
-    checks heads 3 and 12 at full length."""
+    checks every head at full length."""
     inp = wl.headline(with_grads=True)
-    gr = run_bwd(g, inp, dev)
-    heads = [3, 12]
-    sub = sub_heads(inp, heads)
-    want = ref_bwd(sub)
-    got = {k: (v[:, heads] if k != "dh0" else v[:, heads]) for k, v in gr.items()}
-    check(sub, got, want, TOL_BF16, "bwd_headline")
+    check(inp, run_bwd(g, inp, dev), ref_bwd(inp), TOL_BF16, "bwd_headline")
 
 
-def test_bwd_packed_full_size_sampled_heads(g, dev):
+def test_bench_step_configuration_full_size(g, dev):
+    """The training step exactly as the benchmark times it: the forward into
+    caller buffers with the chunk-start states saved, no final state and the
+    forward's workspace kept; the backward reading that workspace's chunk
+    matrices.  Outputs and all eleven gradients against the oracle, every head
+    of the 4 x 8192 workload."""
+    import torch
+    inp = wl.headline(with_grads=True)
+    T, H, d, B = inp.T, inp.H, 128, inp.block_size
+    vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+    args = fwd_args(inp, dev)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    on = torch.empty_like(o)
+    ckpt = torch.empty((g.ckpt_slots(vl, H, d, B, g.BF16), H, d, d), dtype=torch.float32, device=dev)
+    fws = torch.empty((g.workspace_bytes(vl, H, d, B, g.BF16),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((g.workspace_bytes(vl, H, d, B, g.BF16, for_bwd=True),), dtype=torch.uint8, device=dev)
+    _, _, hf, _ = g.gdn_dual_fwd(vl, *args, B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
+    assert hf is None
+    gr = g.gdn_dual_bwd(vl, *args, B, ckpt, to_dev(inp.do, dev, True), to_dev(inp.don, dev, True),
+                        workspace=ws, fwd_workspace=fws)
+    torch.cuda.synchronize()
+    ro, ron, _ = oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(), B)
+    e = {"o": rel_rms(to_np(o), ro), "on": rel_rms(to_np(on), ron)}
+    print("bench_step fwd", e)
+    assert max(e.values()) <= TOL_BF16, e
+    check(inp, gr, ref_bwd(inp), TOL_BF16, "bench_step")
+
+
+def test_bwd_packed_full_size_all_heads(g, dev):
     """One packed row of 32768 tokens, 8 Dirichlet-length documents, 32 heads,
-    d=128, bf16 (q/k pre-normalised); the oracle checks heads 7 and 24."""
+    d=128, bf16 (q/k pre-normalised); the oracle checks every head."""
     lens, prompts = wl.packed_doc_lengths(32768, 8, 4, seed=3)
     inp = wl.gdn_inputs(lens, prompts, 32, 128, 128, 4, seed=13, with_grads=True)
-    gr = run_bwd(g, inp, dev)
-    heads = [7, 24]
-    sub = sub_heads(inp, heads)
-    check(sub, {k: v[:, heads] for k, v in gr.items()}, ref_bwd(sub), TOL_BF16, "bwd_packed")
+    check(inp, run_bwd(g, inp, dev), ref_bwd(inp), TOL_BF16, "bwd_packed")
 
 
 def test_bwd_reusing_forward_chunk_matrices_is_identical(g, dev):

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from gated_deltanet_dual_amd import workloads as wl
-from gpu_util import TOL_BF16, TOL_F32, fwd_args, rel_rms, sub_heads, to_dev, to_np
+from gpu_util import TOL_BF16, TOL_F32, fwd_args, rel_rms, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +100,4 @@ def test_route1_bf16_d128(g, dev, B):
 def test_route1_dual_full_size(g, dev, B):
     inp = wl.dual_bf16(block_size=B)
     r1, _ = run_both(g, inp, dev)
-    heads = [3, 12]
-    sub = sub_heads(inp, heads)
-    got = (r1[0][:, heads], r1[1][:, heads], r1[2][:, heads])
-    check(sub, got, ref(sub), TOL_BF16, "route1_dual_B%d" % B)
+    check(inp, r1[:3], ref(inp), TOL_BF16, "route1_dual_B%d" % B)
