@@ -157,6 +157,164 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# ---------------------------------------------------------------- argument checks
+# The library sees bare device pointers, so every tensor is checked here
+# before the call: dtype, shape (the one the shape struct implies), C
+# contiguity and device.  A mismatch raises FlareError and nothing is launched.
+
+def _fail(msg, status=2):
+    raise FlareError(status, msg)
+
+
+def _gpu_device(t, name):
+    if t is None:
+        _fail("%s is required" % name, 1)
+    if not t.is_cuda:
+        _fail("%s must be a GPU tensor (it is on %s)" % (name, t.device))
+    return t.device
+
+
+def _chk(t, name, shape, dtype, device, optional=False):
+    """t has exactly this shape and dtype, is C-contiguous and on device."""
+    if t is None:
+        if optional:
+            return
+        _fail("%s is required" % name, 1)
+    if t.dtype != dtype:
+        _fail("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        _fail("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        _fail("%s must be contiguous" % name, 3)
+    if t.device != device:
+        _fail("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _chk_buf(t, name, need_bytes, dtype, device, optional=False):
+    """A flat buffer (workspace, checkpoints, candidates): dtype, contiguity,
+    device, and at least need_bytes."""
+    if t is None:
+        if optional:
+            return
+        _fail("%s is required" % name, 1)
+    if t.dtype != dtype:
+        _fail("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        _fail("%s must be contiguous" % name, 3)
+    if t.device != device:
+        _fail("%s is on %s, expected %s" % (name, t.device, device))
+    have = t.numel() * t.element_size()
+    if have < need_bytes:
+        _fail("%s holds %d bytes, %d needed" % (name, have, need_bytes), 5)
+
+
+def _chk_varlen(varlen, T, device):
+    if varlen.cu_dev.device != device:
+        _fail("varlen's device arrays are on %s, the tensors on %s" % (varlen.cu_dev.device, device))
+    if T != varlen.total_tokens:
+        _fail("tensors hold %d tokens, cu_seqlens[-1] = %d" % (T, varlen.total_tokens))
+
+
+def _io_dtype_of(t, name="q"):
+    torch = _torch()
+    if t is None:
+        _fail("%s is required" % name, 1)
+    if t.dtype not in (torch.bfloat16, torch.float32):
+        _fail("%s: io tensors must be bfloat16 or float32, got %s" % (name, t.dtype), 4)
+    return t.dtype
+
+
+def _chk_gdn_inputs(varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0=None):
+    """The ten layer inputs and h0; returns (T, H, d, io dtype, device)."""
+    torch = _torch()
+    dev = _gpu_device(q, "q")
+    io = _io_dtype_of(q)
+    if q.dim() != 3:
+        _fail("q must be [T, H, d], got shape %s" % (tuple(q.shape),))
+    T, H, d = q.shape
+    _chk_varlen(varlen, T, dev)
+    for name, t in (("q", q), ("k", k), ("v", v), ("qn", qn), ("kn", kn), ("vn", vn)):
+        _chk(t, name, (T, H, d), io, dev)
+    for name, t in (("alpha", alpha), ("beta", beta), ("alpha_n", alpha_n), ("beta_n", beta_n)):
+        _chk(t, name, (T, H), torch.float32, dev)
+    _chk(h0, "h0", (varlen.num_docs, H, d, d), torch.float32, dev, optional=True)
+    return T, H, d, io, dev
+
+
+def _chk_rows(t, name, lead, H, d, io, dev, optional=False):
+    """A serving-step tensor [lead..., H, d] of the io dtype."""
+    _chk(t, name, tuple(lead) + (H, d), io, dev, optional)
+
+
+def _chk_pool(pool, H, d, dev):
+    torch = _torch()
+    if pool is None or pool.dim() != 4:
+        _fail("pool must be [n_slots, H, d, d]")
+    _chk(pool, "pool", (pool.shape[0], H, d, d), torch.float32, dev)
+
+
+def _chk_conv_inputs(varlen, x, xn, weight, bias):
+    """ShortConv inputs x, xn [T, C] io, weight [C, W] fp32, bias [C] fp32 or
+    None; returns (T, C, W, device)."""
+    torch = _torch()
+    dev = _gpu_device(x, "x")
+    io = _io_dtype_of(x, "x")
+    if x.dim() != 2 or weight is None or weight.dim() != 2:
+        _fail("x must be [T, C] and weight [C, W]")
+    T, C = x.shape
+    W = weight.shape[1]
+    _chk_varlen(varlen, T, dev)
+    _chk(x, "x", (T, C), io, dev)
+    _chk(xn, "xn", (T, C), io, dev)
+    _chk(weight, "weight", (C, W), torch.float32, dev)
+    _chk(bias, "bias", (C,), torch.float32, dev, optional=True)
+    return T, C, W, dev
+
+
+def _chk_three(ts, name, shape, dtype, dev):
+    if ts is None or len(ts) != 3:
+        _fail("%s must be a list of three tensors" % name, 1)
+    for i, t in enumerate(ts):
+        _chk(t, "%s[%d]" % (name, i), shape, dtype, dev)
+
+
+def _chk_prologue_inputs(varlen, xs, xns, weights):
+    """The prologue's three clean and three noisy projections [T, C] io and
+    three weights [C, W] fp32; returns (T, C, W, device)."""
+    torch = _torch()
+    if xs is None or len(xs) != 3 or xs[0] is None or xs[0].dim() != 2:
+        _fail("xs must be three [T, H*head_dim] io tensors")
+    if weights is None or len(weights) != 3 or weights[0] is None or weights[0].dim() != 2:
+        _fail("weights must be three [H*head_dim, W] fp32 tensors")
+    dev = _gpu_device(xs[0], "xs[0]")
+    io = _io_dtype_of(xs[0], "xs[0]")
+    T, C = xs[0].shape
+    W = weights[0].shape[1]
+    _chk_varlen(varlen, T, dev)
+    _chk_three(xs, "xs", (T, C), io, dev)
+    _chk_three(xns, "xns", (T, C), io, dev)
+    _chk_three(weights, "weights", (C, W), torch.float32, dev)
+    return T, C, W, dev
+
+
+def _chk_step_inputs(slot_idx, pool, q, k, v, alpha, beta):
+    """Serving-step inputs q, k, v [R, B, H, d] io, gates [R, B, H] fp32,
+    slot_idx [R] int32, pool [n_slots, H, d, d] fp32; returns (R, B, H, d, dev)."""
+    torch = _torch()
+    dev = _gpu_device(q, "q")
+    io = _io_dtype_of(q)
+    if q.dim() != 4:
+        _fail("q must be [R, B, H, d], got shape %s" % (tuple(q.shape),))
+    R, B, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _chk_rows(t, name, (R, B), H, d, io, dev)
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _chk(t, name, (R, B, H), torch.float32, dev)
+    _chk(slot_idx, "slot_idx", (R,), torch.int32, dev)
+    _chk_pool(pool, H, d, dev)
+    return R, B, H, d, dev
+
+
 class Varlen:
     """Packed batch description: cu_seqlens [N+1] and prompt_lens [N], kept both on
     the host (validated before launch) and on the device (read by the kernels)."""
@@ -188,11 +346,7 @@ def _shape(H, d, B, io, flags=0, scale=0.0):
 
 def _io_of(t):
     torch = _torch()
-    if t.dtype == torch.bfloat16:
-        return BF16
-    if t.dtype == torch.float32:
-        return F32
-    raise TypeError("io tensors must be bfloat16 or float32, got %s" % t.dtype)
+    return BF16 if _io_dtype_of(t) == torch.bfloat16 else F32
 
 
 def ckpt_slots(varlen: Varlen, H: int, d: int, B: int, io: int, stride: int = 1) -> int:
@@ -210,7 +364,7 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
     bytes (allocated here when needed and not given).  Returns
     (o, on, h_final, ckpt)."""
     torch = _torch()
-    T, H, d = q.shape
+    T, H, d, iot, dev = _chk_gdn_inputs(varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0)
     io = _io_of(q)
     shp = _shape(H, d, block_size, io, flags, scale)
     if out is None:
@@ -218,16 +372,21 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
         on = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
     else:
         o, on = out
+        _chk(o, "o", (T, H, d), iot, dev)
+        _chk(on, "on", (T, H, d), iot, dev)
     hf = torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=q.device) if want_h_final else None
     ck = ckpt
-    if ck is None and want_ckpt:
+    if ck is not None or want_ckpt:
         nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1)
         if nbytes == 0:
             raise FlareError(2, "invalid arguments for the checkpoint size")
-        ck = torch.empty((nbytes // (H * d * d * 4), H, d, d), dtype=torch.float32, device=q.device)
+        if ck is None:
+            ck = torch.empty((nbytes // (H * d * d * 4), H, d, d), dtype=torch.float32, device=q.device)
+        _chk_buf(ck, "ckpt", nbytes, torch.float32, dev)
     ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 0)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    _chk_buf(workspace, "workspace", ws_bytes, torch.uint8, dev, optional=ws_bytes == 0)
     _check(lib().flare_gdn_dual_fwd(varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(alpha), _ptr(beta), _ptr(qn), _ptr(kn), _ptr(vn),
                                     _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(o), _ptr(on),
@@ -242,17 +401,20 @@ def gdn_dual_fwd_route1(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_
     its chunk-start states, every block-boundary state materialised, every
     noisy block refined from it.  Returns (o, on, h_final, ckpt)."""
     torch = _torch()
-    T, H, d = q.shape
+    T, H, d, iot, dev = _chk_gdn_inputs(varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0)
     shp = _shape(H, d, block_size, _io_of(q), 0, scale)
     if out is None:
         o = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
         on = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
     else:
         o, on = out
+        _chk(o, "o", (T, H, d), iot, dev)
+        _chk(on, "on", (T, H, d), iot, dev)
     hf = torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=q.device) if want_h_final else None
+    nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1)
     if ckpt is None:
-        nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1)
         ckpt = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=q.device)
+    _chk_buf(ckpt, "ckpt", nbytes, torch.float32, dev)
     need = int(lib().flare_gdn_route1_workspace_size(varlen.ref(), ctypes.byref(shp)))
     call = lambda ws, nbytes: lib().flare_gdn_dual_fwd_route1(
         varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(qn), _ptr(kn),
@@ -263,6 +425,7 @@ def gdn_dual_fwd_route1(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_
         raise FlareError(4, "route1: unsupported shape")
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _chk_buf(workspace, "workspace", need, torch.uint8, dev)
     _check(call(_ptr(workspace), workspace.numel()))
     return o, on, hf, ckpt
 
@@ -273,16 +436,21 @@ def gdn_dual_fwd_pool(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n,
     from pool[doc_slot[i]] (read_initial) or zero, and its final state written
     to pool[doc_slot[i]].  doc_slot: device int32 [N].  Returns (o, on)."""
     torch = _torch()
-    T, H, d = q.shape
+    T, H, d, iot, dev = _chk_gdn_inputs(varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n)
+    _chk(doc_slot, "doc_slot", (varlen.num_docs,), torch.int32, dev)
+    _chk_pool(pool, H, d, dev)
     shp = _shape(H, d, block_size, _io_of(q), flags, scale)
     if out is None:
         o = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
         on = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
     else:
         o, on = out
+        _chk(o, "o", (T, H, d), iot, dev)
+        _chk(on, "on", (T, H, d), iot, dev)
     ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 0)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    _chk_buf(workspace, "workspace", ws_bytes, torch.uint8, dev, optional=ws_bytes == 0)
     host = None
     if doc_slot_host is not None:
         host = np.ascontiguousarray(np.asarray(doc_slot_host, dtype=np.int32))
@@ -304,20 +472,32 @@ def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
     workspace of the forward call that produced `ckpt` (its chunk matrices are
     then reused)."""
     torch = _torch()
-    T, H, d = q.shape
+    T, H, d, iot, dev = _chk_gdn_inputs(varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0)
     io = _io_of(q)
     shp = _shape(H, d, block_size, io, flags, scale)
-    dev = q.device
+    N = varlen.num_docs
+    _chk(d_o, "d_o", (T, H, d), iot, dev)
+    _chk(d_on, "d_on", (T, H, d), iot, dev)
+    _chk(dh_final, "dh_final", (N, H, d, d), torch.float32, dev, optional=True)
+    _chk_buf(ckpt, "ckpt", lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1), torch.float32, dev)
+    _chk_buf(fwd_workspace, "fwd_workspace", lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 0),
+             torch.uint8, dev, optional=True)
     ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 1)
     if workspace is None:
         workspace = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    _chk_buf(workspace, "workspace", ws_bytes, torch.uint8, dev)
     g = out if out is not None else {
         "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
         "dalpha": torch.empty_like(alpha), "dbeta": torch.empty_like(beta),
         "dqn": torch.empty_like(qn), "dkn": torch.empty_like(kn), "dvn": torch.empty_like(vn),
         "dalpha_n": torch.empty_like(alpha_n), "dbeta_n": torch.empty_like(beta_n),
-        "dh0": torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=dev) if want_dh0 else None,
+        "dh0": torch.empty((N, H, d, d), dtype=torch.float32, device=dev) if want_dh0 else None,
     }
+    for name in ("dq", "dk", "dv", "dqn", "dkn", "dvn"):
+        _chk(g.get(name), name, (T, H, d), iot, dev)
+    for name in ("dalpha", "dbeta", "dalpha_n", "dbeta_n"):
+        _chk(g.get(name), name, (T, H), torch.float32, dev)
+    _chk(g.get("dh0"), "dh0", (N, H, d, d), torch.float32, dev, optional=True)
     _check(lib().flare_gdn_dual_bwd(
         varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
         _ptr(qn), _ptr(kn), _ptr(vn), _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(ckpt), 1,
@@ -333,12 +513,13 @@ def block_step(slot_idx, pool, q, k, v, alpha, beta, mode, scale=0.0, slot_idx_h
     q,k,v [R,B,H,d]; gates [R,B,H].  Returns o [R,B,H,d] (None for COMMIT when
     o is not wanted: pass o=False)."""
     torch = _torch()
-    R, B, H, d = q.shape
+    R, B, H, d, dev = _chk_step_inputs(slot_idx, pool, q, k, v, alpha, beta)
     shp = _shape(H, d, B, _io_of(q), 0, scale)
     if o is None:
         o = torch.empty((R, B, H, d), dtype=q.dtype, device=q.device)
     elif o is False:
         o = None
+    _chk_rows(o, "o", (R, B), H, d, q.dtype, dev, optional=True)
     host = None
     if slot_idx_host is not None:
         host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
@@ -355,13 +536,20 @@ def block_step_conv(slot_idx, pool, cache, weights, xq, xk, xv, alpha, beta, mod
     projections; cache [n_slots, W-1, 3, H*d] io clean histories (None for
     W = 1); weights: three [H*d, W] fp32.  Returns o [R,B,H,d]."""
     torch = _torch()
-    R, B, H, d = xq.shape
+    R, B, H, d, dev = _chk_step_inputs(slot_idx, pool, xq, xk, xv, alpha, beta)
+    if weights is None or len(weights) != 3 or weights[0] is None or weights[0].dim() != 2:
+        _fail("weights must be three [H*d, W] fp32 tensors")
     W = weights[0].shape[1]
+    for i, w in enumerate(weights):
+        _chk(w, "weights[%d]" % i, (H * d, W), torch.float32, dev)
+    if W > 1:
+        _chk(cache, "cache", (pool.shape[0], W - 1, 3, H * d), xq.dtype, dev)
     shp = _shape(H, d, B, _io_of(xq), 0, scale)
     if o is None:
         o = torch.empty((R, B, H, d), dtype=xq.dtype, device=xq.device)
     elif o is False:
         o = None
+    _chk_rows(o, "o", (R, B), H, d, xq.dtype, dev, optional=True)
     host = None
     if slot_idx_host is not None:
         host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
@@ -376,7 +564,19 @@ def block_step_conv(slot_idx, pool, cache, weights, xq, xk, xv, alpha, beta, mod
 def conv_cache_fill(varlen: Varlen, head_dim, width, xs, doc_slot, cache, doc_slot_host=None):
     """Each document's clean history (its last W-1 projection rows, zero
     before its start) into cache[doc_slot[i]]; xs: three [T, H*d] io."""
+    torch = _torch()
+    if xs is None or len(xs) != 3 or xs[0] is None or xs[0].dim() != 2:
+        _fail("xs must be three [T, H*d] io tensors")
+    dev = _gpu_device(xs[0], "xs[0]")
     T, C = xs[0].shape
+    _chk_varlen(varlen, T, dev)
+    for i, x in enumerate(xs):
+        _chk(x, "xs[%d]" % i, (T, C), _io_dtype_of(xs[0], "xs[0]"), dev)
+    _chk(doc_slot, "doc_slot", (varlen.num_docs,), torch.int32, dev)
+    if int(width) > 1:
+        if cache is None or cache.dim() != 4:
+            _fail("cache must be [n_slots, W-1, 3, H*d]")
+        _chk(cache, "cache", (cache.shape[0], int(width) - 1, 3, C), xs[0].dtype, dev)
     host = None
     if doc_slot_host is not None:
         host = np.ascontiguousarray(np.asarray(doc_slot_host, dtype=np.int32))
@@ -392,12 +592,14 @@ def gdn_verify(slot_idx, pool, q, k, v, alpha, beta, scale=0.0, slot_idx_host=No
     gates [R,K,H]) from the pool states (read only).  Returns (o [R,K,H,d],
     cand [R,K,H,d,d] fp32: the state after every token)."""
     torch = _torch()
-    R, K, H, d = q.shape
+    R, K, H, d, dev = _chk_step_inputs(slot_idx, pool, q, k, v, alpha, beta)
     shp = _shape(H, d, K, _io_of(q), 0, scale)
     if o is None:
         o = torch.empty((R, K, H, d), dtype=q.dtype, device=q.device)
     if cand is None:
         cand = torch.empty((R, K, H, d, d), dtype=torch.float32, device=q.device)
+    _chk_rows(o, "o", (R, K), H, d, q.dtype, dev)
+    _chk(cand, "cand", (R, K, H, d, d), torch.float32, dev)
     host = None
     if slot_idx_host is not None:
         host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
@@ -410,7 +612,15 @@ def gdn_verify(slot_idx, pool, q, k, v, alpha, beta, scale=0.0, slot_idx_host=No
 def gdn_scatter(slot_idx, accepted, cand, pool, slot_idx_host=None):
     """AR-Trust rollback: pool[slot_idx[r]] = cand[r, accepted[r] - 1] for the
     device int32 counts accepted [R], clamped to [0, K] (0 leaves the slot)."""
+    torch = _torch()
+    dev = _gpu_device(cand, "cand")
+    if cand.dim() != 5:
+        _fail("cand must be [R, K, H, d, d]")
     R, K, H, d, _ = cand.shape
+    _chk(cand, "cand", (R, K, H, d, d), torch.float32, dev)
+    _chk(accepted, "accepted", (R,), torch.int32, dev)
+    _chk(slot_idx, "slot_idx", (R,), torch.int32, dev)
+    _chk_pool(pool, H, d, dev)
     shp = _shape(H, d, K, BF16, 0, 0.0)
     host = None
     if slot_idx_host is not None:
@@ -424,10 +634,11 @@ def gdn_verify_outputs(slot_idx, pool, q, k, v, alpha, beta, scale=0.0, slot_idx
     """The causal outputs of gdn_verify without the candidate states (pool
     read only).  Returns o [R,K,H,d]."""
     torch = _torch()
-    R, K, H, d = q.shape
+    R, K, H, d, dev = _chk_step_inputs(slot_idx, pool, q, k, v, alpha, beta)
     shp = _shape(H, d, K, _io_of(q), 0, scale)
     if o is None:
         o = torch.empty((R, K, H, d), dtype=q.dtype, device=q.device)
+    _chk_rows(o, "o", (R, K), H, d, q.dtype, dev)
     host = None
     if slot_idx_host is not None:
         host = np.ascontiguousarray(np.asarray(slot_idx_host, dtype=np.int32))
@@ -441,7 +652,10 @@ def gdn_commit_prefix(slot_idx, pool, q, k, v, alpha, beta, accepted, scale=0.0,
     """COMMIT of each request's first accepted[r] drafted tokens (device int32,
     clamped to [0, K]) into its pool slot, in place; 0 leaves the slot.
     o (optional) receives the causal outputs of the replayed tokens."""
-    R, K, H, d = q.shape
+    torch = _torch()
+    R, K, H, d, dev = _chk_step_inputs(slot_idx, pool, q, k, v, alpha, beta)
+    _chk(accepted, "accepted", (R,), torch.int32, dev)
+    _chk_rows(o, "o", (R, K), H, d, q.dtype, dev, optional=True)
     shp = _shape(H, d, K, _io_of(q), 0, scale)
     host = None
     if slot_idx_host is not None:
@@ -455,12 +669,13 @@ def gdn_commit_prefix(slot_idx, pool, q, k, v, alpha, beta, accepted, scale=0.0,
 def shortconv_dual(varlen: Varlen, block_size, x, xn, weight, bias=None, activation=0, out=None):
     """x, xn [T,C] io; weight [C,W] fp32; bias [C] fp32 or None.  Returns (y, yn)."""
     torch = _torch()
-    T, C = x.shape
-    W = weight.shape[1]
+    T, C, W, dev = _chk_conv_inputs(varlen, x, xn, weight, bias)
     if out is None:
         y, yn = torch.empty_like(x), torch.empty_like(x)
     else:
         y, yn = out
+        _chk(y, "y", (T, C), x.dtype, dev)
+        _chk(yn, "yn", (T, C), x.dtype, dev)
     _check(lib().flare_shortconv_dual(varlen.ref(), int(block_size), C, W, _io_of(x), _ptr(x), _ptr(xn),
                                       _ptr(weight), _ptr(bias), int(activation), _ptr(y), _ptr(yn),
                                       _stream(x.device)))
@@ -478,17 +693,23 @@ def shortconv_dual_bwd(varlen: Varlen, block_size, x, xn, weight, dy, dyn, bias=
     """Reverse mode of shortconv_dual.  Returns (dx, dxn, dweight, dbias);
     dbias is None when want_dbias is False."""
     torch = _torch()
-    T, C = x.shape
-    W = weight.shape[1]
+    T, C, W, dev = _chk_conv_inputs(varlen, x, xn, weight, bias)
+    _chk(dy, "dy", (T, C), x.dtype, dev)
+    _chk(dyn, "dyn", (T, C), x.dtype, dev)
     if out is None:
         dx, dxn = torch.empty_like(x), torch.empty_like(x)
         dw = torch.empty((C, W), dtype=torch.float32, device=x.device)
         db = torch.empty((C,), dtype=torch.float32, device=x.device) if want_dbias else None
     else:
         dx, dxn, dw, db = out
+    _chk(dx, "dx", (T, C), x.dtype, dev)
+    _chk(dxn, "dxn", (T, C), x.dtype, dev)
+    _chk(dw, "dweight", (C, W), torch.float32, dev)
+    _chk(db, "dbias", (C,), torch.float32, dev, optional=True)
     need = shortconv_dual_bwd_workspace_bytes(varlen, block_size, C, W)
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    _chk_buf(workspace, "workspace", need, torch.uint8, dev)
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().flare_shortconv_dual_bwd(varlen.ref(), int(block_size), C, W, _io_of(x), _ptr(x), _ptr(xn),
                                           _ptr(weight), _ptr(bias), int(activation), _ptr(dy), _ptr(dyn),
@@ -507,12 +728,13 @@ def qkv_prologue(varlen: Varlen, block_size, head_dim, xs, xns, weights, activat
     weights: three [H*head_dim, W] fp32), optional SiLU, per-head L2 norm of
     q and k.  Returns (ys, yns), lists of three tensors shaped like xs."""
     torch = _torch()
-    T, C = xs[0].shape
-    W = weights[0].shape[1]
+    T, C, W, dev = _chk_prologue_inputs(varlen, xs, xns, weights)
     if out is None:
         ys, yns = [torch.empty_like(x) for x in xs], [torch.empty_like(x) for x in xs]
     else:
         ys, yns = out
+    _chk_three(ys, "ys", (T, C), xs[0].dtype, dev)
+    _chk_three(yns, "yns", (T, C), xs[0].dtype, dev)
     _check(lib().flare_qkv_prologue(varlen.ref(), int(block_size), C // int(head_dim), int(head_dim), W,
                                     _io_of(xs[0]), _a3(xs), _a3(xns), _a3(weights), int(activation),
                                     1 if qk_l2norm else 0, _a3(ys), _a3(yns), _stream(xs[0].device)))
@@ -529,17 +751,23 @@ def qkv_prologue_bwd(varlen: Varlen, block_size, head_dim, xs, xns, weights, dys
                      qk_l2norm=True, workspace=None, out=None):
     """Reverse mode of qkv_prologue.  Returns (dxs, dxns, dws), lists of three."""
     torch = _torch()
-    T, C = xs[0].shape
-    W = weights[0].shape[1]
+    T, C, W, dev = _chk_prologue_inputs(varlen, xs, xns, weights)
+    io = xs[0].dtype
+    _chk_three(dys, "dys", (T, C), io, dev)
+    _chk_three(dyns, "dyns", (T, C), io, dev)
     H = C // int(head_dim)
     if out is None:
         dxs, dxns = [torch.empty_like(x) for x in xs], [torch.empty_like(x) for x in xs]
         dws = [torch.empty((C, W), dtype=torch.float32, device=xs[0].device) for _ in range(3)]
     else:
         dxs, dxns, dws = out
+    _chk_three(dxs, "dxs", (T, C), io, dev)
+    _chk_three(dxns, "dxns", (T, C), io, dev)
+    _chk_three(dws, "dws", (C, W), torch.float32, dev)
     need = qkv_prologue_bwd_workspace_bytes(varlen, block_size, H, head_dim, W)
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=xs[0].device)
+    _chk_buf(workspace, "workspace", need, torch.uint8, dev)
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().flare_qkv_prologue_bwd(varlen.ref(), int(block_size), H, int(head_dim), W, _io_of(xs[0]),
                                         _a3(xs), _a3(xns), _a3(weights), int(activation), 1 if qk_l2norm else 0,
