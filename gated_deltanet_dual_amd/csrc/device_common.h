@@ -67,10 +67,15 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 // ---------------------------------------------------------------- fragments
 // Row fragment of a row-major bf16 matrix: rows row0 + (l & 15), columns
 // k0 + 8*(l>>4) .. +7 (one 16-byte LDS read).
-__device__ __forceinline__ bf16x8 frag_bf16(const u16 *base, int ld, int row0, int k0) {
-  const int l = lane_id();
+// The _l variants take the lane index as an argument: a kernel that loops
+// over work items passes a per-item opaque copy, so the per-lane offsets are
+// formed inside the loop instead of being hoisted out of it.
+__device__ __forceinline__ bf16x8 frag_bf16_l(int l, const u16 *base, int ld, int row0, int k0) {
   const u16x8 *p = reinterpret_cast<const u16x8 *>(base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
   return as_bf16x8(*p);
+}
+__device__ __forceinline__ bf16x8 frag_bf16(const u16 *base, int ld, int row0, int k0) {
+  return frag_bf16_l(lane_id(), base, ld, row0, k0);
 }
 
 // Row fragment of a row-major fp32 matrix rounded to bf16 (hi part).
@@ -105,13 +110,15 @@ __device__ __forceinline__ void frag_f32_split(const float *base, int ld, int ro
 
 // Column-gather fragment: element (r, k) = base[(k0 + 8*(l>>4) + e) * ld + row0 + (l&15)],
 // i.e. the row fragment of the TRANSPOSE of a row-major bf16 matrix.
-__device__ __forceinline__ bf16x8 frag_bf16_T(const u16 *base, int ld, int row0, int k0) {
-  const int l = lane_id();
+__device__ __forceinline__ bf16x8 frag_bf16_T_l(int l, const u16 *base, int ld, int row0, int k0) {
   const u16 *p = base + (k0 + 8 * (l >> 4)) * ld + row0 + (l & 15);
   u16x8 h;
 #pragma unroll
   for (int e = 0; e < 8; ++e) h.v[e] = p[e * ld];
   return as_bf16x8(h);
+}
+__device__ __forceinline__ bf16x8 frag_bf16_T(const u16 *base, int ld, int row0, int k0) {
+  return frag_bf16_T_l(lane_id(), base, ld, row0, k0);
 }
 
 // fp32 MFMA operands (16x16x4): one element per lane.

@@ -59,6 +59,8 @@ struct Chunk2Smem {
   alignas(16) float plgc[kNW];
   alignas(16) float gsum[2][kC];
   alignas(16) float gf[GF_NUM][kC];
+  alignas(16) float alpha[2][kC];        // a, a~ of the chunk's rows (1 past the end / in the prompt)
+  alignas(16) float tot[P_NUM][kC];      // the per-wave gate partials summed over the waves
 };
 
 // 16-byte row fragment of a [T, H, D] bf16 tensor straight from global memory:
@@ -192,6 +194,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     }
   }
   if (tid < 4 * C) gate_scan(gval, B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
+  if (tid < C) sm.alpha[0][tid] = gval;
+  else if (tid >= 2 * C && tid < 3 * C) sm.alpha[1][tid - 2 * C] = gval;
   lds_barrier();
 
   const float lgC = sm.lg[C - 1];
@@ -691,28 +695,13 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       sm.x[2][i][col0 + cl] = f2bf(rs ? dqn[tr][r] : 0.f);
       sm.x[3][i][col0 + cl] = f2bf(rs ? dkn[tr][r] : 0.f);
     }
-  // ---- gates: reduce the per-wave partials in a fixed order and move the
-  // boundary terms to the positions they belong to
-  if (tid < 2 * C) {
-    const int i = tid & (C - 1);
+  // ---- gates, step 1: each partial summed over the waves, in wave order
+  if (tid < P_NUM * C) {
+    const int t = tid / C, i = tid % C;
     float v = 0.f;
-    if (tid < C) {  // clean d gamma_i
-      for (int w = 0; w < kNW; ++w) v += sm.part[w][P_G][i];
-      if (((i + 1) % B) == 0 && i + 1 < C)  // boundary p = i + 1: reads of the block starting there
-        for (int m = i + 1; m < i + 1 + B; ++m)
-          for (int w = 0; w < kNW; ++w) v += sm.part[w][P_GP][m];
-      if (i == C - 1) {
-        for (int w = 0; w < kNW; ++w) v += sm.plgc[w];
-        for (int m = 0; m < C; ++m)
-          for (int w = 0; w < kNW; ++w) v += sm.part[w][P_C][m];
-      }
-    } else {  // noisy d gamma~_i
-      for (int w = 0; w < kNW; ++w) v += sm.part[w][P_GN][i];
-      if (((i + 1) % B) == 0)
-        for (int m = i + 1 - B; m <= i; ++m)
-          for (int w = 0; w < kNW; ++w) v += sm.part[w][P_GE][m];
-    }
-    sm.gsum[tid / C][i] = v;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) v += sm.part[w][t][i];
+    sm.tot[t][i] = v;
   }
   lds_barrier();
   {
@@ -727,26 +716,51 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
           *reinterpret_cast<const uint4 *>(&sm.x[m][row][cu16 * 8]);
     }
   }
-  if (tid < 2 * C) {
-    const int i = tid & (C - 1);
-    const bool noisy = tid >= C;
-    float dg = 0.f, db = 0.f;
-    if (!noisy) {
-      for (int m = i; m < C; ++m) dg += sm.gsum[0][m];
-      for (int w = 0; w < kNW; ++w) db += sm.part[w][P_B][i];
-    } else {
-      const int end = i - (i % B) + B;
-      for (int m = i; m < end; ++m) dg += sm.gsum[1][m];
-      for (int w = 0; w < kNW; ++w) db += sm.part[w][P_BN][i];
+  // ---- gates, step 2 (wave 0; lanes 0-31 the clean rows i, lanes 32-63 the
+  // noisy rows): move the boundary terms to the rows they belong to, then
+  // d alpha_i = sum over m >= i of d gamma_m (clean: to the chunk end; noisy:
+  // to the end of i's block) over alpha_i.  Sums over lanes run as fixed
+  // shuffle trees, so the result is the same on every run.
+  if (wave == 0) {
+    const int i = lane & (C - 1);
+    const bool noisy = lane >= C;
+    const int ib = i % B;
+    // per-block sums of the block-start reads (clean) / block-end reads (noisy):
+    // segmented inclusive prefix over the rows of each block, total at its last row
+    float bs = noisy ? sm.tot[P_GE][i] : sm.tot[P_GP][i];
+    for (int off = 1; off < B; off <<= 1) {
+      const float y = __shfl_up(bs, off, B);
+      if (ib >= off) bs += y;
     }
+    float v = noisy ? sm.tot[P_GN][i] : sm.tot[P_G][i];
+    // clean: the block starting at p = i + 1 reads S_p, whose gates end at row i
+    const float next_block = __shfl_down(bs, B, C);
+    if (!noisy && ib == B - 1 && i + B < C) v += next_block;
+    if (noisy && ib == B - 1) v += bs;
+    // clean, last row: the chunk-end terms (<dS', S_c> and the decay of the write strengths)
+    float pc = noisy ? 0.f : sm.tot[P_C][i];
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) pc += __shfl_xor(pc, off, C);
+    if (!noisy && i == C - 1) {
+      float pl = 0.f;
+      for (int w = 0; w < kNW; ++w) pl += sm.plgc[w];
+      v += pl + pc;
+    }
+    // suffix sums: to the chunk end (clean), to the end of the block (noisy)
+    const int seg = noisy ? B : C, is = noisy ? ib : i;
+    for (int off = 1; off < C; off <<= 1) {
+      const float y = __shfl_down(v, off, C);
+      if (is + off < seg) v += y;
+    }
+    const float db = noisy ? sm.tot[P_BN][i] : sm.tot[P_B][i];
     const int64_t gi = (t0g + c0 + i) * H + h;
     if (c0 + i < n) {
       if (!noisy) {
-        a.dalpha[gi] = dg / f.alpha[gi];
+        a.dalpha[gi] = v / sm.alpha[0][i];
         a.dbeta[gi] = db;
       } else {
         const bool rsp = c0 + i >= P;
-        a.dalpha_n[gi] = rsp ? dg / f.alpha_n[gi] : 0.f;
+        a.dalpha_n[gi] = rsp ? v / sm.alpha[1][i] : 0.f;
         a.dbeta_n[gi] = rsp ? db : 0.f;
       }
     }

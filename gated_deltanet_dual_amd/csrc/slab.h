@@ -32,7 +32,8 @@ __device__ __forceinline__ Slab slab_zero() {
 }
 
 // chunk row held by accumulator register r of tile tr in this lane
-__device__ __forceinline__ int slab_row(int tr, int r) { return 16 * tr + 4 * (lane_id() >> 4) + r; }
+__device__ __forceinline__ int slab_row_l(int l, int tr, int r) { return 16 * tr + 4 * (l >> 4) + r; }
+__device__ __forceinline__ int slab_row(int tr, int r) { return slab_row_l(lane_id(), tr, r); }
 
 // bf16 B fragment (k-permuted) of a slab: hi only.
 __device__ __forceinline__ bf16x8 slab_b_hi(const Slab &s) {
@@ -103,29 +104,35 @@ __device__ __forceinline__ void cc_mul(Slab &out, const float *M, int ld, const 
 // A fragment of rows m0 .. m0+15 of a C x C bf16 plane in LDS (row-major,
 // pitch ld elements, a multiple of 4), columns in the slab's k-permutation:
 // two 8-byte reads, no conversion.
-__device__ __forceinline__ bf16x8 plane_a(const u16 *P, int ld, int m0) {
-  const int l = lane_id(), g = l >> 4;
+__device__ __forceinline__ bf16x8 plane_a_l(int l, const u16 *P, int ld, int m0) {
+  const int g = l >> 4;
   const u16 *p = P + (m0 + (l & 15)) * ld + 4 * g;
   const uint2 lo4 = *reinterpret_cast<const uint2 *>(p);
   const uint2 hi4 = *reinterpret_cast<const uint2 *>(p + 16);
   return __builtin_bit_cast(bf16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
 }
+__device__ __forceinline__ bf16x8 plane_a(const u16 *P, int ld, int m0) { return plane_a_l(lane_id(), P, ld, m0); }
 
 // out += A * in, A (C x C) given as its bf16 hi and lo planes, already in the
 // orientation of the product (a transposed operand is stored transposed).
 // TERMS as for cc_mul.
 template <int TERMS>
-__device__ __forceinline__ void cc_mul_planes(Slab &out, const u16 *Ah, const u16 *Al, int ld, const Slab &in) {
+__device__ __forceinline__ void cc_mul_planes_l(int l, Slab &out, const u16 *Ah, const u16 *Al, int ld,
+                                                const Slab &in) {
   bf16x8 bh, bl;
   if constexpr (TERMS == 3) slab_b_split(in, bh, bl);
   else bh = slab_b_hi(in);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr) {
-    const bf16x8 ah = plane_a(Ah, ld, 16 * tr), al = plane_a(Al, ld, 16 * tr);
+    const bf16x8 ah = plane_a_l(l, Ah, ld, 16 * tr), al = plane_a_l(l, Al, ld, 16 * tr);
     mma_bf16(out.t[tr], ah, bh);
     if constexpr (TERMS == 3) mma_bf16(out.t[tr], ah, bl);
     mma_bf16(out.t[tr], al, bh);
   }
+}
+template <int TERMS>
+__device__ __forceinline__ void cc_mul_planes(Slab &out, const u16 *Ah, const u16 *Al, int ld, const Slab &in) {
+  cc_mul_planes_l<TERMS>(lane_id(), out, Ah, Al, ld, in);
 }
 
 // Sum of x over the 16 lanes that share an accumulator row group.
