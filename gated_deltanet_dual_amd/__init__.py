@@ -114,6 +114,11 @@ def lib():
     L.flare_qkv_prologue_bwd.argtypes = [VP, I32, I32, I32, I32, I32, A3, A3, A3, I32, I32, A3, A3, A3, A3, A3,
                                          P, SZ, P]
     L.flare_qkv_prologue_bwd.restype = ctypes.c_int
+    L.flare_noalloc_scratch_bytes.argtypes = []
+    L.flare_noalloc_scratch_bytes.restype = SZ
+    L.flare_qkv_prologue_bwd_noalloc.argtypes = [VP, I32, I32, I32, I32, I32, A3, A3, A3, I32, I32, A3, A3, A3, A3,
+                                                 A3, P]
+    L.flare_qkv_prologue_bwd_noalloc.restype = ctypes.c_int
     L.flare_timing_enable.argtypes = [I32]
     L.flare_timing_enable.restype = I32
     L.flare_timing_avg_ms.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64)]
@@ -774,6 +779,36 @@ def qkv_prologue_bwd(varlen: Varlen, block_size, head_dim, xs, xns, weights, dys
                                         _a3(dys), _a3(dyns), _a3(dxs), _a3(dxns), _a3(dws), _ptr(workspace),
                                         nbytes, _stream(xs[0].device)))
     return dxs, dxns, dws
+
+
+def qkv_prologue_bwd_noalloc(varlen: Varlen, block_size, head_dim, xs, xns, weights, dys, dyns, out,
+                             activation=0, qk_l2norm=True):
+    """qkv_prologue_bwd with the weight-gradient partials in the library's
+    static device scratch (flare_qkv_prologue_bwd_noalloc): the library
+    allocates nothing, so the caller passes every output buffer, out =
+    (dxs, dxns, dws).  Returns out."""
+    torch = _torch()
+    T, C, W, dev = _chk_prologue_inputs(varlen, xs, xns, weights)
+    io = xs[0].dtype
+    _chk_three(dys, "dys", (T, C), io, dev)
+    _chk_three(dyns, "dyns", (T, C), io, dev)
+    if out is None or len(out) != 3:
+        _fail("out must be (dxs, dxns, dws)", 1)
+    dxs, dxns, dws = out
+    _chk_three(dxs, "dxs", (T, C), io, dev)
+    _chk_three(dxns, "dxns", (T, C), io, dev)
+    _chk_three(dws, "dws", (C, W), torch.float32, dev)
+    H = C // int(head_dim)
+    _check(lib().flare_qkv_prologue_bwd_noalloc(varlen.ref(), int(block_size), H, int(head_dim), W, _io_of(xs[0]),
+                                                _a3(xs), _a3(xns), _a3(weights), int(activation),
+                                                1 if qk_l2norm else 0, _a3(dys), _a3(dyns), _a3(dxs), _a3(dxns),
+                                                _a3(dws), _stream(xs[0].device)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static device scratch behind qkv_prologue_bwd_noalloc."""
+    return int(lib().flare_noalloc_scratch_bytes())
 
 
 def workspace_bytes(varlen: Varlen, H: int, d: int, block_size: int, io: int, flags: int = 0,

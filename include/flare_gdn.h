@@ -462,6 +462,39 @@ flare_status flare_qkv_prologue_bwd(const flare_varlen *varlen,
                                     void *workspace, size_t workspace_bytes,
                                     void *stream);
 
+/* flare_qkv_prologue_bwd without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight training
+ * or serving loops, harnesses that forbid allocation.  The weight-gradient
+ * partials go to a static device array of the library instead,
+ * flare_noalloc_scratch_bytes() = 64 MiB on every GPU the library runs on,
+ * held until the process ends.  The call allocates and frees nothing.
+ * Arguments, results and the other errors as flare_qkv_prologue_bwd.
+ * Errors: FLARE_ERR_WORKSPACE when the batch would need more partials than
+ * the array holds (flare_qkv_prologue_bwd_workspace_size() > 64 MiB, e.g.
+ * more than 3 x 32768 tokens x 4096 channels at width 4).
+ * The first call on a device (with that device current) looks the array's
+ * device address up with hipGetSymbolAddress: make that first call outside a
+ * graph capture.  All calls on one GPU share its array: calls that overlap
+ * in time on one GPU (two streams, two host threads) race; calls ordered on
+ * one stream do not (the partials are fully written before they are read, so
+ * nothing carries over from the previous call). */
+size_t flare_noalloc_scratch_bytes(void);
+flare_status flare_qkv_prologue_bwd_noalloc(const flare_varlen *varlen,
+                                            int32_t block_size, int32_t heads,
+                                            int32_t head_dim, int32_t width,
+                                            int32_t io_dtype,
+                                            const void *const x[3],
+                                            const void *const xn[3],
+                                            const float *const weight[3],
+                                            int32_t activation,
+                                            int32_t qk_l2norm,
+                                            const void *const dy[3],
+                                            const void *const dyn[3],
+                                            void *const dx[3],
+                                            void *const dxn[3],
+                                            float *const dweight[3],
+                                            void *stream);
+
 /* Thread-local message for the last non-OK status; "" if none. */
 const char *flare_last_error(void);
 
