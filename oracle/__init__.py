@@ -53,23 +53,36 @@ FLAG_QK_L2NORM = 1
 EVAL, COMMIT = 0, 1
 
 
-def build() -> str:
-    """Compile ``liboracle.so`` with gcc (always recompiles)."""
-    tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC",
-           "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+# FLARE_ORACLE_SANITIZED=1 loads the AddressSanitizer + UndefinedBehaviorSanitizer
+# build instead (the process must preload libasan; see tests/test_sanitizers.py)
+_SANITIZED = os.environ.get("FLARE_ORACLE_SANITIZED") == "1"
+
+
+def build(sanitized: bool = False) -> str:
+    """Compile ``liboracle.so`` with gcc (always recompiles); with sanitized,
+    ``liboracle_san.so`` built with -fsanitize=address,undefined."""
+    out = _LIB_SAN if sanitized else _LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    flags = ["-O2"]
+    if sanitized:
+        flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                 "-fno-sanitize-recover=all"]
+    cmd = ["gcc"] + flags + ["-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC",
+                             "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    path = _LIB_SAN if _SANITIZED else _LIB
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        build(sanitized=_SANITIZED)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, f64 = ctypes.c_int, ctypes.c_double
     lib.oracle_gdn_dual_fwd.argtypes = [i32, P, P, i32, i32, i32, i32, f64, i32] + [P] * 14 + [i32]
