@@ -210,8 +210,9 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
   if (st != FLARE_OK) return st;
   if (ckpt_stride_chunks != 1)
     return fail(FLARE_ERR_UNSUPPORTED, "checkpoint stride %d (only 1 is built)", ckpt_stride_chunks);
-  if (shape->flags & FLARE_QK_L2NORM)
-    return fail(FLARE_ERR_UNSUPPORTED, "the backward is built without the q/k L2 normalisation");
+  if ((shape->flags & FLARE_QK_L2NORM) && !bwd_uses_scan_pack(shape))
+    return fail(FLARE_ERR_UNSUPPORTED,
+                "the backward takes the q/k L2 flag for bf16 io at d = 128 only (normalise q, k beforehand)");
   if (vi.total_tokens > 0 &&
       (!q || !k || !v || !alpha || !beta || !qn || !kn || !vn || !alpha_n || !beta_n || !ckpt ||
        !d_o || !d_on || !dq || !dk || !dv || !dalpha || !dbeta || !dqn || !dkn || !dvn ||

@@ -71,17 +71,32 @@ __device__ __forceinline__ float gate_load(const FwdArgs &f, int64_t t0g, int c0
   const float *const p0 = f.alpha, *const p1 = f.beta, *const p2 = f.alpha_n, *const p3 = f.beta_n;
   const float *src = g == 0 ? p0 : g == 1 ? p1 : g == 2 ? p2 : p3;
   // unconditional load from a row clamped into the document, masked afterwards
-  const float v = src[(t0g + min(tpos, n - 1)) * f.H + h];
+  const int64_t row = (t0g + min(tpos, n - 1)) * f.H + h;
+  float v = src[row];
+  if (f.l2f && (g & 1)) {  // the q/k L2 flag: folded write strengths (gdn_l2.hip)
+    const float4 r = f.l2f[row];
+    const float rk = g == 1 ? r.y : r.w;
+    v *= rk * rk;
+  }
   return ok ? v : ((g & 1) == 0 ? 1.f : 0.f);
 }
 
 // The same load, split: the raw value now (no use of it, so nothing waits),
 // the mask and padding applied by gate_fix when the value is consumed.
+// With the q/k L2 flag (f.l2f) the write strengths are the folded ones,
+// b r_k^2 and b~ r_k~^2 (gdn_l2.hip).
 __device__ __forceinline__ float gate_load_raw(const FwdArgs &f, int64_t t0g, int c0, int n, int h, int tid) {
   const int g = tid / 32, i = tid % 32;
   const float *const p0 = f.alpha, *const p1 = f.beta, *const p2 = f.alpha_n, *const p3 = f.beta_n;
   const float *src = g == 0 ? p0 : g == 1 ? p1 : g == 2 ? p2 : p3;
-  return src[(t0g + min(c0 + i, n - 1)) * f.H + h];
+  const int64_t row = (t0g + min(c0 + i, n - 1)) * f.H + h;
+  float v = src[row];
+  if (f.l2f && (g & 1)) {
+    const float4 r = f.l2f[row];
+    const float rk = g == 1 ? r.y : r.w;
+    v *= rk * rk;
+  }
+  return v;
 }
 __device__ __forceinline__ float gate_fix(float raw, int c0, int n, int P, int tid) {
   const int g = tid / 32, tpos = c0 + tid % 32;

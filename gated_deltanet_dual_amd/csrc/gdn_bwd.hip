@@ -864,6 +864,14 @@ static hipError_t launch_bwd_t(const BwdArgs &a_in, hipStream_t st) {
   a.tri = reinterpret_cast<float *>(a.workspace) + (size_t)slots * f.H * D * D;
   if constexpr (std::is_same<IO, u16>::value && D == 128) {
     a.pack = a.tri + (size_t)slots * f.H * 6 * Cfg::C * Cfg::C;
+    if (f.flags & 1) {
+      // the q/k L2 flag: per-row factors after the hand-over (gdn_l2.hip)
+      const size_t per_bytes = (size_t)slots * f.H * ((size_t)D * D + 6 * Cfg::C * Cfg::C + kScanPackFloats) * 4;
+      float4 *l2f = reinterpret_cast<float4 *>(reinterpret_cast<char *>(a.workspace) + ((per_bytes + 255) & ~(size_t)255));
+      hipError_t e0 = launch_l2_factors(a.f, l2f, st);
+      if (e0 != hipSuccess) return e0;
+      a.f.l2f = l2f;
+    }
     if (a.fwd_cm) {
       a.tri = const_cast<float *>(a.fwd_cm);  // read only from here on
     } else if (slots > 0) {

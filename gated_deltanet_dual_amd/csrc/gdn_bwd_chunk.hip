@@ -22,6 +22,13 @@
 //            six unweighted Gram matrices in LDS), their contractions with the
 //            q/k rows, gate gradients, stores.
 // Nothing is reduced across workgroups, so the result is deterministic.
+//
+// L2 (the q/k L2 flag, folded into per-row factors as gdn_l2.hip describes):
+// the same kernel on the transformed problem -- folded write strengths from
+// the gate load, v' = v / r_k, the output gradient r_q do -- then the
+// gradients mapped back: dv = dv' / r_k, db = db' r_k^2,
+// dq = dq' - r_q^2 q (q . dq'), dk = dk' + r_k^2 k (dv' . v' - 2 b' db'),
+// and the same for the noisy stream.
 #include "bwd_common.h"
 #include "chunk_common.h"
 #include "device_common.h"
@@ -36,7 +43,7 @@ namespace {
 
 constexpr int kC = 32, kD = 128, kNW = 8, kNT = 64 * kNW;
 constexpr int kLDX = kD + 8, kLDP = kD + 8, kLDG = kC + 8, kLDQ = kC + 4;
-enum { P_G = 0, P_GN, P_B, P_BN, P_GP, P_GE, P_C, P_NUM };
+enum { P_G = 0, P_GN, P_B, P_BN, P_GP, P_GE, P_C, P_DV, P_DVN, P_NUM };
 enum { A_U = 0, A_UN, A_DRHS, A_DRN };
 // the chunk matrices (T, T~, Mwo, Mwq, Mwk, Mw~) as bf16 hi / lo planes in the
 // orientation each product reads them (_N as stored, _T transposed)
@@ -61,7 +68,16 @@ struct Chunk2Smem {
   alignas(16) float gf[GF_NUM][kC];
   alignas(16) float alpha[2][kC];        // a, a~ of the chunk's rows (1 past the end / in the prompt)
   alignas(16) float tot[P_NUM][kC];      // the per-wave gate partials summed over the waves
+  alignas(16) float fac[4][kC];          // L2: r_q, r_k, r_q~, r_k~ of the chunk's rows
+  alignas(16) float vsc[2][kC];          // L2: 1 / r_k, 1 / r_k~
 };
+// L2, after phase 1 (in the bytes of the chunk-matrix planes, dead by then):
+// per-wave row partials of q . dq' and q~ . dq~', and the per-row dk terms
+struct L2Late {
+  float qdot[kNW][2][kC];
+  float ck[2][kC];
+};
+static_assert(sizeof(L2Late) <= sizeof(((Chunk2Smem *)nullptr)->cq), "L2 scratch must fit in the plane bytes");
 
 // 16-byte row fragment of a [T, H, D] bf16 tensor straight from global memory:
 // rows c0 + row0 + (l & 15), columns k0 + 8 (l >> 4) .. +7.  The load is
@@ -82,6 +98,7 @@ __device__ __forceinline__ bf16x8 frag_mask(const uint4 &v, int c0, int n, int P
 
 }  // namespace
 
+template <bool L2>
 __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   constexpr int C = kC, D = kD, NT = kNT, LDX = kLDX, LDP = kLDP, LDG = kLDG, LDQ = kLDQ;
   __shared__ Chunk2Smem sm;
@@ -125,6 +142,11 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     xr[e] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
   }
   const float gval = tid < 4 * C ? gate_load(f, t0g, c0, n, P, h, tid) : 0.f;
+  float l2r = 1.f;  // L2, thread tid < 128: factor tid / 32 of row tid % 32
+  if (L2 && tid < 4 * C) {
+    const float *fr = reinterpret_cast<const float *>(f.l2f + (t0g + min(c0 + (tid & (C - 1)), n - 1)) * H + h);
+    l2r = fr[tid / C];
+  }
   float4 tri4[3];  // the six chunk matrices
 #pragma unroll
   for (int j = 0; j < 3; ++j)
@@ -196,6 +218,10 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   if (tid < 4 * C) gate_scan(gval, B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   if (tid < C) sm.alpha[0][tid] = gval;
   else if (tid >= 2 * C && tid < 3 * C) sm.alpha[1][tid - 2 * C] = gval;
+  if (L2 && tid < 4 * C) {
+    sm.fac[tid / C][tid & (C - 1)] = l2r;
+    if ((tid / C) & 1) sm.vsc[tid / (2 * C)][tid & (C - 1)] = l2r > 0.f ? 1.f / l2r : 0.f;
+  }
   lds_barrier();
 
   const float lgC = sm.lg[C - 1];
@@ -258,7 +284,19 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) sl.t[tr][r] = bf2f(vst[m][slab_row(tr, r)][col0 + cl]);
     return sl;
   };
-  const Slab V = slab_of(0), VN = slab_of(1), DO = slab_of(2), DON = slab_of(3);
+  Slab V = slab_of(0), VN = slab_of(1), DO = slab_of(2), DON = slab_of(3);
+  if constexpr (L2) {  // v' = v / r_k and the output gradient r_q do (both streams)
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = slab_row(tr, r);
+        V.t[tr][r] *= sm.vsc[0][i];
+        VN.t[tr][r] *= sm.vsc[1][i];
+        DO.t[tr][r] *= sm.fac[0][i];
+        DON.t[tr][r] *= sm.fac[2][i];
+      }
+  }
   lds_barrier();  // the Gram matrices visible
 
   // ================================================================ phase 1
@@ -305,7 +343,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     cc_mul_planes<3>(UN, &sm.cq[Q_TN_N][0][0][0], &sm.cq[Q_TN_N][1][0][0], LDQ, rhsn);
     // du~ = s diag(b~) M~^T do~ = s Mw~^T do~
     Slab dun = slab_zero();
-    cc_mul_planes<2>(dun, &sm.cq[Q_MWN_T][0][0][0], &sm.cq[Q_MWN_T][1][0][0], LDQ, DON);
+    cc_mul_planes<L2 ? 3 : 2>(dun, &sm.cq[Q_MWN_T][0][0][0], &sm.cq[Q_MWN_T][1][0][0], LDQ, DON);
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -335,7 +373,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   // dU = D K dS' + diag(b) (s Mo^T do + Mq^T dr_q + Mk^T dr_k)
   //    = D K dS' + s Mwo^T do + Mwq^T dr_q + Mwk^T dr_k
   Slab dU = slab_zero();
-  cc_mul_planes<2>(dU, &sm.cq[Q_MWO_T][0][0][0], &sm.cq[Q_MWO_T][1][0][0], LDQ, DO);
+  cc_mul_planes<L2 ? 3 : 2>(dU, &sm.cq[Q_MWO_T][0][0][0], &sm.cq[Q_MWO_T][1][0][0], LDQ, DO);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr) dU.t[tr] *= s;
   if (has_noisy) {
@@ -364,6 +402,24 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       const int i = slab_row(tr, r);
       pg[tr][r] -= Gm(i) * row_sum16(DRHS.t[tr][r] * KS.t[tr][r]);
     }
+  float pdv[2][4], pdvn[2][4];  // L2: row partials of dv' . v' and dv~' . v~'
+  if constexpr (L2) {
+    u16 *const gdv = reinterpret_cast<u16 *>(a.dv), *const gdvn = reinterpret_cast<u16 *>(a.dvn);
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = slab_row(tr, r);
+        pdv[tr][r] = row_sum16(DRHS.t[tr][r] * V.t[tr][r]);
+        pdvn[tr][r] = row_sum16(DRN.t[tr][r] * VN.t[tr][r]);
+        // dv = dv' / r_k, dv~ = dv~' / r_k~ (drhs~ is zero outside the response rows)
+        if (c0 + i < n) {
+          const int64_t off = ((t0g + c0 + i) * H + h) * D + col0 + cl;
+          gdv[off] = f2bf(DRHS.t[tr][r] * sm.vsc[0][i]);
+          gdvn[off] = f2bf(DRN.t[tr][r] * sm.vsc[1][i]);
+        }
+      }
+  }
 
   // ---- the four shared C x d_v arrays -> LDS as bf16 hi / lo planes; the hi
   // planes of drhs and drhs~ are dv and dv~ rounded to bf16, stored from there
@@ -396,6 +452,10 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         sm.part[wave][P_GP][i] = pgp[tr][r];
         sm.part[wave][P_GE][i] = pge[tr][r];
         sm.part[wave][P_C][i] = pc[tr][r];
+        if constexpr (L2) {
+          sm.part[wave][P_DV][i] = pdv[tr][r];
+          sm.part[wave][P_DVN][i] = pdvn[tr][r];
+        }
       }
   }
   {
@@ -473,6 +533,10 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         else if (m == DM_Q) sc = s * Ge(i);
         else if (m == DM_K) sc = -Gn(i);
         else sc = -1.f;
+        if constexpr (L2) {  // the products with the raw do / do~ rows: r_q do
+          if (m == DM_O) sc *= sm.fac[0][i];
+          else if (m == DM_Q || m == DM_N) sc *= sm.fac[2][i];
+        }
         acc[r] *= sc;
       }
     }
@@ -532,13 +596,17 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         dq[tr][r] = s * Gm(i) * a_dq[tr][r];
         dk[tr][r] = -Gm(i) * a_dk1[tr][r] + Dd(i) * a_dk2[tr][r];
         dqn[tr][r] = Gp(i) * s * Ge(i) * a_dqn[tr][r];
+        if constexpr (L2) {
+          dq[tr][r] *= sm.fac[0][i];
+          dqn[tr][r] *= sm.fac[2][i];
+        }
         dkn[tr][r] = -Gp(i) * Gn(i) * a_dkn[tr][r];
       }
   }
 
   // dv, dv~ rows from the hi planes (drhs~ is zero outside the response rows),
-  // before phase 3 reuses the planes' bytes
-  {
+  // before phase 3 reuses the planes' bytes (L2: stored from registers above)
+  if constexpr (!L2) {
     u16 *const gdv = reinterpret_cast<u16 *>(a.dv), *const gdvn = reinterpret_cast<u16 *>(a.dvn);
 #pragma unroll
     for (int e = 0; e < 2 * PU / NT; ++e) {
@@ -649,6 +717,19 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     }
   }
   lds_barrier();
+  L2Late *const late = reinterpret_cast<L2Late *>(&sm.cq[0][0][0][0]);
+  if (L2 && tid < 2 * C) {
+    // the per-row dk terms r_k^2 (dv' . v' - 2 b' db'), read after the next barrier
+    const int i = tid & (C - 1), ns = tid / C;
+    float dvv = 0.f, dbb = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      dvv += sm.part[w][ns ? P_DVN : P_DV][i];
+      dbb += sm.part[w][ns ? P_BN : P_B][i];
+    }
+    const float rk = sm.fac[ns ? 3 : 1][i];
+    late->ck[ns][i] = rk * rk * (dvv - 2.f * (ns ? sm.betan[i] : sm.beta[i]) * dbb);
+  }
 
   // Gram contractions for d_k tile `wave`: B fragments are columns of q, k, q~, k~
   {
@@ -682,6 +763,20 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       }
     }
   }
+  if constexpr (L2) {  // row partials of q . dq' and q~ . dq~' over this d_k tile
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * tr + g4 + r;
+        const float pq = row_sum16(bf2f(sm.x[0][i][col0 + cl]) * dq[tr][r]);
+        const float pqn = row_sum16(bf2f(sm.x[2][i][col0 + cl]) * dqn[tr][r]);
+        if (cl == 0) {
+          late->qdot[wave][0][i] = pq;
+          late->qdot[wave][1][i] = pqn;
+        }
+      }
+  }
   lds_barrier();
   // ---- stage the four d_k-side gradients in the (now free) q/k tiles, then store rows
 #pragma unroll
@@ -690,6 +785,20 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * tr + g4 + r;
       const bool rs = resp_row(i);
+      if constexpr (L2) {
+        // dq = dq' - r_q^2 q (q . dq'), dk = dk' + k r_k^2 (dv' . v' - 2 b' db'), both streams
+        float qd = 0.f, qnd = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+          qd += late->qdot[w][0][i];
+          qnd += late->qdot[w][1][i];
+        }
+        const float rq = sm.fac[0][i], rqn = sm.fac[2][i];
+        dq[tr][r] -= rq * rq * bf2f(sm.x[0][i][col0 + cl]) * qd;
+        dk[tr][r] += bf2f(sm.x[1][i][col0 + cl]) * late->ck[0][i];
+        dqn[tr][r] -= rqn * rqn * bf2f(sm.x[2][i][col0 + cl]) * qnd;
+        dkn[tr][r] += bf2f(sm.x[3][i][col0 + cl]) * late->ck[1][i];
+      }
       sm.x[0][i][col0 + cl] = f2bf(dq[tr][r]);
       sm.x[1][i][col0 + cl] = f2bf(dk[tr][r]);
       sm.x[2][i][col0 + cl] = f2bf(rs ? dqn[tr][r] : 0.f);
@@ -757,18 +866,21 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     if (c0 + i < n) {
       if (!noisy) {
         a.dalpha[gi] = v / sm.alpha[0][i];
-        a.dbeta[gi] = db;
+        a.dbeta[gi] = L2 ? db * sm.fac[1][i] * sm.fac[1][i] : db;
       } else {
         const bool rsp = c0 + i >= P;
         a.dalpha_n[gi] = rsp ? v / sm.alpha[1][i] : 0.f;
-        a.dbeta_n[gi] = rsp ? db : 0.f;
+        a.dbeta_n[gi] = rsp ? (L2 ? db * sm.fac[3][i] * sm.fac[3][i] : db) : 0.f;
       }
     }
   }
 }
 
 hipError_t launch_bwd_chunk_d128(const BwdArgs &a, hipStream_t st, int64_t slots) {
-  hipLaunchKernelGGL(gdn_bwd_chunk_d128_kernel, dim3((unsigned)(slots * a.f.H)), dim3(kNT), 0, st, a);
+  if (a.f.l2f)
+    hipLaunchKernelGGL(gdn_bwd_chunk_d128_kernel<true>, dim3((unsigned)(slots * a.f.H)), dim3(kNT), 0, st, a);
+  else
+    hipLaunchKernelGGL(gdn_bwd_chunk_d128_kernel<false>, dim3((unsigned)(slots * a.f.H)), dim3(kNT), 0, st, a);
   return hipGetLastError();
 }
 

@@ -17,6 +17,9 @@
 // [16 w, 16 w + 16) of R (a register slab, slab.h) and one of the fragment
 // sets.  LDS holds only what the waves share: q, k, q~, k~ transposed
 // ([d_k][chunk row]) and the six chunk matrices -- 64 KB, two workgroups per CU.
+// L2: the q/k L2 flag folded into per-row factors (gdn_l2.hip): the write
+// strengths arrive folded from the gate load and the output gradients are
+// r_q do, r_q~ do~.
 #include "bwd_common.h"
 #include "device_common.h"
 #include "host_plan.h"
@@ -37,10 +40,12 @@ struct PreSmem {
   alignas(16) u16 xt[4][pD][pLDT];    // q, k, q~, k~ transposed
   alignas(16) float cc[6][pC][pLDM];  // T, T~, Mwo, Mwq, Mwk, Mw~ (b folded)
   alignas(16) float lg[pC], beta[pC], lgn[pC], betan[pC];
+  alignas(16) float rq[2][pC];  // L2: r_q, r_q~ of the chunk's rows
 };
 
 }  // namespace
 
+template <bool L2>
 __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
   constexpr int C = pC, D = pD, NT = pNT, LDM = pLDM;
   __shared__ PreSmem sm;
@@ -77,6 +82,9 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
 #pragma unroll
   for (int j = 0; j < 3; ++j) tv[j] = *reinterpret_cast<const float4 *>(tri + 4 * (j * NT + tid));
   const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
+  float l2r = 1.f;  // L2, thread tid < 64: r_q (tid < 32) or r_q~ of row tid % 32
+  if (L2 && tid < 2 * C) l2r = reinterpret_cast<const float *>(f.l2f + (t0g + min(c0 + (tid & (C - 1)), n - 1)) * H +
+                                                               h)[2 * (tid / C)];
   u16 rdo[2][4], rdon[2][4];
   gslab_raw<D>(rdo, pdo, H, h, t0g, c0, n, col0);
   gslab_raw<D>(rdon, pdon, H, h, t0g, c0, n, col0);
@@ -117,6 +125,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
     *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = tv[j];
   }
   if (tid < 4 * C) gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
+  if (L2 && tid < 2 * C) sm.rq[tid / C][tid & (C - 1)] = l2r;
   lds_barrier();
 
   const float lgC = sm.lg[C - 1];
@@ -158,7 +167,19 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
   // ---- the state-independent chain of this wave's slab
   auto Gm = [&](int i) { return __expf(sm.lg[i]); };
   auto Gp = [&](int i) { const int pi = i - (i % B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
-  const Slab DO = slab_mask(rdo, c0, n, P, false), DON = slab_mask(rdon, c0, n, P, true);
+  Slab DO = slab_mask(rdo, c0, n, P, false), DON = slab_mask(rdon, c0, n, P, true);
+  if constexpr (L2) {
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = slab_row(tr, r);
+        DO.t[tr][r] *= sm.rq[0][i];
+        DON.t[tr][r] *= sm.rq[1][i];
+      }
+  }
+  // with L2 the scaled gradients are no longer exact in bf16: both operands split
+  constexpr int DT = L2 ? 3 : 2;
   Slab Y1, Y2 = slab_zero(), Y3 = slab_zero(), DRQ = slab_zero(), DRK = slab_zero();
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
     for (int r = 0; r < 4; ++r) Y1.t[tr][r] = s * Gm(slab_row(tr, r)) * DO.t[tr][r];
   if (has_noisy) {
     Slab dun = slab_zero();
-    cc_mul<2, true>(dun, &sm.cc[PT_MN][0][0], LDM, DON);  // Mw~^T do~
+    cc_mul<DT, true>(dun, &sm.cc[PT_MN][0][0], LDM, DON);  // Mw~^T do~
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -188,7 +209,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
       }
   }
   Slab dU0 = slab_zero();
-  cc_mul<2, true>(dU0, &sm.cc[PT_MO][0][0], LDM, DO);
+  cc_mul<DT, true>(dU0, &sm.cc[PT_MO][0][0], LDM, DO);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr) dU0.t[tr] *= s;
   if (has_noisy) {
@@ -235,7 +256,10 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
 }
 
 hipError_t launch_bwd_pre_d128(const BwdArgs &a, hipStream_t st, int64_t slots) {
-  hipLaunchKernelGGL(gdn_bwd_pre_d128_kernel, dim3((unsigned)(slots * a.f.H)), dim3(pNT), 0, st, a);
+  if (a.f.l2f)
+    hipLaunchKernelGGL(gdn_bwd_pre_d128_kernel<true>, dim3((unsigned)(slots * a.f.H)), dim3(pNT), 0, st, a);
+  else
+    hipLaunchKernelGGL(gdn_bwd_pre_d128_kernel<false>, dim3((unsigned)(slots * a.f.H)), dim3(pNT), 0, st, a);
   return hipGetLastError();
 }
 

@@ -715,13 +715,22 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st) {
-  if (a.num_docs == 0) return hipSuccess;
+hipError_t launch_gdn_fwd(const FwdArgs &a_in, hipStream_t st) {
+  if (a_in.num_docs == 0) return hipSuccess;
+  FwdArgs a = a_in;
   if (a.workspace) {
-    // bf16, d = 128, no flags: chunk matrices and the scan hand-over in
-    // parallel, the state recurrence (chunk-start states -> ckpt, or the
-    // workspace when no checkpoints are asked for), then the outputs in parallel
+    // bf16, d = 128: chunk matrices and the scan hand-over in parallel, the
+    // state recurrence (chunk-start states -> ckpt, or the workspace when no
+    // checkpoints are asked for), then the outputs in parallel; with the q/k
+    // L2 flag first the per-row factors the kernels fold in (gdn_l2.hip)
     const int64_t slots = a.T / kChunk + a.num_docs;
+    if (a.flags & 1) {
+      const size_t per_bytes = (size_t)slots * a.H * (6 * kChunk * kChunk + kScanPackFloats + (size_t)a.D * a.D) * 4;
+      float4 *l2f = reinterpret_cast<float4 *>(reinterpret_cast<char *>(a.workspace) + ((per_bytes + 255) & ~(size_t)255));
+      hipError_t e = launch_l2_factors(a, l2f, st);
+      if (e != hipSuccess) return e;
+      a.l2f = l2f;
+    }
     const size_t per = (size_t)slots * a.H;
     float *const cmat = a.workspace;
     float *const pack = cmat + per * 6 * kChunk * kChunk;

@@ -20,6 +20,9 @@
 // [16 w, 16 w + 16): every C x 16 quantity is a register slab (slab.h) and
 // S_c's columns are the B operand of X S_c, split hi + lo.  The outputs leave
 // through LDS staging (over the q/k rows) as 16-byte row stores.
+// L2: the q/k L2 flag folded into per-row factors (gdn_l2.hip): the write
+// strengths arrive folded from the gate load, v and v~ rows are divided by
+// r_k and r_k~, and the rows of o and o~ multiplied by r_q and r_q~.
 #include "bwd_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -37,10 +40,12 @@ struct OutSmem {
   alignas(16) u16 x[4][oC][oLDX];     // q, k, q~, k~ rows; then the o, o~ staging
   alignas(16) float cc[6][oC][oLDM];  // T, T~, Mwo, Mwq, Mwk, Mw~
   alignas(16) float lg[oC], beta[oC], lgn[oC], betan[oC];
+  alignas(16) float fac[4][oC];  // L2: r_q, 1 / r_k, r_q~, 1 / r_k~ of the chunk's rows
 };
 
 }  // namespace
 
+template <bool L2>
 __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const float *cmat, const float *states) {
   constexpr int C = oC, D = oD, NT = oNT, LDM = oLDM;
   __shared__ OutSmem sm;
@@ -77,6 +82,11 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
 #pragma unroll
   for (int j = 0; j < 3; ++j) cv[j] = reinterpret_cast<const float4 *>(cm)[j * NT + tid];
   const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
+  float l2r = 1.f;  // thread tid < 128: factor tid / 32 of row tid % 32
+  if (L2 && tid < 4 * C) {
+    const float *fr = reinterpret_cast<const float *>(f.l2f + (t0g + min(c0 + (tid & (C - 1)), n - 1)) * H + h);
+    l2r = fr[tid / C];
+  }
   u16 rv[2][4], rvn[2][4];
   gslab_raw<D>(rv, pv, H, h, t0g, c0, n, col0);
   gslab_raw<D>(rvn, pvn, H, h, t0g, c0, n, col0);
@@ -106,6 +116,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = cv[j];
   }
   if (tid < 4 * C) gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
+  if (L2 && tid < 4 * C) sm.fac[tid / C][tid & (C - 1)] = (tid / C) & 1 ? (l2r > 0.f ? 1.f / l2r : 0.f) : l2r;
   lds_barrier();
 
   // A fragment of rows 16 tr .. of a row tile over d_k step ks, columns in the
@@ -139,7 +150,10 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rhs.t[tr][r] = V.t[tr][r] - Gm(slab_row(tr, r)) * KS.t[tr][r];
+    for (int r = 0; r < 4; ++r) {
+      const int i = slab_row(tr, r);
+      rhs.t[tr][r] = (L2 ? V.t[tr][r] * sm.fac[1][i] : V.t[tr][r]) - Gm(i) * KS.t[tr][r];
+    }
   Slab U = slab_zero();
   cc_mul<3, false>(U, &sm.cc[OC_T][0][0], LDM, rhs);
   // o = s (G Q S_c + Mwo U)
@@ -151,6 +165,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     for (int r = 0; r < 4; ++r) {
       const int i = slab_row(tr, r);
       O.t[tr][r] = s * (Gm(i) * QS.t[tr][r] + O.t[tr][r]);
+      if constexpr (L2) O.t[tr][r] *= sm.fac[0][i];
     }
   // the noisy blocks: reads of their boundary states, then the block
   Slab ON = slab_zero();
@@ -182,7 +197,8 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        rhsn.t[tr][r] = VN.t[tr][r] - __expf(sm.lgn[slab_row(tr, r)]) * RK.t[tr][r];
+        rhsn.t[tr][r] = (L2 ? VN.t[tr][r] * sm.fac[3][slab_row(tr, r)] : VN.t[tr][r]) -
+                        __expf(sm.lgn[slab_row(tr, r)]) * RK.t[tr][r];
     Slab UN = slab_zero();
     cc_mul<3, false>(UN, &sm.cc[OC_TN][0][0], LDM, rhsn);
     cc_mul<3, false>(ON, &sm.cc[OC_MN][0][0], LDM, UN);
@@ -193,6 +209,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
         const int i = slab_row(tr, r), pi = i - (i % B);
         const bool resp = c0 + i < n && c0 + i >= P;
         ON.t[tr][r] = resp ? s * (__expf(sm.lgn[pi + B - 1]) * RQ.t[tr][r] + ON.t[tr][r]) : 0.f;
+        if constexpr (L2) ON.t[tr][r] = resp ? ON.t[tr][r] * sm.fac[2][i] : 0.f;
       }
   }
 
@@ -221,7 +238,12 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
 
 hipError_t launch_fwd_out_d128(const FwdArgs &a, const float *cmat, const float *states, hipStream_t st,
                                int64_t slots) {
-  hipLaunchKernelGGL(gdn_fwd_out_d128_kernel, dim3((unsigned)(slots * a.H)), dim3(oNT), 0, st, a, cmat, states);
+  if (a.l2f)
+    hipLaunchKernelGGL(gdn_fwd_out_d128_kernel<true>, dim3((unsigned)(slots * a.H)), dim3(oNT), 0, st, a, cmat,
+                       states);
+  else
+    hipLaunchKernelGGL(gdn_fwd_out_d128_kernel<false>, dim3((unsigned)(slots * a.H)), dim3(oNT), 0, st, a, cmat,
+                       states);
   return hipGetLastError();
 }
 

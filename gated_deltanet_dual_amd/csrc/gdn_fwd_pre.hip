@@ -16,6 +16,8 @@
 //
 // One workgroup of 8 waves per (chunk slot, head); wave w owns d_v columns
 // [16 w, 16 w + 16) of Z (a register slab, slab.h) and one fragment set.
+// L2: the q/k L2 flag folded into per-row factors (gdn_l2.hip): the write
+// strengths arrive folded from the gate load, the v rows are divided by r_k.
 #include "bwd_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -32,10 +34,12 @@ struct FwdPreSmem {
   alignas(16) u16 kt[fD][fLDT];    // k transposed ([d_k][chunk row])
   alignas(16) float tm[fC][fLDM];  // T
   alignas(16) float lg[fC], beta[fC], lgn[fC], betan[fC];
+  alignas(16) float vsc[fC];  // L2: 1 / r_k of the chunk's rows
 };
 
 }  // namespace
 
+template <bool L2>
 __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const float *cmat, float *pack_all) {
   constexpr int C = fC, D = fD, LDM = fLDM;
   __shared__ FwdPreSmem sm;
@@ -72,6 +76,8 @@ __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const 
   const u16 *ka_src = pk + ((t0g + min(c0 + ka_row, n - 1)) * H + h) * D;
   const uint2 ka0 = *reinterpret_cast<const uint2 *>(ka_src + ka_col);
   const uint2 ka1 = *reinterpret_cast<const uint2 *>(ka_src + ka_col + 16);
+  float rkl = 1.f;
+  if (L2 && tid < C) rkl = f.l2f[(t0g + min(c0 + tid, n - 1)) * H + h].y;
 
   // ---- LDS: k transposed (rows past the document end zero), T, gates
   if (tid < 128) {
@@ -92,6 +98,7 @@ __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const 
   }
   if (tid < C * C / 4) *reinterpret_cast<float4 *>(&sm.tm[tid / (C / 4)][4 * (tid % (C / 4))]) = tv;
   if (tid < 4 * C) gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
+  if (L2 && tid < C) sm.vsc[tid] = rkl > 0.f ? 1.f / rkl : 0.f;
   lds_barrier();
 
   const float lgC = sm.lg[C - 1];
@@ -131,9 +138,17 @@ __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const 
 
   // ---- Z = diag(D) T V for this wave's slab (R = K^T Z: the scan adds Z to
   // W (K S_c) ahead of its K^T product), stored as [slab][tile][lane][4]
-  const Slab V = slab_mask(rv, c0, n, P, false);
+  Slab V = slab_mask(rv, c0, n, P, false);
   Slab Z = slab_zero();
-  cc_mul<2, false>(Z, &sm.tm[0][0], LDM, V);
+  if constexpr (L2) {  // v' = v / r_k is no longer exact in bf16: both operands split
+#pragma unroll
+    for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) V.t[tr][r] *= sm.vsc[slab_row(tr, r)];
+    cc_mul<3, false>(Z, &sm.tm[0][0], LDM, V);
+  } else {
+    cc_mul<2, false>(Z, &sm.tm[0][0], LDM, V);
+  }
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -144,7 +159,11 @@ __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const 
 }
 
 hipError_t launch_fwd_pre_d128(const FwdArgs &a, const float *cmat, float *pack, hipStream_t st, int64_t slots) {
-  hipLaunchKernelGGL(gdn_fwd_pre_d128_kernel, dim3((unsigned)(slots * a.H)), dim3(fNT), 0, st, a, cmat, pack);
+  if (a.l2f)
+    hipLaunchKernelGGL(gdn_fwd_pre_d128_kernel<true>, dim3((unsigned)(slots * a.H)), dim3(fNT), 0, st, a, cmat, pack);
+  else
+    hipLaunchKernelGGL(gdn_fwd_pre_d128_kernel<false>, dim3((unsigned)(slots * a.H)), dim3(fNT), 0, st, a, cmat,
+                       pack);
   return hipGetLastError();
 }
 

@@ -90,16 +90,27 @@ int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride) {
   return vi.total_tokens / span + vi.num_docs;
 }
 
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static size_t l2_factor_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
+  return (s->flags & FLARE_QK_L2NORM) ? (size_t)vi.total_tokens * s->num_heads * 4 * sizeof(float) : 0;
+}
+
+size_t bwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
+  size_t per = (size_t)s->d_k * s->d_v + 6 * kChunk * kChunk;
+  if (bwd_uses_scan_pack(s)) per += kScanPackFloats;
+  return round256((size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float));
+}
+
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   // per chunk slot and head, fp32, in the checkpoint slot layout (stride 1):
   // the chunk's end-state adjoint (d_k x d_v), written by the reverse scan and
   // read by the per-chunk pass, then six kChunk x kChunk chunk matrices (the
   // triangular inverses T, T~ and four weighted Gram matrices), written by the
   // chunk-matrix pass and read by both; for bf16 io at d = 128 then the
-  // pre-pass's hand-over to the reverse scan
-  size_t per = (size_t)s->d_k * s->d_v + 6 * kChunk * kChunk;
-  if (bwd_uses_scan_pack(s)) per += kScanPackFloats;
-  return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float) + 256;
+  // pre-pass's hand-over to the reverse scan; with the q/k L2 flag then the
+  // per-(token, head) factors {r_q, r_k, r_q~, r_k~}
+  return bwd_l2_offset(vi, s) + l2_factor_bytes(vi, s) + 256;
 }
 
 bool bwd_uses_scan_pack(const flare_gdn_shape *s) {
@@ -107,15 +118,20 @@ bool bwd_uses_scan_pack(const flare_gdn_shape *s) {
 }
 
 bool fwd_uses_chunk_matrices(const flare_gdn_shape *s) {
-  return s->io_dtype == FLARE_BF16 && s->d_k == 128 && s->d_v == 128 && s->flags == 0;
+  return s->io_dtype == FLARE_BF16 && s->d_k == 128 && s->d_v == 128 && (s->flags & ~FLARE_QK_L2NORM) == 0;
+}
+
+size_t fwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
+  const size_t per = 6 * kChunk * kChunk + kScanPackFloats + (size_t)s->d_k * s->d_v;
+  return round256((size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float));
 }
 
 size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   if (!fwd_uses_chunk_matrices(s)) return 0;
   // per chunk slot and head, fp32: the six chunk matrices, the scan hand-over,
-  // and room for the chunk-start state when no checkpoints are asked for
-  const size_t per = 6 * kChunk * kChunk + kScanPackFloats + (size_t)s->d_k * s->d_v;
-  return (size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float) + 256;
+  // and room for the chunk-start state when no checkpoints are asked for; with
+  // the q/k L2 flag then the per-(token, head) factors {r_q, r_k, r_q~, r_k~}
+  return fwd_l2_offset(vi, s) + l2_factor_bytes(vi, s) + 256;
 }
 
 int64_t route1_num_blocks(const flare_varlen *v, int32_t block_size) {
@@ -137,8 +153,6 @@ int64_t route1_num_windows(const flare_varlen *v) {
   }
   return nw;
 }
-
-static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t route1_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s, int64_t n_blocks) {
   return round256(fwd_workspace_bytes(vi, s)) + round256((size_t)n_blocks * s->num_heads * s->d_k * s->d_v * 4) +

@@ -51,10 +51,15 @@ int64_t ckpt_num_slots(const VarlenInfo &vi, int32_t stride);
 // scan hand-over (kScanPackFloats).
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
 bool bwd_uses_scan_pack(const flare_gdn_shape *s);
+// Byte offsets of the q/k L2 factors (float4 per token and head) in the
+// backward's and the forward's workspace, when the flag is set.
+size_t bwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s);
+size_t fwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s);
 
 // Bytes of fwd workspace when the forward runs its chunked passes (bf16 io,
-// d = 128, no flags), else 0: per chunk slot and head the six chunk matrices,
-// the scan hand-over and a chunk-start state.
+// d = 128; the q/k L2 flag allowed), else 0: per chunk slot and head the six
+// chunk matrices, the scan hand-over and a chunk-start state, then the L2
+// factors when flagged.
 size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s);
 bool fwd_uses_chunk_matrices(const flare_gdn_shape *s);
 

@@ -52,8 +52,16 @@ struct FwdArgs {
   // pool): document i starts from h0[state_slot[i]] and ends in
   // h_final[state_slot[i]]
   const int32_t *state_slot;
+  // The chunked bf16 d = 128 kernels with the q/k L2 flag: per (token, head)
+  // {r_q, r_k, r_q~, r_k~}, r = 1 / sqrt(sum x^2 + 1e-6) of that row (NULL
+  // without the flag).  The kernels never form the normalised rows: with
+  // k^ = r_k k the step is the plain one on (k, b r_k^2, v / r_k), and
+  // o = r_q s S^T q (gdn_l2.hip).
+  const float4 *l2f;
 };
 hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
+// the per-row L2 factors of q, k, q~, k~ into a.l2f (gdn_l2.hip)
+hipError_t launch_l2_factors(const FwdArgs &a, float4 *out, hipStream_t st);
 
 // bf16 io at d = 128 without flags: the forward's pre-pass (chunk matrices
 // `cmat` -> scan hand-over `pack`, gdn_fwd_pre.hip) and its output pass

@@ -105,8 +105,14 @@ def test_fwd_workspace_checked_before_launch(L):
                               None, 0, None)
     assert st == 5
     # configurations served by the fused kernel need none
-    for other in (g.GDNShape(4, 16, 16, 4, g.BF16, 0, 0.0), g.GDNShape(4, 128, 128, 4, g.BF16, 1, 0.0)):
-        assert L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(other), 0) == 0
+    other = g.GDNShape(4, 16, 16, 4, g.BF16, 0, 0.0)
+    assert L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(other), 0) == 0
+    # the q/k L2 flag adds the per-(token, head) factors (four fp32) after the
+    # per-slot part, which starts the region on a 256-byte boundary
+    l2 = g.GDNShape(4, 128, 128, 4, g.BF16, 1, 0.0)
+    base = need - 256
+    assert L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(l2), 0) == \
+        (base + 255) // 256 * 256 + 164 * 4 * 16 + 256
 
 
 def test_bwd_workspace_checked_before_launch(L):

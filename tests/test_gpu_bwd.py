@@ -26,22 +26,22 @@ def g():
     return g
 
 
-def run_bwd(g, inp, dev, dhf=None, scale=0.0):
+def run_bwd(g, inp, dev, dhf=None, scale=0.0, flags=0):
     import torch
     bf = inp.io == "bf16"
     vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
     args = fwd_args(inp, dev)
     h0 = to_dev(inp.h0, dev) if inp.h0 is not None else None
-    _, _, _, ck = g.gdn_dual_fwd(vl, *args, inp.block_size, h0=h0, scale=scale, want_ckpt=True)
+    _, _, _, ck = g.gdn_dual_fwd(vl, *args, inp.block_size, h0=h0, scale=scale, flags=flags, want_ckpt=True)
     gr = g.gdn_dual_bwd(vl, *args, inp.block_size, ck, to_dev(inp.do, dev, bf), to_dev(inp.don, dev, bf),
-                        h0=h0, dh_final=to_dev(dhf, dev) if dhf is not None else None, scale=scale)
+                        h0=h0, dh_final=to_dev(dhf, dev) if dhf is not None else None, scale=scale, flags=flags)
     torch.cuda.synchronize()
     return gr
 
 
-def ref_bwd(inp, dhf=None, scale=0.0):
+def ref_bwd(inp, dhf=None, scale=0.0, flags=0):
     return oracle.gdn_dual_bwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(),
-                               inp.block_size, inp.do, inp.don, h0=inp.h0, dh_final=dhf, scale=scale)
+                               inp.block_size, inp.do, inp.don, h0=inp.h0, dh_final=dhf, scale=scale, flags=flags)
 
 
 def check(inp, got, want, tol, name):
@@ -154,6 +154,50 @@ def test_bwd_reusing_forward_chunk_matrices_is_identical(g, dev):
     do, don = to_dev(inp.do, dev, True), to_dev(inp.don, dev, True)
     g1 = g.gdn_dual_bwd(vl, *args, 4, ck, do, don)
     g2 = g.gdn_dual_bwd(vl, *args, 4, ck, do, don, fwd_workspace=fws)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("B", [4, 1, 32])
+def test_bwd_bf16_l2norm_flag(g, dev, B):
+    """Reverse mode with the q/k L2 flag on the chunked d = 128 path: the
+    gradients w.r.t. the unnormalised q, k of both streams (through the
+    normalisation), with h0, dh_final and rows of very different norms."""
+    lens = [160, 77, 0, 64, 33]
+    prompts = [min(n, (p // B) * B) for n, p in zip(lens, [64, 32, 0, 0, 32])]
+    inp = wl.gdn_inputs(lens, prompts, 2, 128, 128, B, seed=90 + B, normalize_qk=False, with_h0=True,
+                        with_grads=True)
+    rng = np.random.default_rng(91 + B)
+    for name in ("q", "k", "qn", "kn"):
+        x = getattr(inp, name)
+        setattr(inp, name, wl.round_bf16(x * rng.uniform(0.05, 20.0, x.shape[:2] + (1,)).astype(np.float32)))
+    dhf = (rng.standard_normal((len(lens), 2, 128, 128)) / 16).astype(np.float32)
+    check(inp, run_bwd(g, inp, dev, dhf=dhf, flags=1), ref_bwd(inp, dhf=dhf, flags=oracle.FLAG_QK_L2NORM), TOL_BF16,
+          "bwd_l2_B%d" % B)
+
+
+def test_bwd_l2norm_packed_full_size_all_heads(g, dev):
+    """One packed row of 32768 tokens, 8 Dirichlet-length documents, 32 heads,
+    d = 128, bf16, q/k normalised by the L2 flag in the forward and the
+    reverse mode; every head against the oracle."""
+    lens, prompts = wl.packed_doc_lengths(32768, 8, 4, seed=3)
+    inp = wl.gdn_inputs(lens, prompts, 32, 128, 128, 4, seed=14, normalize_qk=False, with_grads=True)
+    check(inp, run_bwd(g, inp, dev, flags=1), ref_bwd(inp, flags=oracle.FLAG_QK_L2NORM), TOL_BF16, "bwd_l2_packed")
+
+
+def test_bwd_l2norm_reusing_forward_chunk_matrices(g, dev):
+    """With the L2 flag, the backward reading the forward's chunk matrices
+    gives the same bits as forming them again."""
+    import torch
+    inp = wl.gdn_inputs([130, 64, 96], [32, 0, 48], 2, 128, 128, 4, seed=75, normalize_qk=False, with_grads=True)
+    vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+    args = fwd_args(inp, dev)
+    fws = torch.empty((g.workspace_bytes(vl, 2, 128, 4, g.BF16, flags=1),), dtype=torch.uint8, device=dev)
+    _, _, _, ck = g.gdn_dual_fwd(vl, *args, 4, flags=1, want_ckpt=True, workspace=fws)
+    do, don = to_dev(inp.do, dev, True), to_dev(inp.don, dev, True)
+    g1 = g.gdn_dual_bwd(vl, *args, 4, ck, do, don, flags=1)
+    g2 = g.gdn_dual_bwd(vl, *args, 4, ck, do, don, flags=1, fwd_workspace=fws)
     torch.cuda.synchronize()
     for k in GRADS:
         assert torch.equal(g1[k], g2[k]), k

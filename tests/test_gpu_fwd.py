@@ -81,6 +81,23 @@ def test_bf16_l2norm_flag(g, dev):
     check(inp, run(g, inp, dev, flags=1), ref(inp, flags=oracle.FLAG_QK_L2NORM), TOL_BF16, "bf16_l2")
 
 
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_bf16_l2norm_flag_chunked_ragged(g, dev, B):
+    """The q/k L2 flag on the chunked d = 128 path (folded into per-row
+    factors): ragged, empty and sub-chunk documents, prompts mid-chunk, h0,
+    unnormalised q/k of varied scale, checkpoints equal to the unflagged
+    forward's on normalised inputs where those are exact."""
+    lens = [200, 0, 45, 97, 31, 64]
+    prompts = [min(n, (p // B) * B) for n, p in zip(lens, [40, 0, 12, 64, 28, 0])]
+    inp = wl.gdn_inputs(lens, prompts, 3, 128, 128, B, seed=40 + B, normalize_qk=False, with_h0=True)
+    rng = np.random.default_rng(B)
+    for name in ("q", "k", "qn", "kn"):  # rows of very different norms
+        x = getattr(inp, name)
+        setattr(inp, name, wl.round_bf16(x * rng.uniform(0.05, 20.0, x.shape[:2] + (1,)).astype(np.float32)))
+    got = run(g, inp, dev, flags=1, want_ckpt=True)
+    check(inp, got, ref(inp, flags=oracle.FLAG_QK_L2NORM), TOL_BF16, "bf16_l2_B%d" % B)
+
+
 def test_d16_bf16(g, dev):
     inp = wl.gdn_inputs([77, 64], [20, 4], 4, 16, 16, 4, seed=33)
     check(inp, run(g, inp, dev), ref(inp), TOL_BF16, "d16_bf16")
