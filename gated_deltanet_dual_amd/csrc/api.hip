@@ -99,6 +99,11 @@ static flare_status fwd_impl(const flare_varlen *varlen, const flare_gdn_shape *
                        ckpt, ckpt_stride_chunks);
   a.state_slot = state_slot;
   a.workspace = need > 0 ? reinterpret_cast<float *>(workspace) : nullptr;
+  if (need > 0) {  // the state scan in parallel runs for long documents
+    a.scan_span = scan_seg_span(vi, shape->num_heads);
+    a.scan_units = a.scan_span > 0 ? ckpt_num_slots(vi, a.scan_span) : 0;
+    a.scan_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + fwd_seg_offset(vi, shape));
+  }
   return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd launch");
 }
 
@@ -248,6 +253,11 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   a.T = vi.total_tokens;
+  if (bwd_uses_scan_pack(shape)) {  // the reverse scan in parallel runs for long documents
+    a.f.scan_span = scan_seg_span(vi, shape->num_heads);
+    a.f.scan_units = a.f.scan_span > 0 ? ckpt_num_slots(vi, a.f.scan_span) : 0;
+    a.f.scan_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + bwd_seg_offset(vi, shape));
+  }
   return hip_status(launch_gdn_bwd(a, (hipStream_t)stream), "gdn_dual_bwd launch");
 }
 

@@ -896,7 +896,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a_in, hipStream_t st) {
       sa.init = a.dh_final;
       sa.final_out = a.dh0;
       sa.states = reinterpret_cast<float *>(a.workspace);
-      hipError_t e1 = launch_scan_d128(sa, true, st);
+      hipError_t e1 = scan_d128_runs(sa, true, f.scan_span, f.scan_units, f.scan_ws, st);
       if (e1 != hipSuccess) return e1;
     } else {
       hipLaunchKernelGGL((gdn_bwd_scan_kernel<IO, D>), dim3((unsigned)(groups * 8 * Cfg::NTILE)), dim3(256), 0,

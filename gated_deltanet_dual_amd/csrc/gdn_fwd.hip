@@ -760,7 +760,7 @@ hipError_t launch_gdn_fwd(const FwdArgs &a_in, hipStream_t st) {
       sa.slot = a.state_slot;
       sa.states = states;
       TimedLaunch tl(K_FWD_SCAN, st);
-      hipError_t e = launch_scan_d128(sa, false, st);
+      hipError_t e = scan_d128_runs(sa, false, a.scan_span, a.scan_units, a.scan_ws, st);
       if (e != hipSuccess) return e;
     }
     if (slots == 0) return hipSuccess;

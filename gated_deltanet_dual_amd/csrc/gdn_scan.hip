@@ -25,6 +25,14 @@
 // A third wave per workgroup only stores: the compute waves stage each
 // chunk's carried slabs in LDS and it writes them out, so the stores never sit
 // in the compute waves' (in-order) memory counters ahead of their loads.
+//
+// A long document is one long chain.  Its chunks can be cut into runs
+// scanned in parallel (the affine segment scan): the step is affine in X, so
+// a run maps its start value X_0 to M X_0 + N, with M the run's transfer map
+// (the run scanned from the identity without the right-hand side) and N its
+// offset (the run scanned from zero).  The runs' start values then follow
+// from one short sequential pass over the runs (gdn_scan_compose_kernel), and
+// a last parallel scan of every run from its start value writes the states.
 #include "bwd_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -69,20 +77,41 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
 
-  // ---- workgroup -> (document, head, quarter); the quarters of a pair share an XCD
+  // ---- workgroup -> (unit, head, quarter); the quarters of a pair share an XCD
   const int L = blockIdx.x;
   const int grp = L / (8 * sNQ), rem = L % (8 * sNQ);
   const int quarter = rem / 8;
-  const int pair = grp * 8 + (rem % 8);
-  if (pair >= a.num_docs * a.H) return;
-  const int doc = pair / a.H, h = pair % a.H;
+  const int64_t pair = (int64_t)grp * 8 + (rem % 8);
+  const int64_t npairs = (a.seg_span > 0 ? a.units : a.num_docs) * a.H;
+  if (pair >= npairs) return;
+  const int64_t unit = pair / a.H;
+  const int h = (int)(pair % a.H);
   const int H = a.H;
+  int doc = (int)unit, seg = 0;
+  if (a.seg_span > 0) {  // unit -> (document, run): the checkpoint-slot numbering of stride seg_span
+    const int64_t span = (int64_t)C * a.seg_span;
+    int lo = 0, hi = a.num_docs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)a.cu[mid] / span + mid <= unit) lo = mid; else hi = mid - 1;
+    }
+    doc = lo;
+    seg = (int)(unit - (int64_t)a.cu[doc] / span - doc);
+  }
   const int64_t t0g = a.cu[doc];
   const int n = a.cu[doc + 1] - a.cu[doc];
-  const int nchunks = (n + C - 1) / C;
+  const int nchunks_doc = (n + C - 1) / C;
+  // this run's chunks [c_lo, c_hi); an empty document is one empty run (its init passes through)
+  const int c_lo = a.seg_span > 0 ? seg * a.seg_span : 0;
+  const int c_hi = a.seg_span > 0 ? min(c_lo + a.seg_span, nchunks_doc) : nchunks_doc;
+  if (c_lo > 0 && c_lo >= nchunks_doc) return;  // a unit no run maps to
+  const int nchunks = c_hi - c_lo;
+  const bool first_run = REVERSE ? c_hi == nchunks_doc : c_lo == 0;
+  const bool last_run = REVERSE ? c_lo == 0 : c_hi == nchunks_doc;
   const int64_t ck_base = (int64_t)(t0g / C) + doc;
+  const int sstride = a.states_stride > 1 ? a.states_stride : 1;
   // step i handles chunk at(i)
-  auto at = [&](int i) { return REVERSE ? nchunks - 1 - i : i; };
+  auto at = [&](int i) { return REVERSE ? c_hi - 1 - i : c_lo + i; };
 
   // ---- the store wave: after each chunk's barrier, the carried slabs the
   // compute waves staged for that chunk -> global, row-major [d_k][d_v], as
@@ -93,7 +122,9 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     for (int i = 0; i < nchunks; ++i) {
       const int c = at(i);
       lds_barrier();
-      float *dst = a.states + ((ck_base + c) * H + h) * (size_t)D * D;
+      if (!a.states || c % sstride != 0) continue;
+      const int64_t sslot = sstride == 1 ? ck_base + c : t0g / ((int64_t)C * sstride) + doc + c / sstride;
+      float *dst = a.states + (sslot * H + h) * (size_t)D * D;
 #pragma unroll
       for (int w = 0; w < sNW; ++w)
 #pragma unroll
@@ -110,15 +141,23 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
 
   // ---- X slab: tile kt holds rows 16 kt + 4 g + r (d_k), column dv0 + cl
   floatx4 X[8];
+  const float *src = nullptr;
+  if (!a.identity_init) {
+    if (first_run) src = a.init ? a.init + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D : nullptr;
+    else src = a.seg_init ? a.seg_init + ((size_t)unit * H + h) * D * D : nullptr;
+  }
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
     X[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (a.init) {
-      const float *src = a.init + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D;
+    if (src) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) X[kt][r] = src[(size_t)(16 * kt + g4 + r) * D + dv0 + cl];
+    } else if (a.identity_init) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[kt][r] = 16 * kt + g4 + r == dv0 + cl ? 1.f : 0.f;
     }
   }
+  const bool homog = a.homog != 0;
   // the X slab -> the store wave's staging area for chunk parity `par`
   auto stage_X = [&](int par) {
 #pragma unroll
@@ -130,7 +169,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   // an empty document still owns one slot), so no load sits under a branch:
   // the compiler would otherwise wait for every load issued before it.
   auto load_ring = [&](ScanRing &p, int c) {
-    c = max(0, min(c, nchunks - 1));
+    c = max(c_lo, min(c, c_hi - 1));
     const float *pk = a.pack + ((size_t)(ck_base + c) * H + h) * kPackWords;
     constexpr int NR = ZRHS ? 2 : 8;
     const uint4 *pr = reinterpret_cast<const uint4 *>(pk + kPackR) + (size_t)slab * NR * 64;
@@ -183,10 +222,12 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     }
     // X <- g_C X + R + K^T Y, or g_C X + K^T (Y + Z)
     if constexpr (ZRHS) {
+      if (!homog) {
 #pragma unroll
-      for (int tr = 0; tr < 2; ++tr) {
-        const float4 zv = __builtin_bit_cast(float4, p.r[tr]);
-        Y.t[tr] += floatx4{zv.x, zv.y, zv.z, zv.w};
+        for (int tr = 0; tr < 2; ++tr) {
+          const float4 zv = __builtin_bit_cast(float4, p.r[tr]);
+          Y.t[tr] += floatx4{zv.x, zv.y, zv.z, zv.w};
+        }
       }
     }
     bf16x8 yh, yl;
@@ -197,7 +238,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
         X[kt] = p.gc * X[kt];
       } else {
         const float4 rv = __builtin_bit_cast(float4, p.r[kt]);
-        X[kt] = p.gc * X[kt] + floatx4{rv.x, rv.y, rv.z, rv.w};
+        X[kt] = p.gc * X[kt] + (homog ? floatx4{0.f, 0.f, 0.f, 0.f} : floatx4{rv.x, rv.y, rv.z, rv.w});
       }
       mma_bf16(X[kt], bf(sh[12 + kt][lane]), yh);
       mma_bf16(X[kt], bf(sh[12 + kt][lane]), yl);
@@ -221,8 +262,15 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     if (i + 3 >= nchunks) break;
     step(p3, at(i + 3), at(i + 7));
   }
-  if (a.final_out) {
+  if (a.final_out && last_run) {
     float *dst = a.final_out + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kt + g4 + r) * D + dv0 + cl] = X[kt][r];
+  }
+  if (a.seg_final) {
+    float *dst = a.seg_final + ((size_t)unit * H + h) * D * D;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
@@ -230,9 +278,118 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   }
 }
 
+// The runs' start values, one workgroup of 8 waves per (document, head), wave
+// w the 16-column slab w of X, in scan order over the document's runs:
+//   seg_out[unit_g] = X_g,  X_{g+1} = M_g X_g + N_g
+// (M_g X_g on the matrix cores, M split hi + lo as A fragments from global
+// memory, X as split B fragments from its accumulators, the slab
+// k-permutation of slab.h over d_k).
+template <bool REVERSE>
+__global__ __launch_bounds__(512) void gdn_scan_compose_kernel(ScanArgs a, const float *M, const float *Nb,
+                                                               float *seg_out) {
+  constexpr int C = sC, D = sD;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = 4 * (lane >> 4), cl = lane & 15;
+  const int doc = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int H = a.H;
+  const int n = a.cu[doc + 1] - a.cu[doc];
+  const int nchunks = (n + C - 1) / C;
+  const int nruns = nchunks == 0 ? 0 : (nchunks + a.seg_span - 1) / a.seg_span;
+  const int64_t ubase = (int64_t)a.cu[doc] / ((int64_t)C * a.seg_span) + doc;
+  const int dv0 = 16 * wave;
+  floatx4 X[8];
+  const float *src = a.init ? a.init + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D : nullptr;
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) X[kt][r] = src ? src[(size_t)(16 * kt + g4 + r) * D + dv0 + cl] : 0.f;
+  for (int j = 0; j < nruns; ++j) {
+    const int g = REVERSE ? nruns - 1 - j : j;
+    const int64_t u = ubase + g;
+    float *so = seg_out + ((size_t)u * H + h) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) so[(size_t)(16 * kt + g4 + r) * D + dv0 + cl] = X[kt][r];
+    if (j == nruns - 1) break;  // the last run's end value is the scan's own
+    const float *Mg = M + ((size_t)u * H + h) * D * D, *Ng = Nb + ((size_t)u * H + h) * D * D;
+    floatx4 Y[8];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[kt][r] = Ng[(size_t)(16 * kt + g4 + r) * D + dv0 + cl];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      // X rows 32 ks + 4 g + e (e < 4) and 32 ks + 16 + 4 g + e - 4 as the B operand
+      const float xv[8] = {X[2 * ks][0], X[2 * ks][1], X[2 * ks][2], X[2 * ks][3],
+                           X[2 * ks + 1][0], X[2 * ks + 1][1], X[2 * ks + 1][2], X[2 * ks + 1][3]};
+      bf16x8 bh, bl;
+      split8(xv, bh, bl);
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        // A: rows 16 kt + (l & 15) of M, columns in the same permutation
+        const float *mr = Mg + (size_t)(16 * kt + cl) * D + 32 * ks;
+        const float4 m0 = *reinterpret_cast<const float4 *>(mr + g4);
+        const float4 m1 = *reinterpret_cast<const float4 *>(mr + 16 + g4);
+        const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        bf16x8 ah, al;
+        split8(mv, ah, al);
+        mma_bf16(Y[kt], ah, bh);
+        mma_bf16(Y[kt], ah, bl);
+        mma_bf16(Y[kt], al, bh);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) X[kt] = Y[kt];
+  }
+}
+
+hipError_t launch_scan_compose_d128(const ScanArgs &a, const float *M, const float *Nb, float *seg_out, bool reverse,
+                                    hipStream_t st) {
+  const dim3 grid((unsigned)(a.num_docs * a.H)), block(512);
+  if (reverse) hipLaunchKernelGGL(gdn_scan_compose_kernel<true>, grid, block, 0, st, a, M, Nb, seg_out);
+  else hipLaunchKernelGGL(gdn_scan_compose_kernel<false>, grid, block, 0, st, a, M, Nb, seg_out);
+  return hipGetLastError();
+}
+
+hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t units, float *ws, hipStream_t st) {
+  if (span <= 0) return launch_scan_d128(a, reverse, st);
+  const size_t per = (size_t)units * a.H * sD * sD;
+  float *const M = ws, *const Nb = ws + per, *const S = ws + 2 * per;
+  ScanArgs r = a;
+  r.seg_span = span;
+  r.units = units;
+  r.states = nullptr;
+  r.final_out = nullptr;
+  r.seg_init = nullptr;
+  // the runs' transfer maps (from the identity, no right-hand side)
+  ScanArgs m = r;
+  m.init = nullptr;
+  m.identity_init = 1;
+  m.homog = 1;
+  m.seg_final = M;
+  hipError_t e = launch_scan_d128(m, reverse, st);
+  if (e != hipSuccess) return e;
+  // their offsets (from zero)
+  ScanArgs z = r;
+  z.init = nullptr;
+  z.seg_final = Nb;
+  e = launch_scan_d128(z, reverse, st);
+  if (e != hipSuccess) return e;
+  // the runs' start values in scan order, then every run from its start value
+  ScanArgs c = a;
+  c.seg_span = span;
+  e = launch_scan_compose_d128(c, M, Nb, S, reverse, st);
+  if (e != hipSuccess) return e;
+  c.units = units;
+  c.seg_init = S;
+  c.seg_final = nullptr;
+  return launch_scan_d128(c, reverse, st);
+}
+
 hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st) {
-  const int pairs = a.num_docs * a.H;
-  const int groups = (pairs + 7) / 8;
+  const int64_t pairs = (a.seg_span > 0 ? a.units : a.num_docs) * a.H;
+  const int64_t groups = (pairs + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * sNQ)), block(64 * (sNW + 1));
   // the reverse recurrence carries a full R, the forward one K^T Z
   if (reverse) hipLaunchKernelGGL((gdn_scan_d128_kernel<true, false>), grid, block, 0, st, a);

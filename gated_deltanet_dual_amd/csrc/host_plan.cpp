@@ -96,10 +96,35 @@ static size_t l2_factor_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   return (s->flags & FLARE_QK_L2NORM) ? (size_t)vi.total_tokens * s->num_heads * 4 * sizeof(float) : 0;
 }
 
+int scan_seg_span(const VarlenInfo &vi, int32_t heads) {
+  // one chain per (document, head) and four workgroups per chain: cut the
+  // documents into runs when the chains cannot fill the chip, aiming at about
+  // twice kScanWorkgroupTarget workgroups, and only for runs of at least
+  // kScanMinRun chunks (shorter ones cost more in the transfer maps than the
+  // parallel runs save)
+  const int64_t chains = (int64_t)vi.num_docs * heads * 4;
+  if (chains <= 0 || chains >= kScanWorkgroupTarget) return 0;
+  const int64_t runs = (2 * kScanWorkgroupTarget + chains - 1) / chains;
+  const int64_t max_chunks = ((int64_t)vi.max_len + kChunk - 1) / kChunk;
+  const int64_t span = (max_chunks + runs - 1) / runs;
+  return span >= kScanMinRun ? (int)span : 0;
+}
+
+static size_t seg_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
+  const int span = scan_seg_span(vi, s->num_heads);
+  if (span == 0) return 0;
+  // the runs' transfer maps, offsets and start values
+  return 3 * (size_t)ckpt_num_slots(vi, span) * s->num_heads * s->d_k * s->d_v * sizeof(float);
+}
+
 size_t bwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
   size_t per = (size_t)s->d_k * s->d_v + 6 * kChunk * kChunk;
   if (bwd_uses_scan_pack(s)) per += kScanPackFloats;
   return round256((size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float));
+}
+
+size_t bwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
+  return round256(bwd_l2_offset(vi, s) + l2_factor_bytes(vi, s));
 }
 
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
@@ -109,8 +134,10 @@ size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   // triangular inverses T, T~ and four weighted Gram matrices), written by the
   // chunk-matrix pass and read by both; for bf16 io at d = 128 then the
   // pre-pass's hand-over to the reverse scan; with the q/k L2 flag then the
-  // per-(token, head) factors {r_q, r_k, r_q~, r_k~}
-  return bwd_l2_offset(vi, s) + l2_factor_bytes(vi, s) + 256;
+  // per-(token, head) factors {r_q, r_k, r_q~, r_k~}; when the scan runs in
+  // parallel runs (long documents, bf16 io at d = 128), the runs' transfer
+  // maps, offsets and start values
+  return bwd_seg_offset(vi, s) + (bwd_uses_scan_pack(s) ? seg_bytes(vi, s) : 0) + 256;
 }
 
 bool bwd_uses_scan_pack(const flare_gdn_shape *s) {
@@ -126,12 +153,17 @@ size_t fwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
   return round256((size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float));
 }
 
+size_t fwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
+  return round256(fwd_l2_offset(vi, s) + l2_factor_bytes(vi, s));
+}
+
 size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   if (!fwd_uses_chunk_matrices(s)) return 0;
   // per chunk slot and head, fp32: the six chunk matrices, the scan hand-over,
   // and room for the chunk-start state when no checkpoints are asked for; with
-  // the q/k L2 flag then the per-(token, head) factors {r_q, r_k, r_q~, r_k~}
-  return fwd_l2_offset(vi, s) + l2_factor_bytes(vi, s) + 256;
+  // the q/k L2 flag then the per-(token, head) factors {r_q, r_k, r_q~, r_k~};
+  // then the scan's run buffers when it runs in parallel runs
+  return fwd_seg_offset(vi, s) + seg_bytes(vi, s) + 256;
 }
 
 int64_t route1_num_blocks(const flare_varlen *v, int32_t block_size) {

@@ -55,6 +55,16 @@ bool bwd_uses_scan_pack(const flare_gdn_shape *s);
 // backward's and the forward's workspace, when the flag is set.
 size_t bwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s);
 size_t fwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s);
+// The state scans of the chunked path (bf16 io, d = 128) run each document's
+// chunks as one chain per head unless too few chains fill the chip: then each
+// document is cut into runs of scan_seg_span() chunks, scanned in parallel
+// and joined by their affine transfer maps (0: no runs).  The run buffers sit
+// at these offsets of the forward's / backward's workspace.
+constexpr int kScanWorkgroupTarget = 256;  // workgroups that fill the chip (one per CU)
+constexpr int kScanMinRun = 32;            // shortest run worth its transfer map
+int scan_seg_span(const VarlenInfo &vi, int32_t heads);
+size_t fwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s);
+size_t bwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s);
 
 // Bytes of fwd workspace when the forward runs its chunked passes (bf16 io,
 // d = 128; the q/k L2 flag allowed), else 0: per chunk slot and head the six

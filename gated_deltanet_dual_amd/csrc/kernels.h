@@ -58,6 +58,11 @@ struct FwdArgs {
   // k^ = r_k k the step is the plain one on (k, b r_k^2, v / r_k), and
   // o = r_q s S^T q (gdn_l2.hip).
   const float4 *l2f;
+  // the state scan in parallel runs of scan_span chunks (0: one chain per
+  // document and head), scan_units runs, their buffers at scan_ws (gdn_scan.hip)
+  int scan_span;
+  int64_t scan_units;
+  float *scan_ws;
 };
 hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
 // the per-row L2 factors of q, k, q~, k~ into a.l2f (gdn_l2.hip)
@@ -72,16 +77,42 @@ hipError_t launch_fwd_out_d128(const FwdArgs &a, const float *cmat, const float 
 
 // The sequential chunk recurrence X <- g_C X + R + K^T (W (K X)) over the chunks
 // of each document (gdn_scan.hip), forward or in reverse.
+//
+// Runs: with seg_span > 0 each document's chunks are cut into runs of
+// seg_span chunks, scanned in parallel; run (document i, index g) is unit
+// ckpt_slot(cu_i, i, g * seg_span, seg_span) (host_plan.h), units in all
+// ckpt_num_slots(T, N, seg_span).  A document's first run in scan order starts
+// from init (or zero), every other run from seg_init[unit] (or zero when
+// seg_init is NULL); with identity_init every run starts from the identity
+// instead, and with homog the step drops its right-hand side, so the run
+// computes its transfer map X -> M X.  seg_final[unit] receives X after the
+// run's last step.  seg_span = 0: one run per document (unit = document).
 struct ScanArgs {
   int num_docs, H;
   const int32_t *cu;
   const float *pack;   // per (chunk slot, head): the pre-pass's hand-over
   const float *init;   // [N, H, 128, 128] X before the first step, or NULL (zero)
   float *final_out;    // [N, H, 128, 128] X after the last step, or NULL
-  float *states;       // [slots, H, 128, 128]: X before the step of chunk c, at chunk c's slot
+  float *states;       // [slots, H, 128, 128]: X before the step of chunk c, at chunk c's slot (or NULL)
   const int32_t *slot; // NULL, or per document the index of its init / final_out state
+  int states_stride;   // 0 or 1: every chunk; S > 1: chunks c % S == 0 only, at ckpt_slot(cu_i, i, c, S)
+  int seg_span;        // chunks per run (0: whole documents)
+  int64_t units;       // number of units (runs), seg_span > 0
+  const float *seg_init;
+  float *seg_final;
+  int identity_init, homog;
 };
 hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st);
+// The runs' start states from their transfer maps M (identity-init, homog
+// runs) and offsets N (zero-init runs): in scan order X_0 = init (or zero),
+// seg_out[unit_g] = X_g, X_{g+1} = M_g X_g + N_g (gdn_scan.hip).
+hipError_t launch_scan_compose_d128(const ScanArgs &a, const float *M, const float *Nb, float *seg_out, bool reverse,
+                                    hipStream_t st);
+// The scan of a, in one chain per (document, head) when span == 0, else in
+// parallel runs of span chunks joined by their transfer maps: the maps, the
+// offsets, the composition, then every run from its start value (ws holds
+// 3 x units x H x 128 x 128 fp32).
+hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t units, float *ws, hipStream_t st);
 
 struct BwdArgs {
   FwdArgs f;

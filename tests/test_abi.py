@@ -344,3 +344,21 @@ def test_route1_workspace_and_validation(L):
     assert call(ws=None) == 5
     assert call(ws=ctypes.c_void_p(FAKE.value + 64)) == 5  # misaligned
     assert call(shp=odd) == 4
+
+
+def test_parallel_runs_in_workspace_size(L):
+    """Few long documents make the state scans run in parallel runs: their
+    buffers (transfer maps, offsets, start values: 3 x runs x H x 64 KiB) show
+    in the workspace size; many documents, or short ones, need none."""
+    def need(cu, H, bwd=0):
+        v = varlen(cu, [0] * (len(cu) - 1))
+        return L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(g.GDNShape(H, 128, 128, 4, g.BF16, 0,
+                                                                                          0.0)), bwd)
+    slot_bytes = 16 * (6 * 32 * 32 + (128 * 128 + 1024 + 2048 + 2048 + 64) + 128 * 128) * 4
+    # one document of 32768 tokens at 16 heads: 64 chains, 8 runs of 128 chunks, 9 run units
+    base = (32768 // 32 + 1) * slot_bytes
+    assert need([0, 32768], 16) == (base + 255) // 256 * 256 + 3 * 9 * 16 * 128 * 128 * 4 + 256
+    # four documents of 8192 at 16 heads fill the chip: no runs
+    assert need([0, 8192, 16384, 24576, 32768], 16) == (32768 // 32 + 4) * slot_bytes + 256
+    # one short document: runs would be under 32 chunks
+    assert need([0, 4096], 16) == (4096 // 32 + 1) * slot_bytes + 256

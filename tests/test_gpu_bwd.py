@@ -201,3 +201,54 @@ def test_bwd_l2norm_reusing_forward_chunk_matrices(g, dev):
     torch.cuda.synchronize()
     for k in GRADS:
         assert torch.equal(g1[k], g2[k]), k
+
+
+def test_long_document_parallel_runs_full_size(g, dev):
+    """One packed row of 32768 tokens holding a single document (prompt 8192),
+    16 heads, d = 128, bf16: the state scans run as parallel runs joined by
+    their transfer maps; forward and reverse mode against the oracle on every
+    head, with h0 and dh_final."""
+    import torch
+    inp = wl.gdn_inputs([32768], [8192], 16, 128, 128, 4, seed=17, with_h0=True, with_grads=True)
+    dhf = (np.random.default_rng(18).standard_normal((1, 16, 128, 128)) / 16).astype(np.float32)
+    vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+    args = fwd_args(inp, dev)
+    h0 = to_dev(inp.h0, dev)
+    o, on, hf, ck = g.gdn_dual_fwd(vl, *args, 4, h0=h0, want_ckpt=True)
+    gr = g.gdn_dual_bwd(vl, *args, 4, ck, to_dev(inp.do, dev, True), to_dev(inp.don, dev, True), h0=h0,
+                        dh_final=to_dev(dhf, dev))
+    torch.cuda.synchronize()
+    ro, ron, rhf = oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(), 4,
+                                       h0=inp.h0)
+    e = {"o": rel_rms(to_np(o), ro), "on": rel_rms(to_np(on), ron), "h_final": rel_rms(to_np(hf), rhf)}
+    print("long_doc fwd", e)
+    assert max(e.values()) <= TOL_BF16, e
+    check(inp, gr, ref_bwd(inp, dhf=dhf), TOL_BF16, "long_doc")
+
+
+def test_parallel_runs_ragged_documents(g, dev):
+    """Two documents of 8192 and 3010 tokens (prompts 256, 64) at 16 heads:
+    runs of 64 chunks, the shorter document with a partial last run; every
+    checkpoint is the clean state after 32c tokens of its document."""
+    import torch
+    inp = wl.gdn_inputs([8192, 3010], [256, 64], 16, 128, 128, 2, seed=19, with_h0=True, with_grads=True)
+    vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+    args = fwd_args(inp, dev)
+    h0 = to_dev(inp.h0, dev)
+    o, on, hf, ck = g.gdn_dual_fwd(vl, *args, 2, h0=h0, want_ckpt=True)
+    gr = g.gdn_dual_bwd(vl, *args, 2, ck, to_dev(inp.do, dev, True), to_dev(inp.don, dev, True), h0=h0)
+    torch.cuda.synchronize()
+    ro, ron, rhf = oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(), 2,
+                                       h0=inp.h0)
+    e = {"o": rel_rms(to_np(o), ro), "on": rel_rms(to_np(on), ron), "h_final": rel_rms(to_np(hf), rhf)}
+    assert max(e.values()) <= TOL_BF16, e
+    check(inp, gr, ref_bwd(inp), TOL_BF16, "runs_ragged")
+    # a few checkpoint slots across run boundaries of the second document
+    ck = to_np(ck)
+    cu = inp.cu_seqlens
+    for c in (0, 63, 64, 65, 94):
+        L = 32 * c
+        sl = slice(cu[1], cu[1] + L)
+        pre = [x[sl] for x in inp.clean_args() + inp.noisy_args()]
+        _, _, st = oracle.gdn_dual_fwd([0, L], [L], *pre, 2, h0=inp.h0[1:2])
+        assert rel_rms(ck[cu[1] // 32 + 1 + c], st[0]) <= 1e-4, c

@@ -127,3 +127,33 @@ def test_backward_tags_bit_exact(g, dev, B):
         ref = bf16_exact(want[name]) if name in IO_GRADS else want[name]
         np.testing.assert_array_equal(to_np(g1[name]), ref, err_msg=name)
         assert torch.equal(g1[name], g2[name]), name
+
+
+def test_tags_bit_exact_through_parallel_runs(g, dev):
+    """A document long enough, with few enough chains, that the state scans
+    run as parallel runs joined by their transfer maps (one 8192-token and one
+    3000-token document at 16 heads): forward and reverse mode still equal the
+    oracle bit for bit on the integer tags (the transfer maps and offsets of
+    the runs are then integer matrices too)."""
+    import torch
+    docs = [(8192, 100), (3000, 36)]
+    B = 4
+    inp = tag_inputs(B, seed=400, H=16, docs=docs, with_grads=True)
+    vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+    args = fwd_args(inp, dev)
+    h0 = to_dev(inp.h0, dev)
+    dhf = inp.extra["dhf"]
+    o, on, hf, ck = g.gdn_dual_fwd(vl, *args, B, h0=h0, scale=1.0, want_ckpt=True)
+    gr = g.gdn_dual_bwd(vl, *args, B, ck, to_dev(inp.do, dev, True), to_dev(inp.don, dev, True), h0=h0,
+                        dh_final=to_dev(dhf, dev), scale=1.0)
+    torch.cuda.synchronize()
+    ro, ron, rhf = oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(), B,
+                                       h0=inp.h0, scale=1.0)
+    np.testing.assert_array_equal(to_np(o), bf16_exact(ro))
+    np.testing.assert_array_equal(to_np(on), bf16_exact(ron))
+    np.testing.assert_array_equal(to_np(hf), rhf)
+    want = oracle.gdn_dual_bwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(), B,
+                               inp.do, inp.don, h0=inp.h0, dh_final=dhf, scale=1.0)
+    for name in GRADS:
+        ref = bf16_exact(want[name]) if name in IO_GRADS else want[name]
+        np.testing.assert_array_equal(to_np(gr[name]), ref, err_msg=name)
