@@ -1,7 +1,8 @@
 """Benchmark of the dual-stream Gated DeltaNet layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-components] [--only step|step_sweep|infer|serve|serve_sweep|conv|layer|routes|copy] [--json-out PATH]
+                    [--no-components] [--json-out PATH]
+                    [--only step|step_sweep|infer|serve|serve_sweep|conv|layer|routes|memory|copy]
 
 A step is one pass of the layer's hot path over one batch of the headline
 workload -- 4 documents x 8192 tokens (prompt 2048, response in blocks of
@@ -13,7 +14,9 @@ requests x 16 heads, four EVALs + one COMMIT), AR-Trust (verify + scatter, and
 the replay pair), the serving conv step; the packed ShortConv and its reverse
 mode (32768 tokens, 8 documents, 3x32x128 channels); the packed layer
 (unfused, fused, training); the masked route against chunk-then-refine at
-blocks of 4 to 32.  One JSON line is printed.
+blocks of 4 to 32; the training step's device memory with every chunk-start
+state kept, with stride-4 checkpoints, and with stride-4 checkpoints in windows
+of 32 chunks, against the chunk-then-refine forward.  One JSON line is printed.
 
 Method: "FLARE: Diffusion for Hybrid Language Model" (papernotes.org notes),
 Overall framework and Key designs items 2-4.
@@ -97,7 +100,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
-    p.add_argument("--only", choices=["step", "step_sweep", "infer", "serve", "serve_sweep", "conv", "layer", "routes", "copy"], default=None,
+    p.add_argument("--only", choices=["step", "step_sweep", "infer", "serve", "serve_sweep", "conv", "layer", "routes",
+                                      "memory", "copy"], default=None,
                    help="run one part only (copy: a plain 1 GiB device copy, the reference "
                         "transfer for HBM byte counters)")
     p.add_argument("--json-out", default=None)
@@ -211,6 +215,8 @@ def main():
         comps["serving_sweep"] = bench_serving_sweep(torch, g, dev, args)
     if not args.no_components and args.only in (None, "routes"):
         comps["routes"] = bench_routes(torch, g, wl, dev, timer, up, args)
+    if not args.no_components and args.only in (None, "memory"):
+        comps["memory"] = bench_memory(torch, g, wl, dev, timer, up, args)
     if comps:
         result["components"] = comps
 
@@ -836,6 +842,97 @@ def bench_routes(torch, g, wl, dev, timer, up, args):
         out["B%d" % B] = row
         del a10, o, on, fws, rws, ckpt
         torch.cuda.empty_cache()
+    return out
+
+
+def bench_memory(torch, g, wl, dev, timer, up, args):
+    """Device memory of one training step at the headline shape (4 x 8192,
+    prompt 2048, B = 4, H = 16, d = 128, bf16), over what the inputs, output
+    gradients, outputs and gradients already hold: the step's intermediates
+    (checkpoints, workspaces), as torch's peak allocation.  Modes: one pass
+    with every chunk-start state kept and the forward's workspace kept for the
+    backward (the timed step); stride-4 checkpoints in one pass (the backward
+    rebuilds the other states; the forward's workspace freed after it);
+    stride-4 checkpoints with both passes in windows of 32 chunks; and the
+    chunk-then-refine route's forward, which stores every block-boundary
+    state.  Each mode's step time alongside (buffers allocated outside the
+    timed region)."""
+    log("bench: training-step memory, one pass vs strided checkpoints and windows vs route I")
+    bf = torch.bfloat16
+    inp = wl.headline(with_grads=True, round_io=False)
+    B, H, d, T = inp.block_size, inp.H, 128, inp.T
+    vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+    a10 = [up(inp.q, True), up(inp.k, True), up(inp.v, True), up(inp.alpha), up(inp.beta),
+           up(inp.qn, True), up(inp.kn, True), up(inp.vn, True), up(inp.alpha_n), up(inp.beta_n)]
+    do, don = up(inp.do, True), up(inp.don, True)
+    del inp
+    o = torch.empty((T, H, d), dtype=bf, device=dev)
+    on = torch.empty_like(o)
+    grads = {"dq": torch.empty_like(o), "dk": torch.empty_like(o), "dv": torch.empty_like(o),
+             "dalpha": torch.empty_like(a10[3]), "dbeta": torch.empty_like(a10[3]),
+             "dqn": torch.empty_like(o), "dkn": torch.empty_like(o), "dvn": torch.empty_like(o),
+             "dalpha_n": torch.empty_like(a10[3]), "dbeta_n": torch.empty_like(a10[3]), "dh0": None}
+    u8 = lambda n: torch.empty((max(int(n), 256),), dtype=torch.uint8, device=dev)
+
+    def ckpt_buf(stride):
+        return torch.empty((g.ckpt_slots(vl, H, d, B, g.BF16, stride), H, d, d), dtype=torch.float32, device=dev)
+
+    def train(stride, window, keep_fws, bufs=None):
+        """One fwd + bwd; with bufs=None every intermediate is allocated here,
+        in the order a training framework holds them, and freed when dead."""
+        ck = bufs["ck"] if bufs else ckpt_buf(stride)
+        fws = bufs["fws"] if bufs else u8(g.workspace_bytes(vl, H, d, B, g.BF16, window=window))
+        g.gdn_dual_fwd(vl, *a10, B, out=(o, on), ckpt=ck, want_h_final=False, workspace=fws, ckpt_stride=stride,
+                       window=window)
+        if not keep_fws and not bufs:
+            del fws
+            fws = None
+        bws = bufs["bws"] if bufs else u8(g.workspace_bytes(vl, H, d, B, g.BF16, for_bwd=True, stride=stride,
+                                                            window=window))
+        g.gdn_dual_bwd(vl, *a10, B, ck, do, don, out=grads, workspace=bws, ckpt_stride=stride, window=window,
+                       fwd_workspace=fws if keep_fws else None)
+
+    modes = {"one_pass_all_states": (1, 0, True), "one_pass_stride4": (4, 0, False),
+             "window32_stride4": (4, 32, False)}
+    out = {"workload": "training step (dual forward + backward), 4 x 8192 tokens, prompt 2048, B=4, H=16, d=128, "
+                       "bf16; bytes above inputs, output gradients, outputs and gradients"}
+    n = max(args.steps // 2, 3)
+    for name, (stride, window, keep) in modes.items():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        train(stride, window, keep)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        bufs = {"ck": ckpt_buf(stride), "fws": u8(g.workspace_bytes(vl, H, d, B, g.BF16, window=window)),
+                "bws": u8(g.workspace_bytes(vl, H, d, B, g.BF16, for_bwd=True, stride=stride, window=window))}
+        for _ in range(max(args.warmup, 1)):
+            train(stride, window, keep, bufs)
+        torch.cuda.synchronize()
+        for _ in range(n):
+            timer.run("mem_" + name, lambda: train(stride, window, keep, bufs))
+        torch.cuda.synchronize()
+        out[name] = {"ckpt_stride": stride, "window_chunks": window, "peak_bytes": int(peak),
+                     "ckpt_bytes": int(bufs["ck"].numel() * 4), "fwd_workspace_bytes": int(bufs["fws"].numel()),
+                     "bwd_workspace_bytes": int(bufs["bws"].numel()), "ms": timer.avg_ms("mem_" + name)}
+        del bufs
+    # chunk-then-refine: its forward alone stores every block-boundary state
+    shp = g._shape(H, d, B, g.BF16)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    ck = ckpt_buf(1)
+    rws = u8(g.lib().flare_gdn_route1_workspace_size(vl.ref(), ctypes.byref(shp)))
+    g.gdn_dual_fwd_route1(vl, *a10, B, out=(o, on), ckpt=ck, workspace=rws, want_h_final=False)
+    torch.cuda.synchronize()
+    n_blocks = sum((8192 - 2048 + B - 1) // B for _ in range(4))
+    out["route1_forward"] = {"peak_bytes": int(torch.cuda.max_memory_allocated(dev) - base),
+                             "block_states_bytes": n_blocks * H * d * d * 4, "workspace_bytes": int(rws.numel()),
+                             "ckpt_bytes": int(ck.numel() * 4)}
+    del ck, rws
+    torch.cuda.empty_cache()
     return out
 
 

@@ -73,6 +73,8 @@ def lib():
     L.flare_last_error.restype = ctypes.c_char_p
     L.flare_gdn_dual_workspace_size.argtypes = [VP, SP, ctypes.c_int]
     L.flare_gdn_dual_workspace_size.restype = SZ
+    L.flare_gdn_dual_workspace_size_window.argtypes = [VP, SP, ctypes.c_int, I32, I32]
+    L.flare_gdn_dual_workspace_size_window.restype = SZ
     L.flare_gdn_dual_ckpt_size.argtypes = [VP, SP, I32]
     L.flare_gdn_dual_ckpt_size.restype = SZ
     L.flare_gdn_ckpt_slot.argtypes = [I32, I32, I32, I32]
@@ -361,13 +363,14 @@ def ckpt_slots(varlen: Varlen, H: int, d: int, B: int, io: int, stride: int = 1)
 
 def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,
                  h0=None, scale=0.0, flags=0, want_h_final=True, want_ckpt=False, out=None, ckpt=None,
-                 workspace=None):
+                 workspace=None, ckpt_stride=1, window=0):
     """Dual-stream forward.  q,k,qn,kn [T,H,d]; v,vn [T,H,d]; gates [T,H] fp32;
     h0 [N,H,d,d] fp32 or None.  `out` = (o, on) reuses output buffers, `ckpt`
-    a buffer for the chunk-start states (implies saving them), `workspace` a
-    uint8 device buffer of at least flare_gdn_dual_workspace_size(..., 0)
-    bytes (allocated here when needed and not given).  Returns
-    (o, on, h_final, ckpt)."""
+    a buffer for the chunk-start states (implies saving them) of every
+    `ckpt_stride`-th chunk, `workspace` a uint8 device buffer of at least
+    workspace_bytes(..., window=window) bytes (allocated here when needed and
+    not given); window > 0 runs the chunked path in windows of that many
+    chunks of every document.  Returns (o, on, h_final, ckpt)."""
     torch = _torch()
     T, H, d, iot, dev = _chk_gdn_inputs(varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0)
     io = _io_of(q)
@@ -382,22 +385,38 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
     hf = torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=q.device) if want_h_final else None
     ck = ckpt
     if ck is not None or want_ckpt:
-        nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1)
+        nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), int(ckpt_stride))
         if nbytes == 0:
             raise FlareError(2, "invalid arguments for the checkpoint size")
         if ck is None:
             ck = torch.empty((nbytes // (H * d * d * 4), H, d, d), dtype=torch.float32, device=q.device)
         _chk_buf(ck, "ckpt", nbytes, torch.float32, dev)
-    ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 0)
+    ws_bytes = _ws_bytes(varlen, shp, False, 1, window)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
     _chk_buf(workspace, "workspace", ws_bytes, torch.uint8, dev, optional=ws_bytes == 0)
+    # the library runs in windows when the workspace it is told of holds less
+    # than one pass: hand it exactly the size asked for
     _check(lib().flare_gdn_dual_fwd(varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(alpha), _ptr(beta), _ptr(qn), _ptr(kn), _ptr(vn),
                                     _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(o), _ptr(on),
-                                    _ptr(hf), _ptr(ck), 1, _ptr(workspace),
-                                    workspace.numel() if workspace is not None else 0, _stream(q.device)))
+                                    _ptr(hf), _ptr(ck), int(ckpt_stride), _ptr(workspace),
+                                    ws_bytes if workspace is not None else 0, _stream(q.device)))
     return o, on, hf, ck
+
+
+def _ws_bytes(varlen, shp, for_bwd, stride, window):
+    if window < 0:
+        _fail("window must be >= 0")
+    if stride == 1 and window == 0:
+        return int(lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 1 if for_bwd else 0))
+    n = int(lib().flare_gdn_dual_workspace_size_window(varlen.ref(), ctypes.byref(shp), 1 if for_bwd else 0,
+                                                        int(stride), int(window)))
+    if n == 0:
+        _fail("no %s workspace for checkpoint stride %d and window %d with this shape (windows need bf16 io at "
+              "d = 128 and, for the backward, a multiple of the stride)" % ("backward" if for_bwd else "forward",
+                                                                            stride, window))
+    return n
 
 
 def gdn_dual_fwd_route1(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size, h0=None,
@@ -470,12 +489,15 @@ def gdn_dual_fwd_pool(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n,
 
 def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, block_size,
                  ckpt, d_o, d_on, h0=None, dh_final=None, scale=0.0, flags=0, want_dh0=True,
-                 workspace=None, out=None, fwd_workspace=None):
+                 workspace=None, out=None, fwd_workspace=None, ckpt_stride=1, window=0):
     """Reverse mode.  Returns a dict of gradients (same names as the oracle);
     `out` = such a dict reuses its buffers, `workspace` a uint8 device buffer of
-    at least flare_gdn_dual_workspace_size() bytes, `fwd_workspace` the
-    workspace of the forward call that produced `ckpt` (its chunk matrices are
-    then reused)."""
+    at least workspace_bytes(..., for_bwd=True, stride=ckpt_stride,
+    window=window) bytes, `fwd_workspace` the workspace of the one-pass
+    forward call that produced `ckpt` (its chunk matrices are then reused).
+    `ckpt` holds every `ckpt_stride`-th chunk-start state; the others are
+    rebuilt.  window > 0 runs in windows of that many chunks of every document
+    (a multiple of ckpt_stride)."""
     torch = _torch()
     T, H, d, iot, dev = _chk_gdn_inputs(varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0)
     io = _io_of(q)
@@ -484,10 +506,13 @@ def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
     _chk(d_o, "d_o", (T, H, d), iot, dev)
     _chk(d_on, "d_on", (T, H, d), iot, dev)
     _chk(dh_final, "dh_final", (N, H, d, d), torch.float32, dev, optional=True)
-    _chk_buf(ckpt, "ckpt", lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), 1), torch.float32, dev)
+    ck_bytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), int(ckpt_stride))
+    if ck_bytes == 0:
+        _fail("invalid checkpoint stride %r" % (ckpt_stride,))
+    _chk_buf(ckpt, "ckpt", ck_bytes, torch.float32, dev)
     _chk_buf(fwd_workspace, "fwd_workspace", lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 0),
              torch.uint8, dev, optional=True)
-    ws_bytes = lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(shp), 1)
+    ws_bytes = _ws_bytes(varlen, shp, True, ckpt_stride, window)
     if workspace is None:
         workspace = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
     _chk_buf(workspace, "workspace", ws_bytes, torch.uint8, dev)
@@ -505,11 +530,11 @@ def gdn_dual_bwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
     _chk(g.get("dh0"), "dh0", (N, H, d, d), torch.float32, dev, optional=True)
     _check(lib().flare_gdn_dual_bwd(
         varlen.ref(), ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-        _ptr(qn), _ptr(kn), _ptr(vn), _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(ckpt), 1,
+        _ptr(qn), _ptr(kn), _ptr(vn), _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(ckpt), int(ckpt_stride),
         _ptr(fwd_workspace), _ptr(d_o), _ptr(d_on), _ptr(dh_final), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
         _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g["dqn"]), _ptr(g["dkn"]), _ptr(g["dvn"]),
         _ptr(g["dalpha_n"]), _ptr(g["dbeta_n"]), _ptr(g["dh0"]), _ptr(workspace),
-        workspace.numel(), _stream(dev)))
+        ws_bytes, _stream(dev)))
     return g
 
 
@@ -812,10 +837,11 @@ def noalloc_scratch_bytes() -> int:
 
 
 def workspace_bytes(varlen: Varlen, H: int, d: int, block_size: int, io: int, flags: int = 0,
-                    for_bwd: bool = False) -> int:
-    """flare_gdn_dual_workspace_size for this batch and shape."""
-    return int(lib().flare_gdn_dual_workspace_size(varlen.ref(), ctypes.byref(_shape(H, d, block_size, io, flags)),
-                                                   1 if for_bwd else 0))
+                    for_bwd: bool = False, stride: int = 1, window: int = 0) -> int:
+    """flare_gdn_dual_workspace_size for this batch and shape (one pass,
+    stride-1 checkpoints), or flare_gdn_dual_workspace_size_window for a
+    checkpoint stride and a window of chunks."""
+    return _ws_bytes(varlen, _shape(H, d, block_size, io, flags), for_bwd, stride, window)
 
 
 def timing_enable(on: bool = True) -> bool:

@@ -38,10 +38,26 @@ size_t flare_gdn_dual_workspace_size(const flare_varlen *varlen, const flare_gdn
   return for_bwd ? bwd_workspace_bytes(vi, shape) : fwd_workspace_bytes(vi, shape);
 }
 
+size_t flare_gdn_dual_workspace_size_window(const flare_varlen *varlen, const flare_gdn_shape *shape, int for_bwd,
+                                            int32_t ckpt_stride_chunks, int32_t window_chunks) {
+  VarlenInfo vi;
+  if (check_fwd_common(varlen, shape, &vi) != FLARE_OK) return 0;
+  if (ckpt_stride_chunks < 1 || window_chunks < 0) return 0;
+  if (for_bwd) {
+    if (!bwd_uses_scan_pack(shape)) {
+      return ckpt_stride_chunks == 1 && window_chunks == 0 ? bwd_workspace_bytes(vi, shape) : 0;
+    }
+    if (window_chunks % ckpt_stride_chunks != 0) return 0;
+    return bwd_layout(vi, shape, window_chunks, ckpt_stride_chunks).total;
+  }
+  if (!fwd_uses_chunk_matrices(shape)) return 0;
+  return fwd_layout(vi, shape, window_chunks).total;
+}
+
 size_t flare_gdn_dual_ckpt_size(const flare_varlen *varlen, const flare_gdn_shape *shape,
                                 int32_t ckpt_stride_chunks) {
   VarlenInfo vi;
-  if (ckpt_stride_chunks != 1) return 0;
+  if (ckpt_stride_chunks < 1) return 0;
   if (check_fwd_common(varlen, shape, &vi) != FLARE_OK) return 0;
   return (size_t)ckpt_num_slots(vi, ckpt_stride_chunks) * shape->num_heads * shape->d_k *
          shape->d_v * sizeof(float);
@@ -85,26 +101,49 @@ static flare_status fwd_impl(const flare_varlen *varlen, const flare_gdn_shape *
   VarlenInfo vi;
   flare_status st = check_fwd_common(varlen, shape, &vi);
   if (st != FLARE_OK) return st;
-  if (ckpt && ckpt_stride_chunks != 1)
-    return fail(FLARE_ERR_UNSUPPORTED, "checkpoint stride %d (only 1 is built)", ckpt_stride_chunks);
+  if (ckpt && ckpt_stride_chunks < 1)
+    return fail(FLARE_ERR_SHAPE, "checkpoint stride %d (at least 1)", ckpt_stride_chunks);
   if (vi.total_tokens > 0 &&
       (!q || !k || !v || !alpha || !beta || !qn || !kn || !vn || !alpha_n || !beta_n || !o || !on))
     return fail(FLARE_ERR_NULL, "gdn_dual_fwd: a required pointer is NULL");
-  const size_t need = fwd_workspace_bytes(vi, shape);
-  if (vi.total_tokens > 0 && need > 0 && (!workspace || workspace_bytes < need))
-    return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (((uintptr_t)workspace & 255u) != 0)
     return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   FwdArgs a = fwd_args(varlen, shape, vi, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0, o, on, h_final,
                        ckpt, ckpt_stride_chunks);
   a.state_slot = state_slot;
-  a.workspace = need > 0 ? reinterpret_cast<float *>(workspace) : nullptr;
-  if (need > 0) {  // the state scan in parallel runs for long documents
+  if (!fwd_uses_chunk_matrices(shape)) {  // the per-(document, head) kernel
+    a.workspace = nullptr;
+    return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd launch");
+  }
+  // the chunked passes (also for a batch of empty documents: h_final = h0
+  // through the scan): in one pass when the workspace holds every chunk's
+  // buffers, else in windows of as many chunks as it holds
+  const int win = workspace ? pick_window(vi, shape, false, 1, 1, workspace_bytes) : -1;
+  if (win < 0)
+    return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes: %zu needed (%zu for windows of one chunk)",
+                workspace_bytes, fwd_layout(vi, shape, 0).total, fwd_layout(vi, shape, 1).total);
+  if (win > 0 && state_slot)
+    return fail(FLARE_ERR_WORKSPACE, "the pool forward runs in one pass: workspace of %zu bytes, %zu needed",
+                workspace_bytes, fwd_layout(vi, shape, 0).total);
+  const ChunkLayout L = fwd_layout(vi, shape, win);
+  char *const w = reinterpret_cast<char *>(workspace);
+  a.workspace = reinterpret_cast<float *>(workspace);
+  FwdPlan p{};
+  p.win = win;
+  p.max_chunks = max_chunks(vi);
+  p.slots = L.slots;
+  p.cmat = reinterpret_cast<float *>(w + L.cmat);
+  p.pack = reinterpret_cast<float *>(w + L.pack);
+  // one pass with stride-1 checkpoints: the checkpoints are the states
+  p.states = (win == 0 && ckpt && ckpt_stride_chunks == 1) ? nullptr : reinterpret_cast<float *>(w + L.states);
+  p.l2f = reinterpret_cast<float4 *>(w + L.l2f);
+  p.carry = win > 0 ? reinterpret_cast<float *>(w + L.carry) : nullptr;
+  if (win == 0) {  // the state scan in parallel runs for long documents
     a.scan_span = scan_seg_span(vi, shape->num_heads);
     a.scan_units = a.scan_span > 0 ? ckpt_num_slots(vi, a.scan_span) : 0;
-    a.scan_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + fwd_seg_offset(vi, shape));
+    a.scan_ws = reinterpret_cast<float *>(w + L.seg);
   }
-  return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd launch");
+  return hip_status(launch_gdn_fwd(a, (hipStream_t)stream, &p), "gdn_dual_fwd launch");
 }
 
 flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shape *shape,
@@ -213,8 +252,11 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
   VarlenInfo vi;
   flare_status st = check_fwd_common(varlen, shape, &vi);
   if (st != FLARE_OK) return st;
-  if (ckpt_stride_chunks != 1)
-    return fail(FLARE_ERR_UNSUPPORTED, "checkpoint stride %d (only 1 is built)", ckpt_stride_chunks);
+  if (ckpt_stride_chunks < 1)
+    return fail(FLARE_ERR_SHAPE, "checkpoint stride %d (at least 1)", ckpt_stride_chunks);
+  if (ckpt_stride_chunks > 1 && !bwd_uses_scan_pack(shape))
+    return fail(FLARE_ERR_UNSUPPORTED, "checkpoint stride %d: the rebuild is built for bf16 io at d = 128",
+                ckpt_stride_chunks);
   if ((shape->flags & FLARE_QK_L2NORM) && !bwd_uses_scan_pack(shape))
     return fail(FLARE_ERR_UNSUPPORTED,
                 "the backward takes the q/k L2 flag for bf16 io at d = 128 only (normalise q, k beforehand)");
@@ -223,9 +265,22 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
        !d_o || !d_on || !dq || !dk || !dv || !dalpha || !dbeta || !dqn || !dkn || !dvn ||
        !dalpha_n || !dbeta_n))
     return fail(FLARE_ERR_NULL, "gdn_dual_bwd: a required pointer is NULL");
-  const size_t need = bwd_workspace_bytes(vi, shape);
-  if (vi.total_tokens > 0 && (!workspace || workspace_bytes < need))
-    return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const bool chunked = bwd_uses_scan_pack(shape);
+  // the chunked path runs in one pass when the workspace holds every chunk's
+  // buffers, else in windows of a multiple of the stride
+  int win = 0;
+  if (vi.total_tokens > 0 || chunked) {  // the chunked path scans empty documents too (dh0 = dh_final)
+    win = workspace ? (chunked ? pick_window(vi, shape, true, ckpt_stride_chunks, ckpt_stride_chunks, workspace_bytes)
+                               : (workspace_bytes >= bwd_workspace_bytes(vi, shape) ? 0 : -1))
+                    : -1;
+    if (win < 0)
+      return fail(FLARE_ERR_WORKSPACE, "workspace of %zu bytes: %zu needed (%zu for windows of %d chunks)",
+                  workspace_bytes, chunked ? bwd_layout(vi, shape, 0, ckpt_stride_chunks).total
+                                           : bwd_workspace_bytes(vi, shape),
+                  chunked ? bwd_layout(vi, shape, ckpt_stride_chunks, ckpt_stride_chunks).total
+                          : bwd_workspace_bytes(vi, shape),
+                  ckpt_stride_chunks);
+  }
   if (((uintptr_t)workspace & 255u) != 0)
     return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   BwdArgs a{};
@@ -253,12 +308,28 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   a.T = vi.total_tokens;
-  if (bwd_uses_scan_pack(shape)) {  // the reverse scan in parallel runs for long documents
+  if (!chunked) return hip_status(launch_gdn_bwd(a, (hipStream_t)stream), "gdn_dual_bwd launch");
+  const ChunkLayout L = bwd_layout(vi, shape, win, ckpt_stride_chunks);
+  char *const w = reinterpret_cast<char *>(workspace);
+  BwdPlan p{};
+  p.win = win;
+  p.max_chunks = max_chunks(vi);
+  p.stride = ckpt_stride_chunks;
+  p.slots = L.slots;
+  p.rebuild_span = rebuild_span(ckpt_stride_chunks, win);
+  p.rebuild_units = ckpt_num_slots(vi, p.rebuild_span);
+  p.adj = reinterpret_cast<float *>(w + L.adj);
+  p.tri = reinterpret_cast<float *>(w + L.cmat);
+  p.pack = reinterpret_cast<float *>(w + L.pack);
+  p.states = L.states_bytes ? reinterpret_cast<float *>(w + L.states) : nullptr;
+  p.l2f = reinterpret_cast<float4 *>(w + L.l2f);
+  p.carry = win > 0 ? reinterpret_cast<float *>(w + L.carry) : nullptr;
+  if (win == 0) {  // the reverse scan in parallel runs for long documents
     a.f.scan_span = scan_seg_span(vi, shape->num_heads);
     a.f.scan_units = a.f.scan_span > 0 ? ckpt_num_slots(vi, a.f.scan_span) : 0;
-    a.f.scan_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + bwd_seg_offset(vi, shape));
+    a.f.scan_ws = reinterpret_cast<float *>(w + L.seg);
   }
-  return hip_status(launch_gdn_bwd(a, (hipStream_t)stream), "gdn_dual_bwd launch");
+  return hip_status(launch_gdn_bwd(a, (hipStream_t)stream, &p), "gdn_dual_bwd launch");
 }
 
 // The serving step's argument block for num_req requests of shape's blocks.

@@ -275,6 +275,11 @@ __device__ __forceinline__ void chunk_grams(IO (*x)[32][LDX], float (*cc)[32][LD
 // Chunk slot -> (document, chunk index); returns false for a slot past the end
 // of its document.  Slots of document i start at floor(cu_i / 32) + i.
 __device__ __forceinline__ bool slot_to_chunk(const FwdArgs &f, int slot, int &doc, int &c) {
+  if (f.win_len > 0) {  // chunk windows: slot = doc * win_len + (c - win_lo)
+    doc = slot / f.win_len;
+    c = f.win_lo + slot % f.win_len;
+    return doc < f.num_docs && c * 32 < f.cu[doc + 1] - f.cu[doc];
+  }
   int lo = 0, hi = f.num_docs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;

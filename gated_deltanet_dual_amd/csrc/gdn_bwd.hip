@@ -853,6 +853,109 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_kernel(BwdArgs a) {
   }
 }
 
+// The chunked backward (bf16 io, d = 128), per pass (the whole batch, or one
+// window of chunks of every document, last window first): the chunk matrices
+// (or the forward's), the chunk-start states rebuilt from strided checkpoints
+// when only every stride-th one was kept (the forward's hand-over, then runs
+// of a multiple of the stride from checkpoints, all in parallel), the reverse scan's
+// hand-over, the reverse scan (carried between windows), the per-chunk pass.
+static hipError_t launch_bwd_chunked(const BwdArgs &a_in, hipStream_t st, const BwdPlan *plan) {
+  BwdArgs a = a_in;
+  constexpr int C = kChunk, D = 128;
+  BwdPlan p{};
+  if (plan) {
+    p = *plan;
+  } else {  // one pass over the workspace in its one-pass layout, stride-1 checkpoints
+    p.slots = a.T / C + a.f.num_docs;
+    const size_t per = (size_t)p.slots * a.f.H;
+    p.adj = reinterpret_cast<float *>(a.workspace);
+    p.tri = p.adj + per * D * D;
+    p.pack = p.tri + per * 6 * C * C;
+    const size_t per_bytes = per * ((size_t)D * D + 6 * C * C + kScanPackFloats) * 4;
+    p.l2f = reinterpret_cast<float4 *>(reinterpret_cast<char *>(a.workspace) + ((per_bytes + 255) & ~(size_t)255));
+    p.stride = 1;
+  }
+  if (a.f.flags & 1) {  // the q/k L2 flag: per-row factors (gdn_l2.hip)
+    hipError_t e0 = launch_l2_factors(a.f, p.l2f, st);
+    if (e0 != hipSuccess) return e0;
+    a.f.l2f = p.l2f;
+  }
+  const int nwin = p.win > 0 ? max(1, (p.max_chunks + p.win - 1) / p.win) : 1;
+  for (int j = 0; j < nwin; ++j) {
+    const int w = nwin - 1 - j;
+    BwdArgs aw = a;
+    aw.f.win_lo = p.win > 0 ? w * p.win : 0;
+    aw.f.win_len = p.win;
+    aw.workspace = p.adj;
+    aw.tri = p.tri;
+    aw.pack = p.pack;
+    if (a.fwd_cm && p.win == 0) {
+      aw.tri = const_cast<float *>(a.fwd_cm);  // read only from here on
+    } else {
+      TimedLaunch tl(K_TRI, st);
+      hipError_t e0 = launch_tri_d128(aw, st, p.slots);
+      if (e0 != hipSuccess) return e0;
+    }
+    if (p.stride > 1) {
+      {
+        TimedLaunch tl(K_FWD_PRE, st);
+        hipError_t e0 = launch_fwd_pre_d128(aw.f, aw.tri, p.pack, st, p.slots);
+        if (e0 != hipSuccess) return e0;
+      }
+      ScanArgs rb{};
+      rb.num_docs = a.f.num_docs;
+      rb.H = a.f.H;
+      rb.cu = a.f.cu;
+      rb.pack = p.pack;
+      rb.states = p.states;
+      rb.seg_span = p.rebuild_span;
+      rb.seg_init = a.ckpt_in;
+      rb.seg_init_stride = p.stride;
+      rb.seg_init_all = 1;
+      rb.win_lo = aw.f.win_lo;
+      rb.win_len = p.win;
+      rb.units = p.win > 0 ? (int64_t)a.f.num_docs * (p.win / p.rebuild_span) : p.rebuild_units;
+      TimedLaunch tl(K_FWD_SCAN, st);
+      hipError_t e0 = launch_scan_d128(rb, false, st);
+      if (e0 != hipSuccess) return e0;
+      aw.ckpt_in = p.states;
+      aw.ckpt_global = 0;
+    } else {
+      aw.ckpt_global = p.win > 0;
+    }
+    {
+      TimedLaunch tl(K_BWD_PRE, st);
+      hipError_t e0 = launch_bwd_pre_d128(aw, st, p.slots);
+      if (e0 != hipSuccess) return e0;
+    }
+    {
+      ScanArgs sa{};
+      sa.num_docs = a.f.num_docs;
+      sa.H = a.f.H;
+      sa.cu = a.f.cu;
+      sa.pack = p.pack;
+      sa.init = j == 0 ? a.dh_final : p.carry;
+      sa.final_out = j == nwin - 1 ? a.dh0 : p.carry;
+      sa.states = p.adj;
+      TimedLaunch tl(K_BWD_SCAN, st);
+      hipError_t e1;
+      if (p.win > 0) {
+        sa.win_lo = aw.f.win_lo;
+        sa.win_len = p.win;
+        sa.units = a.f.num_docs;
+        e1 = launch_scan_d128(sa, true, st);
+      } else {
+        e1 = scan_d128_runs(sa, true, a.f.scan_span, a.f.scan_units, a.f.scan_ws, st);
+      }
+      if (e1 != hipSuccess) return e1;
+    }
+    TimedLaunch tl(K_BWD_CHUNK, st);
+    hipError_t e2 = launch_bwd_chunk_d128(aw, st, p.slots);
+    if (e2 != hipSuccess) return e2;
+  }
+  return hipSuccess;
+}
+
 template <typename IO, int D>
 static hipError_t launch_bwd_t(const BwdArgs &a_in, hipStream_t st) {
   using Cfg = BwdCfg<IO, D>;
@@ -862,60 +965,23 @@ static hipError_t launch_bwd_t(const BwdArgs &a_in, hipStream_t st) {
   const int groups = (pairs + 7) / 8;
   const int64_t slots = a.T / Cfg::C + f.num_docs;
   a.tri = reinterpret_cast<float *>(a.workspace) + (size_t)slots * f.H * D * D;
-  if constexpr (std::is_same<IO, u16>::value && D == 128) {
-    a.pack = a.tri + (size_t)slots * f.H * 6 * Cfg::C * Cfg::C;
-    if (f.flags & 1) {
-      // the q/k L2 flag: per-row factors after the hand-over (gdn_l2.hip)
-      const size_t per_bytes = (size_t)slots * f.H * ((size_t)D * D + 6 * Cfg::C * Cfg::C + kScanPackFloats) * 4;
-      float4 *l2f = reinterpret_cast<float4 *>(reinterpret_cast<char *>(a.workspace) + ((per_bytes + 255) & ~(size_t)255));
-      hipError_t e0 = launch_l2_factors(a.f, l2f, st);
-      if (e0 != hipSuccess) return e0;
-      a.f.l2f = l2f;
-    }
-    if (a.fwd_cm) {
-      a.tri = const_cast<float *>(a.fwd_cm);  // read only from here on
-    } else if (slots > 0) {
-      TimedLaunch tl(K_TRI, st);
-      hipError_t e0 = launch_tri_d128(a, st, slots);
-      if (e0 != hipSuccess) return e0;
-    }
-    if (slots > 0) {
-      TimedLaunch tl(K_BWD_PRE, st);
-      hipError_t e0 = launch_bwd_pre_d128(a, st, slots);
-      if (e0 != hipSuccess) return e0;
-    }
-  }
   {
     TimedLaunch tl(K_BWD_SCAN, st);
-    if constexpr (std::is_same<IO, u16>::value && D == 128) {
-      ScanArgs sa{};
-      sa.num_docs = f.num_docs;
-      sa.H = f.H;
-      sa.cu = f.cu;
-      sa.pack = a.pack;
-      sa.init = a.dh_final;
-      sa.final_out = a.dh0;
-      sa.states = reinterpret_cast<float *>(a.workspace);
-      hipError_t e1 = scan_d128_runs(sa, true, f.scan_span, f.scan_units, f.scan_ws, st);
-      if (e1 != hipSuccess) return e1;
-    } else {
-      hipLaunchKernelGGL((gdn_bwd_scan_kernel<IO, D>), dim3((unsigned)(groups * 8 * Cfg::NTILE)), dim3(256), 0,
-                         st, a);
-    }
+    hipLaunchKernelGGL((gdn_bwd_scan_kernel<IO, D>), dim3((unsigned)(groups * 8 * Cfg::NTILE)), dim3(256), 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (slots > 0) {
     TimedLaunch tl(K_BWD_CHUNK, st);
-    if constexpr (std::is_same<IO, u16>::value && D == 128) return launch_bwd_chunk_d128(a, st, slots);
     hipLaunchKernelGGL((gdn_bwd_chunk_kernel<IO, D>), dim3((unsigned)(slots * f.H)), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st) {
+hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st, const BwdPlan *plan) {
   if (a.f.num_docs == 0) return hipSuccess;
-  if (a.f.bf16) return a.f.D == 128 ? launch_bwd_t<u16, 128>(a, st) : launch_bwd_t<u16, 16>(a, st);
+  if (a.f.bf16 && a.f.D == 128) return launch_bwd_chunked(a, st, plan);
+  if (a.f.bf16) return launch_bwd_t<u16, 16>(a, st);
   return a.f.D == 16 ? launch_bwd_t<float, 16>(a, st) : hipErrorInvalidValue;
 }
 

@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   const int c0 = c * C;
   const bool has_noisy = (c0 + C > P) && (P < n);
   const float s = f.scale;
-  const float *Sc = a.ckpt_in + ((int64_t)slot * H + h) * (size_t)D * D;
+  const int64_t sslot = a.ckpt_global ? (int64_t)(f.cu[doc] / C) + doc + c : slot;
+  const float *Sc = a.ckpt_in + (sslot * H + h) * (size_t)D * D;
   const float *dSn = reinterpret_cast<const float *>(a.workspace) + ((int64_t)slot * H + h) * (size_t)D * D;
   const u16 *const pq = reinterpret_cast<const u16 *>(f.q), *const pk = reinterpret_cast<const u16 *>(f.k);
   const u16 *const pqn = reinterpret_cast<const u16 *>(f.qn), *const pkn = reinterpret_cast<const u16 *>(f.kn);

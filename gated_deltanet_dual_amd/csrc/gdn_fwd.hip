@@ -715,57 +715,85 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gdn_fwd(const FwdArgs &a_in, hipStream_t st) {
+hipError_t launch_gdn_fwd(const FwdArgs &a_in, hipStream_t st, const FwdPlan *plan) {
   if (a_in.num_docs == 0) return hipSuccess;
   FwdArgs a = a_in;
   if (a.workspace) {
-    // bf16, d = 128: chunk matrices and the scan hand-over in parallel, the
-    // state recurrence (chunk-start states -> ckpt, or the workspace when no
-    // checkpoints are asked for), then the outputs in parallel; with the q/k
-    // L2 flag first the per-row factors the kernels fold in (gdn_l2.hip)
-    const int64_t slots = a.T / kChunk + a.num_docs;
-    if (a.flags & 1) {
-      const size_t per_bytes = (size_t)slots * a.H * (6 * kChunk * kChunk + kScanPackFloats + (size_t)a.D * a.D) * 4;
-      float4 *l2f = reinterpret_cast<float4 *>(reinterpret_cast<char *>(a.workspace) + ((per_bytes + 255) & ~(size_t)255));
-      hipError_t e = launch_l2_factors(a, l2f, st);
-      if (e != hipSuccess) return e;
-      a.l2f = l2f;
+    // bf16, d = 128: per pass (the whole batch, or one window of chunks of
+    // every document) the chunk matrices and the scan hand-over in parallel,
+    // the state recurrence (chunk-start states -> the checkpoints or the
+    // workspace; strided checkpoints besides), then the outputs in parallel;
+    // with the q/k L2 flag first the per-row factors the kernels fold in
+    // (gdn_l2.hip)
+    FwdPlan p{};
+    if (plan) {
+      p = *plan;
+    } else {  // one pass over the workspace in its one-pass layout
+      p.slots = a.T / kChunk + a.num_docs;
+      const size_t per = (size_t)p.slots * a.H;
+      p.cmat = a.workspace;
+      p.pack = p.cmat + per * 6 * kChunk * kChunk;
+      p.states = a.ckpt && a.ckpt_stride == 1 ? nullptr : p.pack + per * kScanPackFloats;
+      const size_t per_bytes = per * (6 * kChunk * kChunk + kScanPackFloats + (size_t)a.D * a.D) * 4;
+      p.l2f = reinterpret_cast<float4 *>(reinterpret_cast<char *>(a.workspace) + ((per_bytes + 255) & ~(size_t)255));
     }
-    const size_t per = (size_t)slots * a.H;
-    float *const cmat = a.workspace;
-    float *const pack = cmat + per * 6 * kChunk * kChunk;
-    float *const states = a.ckpt ? a.ckpt : pack + per * kScanPackFloats;
-    if (slots > 0) {
-      BwdArgs b{};
-      b.f = a;
-      b.T = a.T;
-      b.tri = cmat;
+    if (a.flags & 1) {
+      hipError_t e = launch_l2_factors(a, p.l2f, st);
+      if (e != hipSuccess) return e;
+      a.l2f = p.l2f;
+    }
+    float *const states = p.states ? p.states : a.ckpt;
+    const bool ckpt_apart = a.ckpt && states != a.ckpt;  // checkpoints written besides the states
+    const int nwin = p.win > 0 ? max(1, (p.max_chunks + p.win - 1) / p.win) : 1;
+    for (int w = 0; w < nwin; ++w) {
+      FwdArgs aw = a;
+      aw.win_lo = p.win > 0 ? w * p.win : 0;
+      aw.win_len = p.win;
       {
+        BwdArgs b{};
+        b.f = aw;
+        b.T = aw.T;
+        b.tri = p.cmat;
         TimedLaunch tl(K_TRI, st);
-        hipError_t e = launch_tri_d128(b, st, slots);
+        hipError_t e = launch_tri_d128(b, st, p.slots);
         if (e != hipSuccess) return e;
       }
-      TimedLaunch tl(K_FWD_PRE, st);
-      hipError_t e = launch_fwd_pre_d128(a, cmat, pack, st, slots);
+      {
+        TimedLaunch tl(K_FWD_PRE, st);
+        hipError_t e = launch_fwd_pre_d128(aw, p.cmat, p.pack, st, p.slots);
+        if (e != hipSuccess) return e;
+      }
+      {
+        ScanArgs sa{};
+        sa.num_docs = a.num_docs;
+        sa.H = a.H;
+        sa.cu = a.cu;
+        sa.pack = p.pack;
+        sa.init = w == 0 ? a.h0 : p.carry;
+        sa.final_out = w == nwin - 1 ? a.h_final : p.carry;
+        sa.slot = a.state_slot;
+        sa.states = states;
+        if (ckpt_apart) {
+          sa.ckpt = a.ckpt;
+          sa.ckpt_stride = a.ckpt_stride;
+        }
+        TimedLaunch tl(K_FWD_SCAN, st);
+        hipError_t e;
+        if (p.win > 0) {
+          sa.win_lo = aw.win_lo;
+          sa.win_len = p.win;
+          sa.units = a.num_docs;
+          e = launch_scan_d128(sa, false, st);
+        } else {
+          e = scan_d128_runs(sa, false, a.scan_span, a.scan_units, a.scan_ws, st);
+        }
+        if (e != hipSuccess) return e;
+      }
+      TimedLaunch tl(K_FWD, st);
+      hipError_t e = launch_fwd_out_d128(aw, p.cmat, states, st, p.slots);
       if (e != hipSuccess) return e;
     }
-    {
-      ScanArgs sa{};
-      sa.num_docs = a.num_docs;
-      sa.H = a.H;
-      sa.cu = a.cu;
-      sa.pack = pack;
-      sa.init = a.h0;
-      sa.final_out = a.h_final;
-      sa.slot = a.state_slot;
-      sa.states = states;
-      TimedLaunch tl(K_FWD_SCAN, st);
-      hipError_t e = scan_d128_runs(sa, false, a.scan_span, a.scan_units, a.scan_ws, st);
-      if (e != hipSuccess) return e;
-    }
-    if (slots == 0) return hipSuccess;
-    TimedLaunch tl(K_FWD, st);
-    return launch_fwd_out_d128(a, cmat, states, st, slots);
+    return hipSuccess;
   }
   // fp32 io is instantiated at d = 16 only (the fp32 tiles at d = 128 exceed the LDS budget)
   if (a.bf16) return a.D == 128 ? launch_fwd_t<u16, 128>(a, st) : launch_fwd_t<u16, 16>(a, st);

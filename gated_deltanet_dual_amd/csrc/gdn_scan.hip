@@ -33,6 +33,12 @@
 // offset (the run scanned from zero).  The runs' start values then follow
 // from one short sequential pass over the runs (gdn_scan_compose_kernel), and
 // a last parallel scan of every run from its start value writes the states.
+//
+// Chunk windows bound the memory of the per-chunk buffers: a launch then
+// covers one window of chunks of every document, its chain carried from the
+// previous window's launch through init / final_out.  Inside a window, runs
+// that start at strided checkpoints rebuild every chunk-start state in
+// parallel (the backward's rebuild when only every s-th state was kept).
 #include "bwd_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -82,13 +88,20 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   const int grp = L / (8 * sNQ), rem = L % (8 * sNQ);
   const int quarter = rem / 8;
   const int64_t pair = (int64_t)grp * 8 + (rem % 8);
-  const int64_t npairs = (a.seg_span > 0 ? a.units : a.num_docs) * a.H;
+  const bool win = a.win_len > 0;
+  const int64_t npairs = (a.seg_span > 0 || win ? a.units : a.num_docs) * a.H;
   if (pair >= npairs) return;
   const int64_t unit = pair / a.H;
   const int h = (int)(pair % a.H);
   const int H = a.H;
   int doc = (int)unit, seg = 0;
-  if (a.seg_span > 0) {  // unit -> (document, run): the checkpoint-slot numbering of stride seg_span
+  if (win) {  // unit -> (document, run inside the window)
+    if (a.seg_span > 0) {
+      const int per = a.win_len / a.seg_span;
+      doc = (int)(unit / per);
+      seg = (int)(unit % per);
+    }
+  } else if (a.seg_span > 0) {  // unit -> (document, run): the checkpoint-slot numbering of stride seg_span
     const int64_t span = (int64_t)C * a.seg_span;
     int lo = 0, hi = a.num_docs - 1;
     while (lo < hi) {
@@ -101,14 +114,33 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   const int64_t t0g = a.cu[doc];
   const int n = a.cu[doc + 1] - a.cu[doc];
   const int nchunks_doc = (n + C - 1) / C;
-  // this run's chunks [c_lo, c_hi); an empty document is one empty run (its init passes through)
-  const int c_lo = a.seg_span > 0 ? seg * a.seg_span : 0;
-  const int c_hi = a.seg_span > 0 ? min(c_lo + a.seg_span, nchunks_doc) : nchunks_doc;
-  if (c_lo > 0 && c_lo >= nchunks_doc) return;  // a unit no run maps to
-  const int nchunks = c_hi - c_lo;
-  const bool first_run = REVERSE ? c_hi == nchunks_doc : c_lo == 0;
-  const bool last_run = REVERSE ? c_lo == 0 : c_hi == nchunks_doc;
+  // this chain's chunks [c_lo, c_hi); an empty document (or, in a window, a
+  // document with no chunk there) is one empty chain: its init passes through
+  const int c_base = (win ? a.win_lo : 0) + (a.seg_span > 0 ? seg * a.seg_span : 0);
+  const int c_len = a.seg_span > 0 ? a.seg_span : win ? a.win_len : nchunks_doc;
+  const int c_lo = c_base;
+  const int c_hi = min(c_base + c_len, nchunks_doc);
+  if (a.seg_span > 0 && c_lo > 0 && c_lo >= nchunks_doc) return;  // a unit no run maps to
+  const int nchunks = max(c_hi - c_lo, 0);
+  // where the chain starts (init, or seg_init of its unit) and whether it
+  // ends in final_out: whole chains and window chains take both; runs of a
+  // document take init only for its first run in scan order and write
+  // final_out only from its last; runs inside a window start from seg_init
+  bool use_init, write_final;
+  if (win) {
+    use_init = write_final = a.seg_span == 0;
+  } else {
+    use_init = !a.seg_init_all && (REVERSE ? c_hi == nchunks_doc : c_lo == 0);
+    write_final = REVERSE ? c_lo == 0 : c_hi == nchunks_doc;
+  }
+  // seg_init / seg_final index: the unit, or in a window the run's checkpoint slot
+  const int64_t ck_unit = win && a.seg_span > 0 ? t0g / ((int64_t)C * a.seg_span) + doc + c_lo / a.seg_span : unit;
+  const int64_t ck_init = a.seg_init_stride > 0
+                              ? t0g / ((int64_t)C * a.seg_init_stride) + doc + c_lo / a.seg_init_stride
+                              : ck_unit;
   const int64_t ck_base = (int64_t)(t0g / C) + doc;
+  // the slot of chunk c in pack and states
+  auto wslot = [&](int c) -> int64_t { return win ? (int64_t)doc * a.win_len + (c - a.win_lo) : ck_base + c; };
   const int sstride = a.states_stride > 1 ? a.states_stride : 1;
   // step i handles chunk at(i)
   auto at = [&](int i) { return REVERSE ? c_hi - 1 - i : c_lo + i; };
@@ -122,16 +154,23 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     for (int i = 0; i < nchunks; ++i) {
       const int c = at(i);
       lds_barrier();
-      if (!a.states || c % sstride != 0) continue;
-      const int64_t sslot = sstride == 1 ? ck_base + c : t0g / ((int64_t)C * sstride) + doc + c / sstride;
-      float *dst = a.states + (sslot * H + h) * (size_t)D * D;
+      float *dst = nullptr, *dck = nullptr;
+      if (a.states && c % sstride == 0) {
+        const int64_t sslot = sstride == 1 ? wslot(c) : t0g / ((int64_t)C * sstride) + doc + c / sstride;
+        dst = a.states + (sslot * H + h) * (size_t)D * D;
+      }
+      if (a.ckpt && c % a.ckpt_stride == 0)
+        dck = a.ckpt + ((t0g / ((int64_t)C * a.ckpt_stride) + doc + c / a.ckpt_stride) * H + h) * (size_t)D * D;
+      if (!dst && !dck) continue;
 #pragma unroll
       for (int w = 0; w < sNW; ++w)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int u = j * 64 + lane, row = u >> 2, c4 = u & 3;
-          *reinterpret_cast<float4 *>(dst + (size_t)row * D + 16 * (sNW * quarter + w) + 4 * c4) =
-              *reinterpret_cast<const float4 *>(&sm.stage[c & 1][w][row][4 * c4]);
+          const size_t off = (size_t)row * D + 16 * (sNW * quarter + w) + 4 * c4;
+          const float4 v4 = *reinterpret_cast<const float4 *>(&sm.stage[c & 1][w][row][4 * c4]);
+          if (dst) *reinterpret_cast<float4 *>(dst + off) = v4;
+          if (dck) *reinterpret_cast<float4 *>(dck + off) = v4;
         }
     }
     return;
@@ -143,8 +182,8 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   floatx4 X[8];
   const float *src = nullptr;
   if (!a.identity_init) {
-    if (first_run) src = a.init ? a.init + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D : nullptr;
-    else src = a.seg_init ? a.seg_init + ((size_t)unit * H + h) * D * D : nullptr;
+    if (use_init) src = a.init ? a.init + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D : nullptr;
+    else src = a.seg_init ? a.seg_init + ((size_t)ck_init * H + h) * D * D : nullptr;
   }
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
@@ -170,7 +209,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   // the compiler would otherwise wait for every load issued before it.
   auto load_ring = [&](ScanRing &p, int c) {
     c = max(c_lo, min(c, c_hi - 1));
-    const float *pk = a.pack + ((size_t)(ck_base + c) * H + h) * kPackWords;
+    const float *pk = a.pack + ((size_t)wslot(c) * H + h) * kPackWords;
     constexpr int NR = ZRHS ? 2 : 8;
     const uint4 *pr = reinterpret_cast<const uint4 *>(pk + kPackR) + (size_t)slab * NR * 64;
 #pragma unroll
@@ -262,7 +301,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     if (i + 3 >= nchunks) break;
     step(p3, at(i + 3), at(i + 7));
   }
-  if (a.final_out && last_run) {
+  if (a.final_out && write_final) {
     float *dst = a.final_out + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
@@ -270,7 +309,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
       for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kt + g4 + r) * D + dv0 + cl] = X[kt][r];
   }
   if (a.seg_final) {
-    float *dst = a.seg_final + ((size_t)unit * H + h) * D * D;
+    float *dst = a.seg_final + ((size_t)ck_unit * H + h) * D * D;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
@@ -360,6 +399,7 @@ hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t uni
   r.seg_span = span;
   r.units = units;
   r.states = nullptr;
+  r.ckpt = nullptr;
   r.final_out = nullptr;
   r.seg_init = nullptr;
   // the runs' transfer maps (from the identity, no right-hand side)
@@ -388,7 +428,7 @@ hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t uni
 }
 
 hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st) {
-  const int64_t pairs = (a.seg_span > 0 ? a.units : a.num_docs) * a.H;
+  const int64_t pairs = (a.seg_span > 0 || a.win_len > 0 ? a.units : a.num_docs) * a.H;
   const int64_t groups = (pairs + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * sNQ)), block(64 * (sNW + 1));
   // the reverse recurrence carries a full R, the forward one K^T Z

@@ -117,15 +117,9 @@ static size_t seg_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   return 3 * (size_t)ckpt_num_slots(vi, span) * s->num_heads * s->d_k * s->d_v * sizeof(float);
 }
 
-size_t bwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
-  size_t per = (size_t)s->d_k * s->d_v + 6 * kChunk * kChunk;
-  if (bwd_uses_scan_pack(s)) per += kScanPackFloats;
-  return round256((size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float));
-}
+size_t bwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s) { return bwd_layout(vi, s, 0, 1).l2f; }
 
-size_t bwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
-  return round256(bwd_l2_offset(vi, s) + l2_factor_bytes(vi, s));
-}
+size_t bwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s) { return bwd_layout(vi, s, 0, 1).seg; }
 
 size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   // per chunk slot and head, fp32, in the checkpoint slot layout (stride 1):
@@ -137,7 +131,7 @@ size_t bwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   // per-(token, head) factors {r_q, r_k, r_q~, r_k~}; when the scan runs in
   // parallel runs (long documents, bf16 io at d = 128), the runs' transfer
   // maps, offsets and start values
-  return bwd_seg_offset(vi, s) + (bwd_uses_scan_pack(s) ? seg_bytes(vi, s) : 0) + 256;
+  return bwd_layout(vi, s, 0, 1).total;
 }
 
 bool bwd_uses_scan_pack(const flare_gdn_shape *s) {
@@ -148,14 +142,9 @@ bool fwd_uses_chunk_matrices(const flare_gdn_shape *s) {
   return s->io_dtype == FLARE_BF16 && s->d_k == 128 && s->d_v == 128 && (s->flags & ~FLARE_QK_L2NORM) == 0;
 }
 
-size_t fwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
-  const size_t per = 6 * kChunk * kChunk + kScanPackFloats + (size_t)s->d_k * s->d_v;
-  return round256((size_t)ckpt_num_slots(vi, 1) * s->num_heads * per * sizeof(float));
-}
+size_t fwd_l2_offset(const VarlenInfo &vi, const flare_gdn_shape *s) { return fwd_layout(vi, s, 0).l2f; }
 
-size_t fwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s) {
-  return round256(fwd_l2_offset(vi, s) + l2_factor_bytes(vi, s));
-}
+size_t fwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s) { return fwd_layout(vi, s, 0).seg; }
 
 size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   if (!fwd_uses_chunk_matrices(s)) return 0;
@@ -163,7 +152,86 @@ size_t fwd_workspace_bytes(const VarlenInfo &vi, const flare_gdn_shape *s) {
   // and room for the chunk-start state when no checkpoints are asked for; with
   // the q/k L2 flag then the per-(token, head) factors {r_q, r_k, r_q~, r_k~};
   // then the scan's run buffers when it runs in parallel runs
-  return fwd_seg_offset(vi, s) + seg_bytes(vi, s) + 256;
+  return fwd_layout(vi, s, 0).total;
+}
+
+int max_chunks(const VarlenInfo &vi) { return (int)(((int64_t)vi.max_len + kChunk - 1) / kChunk); }
+
+int rebuild_span(int stride, int win) {
+  int best = stride;
+  for (int span = 2 * stride; span <= kRebuildRun; span += stride)
+    if (win == 0 || win % span == 0) best = span;
+  return best;
+}
+
+ChunkLayout fwd_layout(const VarlenInfo &vi, const flare_gdn_shape *s, int win) {
+  ChunkLayout L;
+  L.win = win;
+  L.slots = win > 0 ? (int64_t)vi.num_docs * win : ckpt_num_slots(vi, 1);
+  const size_t per = (size_t)L.slots * s->num_heads;
+  const size_t dd = (size_t)s->d_k * s->d_v * sizeof(float);
+  L.cmat = 0;
+  L.cmat_bytes = per * 6 * kChunk * kChunk * sizeof(float);
+  L.pack = L.cmat + L.cmat_bytes;
+  L.pack_bytes = per * kScanPackFloats * sizeof(float);
+  L.states = L.pack + L.pack_bytes;
+  L.states_bytes = per * dd;
+  L.l2f = round256(L.states + L.states_bytes);
+  L.l2f_bytes = l2_factor_bytes(vi, s);
+  const size_t tail = round256(L.l2f + L.l2f_bytes);
+  if (win > 0) {
+    L.carry = tail;
+    L.carry_bytes = (size_t)vi.num_docs * s->num_heads * dd;
+    L.total = L.carry + L.carry_bytes + 256;
+  } else {
+    L.seg = tail;
+    L.seg_bytes = seg_bytes(vi, s);
+    L.total = L.seg + L.seg_bytes + 256;
+  }
+  return L;
+}
+
+ChunkLayout bwd_layout(const VarlenInfo &vi, const flare_gdn_shape *s, int win, int stride) {
+  ChunkLayout L;
+  const bool chunked = bwd_uses_scan_pack(s);
+  L.win = win;
+  L.slots = win > 0 ? (int64_t)vi.num_docs * win : ckpt_num_slots(vi, 1);
+  const size_t per = (size_t)L.slots * s->num_heads;
+  const size_t dd = (size_t)s->d_k * s->d_v * sizeof(float);
+  L.adj = 0;
+  L.adj_bytes = per * dd;
+  L.cmat = L.adj + L.adj_bytes;
+  L.cmat_bytes = per * 6 * kChunk * kChunk * sizeof(float);
+  L.pack = L.cmat + L.cmat_bytes;
+  L.pack_bytes = chunked ? per * kScanPackFloats * sizeof(float) : 0;
+  L.states = L.pack + L.pack_bytes;
+  L.states_bytes = chunked && stride > 1 ? per * dd : 0;
+  L.l2f = round256(L.states + L.states_bytes);
+  L.l2f_bytes = l2_factor_bytes(vi, s);
+  const size_t tail = round256(L.l2f + L.l2f_bytes);
+  if (win > 0) {
+    L.carry = tail;
+    L.carry_bytes = (size_t)vi.num_docs * s->num_heads * dd;
+    L.total = L.carry + L.carry_bytes + 256;
+  } else {
+    L.seg = tail;
+    L.seg_bytes = chunked ? seg_bytes(vi, s) : 0;
+    L.total = L.seg + L.seg_bytes + 256;
+  }
+  return L;
+}
+
+int pick_window(const VarlenInfo &vi, const flare_gdn_shape *s, bool bwd, int stride, int unit, size_t bytes) {
+  auto total = [&](int win) { return bwd ? bwd_layout(vi, s, win, stride).total : fwd_layout(vi, s, win).total; };
+  if (total(0) <= bytes) return 0;
+  if (unit < 1 || vi.num_docs == 0) return -1;
+  // the windowed total grows with the window: the largest k with total(k unit) <= bytes
+  int64_t lo = 0, hi = ((int64_t)max_chunks(vi) + unit - 1) / unit;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (total((int)(mid * unit)) <= bytes) lo = mid; else hi = mid - 1;
+  }
+  return lo > 0 ? (int)(lo * unit) : -1;
 }
 
 int64_t route1_num_blocks(const flare_varlen *v, int32_t block_size) {

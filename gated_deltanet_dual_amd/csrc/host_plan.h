@@ -66,6 +66,47 @@ int scan_seg_span(const VarlenInfo &vi, int32_t heads);
 size_t fwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s);
 size_t bwd_seg_offset(const VarlenInfo &vi, const flare_gdn_shape *s);
 
+// Byte layout of the chunked path's workspace (bf16 io, d = 128), as offsets
+// into the caller's buffer; a region of size 0 is absent.  One pass (win = 0)
+// keeps every chunk's buffers at its checkpoint slot of stride 1; chunk
+// windows (win > 0) keep only one window of chunks of every document, at slot
+// doc * win + (c - window start), and carry the state (or its adjoint) from
+// window to window in `carry`.
+struct ChunkLayout {
+  int win = 0;
+  int64_t slots = 0;                     // per-chunk slots of one pass
+  size_t adj = 0, adj_bytes = 0;         // bwd: end-state adjoints [slots][H][D][D]
+  size_t cmat = 0, cmat_bytes = 0;       // six chunk matrices [slots][H][6][32][32]
+  size_t pack = 0, pack_bytes = 0;       // scan hand-over [slots][H][kScanPackFloats]
+  size_t states = 0, states_bytes = 0;   // chunk-start states [slots][H][D][D]
+  size_t l2f = 0, l2f_bytes = 0;         // q/k L2 factors [T][H][4]
+  size_t seg = 0, seg_bytes = 0;         // one pass: the scan's run buffers
+  size_t carry = 0, carry_bytes = 0;     // windows: the carried chain [N][H][D][D]
+  size_t total = 0;
+};
+// The forward's layout (fwd_uses_chunk_matrices only): chunk matrices,
+// hand-over, chunk-start states (used unless stride-1 checkpoints are
+// written), L2 factors, then the run buffers or the carry.
+ChunkLayout fwd_layout(const VarlenInfo &vi, const flare_gdn_shape *s, int win);
+// The backward's layout: adjoints, chunk matrices, and on the chunked path
+// the hand-over, the rebuilt chunk-start states (checkpoint stride > 1),
+// L2 factors, then the run buffers or the carry.  Windows need the chunked
+// path and a multiple of the stride.
+ChunkLayout bwd_layout(const VarlenInfo &vi, const flare_gdn_shape *s, int win, int stride);
+// Chunks of the longest document.
+int max_chunks(const VarlenInfo &vi);
+// Chunks per run when the backward rebuilds the chunk-start states from
+// checkpoints of stride `stride`: the largest multiple of the stride of at
+// most kRebuildRun chunks (the stride itself when larger) that divides the
+// window (win > 0).  Short runs leave the scan waiting on its loads; runs of
+// a few dozen chunks reach the throughput of whole chains.
+constexpr int kRebuildRun = 32;
+int rebuild_span(int stride, int win);
+// The window an entry point runs at with a workspace of `bytes`: 0 (one pass)
+// when the one-pass layout fits, else the largest multiple of `unit` chunks
+// whose windowed layout fits, -1 when none does.
+int pick_window(const VarlenInfo &vi, const flare_gdn_shape *s, bool bwd, int stride, int unit, size_t bytes);
+
 // Bytes of fwd workspace when the forward runs its chunked passes (bf16 io,
 // d = 128; the q/k L2 flag allowed), else 0: per chunk slot and head the six
 // chunk matrices, the scan hand-over and a chunk-start state, then the L2

@@ -63,8 +63,26 @@ struct FwdArgs {
   int scan_span;
   int64_t scan_units;
   float *scan_ws;
+  // Chunk windows (win_len > 0): a launch covers chunks [win_lo, win_lo +
+  // win_len) of every document, and the per-chunk workspace arrays hold only
+  // those, at slot doc * win_len + (c - win_lo); win_len = 0: every chunk, at
+  // its checkpoint slot of stride 1.
+  int win_lo, win_len;
 };
-hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st);
+// Where the chunked forward (bf16 io, d = 128) keeps its per-chunk buffers
+// and how it walks the chunks: one pass (win = 0) or windows of win chunks of
+// every document, the chain carried between them in carry.
+struct FwdPlan {
+  float *cmat, *pack;
+  float *states;  // chunk-start states per slot; NULL: the stride-1 checkpoints (one pass)
+  float4 *l2f;    // q/k L2 factors, when the flag is set
+  float *carry;   // windows: [N, H, 128, 128]
+  int win, max_chunks;
+  int64_t slots;  // per-chunk slots of one pass (window)
+};
+// a.workspace set: the chunked passes, with `plan` (NULL: one pass over the
+// whole workspace in its one-pass layout); else the per-(document, head) kernel
+hipError_t launch_gdn_fwd(const FwdArgs &a, hipStream_t st, const FwdPlan *plan = nullptr);
 // the per-row L2 factors of q, k, q~, k~ into a.l2f (gdn_l2.hip)
 hipError_t launch_l2_factors(const FwdArgs &a, float4 *out, hipStream_t st);
 
@@ -101,6 +119,25 @@ struct ScanArgs {
   const float *seg_init;
   float *seg_final;
   int identity_init, homog;
+  // every run starts from seg_init, a document's first one too (the runs
+  // rebuilding the chunk-start states from strided checkpoints)
+  int seg_init_all;
+  // > 0: seg_init is indexed by the run's checkpoint slot of this stride (a
+  // divisor of seg_span) instead of seg_span's
+  int seg_init_stride;
+  // Chunk windows (win_len > 0, states_stride 1): each document's chain covers
+  // chunks [win_lo, win_lo + win_len) only, from init to final_out (a chain
+  // with no chunk there copies init to final_out); pack and states are
+  // indexed by the window slot doc * win_len + (c - win_lo).  With seg_span
+  // > 0 as well (win_lo and win_len multiples of it) the units are the runs
+  // inside the window, numbered doc * (win_len / seg_span) + g, and
+  // seg_init / seg_final are indexed by the run's checkpoint slot of stride
+  // seg_span (so the strided checkpoints are the runs' start values).
+  int win_lo, win_len;
+  // Strided checkpoints besides states: X before the step of chunk c,
+  // c % ckpt_stride == 0, at ckpt_slot(cu_i, i, c, ckpt_stride) (or NULL).
+  float *ckpt;
+  int ckpt_stride;
 };
 hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st);
 // The runs' start states from their transfer maps M (identity-init, homog
@@ -127,8 +164,26 @@ struct BwdArgs {
   float *tri;            // per slot and head [slots][H][6][32][32]: T, T~, Mwo, Mwq, Mwk, Mw~ (set by the launcher)
   const float *fwd_cm;   // the same matrices from the forward's workspace, or NULL
   float *pack;           // bf16, d = 128: the pre-pass's hand-over to the scan, per slot and head (set by the launcher)
+  // ckpt_in holds every chunk-start state at the chunk's checkpoint slot of
+  // stride 1 (a checkpoint buffer) rather than at the (window) slot
+  int ckpt_global;
 };
-hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
+// The backward's per-chunk buffers on the chunked path (bf16 io, d = 128):
+// as for the forward, plus the rebuilt chunk-start states when the
+// checkpoints hold only every stride-th one.
+struct BwdPlan {
+  float *adj, *tri, *pack;
+  float *states;  // rebuilt chunk-start states per slot (stride > 1), else NULL
+  float4 *l2f;
+  float *carry;   // windows: [N, H, 128, 128]
+  int win, max_chunks, stride;
+  int64_t slots;
+  // the rebuild's runs: rebuild_span chunks each (a multiple of the stride,
+  // dividing the window), rebuild_units of them in one pass
+  int rebuild_span;
+  int64_t rebuild_units;
+};
+hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st, const BwdPlan *plan = nullptr);
 // per-chunk backward kernel for bf16 io at d = 128 (gdn_bwd_chunk.hip)
 hipError_t launch_bwd_chunk_d128(const BwdArgs &a, hipStream_t st, int64_t slots);
 // the chunk solves T, T~ into a.tri for bf16 io at d = 128 (gdn_tri.hip)

@@ -105,14 +105,45 @@ int32_t flare_gdn_chunk_size(void);
 size_t flare_gdn_dual_workspace_size(const flare_varlen *varlen,
                                      const flare_gdn_shape *shape, int for_bwd);
 
+/* Strided checkpoints and chunk windows (Key designs item 2: keep only every
+ * s-th clean state and rebuild the rest when they are needed).  Bytes of
+ * workspace the chunked path (bf16 io, d = 128) needs when flare_gdn_dual_bwd
+ * reads checkpoints of stride ckpt_stride_chunks (for_bwd = 1; the forward's
+ * workspace does not depend on the stride) and when it runs in windows of
+ * window_chunks chunks of every document (0: one pass over the whole batch).
+ * A window keeps the per-chunk buffers of that many chunks of every document
+ * only, so the workspace no longer grows with the sequence length; the chain
+ * of states (and of their adjoints) is carried from window to window.  The
+ * backward needs window_chunks to be a multiple of the stride; with a stride
+ * above 1 it rebuilds the chunk-start states of each window from the
+ * checkpoints, as parallel runs of stride chunks each.  Returns 0 on invalid
+ * arguments and for shapes without the chunked path (there only stride 1,
+ * window 0 and flare_gdn_dual_workspace_size apply).
+ *
+ * flare_gdn_dual_fwd and flare_gdn_dual_bwd choose the window from the
+ * workspace_bytes they are given: one pass when it holds the one-pass layout
+ * (flare_gdn_dual_workspace_size_window(..., 0)), else the largest window
+ * (multiple of the stride for the backward) whose layout fits, else
+ * FLARE_ERR_WORKSPACE.  Results do not depend on the window or on the stride
+ * (the same arithmetic runs in the same order), except where the one-pass
+ * scan of a long document runs in parallel runs (flare_gdn_dual_fwd's state
+ * scan in runs then differs by rounding). */
+size_t flare_gdn_dual_workspace_size_window(const flare_varlen *varlen,
+                                            const flare_gdn_shape *shape,
+                                            int for_bwd,
+                                            int32_t ckpt_stride_chunks,
+                                            int32_t window_chunks);
+
 /* Checkpoints.  With C = flare_gdn_chunk_size() and stride s (in chunks), the
  * checkpoint of document i, local chunk c (c % s == 0) is the clean state at
  * the start of that chunk, fp32 [H, d_k, d_v], stored at slot
  *     floor(cu_seqlens[i] / (C*s)) + i + c / s
  * of a buffer [num_slots, H, d_k, d_v] with num_slots = floor(T / (C*s)) + N.
- * The slots of different documents never overlap.  This build supports s = 1.
- * flare_gdn_dual_ckpt_size returns the buffer size in bytes (0 on invalid
- * arguments); flare_gdn_ckpt_slot is the slot formula above. */
+ * The slots of different documents never overlap.  Any s >= 1 may be written
+ * by flare_gdn_dual_fwd; flare_gdn_dual_bwd reads s > 1 on the chunked path
+ * (bf16 io, d = 128) only.  flare_gdn_dual_ckpt_size returns the buffer size
+ * in bytes (0 on invalid arguments); flare_gdn_ckpt_slot is the slot formula
+ * above. */
 size_t flare_gdn_dual_ckpt_size(const flare_varlen *varlen,
                                 const flare_gdn_shape *shape,
                                 int32_t ckpt_stride_chunks);
@@ -133,8 +164,10 @@ int64_t flare_gdn_ckpt_slot(int32_t cu_seqlens_i, int32_t doc_index,
  *   h_final    [N, H, d_k, d_v] fp32 clean state after each document, or NULL
  *   ckpt       chunk-start clean states for the backward (see
  *              flare_gdn_dual_ckpt_size), or NULL for inference
- *   workspace  device scratch of flare_gdn_dual_workspace_size(..., 0) bytes,
- *              256-byte aligned; may be NULL when that size is 0
+ *   workspace  device scratch of flare_gdn_dual_workspace_size(..., 0) bytes
+ *              (one pass), or of flare_gdn_dual_workspace_size_window(..., 0,
+ *              s, w) bytes for windows of w chunks; 256-byte aligned; may be
+ *              NULL when that size is 0
  * The clean block-boundary states are never written to memory. */
 flare_status flare_gdn_dual_fwd(const flare_varlen *varlen,
                                 const flare_gdn_shape *shape, const void *q,
@@ -208,11 +241,13 @@ flare_status flare_gdn_dual_fwd_pool(const flare_varlen *varlen,
  * Outputs (written, not accumulated): dq, dk [T,H,d_k], dv [T,H,d_v] io;
  * dalpha, dbeta [T,H] fp32; the same five for the noisy stream (prompt rows 0);
  * dh0 [N,H,d_k,d_v] fp32 or NULL.  workspace: see
- * flare_gdn_dual_workspace_size(..., 1), 256-byte aligned.
+ * flare_gdn_dual_workspace_size(..., 1) (one pass, stride 1) and
+ * flare_gdn_dual_workspace_size_window, 256-byte aligned.
  * fwd_workspace: NULL, or the workspace of the flare_gdn_dual_fwd call that
- * produced ckpt, still holding what that call wrote there (same inputs, shape
- * and batch): its chunk matrices are then read instead of formed again.  The
- * result is the same either way. */
+ * produced ckpt, when that call ran in one pass, still holding what it wrote
+ * there (same inputs, shape and batch): its chunk matrices are then read
+ * instead of formed again when this call runs in one pass too (a windowed
+ * call forms its own).  The result is the same either way. */
 flare_status flare_gdn_dual_bwd(
     const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q,
     const void *k, const void *v, const float *alpha, const float *beta,

@@ -79,8 +79,8 @@ def test_fwd_validation(L):
                 g.GDNShape(16, 128, 128, 4, g.F32, 0, 0.0)]:
         assert fwd_status(L, varlen([0, 16], [8]), bad) == 4
     assert fwd_status(L, varlen([0, 16], [8]), g.GDNShape(0, 128, 128, 4, g.BF16, 0, 0.0)) == 2
-    # checkpoint stride other than 1 is not built
-    assert fwd_status(L, varlen([0, 16], [8]), ok_shape, ckpt=FAKE, stride=2) == 4
+    # checkpoint stride below 1
+    assert fwd_status(L, varlen([0, 16], [8]), ok_shape, ckpt=FAKE, stride=0) == 2
     # missing host copies
     v = g._Varlen(1, FAKE.value, None, FAKE.value, None)
     assert fwd_status(L, v, ok_shape) == 1
@@ -98,8 +98,11 @@ def test_fwd_workspace_checked_before_launch(L):
     pack = 128 * 128 + 2 * 32 * 32 // 2 + 2 * (32 * 128 // 2) + 64
     assert need == (164 // 32 + 2) * 4 * (6 * 32 * 32 + pack + 128 * 128) * 4 + 256
     P = [FAKE] * 10
+    # a smaller workspace runs in windows of chunks; below one chunk's window it is refused
+    w1 = L.flare_gdn_dual_workspace_size_window(ctypes.byref(v), ctypes.byref(shape), 0, 1, 1)
+    assert 0 < w1 < need
     st = L.flare_gdn_dual_fwd(ctypes.byref(v), ctypes.byref(shape), *P, None, FAKE, FAKE, None, None, 1,
-                              FAKE, need - 1, None)
+                              FAKE, w1 - 1, None)
     assert st == 5
     st = L.flare_gdn_dual_fwd(ctypes.byref(v), ctypes.byref(shape), *P, None, FAKE, FAKE, None, None, 1,
                               None, 0, None)
@@ -362,3 +365,62 @@ def test_parallel_runs_in_workspace_size(L):
     assert need([0, 8192, 16384, 24576, 32768], 16) == (32768 // 32 + 4) * slot_bytes + 256
     # one short document: runs would be under 32 chunks
     assert need([0, 4096], 16) == (4096 // 32 + 1) * slot_bytes + 256
+
+
+def test_strided_checkpoints_and_windows_sizes(L):
+    """Checkpoints of stride s, the backward's rebuild region and chunk
+    windows in the size queries; the entry points refuse what they do not
+    serve before anything is launched."""
+    H, D = 4, 128
+    cu, pl = [0, 300, 364, 364, 1000], [20, 0, 0, 96]
+    v = varlen(cu, pl)
+    N, T = 4, 1000
+    shape = g.GDNShape(H, D, D, 4, g.BF16, 0, 0.0)
+    dd = D * D * 4
+    wsw = lambda bwd, s, w, sh=shape: L.flare_gdn_dual_workspace_size_window(ctypes.byref(v), ctypes.byref(sh), bwd,
+                                                                            s, w)
+    one_f = L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(shape), 0)
+    one_b = L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(shape), 1)
+    assert wsw(0, 1, 0) == one_f and wsw(1, 1, 0) == one_b
+    assert wsw(0, 4, 0) == one_f  # the forward's workspace does not depend on the stride
+    slots = T // 32 + N
+    pack = 128 * 128 + 1024 + 2048 + 2048 + 64
+    # stride > 1: the backward keeps the rebuilt chunk-start states after the hand-over
+    per_b = H * (dd + 6 * 32 * 32 * 4 + pack * 4)
+    assert wsw(1, 2, 0) == (slots * (per_b + H * dd) + 255) // 256 * 256 + 256
+    # windows of w chunks: N * w slots, then the carried chain [N][H][D][D]
+    per_f = H * (6 * 32 * 32 * 4 + pack * 4 + dd)
+    for w in (1, 3, 8):
+        assert wsw(0, 1, w) == (N * w * per_f + 255) // 256 * 256 + N * H * dd + 256
+    assert wsw(1, 4, 8) == (N * 8 * (per_b + H * dd) + 255) // 256 * 256 + N * H * dd + 256
+    assert wsw(1, 4, 4) < one_b
+    # the backward's window must be a multiple of the stride; no stride < 1
+    assert wsw(1, 4, 6) == 0 and wsw(1, 0, 0) == 0 and wsw(0, 1, -1) == 0
+    # shapes without the chunked path: one pass, stride 1 only
+    small = g.GDNShape(2, 16, 16, 4, g.F32, 0, 0.0)
+    assert wsw(0, 1, 4, small) == 0 and wsw(1, 2, 0, small) == 0
+    assert wsw(1, 1, 0, small) == L.flare_gdn_dual_workspace_size(ctypes.byref(v), ctypes.byref(small), 1)
+    # checkpoint buffers of stride s: floor(T / (32 s)) + N slots
+    for s in (1, 2, 4, 7):
+        assert L.flare_gdn_dual_ckpt_size(ctypes.byref(v), ctypes.byref(shape), s) == (T // (32 * s) + N) * H * dd
+    assert L.flare_gdn_dual_ckpt_size(ctypes.byref(v), ctypes.byref(shape), 0) == 0
+    # the backward: stride 0 is a shape error, stride > 1 needs the chunked path
+    args = [FAKE] * 10 + [None, FAKE]
+    tail = [None, FAKE, FAKE, None] + [FAKE] * 10 + [None]
+    sv = varlen([0, 40, 64], [8, 0])
+    st = L.flare_gdn_dual_bwd(ctypes.byref(sv), ctypes.byref(small), *args, 2, *tail, FAKE, 1 << 30, None)
+    assert st == 4 and b"stride" in L.flare_last_error()
+    st = L.flare_gdn_dual_bwd(ctypes.byref(v), ctypes.byref(shape), *args, 0, *tail, FAKE, 1 << 30, None)
+    assert st == 2
+    # too small for even a one-chunk window (a multiple of the stride for the backward)
+    st = L.flare_gdn_dual_bwd(ctypes.byref(v), ctypes.byref(shape), *args, 4, *tail, FAKE, wsw(1, 4, 4) - 1, None)
+    assert st == 5
+    P = [FAKE] * 10
+    st = L.flare_gdn_dual_fwd(ctypes.byref(v), ctypes.byref(shape), *P, None, FAKE, FAKE, None, None, 1,
+                              FAKE, wsw(0, 1, 1) - 1, None)
+    assert st == 5
+    # the pool forward runs in one pass only
+    host = np.arange(N, dtype=np.int32)
+    st = L.flare_gdn_dual_fwd_pool(ctypes.byref(v), ctypes.byref(shape), *P, FAKE, host.ctypes.data, FAKE, N, 1,
+                                   FAKE, FAKE, None, 1, FAKE, wsw(0, 1, 4), None)
+    assert st == 5 and b"one pass" in L.flare_last_error()
