@@ -61,20 +61,19 @@ PRE_BYTES_PER_TH = 3 * 256 + 8
 PACK_BYTES_PER_SLOT_HEAD = (128 * 128 + 1024 + 2048 + 2048 + 64) * 4
 PRE_BYTES_PER_SLOT_HEAD = 6 * 32 * 32 * 4 + PACK_BYTES_PER_SLOT_HEAD
 SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4
-# the forward pre-pass reads k, v and the clean gates and T, and writes the
-# hand-over; the forward scan reads that and writes the chunk-start states;
-# the output pass reads the layer's inputs, the six chunk matrices and the
-# chunk-start states and writes o, o~ (FWD_BYTES_PER_TH plus the states)
-# (the forward's hand-over carries Z = diag(D) T V, 32 x 128 fp32, in place
-# of the backward's 128 x 128 R)
-FWD_PRE_BYTES_PER_TH = 2 * 256 + 8
+# the forward's preparation pass reads q, k and the gates of both streams and
+# v, and writes the six 32 x 32 fp32 chunk matrices and the hand-over; the
+# forward scan reads that and writes the chunk-start states; the output pass
+# reads the layer's inputs, the six chunk matrices and the chunk-start states
+# and writes o, o~ (FWD_BYTES_PER_TH plus the states) (the forward's hand-over
+# carries Z = diag(D) T V, 32 x 128 fp32, in place of the backward's 128 x 128 R)
 FWD_PACK_BYTES_PER_SLOT_HEAD = (32 * 128 + 1024 + 2048 + 2048 + 64) * 4
-FWD_PRE_BYTES_PER_SLOT_HEAD = 32 * 32 * 4 + FWD_PACK_BYTES_PER_SLOT_HEAD
 FWD_SCAN_BYTES_PER_SLOT_HEAD = FWD_PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4
-# the chunk-matrix pass reads q, k and the gates of both streams and writes six
-# 32 x 32 fp32 matrices per (chunk slot, head)
-TRI_BYTES_PER_TH = 2 * 256 + 8
 TRI_BYTES_PER_SLOT_HEAD = 6 * 32 * 32 * 4
+PREP_BYTES_PER_TH = 2 * 256 + 8
+PREP_BYTES_PER_SLOT_HEAD = TRI_BYTES_PER_SLOT_HEAD + FWD_PACK_BYTES_PER_SLOT_HEAD
+STEP_KERNELS = ("gdn_fwd_prep_kernel", "gdn_fwd_scan_kernel", "gdn_dual_fwd_kernel",
+                "gdn_bwd_pre_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel")
 
 
 def fwd_flops_per_th(d, C, B, noisy):
@@ -287,17 +286,16 @@ def run_headline(torch, g, wl, dev, timer, up, args):
         torch.cuda.synchronize()
         g.timing_enable(False)
         kern = {}
-        for name in ("gdn_tri_kernel", "gdn_fwd_pre_kernel", "gdn_fwd_scan_kernel", "gdn_dual_fwd_kernel",
-                     "gdn_bwd_pre_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel"):
+        for name in STEP_KERNELS:
             ms, n = g.timing_avg_ms(name)
             kern[name] = {"ms": ms, "launches": n}
         g.timing_reset()
         alg = {
-            "gdn_fwd_pre_kernel": FWD_PRE_BYTES_PER_TH * th_total + FWD_PRE_BYTES_PER_SLOT_HEAD * n_chunk_heads,
+            "gdn_fwd_prep_kernel": PREP_BYTES_PER_TH * (th_total + th_resp) + 256 * th_total
+                                   + PREP_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_fwd_scan_kernel": FWD_SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes
                                    + TRI_BYTES_PER_SLOT_HEAD * n_chunk_heads,
-            "gdn_tri_kernel": TRI_BYTES_PER_TH * (th_total + th_resp) + TRI_BYTES_PER_SLOT_HEAD * n_slots * H,
             "gdn_bwd_pre_kernel": PRE_BYTES_PER_TH * (th_total + th_resp) + PRE_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_bwd_scan_kernel": SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_bwd_chunk_kernel": BWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
@@ -692,8 +690,6 @@ def bench_packed_layer(torch, g, wl, dev, timer, up, args):
     return out
 
 
-STEP_KERNELS = ("gdn_tri_kernel", "gdn_fwd_pre_kernel", "gdn_fwd_scan_kernel", "gdn_dual_fwd_kernel",
-                "gdn_bwd_pre_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel")
 
 
 def bench_step_sweep(torch, g, wl, dev, up, args):

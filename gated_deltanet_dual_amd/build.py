@@ -23,7 +23,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
-SOURCES_HIP = ["api.hip", "block_step.hip", "shortconv.hip", "gdn_fwd.hip", "gdn_bwd.hip", "gdn_bwd_chunk.hip", "gdn_scan.hip", "gdn_bwd_pre.hip", "gdn_tri.hip", "gdn_fwd_pre.hip", "gdn_fwd_out.hip", "shortconv_bwd.hip", "route1.hip", "timing.hip", "noalloc.hip", "gdn_l2.hip"]
+SOURCES_HIP = ["api.hip", "block_step.hip", "shortconv.hip", "gdn_fwd.hip", "gdn_bwd.hip", "gdn_bwd_chunk.hip", "gdn_scan.hip", "gdn_bwd_pre.hip", "gdn_tri.hip", "gdn_fwd_pre.hip", "gdn_fwd_out.hip", "shortconv_bwd.hip", "route1.hip", "timing.hip", "noalloc.hip", "gdn_l2.hip", "gdn_fwd_prep.hip"]
 SOURCES_CXX = ["host_plan.cpp"]
 
 

@@ -889,15 +889,16 @@ static hipError_t launch_bwd_chunked(const BwdArgs &a_in, hipStream_t st, const 
     aw.workspace = p.adj;
     aw.tri = p.tri;
     aw.pack = p.pack;
-    if (a.fwd_cm && p.win == 0) {
-      aw.tri = const_cast<float *>(a.fwd_cm);  // read only from here on
-    } else {
-      TimedLaunch tl(K_TRI, st);
-      hipError_t e0 = launch_tri_d128(aw, st, p.slots);
-      if (e0 != hipSuccess) return e0;
-    }
+    const bool own_cm = !(a.fwd_cm && p.win == 0);
+    if (!own_cm) aw.tri = const_cast<float *>(a.fwd_cm);  // read only from here on
     if (p.stride > 1) {
-      {
+      // the forward's hand-over for the rebuild (with the chunk matrices,
+      // when they are not the forward's)
+      if (own_cm) {
+        TimedLaunch tl(K_FWD_PREP, st);
+        hipError_t e0 = launch_fwd_prep_d128(aw.f, aw.tri, p.pack, st, p.slots);
+        if (e0 != hipSuccess) return e0;
+      } else {
         TimedLaunch tl(K_FWD_PRE, st);
         hipError_t e0 = launch_fwd_pre_d128(aw.f, aw.tri, p.pack, st, p.slots);
         if (e0 != hipSuccess) return e0;
@@ -921,6 +922,11 @@ static hipError_t launch_bwd_chunked(const BwdArgs &a_in, hipStream_t st, const 
       aw.ckpt_in = p.states;
       aw.ckpt_global = 0;
     } else {
+      if (own_cm) {
+        TimedLaunch tl(K_TRI, st);
+        hipError_t e0 = launch_tri_d128(aw, st, p.slots);
+        if (e0 != hipSuccess) return e0;
+      }
       aw.ckpt_global = p.win > 0;
     }
     {

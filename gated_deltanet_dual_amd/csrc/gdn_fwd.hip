@@ -720,7 +720,8 @@ hipError_t launch_gdn_fwd(const FwdArgs &a_in, hipStream_t st, const FwdPlan *pl
   FwdArgs a = a_in;
   if (a.workspace) {
     // bf16, d = 128: per pass (the whole batch, or one window of chunks of
-    // every document) the chunk matrices and the scan hand-over in parallel,
+    // every document) the chunk matrices and the scan hand-over in one
+    // parallel pass (gdn_fwd_prep.hip),
     // the state recurrence (chunk-start states -> the checkpoints or the
     // workspace; strided checkpoints besides), then the outputs in parallel;
     // with the q/k L2 flag first the per-row factors the kernels fold in
@@ -750,17 +751,8 @@ hipError_t launch_gdn_fwd(const FwdArgs &a_in, hipStream_t st, const FwdPlan *pl
       aw.win_lo = p.win > 0 ? w * p.win : 0;
       aw.win_len = p.win;
       {
-        BwdArgs b{};
-        b.f = aw;
-        b.T = aw.T;
-        b.tri = p.cmat;
-        TimedLaunch tl(K_TRI, st);
-        hipError_t e = launch_tri_d128(b, st, p.slots);
-        if (e != hipSuccess) return e;
-      }
-      {
-        TimedLaunch tl(K_FWD_PRE, st);
-        hipError_t e = launch_fwd_pre_d128(aw, p.cmat, p.pack, st, p.slots);
+        TimedLaunch tl(K_FWD_PREP, st);
+        hipError_t e = launch_fwd_prep_d128(aw, p.cmat, p.pack, st, p.slots);
         if (e != hipSuccess) return e;
       }
       {

@@ -90,6 +90,9 @@ hipError_t launch_l2_factors(const FwdArgs &a, float4 *out, hipStream_t st);
 // `cmat` -> scan hand-over `pack`, gdn_fwd_pre.hip) and its output pass
 // (chunk-start states -> o, o~, gdn_fwd_out.hip)
 hipError_t launch_fwd_pre_d128(const FwdArgs &a, const float *cmat, float *pack, hipStream_t st, int64_t slots);
+// both in one pass: the chunk matrices into `cmat` and the hand-over into
+// `pack` from one load of the chunk (gdn_fwd_prep.hip)
+hipError_t launch_fwd_prep_d128(const FwdArgs &a, float *cmat, float *pack, hipStream_t st, int64_t slots);
 hipError_t launch_fwd_out_d128(const FwdArgs &a, const float *cmat, const float *states, hipStream_t st,
                                int64_t slots);
 

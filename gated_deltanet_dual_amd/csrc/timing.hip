@@ -16,7 +16,7 @@ const char *const kNames[K_COUNT] = {"gdn_dual_fwd_kernel", "gdn_bwd_scan_kernel
                                      "gdn_bwd_chunk_kernel", "block_step_kernel",
                                      "shortconv_dual_kernel", "gdn_tri_kernel", "gdn_bwd_pre_kernel",
                                      "gdn_fwd_pre_kernel", "gdn_fwd_scan_kernel", "shortconv_dual_bwd_kernel",
-                                     "gdn_scatter_kernel"};
+                                     "gdn_scatter_kernel", "gdn_fwd_prep_kernel"};
 std::atomic<int> g_on{0};
 std::mutex g_mu;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_rec[K_COUNT];
