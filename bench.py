@@ -606,8 +606,10 @@ def bench_packed_layer(torch, g, wl, dev, timer, up, args):
     32 heads x 128, W=4, bf16): ShortConv on q, k, v of both streams, q/k L2
     norm, dual GDN.  Unfused: three flare_shortconv_dual calls, then the GDN
     forward with its q/k L2 flag.  Fused: flare_qkv_prologue, then the GDN
-    forward without flags.  Training: the fused forward with chunk-start
-    states, the GDN backward and the prologue's reverse mode."""
+    forward without flags.  Conv in the loads: flare_gdn_dual_fwd_conv, the
+    ShortConv formed where the GDN kernels load their rows (no rows written).
+    Training: the fused forward with chunk-start states, the GDN backward and
+    the prologue's reverse mode."""
     log("bench: packed layer (32768 tokens, 8 docs, 32 heads x 128, ShortConv W=4 + L2 + dual GDN)")
     bf = torch.bfloat16
     p = wl.packed_conv(round_io=False)
@@ -641,9 +643,13 @@ def bench_packed_layer(torch, g, wl, dev, timer, up, args):
         g.qkv_prologue(vl, B, d, xs, xns, ws_, out=(ys, yns))
         g.gdn_dual_fwd(vl, *gdn_args(*ys, *yns), B, out=(o, on), want_h_final=False, workspace=fws)
 
+    def conv_in_load():  # the ShortConv formed where the GDN kernels load q, k, v: no rows written
+        g.gdn_dual_fwd_conv(vl, xs, xns, ws_, *gates, B, activation=0, flags=g.QK_L2NORM, out=(o, on),
+                            want_h_final=False, workspace=fws)
+
     n = max(args.steps // 2, 3)
     res = {}
-    for name, fn in (("unfused_fwd", unfused), ("fused_fwd", fused)):
+    for name, fn in (("unfused_fwd", unfused), ("fused_fwd", fused), ("conv_in_load_fwd", conv_in_load)):
         for _ in range(max(args.warmup, 1)):
             fn()
         torch.cuda.synchronize()
@@ -687,6 +693,10 @@ def bench_packed_layer(torch, g, wl, dev, timer, up, args):
     for k, ms in res.items():
         out[k] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
     out["fused_speedup_fwd"] = res["unfused_fwd"] / res["fused_fwd"]
+    out["conv_in_load_speedup_fwd"] = res["unfused_fwd"] / res["conv_in_load_fwd"]
+    # one pass of the projections: x (all rows) and x~ (response rows) read, o, o~ written
+    n_resp = int(sum(p["cu_seqlens"][i + 1] - p["cu_seqlens"][i] - p["prompt_lens"][i] for i in range(vl.num_docs)))
+    out["conv_in_load_fwd"]["layer_io_bytes"] = 3 * H * d * 2 * (T + n_resp) + 2 * H * d * 2 * (T + n_resp)
     return out
 
 

@@ -17,7 +17,7 @@ import os
 import numpy as np
 
 __all__ = ["Varlen", "GDNShape", "FlareError", "lib", "gdn_dual_fwd", "gdn_dual_fwd_pool", "gdn_dual_fwd_route1", "gdn_dual_bwd",
-           "block_step", "block_step_conv", "conv_cache_fill", "gdn_verify", "gdn_scatter", "gdn_verify_outputs", "gdn_commit_prefix", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
+           "gdn_dual_fwd_conv", "block_step", "block_step_conv", "conv_cache_fill", "gdn_verify", "gdn_scatter", "gdn_verify_outputs", "gdn_commit_prefix", "shortconv_dual", "shortconv_dual_bwd", "shortconv_dual_bwd_workspace_bytes", "qkv_prologue",
            "qkv_prologue_bwd", "qkv_prologue_bwd_workspace_bytes", "chunk_size", "ckpt_slots", "EVAL", "COMMIT",
            "QK_L2NORM", "F32", "BF16"]
 
@@ -81,6 +81,8 @@ def lib():
     L.flare_gdn_ckpt_slot.restype = ctypes.c_int64
     L.flare_gdn_dual_fwd.argtypes = [VP, SP] + [P] * 10 + [P, P, P, P, P, I32, P, SZ, P]
     L.flare_gdn_dual_fwd.restype = ctypes.c_int
+    L.flare_gdn_dual_fwd_conv.argtypes = [VP, SP, I32, A3, I32, A3, A3] + [P] * 4 + [P, P, P, P, P, I32, P, SZ, P]
+    L.flare_gdn_dual_fwd_conv.restype = ctypes.c_int
     L.flare_gdn_dual_bwd.argtypes = [VP, SP] + [P] * 10 + [P, P, I32, P, P, P, P] + [P] * 11 + [P, SZ, P]
     L.flare_gdn_dual_bwd.restype = ctypes.c_int
     L.flare_gdn_block_step.argtypes = [I32, P, P, P, I32, SP, P, P, P, P, P, P, I32, P]
@@ -402,6 +404,53 @@ def gdn_dual_fwd(varlen: Varlen, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta
                                     _ptr(alpha_n), _ptr(beta_n), _ptr(h0), _ptr(o), _ptr(on),
                                     _ptr(hf), _ptr(ck), int(ckpt_stride), _ptr(workspace),
                                     ws_bytes if workspace is not None else 0, _stream(q.device)))
+    return o, on, hf, ck
+
+
+def gdn_dual_fwd_conv(varlen: Varlen, xs, xns, weights, alpha, beta, alpha_n, beta_n, block_size, activation=1,
+                      h0=None, scale=0.0, flags=0, want_h_final=True, want_ckpt=False, out=None, ckpt=None,
+                      workspace=None, ckpt_stride=1, window=0):
+    """The dual-stream forward with the layer's ShortConv in its loads: xs,
+    xns are the clean and noisy q, k, v projections (three [T, H*128] bf16
+    tensors each), weights three [H*128, W] fp32 (W <= 4), SiLU when
+    activation = 1; flags = QK_L2NORM normalises the q, k rows after the
+    convolution.  Same results as qkv_prologue(..., qk_l2norm=False) followed
+    by gdn_dual_fwd.  Returns (o, on, h_final, ckpt)."""
+    torch = _torch()
+    T, C, W, dev = _chk_prologue_inputs(varlen, xs, xns, weights)
+    d = 128
+    if C % d != 0:
+        _fail("the projections must hold whole heads of 128 channels (got %d channels)" % C)
+    H = C // d
+    iot = _io_dtype_of(xs[0], "xs[0]")
+    for name, t in (("alpha", alpha), ("beta", beta), ("alpha_n", alpha_n), ("beta_n", beta_n)):
+        _chk(t, name, (T, H), torch.float32, dev)
+    _chk(h0, "h0", (varlen.num_docs, H, d, d), torch.float32, dev, optional=True)
+    shp = _shape(H, d, block_size, _io_of(xs[0]), flags, scale)
+    if out is None:
+        o = torch.empty((T, H, d), dtype=iot, device=dev)
+        on = torch.empty((T, H, d), dtype=iot, device=dev)
+    else:
+        o, on = out
+        _chk(o, "o", (T, H, d), iot, dev)
+        _chk(on, "on", (T, H, d), iot, dev)
+    hf = torch.empty((varlen.num_docs, H, d, d), dtype=torch.float32, device=dev) if want_h_final else None
+    ck = ckpt
+    if ck is not None or want_ckpt:
+        nbytes = lib().flare_gdn_dual_ckpt_size(varlen.ref(), ctypes.byref(shp), int(ckpt_stride))
+        if nbytes == 0:
+            raise FlareError(2, "invalid arguments for the checkpoint size")
+        if ck is None:
+            ck = torch.empty((nbytes // (H * d * d * 4), H, d, d), dtype=torch.float32, device=dev)
+        _chk_buf(ck, "ckpt", nbytes, torch.float32, dev)
+    ws_bytes = _ws_bytes(varlen, shp, False, 1, window)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    _chk_buf(workspace, "workspace", ws_bytes, torch.uint8, dev, optional=ws_bytes == 0)
+    _check(lib().flare_gdn_dual_fwd_conv(varlen.ref(), ctypes.byref(shp), W, _a3(weights), int(activation), _a3(xs),
+                                         _a3(xns), _ptr(alpha), _ptr(beta), _ptr(alpha_n), _ptr(beta_n), _ptr(h0),
+                                         _ptr(o), _ptr(on), _ptr(hf), _ptr(ck), int(ckpt_stride), _ptr(workspace),
+                                         ws_bytes if workspace is not None else 0, _stream(dev)))
     return o, on, hf, ck
 
 

@@ -93,24 +93,57 @@ static FwdArgs fwd_args(const flare_varlen *varlen, const flare_gdn_shape *shape
   return a;
 }
 
+// The ShortConv the forward forms its q, k, v rows with (flare_gdn_dual_fwd_conv).
+struct ConvSpec {
+  int width, activation;
+  const void *const *x, *const *xn;
+  const float *const *w;
+};
+
 static flare_status fwd_impl(const flare_varlen *varlen, const flare_gdn_shape *shape, const void *q, const void *k,
                              const void *v, const float *alpha, const float *beta, const void *qn, const void *kn,
                              const void *vn, const float *alpha_n, const float *beta_n, const float *h0, void *o,
                              void *on, float *h_final, const int32_t *state_slot, float *ckpt,
-                             int32_t ckpt_stride_chunks, void *workspace, size_t workspace_bytes, void *stream) {
+                             int32_t ckpt_stride_chunks, void *workspace, size_t workspace_bytes, void *stream,
+                             const ConvSpec *conv = nullptr) {
   VarlenInfo vi;
   flare_status st = check_fwd_common(varlen, shape, &vi);
   if (st != FLARE_OK) return st;
   if (ckpt && ckpt_stride_chunks < 1)
     return fail(FLARE_ERR_SHAPE, "checkpoint stride %d (at least 1)", ckpt_stride_chunks);
-  if (vi.total_tokens > 0 &&
-      (!q || !k || !v || !alpha || !beta || !qn || !kn || !vn || !alpha_n || !beta_n || !o || !on))
+  if (conv) {
+    if (!fwd_uses_chunk_matrices(shape))
+      return fail(FLARE_ERR_UNSUPPORTED, "gdn_dual_fwd_conv: bf16 io at d = 128 only");
+    if (conv->width < 1 || conv->width > 4)
+      return fail(FLARE_ERR_UNSUPPORTED, "gdn_dual_fwd_conv: width %d not in [1, 4]", conv->width);
+    if (conv->activation != 0 && conv->activation != 1)
+      return fail(FLARE_ERR_UNSUPPORTED, "activation %d unknown", conv->activation);
+    if (vi.total_tokens > 0) {
+      if (!conv->x || !conv->xn || !conv->w) return fail(FLARE_ERR_NULL, "gdn_dual_fwd_conv: a pointer array is NULL");
+      for (int i = 0; i < 3; ++i)
+        if (!conv->x[i] || !conv->xn[i] || !conv->w[i])
+          return fail(FLARE_ERR_NULL, "gdn_dual_fwd_conv: projection or weight %d is NULL", i);
+      if (!alpha || !beta || !alpha_n || !beta_n || !o || !on)
+        return fail(FLARE_ERR_NULL, "gdn_dual_fwd_conv: a required pointer is NULL");
+    }
+  } else if (vi.total_tokens > 0 &&
+             (!q || !k || !v || !alpha || !beta || !qn || !kn || !vn || !alpha_n || !beta_n || !o || !on)) {
     return fail(FLARE_ERR_NULL, "gdn_dual_fwd: a required pointer is NULL");
+  }
   if (((uintptr_t)workspace & 255u) != 0)
     return fail(FLARE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   FwdArgs a = fwd_args(varlen, shape, vi, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0, o, on, h_final,
                        ckpt, ckpt_stride_chunks);
   a.state_slot = state_slot;
+  if (conv && vi.total_tokens > 0) {
+    for (int i = 0; i < 3; ++i) {
+      a.cx[i] = conv->x[i];
+      a.cxn[i] = conv->xn[i];
+      a.cwt[i] = conv->w[i];
+    }
+    a.cw = conv->width;
+    a.cact = conv->activation;
+  }
   if (!fwd_uses_chunk_matrices(shape)) {  // the per-(document, head) kernel
     a.workspace = nullptr;
     return hip_status(launch_gdn_fwd(a, (hipStream_t)stream), "gdn_dual_fwd launch");
@@ -156,6 +189,18 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen, const flare_gdn_shap
   clear_error();
   return fwd_impl(varlen, shape, q, k, v, alpha, beta, qn, kn, vn, alpha_n, beta_n, h0, o, on, h_final, nullptr,
                   ckpt, ckpt_stride_chunks, workspace, workspace_bytes, stream);
+}
+
+flare_status flare_gdn_dual_fwd_conv(const flare_varlen *varlen, const flare_gdn_shape *shape, int32_t width,
+                                     const float *const weight[3], int32_t activation, const void *const x[3],
+                                     const void *const xn[3], const float *alpha, const float *beta,
+                                     const float *alpha_n, const float *beta_n, const float *h0, void *o, void *on,
+                                     float *h_final, float *ckpt, int32_t ckpt_stride_chunks, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  clear_error();
+  const ConvSpec cs{width, activation, x, xn, weight};
+  return fwd_impl(varlen, shape, nullptr, nullptr, nullptr, alpha, beta, nullptr, nullptr, nullptr, alpha_n, beta_n,
+                  h0, o, on, h_final, nullptr, ckpt, ckpt_stride_chunks, workspace, workspace_bytes, stream, &cs);
 }
 
 size_t flare_gdn_route1_workspace_size(const flare_varlen *varlen, const flare_gdn_shape *shape) {

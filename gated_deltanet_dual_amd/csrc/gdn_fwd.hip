@@ -739,8 +739,10 @@ hipError_t launch_gdn_fwd(const FwdArgs &a_in, hipStream_t st, const FwdPlan *pl
       p.l2f = reinterpret_cast<float4 *>(reinterpret_cast<char *>(a.workspace) + ((per_bytes + 255) & ~(size_t)255));
     }
     if (a.flags & 1) {
-      hipError_t e = launch_l2_factors(a, p.l2f, st);
-      if (e != hipSuccess) return e;
+      if (a.cw == 0) {  // with the conv loads the preparation pass forms them
+        hipError_t e = launch_l2_factors(a, p.l2f, st);
+        if (e != hipSuccess) return e;
+      }
       a.l2f = p.l2f;
     }
     float *const states = p.states ? p.states : a.ckpt;

@@ -23,7 +23,13 @@
 // L2: the q/k L2 flag folded into per-row factors (gdn_l2.hip): the write
 // strengths arrive folded from the gate load, v and v~ rows are divided by
 // r_k and r_k~, and the rows of o and o~ multiplied by r_q and r_q~.
+// CW > 0: the ShortConv in the loads (conv_load.h): the q, k, q~, k~ rows and
+// the v, v~ rows are formed from the raw projections, two rows of one section
+// and stream per thread; v and v~ are staged in LDS for the slabs.
+#include <type_traits>
+
 #include "bwd_common.h"
+#include "conv_load.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "slab.h"
@@ -42,13 +48,17 @@ struct OutSmem {
   alignas(16) float lg[oC], beta[oC], lgn[oC], betan[oC];
   alignas(16) float fac[4][oC];  // L2: r_q, 1 / r_k, r_q~, 1 / r_k~ of the chunk's rows
 };
+struct OutSmemConv : OutSmem {
+  alignas(16) u16 v[2][oC][oLDX];  // the v, v~ rows formed by the conv loads
+};
 
 }  // namespace
 
-template <bool L2>
+template <bool L2, int CW>
 __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const float *cmat, const float *states) {
   constexpr int C = oC, D = oD, NT = oNT, LDM = oLDM;
-  __shared__ OutSmem sm;
+  using Smem = typename std::conditional<(CW > 0), OutSmemConv, OutSmem>::type;
+  __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
   const int H = f.H;
@@ -69,18 +79,27 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
   const float *const Sc = states + ((size_t)slot * H + h) * D * D;
 
   // ---- every global load first (unconditional, rows clamped into the document)
-  constexpr int RU = D / 8, PU = C * RU, UX = 4 * PU / NT;
+  constexpr int RU = D / 8, PU = C * RU, UX = CW > 0 ? 1 : 4 * PU / NT;
+  constexpr int CWW = CW > 0 ? CW : 1;
   uint4 xr[UX];
+  ConvRows<CWW, 2> cqk, cvr;  // CW: rows 2 (tid / 16 % 16) .. +1 of q / k (by tid / 256), and of v / v~
+  const int csel = tid >> 8, crg = (tid >> 4) & 15, cu16 = tid & 15;
+  if constexpr (CW > 0) {
+    cqk.load(f, csel, t0g, c0, 2 * crg, n, h, cu16, has_noisy);
+  } else {
 #pragma unroll
-  for (int e = 0; e < UX; ++e) {
-    const int u = e * NT + tid;
-    const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
-    xr[e] = *reinterpret_cast<const uint4 *>(px[m] + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu16 * 8);
+    for (int e = 0; e < UX; ++e) {
+      const int u = e * NT + tid;
+      const int m = u / PU, r = u % PU, row = r / RU, cu = r % RU;
+      xr[e] = *reinterpret_cast<const uint4 *>(px[m] + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu * 8);
+    }
   }
   const float *cm = cmat + ((size_t)slot * H + h) * 6 * C * C;
-  float4 cv[3];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) cv[j] = reinterpret_cast<const float4 *>(cm)[j * NT + tid];
+  // three named registers, not an array: an array the compiler leaves
+  // un-unrolled would live in scratch
+  const float4 cv0 = reinterpret_cast<const float4 *>(cm)[tid];
+  const float4 cv1 = reinterpret_cast<const float4 *>(cm)[NT + tid];
+  const float4 cv2 = reinterpret_cast<const float4 *>(cm)[2 * NT + tid];
   const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
   float l2r = 1.f;  // thread tid < 128: factor tid / 32 of row tid % 32
   if (L2 && tid < 4 * C) {
@@ -88,33 +107,67 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     l2r = fr[tid / C];
   }
   u16 rv[2][4], rvn[2][4];
-  gslab_raw<D>(rv, pv, H, h, t0g, c0, n, col0);
-  gslab_raw<D>(rvn, pvn, H, h, t0g, c0, n, col0);
+  if constexpr (CW == 0) {
+    gslab_raw<D>(rv, pv, H, h, t0g, c0, n, col0);
+    gslab_raw<D>(rvn, pvn, H, h, t0g, c0, n, col0);
+  }
   // S_c column slab as B fragments: k-slots of step ks are d_k rows
   // 32 ks + 4 g + e (e < 4) and 32 ks + 16 + 4 g + e - 4
   float xs[4][8];
+  auto load_sc = [&]() {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = 32 * ks + (e < 4 ? g4 + e : 16 + g4 + e - 4);
-      xs[ks][e] = Sc[(size_t)row * D + col0 + cl];
-    }
+      for (int e = 0; e < 8; ++e) {
+        const int row = 32 * ks + (e < 4 ? g4 + e : 16 + g4 + e - 4);
+        xs[ks][e] = Sc[(size_t)row * D + col0 + cl];
+      }
+  };
+  if constexpr (CW == 0) load_sc();
 
   // ---- LDS: rows (masked), chunk matrices, gates
+  if constexpr (CW > 0) {
+    uint4 y[2], yn[2];
+    cqk.rows(c0, 2 * crg, P, B, f.cact != 0, y, yn);
 #pragma unroll
-  for (int e = 0; e < UX; ++e) {
-    const int u = e * NT + tid;
-    const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
-    const int tpos = c0 + row;
-    const bool ok = tpos < n && (m < 2 || tpos >= P);
-    *reinterpret_cast<uint4 *>(&sm.x[m][row][cu16 * 8]) = ok ? xr[e] : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 2; ++i) {
+      const int row = 2 * crg + i, tpos = c0 + row;
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(&sm.x[csel][row][cu16 * 8]) = sel4(tpos < n, y[i], z);
+      *reinterpret_cast<uint4 *>(&sm.x[2 + csel][row][cu16 * 8]) = sel4(tpos < n && tpos >= P, yn[i], z);
+    }
+    // the S_c columns and the v, v~ rows after the q, k rows (their loads
+    // all at once would double the registers live)
+    lds_barrier();
+    load_sc();
+    cvr.load(f, 2, t0g, c0, 2 * crg, n, h, cu16, csel == 1 && has_noisy);
+    uint4 vy[2], vyn[2];
+    cvr.rows(c0, 2 * crg, P, B, f.cact != 0, vy, vyn);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 2 * crg + i, tpos = c0 + row;
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(&sm.v[csel][row][cu16 * 8]) =
+          sel4(csel == 0, sel4(tpos < n, vy[i], z), sel4(tpos < n && tpos >= P, vyn[i], z));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < UX; ++e) {
+      const int u = e * NT + tid;
+      const int m = u / PU, r = u % PU, row = r / RU, cu = r % RU;
+      const int tpos = c0 + row;
+      const bool ok = tpos < n && (m < 2 || tpos >= P);
+      *reinterpret_cast<uint4 *>(&sm.x[m][row][cu * 8]) = ok ? xr[e] : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
+  auto put_cm = [&](int j, const float4 &v) {
     const int u = j * NT + tid, which = u / (C * C / 4), rr = u % (C * C / 4);
-    *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = cv[j];
-  }
+    *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = v;
+  };
+  put_cm(0, cv0);
+  put_cm(1, cv1);
+  put_cm(2, cv2);
+
   if (tid < 4 * C) gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   if (L2 && tid < 4 * C) sm.fac[tid / C][tid & (C - 1)] = (tid / C) & 1 ? (l2r > 0.f ? 1.f / l2r : 0.f) : l2r;
   lds_barrier();
@@ -144,8 +197,21 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
       mma_bf16(QS.t[tr], aq, sh[ks]);
       mma_bf16(QS.t[tr], aq, sl[ks]);
     }
+  // the v, v~ slabs: staged rows (the conv loads, already masked) or the raw loads
+  auto vslab = [&](int m) {
+    Slab sl;
+    if constexpr (CW > 0) {
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sl.t[tr][r] = bf2f(sm.v[m][slab_row(tr, r)][col0 + cl]);
+    } else {
+      sl = slab_mask(m == 0 ? rv : rvn, c0, n, P, m == 1);
+    }
+    return sl;
+  };
   // U = T (v - G K S_c)
-  const Slab V = slab_mask(rv, c0, n, P, false);
+  const Slab V = vslab(0);
   Slab rhs;
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
@@ -191,7 +257,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
       }
     cc_mul<3, false>(RQ, &sm.cc[OC_MQ][0][0], LDM, U);
     cc_mul<3, false>(RK, &sm.cc[OC_MK][0][0], LDM, U);
-    const Slab VN = slab_mask(rvn, c0, n, P, true);
+    const Slab VN = vslab(1);
     Slab rhsn;
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr)
@@ -236,14 +302,23 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
   }
 }
 
+template <int CW>
+static void launch_out_w(const FwdArgs &a, const float *cmat, const float *states, hipStream_t st, int64_t slots) {
+  const dim3 grid((unsigned)(slots * a.H)), block(oNT);
+  if (a.l2f) hipLaunchKernelGGL((gdn_fwd_out_d128_kernel<true, CW>), grid, block, 0, st, a, cmat, states);
+  else hipLaunchKernelGGL((gdn_fwd_out_d128_kernel<false, CW>), grid, block, 0, st, a, cmat, states);
+}
+
 hipError_t launch_fwd_out_d128(const FwdArgs &a, const float *cmat, const float *states, hipStream_t st,
                                int64_t slots) {
-  if (a.l2f)
-    hipLaunchKernelGGL(gdn_fwd_out_d128_kernel<true>, dim3((unsigned)(slots * a.H)), dim3(oNT), 0, st, a, cmat,
-                       states);
-  else
-    hipLaunchKernelGGL(gdn_fwd_out_d128_kernel<false>, dim3((unsigned)(slots * a.H)), dim3(oNT), 0, st, a, cmat,
-                       states);
+  switch (a.cw) {
+    case 0: launch_out_w<0>(a, cmat, states, st, slots); break;
+    case 1: launch_out_w<1>(a, cmat, states, st, slots); break;
+    case 2: launch_out_w<2>(a, cmat, states, st, slots); break;
+    case 3: launch_out_w<3>(a, cmat, states, st, slots); break;
+    case 4: launch_out_w<4>(a, cmat, states, st, slots); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -19,8 +19,14 @@
 // reads k, the gates and the chunk matrices once instead of twice.
 // L2: the q/k L2 flag folded into per-row factors (gdn_l2.hip): the write
 // strengths arrive folded from the gate load, the v rows are divided by r_k.
+// CW > 0: the ShortConv in the loads (conv_load.h): the q, k, q~, k~ rows and
+// the v rows are formed from the raw projections (each thread four rows of one
+// section and both streams, the v rows two at a time), and with the L2 flag
+// this pass also forms the factors from those rows (the same sums as the
+// factor pass) and writes them for the output pass.
 #include "bwd_common.h"
 #include "chunk_common.h"
+#include "conv_load.h"
 #include "device_common.h"
 #include "gemm_lds.h"
 #include "kernels.h"
@@ -37,10 +43,11 @@ struct PrepSmem {
   alignas(16) float tmp[2][16][17];
   alignas(16) float lg[pC], beta[pC], lgn[pC], betan[pC];
   alignas(16) float vsc[pC];  // L2: 1 / r_k of the chunk's rows
+  alignas(16) float fac[4][pC];  // L2 with the conv loads: r_q, r_k, r_q~, r_k~ of the chunk's rows
 };
 }  // namespace
 
-template <bool L2>
+template <bool L2, int CW>
 __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float *cmat, float *pack_all) {
   constexpr int C = pC, D = pD, NT = pNT, LDX = pLDX, LDM = pLDM;
   __shared__ PrepSmem sm;
@@ -64,32 +71,83 @@ __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float
   // ---- every global load first (unconditional, rows clamped into the
   // document): q, k, q~, k~ rows (8 16-byte units per thread), gates, the v
   // columns of this wave's two d_v slabs, the L2 factors
-  constexpr int RU = D / 8, PU = C * RU, UX = 4 * PU / NT;
+  constexpr int RU = D / 8, PU = C * RU, UX = CW > 0 ? 1 : 4 * PU / NT;
+  constexpr int CWW = CW > 0 ? CW : 1;
   uint4 xr[UX];
-#pragma unroll
-  for (int e = 0; e < UX; ++e) {
-    const int u = e * NT + tid;
-    const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
-    xr[e] = *reinterpret_cast<const uint4 *>(px[m] + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu16 * 8);
-  }
-  const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
   u16 rv[2][2][4];
+  ConvRows<CWW, 4> cqk;  // CW: rows 4 (tid / 16 % 8) .. +3 of q (tid < 128) or k, both streams
+  ConvRows<CWW, 2> cvr;  // CW: rows 2 (tid / 16) .. +1 of v
+  const int csec = tid >> 7, crg = (tid >> 4) & 7, cvg = tid >> 4, cu16 = tid & 15;
+  if constexpr (CW > 0) {
+    cqk.load(f, csec, t0g, c0, 4 * crg, n, h, cu16, has_noisy);
+    cvr.load(f, 2, t0g, c0, 2 * cvg, n, h, cu16, false);
+  } else {
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) gslab_raw<D>(rv[sb], pv, H, h, t0g, c0, n, 32 * wave + 16 * sb);
+    for (int e = 0; e < UX; ++e) {
+      const int u = e * NT + tid;
+      const int m = u / PU, r = u % PU, row = r / RU, cu = r % RU;
+      xr[e] = *reinterpret_cast<const uint4 *>(px[m] + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu * 8);
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) gslab_raw<D>(rv[sb], pv, H, h, t0g, c0, n, 32 * wave + 16 * sb);
+  }
+  // the gates (with the conv loads unfolded: this pass forms the factors)
+  FwdArgs fg = f;
+  if (CW > 0) fg.l2f = nullptr;
+  const float graw = tid < 4 * C ? gate_load_raw(fg, t0g, c0, n, h, tid) : 0.f;
   float rkl = 1.f;
-  if (L2 && tid < C) rkl = f.l2f[(t0g + min(c0 + tid, n - 1)) * H + h].y;
+  if (L2 && CW == 0 && tid < C) rkl = f.l2f[(t0g + min(c0 + tid, n - 1)) * H + h].y;
 
   // ---- LDS: zeroed chunk matrices, the masked rows, gates
   for (int e = tid; e < 8 * C * LDM; e += NT) (&sm.at[0][0][0])[e] = 0.f;  // at and tm
+  uint4 yv[2];  // CW: the v rows, kept until the rows' LDS is free
+  if constexpr (CW > 0) {
+    uint4 y[4], yn[4];
+    cqk.rows(c0, 4 * crg, P, B, f.cact != 0, y, yn);
 #pragma unroll
-  for (int e = 0; e < UX; ++e) {
-    const int u = e * NT + tid;
-    const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
-    const int tpos = c0 + row;
-    const bool ok = tpos < n && (m < 2 || tpos >= P);
-    *reinterpret_cast<uint4 *>(&sm.x[m][row][cu16 * 8]) = ok ? xr[e] : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * crg + i, tpos = c0 + row;
+      const uint4 yc = sel4(tpos < n, y[i], make_uint4(0u, 0u, 0u, 0u));
+      const uint4 ynv = sel4(tpos < n && tpos >= P, yn[i], make_uint4(0u, 0u, 0u, 0u));
+      *reinterpret_cast<uint4 *>(&sm.x[csec][row][cu16 * 8]) = yc;
+      *reinterpret_cast<uint4 *>(&sm.x[2 + csec][row][cu16 * 8]) = ynv;
+      if (L2) {  // the row factors, from the same sums as the factor pass
+        const float rc = l2_factor(l2_rowsum16(yc)), rn = l2_factor(l2_rowsum16(ynv));
+        if (cu16 == 0) {
+          sm.fac[csec][row] = rc;
+          sm.fac[2 + csec][row] = rn;
+        }
+      }
+    }
+    uint4 vdum[2];
+    cvr.rows(c0, 2 * cvg, P, B, f.cact != 0, yv, vdum);
+  } else {
+#pragma unroll
+    for (int e = 0; e < UX; ++e) {
+      const int u = e * NT + tid;
+      const int m = u / PU, r = u % PU, row = r / RU, cu = r % RU;
+      const int tpos = c0 + row;
+      const bool ok = tpos < n && (m < 2 || tpos >= P);
+      *reinterpret_cast<uint4 *>(&sm.x[m][row][cu * 8]) = ok ? xr[e] : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
-  if (tid < 4 * C) gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
+  if constexpr (CW > 0 && L2) {
+    lds_barrier();  // the factors: fold them into the write strengths, hand them to the output pass
+    if (tid < C) {
+      rkl = sm.fac[1][tid];
+      if (c0 + tid < n)
+        const_cast<float4 *>(f.l2f)[(t0g + c0 + tid) * H + h] =
+            make_float4(sm.fac[0][tid], sm.fac[1][tid], sm.fac[2][tid], sm.fac[3][tid]);
+    }
+  }
+  if (tid < 4 * C) {
+    float gv = graw;
+    if (CW > 0 && L2 && ((tid / C) & 1)) {  // folded write strengths b r_k^2 (gdn_l2.hip)
+      const float rk = sm.fac[tid / C][tid & (C - 1)];
+      gv *= rk * rk;
+    }
+    gate_scan(gate_fix(gv, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
+  }
   if (L2 && tid < C) sm.vsc[tid] = rkl > 0.f ? 1.f / rkl : 0.f;
   lds_barrier();
 
@@ -164,12 +222,28 @@ __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float
     dst[(2 * tr + 1) * 64 + lane] = __builtin_bit_cast(uint4, wl);
   }
   if (tid == 0) pack[kPackG] = __expf(lgC);
+  if constexpr (CW > 0) {  // the v rows -> the q rows' LDS (every wave is done with them)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 2 * cvg + i;
+      *reinterpret_cast<uint4 *>(&sm.x[0][row][cu16 * 8]) = sel4(c0 + row < n, yv[i], make_uint4(0u, 0u, 0u, 0u));
+    }
+    lds_barrier();
+  }
 
   // ---- Z = diag(D) T V for this wave's two slabs, stored as [slab][tile][lane][4]
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     const int slab = 2 * wave + sb;
-    Slab V = slab_mask(rv[sb], c0, n, P, false);
+    Slab V;
+    if constexpr (CW > 0) {
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) V.t[tr][r] = bf2f(sm.x[0][slab_row(tr, r)][16 * slab + cl]);
+    } else {
+      V = slab_mask(rv[sb], c0, n, P, false);
+    }
     Slab Z = slab_zero();
     if constexpr (L2) {  // v' = v / r_k is no longer exact in bf16: both operands split
 #pragma unroll
@@ -190,13 +264,22 @@ __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float
   }
 }
 
+template <int CW>
+static void launch_prep_w(const FwdArgs &a, float *cmat, float *pack, hipStream_t st, int64_t slots) {
+  const dim3 grid((unsigned)(slots * a.H)), block(pNT);
+  if (a.l2f) hipLaunchKernelGGL((gdn_fwd_prep_d128_kernel<true, CW>), grid, block, 0, st, a, cmat, pack);
+  else hipLaunchKernelGGL((gdn_fwd_prep_d128_kernel<false, CW>), grid, block, 0, st, a, cmat, pack);
+}
+
 hipError_t launch_fwd_prep_d128(const FwdArgs &a, float *cmat, float *pack, hipStream_t st, int64_t slots) {
-  if (a.l2f)
-    hipLaunchKernelGGL(gdn_fwd_prep_d128_kernel<true>, dim3((unsigned)(slots * a.H)), dim3(pNT), 0, st, a, cmat,
-                       pack);
-  else
-    hipLaunchKernelGGL(gdn_fwd_prep_d128_kernel<false>, dim3((unsigned)(slots * a.H)), dim3(pNT), 0, st, a, cmat,
-                       pack);
+  switch (a.cw) {
+    case 0: launch_prep_w<0>(a, cmat, pack, st, slots); break;
+    case 1: launch_prep_w<1>(a, cmat, pack, st, slots); break;
+    case 2: launch_prep_w<2>(a, cmat, pack, st, slots); break;
+    case 3: launch_prep_w<3>(a, cmat, pack, st, slots); break;
+    case 4: launch_prep_w<4>(a, cmat, pack, st, slots); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

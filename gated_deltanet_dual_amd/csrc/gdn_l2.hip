@@ -20,6 +20,7 @@
 //
 // This file holds the factor pass: per (token, head) of the packed batch,
 // {r_q, r_k, r_q~, r_k~} into a float4, one 16-lane group per row and array.
+#include "conv_load.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,17 +35,7 @@ __global__ __launch_bounds__(256) void gdn_l2_factors_kernel(FwdArgs f, float4 *
   const u16 *src = reinterpret_cast<const u16 *>(m == 0 ? f.q : m == 1 ? f.k : m == 2 ? f.qn : f.kn);
   const int64_t r = row < rows ? row : rows - 1;
   const uint4 v = *reinterpret_cast<const uint4 *>(src + r * 128 + lane * 8);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xffff0000u);
-    ss += a * a + b * b;
-  }
-  ss = dpp_sum16(ss);
-  float rf = 1.f / sqrtf(ss + 1e-6f);
-  // rows never read (noisy prompt rows may hold anything): keep the factor finite
-  if (!(rf < 3.0e38f)) rf = 0.f;
+  const float rf = l2_factor(l2_rowsum16(v));
   if (lane == 0 && row < rows) reinterpret_cast<float *>(out + row)[m] = rf;
 }
 

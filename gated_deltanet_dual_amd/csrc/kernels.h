@@ -68,6 +68,15 @@ struct FwdArgs {
   // those, at slot doc * win_len + (c - win_lo); win_len = 0: every chunk, at
   // its checkpoint slot of stride 1.
   int win_lo, win_len;
+  // The ShortConv in the loads (cw > 0; chunked forward only): q, k, v and
+  // their noisy twins are not read; every row is formed from the raw
+  // projections cx / cxn ([T, H * 128] bf16: q, k, v) by the dual ShortConv
+  // of width cw with weights cwt ([H * 128, cw] fp32) and SiLU when cact
+  // (conv_load.h); with the q/k L2 flag the preparation pass forms the L2
+  // factors from those rows into l2f.
+  const void *cx[3], *cxn[3];
+  const float *cwt[3];
+  int cw, cact;
 };
 // Where the chunked forward (bf16 io, d = 128) keeps its per-chunk buffers
 // and how it walks the chunks: one pass (win = 0) or windows of win chunks of

@@ -180,6 +180,35 @@ flare_status flare_gdn_dual_fwd(const flare_varlen *varlen,
                                 int32_t ckpt_stride_chunks, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* The same forward with the layer's ShortConv in its loads (Key designs items
+ * 2 and 3: the dual ShortConv in front of the GDN layer, fused): q, k, v and
+ * their noisy twins are never read or written.  Every row is formed, where the
+ * chunked kernels load it, from the raw projections by the dual ShortConv of
+ * flare_qkv_prologue (a noisy tap before the start of its block reads the
+ * clean projection, taps before the document start read zero, noisy prompt
+ * rows are zero), then SiLU when activation = 1, then rounded to bf16.
+ *   width       1..4
+ *   weight[3]   fp32 [H * d, width] for q, k, v (tap width - 1 on the current
+ *               token), no bias
+ *   x[3], xn[3] bf16 [T, H * d] clean and noisy projections of q, k, v
+ *               (prompt rows of xn never read)
+ * shape->flags = FLARE_QK_L2NORM normalises the q and k rows after the
+ * convolution.  The result equals flare_qkv_prologue(..., qk_l2norm = 0)
+ * followed by flare_gdn_dual_fwd with the same shape, bit for bit.  bf16 io at
+ * d = 128 only (FLARE_ERR_UNSUPPORTED otherwise).  All other arguments,
+ * checkpoints and the workspace (one pass or windows) as flare_gdn_dual_fwd. */
+flare_status flare_gdn_dual_fwd_conv(const flare_varlen *varlen,
+                                     const flare_gdn_shape *shape, int32_t width,
+                                     const float *const weight[3],
+                                     int32_t activation, const void *const x[3],
+                                     const void *const xn[3], const float *alpha,
+                                     const float *beta, const float *alpha_n,
+                                     const float *beta_n, const float *h0,
+                                     void *o, void *on, float *h_final,
+                                     float *ckpt, int32_t ckpt_stride_chunks,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 /* The chunk-then-refine route for the same forward (Key designs item 2 and
  * the pages' comparison of the two ways to give every noisy block its clean
  * boundary state): the clean stream with its chunk-start states (ckpt,
