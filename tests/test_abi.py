@@ -424,3 +424,25 @@ def test_strided_checkpoints_and_windows_sizes(L):
     st = L.flare_gdn_dual_fwd_pool(ctypes.byref(v), ctypes.byref(shape), *P, FAKE, host.ctypes.data, FAKE, N, 1,
                                    FAKE, FAKE, None, 1, FAKE, wsw(0, 1, 4), None)
     assert st == 5 and b"one pass" in L.flare_last_error()
+
+
+def test_fwd_conv_validation(L):
+    """flare_gdn_dual_fwd_conv refuses what it does not serve before launching:
+    widths outside 1..4, unknown activations, shapes without the chunked path,
+    missing projections or weights, a workspace below one chunk's window."""
+    v = varlen([0, 100, 164], [20, 0])
+    shape = g.GDNShape(4, 128, 128, 4, g.BF16, 0, 0.0)
+    A3 = ctypes.c_void_p * 3
+    full = A3(FAKE, FAKE, FAKE)
+    hole = A3(FAKE, None, FAKE)
+
+    def call(sh=shape, width=4, act=1, x=full, xn=full, w=full, ws_bytes=1 << 34):
+        return L.flare_gdn_dual_fwd_conv(ctypes.byref(v), ctypes.byref(sh), width, w, act, x, xn, FAKE, FAKE, FAKE,
+                                         FAKE, None, FAKE, FAKE, None, None, 1, FAKE, ws_bytes, None)
+
+    assert call(width=0) == 4 and call(width=5) == 4
+    assert call(act=2) == 4
+    assert call(sh=g.GDNShape(4, 16, 16, 4, g.F32, 0, 0.0)) == 4
+    assert call(x=hole) == 1 and call(xn=hole) == 1 and call(w=hole) == 1
+    w1 = L.flare_gdn_dual_workspace_size_window(ctypes.byref(v), ctypes.byref(shape), 0, 1, 1)
+    assert call(ws_bytes=w1 - 1) == 5
