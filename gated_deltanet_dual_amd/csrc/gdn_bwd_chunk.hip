@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const uint4 v = *reinterpret_cast<const uint4 *>(src + ((t0g + min(tpos, n - 1)) * H + h) * D + cu16 * 8);
     xr[e] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
   }
-  const float gval = tid < 4 * C ? gate_load(f, t0g, c0, n, P, h, tid) : 0.f;
+  // the gate value raw (no use yet, so no wait on the loads issued before it)
+  const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
   float l2r = 1.f;  // L2, thread tid < 128: factor tid / 32 of row tid % 32
   if (L2 && tid < 4 * C) {
     const float *fr = reinterpret_cast<const float *>(f.l2f + (t0g + min(c0 + (tid & (C - 1)), n - 1)) * H + h);
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       sm.cq[qt][1][col + e][row] = lb[e];
     }
   }
+  const float gval = gate_fix(graw, c0, n, P, tid);
   if (tid < 4 * C) gate_scan(gval, B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   if (tid < C) sm.alpha[0][tid] = gval;
   else if (tid >= 2 * C && tid < 3 * C) sm.alpha[1][tid - 2 * C] = gval;
