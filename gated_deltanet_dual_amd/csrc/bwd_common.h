@@ -121,7 +121,7 @@ __device__ __forceinline__ void gate_scan(float val, int B, int tid, float *lg, 
     } else {
       for (int off = 1; off < B; off <<= 1) {
         const float y = __shfl_up(la, off, B);
-        if ((i % B) >= off) la += y;
+        if ((i & (B - 1)) >= off) la += y;
       }
       lgn[i] = la;
     }
@@ -155,7 +155,7 @@ __device__ __forceinline__ void load_gates(const FwdArgs &f, int64_t t0g, int c0
       } else {
         for (int off = 1; off < B; off <<= 1) {
           const float y = __shfl_up(la, off, B);
-          if ((i % B) >= off) la += y;
+          if ((i & (B - 1)) >= off) la += y;
         }
         lgn[i] = la;
       }
@@ -217,7 +217,7 @@ __device__ __forceinline__ void chunk_grams(IO (*x)[32][LDX], float (*cc)[32][LD
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       gemm_tile<BF, D, XL, XL>(acc, &x[1][0][0], LDX, 16 * tj, &x[xm][0][0], LDX, 16 * ti);
       const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-      const int pi = i - (i % B);
+      const int pi = (i & -B);
       const bool resp = c0 + i < n && c0 + i >= P;
       const float lgp = pi > 0 ? lg[pi - 1] : 0.f;
       float o4[4];
@@ -237,7 +237,7 @@ __device__ __forceinline__ void chunk_grams(IO (*x)[32][LDX], float (*cc)[32][LD
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
         gemm_tile<BF, D, XL, XL>(acc, &x[3][0][0], LDX, 16 * tj, &x[2][0][0], LDX, 16 * ti);
         const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-        const int pi = i - (i % B);
+        const int pi = (i & -B);
         const bool resp = c0 + i < n && c0 + i >= P;
         const float lge = lgn[pi + B - 1];
         float o4[4];
@@ -257,14 +257,14 @@ __device__ __forceinline__ void chunk_grams(IO (*x)[32][LDX], float (*cc)[32][LD
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
         gemm_tile<BF, D, XL, XL>(acc, &x[3][0][0], LDX, 16 * ti, &x[3][0][0], LDX, 16 * tj);
         const int j = 16 * tj + cl;
-        const int pj = j - (j % B);
+        const int pj = (j & -B);
         const float wj = fold_w ? betan[j] : 1.f;
         float o4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * ti + g4 + r;
           const bool resp = c0 + i < n && c0 + i >= P;
-          o4[r] = (resp && j < i && i - (i % B) == pj) ? acc[r] * __expf(lgn[i] - lgn[j]) * wj : 0.f;
+          o4[r] = (resp && j < i && (i & -B) == pj) ? acc[r] * __expf(lgn[i] - lgn[j]) * wj : 0.f;
         }
         *reinterpret_cast<float4 *>(&cc[CC_ANT][j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
       }
@@ -326,13 +326,13 @@ __device__ __forceinline__ void gram_ant(const u16 (*kn)[LDX], float (*at)[LDM],
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     gemm_tile<true, D, RowU16, RowU16>(acc, &kn[0][0], LDX, 16 * ti, &kn[0][0], LDX, 16 * tj);
     const int j = 16 * tj + cl;
-    const int pj = j - (j % B);
+    const int pj = (j & -B);
     float o4[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * ti + g4 + r;
       const bool resp = c0 + i < n && c0 + i >= P;
-      o4[r] = (resp && j < i && i - (i % B) == pj) ? acc[r] * __expf(lgn[i] - lgn[j]) : 0.f;
+      o4[r] = (resp && j < i && (i & -B) == pj) ? acc[r] * __expf(lgn[i] - lgn[j]) : 0.f;
     }
     *reinterpret_cast<float4 *>(&at[j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
@@ -377,7 +377,7 @@ __device__ __forceinline__ void grams_weighted(int wave, const u16 (*x)[32][LDX]
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     gemm_tile<true, D, RowU16, RowU16>(acc, &x[1][0][0], LDX, 16 * tj, &x[xm][0][0], LDX, 16 * ti);
     const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-    const int pi = i - (i % B);
+    const int pi = (i & -B);
     const bool resp = c0 + i < n && c0 + i >= P;
     const float lgp = pi > 0 ? lg[pi - 1] : 0.f;
     float o4[4];
@@ -397,7 +397,7 @@ __device__ __forceinline__ void grams_weighted(int wave, const u16 (*x)[32][LDX]
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       gemm_tile<true, D, RowU16, RowU16>(acc, &x[3][0][0], LDX, 16 * tj, &x[2][0][0], LDX, 16 * ti);
       const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-      const int pi = i - (i % B);
+      const int pi = (i & -B);
       const bool resp = c0 + i < n && c0 + i >= P;
       const float lge = lgn[pi + B - 1];
       float o4[4];

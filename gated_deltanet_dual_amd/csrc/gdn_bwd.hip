@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_scan_kernel(BwdArgs a) {
   const int64_t t0g = f.cu[doc];
   const int n = f.cu[doc + 1] - f.cu[doc];
   const int P = f.plen[doc];
-  const int B = f.B;
+  const int B = f.B;  // a power of two up to 32 (checked by the host): i % B = i & (B - 1)
   const int nchunks = (n + C - 1) / C;
   const int dv0 = tile * DV;
   const float s = f.scale;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_scan_kernel(BwdArgs a) {
     } else if (wave == 2 && has_noisy) {
       for (int e = lane; e < C * DV; e += 64) {
         const int i = e / DV, col = e % DV;
-        const int pi = i - (i % B);
+        const int pi = (i & -B);
         const float drq = s * __expf(sm.lgn[pi + B - 1]) * sm.dob[1][i][col];
         sm.vec[V_DRQ][i][col] = drq;
         sm.vec[V_Y2][i][col] = (pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f) * drq;
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * tr + g4 + r;
-            const int pi = i - (i % B);
+            const int pi = (i & -B);
             const float drk = -__expf(sm.lgn[i]) * acc[r];
             sm.vec[V_DRK][i][16 * tc + cl] = drk;
             sm.vec[V_Y3][i][16 * tc + cl] = (pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f) * drk;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_kernel(BwdArgs a) {
   const int c = slot - (int)(t0g / C) - doc;
   if (c < 0 || c * C >= n) return;
   const int P = f.plen[doc];
-  const int B = f.B;
+  const int B = f.B;  // a power of two up to 32 (checked by the host): i % B = i & (B - 1)
   const int c0 = c * C;
   const bool has_noisy = (c0 + C > P) && (P < n);
   const float s = f.scale;
@@ -382,8 +382,8 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_kernel(BwdArgs a) {
     solve_unit_lower<LDM>(&sm.cc[CC_ANT][0][0], &sm.cc[CC_TN][0][0], &sm.tmp[1][0][0], B > 16, sm.betan);
 
   const float lgC = sm.lg[C - 1];
-  auto Gp = [&](int i) { const int pi = i - (i % B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
-  auto Ge = [&](int i) { const int pi = i - (i % B); return __expf(sm.lgn[pi + B - 1]); };
+  auto Gp = [&](int i) { const int pi = (i & -B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
+  auto Ge = [&](int i) { const int pi = (i & -B); return __expf(sm.lgn[pi + B - 1]); };
   auto Dd = [&](int i) { return sm.beta[i] * __expf(lgC - sm.lg[i]); };
   auto resp_row = [&](int i) { return c0 + i < n && c0 + i >= P; };
 
@@ -702,15 +702,15 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_kernel(BwdArgs a) {
         if (m == DM_O) { ei = sm.lg[i]; mask = j <= i; }
         else if (m == DM_A) { ei = sm.lg[i]; mask = j < i; }
         else if (m == DM_Q || m == DM_K) {
-          const int pi = i - (i % B);
+          const int pi = (i & -B);
           ei = pi > 0 ? sm.lg[pi - 1] : 0.f;
           mask = resp_row(i) && j < pi;
         } else if (m == DM_N) {
-          const int pi = i - (i % B);
+          const int pi = (i & -B);
           ei = sm.lgn[pi + B - 1];
           mask = resp_row(i) && j >= pi && j < pi + B;
         } else {
-          const int pi = i - (i % B);
+          const int pi = (i & -B);
           ei = sm.lgn[i];
           mask = resp_row(i) && j < i && j >= pi;
         }
@@ -806,7 +806,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_kernel(BwdArgs a) {
   // sum of d gamma and d a = d log a / a
   if (tid == 0) {
     for (int i = 0; i < C; ++i) {
-      const int pi = i - (i % B);
+      const int pi = (i & -B);
       for (int w = 0; w < 4; ++w) {
         if (pi > 0) sm.pg[0][pi - 1] += sm.pgp[w][i];
         sm.pgn[0][pi + B - 1] += sm.pge[w][i];
@@ -827,7 +827,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_kernel(BwdArgs a) {
       }
       db = sm.pb[0][i] + sm.pb[1][i] + sm.pb[2][i] + sm.pb[3][i];
     } else {
-      const int end = i - (i % B) + B;
+      const int end = (i & -B) + B;
       for (int m = i; m < end; ++m) dg += sm.pgn[0][m] + sm.pgn[1][m] + sm.pgn[2][m] + sm.pgn[3][m];
       db = sm.pbn[0][i] + sm.pbn[1][i] + sm.pbn[2][i] + sm.pbn[3][i];
     }

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   const int64_t t0g = f.cu[doc];
   const int n = f.cu[doc + 1] - f.cu[doc];
   const int P = f.plen[doc];
-  const int B = f.B;
+  const int B = f.B;  // a power of two up to 32 (checked by the host): i % B = i & (B - 1)
   const int c0 = c * C;
   const bool has_noisy = (c0 + C > P) && (P < n);
   const float s = f.scale;
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
 
   const float lgC = sm.lg[C - 1];
   if (tid < C) {  // the gate factor table, visible after the next barrier
-    const int i = tid, pi = i - (i % B);
+    const int i = tid, pi = (i & -B);
     const float ec = __expf(lgC - sm.lg[i]);
     sm.gf[GF_M][i] = __expf(sm.lg[i]);
     sm.gf[GF_P][i] = pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f;
@@ -661,15 +661,15 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       if (m == DM_O) { ei = sm.lg[i]; mask = j <= i; }
       else if (m == DM_A) { ei = sm.lg[i]; mask = j < i; }
       else if (m == DM_Q || m == DM_K) {
-        const int pi = i - (i % B);
+        const int pi = (i & -B);
         ei = pi > 0 ? sm.lg[pi - 1] : 0.f;
         mask = resp_row(i) && j < pi;
       } else if (m == DM_N) {
-        const int pi = i - (i % B);
+        const int pi = (i & -B);
         ei = sm.lgn[pi + B - 1];
         mask = resp_row(i) && j >= pi && j < pi + B;
       } else {
-        const int pi = i - (i % B);
+        const int pi = (i & -B);
         ei = sm.lgn[i];
         mask = resp_row(i) && j < i && j >= pi;
       }
@@ -836,7 +836,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   if (wave == 0) {
     const int i = lane & (C - 1);
     const bool noisy = lane >= C;
-    const int ib = i % B;
+    const int ib = i & (B - 1);
     // per-block sums of the block-start reads (clean) / block-end reads (noisy):
     // segmented inclusive prefix over the rows of each block, total at its last row
     float bs = noisy ? sm.tot[P_GE][i] : sm.tot[P_GP][i];

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
   const int64_t t0g = f.cu[doc];
   const int n = f.cu[doc + 1] - f.cu[doc];
   const int P = f.plen[doc];
-  const int B = f.B;
+  const int B = f.B;  // a power of two up to 32 (checked by the host): i % B = i & (B - 1)
   const int c0 = c * C;
   const bool has_noisy = (c0 + C > P) && (P < n);
   const float s = f.scale;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
 
   // ---- the state-independent chain of this wave's slab
   auto Gm = [&](int i) { return __expf(sm.lg[i]); };
-  auto Gp = [&](int i) { const int pi = i - (i % B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
+  auto Gp = [&](int i) { const int pi = (i & -B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
   Slab DO = slab_mask(rdo, c0, n, P, false), DON = slab_mask(rdon, c0, n, P, true);
   if constexpr (L2) {
 #pragma unroll
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = slab_row(tr, r), pi = i - (i % B);
+        const int i = slab_row(tr, r), pi = (i & -B);
         dun.t[tr][r] *= s;
         DRQ.t[tr][r] = s * __expf(sm.lgn[pi + B - 1]) * DON.t[tr][r];
         Y2.t[tr][r] = Gp(i) * DRQ.t[tr][r];

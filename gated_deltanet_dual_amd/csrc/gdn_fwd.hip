@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
   const int64_t t0g = a.cu[doc];
   const int n = a.cu[doc + 1] - a.cu[doc];
   const int P = a.plen[doc];
-  const int B = a.B;
+  const int B = a.B;  // a power of two up to 32 (checked by the host): i % B = i & (B - 1)
   const int nchunks = (n + C - 1) / C;
   const int dv0 = tile * DV;
   const float scale = a.scale;
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
           // segmented scan inside blocks of B tokens (blocks are B-aligned in the chunk)
           for (int off = 1; off < B; off <<= 1) {
             const float y = __shfl_up(la, off, B);
-            if ((i % B) >= off) la += y;
+            if ((i & (B - 1)) >= off) la += y;
           }
           sm.lgn[i] = la;
         }
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
         mma_frags(acc, kf, tj, xf, ti);
         const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-        const int pi = i - (i % B);
+        const int pi = (i & -B);
         const bool resp = c0 + i < n && c0 + i >= P;
         const float lgp = pi > 0 ? sm.lg[pi - 1] : 0.f;
         const float ni = sm.nrm[xm][i];
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
           mma_frags(acc, knf, tj, xf, ti);
           const int i = 16 * ti + cl, j0 = 16 * tj + g4;
-          const int pi = i - (i % B);
+          const int pi = (i & -B);
           const bool resp = c0 + i < n && c0 + i >= P;
           const float lge = sm.lgn[pi + B - 1], ni = sm.nrm[2][i];
           float o4[4];
@@ -568,14 +568,14 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
           mma_frags(acc, xf, ti, xf, tj);
           const int j = 16 * tj + cl;
-          const int pj = j - (j % B);
+          const int pj = (j & -B);
           const float lgj = sm.lgn[j], bj = sm.betan[j] * sm.nrm[3][j];
           float o4[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * ti + g4 + r;
             const bool resp = c0 + i < n && c0 + i >= P;
-            o4[r] = (resp && j < i && i - (i % B) == pj) ? acc[r] * sm.nrm[3][i] * fast_exp(sm.lgn[i] - lgj) * bj : 0.f;
+            o4[r] = (resp && j < i && (i & -B) == pj) ? acc[r] * sm.nrm[3][i] * fast_exp(sm.lgn[i] - lgj) * bj : 0.f;
           }
           *reinterpret_cast<float4 *>(&sm.cc[CC_ANT][j][16 * ti + g4]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
         }
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int tok = 16 * tr + g4 + r;
-            const int pt = tok - (tok % B);
+            const int pt = (tok & -B);
             acc[r] *= sm.nrm[xm][tok] * (pt > 0 ? fast_exp(sm.lg[pt - 1]) : 1.f);
           }
           xs[tr][tc] = acc;
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(256) void gdn_dual_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * tr + g4 + r;
-            acc[r] *= fast_exp(sm.lgn[i - (i % B) + B - 1]);
+            acc[r] *= fast_exp(sm.lgn[(i & -B) + B - 1]);
           }
           mm_ff<BF, C, 3>(acc, &sm.cc[CC_MN][0][0], LDM, 16 * tr, &sm.vt[VT_UN][0][0], LDM, 16 * tc);
           const int dv = 16 * tc + cl;

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
   const int64_t t0g = f.cu[doc];
   const int n = f.cu[doc + 1] - f.cu[doc];
   const int P = f.plen[doc];
-  const int B = f.B;
+  const int B = f.B;  // a power of two up to 32 (checked by the host): i % B = i & (B - 1)
   const int c0 = c * C;
   const bool has_noisy = (c0 + C > P) && (P < n);
   const float s = f.scale;
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     return __builtin_bit_cast(bf16x8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
   };
   auto Gm = [&](int i) { return __expf(sm.lg[i]); };
-  auto Gp = [&](int i) { const int pi = i - (i % B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
+  auto Gp = [&](int i) { const int pi = (i & -B); return pi > 0 ? __expf(sm.lg[pi - 1]) : 1.f; };
 
   bf16x8 sh[4], sl[4];
 #pragma unroll
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = slab_row(tr, r), pi = i - (i % B);
+        const int i = slab_row(tr, r), pi = (i & -B);
         const bool resp = c0 + i < n && c0 + i >= P;
         ON.t[tr][r] = resp ? s * (__expf(sm.lgn[pi + B - 1]) * RQ.t[tr][r] + ON.t[tr][r]) : 0.f;
         if constexpr (L2) ON.t[tr][r] = resp ? ON.t[tr][r] * sm.fac[2][i] : 0.f;

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const 
   const int64_t t0g = f.cu[doc];
   const int n = f.cu[doc + 1] - f.cu[doc];
   const int P = f.plen[doc];
-  const int B = f.B;
+  const int B = f.B;  // a power of two up to 32 (checked by the host): i % B = i & (B - 1)
   const int c0 = c * C;
   const int col0 = 16 * wave;
   const u16 *const pk = reinterpret_cast<const u16 *>(f.k), *const pv = reinterpret_cast<const u16 *>(f.v);

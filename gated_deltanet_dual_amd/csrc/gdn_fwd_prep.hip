@@ -60,7 +60,7 @@ __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float
   const int64_t t0g = f.cu[doc];
   const int n = f.cu[doc + 1] - f.cu[doc];
   const int P = f.plen[doc];
-  const int B = f.B;
+  const int B = f.B;  // a power of two up to 32 (checked by the host): i % B = i & (B - 1)
   const int c0 = c * C;
   const bool has_noisy = (c0 + C > P) && (P < n);
   const u16 *const px[4] = {reinterpret_cast<const u16 *>(f.q), reinterpret_cast<const u16 *>(f.k),

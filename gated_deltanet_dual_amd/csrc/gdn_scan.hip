@@ -145,12 +145,20 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
   // step i handles chunk at(i)
   auto at = [&](int i) { return REVERSE ? c_hi - 1 - i : c_lo + i; };
 
-  // ---- the store wave: after each chunk's barrier, the carried slabs the
-  // compute waves staged for that chunk -> global, row-major [d_k][d_v], as
-  // 16-byte stores.  Its stores never hold up the compute waves' loads (each
-  // wave's memory counter is in order).  Same barrier count as the compute
-  // waves: one per chunk.
+  // The step order (measured per direction): the forward scan stages the
+  // carried X for the store wave and publishes the chunk's shared operands
+  // before each step's barrier; the reverse scan (LAG) does both after it,
+  // during the step's products, with the store wave one chunk behind.
+  constexpr bool LAG = REVERSE;
+
+  // ---- the store wave: after barrier i (LAG: i + 1) the carried slabs the
+  // compute waves staged for step i (chunk at(i), staging parity i & 1) ->
+  // global, row-major [d_k][d_v], as 16-byte stores.  Its stores never hold
+  // up the compute waves' loads (each wave's memory counter is in order).
+  // Same barrier count as the compute waves: one per step (LAG: and one
+  // after the last).
   if (wave == sNW) {
+    if constexpr (LAG) lds_barrier();
     for (int i = 0; i < nchunks; ++i) {
       const int c = at(i);
       lds_barrier();
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
         for (int j = 0; j < 8; ++j) {
           const int u = j * 64 + lane, row = u >> 2, c4 = u & 3;
           const size_t off = (size_t)row * D + 16 * (sNW * quarter + w) + 4 * c4;
-          const float4 v4 = *reinterpret_cast<const float4 *>(&sm.stage[c & 1][w][row][4 * c4]);
+          const float4 v4 = *reinterpret_cast<const float4 *>(&sm.stage[i & 1][w][row][4 * c4]);
           if (dst) *reinterpret_cast<float4 *>(dst + off) = v4;
           if (dck) *reinterpret_cast<float4 *>(dck + off) = v4;
         }
@@ -222,16 +230,38 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     p.gc = pk[kPackG];
   };
   auto bf = [](const uint4 &v) { return __builtin_bit_cast(bf16x8, v); };
-  // one chunk: stage the carried X for the store wave (it goes to the chunk's
-  // slot), publish this wave's half of the shared operands, then the step;
-  // the ring slot is refilled with chunk `refill` once R is used
-  auto step = [&](ScanRing &p, int c, int refill) {
-    stage_X(c & 1);
-    uint4 (*sh)[64] = sm.sh[c & 1];
+  // this wave's half of a chunk's shared operands -> the LDS area of parity par
+  auto publish = [&](const ScanRing &p, int par) {
+    uint4 (*sh)[64] = sm.sh[par];
 #pragma unroll
     for (int j = 0; j < sSHW; ++j)
       if (j * sNW + wave < sSH) sh[j * sNW + wave][lane] = p.sh[j];
+  };
+  // step i (chunk c = at(i)): after barrier i its shared operands are in
+  // sh[i & 1].  LAG: the carried X is staged for the store wave and the next
+  // chunk's operands (ring slot pn) published while the products run, every
+  // operand fragment read first so those writes never queue ahead of a read
+  // the products wait for.  The ring slot is refilled with chunk `refill`
+  // once R is used.
+  auto step = [&](ScanRing &p, const ScanRing &pn, int i, int refill) {
+    if constexpr (!LAG) {
+      stage_X(i & 1);
+      publish(p, i & 1);
+    }
     lds_barrier();
+    const uint4 (*sh)[64] = sm.sh[i & 1];
+    bf16x8 fka[8], fw[4], fkt[8];
+    if constexpr (LAG) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fka[j] = bf(sh[4 + j][lane]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fw[j] = bf(sh[j][lane]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fkt[j] = bf(sh[12 + j][lane]);
+    }
+    auto KA = [&](int j) { if constexpr (LAG) return fka[j]; else return bf(sh[4 + j][lane]); };
+    auto WF = [&](int j) { if constexpr (LAG) return fw[j]; else return bf(sh[j][lane]); };
+    auto KT = [&](int j) { if constexpr (LAG) return fkt[j]; else return bf(sh[12 + j][lane]); };
     // KX = K X (X from the accumulators: k-slots of step ks are d_k rows
     // 32 ks + 4 g + e (e < 4) and 32 ks + 16 + 4 g + e - 4, split hi + lo)
     Slab KX = slab_zero();
@@ -243,10 +273,14 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
       split8(xv, bh, bl);
 #pragma unroll
       for (int tr = 0; tr < 2; ++tr) {
-        const bf16x8 ak = bf(sh[4 + 2 * ks + tr][lane]);
+        const bf16x8 ak = KA(2 * ks + tr);
         mma_bf16(KX.t[tr], ak, bh);
         mma_bf16(KX.t[tr], ak, bl);
       }
+    }
+    if constexpr (LAG) {
+      stage_X(i & 1);
+      if (i + 1 < nchunks) publish(pn, (i + 1) & 1);
     }
     // Y = W KX
     bf16x8 xh, xl;
@@ -254,7 +288,7 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     Slab Y = slab_zero();
 #pragma unroll
     for (int tr = 0; tr < 2; ++tr) {
-      const bf16x8 wh = bf(sh[2 * tr][lane]), wl = bf(sh[2 * tr + 1][lane]);
+      const bf16x8 wh = WF(2 * tr), wl = WF(2 * tr + 1);
       mma_bf16(Y.t[tr], wh, xh);
       mma_bf16(Y.t[tr], wh, xl);
       mma_bf16(Y.t[tr], wl, xh);
@@ -279,28 +313,31 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
         const float4 rv = __builtin_bit_cast(float4, p.r[kt]);
         X[kt] = p.gc * X[kt] + (homog ? floatx4{0.f, 0.f, 0.f, 0.f} : floatx4{rv.x, rv.y, rv.z, rv.w});
       }
-      mma_bf16(X[kt], bf(sh[12 + kt][lane]), yh);
-      mma_bf16(X[kt], bf(sh[12 + kt][lane]), yl);
+      mma_bf16(X[kt], KT(kt), yh);
+      mma_bf16(X[kt], KT(kt), yl);
     }
     load_ring(p, refill);
   };
 
-  // sRING operand sets in rotation, sRING - 1 chunks in flight while one computes
+  // sRING operand sets in rotation, sRING - 1 chunks in flight while one
+  // computes; LAG: the first chunk's shared operands are published up front
   ScanRing p0, p1, p2, p3;
   static_assert(sRING == 4, "the rotation below names four sets");
   load_ring(p0, at(0));
   load_ring(p1, at(1));
   load_ring(p2, at(2));
   load_ring(p3, at(3));
+  if constexpr (LAG) publish(p0, 0);
   for (int i = 0; i < nchunks; i += 4) {
-    step(p0, at(i), at(i + 4));
+    step(p0, p1, i, at(i + 4));
     if (i + 1 >= nchunks) break;
-    step(p1, at(i + 1), at(i + 5));
+    step(p1, p2, i + 1, at(i + 5));
     if (i + 2 >= nchunks) break;
-    step(p2, at(i + 2), at(i + 6));
+    step(p2, p3, i + 2, at(i + 6));
     if (i + 3 >= nchunks) break;
-    step(p3, at(i + 3), at(i + 7));
+    step(p3, p0, i + 3, at(i + 7));
   }
+  if constexpr (LAG) lds_barrier();  // the last step's staging, for the store wave
   if (a.final_out && write_final) {
     float *dst = a.final_out + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D;
 #pragma unroll
