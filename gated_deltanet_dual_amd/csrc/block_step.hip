@@ -90,6 +90,12 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
   // runs over exactly the tokens before its last block start (possibly none)
   const int cnt = a.count ? min(max(a.count[req], 0), a.B) : a.B;
   const int B = KIND == 2 && a.mode == 3 ? cnt : a.B;
+  // EVAL and COMMIT: B is the block size, a power of two up to 32 (checked by
+  // the host), so dividing by it is a shift; the token-wise writers' window
+  // counts are arbitrary
+  const int lgB = 31 - __clz(B > 0 ? B : 1);
+  auto divB = [&](int x) { return KIND == 2 ? x / B : x >> lgB; };
+  auto modB = [&](int x) { return KIND == 2 ? x % B : x & (B - 1); };
   if (KIND == 1 && cnt == 0) return;  // a COMMIT of no token leaves the state as it is
   const int t = threadIdx.x;
   const int rg = t % NRG, cq = t / NRG;
@@ -151,7 +157,7 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
           in_raw[e] = *reinterpret_cast<const uint4 *>(src + cu * EPU);
         }
       } else if (u < 2 * B * UPR) {  // k and q rows, whole
-        const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
+        const int which = divB(u / UPR), r = modB(u / UPR), cu = u % UPR;
         in_raw[e] = *reinterpret_cast<const uint4 *>((which == 0 ? pk : pq) + ((size_t)trow(r) * a.H + h) * D +
                                                      cu * EPU);
       } else if (u < B * (2 * UPR + UPRV)) {  // v rows, this workgroup's columns
@@ -205,7 +211,7 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
           const int sec = u / (NR * UPR), row = (u / UPR) % NR, cu = u % UPR;
           dst = &sRaw[sec][row][cu * EPU];
         } else if (u < 2 * B * UPR) {
-          const int which = u / (B * UPR), r = (u / UPR) % B, cu = u % UPR;
+          const int which = divB(u / UPR), r = modB(u / UPR), cu = u % UPR;
           dst = which == 0 ? &sX[r][cu * EPU] : &sX[BMAX + r][cu * EPU];
         } else {
           const int uv = u - 2 * B * UPR;
@@ -267,7 +273,7 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
       }
       // the convolution: block row j, tap i reads raw row j + i (history first)
       for (int e = t; e < 3 * B * D; e += NT) {
-        const int sec = e / (B * D), j = (e / D) % B, c = e % D;
+        const int sec = divB(e / D), j = modB(e / D), c = e % D;
         const float *w = &sCW[sec][c * a.W];
         float y = 0.f;
         for (int i = 0; i < a.W; ++i) y = fmaf(w[i], sRaw[sec][j + i][c], y);
@@ -325,8 +331,8 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
       for (int d0 = 0; d0 < ndots; d0 += GROUPS) {  // uniform trip count: every lane joins the DPP sums
         const int dd = d0 + grp;
         const bool valid = dd < ndots;
-        const int which = valid ? dd / (B * B) : 0, ij = valid ? dd % (B * B) : 0;
-        const int i = ij / B, j = ij % B;
+        const int which = valid ? divB(divB(dd)) : 0, ij = valid ? dd - which * B * B : 0;
+        const int i = divB(ij), j = modB(ij);
         const float *x = sX[which ? BMAX + i : i];
         const float *y = sX[j];
         float p = 0.f;
