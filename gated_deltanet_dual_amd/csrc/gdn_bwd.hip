@@ -943,6 +943,7 @@ static hipError_t launch_bwd_chunked(const BwdArgs &a_in, hipStream_t st, const 
       sa.init = j == 0 ? a.dh_final : p.carry;
       sa.final_out = j == nwin - 1 ? a.dh0 : p.carry;
       sa.states = p.adj;
+      sa.kx = p.pack;  // K dS' per chunk, for the per-chunk pass
       TimedLaunch tl(K_BWD_SCAN, st);
       hipError_t e1;
       if (p.win > 0) {

@@ -12,10 +12,13 @@
 //            adjoints, dU, drhs -- is computed in MFMA accumulator registers and
 //            fed straight back into the next product (slab.h), so the whole
 //            column-separable chain runs without LDS round trips or barriers.
-//            S_c and dS' columns come straight from global memory as B
-//            fragments; v, v~, do, do~ rows are staged through LDS.
-//   phase 2  the products that reduce over d_v: wave w takes three 16 x 16
-//            tiles of the six Gram adjoints and the 16-column d_k tile w of
+//            S_c columns come straight from global memory as B fragments
+//            (its rows for phase 2 are read in the same phase, so they come
+//            from L2); K dS' is the reverse scan's own product, stored by it
+//            in the hand-over; v, v~, do, do~ rows are staged through LDS.
+//   phase 2  the products that reduce over d_v: wave w takes up to two of the
+//            16 x 16 tiles of the six Gram adjoints that the masks leave
+//            non-zero (at most 16 of the 24) and the 16-column d_k tile w of
 //            dq, dk, dq~, dk~, with U, u~, drhs, drhs~ shared through LDS.
 //   phase 3  Gram adjoints -> Gram-weight gradients (each wave recomputes the
 //            raw q/k products of its three tiles with MFMA, instead of keeping
@@ -96,6 +99,36 @@ __device__ __forceinline__ bf16x8 frag_mask(const uint4 &v, int c0, int n, int P
   return __builtin_bit_cast(bf16x8, ok ? v : make_uint4(0u, 0u, 0u, 0u));
 }
 
+// The Gram tiles some position of the chunk's masks lets through, bit t for
+// tile (m = t / 4, rows 16 ((t >> 1) & 1) .., columns 16 (t & 1) ..) of the
+// six Gram adjoints, in the order Mo, Mq, Mk, M~, A, A~ (B the block size, a
+// power of two up to 32; p_i = i & -B the start of row i's block):
+//   Mo (j <= i), A (j < i): all but the upper right tile
+//   Mq, Mk (j < p_i): tile (ti, tj) iff 16 tj < max p_i over its rows
+//   M~ (j in i's block): the diagonal tiles, all four when B = 32
+//   A~ (j < i in i's block): none when B = 1, else as M~ but not upper right
+// Without noisy rows only Mo and A.
+__device__ __forceinline__ uint32_t gram_live_tiles(int B, bool has_noisy) {
+  uint32_t live = 0;
+#pragma unroll
+  for (int t = 0; t < 24; ++t) {
+    const int m = t >> 2, ti = (t >> 1) & 1, tj = t & 1;
+    bool on;
+    if (m == 0 || m == 4) on = !(ti == 0 && tj == 1);
+    else if (!has_noisy) on = false;
+    else if (m == 1 || m == 2) on = 16 * tj < ((16 * ti + 15) & -B);
+    else if (m == 3) on = B == 32 || ti == tj;
+    else on = B > 1 && (ti == tj || (B == 32 && ti == 1));
+    live |= on ? 1u << t : 0u;
+  }
+  return live;
+}
+// Index of the n-th (from 0) set bit of x, or -1 (x and n wave-uniform).
+__device__ __forceinline__ int nth_set_bit(uint32_t x, int n) {
+  for (int k = 0; k < n && x; ++k) x &= x - 1;
+  return x ? __builtin_ctz(x) : -1;
+}
+
 }  // namespace
 
 template <bool L2>
@@ -164,17 +197,31 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     vr[e] = *reinterpret_cast<const uint4 *>(src + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu16 * 8);
   }
   u16 (*const vst)[C][LDX] = reinterpret_cast<u16 (*)[C][LDX]>(&sm.arrp[0][0][0][0]);
-  // S_c and dS' columns of the slab (k = 32 ks + 8 g + e over d_k), converted to
+  // S_c columns of the slab (k = 32 ks + 8 g + e over d_k), converted to
   // B fragments after the Gram phase
-  float xs[4][8], xd[4][8];
+  float xs[4][8];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const size_t off = (size_t)(32 * ks + 2 * g4 + e) * D + col0 + cl;
-      xs[ks][e] = Sc[off];
-      xd[ks][e] = dSn[off];
-    }
+    for (int e = 0; e < 8; ++e) xs[ks][e] = Sc[(size_t)(32 * ks + 2 * g4 + e) * D + col0 + cl];
+  // rows [16 wave, 16 wave + 16) of S_c for the d_k tile of dq..dk~ (raw fp32,
+  // held to phase 2): read while the workgroup's column reads of the same
+  // state are in flight, so they come from L2
+  float4 rsc[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const size_t off = (size_t)(col0 + cl) * D + 32 * ks + 2 * g4;
+    rsc[ks][0] = *reinterpret_cast<const float4 *>(Sc + off);
+    rsc[ks][1] = *reinterpret_cast<const float4 *>(Sc + off + 4);
+  }
+  // K dS' of the slab, as the reverse scan formed it in its step (slab layout)
+  Slab KD;
+  {
+    const floatx4 *kxp = reinterpret_cast<const floatx4 *>(a.pack + ((size_t)slot * H + h) * kPackWords + kPackR) +
+                         wave * (8 * 64);
+    KD.t[0] = kxp[lane];
+    KD.t[1] = kxp[64 + lane];
+  }
   // LDS: zero the partials, then the loaded rows, the chunk matrices, gates
   for (int e = tid; e < kNW * P_NUM * C; e += NT) (&sm.part[0][0][0])[e] = 0.f;
   lds_barrier();
@@ -245,18 +292,12 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   auto Gn = [&](int i) { return sm.gf[GF_N][i]; };
   auto resp_row = [&](int i) { return c0 + i < n && c0 + i >= P; };
 
-  bf16x8 sbh[4], sbl[4], dbh[4], dbl[4];
-  float plg = 0.f;  // <dS', S_c> over this slab, fp32
+  bf16x8 sbh[4], sbl[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) plg += xs[ks][e] * xd[ks][e];
-    split8(xs[ks], sbh[ks], sbl[ks]);
-    split8(xd[ks], dbh[ks], dbl[ks]);
-  }
+  for (int ks = 0; ks < 4; ++ks) split8(xs[ks], sbh[ks], sbl[ks]);
 
-  // ---- X S_c and K dS' products
-  Slab KS = slab_zero(), QS = slab_zero(), QNS = slab_zero(), KNS = slab_zero(), KD = slab_zero();
+  // ---- X S_c products
+  Slab KS = slab_zero(), QS = slab_zero(), QNS = slab_zero(), KNS = slab_zero();
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
@@ -265,8 +306,6 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       const bf16x8 aq = frag_bf16(&sm.x[0][0][0], LDX, 16 * tr, 32 * ks);
       mma_bf16(KS.t[tr], ak, sbh[ks]);
       mma_bf16(KS.t[tr], ak, sbl[ks]);
-      mma_bf16(KD.t[tr], ak, dbh[ks]);
-      mma_bf16(KD.t[tr], ak, dbl[ks]);
       mma_bf16(QS.t[tr], aq, sbh[ks]);
       if (has_noisy) {
         const bf16x8 aqn = frag_bf16(&sm.x[2][0][0], LDX, 16 * tr, 32 * ks);
@@ -461,10 +500,6 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
         }
       }
   }
-  {
-    const float t = xsum32(xsum16(dpp_sum16(plg)));
-    if (lane == 0) sm.plgc[wave] = __expf(lgC) * t;
-  }
   // ---- phase 2's do, do~ row fragments (rows 16 tr .., k-step ks over d_v),
   // issued after the phase-1 values are stored, so they arrive during the barrier
   uint4 rfdo[2][4], rfdon[2][4];
@@ -476,19 +511,28 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       rfdon[tr][ks] = gfrag_raw(pdon, H, h, t0g, c0, n, 16 * tr, 32 * ks);
     }
 
-  // rows [16 wave, 16 wave + 16) of S_c and dS' for the d_k tile of dq..dk~,
-  // raw fp32, in flight during the Gram adjoints
-  float4 rsc[4][2], rds[4][2];
+  // rows [16 wave, 16 wave + 16) of dS' for the d_k tile of dk, raw fp32, in
+  // flight during the Gram adjoints
+  float4 rds[4][2];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const size_t off = (size_t)(col0 + cl) * D + 32 * ks + 2 * g4;
-    rsc[ks][0] = *reinterpret_cast<const float4 *>(Sc + off);
-    rsc[ks][1] = *reinterpret_cast<const float4 *>(Sc + off + 4);
     rds[ks][0] = *reinterpret_cast<const float4 *>(dSn + off);
     rds[ks][1] = *reinterpret_cast<const float4 *>(dSn + off + 4);
   }
   lds_barrier();
   // ================================================================ phase 2
+  {  // <dS', S_c> over rows [16 wave, 16 wave + 16), fp32
+    float plg = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        plg += rsc[ks][j].x * rds[ks][j].x + rsc[ks][j].y * rds[ks][j].y + rsc[ks][j].z * rds[ks][j].z +
+               rsc[ks][j].w * rds[ks][j].w;
+    const float t = xsum32(xsum16(dpp_sum16(plg)));
+    if (lane == 0) sm.plgc[wave] = __expf(lgC) * t;
+  }
   bf16x8 fdo[2][4], fdon[2][4];
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr)
@@ -497,16 +541,20 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       fdo[tr][ks] = frag_mask(rfdo[tr][ks], c0, n, P, false, 16 * tr);
       fdon[tr][ks] = frag_mask(rfdon[tr][ks], c0, n, P, true, 16 * tr);
     }
-  // Gram adjoints: 6 matrices x 4 tiles, tile t = wave + 8 j -> (m = t / 4, ti, tj)
+  // Gram adjoints: 6 matrices x 4 tiles, tile t -> (m = t / 4, ti, tj).  Only
+  // the tiles the masks leave non-zero are formed (at most 16 of the 24: the
+  // masks are lower triangular, and the noisy ones confined to blocks), dealt
+  // to the waves in order: wave w takes the (w + 8 jt)-th live tile.
   enum { DM_O = 0, DM_Q, DM_K, DM_N, DM_A, DM_AN };
-  floatx4 dM[3];
+  const uint32_t live = gram_live_tiles(B, has_noisy);
+  const int tl[2] = {nth_set_bit(live, wave), nth_set_bit(live, wave + 8)};
+  floatx4 dM[2];
 #pragma unroll
-  for (int jt = 0; jt < 3; ++jt) {
-    const int t = wave + 8 * jt;
+  for (int jt = 0; jt < 2; ++jt) {
+    const int t = tl[jt];
     const int m = t >> 2, ti = (t >> 1) & 1, tj = t & 1;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    const bool noisy_m = m == DM_Q || m == DM_K || m == DM_N || m == DM_AN;
-    if (!noisy_m || has_noisy) {
+    if (t >= 0) {
       const int right = (m == DM_N || m == DM_AN) ? A_UN : A_U;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -628,11 +676,27 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   auto dgp = [&](int mtx, int orient, int plane) {  // [32][LDG] u16
     return reinterpret_cast<u16 *>(&sm.arrp[0][0][0][0]) + (((size_t)mtx * 2 + orient) * 2 + plane) * C * LDG;
   };
+  {  // the tiles no mask lets through read as zero (both orientations, both
+     // planes); without noisy rows only Mo and A are read
+    const uint32_t dead = ~live & (has_noisy ? 0xFFFFFFu : 0xF000Fu);
 #pragma unroll
-  for (int jt = 0; jt < 3; ++jt) {
-    const int t = wave + 8 * jt;
+    for (int jt = 0; jt < 3; ++jt) {
+      const int t = nth_set_bit(dead, wave + 8 * jt);
+      if (t < 0) break;
+      const int m = t >> 2, ti = (t >> 1) & 1, tj = t & 1;
+      const int rr = lane >> 2, c4 = 4 * (lane & 3);
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        *reinterpret_cast<uint2 *>(dgp(m, 0, pl) + (16 * ti + rr) * LDG + 16 * tj + c4) = make_uint2(0u, 0u);
+        *reinterpret_cast<uint2 *>(dgp(m, 1, pl) + (16 * tj + rr) * LDG + 16 * ti + c4) = make_uint2(0u, 0u);
+      }
+    }
+  }
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+    const int t = tl[jt];
+    if (t < 0) continue;
     const int m = t >> 2, ti = (t >> 1) & 1, tj = t & 1;
-    if (!has_noisy && (m == DM_Q || m == DM_K || m == DM_N || m == DM_AN)) continue;
     const int i0 = 16 * ti + g4, j = 16 * tj + cl;
     // the raw products x_i . y_j of this tile (bf16 rows, exact products):
     //   Mo: q.k   Mq: q~.k   Mk: k~.k   M~: q~.k~   A: k.k   A~: k~.k~

@@ -25,6 +25,9 @@
 // A third wave per workgroup only stores: the compute waves stage each
 // chunk's carried slabs in LDS and it writes them out, so the stores never sit
 // in the compute waves' (in-order) memory counters ahead of their loads.
+// In reverse the store wave also writes each chunk's K dS' (the step's first
+// product) over the chunk's R slabs in the hand-over, for the per-chunk
+// gradient kernel (ScanArgs::kx).
 //
 // A long document is one long chain.  Its chunks can be cut into runs
 // scanned in parallel (the affine segment scan): the step is affine in X, so
@@ -67,7 +70,9 @@ struct ScanRing {
 
 struct ScanSmem {
   alignas(16) uint4 sh[2][sSH][64];             // shared units, double-buffered by chunk parity
-  alignas(16) float stage[2][sNW][sD][16 + 4];  // the carried slabs for the store wave, by chunk parity
+  // the carried slabs for the store wave, by chunk parity; the reverse scan
+  // stages its K X slab in the row padding (row 64 tr + lane, columns 16-19)
+  alignas(16) float stage[2][sNW][sD][16 + 4];
 };
 
 }  // namespace
@@ -169,6 +174,15 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
       }
       if (a.ckpt && c % a.ckpt_stride == 0)
         dck = a.ckpt + ((t0g / ((int64_t)C * a.ckpt_stride) + doc + c / a.ckpt_stride) * H + h) * (size_t)D * D;
+      float *const dkx = REVERSE && a.kx ? a.kx + ((size_t)wslot(c) * H + h) * kPackWords + kPackR : nullptr;
+      if (dkx) {  // slab s of K X at the start of the chunk's R slab s
+#pragma unroll
+        for (int w = 0; w < sNW; ++w)
+#pragma unroll
+          for (int tr = 0; tr < 2; ++tr)
+            *reinterpret_cast<floatx4 *>(dkx + (size_t)(sNW * quarter + w) * (8 * 256) + tr * 256 + 4 * lane) =
+                *reinterpret_cast<const floatx4 *>(&sm.stage[i & 1][w][64 * tr + lane][16]);
+      }
       if (!dst && !dck) continue;
 #pragma unroll
       for (int w = 0; w < sNW; ++w)
@@ -280,6 +294,10 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     }
     if constexpr (LAG) {
       stage_X(i & 1);
+      if (REVERSE && a.kx) {
+        *reinterpret_cast<floatx4 *>(&sm.stage[i & 1][wave][lane][16]) = KX.t[0];
+        *reinterpret_cast<floatx4 *>(&sm.stage[i & 1][wave][64 + lane][16]) = KX.t[1];
+      }
       if (i + 1 < nchunks) publish(pn, (i + 1) & 1);
     }
     // Y = W KX
@@ -437,6 +455,7 @@ hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t uni
   r.units = units;
   r.states = nullptr;
   r.ckpt = nullptr;
+  r.kx = nullptr;
   r.final_out = nullptr;
   r.seg_init = nullptr;
   // the runs' transfer maps (from the identity, no right-hand side)

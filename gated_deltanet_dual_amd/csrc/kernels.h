@@ -150,6 +150,12 @@ struct ScanArgs {
   // c % ckpt_stride == 0, at ckpt_slot(cu_i, i, c, ckpt_stride) (or NULL).
   float *ckpt;
   int ckpt_stride;
+  // Reverse scan only: K X of every chunk, the product its step forms anyway
+  // (for the per-chunk backward kernel, which would otherwise form K dS' from
+  // dS' itself), as slabs [slab 8][tile 2][lane 64][4] at the start of the
+  // chunk's R area in the hand-over (kx = pack): each wave writes only over
+  // its own R slab, after its step has consumed it.  NULL: not written.
+  float *kx;
 };
 hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st);
 // The runs' start states from their transfer maps M (identity-init, homog
