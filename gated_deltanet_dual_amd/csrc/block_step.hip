@@ -188,7 +188,9 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
     }
     // the state: thread (rg, cq) holds rows rg * RPG .. + RPG - 1, columns
     // 4 cq .. 4 cq + 3 (a wave reads whole 128-byte row segments); nothing
-    // waits for it until the reduction
+    // waits for it until the reduction.  Each state is read once per call,
+    // so the loads are non-temporal (they do not displace other lines from
+    // the caches)
     if constexpr (MF) {
       const float *Sw = S + 16 * wvs + n16;
 #pragma unroll
@@ -198,7 +200,11 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
     } else {
 #pragma unroll
       for (int i = 0; i < RPG; ++i)
-        s4[i] = *reinterpret_cast<const float4 *>(S + (size_t)(rg * RPG + i) * D + 4 * cq);
+      {
+        const floatx4 v =
+            __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(S + (size_t)(rg * RPG + i) * D + 4 * cq));
+        s4[i] = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
 
     // 1. block inputs -> LDS as fp32 (CONV: the raw rows, convolved below)
@@ -489,10 +495,12 @@ __global__ __launch_bounds__((StepCfg<D, DV>::NT)) void block_step_kernel(BlockS
     //    COMMIT (1): S <- G_e S + sum_j (G_e / G_j) b_j k_j u_j^T, written back
     //      (or to pool_out)
     const int toff = rg * RPG * D + 4 * cq;  // the thread's first state element; rows follow at D
+    // states are written once and not read back by this call: non-temporal
     auto store = [&](float *base, const float4 *n) {
       float *const p = base + toff;
 #pragma unroll
-      for (int i = 0; i < RPG; ++i) *reinterpret_cast<float4 *>(p + i * D) = n[i];
+      for (int i = 0; i < RPG; ++i)
+        __builtin_nontemporal_store(floatx4{n[i].x, n[i].y, n[i].z, n[i].w}, reinterpret_cast<floatx4 *>(p + i * D));
     };
     // MF layout: one token's update n = a n + (b k_j) u_j^T and the stores
     auto mf_step = [&](float (*nn)[8], int j, float aj, float wk) {
@@ -717,9 +725,9 @@ __global__ __launch_bounds__(256) void gdn_scatter_kernel(ScatterArgs a, const i
     for (int e0 = 0; e0 < PER; e0 += GRP) {
       v4f v[GRP];
 #pragma unroll
-      for (int e = 0; e < GRP; ++e) v[e] = src[(e0 + e) * 256 + threadIdx.x];
+      for (int e = 0; e < GRP; ++e) v[e] = __builtin_nontemporal_load(&src[(e0 + e) * 256 + threadIdx.x]);
 #pragma unroll
-      for (int e = 0; e < GRP; ++e) dst[(e0 + e) * 256 + threadIdx.x] = v[e];
+      for (int e = 0; e < GRP; ++e) __builtin_nontemporal_store(v[e], &dst[(e0 + e) * 256 + threadIdx.x]);
     }
   } else {
     if ((int)threadIdx.x < NV) dst[threadIdx.x] = src[threadIdx.x];
