@@ -53,6 +53,7 @@ namespace {
 
 constexpr int sC = 32, sD = 128, sNW = 2, sNQ = sD / (16 * sNW);  // waves per workgroup, workgroups per (doc, head)
 constexpr int sRING = 4;                                            // register ring depth (chunks)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));           // a native vector for the nontemporal builtin
 // the operands every slab needs (W, then K and K^T fragments: contiguous in the
 // hand-over), in 1 KB units of 64 lanes x 16 bytes, dealt round-robin to the waves
 constexpr int sSH = (kPackKT + 2048 - kPackW) / 256, sSHW = (sSH + sNW - 1) / sNW;
@@ -235,7 +236,10 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     constexpr int NR = ZRHS ? 2 : 8;
     const uint4 *pr = reinterpret_cast<const uint4 *>(pk + kPackR) + (size_t)slab * NR * 64;
 #pragma unroll
-    for (int j = 0; j < NR; ++j) p.r[j] = pr[j * 64 + lane];
+    for (int j = 0; j < NR; ++j) {  // read once: non-temporal
+      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(pr) + j * 64 + lane);
+      p.r[j] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
     // shared unit j * sNW + wave (clamped: the last round is partial, and
     // its surplus loads are repeats that are never published)
     const uint4 *ps = reinterpret_cast<const uint4 *>(pk + kPackW);
