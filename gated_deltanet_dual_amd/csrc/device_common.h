@@ -64,6 +64,18 @@ __device__ __forceinline__ void mma_f32(floatx4 &acc, float a, float b) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// 16-byte non-temporal loads (for data a kernel reads once): the builtin
+// takes native vectors only
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt_u4(const void *p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float4 ld_nt_f4(const void *p) {
+  const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // ---------------------------------------------------------------- fragments
 // Row fragment of a row-major bf16 matrix: rows row0 + (l & 15), columns
 // k0 + 8*(l>>4) .. +7 (one 16-byte LDS read).

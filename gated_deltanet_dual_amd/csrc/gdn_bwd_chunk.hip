@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   float4 tri4[3];  // the six chunk matrices
 #pragma unroll
   for (int j = 0; j < 3; ++j)
-    tri4[j] = reinterpret_cast<const float4 *>(a.tri + ((size_t)slot * H + h) * 6 * C * C)[j * NT + tid];
+    tri4[j] = ld_nt_f4(a.tri + ((size_t)slot * H + h) * 6 * C * C + 4 * (j * NT + tid));  // read once
   // v, v~, do, do~ rows: staged through LDS (the bytes of the d_v arrays, which
   // phase 1 fills only after every wave has taken its slab from them)
   uint4 vr[UX];
@@ -219,8 +219,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   {
     const floatx4 *kxp = reinterpret_cast<const floatx4 *>(a.pack + ((size_t)slot * H + h) * kPackWords + kPackR) +
                          wave * (8 * 64);
-    KD.t[0] = kxp[lane];
-    KD.t[1] = kxp[64 + lane];
+    KD.t[0] = __builtin_nontemporal_load(&kxp[lane]);  // read once
+    KD.t[1] = __builtin_nontemporal_load(&kxp[64 + lane]);
   }
   // LDS: zero the partials, then the loaded rows, the chunk matrices, gates
   for (int e = tid; e < kNW * P_NUM * C; e += NT) (&sm.part[0][0][0])[e] = 0.f;

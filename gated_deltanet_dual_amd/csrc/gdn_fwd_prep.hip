@@ -86,7 +86,7 @@ __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float
     for (int e = 0; e < UX; ++e) {
       const int u = e * NT + tid;
       const int m = u / PU, r = u % PU, row = r / RU, cu = r % RU;
-      xr[e] = *reinterpret_cast<const uint4 *>(px[m] + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu * 8);
+      xr[e] = ld_nt_u4(px[m] + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu * 8);  // read once here
     }
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) gslab_raw<D>(rv[sb], pv, H, h, t0g, c0, n, 32 * wave + 16 * sb);
