@@ -56,11 +56,11 @@ BWD_BYTES_PER_TH = 4 * 256 + 8 + 3 * 256 + 8
 # and the six chunk matrices, and hands the reverse scan, per (chunk slot,
 # head), R (128 x 128 fp32), W (hi + lo bf16), two fragment sets of K and the
 # chunk decay; the scan reads that and writes the chunk's end-state adjoint
-# (128 x 128 fp32) for the per-chunk pass
+# (128 x 128 fp32) and K dS' (32 x 128 fp32) for the per-chunk pass
 PRE_BYTES_PER_TH = 3 * 256 + 8
 PACK_BYTES_PER_SLOT_HEAD = (128 * 128 + 1024 + 2048 + 2048 + 64) * 4
 PRE_BYTES_PER_SLOT_HEAD = 6 * 32 * 32 * 4 + PACK_BYTES_PER_SLOT_HEAD
-SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4
+SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4 + 32 * 128 * 4
 # the forward's preparation pass reads q, k and the gates of both streams and
 # v, and writes the six 32 x 32 fp32 chunk matrices and the hand-over; the
 # forward scan reads that and writes the chunk-start states; the output pass
