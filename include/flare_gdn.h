@@ -22,8 +22,9 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the name ends in _host.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
- *     device work is enqueued on it; no entry point synchronises, allocates or
- *     frees device memory.
+ *     device work is enqueued on it; no compute entry point synchronises,
+ *     allocates or frees device memory (the measurement aid
+ *     flare_timing_avg_ms, outside this contract, waits on its own events).
  *   - The caller owns every buffer.  Host arrays are read during the call only.
  *   - Outputs are fully overwritten (rows that are zero by definition are
  *     written as zeros); nothing is accumulated into.  Outputs must not alias
@@ -575,9 +576,13 @@ int32_t flare_version(void);
  * "shortconv_dual_bwd_kernel" (both kernels of flare_shortconv_dual_bwd;
  * flare_qkv_prologue and its reverse mode are timed under the ShortConv names;
  * flare_gdn_verify under "block_step_kernel"), "gdn_scatter_kernel",
- * and, for bf16 io at d = 128, the chunked passes: "gdn_tri_kernel" (the
- * chunk matrices, forward and backward), "gdn_fwd_pre_kernel" and
- * "gdn_bwd_pre_kernel" (the state-independent parts of the chunk steps),
+ * and, for bf16 io at d = 128, the chunked passes: "gdn_fwd_prep_kernel"
+ * (the forward's chunk matrices and scan hand-over in one pass; also the
+ * backward's re-formed hand-over when it rebuilds states from strided
+ * checkpoints), "gdn_tri_kernel" (the chunk matrices alone, for a backward
+ * that does not take the forward's), "gdn_fwd_pre_kernel" (the hand-over
+ * from given chunk matrices) and "gdn_bwd_pre_kernel" (the state-independent
+ * parts of the reverse chunk step),
  * "gdn_fwd_scan_kernel" (the forward state recurrence; "gdn_dual_fwd_kernel"
  * then names the forward's output pass) and "gdn_bwd_scan_kernel" (the
  * reverse recurrence).
