@@ -75,6 +75,14 @@ __device__ __forceinline__ float4 ld_nt_f4(const void *p) {
   const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
   return make_float4(v[0], v[1], v[2], v[3]);
 }
+// 16-byte non-temporal stores (for data a kernel writes once and no later
+// access of the same kernel reads)
+__device__ __forceinline__ void st_nt_u4(void *p, const uint4 &v) {
+  __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v *>(p));
+}
+__device__ __forceinline__ void st_nt_f4(void *p, const float4 &v) {
+  __builtin_nontemporal_store(floatx4{v.x, v.y, v.z, v.w}, reinterpret_cast<floatx4 *>(p));
+}
 
 // ---------------------------------------------------------------- fragments
 // Row fragment of a row-major bf16 matrix: rows row0 + (l & 15), columns

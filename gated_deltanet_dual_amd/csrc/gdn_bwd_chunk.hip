@@ -664,8 +664,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       const int u = e * NT + tid;
       const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
       if (c0 + row < n)
-        *reinterpret_cast<uint4 *>((m == 0 ? gdv : gdvn) + ((t0g + c0 + row) * H + h) * D + cu16 * 8) =
-            *reinterpret_cast<const uint4 *>(&sm.arrp[m == 0 ? A_DRHS : A_DRN][0][row][cu16 * 8]);
+        st_nt_u4((m == 0 ? gdv : gdvn) + ((t0g + c0 + row) * H + h) * D + cu16 * 8,
+                 *reinterpret_cast<const uint4 *>(&sm.arrp[m == 0 ? A_DRHS : A_DRN][0][row][cu16 * 8]));
     }
   }
 
@@ -888,8 +888,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
       const int m = u / (C * RU), rr = u % (C * RU), row = rr / RU, cu16 = rr % RU;
       if (c0 + row >= n) continue;
       u16 *dst = m == 0 ? outp[0] : m == 1 ? outp[1] : m == 2 ? outp[2] : outp[3];
-      *reinterpret_cast<uint4 *>(dst + ((t0g + c0 + row) * H + h) * D + cu16 * 8) =
-          *reinterpret_cast<const uint4 *>(&sm.x[m][row][cu16 * 8]);
+      st_nt_u4(dst + ((t0g + c0 + row) * H + h) * D + cu16 * 8, *reinterpret_cast<const uint4 *>(&sm.x[m][row][cu16 * 8]));
     }
   }
   // ---- gates, step 2 (wave 0; lanes 0-31 the clean rows i, lanes 32-63 the

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
       mma_bf16(acc, akn, yh[3]);
       mma_bf16(acc, akn, yl[3]);
     }
-    rdst[kt * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    st_nt_f4(&rdst[kt * 64 + lane], make_float4(acc[0], acc[1], acc[2], acc[3]));
   }
 }
 

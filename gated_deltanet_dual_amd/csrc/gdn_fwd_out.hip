@@ -297,7 +297,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
     if (c0 + row < n) {
       u16 *dst = (m == 0 ? po : pon) + ((t0g + c0 + row) * H + h) * D + cu16 * 8;
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&sm.x[m][row][cu16 * 8]);
+      st_nt_u4(dst, *reinterpret_cast<const uint4 *>(&sm.x[m][row][cu16 * 8]));
     }
   }
 }

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float
       for (int r = 0; r < 4; ++r) Z.t[tr][r] *= Dd(slab_row(tr, r));
     float4 *zdst = reinterpret_cast<float4 *>(pack + kPackR) + (size_t)slab * 2 * 64;
 #pragma unroll
-    for (int tr = 0; tr < 2; ++tr) zdst[tr * 64 + lane] = make_float4(Z.t[tr][0], Z.t[tr][1], Z.t[tr][2], Z.t[tr][3]);
+    for (int tr = 0; tr < 2; ++tr) st_nt_f4(&zdst[tr * 64 + lane], make_float4(Z.t[tr][0], Z.t[tr][1], Z.t[tr][2], Z.t[tr][3]));
   }
 }
 
