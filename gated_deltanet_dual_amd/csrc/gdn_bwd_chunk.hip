@@ -21,7 +21,7 @@
 //            non-zero (at most 16 of the 24) and the 16-column d_k tile w of
 //            dq, dk, dq~, dk~, with U, u~, drhs, drhs~ shared through LDS.
 //   phase 3  Gram adjoints -> Gram-weight gradients (each wave recomputes the
-//            raw q/k products of its three tiles with MFMA, instead of keeping
+//            raw q/k products of its tiles with MFMA, instead of keeping
 //            six unweighted Gram matrices in LDS), their contractions with the
 //            q/k rows, gate gradients, stores.
 // Nothing is reduced across workgroups, so the result is deterministic.
