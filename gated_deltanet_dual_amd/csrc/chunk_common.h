@@ -1,5 +1,7 @@
 // chunk_common.h -- the unit-lower-triangular chunk solve shared by the
-// forward and backward kernels.
+// forward and backward kernels, and the rule for which parts of a stored
+// chunk-matrix record can be non-zero (the record's writer and readers
+// touch only those).
 #pragma once
 
 #include "device_common.h"
@@ -64,6 +66,55 @@ __device__ __forceinline__ void solve_unit_lower(const float *At, float *Tm, flo
 #pragma unroll
     for (int r = 0; r < 4; ++r) Tm[(16 + acc_row(r)) * LDM + acc_col()] = -ta[r];
   }
+}
+
+}  // namespace flare
+
+namespace flare {
+
+// Whether half-row `half` (columns 16 half .. 16 half + 15, 64 bytes of fp32)
+// of row `row` of chunk matrix `mtx` can hold a non-zero entry.  The order is
+// the chunk-matrix pass's: T, T~, Mwo, Mwq, Mwk, Mw~.  B is the block size (a
+// power of two dividing the 32-token chunk), p = row & -B the start of the
+// row's noisy block and p + B - 1 its end.  From the masks that define them:
+//   T = (I + A)^-1, A strictly lower    -> j <= i
+//   T~, inverse of the in-block system  -> p <= j <= i
+//   Mwo (masked clean Gram, j <= i)     -> j <= i
+//   Mwq, Mwk (reads before the block)   -> j < p
+//   Mw~ (the block-end read)            -> p <= j <= p + B - 1
+// and the four noisy ones are not formed in a chunk without response rows.
+// The pass that forms them stores only live half-rows; every reader loads
+// only those and takes the others as zero, which they are.
+__device__ __forceinline__ bool cm_half_live(int mtx, int row, int half, int B, bool has_noisy) {
+  const int lo = 16 * half, hi = lo + 15;
+  const int p = row & -B, e = p + B - 1;
+  switch (mtx) {
+    case 0:
+    case 2: return lo <= row;
+    case 1: return has_noisy && lo <= row && hi >= p;
+    case 3:
+    case 4: return has_noisy && lo < p;
+    default: return has_noisy && lo <= e && hi >= p;
+  }
+}
+
+// Float4 u (0 .. 1535) of a chunk-matrix record ([6][32][32] fp32, row-major):
+// whether it is live.
+__device__ __forceinline__ bool cm_f4_live(int u, int B, bool has_noisy) {
+  const int mtx = u >> 8, rr = u & 255;
+  return cm_half_live(mtx, rr >> 3, (rr >> 2) & 1, B, has_noisy);
+}
+
+// Load float4 u of a chunk-matrix record, or zero when it is not live.  The
+// load is always issued (no load sits under a branch): a dead one is aimed at
+// the record's first float4 (live in every chunk: T's diagonal starts there),
+// which the same launch reads anyway, so it costs no HBM traffic.
+template <bool NT>
+__device__ __forceinline__ float4 cm_load_f4(const float *rec, int u, int B, bool has_noisy) {
+  const bool live = cm_f4_live(u, B, has_noisy);
+  const float *src = rec + 4 * (live ? u : 0);
+  const float4 v = NT ? ld_nt_f4(src) : *reinterpret_cast<const float4 *>(src);
+  return live ? v : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 }  // namespace flare

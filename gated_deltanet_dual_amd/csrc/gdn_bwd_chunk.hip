@@ -185,7 +185,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   float4 tri4[3];  // the six chunk matrices
 #pragma unroll
   for (int j = 0; j < 3; ++j)
-    tri4[j] = ld_nt_f4(a.tri + ((size_t)slot * H + h) * 6 * C * C + 4 * (j * NT + tid));  // read once
+    tri4[j] = cm_load_f4<true>(a.tri + ((size_t)slot * H + h) * 6 * C * C, j * NT + tid, B,
+                               has_noisy);  // read once; live half-rows only
   // v, v~, do, do~ rows: staged through LDS (the bytes of the d_v arrays, which
   // phase 1 fills only after every wave has taken its slab from them)
   uint4 vr[UX];

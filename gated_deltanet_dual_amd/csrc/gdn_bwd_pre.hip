@@ -21,6 +21,7 @@
 // strengths arrive folded from the gate load and the output gradients are
 // r_q do, r_q~ do~.
 #include "bwd_common.h"
+#include "chunk_common.h"
 #include "device_common.h"
 #include "host_plan.h"
 #include "kernels.h"
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
   const float *tri = a.tri + ((size_t)slot * H + h) * 6 * C * C;
   float4 tv[3];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) tv[j] = *reinterpret_cast<const float4 *>(tri + 4 * (j * NT + tid));
+  for (int j = 0; j < 3; ++j) tv[j] = cm_load_f4<false>(tri, j * NT + tid, B, has_noisy);  // live half-rows only
   const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
   float l2r = 1.f;  // L2, thread tid < 64: r_q (tid < 32) or r_q~ of row tid % 32
   if (L2 && tid < 2 * C) l2r = reinterpret_cast<const float *>(f.l2f + (t0g + min(c0 + (tid & (C - 1)), n - 1)) * H +

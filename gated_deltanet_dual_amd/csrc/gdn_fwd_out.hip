@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "bwd_common.h"
+#include "chunk_common.h"
 #include "conv_load.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -97,9 +98,10 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
   const float *cm = cmat + ((size_t)slot * H + h) * 6 * C * C;
   // three named registers, not an array: an array the compiler leaves
   // un-unrolled would live in scratch
-  const float4 cv0 = reinterpret_cast<const float4 *>(cm)[tid];
-  const float4 cv1 = reinterpret_cast<const float4 *>(cm)[NT + tid];
-  const float4 cv2 = reinterpret_cast<const float4 *>(cm)[2 * NT + tid];
+  // (only the half-rows that can be non-zero are read; the others are zero)
+  const float4 cv0 = cm_load_f4<false>(cm, tid, B, has_noisy);
+  const float4 cv1 = cm_load_f4<false>(cm, NT + tid, B, has_noisy);
+  const float4 cv2 = cm_load_f4<false>(cm, 2 * NT + tid, B, has_noisy);
   const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
   float l2r = 1.f;  // thread tid < 128: factor tid / 32 of row tid % 32
   if (L2 && tid < 4 * C) {

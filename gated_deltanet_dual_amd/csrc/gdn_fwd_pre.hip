@@ -19,6 +19,7 @@
 // L2: the q/k L2 flag folded into per-row factors (gdn_l2.hip): the write
 // strengths arrive folded from the gate load, the v rows are divided by r_k.
 #include "bwd_common.h"
+#include "chunk_common.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "slab.h"
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const 
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr)
     xv[rr] = *reinterpret_cast<const uint4 *>(pk + ((t0g + min(c0 + prow + rr, n - 1)) * H + h) * D + 8 * pu);
-  const float4 tv = reinterpret_cast<const float4 *>(cmat + ((size_t)slot * H + h) * 6 * C * C)[tid & 255];
+  const float4 tv = cm_load_f4<false>(cmat + ((size_t)slot * H + h) * 6 * C * C, tid & 255, B, false);  // T
   const float graw = tid < 4 * C ? gate_load_raw(f, t0g, c0, n, h, tid) : 0.f;
   u16 rv[2][4];
   gslab_raw<D>(rv, pv, H, h, t0g, c0, n, col0);

@@ -173,8 +173,9 @@ __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float
 #pragma unroll
       for (int e = 0; e < C * C / 4 / 64; ++e) {
         const int u = e * 64 + lane, row = u / (C / 4), c4 = u % (C / 4);
-        *reinterpret_cast<float4 *>(dst + (size_t)mtx * C * C + row * C + 4 * c4) =
-            *reinterpret_cast<const float4 *>(&sm.tm[mtx][row][4 * c4]);
+        if (cm_half_live(mtx, row, c4 >> 2, B, has_noisy))  // structurally zero half-rows are not stored
+          *reinterpret_cast<float4 *>(dst + (size_t)mtx * C * C + row * C + 4 * c4) =
+              *reinterpret_cast<const float4 *>(&sm.tm[mtx][row][4 * c4]);
       }
     }
   }
