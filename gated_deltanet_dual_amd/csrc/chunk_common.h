@@ -72,8 +72,8 @@ __device__ __forceinline__ void solve_unit_lower(const float *At, float *Tm, flo
 
 namespace flare {
 
-// Whether half-row `half` (columns 16 half .. 16 half + 15, 64 bytes of fp32)
-// of row `row` of chunk matrix `mtx` can hold a non-zero entry.  The order is
+// Whether the half-row starting at column lo (0 or 16; 64 bytes of fp32) of
+// row `row` of chunk matrix `mtx` can hold a non-zero entry.  The order is
 // the chunk-matrix pass's: T, T~, Mwo, Mwq, Mwk, Mw~.  B is the block size (a
 // power of two dividing the 32-token chunk), p = row & -B the start of the
 // row's noisy block and p + B - 1 its end.  From the masks that define them:
@@ -83,32 +83,42 @@ namespace flare {
 //   Mwq, Mwk (reads before the block)   -> j < p
 //   Mw~ (the block-end read)            -> p <= j <= p + B - 1
 // and the four noisy ones are not formed in a chunk without response rows.
-// The pass that forms them stores only live half-rows; every reader loads
-// only those and takes the others as zero, which they are.
-__device__ __forceinline__ bool cm_half_live(int mtx, int row, int half, int B, bool has_noisy) {
-  const int lo = 16 * half, hi = lo + 15;
-  const int p = row & -B, e = p + B - 1;
-  switch (mtx) {
-    case 0:
-    case 2: return lo <= row;
-    case 1: return has_noisy && lo <= row && hi >= p;
-    case 3:
-    case 4: return has_noisy && lo < p;
-    default: return has_noisy && lo <= e && hi >= p;
-  }
+// The passes that form them store only live parts; every reader loads only
+// those and takes the others as zero, which they are.  mtx, lo, B and
+// has_noisy are wave-uniform, so the choice of rule is a scalar branch.
+__device__ __forceinline__ bool cm_half_live(int mtx, int row, int lo, int B, bool has_noisy) {
+  const int p = row & -B;
+  if (mtx == 0 || mtx == 2) return lo <= row;
+  if (!has_noisy) return false;
+  if (mtx == 1) return lo <= row && lo + 15 >= p;
+  if (mtx == 5) return lo <= p + B - 1 && lo + 15 >= p;
+  return lo < p;
 }
 
-// Float4 u (0 .. 1535) of a chunk-matrix record ([6][32][32] fp32, row-major):
-// whether it is live.
+// A chunk-matrix record in memory: the six 32 x 32 fp32 matrices, each stored
+// tile-major as four 16 x 16 tiles (tile (ti, tj) at 2 ti + tj, rows of 64
+// bytes), so that a dead tile is whole 128-byte lines.  Float4 u (0 .. 1535)
+// holds row cm_row(u), columns cm_col(u) .. + 3 of matrix u >> 8; the 64
+// float4s of a tile are one wave's share when a wave takes 64 consecutive u.
+__device__ __forceinline__ int cm_row(int u) { return 16 * ((u >> 7) & 1) + ((u >> 2) & 15); }
+__device__ __forceinline__ int cm_col(int u) { return 16 * ((u >> 6) & 1) + 4 * (u & 3); }
+// The float4 of matrix mtx holding row `row`, columns col .. col + 3 (col a multiple of 4).
+__device__ __forceinline__ int cm_f4_index(int mtx, int row, int col) {
+  return 256 * mtx + 64 * (2 * (row >> 4) + (col >> 4)) + 4 * (row & 15) + ((col & 15) >> 2);
+}
+// Whether float4 u of a record is live.  The wave's lanes must hold 64
+// consecutive u starting at a multiple of 64 (one tile), so that the matrix
+// and the tile are the wave's.
 __device__ __forceinline__ bool cm_f4_live(int u, int B, bool has_noisy) {
-  const int mtx = u >> 8, rr = u & 255;
-  return cm_half_live(mtx, rr >> 3, (rr >> 2) & 1, B, has_noisy);
+  const int t = __builtin_amdgcn_readfirstlane(u >> 6);  // matrix 4 t / 16 .., tile t & 3
+  return cm_half_live(t >> 2, 16 * ((t >> 1) & 1) + ((u >> 2) & 15), 16 * (t & 1), B, has_noisy);
 }
 
-// Load float4 u of a chunk-matrix record, or zero when it is not live.  The
-// load is always issued (no load sits under a branch): a dead one is aimed at
-// the record's first float4 (live in every chunk: T's diagonal starts there),
-// which the same launch reads anyway, so it costs no HBM traffic.
+// Load float4 u of a chunk-matrix record (lanes as for cm_f4_live), or zero
+// when it is not live.  The load is always issued (no load sits under a
+// branch): a dead one is aimed at the record's first float4 (live in every
+// chunk: T's diagonal starts there), which the same launch reads anyway, so
+// it costs no HBM traffic.
 template <bool NT>
 __device__ __forceinline__ float4 cm_load_f4(const float *rec, int u, int B, bool has_noisy) {
   const bool live = cm_f4_live(u, B, has_noisy);

@@ -182,11 +182,18 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const float *fr = reinterpret_cast<const float *>(f.l2f + (t0g + min(c0 + (tid & (C - 1)), n - 1)) * H + h);
     l2r = fr[tid / C];
   }
-  float4 tri4[3];  // the six chunk matrices
+  // the six chunk matrices: thread tid takes 4 consecutive entries of a row
+  // (8 threads per row, the matrix the same across a wave), read once, only
+  // the parts that can be non-zero (exec-masked loads; the rest is zero)
+  float4 tri4[3];
+  const float *const trec = a.tri + ((size_t)slot * H + h) * 6 * C * C;
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
-    tri4[j] = cm_load_f4<true>(a.tri + ((size_t)slot * H + h) * 6 * C * C, j * NT + tid, B,
-                               has_noisy);  // read once; live half-rows only
+  for (int j = 0; j < 3; ++j) {
+    const int u = j * NT + tid, mtx = __builtin_amdgcn_readfirstlane(u >> 8);
+    const int row = (u & 255) >> 3, col = 4 * (u & 7);
+    tri4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (cm_half_live(mtx, row, col & 16, B, has_noisy)) tri4[j] = ld_nt_f4(trec + 4 * cm_f4_index(mtx, row, col));
+  }
   // v, v~, do, do~ rows: staged through LDS (the bytes of the d_v arrays, which
   // phase 1 fills only after every wave has taken its slab from them)
   uint4 vr[UX];
@@ -241,8 +248,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   // transposed (the matrix index is the same across a wave)
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const int u = j * NT + tid, which = u / (C * C / 4), rr = u % (C * C / 4);
-    const int row = rr / (C / 4), col = 4 * (rr % (C / 4));
+    const int u = j * NT + tid, which = u / (C * C / 4);
+    const int row = (u & 255) >> 3, col = 4 * (u & 7);
     const float x4[4] = {tri4[j].x, tri4[j].y, tri4[j].z, tri4[j].w};
     u16 hb[4], lb[4];
 #pragma unroll

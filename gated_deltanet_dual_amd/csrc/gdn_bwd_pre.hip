@@ -122,8 +122,8 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const int u = j * NT + tid, which = u / (C * C / 4), rr = u % (C * C / 4);
-    *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = tv[j];
+    const int u = j * NT + tid, which = u / (C * C / 4);
+    *reinterpret_cast<float4 *>(&sm.cc[which][cm_row(u)][cm_col(u)]) = tv[j];
   }
   if (tid < 4 * C) gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   if (L2 && tid < 2 * C) sm.rq[tid / C][tid & (C - 1)] = l2r;

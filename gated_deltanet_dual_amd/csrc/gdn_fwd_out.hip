@@ -163,8 +163,8 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     }
   }
   auto put_cm = [&](int j, const float4 &v) {
-    const int u = j * NT + tid, which = u / (C * C / 4), rr = u % (C * C / 4);
-    *reinterpret_cast<float4 *>(&sm.cc[which][rr / (C / 4)][4 * (rr % (C / 4))]) = v;
+    const int u = j * NT + tid, which = u / (C * C / 4);
+    *reinterpret_cast<float4 *>(&sm.cc[which][cm_row(u)][cm_col(u)]) = v;
   };
   put_cm(0, cv0);
   put_cm(1, cv1);

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(fNT) void gdn_fwd_pre_d128_kernel(FwdArgs f, const 
       *reinterpret_cast<uint2 *>(&sm.kt[8 * pu + e][prow]) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
     }
   }
-  if (tid < C * C / 4) *reinterpret_cast<float4 *>(&sm.tm[tid / (C / 4)][4 * (tid % (C / 4))]) = tv;
+  if (tid < C * C / 4) *reinterpret_cast<float4 *>(&sm.tm[cm_row(tid)][cm_col(tid)]) = tv;
   if (tid < 4 * C) gate_scan(gate_fix(graw, c0, n, P, tid), B, tid, sm.lg, sm.beta, sm.lgn, sm.betan);
   if (L2 && tid < C) sm.vsc[tid] = rkl > 0.f ? 1.f / rkl : 0.f;
   lds_barrier();

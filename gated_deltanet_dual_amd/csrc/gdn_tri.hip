@@ -88,9 +88,10 @@ __global__ __launch_bounds__(tNT) void gdn_tri_d128_kernel(BwdArgs a) {
     const int mtx = wave < 2 ? wave : (wave == 2 ? 2 : 4) + mi;
 #pragma unroll
     for (int e = 0; e < C * C / 4 / 64; ++e) {
-      const int u = e * 64 + lane, row = u / (C / 4), c4 = u % (C / 4);
-      *reinterpret_cast<float4 *>(dst + (size_t)mtx * C * C + row * C + 4 * c4) =
-          *reinterpret_cast<const float4 *>(&sm.tm[mtx][row][4 * c4]);
+      const int u = mtx * (C * C / 4) + e * 64 + lane;  // the record's tile-major order
+      if (cm_f4_live(u, B, has_noisy))  // structurally zero parts are not stored
+        *reinterpret_cast<float4 *>(dst + 4 * (size_t)u) =
+            *reinterpret_cast<const float4 *>(&sm.tm[mtx][cm_row(u)][cm_col(u)]);
     }
   }
 }

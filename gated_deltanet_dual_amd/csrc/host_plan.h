@@ -76,7 +76,7 @@ struct ChunkLayout {
   int win = 0;
   int64_t slots = 0;                     // per-chunk slots of one pass
   size_t adj = 0, adj_bytes = 0;         // bwd: end-state adjoints [slots][H][D][D]
-  size_t cmat = 0, cmat_bytes = 0;       // six chunk matrices [slots][H][6][32][32]
+  size_t cmat = 0, cmat_bytes = 0;       // six chunk matrices [slots][H][6][32][32], each tile-major (chunk_common.h)
   size_t pack = 0, pack_bytes = 0;       // scan hand-over [slots][H][kScanPackFloats]
   size_t states = 0, states_bytes = 0;   // chunk-start states [slots][H][D][D]
   size_t l2f = 0, l2f_bytes = 0;         // q/k L2 factors [T][H][4]

@@ -179,7 +179,7 @@ struct BwdArgs {
   void *workspace;       // end-state adjoints [slots][H][D][D], then `tri`
   size_t workspace_bytes;
   int64_t T;
-  float *tri;            // per slot and head [slots][H][6][32][32]: T, T~, Mwo, Mwq, Mwk, Mw~ (set by the launcher)
+  float *tri;            // per slot and head [slots][H][6][32][32] (each matrix tile-major, chunk_common.h): T, T~, Mwo, Mwq, Mwk, Mw~ (set by the launcher)
   const float *fwd_cm;   // the same matrices from the forward's workspace, or NULL
   float *pack;           // bf16, d = 128: the pre-pass's hand-over to the scan, per slot and head (set by the launcher)
   // ckpt_in holds every chunk-start state at the chunk's checkpoint slot of
