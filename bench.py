@@ -53,13 +53,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FWD_BYTES_PER_TH = 3 * 256 + 8 + 256
 BWD_BYTES_PER_TH = 4 * 256 + 8 + 3 * 256 + 8
 # the backward pre-pass reads q, k, do and the gates of both streams (not v)
-# and the six chunk matrices, and hands the reverse scan, per (chunk slot,
+# and the six chunk matrices (their live parts, chunk_matrix_bytes), and hands the reverse scan, per (chunk slot,
 # head), R (128 x 128 fp32), W (hi + lo bf16), two fragment sets of K and the
 # chunk decay; the scan reads that and writes the chunk's end-state adjoint
 # (128 x 128 fp32) and K dS' (32 x 128 fp32) for the per-chunk pass
 PRE_BYTES_PER_TH = 3 * 256 + 8
 PACK_BYTES_PER_SLOT_HEAD = (128 * 128 + 1024 + 2048 + 2048 + 64) * 4
-PRE_BYTES_PER_SLOT_HEAD = 6 * 32 * 32 * 4 + PACK_BYTES_PER_SLOT_HEAD
 SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4 + 32 * 128 * 4
 # the forward's preparation pass reads q, k and the gates of both streams and
 # v, and writes the six 32 x 32 fp32 chunk matrices and the hand-over; the
@@ -69,9 +68,42 @@ SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4 + 32 * 128 *
 # carries Z = diag(D) T V, 32 x 128 fp32, in place of the backward's 128 x 128 R)
 FWD_PACK_BYTES_PER_SLOT_HEAD = (32 * 128 + 1024 + 2048 + 2048 + 64) * 4
 FWD_SCAN_BYTES_PER_SLOT_HEAD = FWD_PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4
-TRI_BYTES_PER_SLOT_HEAD = 6 * 32 * 32 * 4
+
+def chunk_matrix_live_bytes(B, has_noisy, C=32):
+    """Bytes of one (chunk, head) record of the six C x C fp32 chunk matrices
+    (T, T~, Mwo, Mwq, Mwk, Mw~) that are stored and read: the library moves
+    only the 64-byte half-rows whose masks can hold a non-zero entry (T, Mwo:
+    j <= i; T~: p_i <= j <= i; Mwq, Mwk: j < p_i; Mw~: j in i's block; the
+    noisy four not at all in a chunk without response rows)."""
+    live = 0
+    for mtx in range(6):
+        for row in range(C):
+            p = row & -B
+            for lo in (0, 16):
+                if mtx in (0, 2):
+                    on = lo <= row
+                elif not has_noisy:
+                    on = False
+                elif mtx == 1:
+                    on = lo <= row and lo + 15 >= p
+                elif mtx == 5:
+                    on = lo <= p + B - 1 and lo + 15 >= p
+                else:
+                    on = lo < p
+                live += 64 if on else 0
+    return live
+
+
+def chunk_matrix_bytes(cu_seqlens, prompt_lens, H, B, C=32):
+    """The chunk-matrix bytes one pass writes or reads for a packed batch."""
+    per = {nz: chunk_matrix_live_bytes(B, nz, C) for nz in (False, True)}
+    tot = 0
+    for i in range(len(prompt_lens)):
+        n, P = int(cu_seqlens[i + 1] - cu_seqlens[i]), int(prompt_lens[i])
+        for c in range((n + C - 1) // C):
+            tot += per[(c * C + C > P) and (P < n)]
+    return tot * H
 PREP_BYTES_PER_TH = 2 * 256 + 8
-PREP_BYTES_PER_SLOT_HEAD = TRI_BYTES_PER_SLOT_HEAD + FWD_PACK_BYTES_PER_SLOT_HEAD
 STEP_KERNELS = ("gdn_fwd_prep_kernel", "gdn_fwd_scan_kernel", "gdn_dual_fwd_kernel",
                 "gdn_bwd_pre_kernel", "gdn_bwd_scan_kernel", "gdn_bwd_chunk_kernel")
 
@@ -260,6 +292,7 @@ def run_headline(torch, g, wl, dev, timer, up, args):
     ckpt_bytes = n_slots * H * d * d * 4
     n_chunk_heads = H * sum((int(inp.cu_seqlens[i + 1] - inp.cu_seqlens[i]) + C - 1) // C
                             for i in range(vl.num_docs))
+    cm_bytes = chunk_matrix_bytes(inp.cu_seqlens, inp.prompt_lens, H, B, C)
 
     def step():
         g.gdn_dual_fwd(vl, *args10, B, out=(o, on), ckpt=ckpt, want_h_final=False, workspace=fws)
@@ -292,11 +325,11 @@ def run_headline(torch, g, wl, dev, timer, up, args):
         g.timing_reset()
         alg = {
             "gdn_fwd_prep_kernel": PREP_BYTES_PER_TH * (th_total + th_resp) + 256 * th_total
-                                   + PREP_BYTES_PER_SLOT_HEAD * n_chunk_heads,
+                                   + FWD_PACK_BYTES_PER_SLOT_HEAD * n_chunk_heads + cm_bytes,
             "gdn_fwd_scan_kernel": FWD_SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
-            "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes
-                                   + TRI_BYTES_PER_SLOT_HEAD * n_chunk_heads,
-            "gdn_bwd_pre_kernel": PRE_BYTES_PER_TH * (th_total + th_resp) + PRE_BYTES_PER_SLOT_HEAD * n_chunk_heads,
+            "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes + cm_bytes,
+            "gdn_bwd_pre_kernel": PRE_BYTES_PER_TH * (th_total + th_resp) + PACK_BYTES_PER_SLOT_HEAD * n_chunk_heads
+                                  + cm_bytes,
             "gdn_bwd_scan_kernel": SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_bwd_chunk_kernel": BWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
         }
