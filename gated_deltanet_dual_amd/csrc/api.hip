@@ -347,6 +347,10 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
   // the forward's chunk matrices, when its workspace held them
   a.fwd_cm = (fwd_workspace && fwd_workspace_bytes(vi, shape) > 0) ? reinterpret_cast<const float *>(fwd_workspace)
                                                                       : nullptr;
+  // and its scan hand-over, whose K fragment sets the reverse scan reuses
+  a.fwd_pack = a.fwd_cm ? reinterpret_cast<const float *>(reinterpret_cast<const char *>(fwd_workspace) +
+                                                          fwd_layout(vi, shape, 0).pack)
+                        : nullptr;
   a.d_o = d_o; a.d_on = d_on; a.dh_final = dh_final;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dqn = dqn; a.dkn = dkn; a.dvn = dvn;
   a.dalpha = dalpha; a.dbeta = dbeta; a.dalpha_n = dalpha_n; a.dbeta_n = dbeta_n; a.dh0 = dh0;

@@ -891,6 +891,7 @@ static hipError_t launch_bwd_chunked(const BwdArgs &a_in, hipStream_t st, const 
     aw.pack = p.pack;
     const bool own_cm = !(a.fwd_cm && p.win == 0);
     if (!own_cm) aw.tri = const_cast<float *>(a.fwd_cm);  // read only from here on
+    aw.kpack = own_cm ? nullptr : a.fwd_pack;  // the forward's K fragment sets, when its hand-over is there
     if (p.stride > 1) {
       // the forward's hand-over for the rebuild (with the chunk matrices,
       // when they are not the forward's)
@@ -944,6 +945,7 @@ static hipError_t launch_bwd_chunked(const BwdArgs &a_in, hipStream_t st, const 
       sa.final_out = j == nwin - 1 ? a.dh0 : p.carry;
       sa.states = p.adj;
       sa.kx = p.pack;  // K dS' per chunk, for the per-chunk pass
+      sa.kpack = aw.kpack;
       TimedLaunch tl(K_BWD_SCAN, st);
       hipError_t e1;
       if (p.win > 0) {

@@ -130,14 +130,16 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
   lds_barrier();
 
   const float lgC = sm.lg[C - 1];
-  // the fragment sets (one per wave, stored as they are consumed)
-  {
+  // the fragment sets (one per wave, stored as they are consumed), unless
+  // the scan reads the forward's (the same values: k rows, zero past the
+  // document end)
+  if (!a.kpack) {
     // K: rows past the document end are zero
     const bool ok = c0 + ka_row < n;
     const uint4 v = ok ? make_uint4(ka0.x, ka0.y, ka1.x, ka1.y) : make_uint4(0u, 0u, 0u, 0u);
     reinterpret_cast<uint4 *>(pack + kPackKA)[wave * 64 + lane] = v;
   }
-  {
+  if (!a.kpack) {
     // K^T tile kt = wave: d_k row 16 kt + (l & 15), tokens 4 g .. +3, 16 + 4 g .. +3
     const u16 *col = &sm.xt[1][16 * wave + cl][0];
     const uint2 lo4 = *reinterpret_cast<const uint2 *>(col + g4);

@@ -241,10 +241,17 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
       p.r[j] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     // shared unit j * sNW + wave (clamped: the last round is partial, and
-    // its surplus loads are repeats that are never published)
+    // its surplus loads are repeats that are never published); the K units
+    // (all but W's first four) from kpack's hand-over when it is given
     const uint4 *ps = reinterpret_cast<const uint4 *>(pk + kPackW);
+    const uint4 *psk = ps;  // (the forward scan is compiled without kpack)
+    if constexpr (REVERSE)
+      if (a.kpack) psk = reinterpret_cast<const uint4 *>(a.kpack + ((size_t)wslot(c) * H + h) * kPackWords + kPackW);
+    // (round j holds units j sNW .. j sNW + sNW - 1: W's in the first rounds)
+    static_assert(((kPackKA - kPackW) / 256) % sNW == 0, "W's units must fill whole rounds");
 #pragma unroll
-    for (int j = 0; j < sSHW; ++j) p.sh[j] = ps[min(j * sNW + wave, sSH - 1) * 64 + lane];
+    for (int j = 0; j < sSHW; ++j)
+      p.sh[j] = (j * sNW < (kPackKA - kPackW) / 256 ? ps : psk)[min(j * sNW + wave, sSH - 1) * 64 + lane];
     p.gc = pk[kPackG];
   };
   auto bf = [](const uint4 &v) { return __builtin_bit_cast(bf16x8, v); };

@@ -156,6 +156,11 @@ struct ScanArgs {
   // chunk's R area in the hand-over (kx = pack): each wave writes only over
   // its own R slab, after its step has consumed it.  NULL: not written.
   float *kx;
+  // NULL, or a hand-over of the same slot layout whose K fragment units (the
+  // A operands of K X and K^T Y, identical in every hand-over of the chunk)
+  // the reverse scan reads instead of pack's (the forward's hand-over; the
+  // forward scan ignores this field).
+  const float *kpack;
 };
 hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st);
 // The runs' start states from their transfer maps M (identity-init, homog
@@ -181,6 +186,11 @@ struct BwdArgs {
   int64_t T;
   float *tri;            // per slot and head [slots][H][6][32][32] (each matrix tile-major, chunk_common.h): T, T~, Mwo, Mwq, Mwk, Mw~ (set by the launcher)
   const float *fwd_cm;   // the same matrices from the forward's workspace, or NULL
+  const float *fwd_pack; // the forward's scan hand-over in the same workspace, or NULL
+  // the hand-over whose K fragment sets the reverse scan reads (the forward's,
+  // when its chunk matrices are reused); the pre-pass then does not write
+  // its own (set by the launcher)
+  const float *kpack;
   float *pack;           // bf16, d = 128: the pre-pass's hand-over to the scan, per slot and head (set by the launcher)
   // ckpt_in holds every chunk-start state at the chunk's checkpoint slot of
   // stride 1 (a checkpoint buffer) rather than at the (window) slot
