@@ -44,6 +44,7 @@
 // parallel (the backward's rebuild when only every s-th state was kept).
 #include "bwd_common.h"
 #include "device_common.h"
+#include "host_plan.h"
 #include "kernels.h"
 #include "slab.h"
 
@@ -52,7 +53,11 @@ namespace flare {
 namespace {
 
 constexpr int sC = 32, sD = 128, sNW = 2, sNQ = sD / (16 * sNW);  // waves per workgroup, workgroups per (doc, head)
-constexpr int sRING = 4;                                            // register ring depth (chunks)
+// register ring depth (chunks): 4 keeps one workgroup per CU (the deep
+// ring's registers take a SIMD's whole file per wave); 2 lets the scan's
+// registers fit two workgroups per CU (2 waves per SIMD), so that a second
+// chain hides each one's latency (launch_scan_d128 picks per launch)
+constexpr int sRING_DEEP = 4, sRING_SHALLOW = 2;
 typedef unsigned v4u __attribute__((ext_vector_type(4)));           // a native vector for the nontemporal builtin
 // the operands every slab needs (W, then K and K^T fragments: contiguous in the
 // hand-over), in 1 KB units of 64 lanes x 16 bytes, dealt round-robin to the waves
@@ -81,8 +86,8 @@ struct ScanSmem {
 // ZRHS: the right-hand side is K^T Z with Z a C x d_v matrix (stored as
 // slabs, [slab 8][tile 2][lane 64][4], in the R area of the hand-over), added
 // to W (K X) before the K^T product; else a full 128 x 128 R.
-template <bool REVERSE, bool ZRHS>
-__global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs a) {
+template <bool REVERSE, bool ZRHS, int RING>
+__global__ __launch_bounds__(64 * (sNW + 1), RING == sRING_SHALLOW ? 2 : 1) void gdn_scan_d128_kernel(ScanArgs a) {
   using ScanRing = ScanRing<ZRHS>;
   constexpr int C = sC, D = sD;
   __shared__ ScanSmem sm;
@@ -348,23 +353,35 @@ __global__ __launch_bounds__(64 * (sNW + 1)) void gdn_scan_d128_kernel(ScanArgs 
     load_ring(p, refill);
   };
 
-  // sRING operand sets in rotation, sRING - 1 chunks in flight while one
+  // RING operand sets in rotation, RING - 1 chunks in flight while one
   // computes; LAG: the first chunk's shared operands are published up front
-  ScanRing p0, p1, p2, p3;
-  static_assert(sRING == 4, "the rotation below names four sets");
-  load_ring(p0, at(0));
-  load_ring(p1, at(1));
-  load_ring(p2, at(2));
-  load_ring(p3, at(3));
-  if constexpr (LAG) publish(p0, 0);
-  for (int i = 0; i < nchunks; i += 4) {
-    step(p0, p1, i, at(i + 4));
-    if (i + 1 >= nchunks) break;
-    step(p1, p2, i + 1, at(i + 5));
-    if (i + 2 >= nchunks) break;
-    step(p2, p3, i + 2, at(i + 6));
-    if (i + 3 >= nchunks) break;
-    step(p3, p0, i + 3, at(i + 7));
+  static_assert(RING == sRING_DEEP || RING == sRING_SHALLOW, "the rotations below name four or two sets");
+  if constexpr (RING == sRING_DEEP) {
+    ScanRing p0, p1, p2, p3;
+    load_ring(p0, at(0));
+    load_ring(p1, at(1));
+    load_ring(p2, at(2));
+    load_ring(p3, at(3));
+    if constexpr (LAG) publish(p0, 0);
+    for (int i = 0; i < nchunks; i += 4) {
+      step(p0, p1, i, at(i + 4));
+      if (i + 1 >= nchunks) break;
+      step(p1, p2, i + 1, at(i + 5));
+      if (i + 2 >= nchunks) break;
+      step(p2, p3, i + 2, at(i + 6));
+      if (i + 3 >= nchunks) break;
+      step(p3, p0, i + 3, at(i + 7));
+    }
+  } else {
+    ScanRing p0, p1;
+    load_ring(p0, at(0));
+    load_ring(p1, at(1));
+    if constexpr (LAG) publish(p0, 0);
+    for (int i = 0; i < nchunks; i += 2) {
+      step(p0, p1, i, at(i + 2));
+      if (i + 1 >= nchunks) break;
+      step(p1, p0, i + 1, at(i + 3));
+    }
   }
   if constexpr (LAG) lds_barrier();  // the last step's staging, for the store wave
   if (a.final_out && write_final) {
@@ -498,9 +515,24 @@ hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st) {
   const int64_t pairs = (a.seg_span > 0 || a.win_len > 0 ? a.units : a.num_docs) * a.H;
   const int64_t groups = (pairs + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * sNQ)), block(64 * (sNW + 1));
-  // the reverse recurrence carries a full R, the forward one K^T Z
-  if (reverse) hipLaunchKernelGGL((gdn_scan_d128_kernel<true, false>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((gdn_scan_d128_kernel<false, true>), grid, block, 0, st, a);
+  // the reverse recurrence carries a full R, the forward one K^T Z.  The
+  // shallow ring (two workgroups per CU) when the launch has more workgroups
+  // than CUs and either stores nothing per chunk (a long document's transfer
+  // map and offset runs: latency-bound, a second chain per CU hides it) or
+  // has many short chains (their start-up latency dominates); a launch that
+  // streams every chunk's state out keeps the deep ring, one per CU (measured
+  // at 8 x 4096 and 32 x 1024 tokens, 16 heads: the shallow ring was 4-27 %
+  // slower there, 20-26 % faster for the runs and at 128 x 256)
+  const bool stores = a.states || a.ckpt || a.kx;
+  const bool shallow = grid.x > (unsigned)kScanWorkgroupTarget &&
+                       (!stores || grid.x >= 16u * (unsigned)kScanWorkgroupTarget);
+  if (reverse) {
+    if (shallow) hipLaunchKernelGGL((gdn_scan_d128_kernel<true, false, sRING_SHALLOW>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gdn_scan_d128_kernel<true, false, sRING_DEEP>), grid, block, 0, st, a);
+  } else {
+    if (shallow) hipLaunchKernelGGL((gdn_scan_d128_kernel<false, true, sRING_SHALLOW>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((gdn_scan_d128_kernel<false, true, sRING_DEEP>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
