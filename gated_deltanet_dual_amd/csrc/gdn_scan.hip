@@ -403,13 +403,18 @@ __global__ __launch_bounds__(64 * (sNW + 1), RING == sRING_SHALLOW ? 2 : 1) void
 // The runs' start values, one workgroup of 8 waves per (document, head), wave
 // w the 16-column slab w of X, in scan order over the document's runs:
 //   seg_out[unit_g] = X_g,  X_{g+1} = M_g X_g + N_g
-// (M_g X_g on the matrix cores, M split hi + lo as A fragments from global
-// memory, X as split B fragments from its accumulators, the slab
-// k-permutation of slab.h over d_k).
+// (M_g X_g on the matrix cores, M split hi + lo as A fragments, X as split B
+// fragments from its accumulators, the slab k-permutation of slab.h over
+// d_k).  The maps pass through LDS, double-buffered by step parity: the
+// workgroup loads the next map (8 float4s per thread, once for all waves)
+// and the next offset slab while the current step runs from the other
+// buffer, so the sequential steps do not wait on HBM.
+constexpr int sLDM = sD + 4;  // map rows in LDS, padded
 template <bool REVERSE>
 __global__ __launch_bounds__(512) void gdn_scan_compose_kernel(ScanArgs a, const float *M, const float *Nb,
                                                                float *seg_out) {
-  constexpr int C = sC, D = sD;
+  constexpr int C = sC, D = sD, NT = 512;
+  __shared__ float mb[2][D][sLDM];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
   const int doc = blockIdx.x / a.H, h = blockIdx.x % a.H;
@@ -419,27 +424,69 @@ __global__ __launch_bounds__(512) void gdn_scan_compose_kernel(ScanArgs a, const
   const int nruns = nchunks == 0 ? 0 : (nchunks + a.seg_span - 1) / a.seg_span;
   const int64_t ubase = (int64_t)a.cu[doc] / ((int64_t)C * a.seg_span) + doc;
   const int dv0 = 16 * wave;
+  // run unit of step j (scan order)
+  auto unit_of = [&](int j) { return ubase + (REVERSE ? nruns - 1 - j : j); };
+  // thread tid's share of a map: float4 f = e NT + tid, row f / 32, columns 4 (f % 32) ..
+  constexpr int NE = D * D / 4 / NT;
+  float4 m0r, m1r, m2r, m3r, m4r, m5r, m6r, m7r;  // named: an array here would live in scratch
+  static_assert(NE == 8, "eight float4s per thread");
+#define FLARE_MAP_LOAD(Mg)                                                                       \
+  do {                                                                                         \
+    const float *mg_ = (Mg);                                                                   \
+    m0r = *reinterpret_cast<const float4 *>(mg_ + 4 * (size_t)(0 * NT + tid));                  \
+    m1r = *reinterpret_cast<const float4 *>(mg_ + 4 * (size_t)(1 * NT + tid));                  \
+    m2r = *reinterpret_cast<const float4 *>(mg_ + 4 * (size_t)(2 * NT + tid));                  \
+    m3r = *reinterpret_cast<const float4 *>(mg_ + 4 * (size_t)(3 * NT + tid));                  \
+    m4r = *reinterpret_cast<const float4 *>(mg_ + 4 * (size_t)(4 * NT + tid));                  \
+    m5r = *reinterpret_cast<const float4 *>(mg_ + 4 * (size_t)(5 * NT + tid));                  \
+    m6r = *reinterpret_cast<const float4 *>(mg_ + 4 * (size_t)(6 * NT + tid));                  \
+    m7r = *reinterpret_cast<const float4 *>(mg_ + 4 * (size_t)(7 * NT + tid));                  \
+  } while (0)
+  auto put_one = [&](int buf, int e, const float4 &v) {
+    const int f = e * NT + tid;
+    *reinterpret_cast<float4 *>(&mb[buf][f >> 5][4 * (f & 31)]) = v;
+  };
+  auto put_map = [&](int buf) {
+    put_one(buf, 0, m0r); put_one(buf, 1, m1r); put_one(buf, 2, m2r); put_one(buf, 3, m3r);
+    put_one(buf, 4, m4r); put_one(buf, 5, m5r); put_one(buf, 6, m6r); put_one(buf, 7, m7r);
+  };
+  floatx4 Yn[8];  // the next step's offset slab
+  auto load_off = [&](int j) {
+    const float *Ng = Nb + ((size_t)unit_of(j) * H + h) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Yn[kt][r] = Ng[(size_t)(16 * kt + g4 + r) * D + dv0 + cl];
+  };
+  auto map_ptr = [&](int j) { return M + ((size_t)unit_of(j) * H + h) * D * D; };
   floatx4 X[8];
   const float *src = a.init ? a.init + ((size_t)(a.slot ? a.slot[doc] : doc) * H + h) * D * D : nullptr;
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) X[kt][r] = src ? src[(size_t)(16 * kt + g4 + r) * D + dv0 + cl] : 0.f;
+  if (nruns > 1) {
+    FLARE_MAP_LOAD(map_ptr(0));
+    load_off(0);
+    put_map(0);
+  }
+  lds_barrier();
   for (int j = 0; j < nruns; ++j) {
-    const int g = REVERSE ? nruns - 1 - j : j;
-    const int64_t u = ubase + g;
-    float *so = seg_out + ((size_t)u * H + h) * D * D;
+    float *so = seg_out + ((size_t)unit_of(j) * H + h) * D * D;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) so[(size_t)(16 * kt + g4 + r) * D + dv0 + cl] = X[kt][r];
     if (j == nruns - 1) break;  // the last run's end value is the scan's own
-    const float *Mg = M + ((size_t)u * H + h) * D * D, *Ng = Nb + ((size_t)u * H + h) * D * D;
     floatx4 Y[8];
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Y[kt][r] = Ng[(size_t)(16 * kt + g4 + r) * D + dv0 + cl];
+    for (int kt = 0; kt < 8; ++kt) Y[kt] = Yn[kt];
+    const bool more = j + 1 < nruns - 1;  // the next step multiplies too
+    if (more) {
+      FLARE_MAP_LOAD(map_ptr(j + 1));
+      load_off(j + 1);
+    }
+    const float (*Mg)[sLDM] = mb[j & 1];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       // X rows 32 ks + 4 g + e (e < 4) and 32 ks + 16 + 4 g + e - 4 as the B operand
@@ -450,7 +497,7 @@ __global__ __launch_bounds__(512) void gdn_scan_compose_kernel(ScanArgs a, const
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         // A: rows 16 kt + (l & 15) of M, columns in the same permutation
-        const float *mr = Mg + (size_t)(16 * kt + cl) * D + 32 * ks;
+        const float *mr = &Mg[16 * kt + cl][32 * ks];
         const float4 m0 = *reinterpret_cast<const float4 *>(mr + g4);
         const float4 m1 = *reinterpret_cast<const float4 *>(mr + 16 + g4);
         const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
@@ -463,7 +510,12 @@ __global__ __launch_bounds__(512) void gdn_scan_compose_kernel(ScanArgs a, const
     }
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) X[kt] = Y[kt];
+    // the next map into the other buffer (its last reader was step j - 1,
+    // before the previous barrier)
+    if (more) put_map((j + 1) & 1);
+    lds_barrier();
   }
+#undef FLARE_MAP_LOAD
 }
 
 hipError_t launch_scan_compose_d128(const ScanArgs &a, const float *M, const float *Nb, float *seg_out, bool reverse,
