@@ -377,6 +377,10 @@ flare_status flare_gdn_dual_bwd(const flare_varlen *varlen, const flare_gdn_shap
     a.f.scan_span = scan_seg_span(vi, shape->num_heads);
     a.f.scan_units = a.f.scan_span > 0 ? ckpt_num_slots(vi, a.f.scan_span) : 0;
     a.f.scan_ws = reinterpret_cast<float *>(w + L.seg);
+    // the forward's runs' transfer maps, at the start of its run buffers
+    if (a.fwd_cm && a.f.scan_span > 0)
+      a.fwd_maps = reinterpret_cast<const float *>(reinterpret_cast<const char *>(fwd_workspace) +
+                                                   fwd_seg_offset(vi, shape));
   }
   return hip_status(launch_gdn_bwd(a, (hipStream_t)stream, &p), "gdn_dual_bwd launch");
 }

@@ -954,7 +954,7 @@ static hipError_t launch_bwd_chunked(const BwdArgs &a_in, hipStream_t st, const 
         sa.units = a.f.num_docs;
         e1 = launch_scan_d128(sa, true, st);
       } else {
-        e1 = scan_d128_runs(sa, true, a.f.scan_span, a.f.scan_units, a.f.scan_ws, st);
+        e1 = scan_d128_runs(sa, true, a.f.scan_span, a.f.scan_units, a.f.scan_ws, st, own_cm ? nullptr : a.fwd_maps);
       }
       if (e1 != hipSuccess) return e1;
     }

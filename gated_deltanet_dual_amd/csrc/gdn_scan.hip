@@ -408,9 +408,11 @@ __global__ __launch_bounds__(64 * (sNW + 1), RING == sRING_SHALLOW ? 2 : 1) void
 // d_k).  The maps pass through LDS, double-buffered by step parity: the
 // workgroup loads the next map (8 float4s per thread, once for all waves)
 // and the next offset slab while the current step runs from the other
-// buffer, so the sequential steps do not wait on HBM.
+// buffer, so the sequential steps do not wait on HBM.  MT: the maps are
+// given transposed (M_g^T stored), and the A fragments are read down the
+// staged columns.
 constexpr int sLDM = sD + 4;  // map rows in LDS, padded
-template <bool REVERSE>
+template <bool REVERSE, bool MT>
 __global__ __launch_bounds__(512) void gdn_scan_compose_kernel(ScanArgs a, const float *M, const float *Nb,
                                                                float *seg_out) {
   constexpr int C = sC, D = sD, NT = 512;
@@ -497,10 +499,20 @@ __global__ __launch_bounds__(512) void gdn_scan_compose_kernel(ScanArgs a, const
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         // A: rows 16 kt + (l & 15) of M, columns in the same permutation
-        const float *mr = &Mg[16 * kt + cl][32 * ks];
-        const float4 m0 = *reinterpret_cast<const float4 *>(mr + g4);
-        const float4 m1 = *reinterpret_cast<const float4 *>(mr + 16 + g4);
-        const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float mv[8];
+        if constexpr (MT) {  // M[i][k] = staged[k][i]: one column down the staged rows
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            mv[e] = Mg[32 * ks + g4 + e][16 * kt + cl];
+            mv[4 + e] = Mg[32 * ks + 16 + g4 + e][16 * kt + cl];
+          }
+        } else {
+          const float *mr = &Mg[16 * kt + cl][32 * ks];
+          const float4 m0 = *reinterpret_cast<const float4 *>(mr + g4);
+          const float4 m1 = *reinterpret_cast<const float4 *>(mr + 16 + g4);
+          mv[0] = m0.x; mv[1] = m0.y; mv[2] = m0.z; mv[3] = m0.w;
+          mv[4] = m1.x; mv[5] = m1.y; mv[6] = m1.z; mv[7] = m1.w;
+        }
         bf16x8 ah, al;
         split8(mv, ah, al);
         mma_bf16(Y[kt], ah, bh);
@@ -519,14 +531,21 @@ __global__ __launch_bounds__(512) void gdn_scan_compose_kernel(ScanArgs a, const
 }
 
 hipError_t launch_scan_compose_d128(const ScanArgs &a, const float *M, const float *Nb, float *seg_out, bool reverse,
-                                    hipStream_t st) {
+                                    hipStream_t st, bool m_transposed) {
   const dim3 grid((unsigned)(a.num_docs * a.H)), block(512);
-  if (reverse) hipLaunchKernelGGL(gdn_scan_compose_kernel<true>, grid, block, 0, st, a, M, Nb, seg_out);
-  else hipLaunchKernelGGL(gdn_scan_compose_kernel<false>, grid, block, 0, st, a, M, Nb, seg_out);
+  if (reverse && m_transposed)
+    hipLaunchKernelGGL((gdn_scan_compose_kernel<true, true>), grid, block, 0, st, a, M, Nb, seg_out);
+  else if (reverse)
+    hipLaunchKernelGGL((gdn_scan_compose_kernel<true, false>), grid, block, 0, st, a, M, Nb, seg_out);
+  else if (m_transposed)
+    hipLaunchKernelGGL((gdn_scan_compose_kernel<false, true>), grid, block, 0, st, a, M, Nb, seg_out);
+  else
+    hipLaunchKernelGGL((gdn_scan_compose_kernel<false, false>), grid, block, 0, st, a, M, Nb, seg_out);
   return hipGetLastError();
 }
 
-hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t units, float *ws, hipStream_t st) {
+hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t units, float *ws, hipStream_t st,
+                          const float *maps_t) {
   if (span <= 0) return launch_scan_d128(a, reverse, st);
   const size_t per = (size_t)units * a.H * sD * sD;
   float *const M = ws, *const Nb = ws + per, *const S = ws + 2 * per;
@@ -538,14 +557,17 @@ hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t uni
   r.kx = nullptr;
   r.final_out = nullptr;
   r.seg_init = nullptr;
-  // the runs' transfer maps (from the identity, no right-hand side)
-  ScanArgs m = r;
-  m.init = nullptr;
-  m.identity_init = 1;
-  m.homog = 1;
-  m.seg_final = M;
-  hipError_t e = launch_scan_d128(m, reverse, st);
-  if (e != hipSuccess) return e;
+  // the runs' transfer maps (from the identity, no right-hand side), unless given
+  hipError_t e = hipSuccess;
+  if (!maps_t) {
+    ScanArgs m = r;
+    m.init = nullptr;
+    m.identity_init = 1;
+    m.homog = 1;
+    m.seg_final = M;
+    e = launch_scan_d128(m, reverse, st);
+    if (e != hipSuccess) return e;
+  }
   // their offsets (from zero)
   ScanArgs z = r;
   z.init = nullptr;
@@ -555,7 +577,7 @@ hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t uni
   // the runs' start values in scan order, then every run from its start value
   ScanArgs c = a;
   c.seg_span = span;
-  e = launch_scan_compose_d128(c, M, Nb, S, reverse, st);
+  e = launch_scan_compose_d128(c, maps_t ? maps_t : M, Nb, S, reverse, st, maps_t != nullptr);
   if (e != hipSuccess) return e;
   c.units = units;
   c.seg_init = S;

@@ -167,12 +167,15 @@ hipError_t launch_scan_d128(const ScanArgs &a, bool reverse, hipStream_t st);
 // runs) and offsets N (zero-init runs): in scan order X_0 = init (or zero),
 // seg_out[unit_g] = X_g, X_{g+1} = M_g X_g + N_g (gdn_scan.hip).
 hipError_t launch_scan_compose_d128(const ScanArgs &a, const float *M, const float *Nb, float *seg_out, bool reverse,
-                                    hipStream_t st);
+                                    hipStream_t st, bool m_transposed = false);
 // The scan of a, in one chain per (document, head) when span == 0, else in
 // parallel runs of span chunks joined by their transfer maps: the maps, the
 // offsets, the composition, then every run from its start value (ws holds
 // 3 x units x H x 128 x 128 fp32).
-hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t units, float *ws, hipStream_t st);
+// maps_t: the runs' transfer maps given transposed (the reverse scan taking
+// the forward's), so that their scan pass is skipped; NULL: formed here.
+hipError_t scan_d128_runs(const ScanArgs &a, bool reverse, int span, int64_t units, float *ws, hipStream_t st,
+                          const float *maps_t = nullptr);
 
 struct BwdArgs {
   FwdArgs f;
@@ -191,6 +194,10 @@ struct BwdArgs {
   // when its chunk matrices are reused); the pre-pass then does not write
   // its own (set by the launcher)
   const float *kpack;
+  // the forward's runs' transfer maps (long documents, one pass), or NULL: the
+  // reverse scan's map of a run is the transpose of the forward's (its chain
+  // matrix is the forward's transposed), so it composes with those
+  const float *fwd_maps;
   float *pack;           // bf16, d = 128: the pre-pass's hand-over to the scan, per slot and head (set by the launcher)
   // ckpt_in holds every chunk-start state at the chunk's checkpoint slot of
   // stride 1 (a checkpoint buffer) rather than at the (window) slot

@@ -207,23 +207,63 @@ def test_long_document_parallel_runs_full_size(g, dev):
     """One packed row of 32768 tokens holding a single document (prompt 8192),
     16 heads, d = 128, bf16: the state scans run as parallel runs joined by
     their transfer maps; forward and reverse mode against the oracle on every
-    head, with h0 and dh_final."""
+    head, with h0 and dh_final; the reverse mode also composing with the
+    forward's transfer maps (transposed) from the forward's workspace."""
     import torch
     inp = wl.gdn_inputs([32768], [8192], 16, 128, 128, 4, seed=17, with_h0=True, with_grads=True)
     dhf = (np.random.default_rng(18).standard_normal((1, 16, 128, 128)) / 16).astype(np.float32)
     vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
     args = fwd_args(inp, dev)
     h0 = to_dev(inp.h0, dev)
-    o, on, hf, ck = g.gdn_dual_fwd(vl, *args, 4, h0=h0, want_ckpt=True)
+    fws = torch.empty((g.workspace_bytes(vl, 16, 128, 4, g.BF16),), dtype=torch.uint8, device=dev)
+    o, on, hf, ck = g.gdn_dual_fwd(vl, *args, 4, h0=h0, want_ckpt=True, workspace=fws)
     gr = g.gdn_dual_bwd(vl, *args, 4, ck, to_dev(inp.do, dev, True), to_dev(inp.don, dev, True), h0=h0,
                         dh_final=to_dev(dhf, dev))
+    grf = g.gdn_dual_bwd(vl, *args, 4, ck, to_dev(inp.do, dev, True), to_dev(inp.don, dev, True), h0=h0,
+                         dh_final=to_dev(dhf, dev), fwd_workspace=fws)
     torch.cuda.synchronize()
     ro, ron, rhf = oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(), 4,
                                        h0=inp.h0)
     e = {"o": rel_rms(to_np(o), ro), "on": rel_rms(to_np(on), ron), "h_final": rel_rms(to_np(hf), rhf)}
     print("long_doc fwd", e)
     assert max(e.values()) <= TOL_BF16, e
-    check(inp, gr, ref_bwd(inp, dhf=dhf), TOL_BF16, "long_doc")
+    want = ref_bwd(inp, dhf=dhf)
+    check(inp, gr, want, TOL_BF16, "long_doc")
+    check(inp, grf, want, TOL_BF16, "long_doc_fwd_maps")
+
+
+def test_parallel_runs_long_memory(g, dev):
+    """Parallel runs whose transfer maps are far from zero: decays in
+    [0.999, 1) per token, so a 2048-token run keeps about e^-1 of its start
+    value (with the smooth gates of the other tests the maps underflow to
+    zero and the runs' composition reduces to the offsets).  Two documents of
+    8192 and 3000 tokens at 16 heads (runs of 64 chunks), h0 and dh_final:
+    forward and reverse mode against the oracle, the reverse mode once with
+    its own transfer maps and once composing with the forward's (transposed)."""
+    import torch
+    inp = wl.gdn_inputs([8192, 3000], [100, 36], 16, 128, 128, 4, seed=23, with_h0=True,
+                        with_grads=True)
+    rng = np.random.default_rng(24)
+    inp.alpha = (0.999 + 0.001 * rng.random(inp.alpha.shape)).astype(np.float32)
+    inp.alpha_n = (0.999 + 0.001 * rng.random(inp.alpha_n.shape)).astype(np.float32)
+    dhf = (rng.standard_normal((2, 16, 128, 128)) / 16).astype(np.float32)
+    vl = g.Varlen(inp.cu_seqlens, inp.prompt_lens, dev)
+    args = fwd_args(inp, dev)
+    h0 = to_dev(inp.h0, dev)
+    fws = torch.empty((g.workspace_bytes(vl, 16, 128, 4, g.BF16),), dtype=torch.uint8, device=dev)
+    o, on, hf, ck = g.gdn_dual_fwd(vl, *args, 4, h0=h0, want_ckpt=True, workspace=fws)
+    do, don = to_dev(inp.do, dev, True), to_dev(inp.don, dev, True)
+    gr = g.gdn_dual_bwd(vl, *args, 4, ck, do, don, h0=h0, dh_final=to_dev(dhf, dev))
+    grf = g.gdn_dual_bwd(vl, *args, 4, ck, do, don, h0=h0, dh_final=to_dev(dhf, dev), fwd_workspace=fws)
+    torch.cuda.synchronize()
+    ro, ron, rhf = oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(), 4,
+                                       h0=inp.h0)
+    e = {"o": rel_rms(to_np(o), ro), "on": rel_rms(to_np(on), ron), "h_final": rel_rms(to_np(hf), rhf)}
+    print("long_memory fwd", e)
+    assert max(e.values()) <= TOL_BF16, e
+    want = ref_bwd(inp, dhf=dhf)
+    check(inp, gr, want, TOL_BF16, "long_memory")
+    check(inp, grf, want, TOL_BF16, "long_memory_fwd_maps")
 
 
 def test_parallel_runs_ragged_documents(g, dev):

@@ -134,7 +134,9 @@ def test_tags_bit_exact_through_parallel_runs(g, dev):
     run as parallel runs joined by their transfer maps (one 8192-token and one
     3000-token document at 16 heads): forward and reverse mode still equal the
     oracle bit for bit on the integer tags (the transfer maps and offsets of
-    the runs are then integer matrices too)."""
+    the runs are then integer matrices too).  The reverse mode runs twice:
+    forming its own transfer maps, and composing with the forward's
+    (transposed) from the forward's workspace."""
     import torch
     docs = [(8192, 100), (3000, 36)]
     B = 4
@@ -143,9 +145,12 @@ def test_tags_bit_exact_through_parallel_runs(g, dev):
     args = fwd_args(inp, dev)
     h0 = to_dev(inp.h0, dev)
     dhf = inp.extra["dhf"]
-    o, on, hf, ck = g.gdn_dual_fwd(vl, *args, B, h0=h0, scale=1.0, want_ckpt=True)
+    fws = torch.empty((g.workspace_bytes(vl, inp.H, 128, B, g.BF16),), dtype=torch.uint8, device=dev)
+    o, on, hf, ck = g.gdn_dual_fwd(vl, *args, B, h0=h0, scale=1.0, want_ckpt=True, workspace=fws)
     gr = g.gdn_dual_bwd(vl, *args, B, ck, to_dev(inp.do, dev, True), to_dev(inp.don, dev, True), h0=h0,
                         dh_final=to_dev(dhf, dev), scale=1.0)
+    grf = g.gdn_dual_bwd(vl, *args, B, ck, to_dev(inp.do, dev, True), to_dev(inp.don, dev, True), h0=h0,
+                         dh_final=to_dev(dhf, dev), scale=1.0, fwd_workspace=fws)
     torch.cuda.synchronize()
     ro, ron, rhf = oracle.gdn_dual_fwd(inp.cu_seqlens, inp.prompt_lens, *inp.clean_args(), *inp.noisy_args(), B,
                                        h0=inp.h0, scale=1.0)
@@ -157,3 +162,4 @@ def test_tags_bit_exact_through_parallel_runs(g, dev):
     for name in GRADS:
         ref = bf16_exact(want[name]) if name in IO_GRADS else want[name]
         np.testing.assert_array_equal(to_np(gr[name]), ref, err_msg=name)
+        np.testing.assert_array_equal(to_np(grf[name]), ref, err_msg=name + " (forward's maps)")
