@@ -59,6 +59,9 @@ BWD_BYTES_PER_TH = 4 * 256 + 8 + 3 * 256 + 8
 # (128 x 128 fp32) and K dS' (32 x 128 fp32) for the per-chunk pass
 PRE_BYTES_PER_TH = 3 * 256 + 8
 PACK_BYTES_PER_SLOT_HEAD = (128 * 128 + 1024 + 2048 + 2048 + 64) * 4
+# the same without the two K fragment sets, which the reverse scan takes from
+# the forward's hand-over when the backward reuses the forward's workspace
+PRE_PACK_BYTES_PER_SLOT_HEAD = (128 * 128 + 1024 + 64) * 4
 SCAN_BYTES_PER_SLOT_HEAD = PACK_BYTES_PER_SLOT_HEAD + 128 * 128 * 4 + 32 * 128 * 4
 # the forward's preparation pass reads q, k and the gates of both streams and
 # v, and writes the six 32 x 32 fp32 chunk matrices and the hand-over; the
@@ -328,7 +331,7 @@ def run_headline(torch, g, wl, dev, timer, up, args):
                                    + FWD_PACK_BYTES_PER_SLOT_HEAD * n_chunk_heads + cm_bytes,
             "gdn_fwd_scan_kernel": FWD_SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_dual_fwd_kernel": FWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes + cm_bytes,
-            "gdn_bwd_pre_kernel": PRE_BYTES_PER_TH * (th_total + th_resp) + PACK_BYTES_PER_SLOT_HEAD * n_chunk_heads
+            "gdn_bwd_pre_kernel": PRE_BYTES_PER_TH * (th_total + th_resp) + PRE_PACK_BYTES_PER_SLOT_HEAD * n_chunk_heads
                                   + cm_bytes,
             "gdn_bwd_scan_kernel": SCAN_BYTES_PER_SLOT_HEAD * n_chunk_heads,
             "gdn_bwd_chunk_kernel": BWD_BYTES_PER_TH * (th_total + th_resp) + ckpt_bytes,
