@@ -161,6 +161,8 @@ static flare_status fwd_impl(const flare_varlen *varlen, const flare_gdn_shape *
   const ChunkLayout L = fwd_layout(vi, shape, win);
   char *const w = reinterpret_cast<char *>(workspace);
   a.workspace = reinterpret_cast<float *>(workspace);
+  if (win == 0 && vi.uniform_len > 0 && vi.uniform_len % kChunk == 0 && vi.num_docs > 1)
+    a.slot_order = vi.uniform_len / kChunk + 1;
   FwdPlan p{};
   p.win = win;
   p.max_chunks = max_chunks(vi);

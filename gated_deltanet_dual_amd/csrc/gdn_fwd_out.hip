@@ -63,7 +63,11 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = 4 * (lane >> 4), cl = lane & 15;
   const int H = f.H;
-  const int slot = blockIdx.x / H, h = blockIdx.x % H;
+  // the slot: in document order, or (equal documents) chunk-major from the
+  // last chunks down, so the chunk-start states the scan wrote last are read
+  // while they are still in the last-level cache
+  const int q = blockIdx.x / H, h = blockIdx.x % H;
+  const int slot = f.slot_order > 0 ? (q % f.num_docs) * f.slot_order + (f.slot_order - 1 - q / f.num_docs) : q;
   int doc, c;
   if (!slot_to_chunk(f, slot, doc, c)) return;
   const int64_t t0g = f.cu[doc];

@@ -51,6 +51,7 @@ flare_status check_varlen(const flare_varlen *v, int32_t block_size, VarlenInfo 
       return fail(FLARE_ERR_ALIGN, "prompt_lens[%d] = %d is not a multiple of block_size %d", i,
                   pl[i], block_size);
     if (n > vi.max_len) vi.max_len = (int32_t)n;
+    vi.uniform_len = i == 0 ? (int32_t)n : (vi.uniform_len == (int32_t)n ? vi.uniform_len : -1);
     vi.total_chunks += (n + kChunk - 1) / kChunk;
   }
   vi.total_tokens = cu[v->num_docs];

@@ -30,6 +30,7 @@ struct VarlenInfo {
   int64_t total_tokens = 0;
   int32_t max_len = 0;
   int64_t total_chunks = 0;  // sum over documents of ceil(n_i / kChunk)
+  int32_t uniform_len = -1;  // the documents' common length, or -1 when they differ (or there are none)
 };
 
 // Checks a flare_varlen: non-NULL host and device arrays (device arrays may be

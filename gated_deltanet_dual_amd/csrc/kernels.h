@@ -40,6 +40,10 @@ hipError_t launch_shortconv_bwd(const ShortConvBwdArgs &a, hipStream_t st);
 
 struct FwdArgs {
   int num_docs, H, D, B, flags, bf16, ckpt_stride;
+  // 0, or S when every document has S chunk slots (equal lengths, a multiple
+  // of the chunk, one pass): the output pass then visits the slots chunk-major
+  // from the last chunks down, the states the scan wrote last first
+  int slot_order;
   float scale;
   const int32_t *cu, *plen;
   const void *q, *k, *v, *qn, *kn, *vn;
