@@ -21,6 +21,20 @@ __device__ __forceinline__ void gslab_raw(u16 (&dst)[2][4], const u16 *src, int 
     for (int r = 0; r < 4; ++r)
       dst[tr][r] = src[((t0g + min(c0 + slab_row(tr, r), n - 1)) * H + h) * D + col0 + acc_col()];
 }
+// The same for a noisy-stream tensor: its prompt rows (never used, they read
+// as 0 through slab_mask) are loaded from the clean twin's same row instead,
+// which the same lanes load too, so they cost no HBM traffic.
+template <int D>
+__device__ __forceinline__ void gslab_raw_noisy(u16 (&dst)[2][4], const u16 *src, const u16 *clean, int H, int h,
+                                                int64_t t0g, int c0, int n, int P, int col0) {
+#pragma unroll
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = c0 + slab_row(tr, r);
+      dst[tr][r] = (row < P ? clean : src)[((t0g + min(row, n - 1)) * H + h) * D + col0 + acc_col()];
+    }
+}
 // rows past the document end, and prompt rows of the noisy stream, read as 0
 __device__ __forceinline__ Slab slab_mask(const u16 (&raw)[2][4], int c0, int n, int P, bool noisy) {
   Slab s;

@@ -93,6 +93,15 @@ __device__ __forceinline__ uint4 gfrag_raw(const u16 *src, int H, int h, int64_t
   const int tpos = c0 + row0 + (l & 15);
   return *reinterpret_cast<const uint4 *>(src + ((t0g + min(tpos, n - 1)) * H + h) * kD + k0 + 8 * (l >> 4));
 }
+// The same for a noisy-stream tensor: a prompt row (masked by frag_mask) is
+// read from the clean twin's same row, which the same lane loads too.
+__device__ __forceinline__ uint4 gfrag_raw_noisy(const u16 *src, const u16 *clean, int H, int h, int64_t t0g, int c0,
+                                                int n, int P, int row0, int k0) {
+  const int l = lane_id();
+  const int tpos = c0 + row0 + (l & 15);
+  return *reinterpret_cast<const uint4 *>((tpos < P ? clean : src) + ((t0g + min(tpos, n - 1)) * H + h) * kD + k0 +
+                                          8 * (l >> 4));
+}
 __device__ __forceinline__ bf16x8 frag_mask(const uint4 &v, int c0, int n, int P, bool noisy, int row0) {
   const int tpos = c0 + row0 + (lane_id() & 15);
   const bool ok = tpos < n && (!noisy || tpos >= P);
@@ -171,7 +180,8 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
     const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
     const int tpos = c0 + row;
     const bool ok = tpos < n && (m < 2 || tpos >= P);
-    const u16 *src = m == 0 ? pq : m == 1 ? pk : m == 2 ? pqn : pkn;
+    // a noisy prompt row (zeroed here) is read from the clean twin this thread loads too
+    const u16 *src = m == 0 || (m == 2 && tpos < P) ? pq : m == 1 || (m == 3 && tpos < P) ? pk : m == 2 ? pqn : pkn;
     const uint4 v = *reinterpret_cast<const uint4 *>(src + ((t0g + min(tpos, n - 1)) * H + h) * D + cu16 * 8);
     xr[e] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
   }
@@ -201,7 +211,9 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
   for (int e = 0; e < UX; ++e) {
     const int u = e * NT + tid;
     const int m = u / PU, r = u % PU, row = r / RU, cu16 = r % RU;
-    const u16 *src = m == 0 ? pv : m == 1 ? pvn : m == 2 ? pdo : pdon;
+    // (a noisy prompt row, zeroed when staged, is read from the clean twin this thread loads too)
+    const bool pr = c0 + row < P;
+    const u16 *src = m == 0 || (m == 1 && pr) ? pv : m == 1 ? pvn : m == 2 || pr ? pdo : pdon;
     vr[e] = *reinterpret_cast<const uint4 *>(src + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu16 * 8);
   }
   u16 (*const vst)[C][LDX] = reinterpret_cast<u16 (*)[C][LDX]>(&sm.arrp[0][0][0][0]);
@@ -516,7 +528,7 @@ __global__ __launch_bounds__(kNT) void gdn_bwd_chunk_d128_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       rfdo[tr][ks] = gfrag_raw(pdo, H, h, t0g, c0, n, 16 * tr, 32 * ks);
-      rfdon[tr][ks] = gfrag_raw(pdon, H, h, t0g, c0, n, 16 * tr, 32 * ks);
+      rfdon[tr][ks] = gfrag_raw_noisy(pdon, pdo, H, h, t0g, c0, n, P, 16 * tr, 32 * ks);
     }
 
   // rows [16 wave, 16 wave + 16) of dS' for the d_k tile of dk, raw fp32, in

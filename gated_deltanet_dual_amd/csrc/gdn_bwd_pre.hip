@@ -76,8 +76,13 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
   const int m = tid >> 7, tq = tid & 127, prow = 4 * (tq & 7), pu = tq >> 3;
   uint4 xv[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
-    xv[rr] = *reinterpret_cast<const uint4 *>(px[m] + ((t0g + min(c0 + prow + rr, n - 1)) * H + h) * D + 8 * pu);
+  for (int rr = 0; rr < 4; ++rr) {
+    // a noisy prompt row (masked below) is read from the clean twin, which
+    // another wave of the workgroup loads (selects, not an indexed array: no scratch)
+    const int ms = m >= 2 && c0 + prow + rr < P ? m - 2 : m;
+    const u16 *src = ms == 0 ? px[0] : ms == 1 ? px[1] : ms == 2 ? px[2] : px[3];
+    xv[rr] = *reinterpret_cast<const uint4 *>(src + ((t0g + min(c0 + prow + rr, n - 1)) * H + h) * D + 8 * pu);
+  }
   const float *tri = a.tri + ((size_t)slot * H + h) * 6 * C * C;
   float4 tv[3];
 #pragma unroll
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(pNT) void gdn_bwd_pre_d128_kernel(BwdArgs a) {
                                                                h)[2 * (tid / C)];
   u16 rdo[2][4], rdon[2][4];
   gslab_raw<D>(rdo, pdo, H, h, t0g, c0, n, col0);
-  gslab_raw<D>(rdon, pdon, H, h, t0g, c0, n, col0);
+  gslab_raw_noisy<D>(rdon, pdon, pdo, H, h, t0g, c0, n, P, col0);
   // this wave's K fragment (ks, tr) = (wave / 2, wave % 2): row 16 tr + (l & 15),
   // d_k 32 ks + 4 g .. +3 and 32 ks + 16 + 4 g .. +3
   uint2 ka0, ka1;

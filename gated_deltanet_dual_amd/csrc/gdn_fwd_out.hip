@@ -96,7 +96,10 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
     for (int e = 0; e < UX; ++e) {
       const int u = e * NT + tid;
       const int m = u / PU, r = u % PU, row = r / RU, cu = r % RU;
-      xr[e] = *reinterpret_cast<const uint4 *>(px[m] + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu * 8);
+      // a noisy prompt row (masked below) is read from the clean twin this thread loads too
+      const int ms = m >= 2 && c0 + row < P ? m - 2 : m;  // (selects, not an indexed array: no scratch)
+      const u16 *src = ms == 0 ? px[0] : ms == 1 ? px[1] : ms == 2 ? px[2] : px[3];
+      xr[e] = *reinterpret_cast<const uint4 *>(src + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu * 8);
     }
   }
   const float *cm = cmat + ((size_t)slot * H + h) * 6 * C * C;
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(oNT) void gdn_fwd_out_d128_kernel(FwdArgs f, const 
   u16 rv[2][4], rvn[2][4];
   if constexpr (CW == 0) {
     gslab_raw<D>(rv, pv, H, h, t0g, c0, n, col0);
-    gslab_raw<D>(rvn, pvn, H, h, t0g, c0, n, col0);
+    gslab_raw_noisy<D>(rvn, pvn, pv, H, h, t0g, c0, n, P, col0);
   }
   // S_c column slab as B fragments: k-slots of step ks are d_k rows
   // 32 ks + 4 g + e (e < 4) and 32 ks + 16 + 4 g + e - 4

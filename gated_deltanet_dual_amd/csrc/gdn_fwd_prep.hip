@@ -86,7 +86,10 @@ __global__ __launch_bounds__(pNT) void gdn_fwd_prep_d128_kernel(FwdArgs f, float
     for (int e = 0; e < UX; ++e) {
       const int u = e * NT + tid;
       const int m = u / PU, r = u % PU, row = r / RU, cu = r % RU;
-      xr[e] = ld_nt_u4(px[m] + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu * 8);  // read once here
+      // a noisy prompt row (masked later) is read from the clean twin this thread loads too
+      const int ms = m >= 2 && c0 + row < P ? m - 2 : m;  // (selects, not an indexed array: no scratch)
+      const u16 *src = ms == 0 ? px[0] : ms == 1 ? px[1] : ms == 2 ? px[2] : px[3];
+      xr[e] = ld_nt_u4(src + ((t0g + min(c0 + row, n - 1)) * H + h) * D + cu * 8);  // read once here
     }
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) gslab_raw<D>(rv[sb], pv, H, h, t0g, c0, n, 32 * wave + 16 * sb);
